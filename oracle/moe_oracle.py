@@ -1,0 +1,435 @@
+"""Plain fp64 CPU oracle of one MoE layer forward -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may use this module.  It is written from the pages alone, in
+NumPy float64 from exactly decoded inputs, shares no code with the HIP library,
+and is deliberately unoptimised: every step is its textbook definition or the
+algorithm's steps in the pages' order.
+
+Sources (cited by page title and section):
+
+* [SPICE] "SPICE: Speculative Prefetching with Low-Rank Expert Surrogates and
+  Heterogeneous Orchestration for MoE Inference Acceleration" (PaperDaily
+  summary).  Sections "MoE inference I/O bottleneck" (router picks top-k of N
+  experts per token), "Confidence-aware adaptive prefetch" (confidence = the
+  probability mass on the predicted top-K), "LoRE low-rank surrogate" (a
+  missing expert's output is replaced by y_shared + B_e A_e h).
+* [FloE] "FloE: On-the-Fly MoE Inference on Memory-constrained GPU" (Paper
+  Notes).  Sec. 1 "Hybrid compression": contextual sparsification forward
+  a^S(x) = (SiLU(x W_gate) * S_t(x W_up)) W_down with S_t a mask from the
+  magnitude of the up output; up projection stored as INT2.
+* [APEX] "APEX: Adaptive Expert Prefetching for Edge MoE Inference" (blog
+  summary).  Sec. 1 (router picks top-k of N), Sec. 4.1 (prefetch router: a
+  linear layer + softmax over experts), Sec. 4.2 (oracle budget delta*,
+  prefetch list = top-(k+delta)), Sec. 4.3 (stall-free mode, Algorithm 1).
+
+Readings where the pages are silent or garbled (each also listed in the design
+notes):
+
+* LoRE factor shapes: A_e is r x H and B_e is H x r, so B_e A_e h is an H-vector
+  (the page prints the two shapes the other way round, which cannot multiply h).
+* y_shared in the surrogate is the raw (ungated) sum of the shared-expert FFN
+  outputs; a surrogate slot keeps the missing expert's own routing weight; h is
+  the layer input x_t.
+* Ties in every ranking go to the lower expert id (lower channel for FloE).  A
+  decision whose deciding gap is below ``tie_margin`` (1e-4, absolute, in
+  logits or |u|) is flagged as a near-tie: several answers are correct there.
+* Stall-free: a substitute keeps its own original-router probability; weights
+  are renormalised over the final set when the layer renormalises; the final
+  slots are ordered by (-logit, id).
+* FloE keeps ``floe_keep`` channels per (token, routed expert) pair, ranked by
+  (-|u_i|, i); the gate is evaluated only where kept (SiLU(g)*0 = 0 elsewhere).
+* INT2 up weights decode as (q - z) * s with q the 2-bit code of input h at bits
+  2*(h%4) of byte h/4 and fp16 s, z per group of 64 consecutive inputs.
+* Dense expert down weights are stored [H][I] (output row h holds the I inputs);
+  FloE down weights are stored [I][H] (one channel's H-vector contiguous).
+
+Flag bits per token: 1 route near-tie, 2 prefetch near-tie, 4 substitution
+near-tie, 8 FloE mask near-tie.
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, Dict, List, Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "FLAG_ROUTE", "FLAG_PREFETCH", "FLAG_SUBST", "FLAG_FLOE",
+    "bf16_to_f64", "fp16_to_f64", "decode", "silu", "sigmoid",
+    "router_logits", "softmax", "rank_experts", "route_token",
+    "prefetch_set", "prefetch_masks", "delta_star", "stall_free_select",
+    "permute", "swiglu_expert", "dequant_int2", "floe_expert",
+    "shared_experts", "lore_residual", "layer_forward", "WeightSource",
+]
+
+FLAG_ROUTE, FLAG_PREFETCH, FLAG_SUBST, FLAG_FLOE = 1, 2, 4, 8
+MODES = ("standard", "lore", "stall_free", "floe")
+
+
+# ---------------------------------------------------------------- decoding --
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit pattern -> float64 (exact: a bf16 is the top half of an fp32)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def fp16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def decode(a: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return bf16_to_f64(a)
+    return np.asarray(a, dtype=np.float64)
+
+
+def silu(z):
+    """SiLU(z) = z / (1 + exp(-z))."""
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def sigmoid(z):
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-z))
+
+
+# ------------------------------------------------------------------ routing --
+def router_logits(x: np.ndarray, w_router: np.ndarray) -> np.ndarray:
+    """l[t, e] = sum_h x[t, h] W_r[h, e]: the router is a linear head over the
+    experts [APEX Sec. 1; SPICE "MoE inference I/O bottleneck"]."""
+    return x @ w_router
+
+
+def softmax(l: np.ndarray) -> np.ndarray:
+    """Max-subtracted softmax over the last axis."""
+    m = np.max(l, axis=-1, keepdims=True)
+    e = np.exp(l - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def rank_experts(score_row: Sequence[float]) -> List[int]:
+    """All expert ids ordered by (-score, id): ties go to the lower id."""
+    return sorted(range(len(score_row)), key=lambda e: (-float(score_row[e]), e))
+
+
+def route_token(l_row: np.ndarray, k: int, renormalize: bool, margin: float):
+    """Top-k routing of one token [APEX Sec. 1; SPICE "MoE inference I/O
+    bottleneck"], with the SPICE confidence = probability mass on the chosen
+    top-k [SPICE "Confidence-aware adaptive prefetch", Eq. 5].
+
+    Returns (ids in rank order, weights, mass, near-tie flag)."""
+    E = len(l_row)
+    order = rank_experts(l_row)
+    ids = order[:k]
+    p = softmax(np.asarray(l_row, dtype=np.float64))
+    mass = float(sum(p[e] for e in ids))
+    w = [p[e] / mass for e in ids] if renormalize else [p[e] for e in ids]
+    flag = k < E and (l_row[order[k - 1]] - l_row[order[k]]) < margin
+    return ids, np.array(w), mass, bool(flag)
+
+
+def prefetch_set(lp_row: np.ndarray, n: int, margin: float):
+    """K_p = the top-n experts by the prefetch router's score; the prefetch
+    router is linear + softmax and softmax keeps the order, so its logits rank
+    the same [APEX Sec. 4.1, Sec. 4.2 top-(k+delta) list].  Returns (bit mask,
+    near-tie flag)."""
+    E = len(lp_row)
+    order = rank_experts(lp_row)
+    mask = 0
+    for e in order[:n]:
+        mask |= 1 << e
+    flag = n < E and (lp_row[order[n - 1]] - lp_row[order[n]]) < margin
+    return mask, bool(flag)
+
+
+def prefetch_masks(x: np.ndarray, w_prefetch: np.ndarray, delta: np.ndarray, k: int,
+                   margin: float = 1e-4):
+    """Per-token prefetch masks top-(k + delta_t) of x W_p, and flag bit 2 for
+    near-ties at the list's edge."""
+    lp = router_logits(x, w_prefetch)
+    masks, flags = [], []
+    for t in range(x.shape[0]):
+        m, f = prefetch_set(lp[t], k + int(delta[t]), margin)
+        masks.append(m)
+        flags.append(FLAG_PREFETCH if f else 0)
+    return masks, np.array(flags, dtype=np.uint32), lp
+
+
+def delta_star(routed: Sequence[int], lp_row: np.ndarray, k: int) -> int:
+    """APEX oracle budget [Sec. 4.2]: the least delta in {0..N-k} such that the
+    routed set lies inside the top-(k+delta) prefetch list."""
+    E = len(lp_row)
+    order = rank_experts(lp_row)
+    for d in range(0, E - k + 1):
+        if set(routed) <= set(order[: k + d]):
+            return d
+    raise AssertionError("unreachable: delta = N-k lists every expert")
+
+
+def stall_free_select(k_routed: Sequence[int], q_r: np.ndarray, k_prefetched: set,
+                      margin: float):
+    """Stall-free substitution [APEX Sec. 4.3, Algorithm 1].
+
+    Every routed expert that was prefetched is kept; each missing one is
+    replaced by the prefetched, not-kept expert with the highest score under
+    the ORIGINAL router's softmax alpha = softmax(q_r).  Returns (final set,
+    near-tie flag).  The flag is raised when the last chosen substitute and
+    the best rejected candidate differ by less than ``margin`` in logits.
+    """
+    routed = set(k_routed)
+    prefetched = set(k_prefetched)
+    alpha = softmax(np.asarray(q_r, dtype=np.float64))
+    if routed <= prefetched:
+        return routed, False
+    keep = routed & prefetched
+    missing = routed - prefetched
+    candidates = sorted(prefetched - keep, key=lambda e: (-alpha[e], e))
+    n = len(missing)
+    subs = candidates[:n]
+    flag = len(candidates) > n and (q_r[candidates[n - 1]] - q_r[candidates[n]]) < margin
+    return keep | set(subs), bool(flag)
+
+
+# -------------------------------------------------------------- permutation --
+def permute(ids: np.ndarray, exact: np.ndarray, n_experts: int):
+    """Token->expert permutation: the exactly computed (token, slot) pairs,
+    flattened as f = t*k + j, grouped by expert with f increasing inside each
+    group.  Returns (offsets[E+1], perm[P] of f, inv[T*k] with -1 for pairs
+    that are not computed exactly)."""
+    flat_ids = np.asarray(ids, dtype=np.int64).reshape(-1)
+    flat_exact = np.asarray(exact, dtype=bool).reshape(-1)
+    groups = [np.nonzero((flat_ids == e) & flat_exact)[0] for e in range(n_experts)]
+    counts = np.array([len(g) for g in groups], dtype=np.int64)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    perm = (np.concatenate(groups) if len(groups) else np.zeros(0)).astype(np.int32)
+    inv = np.full(flat_ids.shape[0], -1, dtype=np.int32)
+    for p, f in enumerate(perm):
+        inv[f] = p
+    return offsets, perm, inv
+
+
+# ---------------------------------------------------------------- expert FFN --
+def swiglu_expert(x: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
+                  w_down_hi: np.ndarray) -> np.ndarray:
+    """SwiGLU expert FFN on rows of x: (SiLU(x W_gate) * (x W_up)) W_down
+    [FloE Sec. 1, sparsified forward with S_t = identity].  w_gate, w_up are
+    stored [I][H]; w_down_hi is stored [H][I]."""
+    g = x @ w_gate.T
+    u = x @ w_up.T
+    a = silu(g) * u
+    return a @ w_down_hi.T
+
+
+def dequant_int2(q_packed: np.ndarray, scale_bits: np.ndarray, zero_bits: np.ndarray) -> np.ndarray:
+    """Decode 2-bit group-quantised weights [FloE Sec. 1, ultra-low-bit up
+    projection]: code of input h is bits 2*(h%4)..2*(h%4)+1 of byte h/4; every
+    64 consecutive inputs share an fp16 scale s and zero z; weight = (q - z) * s.
+    Shapes: q [..., H/4], s and z [..., H/64] -> [..., H] float64."""
+    q = np.asarray(q_packed, dtype=np.uint8)
+    codes = np.stack([(q >> (2 * i)) & 3 for i in range(4)], axis=-1)
+    codes = codes.reshape(*q.shape[:-1], q.shape[-1] * 4).astype(np.float64)
+    s = np.repeat(fp16_to_f64(scale_bits), 64, axis=-1)
+    z = np.repeat(fp16_to_f64(zero_bits), 64, axis=-1)
+    return (codes - z) * s
+
+
+def floe_expert(x_t: np.ndarray, w_gate: np.ndarray, up_q, up_scale, up_zero,
+                w_down_ih: np.ndarray, n_keep: int, margin: float,
+                force_keep: Optional[np.ndarray] = None):
+    """FloE expert on one token [FloE Sec. 1, contextual sparsification]:
+    u = x W_up with INT2 W_up; S_t keeps the n_keep channels of largest |u|
+    (ties -> lower channel) and zeroes the rest; gate is applied only where
+    kept; y = (SiLU(x W_gate) * S_t(u)) W_down.  w_gate is [I][H]; w_down_ih is
+    [I][H] (channel rows).  Returns (y[H], u[I], keep ascending, flag)."""
+    w_up = dequant_int2(up_q, up_scale, up_zero)
+    u = w_up @ x_t
+    I = u.shape[0]
+    order = sorted(range(I), key=lambda i: (-abs(u[i]), i))
+    flag = n_keep < I and (abs(u[order[n_keep - 1]]) - abs(u[order[n_keep]])) < margin
+    keep = np.sort(np.array(order[:n_keep], dtype=np.int64)) if force_keep is None \
+        else np.sort(np.asarray(force_keep, dtype=np.int64))
+    g = w_gate[keep] @ x_t
+    a = silu(g) * u[keep]
+    y = a @ w_down_ih[keep]
+    return y, u, keep.astype(np.int32), bool(flag)
+
+
+def shared_experts(x: np.ndarray, ws_gate, ws_up, ws_down_hi, w_shared_gate=None):
+    """Always-active shared experts [SPICE "LoRE low-rank surrogate": the shared
+    expert is active for every token]: y_s = sum over shared experts of their
+    SwiGLU FFN; gate g_s = sigmoid(x . w_sg) when the layer has a scalar shared
+    gate, else 1.  Returns (y_s [T][H], g_s [T])."""
+    T, H = x.shape
+    y = np.zeros((T, H))
+    for s in range(len(ws_gate)):
+        y += swiglu_expert(x, ws_gate[s], ws_up[s], ws_down_hi[s])
+    g = sigmoid(x @ w_shared_gate) if w_shared_gate is not None else np.ones(T)
+    return y, g
+
+
+def lore_residual(x_t: np.ndarray, lore_a: np.ndarray, lore_b: np.ndarray) -> np.ndarray:
+    """LoRE low-rank residual B_e (A_e h) with A_e [r][H], B_e [H][r] [SPICE
+    "LoRE low-rank surrogate"]."""
+    return lore_b @ (lore_a @ x_t)
+
+
+# ---------------------------------------------------------- weight access --
+class WeightSource:
+    """Uniform access to a layer's weights in storage form.
+
+    ``src`` is either a mapping name -> stacked array, or an object with
+    ``expert(name, e)`` (per-expert draw) plus ``w_router()`` etc."""
+
+    def __init__(self, src, dtype: str):
+        self.src = src
+        self.dtype = dtype
+        self._memo: Dict = {}
+
+    def small(self, name: str):
+        if isinstance(self.src, dict):
+            v = self.src.get(name)
+        else:
+            v = getattr(self.src, name)() if hasattr(self.src, name) else None
+        return v
+
+    def expert(self, name: str, e: int):
+        if isinstance(self.src, dict):
+            return self.src[name][e]
+        return self.src.expert(name, e)
+
+    def f64(self, name: str, e: int) -> np.ndarray:
+        key = (name, e)
+        if key not in self._memo:
+            self._memo[key] = decode(self.expert(name, e), self.dtype)
+        return self._memo[key]
+
+
+# ------------------------------------------------------------- layer forward --
+def layer_forward(x, weights, dims: dict, mode: str, resident=None,
+                  force: Optional[dict] = None, tie_margin: float = 1e-4) -> dict:
+    """One MoE layer forward, every step in fp64.
+
+    x: [T][H] storage (bf16 bits or fp32); weights: mapping or per-expert source;
+    dims: hidden, n_experts, top_k, inter, n_shared, shared_inter, lore_rank,
+    renormalize, shared_gate, dtype, up_format, floe_keep.
+    resident: int bit mask (one for all tokens) or a length-T sequence of masks
+    (per token; the APEX prefetched set in mode stall_free).
+    force: optional {"ids": {t: final ids}, "keep": {(t, j): channels}} to
+    re-run with decisions taken elsewhere at flagged near-ties.
+
+    Steps: router logits -> softmax -> top-k [APEX Sec. 1]; stall-free
+    substitution [APEX Sec. 4.3]; residency split and LoRE surrogate for
+    non-resident experts [SPICE "LoRE low-rank surrogate"]; permutation;
+    SwiGLU experts, FloE experts [FloE Sec. 1]; shared experts; weighted
+    combine out = g_s y_s + sum_j w_j yhat_j.
+    """
+    assert mode in MODES, mode
+    force = force or {}
+    dt = dims["dtype"]
+    H, E, k = dims["hidden"], dims["n_experts"], dims["top_k"]
+    src = weights if isinstance(weights, WeightSource) else WeightSource(weights, dt)
+    X = decode(x, dt)
+    T = X.shape[0]
+    w_router = decode(src.small("w_router"), dt)
+    logits = router_logits(X, w_router)
+    probs = softmax(logits)
+
+    if resident is None:
+        res = [(1 << E) - 1] * T
+    elif isinstance(resident, (int, np.integer)):
+        res = [int(resident)] * T
+    else:
+        res = [int(m) for m in resident]
+
+    ids = np.zeros((T, k), dtype=np.int32)
+    wts = np.zeros((T, k))
+    mass = np.zeros(T)
+    flags = np.zeros(T, dtype=np.uint32)
+    n_subst = np.zeros(T, dtype=np.int32)
+    for t in range(T):
+        r_ids, r_w, m, f = route_token(logits[t], k, dims["renormalize"], tie_margin)
+        mass[t] = m
+        flags[t] |= FLAG_ROUTE if f else 0
+        final = list(r_ids)
+        if mode == "stall_free":
+            kp = {e for e in range(E) if (res[t] >> e) & 1}
+            S, fs = stall_free_select(r_ids, logits[t], kp, tie_margin)
+            flags[t] |= FLAG_SUBST if fs else 0
+            final = sorted(S, key=lambda e: (-logits[t][e], e))
+            n_subst[t] = len(set(final) - set(r_ids))
+        if t in force.get("ids", {}):
+            final = [int(e) for e in force["ids"][t]]
+        ids[t] = final
+        pw = np.array([probs[t][e] for e in final])
+        wts[t] = pw / pw.sum() if dims["renormalize"] else pw
+
+    if mode == "lore":
+        exact = np.array([[(res[t] >> int(ids[t, j])) & 1 for j in range(k)] for t in range(T)],
+                         dtype=np.uint8)
+    else:
+        exact = np.ones((T, k), dtype=np.uint8)
+
+    offsets, perm, inv = permute(ids, exact, E)
+
+    # routed experts, exact pairs (grouped by expert; each pair is independent)
+    y_pair = np.zeros((len(perm), H))
+    floe_keep: Dict = {}
+    floe_u: Dict = {}
+    for e in range(E):
+        seg = perm[offsets[e]:offsets[e + 1]]
+        if len(seg) == 0:
+            continue
+        toks = seg // k
+        if mode == "floe":
+            wg = src.f64("w_gate", e)
+            wd = src.f64("w_down", e)
+            for pos, f in zip(range(offsets[e], offsets[e + 1]), seg):
+                t, j = int(f) // k, int(f) % k
+                y, u, keep, fl = floe_expert(
+                    X[t], wg, src.expert("up_q", e), src.expert("up_scale", e),
+                    src.expert("up_zero", e), wd, dims["floe_keep"], tie_margin,
+                    force.get("keep", {}).get((t, j)))
+                y_pair[pos] = y
+                floe_keep[(t, j)] = keep
+                floe_u[(t, j)] = u
+                flags[t] |= FLAG_FLOE if fl else 0
+        else:
+            y_pair[offsets[e]:offsets[e + 1]] = swiglu_expert(
+                X[toks], src.f64("w_gate", e), src.f64("w_up", e), src.f64("w_down", e))
+
+    # shared experts
+    if dims["n_shared"] > 0:
+        ws_g = [src.f64("ws_gate", s) for s in range(dims["n_shared"])]
+        ws_u = [src.f64("ws_up", s) for s in range(dims["n_shared"])]
+        ws_d = [src.f64("ws_down", s) for s in range(dims["n_shared"])]
+        wsg = decode(src.small("w_shared_gate"), dt) if dims["shared_gate"] else None
+        y_shared, g_shared = shared_experts(X, ws_g, ws_u, ws_d, wsg)
+    else:
+        y_shared, g_shared = np.zeros((T, H)), np.zeros(T)
+
+    # LoRE residuals for non-exact slots
+    lore = np.zeros((T, k, H))
+    for t in range(T):
+        for j in range(k):
+            if not exact[t, j]:
+                e = int(ids[t, j])
+                lore[t, j] = lore_residual(X[t], src.f64("lore_A", e), src.f64("lore_B", e))
+
+    # weighted combine
+    out = np.zeros((T, H))
+    for t in range(T):
+        acc = g_shared[t] * y_shared[t]
+        for j in range(k):
+            if exact[t, j]:
+                yj = y_pair[inv[t * k + j]]
+            else:
+                yj = y_shared[t] + lore[t, j]
+            acc = acc + wts[t, j] * yj
+        out[t] = acc
+
+    return dict(out=out, logits=logits, probs=probs, ids=ids, weights=wts, mass=mass,
+                flags=flags, exact=exact, offsets=offsets, perm=perm, inv=inv,
+                y_pair=y_pair, y_shared=y_shared, g_shared=g_shared, lore=lore,
+                floe_keep=floe_keep, floe_u=floe_u, n_subst=n_subst)

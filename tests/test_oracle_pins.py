@@ -1,0 +1,501 @@
+"""Pins of the CPU oracle to facts the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a worked
+example derived by hand from scalar closed forms, brute force over all subsets,
+pure-Python loops on tiny shapes, identities, or reductions between modes.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------- hand example --
+def _hand():
+    with open(os.path.join(GOLD, "hand_example.json")) as f:
+        g = json.load(f)
+    w = {k: np.array(g[k], dtype=np.float32) for k in
+         ("w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down",
+          "lore_A", "lore_B")}
+    return g, np.array(g["x"], dtype=np.float32), w
+
+
+def _mask(ids):
+    m = 0
+    for e in ids:
+        m |= 1 << e
+    return m
+
+
+def _hand_expected():
+    """Worked by hand.  Logits are [2, 1, 0.5, 0] (x picks row 0 of W_r).
+    Expert outputs with x = [1, 0]: g = gate[0], u = up[0], y = SiLU(g) u down.
+    SiLU(z) = z sigma(z)."""
+    sig = lambda z: 1.0 / (1.0 + math.exp(-z))
+    s1, sm1, s2 = 1 * sig(1), -1 * sig(-1), 2 * sig(2)
+    y0 = (2 * s1, -2 * s1)            # g=1, u=2, down=[1,-1]
+    y1 = (0.0, 4 * sm1)               # g=-1, u=1, down=[0,4]
+    y2 = (s2, s2)                     # g=2, u=1, down=[1,1]
+    ys = (2 * s1, 0.0)                # shared: g=1, u=1, down=[2,0]
+    Z = math.exp(2) + math.exp(1) + math.exp(0.5) + 1.0
+    p = [math.exp(2) / Z, math.exp(1) / Z, math.exp(0.5) / Z, 1.0 / Z]
+    w_ren = (p[0] / (p[0] + p[1]), p[1] / (p[0] + p[1]))     # = sigma(1), sigma(-1)
+    w_un = (p[0], p[1])
+    comb = lambda w, ya, yb: tuple(ys[i] + w[0] * ya[i] + w[1] * yb[i] for i in range(2))
+    lore1 = (ys[0] + 0.0, ys[1] + 1.0)   # B1 A1 x = [0,1] * (1*1)
+    w_sf = (p[0] / (p[0] + p[2]), p[2] / (p[0] + p[2]))      # = sigma(1.5), sigma(-1.5)
+    return dict(p=p, w_ren=w_ren, sig15=sig(1.5),
+                standard_renorm=comb(w_ren, y0, y1), standard_unnorm=comb(w_un, y0, y1),
+                lore=comb(w_ren, y0, lore1),
+                lore_zero=comb(w_ren, y0, ys),
+                stall_free=comb(w_sf, y0, y2))
+
+
+def test_hand_example_closed_forms_match_decimal_values():
+    # The closed forms above reproduce the decimal values worked out by hand.
+    ex = _hand_expected()
+    np.testing.assert_allclose(ex["p"], [0.5792585299413738, 0.2130973042886238,
+                                         0.1292500485531628, 0.0783941172168397], rtol=1e-15)
+    np.testing.assert_allclose(ex["w_ren"][0], 0.7310585786300049, rtol=1e-15)
+    np.testing.assert_allclose(ex["standard_renorm"], [2.5310104480370557, -1.358211243291099], rtol=1e-14)
+    np.testing.assert_allclose(ex["stall_free"], [2.978866562875048, -0.8740299323461453], rtol=1e-14)
+
+
+@pytest.mark.parametrize("case", ["standard_renorm", "standard_unnorm", "lore", "lore_zero", "stall_free"])
+def test_hand_example(case):
+    g, x, w = _hand()
+    dims = dict(g["dims"])
+    ex = _hand_expected()
+    if case == "standard_unnorm":
+        dims["renormalize"] = False
+    mode = {"standard_renorm": "standard", "standard_unnorm": "standard", "lore": "lore",
+            "lore_zero": "lore", "stall_free": "stall_free"}[case]
+    if case == "lore_zero":
+        w["lore_A"] = np.zeros_like(w["lore_A"])
+        w["lore_B"] = np.zeros_like(w["lore_B"])
+    resident = None
+    if mode == "lore":
+        resident = _mask(g["resident_lore"])
+    if mode == "stall_free":
+        resident = [_mask(g["prefetched_stall_free"])]
+    r = O.layer_forward(x, w, dims, mode, resident=resident)
+    np.testing.assert_allclose(r["out"][0], ex[case], rtol=1e-14, atol=1e-15)
+    # decisions
+    if mode == "stall_free":
+        assert list(r["ids"][0]) == [0, 2] and r["n_subst"][0] == 1
+        np.testing.assert_allclose(r["weights"][0], [ex["sig15"], 1 - ex["sig15"]], rtol=1e-14)
+    else:
+        assert list(r["ids"][0]) == [0, 1]
+    np.testing.assert_allclose(r["mass"][0], ex["p"][0] + ex["p"][1], rtol=1e-15)
+    if mode == "lore":
+        assert list(r["exact"][0]) == [1, 0]
+
+
+# ------------------------------------------------------- routing pins ----
+def _rand_logits(rng, T, E, scale=1.0):
+    return rng.standard_normal((T, E)) * scale
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (8, 3), (6, 1), (5, 5), (7, 4)])
+def test_topk_is_max_mass_subset(E, k):
+    """Brute force over all C(E,k) subsets: the routed set maximises the
+    probability mass (no ties in continuous random logits)."""
+    rng = np.random.default_rng(10 + E * 10 + k)
+    for l in _rand_logits(rng, 50, E, 2.0):
+        ids, w, mass, flag = O.route_token(l, k, False, 1e-4)
+        p = np.exp(l - l.max()); p /= p.sum()
+        best = max(itertools.combinations(range(E), k), key=lambda s: sum(p[list(s)]))
+        assert set(ids) == set(best)
+        assert math.isclose(mass, sum(p[list(best)]), rel_tol=1e-12)
+        # rank order: descending logit
+        assert all(l[ids[i]] >= l[ids[i + 1]] for i in range(k - 1))
+
+
+def test_topk_ties_go_to_lower_id():
+    l = np.array([1.0, 3.0, 3.0, 0.5, 3.0])
+    ids, _, _, flag = O.route_token(l, 2, False, 1e-4)
+    assert ids == [1, 2] and flag  # 3.0 vs 3.0 at the cut: near-tie
+    ids, _, _, flag = O.route_token(l, 3, False, 1e-4)
+    assert ids == [1, 2, 4] and not flag
+
+
+def test_weights_mass_identities():
+    """Renormalised weights sum to 1; unnormalised sum to the SPICE confidence
+    mass C in [k/E, 1]; softmax sums to 1 and ignores a logit shift."""
+    rng = np.random.default_rng(3)
+    for E, k in [(8, 2), (64, 6), (64, 8), (40, 8)]:
+        for l in _rand_logits(rng, 20, E):
+            _, wr, C, _ = O.route_token(l, k, True, 1e-4)
+            _, wu, C2, _ = O.route_token(l, k, False, 1e-4)
+            assert math.isclose(wr.sum(), 1.0, rel_tol=1e-12)
+            assert math.isclose(wu.sum(), C, rel_tol=1e-12) and C == C2
+            assert k / E - 1e-12 <= C <= 1.0 + 1e-12
+            p = O.softmax(l)
+            assert math.isclose(p.sum(), 1.0, rel_tol=1e-12)
+            np.testing.assert_allclose(O.softmax(l + 7.25), p, rtol=1e-12)
+
+
+def test_softmax_two_expert_closed_form():
+    for a, b in [(0.0, 0.0), (1.0, -2.0), (30.0, 29.5)]:
+        p = O.softmax(np.array([a, b]))
+        assert math.isclose(p[0], 1.0 / (1.0 + math.exp(b - a)), rel_tol=1e-14)
+
+
+def test_router_logits_brute_force():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((3, 5)); wr = rng.standard_normal((5, 4))
+    l = O.router_logits(x, wr)
+    for t in range(3):
+        for e in range(4):
+            assert math.isclose(l[t, e], sum(x[t, h] * wr[h, e] for h in range(5)), rel_tol=1e-12)
+
+
+# ----------------------------------------------------- stall-free pins ----
+def _masked_topk(l, allowed, k):
+    return set(sorted(allowed, key=lambda e: (-l[e], e))[:k])
+
+
+def test_stall_free_equals_topk_within_prefetched_set():
+    """Algorithm 1 picks keep = routed and prefetched, and fills each miss with
+    the best remaining prefetched expert.  Every routed expert outranks every
+    non-routed one, so the result is the top-k of the router restricted to the
+    prefetched set -- checked by brute force on random tiny layers."""
+    rng = np.random.default_rng(5)
+    for _ in range(400):
+        E = int(rng.integers(3, 10)); k = int(rng.integers(1, E + 1))
+        l = rng.standard_normal(E)
+        routed = O.rank_experts(l)[:k]
+        n = int(rng.integers(k, E + 1))
+        kp = set(rng.permutation(E)[:n].tolist())
+        S, _ = O.stall_free_select(routed, l, kp, 1e-4)
+        assert len(S) == k and S <= kp
+        assert S == _masked_topk(l, kp, k)
+        assert set(routed) & kp <= S          # everything prefetched and routed is kept
+
+
+def test_stall_free_literal_sets():
+    l = np.array([5.0, 4.0, 3.0, 2.0, 1.0, 0.0])
+    # all hit
+    assert O.stall_free_select([0, 1], l, {0, 1, 5}, 1e-4) == ({0, 1}, False)
+    # one miss (1), candidates {3, 5}: the higher score 3 substitutes
+    assert O.stall_free_select([0, 1], l, {0, 3, 5}, 1e-4)[0] == {0, 3}
+    # both missing, take the best two of {2, 4, 5}
+    assert O.stall_free_select([0, 1], l, {2, 4, 5}, 1e-4)[0] == {2, 4}
+    # near-tie between the last substitute and the next candidate is flagged
+    l2 = np.array([5.0, 4.0, 1.0, 1.00005, 0.0])
+    S, f = O.stall_free_select([0, 1], l2, {0, 2, 3}, 1e-4)
+    assert S == {0, 3} and f
+
+
+def test_delta_star_bounds_substitution():
+    """With delta >= delta* the routed set is inside the prefetched list, so no
+    substitution happens [APEX Sec. 4.2]; delta = N-k prefetches everything;
+    a prefetch router equal to the router with delta = 0 prefetches K_r."""
+    rng = np.random.default_rng(6)
+    E, k = 12, 3
+    for _ in range(100):
+        l = rng.standard_normal(E); lp = rng.standard_normal(E)
+        routed = O.rank_experts(l)[:k]
+        ds = O.delta_star(routed, lp, k)
+        for d in range(ds, E - k + 1):
+            m, _ = O.prefetch_set(lp, k + d, 1e-4)
+            kp = {e for e in range(E) if (m >> e) & 1}
+            assert O.stall_free_select(routed, l, kp, 1e-4)[0] == set(routed)
+        if ds > 0:
+            m, _ = O.prefetch_set(lp, k + ds - 1, 1e-4)
+            kp = {e for e in range(E) if (m >> e) & 1}
+            assert not set(routed) <= kp
+        m, _ = O.prefetch_set(l, k, 1e-4)
+        assert {e for e in range(E) if (m >> e) & 1} == set(routed)
+
+
+# ------------------------------------------------------ permutation pins --
+def test_permutation_bucket_append_brute_force():
+    """Against a list-append counting sort written with plain loops."""
+    rng = np.random.default_rng(7)
+    for _ in range(50):
+        T, k, E = int(rng.integers(1, 12)), int(rng.integers(1, 5)), int(rng.integers(1, 9))
+        ids = rng.integers(0, E, size=(T, k))
+        exact = rng.integers(0, 2, size=(T, k))
+        off, perm, inv = O.permute(ids, exact, E)
+        buckets = [[] for _ in range(E)]
+        for t in range(T):
+            for j in range(k):
+                if exact[t, j]:
+                    buckets[ids[t, j]].append(t * k + j)
+        assert list(perm) == [f for b in buckets for f in b]
+        assert list(off) == [sum(len(b) for b in buckets[:e]) for e in range(E + 1)]
+        for f in range(T * k):
+            if exact.reshape(-1)[f]:
+                assert perm[inv[f]] == f
+            else:
+                assert inv[f] == -1
+
+
+# --------------------------------------------------------------- FFN pins --
+def test_swiglu_brute_force_loops():
+    rng = np.random.default_rng(8)
+    H, I, T = 5, 3, 2
+    x = rng.standard_normal((T, H))
+    wg = rng.standard_normal((I, H)); wu = rng.standard_normal((I, H)); wd = rng.standard_normal((H, I))
+    y = O.swiglu_expert(x, wg, wu, wd)
+    for t in range(T):
+        a = []
+        for i in range(I):
+            g = sum(x[t, h] * wg[i, h] for h in range(H))
+            u = sum(x[t, h] * wu[i, h] for h in range(H))
+            a.append(g / (1 + math.exp(-g)) * u)
+        for h in range(H):
+            assert math.isclose(y[t, h], sum(a[i] * wd[h, i] for i in range(I)), rel_tol=1e-12)
+
+
+def test_silu_sigmoid_closed_forms():
+    assert O.silu(np.float64(0.0)) == 0.0
+    assert math.isclose(O.silu(np.float64(1.0)), 0.7310585786300049, rel_tol=1e-15)
+    assert O.silu(np.float64(-800.0)) == 0.0          # no NaN at the far tail
+    assert O.silu(np.float64(800.0)) == 800.0
+    assert O.sigmoid(np.float64(0.0)) == 0.5
+
+
+def test_lore_brute_force_and_rank1():
+    rng = np.random.default_rng(9)
+    H, r = 6, 3
+    x = rng.standard_normal(H); A = rng.standard_normal((r, H)); B = rng.standard_normal((H, r))
+    res = O.lore_residual(x, A, B)
+    for h in range(H):
+        z = [sum(A[q, i] * x[i] for i in range(H)) for q in range(r)]
+        assert math.isclose(res[h], sum(B[h, q] * z[q] for q in range(r)), rel_tol=1e-12)
+    # rank 1, A = e_j^T, B = b  =>  residual = x_j b
+    j = 4; b = rng.standard_normal(H)
+    A1 = np.zeros((1, H)); A1[0, j] = 1.0
+    np.testing.assert_allclose(O.lore_residual(x, A1, b[:, None]), x[j] * b, rtol=1e-15)
+
+
+# -------------------------------------------------------------- INT2 pins --
+def test_int2_unpack_and_dequant_closed_forms():
+    # byte 0xE4 = 0b11_10_01_00 holds codes h0..h3 = 0, 1, 2, 3
+    q = np.full((1, 16), 0xE4, dtype=np.uint8)            # H = 64
+    s = np.array([[np.float16(2.0).view(np.uint16)]], dtype=np.uint16)
+    z = np.array([[np.float16(1.5).view(np.uint16)]], dtype=np.uint16)
+    w = O.dequant_int2(q, s, z)
+    np.testing.assert_array_equal(w[0, :4], [-3.0, -1.0, 1.0, 3.0])
+    np.testing.assert_array_equal(w[0], np.tile([-3.0, -1.0, 1.0, 3.0], 16))
+    # a second group uses its own scale/zero
+    q2 = np.zeros((1, 32), dtype=np.uint8); q2[0, 16:] = 0xFF      # group 1: all code 3
+    s2 = np.array([[np.float16(1.0).view(np.uint16), np.float16(0.5).view(np.uint16)]])
+    z2 = np.array([[np.float16(0.0).view(np.uint16), np.float16(1.0).view(np.uint16)]])
+    w2 = O.dequant_int2(q2, s2, z2)
+    assert np.all(w2[0, :64] == 0.0) and np.all(w2[0, 64:] == 1.0)
+
+
+def test_quantiser_error_bound():
+    """Round-to-nearest codes are within s/2 of the weight (the fp16 rounding
+    of s and z adds a little; clamping only affects the group's extremes)."""
+    rng = np.random.default_rng(11)
+    w = rng.standard_normal((4, 256)).astype(np.float32) * 0.02
+    q, s, z = W.quantize_int2_g64(w)
+    wh = O.dequant_int2(q, s, z)
+    sf = np.repeat(O.fp16_to_f64(s), 64, axis=-1)
+    assert np.all(np.abs(wh - w) <= 0.5 * sf * (1 + 4e-3) + 1e-7)
+
+
+def _floe_layer(rng, H=128, I=24, keep=5):
+    q, s, z = W.quantize_int2_g64(rng.standard_normal((I, H)).astype(np.float32) * 0.1)
+    wg = rng.standard_normal((I, H)) * 0.1
+    wd = rng.standard_normal((I, H)) * 0.1
+    return q, s, z, wg, wd
+
+
+def test_floe_full_keep_equals_dense_swiglu():
+    """keep = 100% makes FloE's forward the dense SwiGLU FFN on the decoded up
+    weights [FloE Sec. 1, S_t = identity]."""
+    rng = np.random.default_rng(12)
+    q, s, z, wg, wd = _floe_layer(rng)
+    x = rng.standard_normal(128)
+    y, u, keep, _ = O.floe_expert(x, wg, q, s, z, wd, 24, 1e-4)
+    dense = O.swiglu_expert(x[None], wg, O.dequant_int2(q, s, z), wd.T)[0]
+    np.testing.assert_allclose(y, dense, rtol=1e-12, atol=1e-14)
+    assert list(keep) == list(range(24))
+
+
+def test_floe_keep_one_closed_form_and_mask_rule():
+    rng = np.random.default_rng(13)
+    q, s, z, wg, wd = _floe_layer(rng)
+    x = rng.standard_normal(128)
+    y, u, keep, _ = O.floe_expert(x, wg, q, s, z, wd, 1, 1e-4)
+    i = int(np.argmax(np.abs(u)))
+    assert list(keep) == [i]
+    g = float(wg[i] @ x)
+    np.testing.assert_allclose(y, g / (1 + math.exp(-g)) * u[i] * wd[i], rtol=1e-12)
+    # keep = 5: exactly the five largest |u|, listed ascending
+    y5, u5, keep5, _ = O.floe_expert(x, wg, q, s, z, wd, 5, 1e-4)
+    assert set(keep5) == set(np.argsort(-np.abs(u5), kind="stable")[:5]) and list(keep5) == sorted(keep5)
+
+
+# ------------------------------------------------------- layer-level pins --
+def _small_layer(name="tiny", **kw):
+    cfg = W.CONFIGS[name]
+    lay = W.make_layer(name, **kw)
+    return lay
+
+
+def _dims(cfg):
+    return dict(hidden=cfg.hidden, n_experts=cfg.n_experts, top_k=cfg.top_k, inter=cfg.inter,
+                n_shared=cfg.n_shared, shared_inter=cfg.shared_inter, lore_rank=cfg.lore_rank,
+                renormalize=cfg.renormalize, shared_gate=cfg.shared_gate, dtype=cfg.dtype,
+                up_format=cfg.up_format, floe_keep=cfg.floe_keep)
+
+
+def _weights(lay):
+    w = {n: lay.full(n) for n in lay.tensor_names()}
+    w["w_router"] = lay.w_router()
+    if lay.cfg.shared_gate:
+        w["w_shared_gate"] = lay.w_shared_gate()
+    return w
+
+
+def test_all_resident_reduces_to_standard():
+    lay = _small_layer(); cfg = lay.cfg; w = _weights(lay); x = lay.x()
+    d = _dims(cfg)
+    std = O.layer_forward(x, w, d, "standard")
+    allres = (1 << cfg.n_experts) - 1
+    lore = O.layer_forward(x, w, d, "lore", resident=allres)
+    sf = O.layer_forward(x, w, d, "stall_free", resident=[allres] * x.shape[0])
+    for r in (lore, sf):
+        np.testing.assert_array_equal(r["ids"], std["ids"])
+        np.testing.assert_array_equal(r["out"], std["out"])
+
+
+def test_lore_zero_factors_give_shared_output_and_standard_when_experts_equal_shared():
+    lay = _small_layer(); cfg = lay.cfg; w = _weights(lay); x = lay.x(); d = _dims(cfg)
+    w["lore_A"] = np.zeros_like(w["lore_A"]); w["lore_B"] = np.zeros_like(w["lore_B"])
+    r = O.layer_forward(x, w, d, "lore", resident=lay.resident())
+    for t in range(x.shape[0]):
+        for j in range(cfg.top_k):
+            if not r["exact"][t, j]:
+                np.testing.assert_array_equal(r["lore"][t, j], 0.0)
+    # every routed expert equal to the single shared expert => LORE == STANDARD
+    for n, sn in (("w_gate", "ws_gate"), ("w_up", "ws_up"), ("w_down", "ws_down")):
+        w[n] = np.repeat(w[sn][:1], cfg.n_experts, axis=0)
+    a = O.layer_forward(x, w, d, "lore", resident=lay.resident())
+    b = O.layer_forward(x, w, d, "standard")
+    np.testing.assert_allclose(a["out"], b["out"], rtol=1e-12, atol=1e-14)
+    assert (a["exact"] == 0).any()
+
+
+def test_batch_invariance():
+    lay = _small_layer(); cfg = lay.cfg; w = _weights(lay); d = _dims(cfg)
+    full = O.layer_forward(lay.x(), w, d, "lore", resident=lay.resident())
+    for t in (0, 5, 15):
+        one = O.layer_forward(lay.x()[t:t + 1], w, d, "lore", resident=lay.resident())
+        np.testing.assert_allclose(one["out"][0], full["out"][t], rtol=1e-12, atol=1e-15)
+        np.testing.assert_array_equal(one["ids"][0], full["ids"][t])
+
+
+def test_expert_relabelling_equivariance():
+    lay = _small_layer(); cfg = lay.cfg; w = _weights(lay); x = lay.x(); d = _dims(cfg)
+    pi = np.random.default_rng(14).permutation(cfg.n_experts)     # new id j holds old expert pi[j]
+    w2 = dict(w)
+    w2["w_router"] = w["w_router"][:, pi]
+    for n in ("w_gate", "w_up", "w_down", "lore_A", "lore_B"):
+        w2[n] = w[n][pi]
+    res = lay.resident()
+    res2 = sum(1 << j for j in range(cfg.n_experts) if (res >> int(pi[j])) & 1)
+    a = O.layer_forward(x, w, d, "lore", resident=res)
+    b = O.layer_forward(x, w2, d, "lore", resident=res2)
+    np.testing.assert_allclose(a["out"], b["out"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(a["ids"], pi[b["ids"]])
+
+
+def test_down_scaling_is_linear():
+    lay = _small_layer(); cfg = lay.cfg; w = _weights(lay); x = lay.x(); d = _dims(cfg)
+    a = O.layer_forward(x, w, d, "standard")
+    w2 = dict(w); w2["w_down"] = w["w_down"] * 2; w2["ws_down"] = w["ws_down"] * 2
+    b = O.layer_forward(x, w2, d, "standard")
+    np.testing.assert_array_equal(b["out"], 2 * a["out"])
+
+
+def test_shared_gate_closed_form():
+    lay = _small_layer("tiny"); cfg = lay.cfg; w = _weights(lay); x = lay.x(); d = _dims(cfg)
+    d2 = dict(d, shared_gate=True)
+    w["w_shared_gate"] = np.zeros(cfg.hidden, dtype=np.float32)
+    a = O.layer_forward(x, w, d2, "standard")     # sigma(0) = 1/2
+    b = O.layer_forward(x, w, d, "standard")
+    np.testing.assert_allclose(a["out"], b["out"] - 0.5 * b["y_shared"], rtol=1e-12, atol=1e-14)
+
+
+def test_two_shared_experts_sum():
+    lay = _small_layer("tiny"); cfg = lay.cfg; w = _weights(lay); x = lay.x(); d = _dims(cfg)
+    w2 = dict(w)
+    for n in ("ws_gate", "ws_up", "ws_down"):
+        w2[n] = np.concatenate([w[n], w[n]], 0)
+    d2 = dict(d, n_shared=2)
+    a = O.layer_forward(x, w, d, "standard"); b = O.layer_forward(x, w2, d2, "standard")
+    np.testing.assert_allclose(b["y_shared"], 2 * a["y_shared"], rtol=1e-12)
+
+
+def _tiny_cfg(**kw):
+    import dataclasses
+    return dataclasses.replace(W.CONFIGS["tiny"], **kw)
+
+
+def test_floe_layer_full_keep_equals_standard_on_decoded_up():
+    """Layer level: FLOE with keep = I equals STANDARD run on the decoded INT2
+    up weights and the [H][I] view of the channel-major down weights."""
+    cfg = _tiny_cfg(name="tiny_floe", hidden=128, n_experts=4, top_k=2, inter=32, n_shared=0,
+                    shared_inter=0, lore_rank=0, dtype="bf16", up_format="int2_g64",
+                    floe_keep=32, renormalize=True, token_counts=(3,), modes=("floe",))
+    lay = W.Layer(cfg, 21)
+    w = _weights(lay); x = lay.x(); d = _dims(cfg)
+    r = O.layer_forward(x, w, d, "floe")
+    wd = dict(hidden=128, n_experts=4, top_k=2, inter=32, n_shared=0, shared_inter=0, lore_rank=0,
+              renormalize=True, shared_gate=False, dtype="f32", up_format="dense", floe_keep=0)
+    dense = {"w_router": O.bf16_to_f64(w["w_router"]), "w_gate": O.bf16_to_f64(w["w_gate"]),
+             "w_up": O.dequant_int2(w["up_q"], w["up_scale"], w["up_zero"]),
+             "w_down": np.transpose(O.bf16_to_f64(w["w_down"]), (0, 2, 1))}
+    s = O.layer_forward(O.bf16_to_f64(x), dense, wd, "standard")
+    np.testing.assert_array_equal(r["ids"], s["ids"])
+    np.testing.assert_allclose(r["out"], s["out"], rtol=1e-12, atol=1e-14)
+
+
+def test_stall_free_layer_uses_prefetch_masks():
+    cfg = _tiny_cfg(name="tiny_sf", n_experts=8, top_k=2, n_shared=0, shared_inter=0, lore_rank=0,
+                    renormalize=True, prefetch=True, modes=("standard", "stall_free"))
+    lay = W.Layer(cfg, 22)
+    w = _weights(lay); x = lay.x(); d = _dims(cfg)
+    masks, pflags, lp = O.prefetch_masks(O.decode(x, "f32"), O.decode(lay.w_prefetch(), "f32"),
+                                         np.zeros(x.shape[0], np.int32), cfg.top_k)
+    r = O.layer_forward(x, w, d, "stall_free", resident=masks)
+    l = r["logits"]
+    for t in range(x.shape[0]):
+        allowed = [e for e in range(8) if (masks[t] >> e) & 1]
+        assert list(r["ids"][t]) == sorted(allowed, key=lambda e: (-l[t, e], e))[:2]
+    assert r["n_subst"].sum() > 0
+
+
+def test_workload_generator_shapes_and_determinism():
+    for name, cfg in W.CONFIGS.items():
+        lay = W.make_layer(name)
+        assert lay.x().shape == (cfg.t_max, cfg.hidden)
+        m = lay.resident()
+        if cfg.resident_count:
+            assert bin(m).count("1") == cfg.resident_count
+        if cfg.prefetch:
+            d = lay.delta()
+            assert d.min() >= 0 and d.max() <= cfg.delta_cap
+            assert abs(d.mean() - 1.5) < 0.15          # Geometric(0.4) on {0,1,...}: mean 1.5
+    a = W.make_layer("tiny").expert("w_gate", 3); b = W.make_layer("tiny").expert("w_gate", 3)
+    np.testing.assert_array_equal(a, b)
+    assert W.make_layer("tiny").resident() == 0b1111
+    # bf16 rounding is round-to-nearest-even
+    v = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, 1.0 + 2**-8 + 2**-20], dtype=np.float32)
+    bits = W.bf16_bits_from_f32(v)
+    np.testing.assert_array_equal(O.bf16_to_f64(bits), [1.0, 1.0, 1.0 + 4 * 2**-8, 1.0 + 2**-7])
