@@ -1,0 +1,214 @@
+/*
+ * moe_route.h -- C ABI of the MI355X (gfx950) MoE-layer forward library.
+ *
+ * One MoE layer forward at decode and prefill token counts:
+ *   router logits -> softmax -> per-token top-k       [APEX page, Sec. 1;
+ *                                                       SPICE page, "MoE inference I/O bottleneck"]
+ *   stall-free substitution of non-prefetched experts  [APEX page, Sec. 4.3, Algorithm 1]
+ *   residency split + LoRE surrogate y_shared + B_e A_e h
+ *                                                      [SPICE page, "LoRE low-rank surrogate"]
+ *   token->expert permutation (stable counting sort)
+ *   SwiGLU expert FFNs, shared experts                 [FloE page, Sec. 1, forward a^S(x)]
+ *   FloE: up-magnitude channel mask + INT2 up weights  [FloE page, Sec. 1]
+ *   weighted combine.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named in a signature are DEVICE pointers unless marked (host).
+ *     moe_dims_t, moe_weights_t and moe_debug_t are host structs that hold
+ *     device pointers.  Every device pointer must be 16-byte aligned.
+ *   - The caller owns every buffer.  The library allocates nothing, frees
+ *     nothing, never synchronises, and keeps no state between calls; scratch
+ *     memory comes from the caller's workspace (moe_workspace_size()).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without waiting.  Calls on one stream are ordered.
+ *   - Errors are return codes.  All argument checks run on the host before
+ *     anything is enqueued: on any status other than MOE_OK nothing has been
+ *     enqueued.  MOE_EHIP reports a failed kernel launch.
+ *   - Layouts are row-major (C order).  "bf16" buffers hold bfloat16 bit
+ *     patterns, "fp16" buffers IEEE half bit patterns.  dtype (MOE_F32 or
+ *     MOE_BF16) applies to x, every dense weight, LoRE factors and out.
+ *   - Limits: E <= 64, 1 <= k <= min(8, E), H % 64 == 0, I % 16 == 0,
+ *     lore_rank <= 64, T >= 0 (T = 0 enqueues nothing and returns MOE_OK).
+ *
+ * Decisions.  Every ranking orders experts by (-logit, id) -- ties go to the
+ * lower expert id -- and FloE channels by (-|u|, channel).  A token whose
+ * deciding gap is below dims.tie_margin gets a flag bit (several answers are
+ * correct there): 1 route, 2 prefetch, 4 substitution, 8 FloE mask.
+ */
+#ifndef MOE_ROUTE_H
+#define MOE_ROUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+#define MOE_MAX_EXPERTS 64
+#define MOE_MAX_TOPK 8
+#define MOE_MAX_LORE_RANK 64
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,       /* null pointer where one is required, bad value, misaligned */
+  MOE_EUNSUPPORTED = 2, /* shape or mode outside the limits above                    */
+  MOE_EWORKSPACE = 3,   /* workspace smaller than moe_workspace_size()               */
+  MOE_EHIP = 4          /* a kernel launch failed                                    */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+typedef enum {
+  MOE_MODE_STANDARD = 0,   /* every routed expert computed exactly                     */
+  MOE_MODE_LORE = 1,       /* non-resident routed experts -> LoRE surrogate [SPICE]     */
+  MOE_MODE_STALL_FREE = 2, /* non-prefetched routed experts -> best prefetched [APEX]   */
+  MOE_MODE_FLOE = 3        /* INT2 up, top-|u| channel mask on gate/down [FloE]         */
+} moe_mode_t;
+
+typedef enum { MOE_UP_DENSE = 0, MOE_UP_INT2_G64 = 1 } moe_up_format_t;
+
+/* Layer shape (host struct). */
+typedef struct {
+  int32_t hidden;        /* H                                                     */
+  int32_t n_experts;     /* E, routed experts                                     */
+  int32_t top_k;         /* k                                                     */
+  int32_t inter;         /* I, routed expert intermediate size                    */
+  int32_t n_shared;      /* number of always-active shared experts (may be 0)     */
+  int32_t shared_inter;  /* I_s                                                   */
+  int32_t lore_rank;     /* r (0 when the layer has no LoRE factors)              */
+  int32_t renormalize;   /* 1: weights p_e / sum over the chosen set; 0: p_e      */
+  int32_t shared_gate;   /* 1: shared output scaled by sigmoid(x . w_sg)          */
+  int32_t floe_keep;     /* FloE channels kept per (token, expert) pair, 1..I     */
+  moe_dtype_t dtype;
+  moe_up_format_t up_format;
+  float tie_margin;      /* near-tie threshold for the flags (1e-4)               */
+} moe_dims_t;
+
+/* Layer weights (host struct of device pointers; unused entries may be NULL). */
+typedef struct {
+  const void* w_router;       /* [H][E] dtype                                          */
+  const void* w_gate;         /* [E][I][H] dtype: channel i's H inputs contiguous      */
+  const void* w_up;           /* [E][I][H] dtype (MOE_UP_DENSE)                        */
+  const void* w_down;         /* MOE_UP_DENSE: [E][H][I]; MOE_UP_INT2_G64: [E][I][H]   */
+  const uint8_t* up_q;        /* [E][I][H/4] INT2 codes, input h at bits 2*(h%4)       */
+  const uint16_t* up_scale;   /* [E][I][H/64] fp16 scale s                             */
+  const uint16_t* up_zero;    /* [E][I][H/64] fp16 zero z; weight = (q - z) * s        */
+  const void* ws_gate;        /* [n_s][I_s][H] dtype                                   */
+  const void* ws_up;          /* [n_s][I_s][H] dtype                                   */
+  const void* ws_down;        /* [n_s][H][I_s] dtype                                   */
+  const void* w_shared_gate;  /* [H] dtype, required when dims.shared_gate             */
+  const void* lore_A;         /* [E][r][H] dtype                                       */
+  const void* lore_B;         /* [E][H][r] dtype                                       */
+} moe_weights_t;
+
+/* Optional copies of intermediate results from moe_layer_forward (host
+ * struct of device pointers; each entry may be NULL). */
+typedef struct {
+  int32_t* topk_ids;     /* [T][k] final expert per slot, ordered by (-logit, id)  */
+  float* topk_w;         /* [T][k] combine weight per slot                          */
+  uint8_t* exact;        /* [T][k] 1 = computed exactly, 0 = LoRE surrogate         */
+  uint32_t* flags;       /* [T] near-tie flag bits                                  */
+  float* logits;         /* [T][E] router logits                                    */
+  float* mass;           /* [T] probability mass of the routed top-k                */
+  int32_t* expert_offsets; /* [E+1]                                                 */
+  int32_t* perm;         /* [T*k] (first offsets[E] entries meaningful)             */
+  int32_t* floe_keep;    /* [T][k][floe_keep] kept channels, ascending (FLOE)       */
+} moe_debug_t;
+
+int moe_abi_version(void);
+const char* moe_status_string(moe_status_t status);
+
+/* Bytes of device workspace that moe_layer_forward / moe_expert_ffn /
+ * moe_permute need for T tokens in `mode` (host output). */
+moe_status_t moe_workspace_size(const moe_dims_t* dims, int32_t T, moe_mode_t mode,
+                                size_t* bytes /* host */);
+
+/* Router: logits l = x W_r, softmax p, top-k by (-l, id) [APEX page, Sec. 1;
+ * SPICE page, "MoE inference I/O bottleneck"].
+ *   x [T][H] dtype, w_router [H][E] dtype.
+ *   resident: uint64 expert bit masks; resident_stride 0 = one mask for all
+ *     tokens, 1 = one mask per token.  LORE: exact[t][j] = bit of expert.
+ *     STALL_FREE: the token's prefetched set; the final set is the routed set
+ *     with each non-prefetched expert replaced by the best-scoring prefetched
+ *     one under the original router [APEX page, Sec. 4.3, Algorithm 1].
+ *     STANDARD / FLOE: ignored (may be NULL); every slot exact.
+ *   Outputs: topk_ids [T][k] int32 ordered by (-l, id); topk_w [T][k] fp32
+ *     (p_e, or p_e / sum over the set when dims.renormalize); exact [T][k];
+ *     flags [T]; logits_opt [T][E] fp32 and mass_opt [T] fp32 (SPICE
+ *     confidence: mass of the routed top-k) may be NULL. */
+moe_status_t moe_route(const moe_dims_t* dims, int32_t T, const void* x, const void* w_router,
+                       const uint64_t* resident, int64_t resident_stride, moe_mode_t mode,
+                       int32_t* topk_ids, float* topk_w, uint8_t* exact, uint32_t* flags,
+                       float* logits_opt, float* mass_opt, void* stream);
+
+/* APEX prefetch set: mask_out[t] = bit mask of the top-(k + delta[t]) experts
+ * of x W_p (a linear prefetch router; softmax keeps the order) [APEX page,
+ * Sec. 4.1 and Sec. 4.2].  delta [T] int32 in 0..E-k.  flags [T] is
+ * overwritten: bit 2 where the list's last member and the next expert differ
+ * by less than dims.tie_margin in logits, else 0. */
+moe_status_t moe_prefetch_mask(const moe_dims_t* dims, int32_t T, const void* x,
+                               const void* w_prefetch, const int32_t* delta,
+                               uint64_t* mask_out, uint32_t* flags, void* stream);
+
+/* Stable counting sort of the exact (token, slot) pairs by expert: pair
+ * f = t*k + j.  expert_offsets [E+1]; perm [T*k] holds f, grouped by expert,
+ * f increasing inside a group (first offsets[E] entries); inv [T*k] = position
+ * of pair f in perm, or -1 when not exact.  ws: at least
+ * moe_workspace_size(dims with these T, k, E, STANDARD) bytes. */
+moe_status_t moe_permute(int32_t T, int32_t k, int32_t E, const int32_t* topk_ids,
+                         const uint8_t* exact, int32_t* expert_offsets, int32_t* perm,
+                         int32_t* inv, void* ws, size_t ws_bytes, void* stream);
+
+/* Expert FFNs for the permuted pairs and the shared experts.
+ *   Dense: y_perm[p] = SwiGLU_e(x_t) = (SiLU(x W_g) * (x W_u)) W_d for pair
+ *     p = (t, e) [FloE page, Sec. 1, S_t = identity], unweighted, fp32 [T*k][H].
+ *   FLOE: u = x W_up with W_up = (q - z) * s; keep the dims.floe_keep channels
+ *     of largest |u| (ties -> lower channel); y = sum over kept i of
+ *     SiLU(g_i) u_i W_d[i,:] [FloE page, Sec. 1].  floe_keep_opt [T*k][keep]
+ *     receives the kept channels of slot f = t*k + j (ascending); flags_opt [T] gets
+ *     bit 8 OR-ed in for a near-tie at the mask edge (may be NULL).
+ *   Shared: y_shared [T][H] fp32 = sum of the shared SwiGLU FFNs (ungated);
+ *     shared_gate [T] fp32 = sigmoid(x . w_sg), or 1.  Both may be NULL when
+ *     n_shared = 0.
+ *   expert_offsets / perm come from moe_permute. */
+moe_status_t moe_expert_ffn(const moe_dims_t* dims, int32_t T, const void* x,
+                            const moe_weights_t* w, moe_mode_t mode,
+                            const int32_t* expert_offsets, const int32_t* perm,
+                            float* y_perm, float* y_shared, float* shared_gate,
+                            int32_t* floe_keep_opt, uint32_t* flags_opt,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* LoRE residual [SPICE page, "LoRE low-rank surrogate"]: for each slot with
+ * exact[t][j] == 0, lore_out[t][j] = B_e (A_e x_t) with A_e [r][H] and
+ * B_e [H][r]; slots with exact == 1 get 0.  lore_out [T][k][H] fp32. */
+moe_status_t moe_lore_surrogate(const moe_dims_t* dims, int32_t T, const void* x,
+                                const int32_t* topk_ids, const uint8_t* exact,
+                                const void* lore_A, const void* lore_B, float* lore_out,
+                                void* stream);
+
+/* Weighted combine: out[t] = g_s(t) y_s(t) + sum_j w_tj yhat_tj with
+ * yhat = y_perm[inv[t*k+j]] for exact slots and y_s(t) + lore_out[t][j]
+ * otherwise.  y_shared / shared_gate / lore_out may be NULL (read as 0, 1, 0).
+ * out [T][H] dtype, rounded to nearest even for bf16. */
+moe_status_t moe_combine(const moe_dims_t* dims, int32_t T, const float* y_perm,
+                         const int32_t* inv, const float* topk_w, const uint8_t* exact,
+                         const float* y_shared, const float* shared_gate,
+                         const float* lore_out, void* out, void* stream);
+
+/* The whole layer in one call: route (+ substitution / residency split),
+ * permute, expert FFNs, shared experts, LoRE surrogate fused into the
+ * combine.  x [T][H] dtype -> out [T][H] dtype.  resident / resident_stride
+ * as in moe_route.  dbg_opt (host struct, may be NULL) receives copies of
+ * intermediates.  ws: moe_workspace_size(dims, T, mode) bytes. */
+moe_status_t moe_layer_forward(const moe_dims_t* dims, int32_t T, const void* x,
+                               const moe_weights_t* w, const uint64_t* resident,
+                               int64_t resident_stride, moe_mode_t mode, void* out,
+                               const moe_debug_t* dbg_opt, void* ws, size_t ws_bytes,
+                               void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_ROUTE_H */

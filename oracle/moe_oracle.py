@@ -300,10 +300,15 @@ class WeightSource:
         return self.src.expert(name, e)
 
     def f64(self, name: str, e: int) -> np.ndarray:
+        """Decoded float64 copy; small tensors are kept, large ones re-decoded
+        on each request so a sampled forward of a large layer stays small."""
         key = (name, e)
-        if key not in self._memo:
-            self._memo[key] = decode(self.expert(name, e), self.dtype)
-        return self._memo[key]
+        if key in self._memo:
+            return self._memo[key]
+        v = decode(self.expert(name, e), self.dtype)
+        if v.nbytes <= (1 << 22):
+            self._memo[key] = v
+        return v
 
 
 # ------------------------------------------------------------- layer forward --

@@ -1,0 +1,213 @@
+"""ctypes binding of libmoe_route.so: argument marshalling only.
+
+Every function named ``moe_*`` here calls the C entry point of the same name
+declared in include/moe_route.h; all work runs in the library's HIP kernels.
+PyTorch supplies device memory (tensors are passed by ``data_ptr()``) and the
+current stream.  A missing library is an ImportError: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Dict, Optional
+
+import torch  # loaded first so the library binds to the same HIP runtime
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_route.so")
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+MODES = {"standard": 0, "lore": 1, "stall_free": 2, "floe": 3}
+MOE_UP_DENSE, MOE_UP_INT2_G64 = 0, 1
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_lib.moe_status_string(status).decode()} (status {status})")
+
+
+class MoeDims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("n_shared", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
+                ("lore_rank", ctypes.c_int32), ("renormalize", ctypes.c_int32),
+                ("shared_gate", ctypes.c_int32), ("floe_keep", ctypes.c_int32),
+                ("dtype", ctypes.c_int), ("up_format", ctypes.c_int),
+                ("tie_margin", ctypes.c_float)]
+
+
+_WEIGHT_FIELDS = ["w_router", "w_gate", "w_up", "w_down", "up_q", "up_scale", "up_zero",
+                  "ws_gate", "ws_up", "ws_down", "w_shared_gate", "lore_A", "lore_B"]
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in _WEIGHT_FIELDS]
+
+
+_DEBUG_FIELDS = ["topk_ids", "topk_w", "exact", "flags", "logits", "mass", "expert_offsets",
+                 "perm", "floe_keep"]
+
+
+class MoeDebug(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in _DEBUG_FIELDS]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run sparse_moe_layer_route_amd.build.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    D, Wp, Dbg = ctypes.POINTER(MoeDims), ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeDebug)
+    sig = {
+        "moe_abi_version": ([], ctypes.c_int),
+        "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "moe_workspace_size": ([D, I32, ctypes.c_int, ctypes.POINTER(SZ)], ctypes.c_int),
+        "moe_route": ([D, I32, P, P, P, I64, ctypes.c_int, P, P, P, P, P, P, P], ctypes.c_int),
+        "moe_prefetch_mask": ([D, I32, P, P, P, P, P, P], ctypes.c_int),
+        "moe_permute": ([I32, I32, I32, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+        "moe_expert_ffn": ([D, I32, P, Wp, ctypes.c_int, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+        "moe_lore_surrogate": ([D, I32, P, P, P, P, P, P, P], ctypes.c_int),
+        "moe_combine": ([D, I32, P, P, P, P, P, P, P, P, P], ctypes.c_int),
+        "moe_layer_forward": ([D, I32, P, Wp, P, I64, ctypes.c_int, P, Dbg, P, SZ, P], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+EXPORTED = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_route",
+            "moe_prefetch_mask", "moe_permute", "moe_expert_ffn", "moe_lore_surrogate",
+            "moe_combine", "moe_layer_forward")
+
+
+# ------------------------------------------------------------------ helpers --
+@dataclasses.dataclass
+class Dims:
+    hidden: int
+    n_experts: int
+    top_k: int
+    inter: int
+    n_shared: int = 0
+    shared_inter: int = 0
+    lore_rank: int = 0
+    renormalize: bool = False
+    shared_gate: bool = False
+    floe_keep: int = 0
+    dtype: str = "bf16"
+    up_format: str = "dense"
+    tie_margin: float = 1e-4
+
+    def c(self) -> MoeDims:
+        return MoeDims(self.hidden, self.n_experts, self.top_k, self.inter, self.n_shared,
+                       self.shared_inter, self.lore_rank, int(self.renormalize),
+                       int(self.shared_gate), self.floe_keep,
+                       MOE_BF16 if self.dtype == "bf16" else MOE_F32,
+                       MOE_UP_INT2_G64 if self.up_format == "int2_g64" else MOE_UP_DENSE,
+                       self.tie_margin)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(stream)
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoEError(status, where)
+
+
+def _mode(mode) -> int:
+    return MODES[mode] if isinstance(mode, str) else int(mode)
+
+
+def _dims(d) -> MoeDims:
+    return d.c() if isinstance(d, Dims) else d
+
+
+# ------------------------------------------------------------- entry points --
+def moe_abi_version() -> int:
+    return _lib.moe_abi_version()
+
+
+def moe_workspace_size(dims, T: int, mode) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.moe_workspace_size(ctypes.byref(_dims(dims)), T, _mode(mode), ctypes.byref(n)),
+           "moe_workspace_size")
+    return n.value
+
+
+def moe_route(dims, T, x, w_router, resident, resident_stride, mode, topk_ids, topk_w, exact,
+              flags, logits=None, mass=None, stream=None):
+    _check(_lib.moe_route(ctypes.byref(_dims(dims)), T, _ptr(x), _ptr(w_router), _ptr(resident),
+                          resident_stride, _mode(mode), _ptr(topk_ids), _ptr(topk_w), _ptr(exact),
+                          _ptr(flags), _ptr(logits), _ptr(mass), _stream(stream)), "moe_route")
+
+
+def moe_prefetch_mask(dims, T, x, w_prefetch, delta, mask_out, flags, stream=None):
+    _check(_lib.moe_prefetch_mask(ctypes.byref(_dims(dims)), T, _ptr(x), _ptr(w_prefetch),
+                                  _ptr(delta), _ptr(mask_out), _ptr(flags), _stream(stream)),
+           "moe_prefetch_mask")
+
+
+def moe_permute(T, k, E, topk_ids, exact, expert_offsets, perm, inv, ws=None, stream=None):
+    _check(_lib.moe_permute(T, k, E, _ptr(topk_ids), _ptr(exact), _ptr(expert_offsets), _ptr(perm),
+                            _ptr(inv), _ptr(ws), ws.numel() if ws is not None else 0,
+                            _stream(stream)), "moe_permute")
+
+
+def weights_struct(w: Dict[str, torch.Tensor]) -> MoeWeights:
+    return MoeWeights(*[_ptr(w.get(n)) for n in _WEIGHT_FIELDS])
+
+
+def moe_expert_ffn(dims, T, x, weights, mode, expert_offsets, perm, y_perm, y_shared, shared_gate,
+                   ws, floe_keep=None, flags=None, stream=None):
+    ws_struct = weights if isinstance(weights, MoeWeights) else weights_struct(weights)
+    _check(_lib.moe_expert_ffn(ctypes.byref(_dims(dims)), T, _ptr(x), ctypes.byref(ws_struct),
+                               _mode(mode), _ptr(expert_offsets), _ptr(perm), _ptr(y_perm),
+                               _ptr(y_shared), _ptr(shared_gate), _ptr(floe_keep), _ptr(flags),
+                               _ptr(ws), ws.numel(), _stream(stream)), "moe_expert_ffn")
+
+
+def moe_lore_surrogate(dims, T, x, topk_ids, exact, lore_A, lore_B, lore_out, stream=None):
+    _check(_lib.moe_lore_surrogate(ctypes.byref(_dims(dims)), T, _ptr(x), _ptr(topk_ids),
+                                   _ptr(exact), _ptr(lore_A), _ptr(lore_B), _ptr(lore_out),
+                                   _stream(stream)), "moe_lore_surrogate")
+
+
+def moe_combine(dims, T, y_perm, inv, topk_w, exact, y_shared, shared_gate, lore_out, out,
+                stream=None):
+    _check(_lib.moe_combine(ctypes.byref(_dims(dims)), T, _ptr(y_perm), _ptr(inv), _ptr(topk_w),
+                            _ptr(exact), _ptr(y_shared), _ptr(shared_gate), _ptr(lore_out),
+                            _ptr(out), _stream(stream)), "moe_combine")
+
+
+def moe_layer_forward(dims, T, x, weights, resident, resident_stride, mode, out, ws, debug=None,
+                      stream=None):
+    ws_struct = weights if isinstance(weights, MoeWeights) else weights_struct(weights)
+    dbg = None
+    if debug is not None:
+        dbg = ctypes.byref(MoeDebug(*[_ptr(debug.get(n)) for n in _DEBUG_FIELDS]))
+    _check(_lib.moe_layer_forward(ctypes.byref(_dims(dims)), T, _ptr(x), ctypes.byref(ws_struct),
+                                  _ptr(resident), resident_stride, _mode(mode), _ptr(out), dbg,
+                                  _ptr(ws), ws.numel(), _stream(stream)), "moe_layer_forward")

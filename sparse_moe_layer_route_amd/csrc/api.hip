@@ -1,0 +1,346 @@
+// Host side of the C ABI declared in include/moe_route.h: argument checks,
+// workspace carving and kernel enqueueing.  Nothing here allocates, frees or
+// synchronises; every check runs before the first enqueue.
+#include <string.h>
+
+#include "common.h"
+
+namespace moe {
+hipError_t launch_route(const moe_dims_t& d, int T, const void* x, const void* w_router,
+                        const uint64_t* resident, int64_t res_stride, int mode, int32_t* ids,
+                        float* w, uint8_t* exact, uint32_t* flags, float* logits, float* mass,
+                        hipStream_t s);
+hipError_t launch_prefetch(const moe_dims_t& d, int T, const void* x, const void* w_p,
+                           const int32_t* delta, uint64_t* mask_out, uint32_t* flags,
+                           hipStream_t s);
+hipError_t launch_permute(int n_pairs, int E, const int32_t* ids, const uint8_t* exact,
+                          int32_t* offsets, int32_t* perm, int32_t* inv, hipStream_t s);
+hipError_t launch_dense_ffn(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
+                            const int32_t* offsets, const int32_t* perm, int n_pairs_max,
+                            float* act, float* y_perm, float* act_s, float* y_s, float* g_s,
+                            hipStream_t s);
+hipError_t launch_floe(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
+                       const int32_t* offsets, const int32_t* perm, float* u, int32_t* keep,
+                       float* a, float* part, float* y_perm, uint32_t* flags, hipStream_t s);
+hipError_t launch_combine(const moe_dims_t& d, int T, const float* y_perm, const int32_t* inv,
+                          const float* topk_w, const uint8_t* exact, const int32_t* ids,
+                          const float* y_s, const float* g_s, const float* lore_out, const void* x,
+                          const void* lore_A, const void* lore_B, void* out, hipStream_t s);
+hipError_t launch_lore(const moe_dims_t& d, int T, const void* x, const int32_t* ids,
+                       const uint8_t* exact, const void* lore_A, const void* lore_B,
+                       float* lore_out, hipStream_t s);
+int floe_slices(int n_keep);
+int floe_max_inter();
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+constexpr int32_t kMaxTokens = 1 << 22;
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
+inline bool ok_opt(const void* p) { return p == nullptr || aligned16(p); }
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+moe_status_t check_dims(const moe_dims_t* d) {
+  if (!d) return MOE_EINVAL;
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_EINVAL;
+  if (d->up_format != MOE_UP_DENSE && d->up_format != MOE_UP_INT2_G64) return MOE_EINVAL;
+  if (d->hidden <= 0 || d->n_experts <= 0 || d->top_k <= 0 || d->inter <= 0) return MOE_EINVAL;
+  if (d->n_shared < 0 || d->shared_inter < 0 || d->lore_rank < 0) return MOE_EINVAL;
+  if (!(d->tie_margin >= 0.f)) return MOE_EINVAL;
+  if (d->n_experts > MOE_MAX_EXPERTS || d->top_k > MOE_MAX_TOPK || d->top_k > d->n_experts)
+    return MOE_EUNSUPPORTED;
+  if (d->hidden % 64 != 0 || d->inter % 16 != 0) return MOE_EUNSUPPORTED;
+  if (d->n_shared > 0 && (d->shared_inter <= 0 || d->shared_inter % 16 != 0)) return MOE_EUNSUPPORTED;
+  if (d->lore_rank > MOE_MAX_LORE_RANK || d->lore_rank % 8 != 0) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status_t check_mode(const moe_dims_t* d, moe_mode_t mode) {
+  switch (mode) {
+    case MOE_MODE_STANDARD:
+    case MOE_MODE_STALL_FREE:
+      return d->up_format == MOE_UP_DENSE ? MOE_OK : MOE_EUNSUPPORTED;
+    case MOE_MODE_LORE:
+      if (d->up_format != MOE_UP_DENSE || d->lore_rank == 0) return MOE_EUNSUPPORTED;
+      return MOE_OK;
+    case MOE_MODE_FLOE:
+      if (d->up_format != MOE_UP_INT2_G64) return MOE_EUNSUPPORTED;
+      if (d->floe_keep < 1 || d->floe_keep > d->inter) return MOE_EINVAL;
+      if (d->inter > floe_max_inter()) return MOE_EUNSUPPORTED;
+      return MOE_OK;
+  }
+  return MOE_EINVAL;
+}
+
+moe_status_t check_weights(const moe_dims_t* d, const moe_weights_t* w, moe_mode_t mode) {
+  if (!w) return MOE_EINVAL;
+  if (!ok_ptr(w->w_router) || !ok_ptr(w->w_gate) || !ok_ptr(w->w_down)) return MOE_EINVAL;
+  if (mode == MOE_MODE_FLOE) {
+    if (!ok_ptr(w->up_q) || !ok_ptr(w->up_scale) || !ok_ptr(w->up_zero)) return MOE_EINVAL;
+  } else if (!ok_ptr(w->w_up)) {
+    return MOE_EINVAL;
+  }
+  if (d->n_shared > 0) {
+    if (!ok_ptr(w->ws_gate) || !ok_ptr(w->ws_up) || !ok_ptr(w->ws_down)) return MOE_EINVAL;
+    if (d->shared_gate && !ok_ptr(w->w_shared_gate)) return MOE_EINVAL;
+  }
+  if (mode == MOE_MODE_LORE && (!ok_ptr(w->lore_A) || !ok_ptr(w->lore_B))) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+// Workspace plan for T tokens.
+struct Plan {
+  size_t ids, w, exact, flags, offsets, perm, inv;       // routing + permutation
+  size_t act, act_s, y_perm, y_s, g_s;                   // dense FFN
+  size_t u, keep, fa, part;                              // FloE
+  size_t ffn_begin, total;
+};
+
+Plan make_plan(const moe_dims_t& d, int T, moe_mode_t mode) {
+  Plan p{};
+  const size_t P = (size_t)T * d.top_k;
+  const size_t H = d.hidden, I = d.inter;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o = align256(o + bytes); return at; };
+  p.ids = take(P * 4);
+  p.w = take(P * 4);
+  p.exact = take(P);
+  p.flags = take((size_t)T * 4);
+  p.offsets = take((size_t)(d.n_experts + 1) * 4);
+  p.perm = take(P * 4);
+  p.inv = take(P * 4);
+  p.ffn_begin = o;
+  p.y_perm = take(P * H * 4);
+  if (mode == MOE_MODE_FLOE) {
+    p.u = take(P * I * 4);
+    p.keep = take(P * (size_t)d.floe_keep * 4);
+    p.fa = take(P * (size_t)d.floe_keep * 4);
+    p.part = take((size_t)floe_slices(d.floe_keep) * P * H * 4);
+  } else {
+    p.act = take(P * I * 4);
+  }
+  if (d.n_shared > 0) {
+    p.act_s = take((size_t)T * d.n_shared * d.shared_inter * 4);
+    p.y_s = take((size_t)T * H * 4);
+    p.g_s = take((size_t)T * 4);
+  }
+  p.total = o;
+  return p;
+}
+
+template <typename T>
+inline T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+inline moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+// Dense or FloE expert FFNs + shared experts into the plan's buffers.
+hipError_t run_ffn(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
+                   moe_mode_t mode, const int32_t* offsets, const int32_t* perm, float* y_perm,
+                   float* y_s, float* g_s, int32_t* keep, uint32_t* flags, void* ws, const Plan& p,
+                   hipStream_t s) {
+  if (mode == MOE_MODE_FLOE)
+    return launch_floe(d, T, x, w, offsets, perm, at<float>(ws, p.u), keep, at<float>(ws, p.fa),
+                       at<float>(ws, p.part), y_perm, flags, s);
+  return launch_dense_ffn(d, T, x, w, offsets, perm, T * d.top_k, at<float>(ws, p.act), y_perm,
+                          d.n_shared > 0 ? at<float>(ws, p.act_s) : nullptr, y_s, g_s, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported shape or mode";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EHIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+moe_status_t moe_workspace_size(const moe_dims_t* dims, int32_t T, moe_mode_t mode, size_t* bytes) {
+  moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if ((st = check_mode(dims, mode)) != MOE_OK) return st;
+  if (!bytes || T < 0) return MOE_EINVAL;
+  if (T > kMaxTokens) return MOE_EUNSUPPORTED;
+  *bytes = make_plan(*dims, T, mode).total;
+  return MOE_OK;
+}
+
+moe_status_t moe_route(const moe_dims_t* dims, int32_t T, const void* x, const void* w_router,
+                       const uint64_t* resident, int64_t resident_stride, moe_mode_t mode,
+                       int32_t* topk_ids, float* topk_w, uint8_t* exact, uint32_t* flags,
+                       float* logits_opt, float* mass_opt, void* stream) {
+  moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (mode < MOE_MODE_STANDARD || mode > MOE_MODE_FLOE) return MOE_EINVAL;
+  if (T < 0) return MOE_EINVAL;
+  if (T > kMaxTokens) return MOE_EUNSUPPORTED;
+  if (!ok_ptr(x) || !ok_ptr(w_router) || !ok_ptr(topk_ids) || !ok_ptr(topk_w) || !ok_ptr(exact) ||
+      !ok_ptr(flags) || !ok_opt(logits_opt) || !ok_opt(mass_opt))
+    return MOE_EINVAL;
+  const bool needs_mask = mode == MOE_MODE_LORE || mode == MOE_MODE_STALL_FREE;
+  if (needs_mask && (!ok_ptr(resident) || (resident_stride != 0 && resident_stride != 1)))
+    return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  return hip_status(launch_route(*dims, T, x, w_router, resident, resident_stride, mode, topk_ids,
+                                 topk_w, exact, flags, logits_opt, mass_opt, (hipStream_t)stream));
+}
+
+moe_status_t moe_prefetch_mask(const moe_dims_t* dims, int32_t T, const void* x,
+                               const void* w_prefetch, const int32_t* delta, uint64_t* mask_out,
+                               uint32_t* flags, void* stream) {
+  moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_EINVAL;
+  if (T > kMaxTokens) return MOE_EUNSUPPORTED;
+  if (!ok_ptr(x) || !ok_ptr(w_prefetch) || !ok_ptr(delta) || !ok_ptr(mask_out) || !ok_ptr(flags))
+    return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  return hip_status(launch_prefetch(*dims, T, x, w_prefetch, delta, mask_out, flags,
+                                    (hipStream_t)stream));
+}
+
+moe_status_t moe_permute(int32_t T, int32_t k, int32_t E, const int32_t* topk_ids,
+                         const uint8_t* exact, int32_t* expert_offsets, int32_t* perm, int32_t* inv,
+                         void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (T < 0 || k <= 0 || E <= 0) return MOE_EINVAL;
+  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || T > kMaxTokens) return MOE_EUNSUPPORTED;
+  if (!ok_ptr(topk_ids) || !ok_ptr(exact) || !ok_ptr(expert_offsets) || !ok_ptr(perm) ||
+      !ok_ptr(inv))
+    return MOE_EINVAL;
+  return hip_status(launch_permute(T * k, E, topk_ids, exact, expert_offsets, perm, inv,
+                                   (hipStream_t)stream));
+}
+
+moe_status_t moe_expert_ffn(const moe_dims_t* dims, int32_t T, const void* x,
+                            const moe_weights_t* w, moe_mode_t mode, const int32_t* expert_offsets,
+                            const int32_t* perm, float* y_perm, float* y_shared, float* shared_gate,
+                            int32_t* floe_keep_opt, uint32_t* flags_opt, void* ws, size_t ws_bytes,
+                            void* stream) {
+  moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if ((st = check_mode(dims, mode)) != MOE_OK) return st;
+  if ((st = check_weights(dims, w, mode)) != MOE_OK) return st;
+  if (T < 0) return MOE_EINVAL;
+  if (T > kMaxTokens) return MOE_EUNSUPPORTED;
+  if (!ok_ptr(x) || !ok_ptr(expert_offsets) || !ok_ptr(perm) || !ok_ptr(y_perm) || !ok_ptr(ws))
+    return MOE_EINVAL;
+  if (dims->n_shared > 0 && (!ok_ptr(y_shared) || !ok_ptr(shared_gate))) return MOE_EINVAL;
+  if (!ok_opt(floe_keep_opt) || !ok_opt(flags_opt)) return MOE_EINVAL;
+  if (mode == MOE_MODE_FLOE && !flags_opt) return MOE_EINVAL;
+  const Plan p = make_plan(*dims, T, mode);
+  if (ws_bytes < p.total) return MOE_EWORKSPACE;
+  if (T == 0) return MOE_OK;
+  int32_t* keep = floe_keep_opt ? floe_keep_opt : at<int32_t>(ws, p.keep);
+  return hip_status(run_ffn(*dims, T, x, *w, mode, expert_offsets, perm, y_perm, y_shared,
+                            shared_gate, keep, flags_opt, ws, p, (hipStream_t)stream));
+}
+
+moe_status_t moe_lore_surrogate(const moe_dims_t* dims, int32_t T, const void* x,
+                                const int32_t* topk_ids, const uint8_t* exact, const void* lore_A,
+                                const void* lore_B, float* lore_out, void* stream) {
+  moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (dims->lore_rank == 0) return MOE_EUNSUPPORTED;
+  if (T < 0) return MOE_EINVAL;
+  if (T > kMaxTokens) return MOE_EUNSUPPORTED;
+  if (!ok_ptr(x) || !ok_ptr(topk_ids) || !ok_ptr(exact) || !ok_ptr(lore_A) || !ok_ptr(lore_B) ||
+      !ok_ptr(lore_out))
+    return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  return hip_status(launch_lore(*dims, T, x, topk_ids, exact, lore_A, lore_B, lore_out,
+                                (hipStream_t)stream));
+}
+
+moe_status_t moe_combine(const moe_dims_t* dims, int32_t T, const float* y_perm, const int32_t* inv,
+                         const float* topk_w, const uint8_t* exact, const float* y_shared,
+                         const float* shared_gate, const float* lore_out, void* out, void* stream) {
+  moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_EINVAL;
+  if (T > kMaxTokens) return MOE_EUNSUPPORTED;
+  if (!ok_ptr(y_perm) || !ok_ptr(inv) || !ok_ptr(topk_w) || !ok_ptr(exact) || !ok_ptr(out) ||
+      !ok_opt(y_shared) || !ok_opt(shared_gate) || !ok_opt(lore_out))
+    return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  return hip_status(launch_combine(*dims, T, y_perm, inv, topk_w, exact, nullptr, y_shared,
+                                   shared_gate, lore_out, nullptr, nullptr, nullptr, out,
+                                   (hipStream_t)stream));
+}
+
+moe_status_t moe_layer_forward(const moe_dims_t* dims, int32_t T, const void* x,
+                               const moe_weights_t* w, const uint64_t* resident,
+                               int64_t resident_stride, moe_mode_t mode, void* out,
+                               const moe_debug_t* dbg, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if ((st = check_mode(dims, mode)) != MOE_OK) return st;
+  if ((st = check_weights(dims, w, mode)) != MOE_OK) return st;
+  if (T < 0) return MOE_EINVAL;
+  if (T > kMaxTokens) return MOE_EUNSUPPORTED;
+  if (!ok_ptr(x) || !ok_ptr(out) || !ok_ptr(ws)) return MOE_EINVAL;
+  const bool needs_mask = mode == MOE_MODE_LORE || mode == MOE_MODE_STALL_FREE;
+  if (needs_mask && (!ok_ptr(resident) || (resident_stride != 0 && resident_stride != 1)))
+    return MOE_EINVAL;
+  if (dbg) {
+    if (!ok_opt(dbg->topk_ids) || !ok_opt(dbg->topk_w) || !ok_opt(dbg->exact) ||
+        !ok_opt(dbg->flags) || !ok_opt(dbg->logits) || !ok_opt(dbg->mass) ||
+        !ok_opt(dbg->expert_offsets) || !ok_opt(dbg->perm) || !ok_opt(dbg->floe_keep))
+      return MOE_EINVAL;
+  }
+  const Plan p = make_plan(*dims, T, mode);
+  if (ws_bytes < p.total) return MOE_EWORKSPACE;
+  if (T == 0) return MOE_OK;
+
+  const moe_dims_t& d = *dims;
+  hipStream_t s = (hipStream_t)stream;
+  const int k = d.top_k, E = d.n_experts, P = T * k;
+  int32_t* ids = at<int32_t>(ws, p.ids);
+  float* wts = at<float>(ws, p.w);
+  uint8_t* exact = at<uint8_t>(ws, p.exact);
+  uint32_t* flags = at<uint32_t>(ws, p.flags);
+  int32_t* offsets = at<int32_t>(ws, p.offsets);
+  int32_t* perm = at<int32_t>(ws, p.perm);
+  int32_t* inv = at<int32_t>(ws, p.inv);
+  float* y_perm = at<float>(ws, p.y_perm);
+  float* y_s = d.n_shared > 0 ? at<float>(ws, p.y_s) : nullptr;
+  float* g_s = d.n_shared > 0 ? at<float>(ws, p.g_s) : nullptr;
+  int32_t* keep = (mode == MOE_MODE_FLOE) ? at<int32_t>(ws, p.keep) : nullptr;
+
+  hipError_t e = launch_route(d, T, x, w->w_router, resident, resident_stride, mode, ids, wts, exact,
+                              flags, dbg ? dbg->logits : nullptr, dbg ? dbg->mass : nullptr, s);
+  if (e == hipSuccess) e = launch_permute(P, E, ids, exact, offsets, perm, inv, s);
+  if (e == hipSuccess)
+    e = run_ffn(d, T, x, *w, mode, offsets, perm, y_perm, y_s, g_s, keep, flags, ws, p, s);
+  if (e == hipSuccess)
+    e = launch_combine(d, T, y_perm, inv, wts, exact, ids, y_s, g_s, nullptr, x,
+                       mode == MOE_MODE_LORE ? w->lore_A : nullptr,
+                       mode == MOE_MODE_LORE ? w->lore_B : nullptr, out, s);
+  if (e == hipSuccess && dbg) {
+    auto cp = [&](void* dst, const void* src, size_t bytes) {
+      if (dst && e == hipSuccess) e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
+    };
+    cp(dbg->topk_ids, ids, (size_t)P * 4);
+    cp(dbg->topk_w, wts, (size_t)P * 4);
+    cp(dbg->exact, exact, (size_t)P);
+    cp(dbg->flags, flags, (size_t)T * 4);
+    cp(dbg->expert_offsets, offsets, (size_t)(E + 1) * 4);
+    cp(dbg->perm, perm, (size_t)P * 4);
+    if (keep) cp(dbg->floe_keep, keep, (size_t)P * d.floe_keep * 4);
+  }
+  return hip_status(e);
+}
+
+}  // extern "C"

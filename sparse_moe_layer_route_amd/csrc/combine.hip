@@ -1,0 +1,153 @@
+// Weighted combine with the LoRE surrogate fused in [SPICE page, "LoRE
+// low-rank surrogate"]:
+//   out[t] = g_s(t) y_s(t) + sum_j w_tj yhat_tj,
+//   yhat_tj = y_perm[inv[t*k+j]]            (exact slot)
+//           = y_s(t) + B_e (A_e x_t)        (non-resident slot).
+// One 256-thread block per token.  The rank-r projections z_j = A_e x_t of
+// the token's non-exact slots are wave dot products over H into LDS; each
+// thread then owns output columns and adds B_e[h, :] . z_j (r contiguous
+// values, 16-byte loads) for those slots.
+#include "common.h"
+
+namespace moe {
+
+constexpr int COMBINE_THREADS = 256;
+
+template <typename Tin>
+__device__ __forceinline__ void lore_project(const Tin* __restrict__ xr, const Tin* __restrict__ lore_A,
+                                             int H, int k, int r, const int* s_ids, const int* s_ex,
+                                             float (*z)[MOE_MAX_LORE_RANK]) {
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  for (int idx = wv; idx < k * r; idx += COMBINE_THREADS / MOE_WAVE) {
+    const int j = idx / r, q = idx - j * r;
+    if (s_ex[j]) continue;
+    const Tin* arow = lore_A + ((int64_t)s_ids[j] * r + q) * H;
+    float acc = 0.f;
+    for (int h = lane * 8; h < H; h += 8 * MOE_WAVE) {
+      float a8[8], x8[8];
+      elem<Tin>::load8(arow + h, a8);
+      elem<Tin>::load8(xr + h, x8);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc = fmaf(a8[c], x8[c], acc);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) z[j][q] = acc;
+  }
+}
+
+template <typename Tin>
+__device__ __forceinline__ float lore_apply(const Tin* __restrict__ brow, int r, const float* zj) {
+  float acc = 0.f;
+  for (int q = 0; q < r; q += 8) {
+    float b8[8];
+    elem<Tin>::load8(brow + q, b8);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc = fmaf(b8[c], zj[q + c], acc);
+  }
+  return acc;
+}
+
+// lore_A / lore_B non-null: LoRE computed here.  Else lore_out (may be null)
+// supplies the residuals.
+template <typename Tin>
+__global__ void __launch_bounds__(COMBINE_THREADS)
+combine_kernel(int H, int k, int r, const float* __restrict__ y_perm, const int32_t* __restrict__ inv,
+               const float* __restrict__ topk_w, const uint8_t* __restrict__ exact,
+               const int32_t* __restrict__ ids, const float* __restrict__ y_s,
+               const float* __restrict__ g_s, const float* __restrict__ lore_out,
+               const Tin* __restrict__ x, const Tin* __restrict__ lore_A,
+               const Tin* __restrict__ lore_B, Tin* __restrict__ out) {
+  __shared__ float z[MOE_MAX_TOPK][MOE_MAX_LORE_RANK];
+  __shared__ int s_ids[MOE_MAX_TOPK], s_ex[MOE_MAX_TOPK], s_row[MOE_MAX_TOPK];
+  __shared__ float s_w[MOE_MAX_TOPK];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (tid < k) {
+    const int64_t o = (int64_t)t * k + tid;
+    s_ids[tid] = ids ? ids[o] : 0;
+    s_ex[tid] = exact ? exact[o] : 1;
+    s_row[tid] = inv[o];
+    s_w[tid] = topk_w[o];
+  }
+  __syncthreads();
+  const bool fused = lore_A != nullptr;
+  if (fused) {
+    lore_project<Tin>(x + (int64_t)t * H, lore_A, H, k, r, s_ids, s_ex, z);
+    __syncthreads();
+  }
+  const float gs = g_s ? g_s[t] : 1.f;
+  for (int h = tid; h < H; h += COMBINE_THREADS) {
+    const float ys = y_s ? y_s[(int64_t)t * H + h] : 0.f;
+    float acc = gs * ys;
+    for (int j = 0; j < k; ++j) {
+      float yj;
+      if (s_ex[j] && s_row[j] >= 0) {
+        yj = y_perm[(int64_t)s_row[j] * H + h];
+      } else {
+        float lr = 0.f;
+        if (fused)
+          lr = lore_apply<Tin>(lore_B + ((int64_t)s_ids[j] * H + h) * r, r, z[j]);
+        else if (lore_out)
+          lr = lore_out[((int64_t)t * k + j) * H + h];
+        yj = ys + lr;
+      }
+      acc = fmaf(s_w[j], yj, acc);
+    }
+    elem<Tin>::store(out, (int64_t)t * H + h, acc);
+  }
+}
+
+// Standalone LoRE residuals: lore_out[t][j] = B_e (A_e x_t) for non-exact
+// slots, 0 for exact ones.
+template <typename Tin>
+__global__ void __launch_bounds__(COMBINE_THREADS)
+lore_kernel(int H, int k, int r, const Tin* __restrict__ x, const int32_t* __restrict__ ids,
+            const uint8_t* __restrict__ exact, const Tin* __restrict__ lore_A,
+            const Tin* __restrict__ lore_B, float* __restrict__ lore_out) {
+  __shared__ float z[MOE_MAX_TOPK][MOE_MAX_LORE_RANK];
+  __shared__ int s_ids[MOE_MAX_TOPK], s_ex[MOE_MAX_TOPK];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (tid < k) {
+    s_ids[tid] = ids[(int64_t)t * k + tid];
+    s_ex[tid] = exact[(int64_t)t * k + tid];
+  }
+  __syncthreads();
+  lore_project<Tin>(x + (int64_t)t * H, lore_A, H, k, r, s_ids, s_ex, z);
+  __syncthreads();
+  for (int j = 0; j < k; ++j) {
+    float* o = lore_out + ((int64_t)t * k + j) * H;
+    for (int h = tid; h < H; h += COMBINE_THREADS)
+      o[h] = s_ex[j] ? 0.f : lore_apply<Tin>(lore_B + ((int64_t)s_ids[j] * H + h) * r, r, z[j]);
+  }
+}
+
+hipError_t launch_combine(const moe_dims_t& d, int T, const float* y_perm, const int32_t* inv,
+                          const float* topk_w, const uint8_t* exact, const int32_t* ids,
+                          const float* y_s, const float* g_s, const float* lore_out, const void* x,
+                          const void* lore_A, const void* lore_B, void* out, hipStream_t s) {
+  if (d.dtype == MOE_BF16)
+    combine_kernel<bf16><<<T, COMBINE_THREADS, 0, s>>>(
+        d.hidden, d.top_k, d.lore_rank, y_perm, inv, topk_w, exact, ids, y_s, g_s, lore_out,
+        (const bf16*)x, (const bf16*)lore_A, (const bf16*)lore_B, (bf16*)out);
+  else
+    combine_kernel<float><<<T, COMBINE_THREADS, 0, s>>>(
+        d.hidden, d.top_k, d.lore_rank, y_perm, inv, topk_w, exact, ids, y_s, g_s, lore_out,
+        (const float*)x, (const float*)lore_A, (const float*)lore_B, (float*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_lore(const moe_dims_t& d, int T, const void* x, const int32_t* ids,
+                       const uint8_t* exact, const void* lore_A, const void* lore_B,
+                       float* lore_out, hipStream_t s) {
+  if (d.dtype == MOE_BF16)
+    lore_kernel<bf16><<<T, COMBINE_THREADS, 0, s>>>(d.hidden, d.top_k, d.lore_rank, (const bf16*)x,
+                                                    ids, exact, (const bf16*)lore_A,
+                                                    (const bf16*)lore_B, lore_out);
+  else
+    lore_kernel<float><<<T, COMBINE_THREADS, 0, s>>>(d.hidden, d.top_k, d.lore_rank,
+                                                     (const float*)x, ids, exact,
+                                                     (const float*)lore_A, (const float*)lore_B,
+                                                     lore_out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

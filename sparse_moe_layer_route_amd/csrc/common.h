@@ -1,0 +1,95 @@
+// Device helpers shared by the gfx950 kernels: bf16 packing, 16-byte vector
+// loads, wave64 reductions and the workspace plan.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe_route.h"
+
+#define MOE_WAVE 64
+
+namespace moe {
+
+// ---------------------------------------------------------------- bf16 ----
+struct bf16 {
+  uint16_t b;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float half_bits_to_f(uint16_t b) {
+  _Float16 h = __builtin_bit_cast(_Float16, b);
+  return (float)h;
+}
+
+// Element type traits: F32 = float storage, BF16 = bf16 storage.
+template <typename T> struct elem;
+template <> struct elem<float> {
+  static constexpr int bytes = 4;
+  __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
+  __device__ __forceinline__ static void store(float* p, int64_t i, float v) { p[i] = v; }
+  // 8 consecutive elements starting at p (p 16-byte aligned)
+  __device__ __forceinline__ static void load8(const float* p, float (&v)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+template <> struct elem<bf16> {
+  static constexpr int bytes = 2;
+  __device__ __forceinline__ static float load(const bf16* p, int64_t i) { return bf16_to_f(p[i].b); }
+  __device__ __forceinline__ static void store(bf16* p, int64_t i, float v) { p[i].b = f_to_bf16(v); }
+  __device__ __forceinline__ static void load8(const bf16* p, float (&v)[8]) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
+    v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
+  }
+};
+
+// --------------------------------------------------------- wave64 ops -----
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, MOE_WAVE));
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint64_t w = __shfl_xor(v, o, MOE_WAVE);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
+  return v;
+}
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (MOE_WAVE - 1); }
+
+// Monotone map of a float to uint32: a < b  <=>  key(a) < key(b) (no NaN).
+__device__ __forceinline__ uint32_t float_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+}  // namespace moe

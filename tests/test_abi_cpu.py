@@ -1,0 +1,127 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point the header declares, and rejects bad arguments on the host before any
+HIP call (status codes from include/moe_route.h)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_moe_layer_route_amd as M
+from sparse_moe_layer_route_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "moe_route.h")
+L = B._lib
+FAKE = 0x10000          # aligned, never dereferenced: every call below fails validation first
+
+
+def declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status_t|int|const char\*)\s+(moe_\w+)\s*\(", src, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(M.EXPORTED) == names
+
+
+def test_version_and_status_strings():
+    assert M.moe_abi_version() == 1
+    for s in range(5):
+        assert L.moe_status_string(s)
+    assert L.moe_status_string(99) == b"unknown status"
+
+
+def dims(**kw):
+    d = dict(hidden=256, n_experts=8, top_k=2, inter=512, n_shared=1, shared_inter=512,
+             lore_rank=8, renormalize=False, shared_gate=False, floe_keep=0, dtype="f32")
+    d.update(kw)
+    return M.Dims(**d).c()
+
+
+def ws_size(d, T, mode):
+    n = ctypes.c_size_t(0)
+    st = L.moe_workspace_size(ctypes.byref(d), T, mode, ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_experts=65), B.MOE_EUNSUPPORTED), (dict(top_k=9), B.MOE_EUNSUPPORTED),
+    (dict(top_k=9, n_experts=8), B.MOE_EUNSUPPORTED), (dict(hidden=250), B.MOE_EUNSUPPORTED),
+    (dict(inter=500), B.MOE_EUNSUPPORTED), (dict(lore_rank=12), B.MOE_EUNSUPPORTED),
+    (dict(lore_rank=128), B.MOE_EUNSUPPORTED), (dict(hidden=0), B.MOE_EINVAL),
+    (dict(top_k=0), B.MOE_EINVAL), (dict(shared_inter=100), B.MOE_EUNSUPPORTED),
+    (dict(tie_margin=-1.0), B.MOE_EINVAL), ({}, B.MOE_OK),
+])
+def test_dims_validation(kw, status):
+    assert ws_size(dims(**kw), 16, 0)[0] == status
+
+
+def test_mode_validation():
+    assert ws_size(dims(), 16, 3)[0] == B.MOE_EUNSUPPORTED            # FLOE needs INT2 up
+    assert ws_size(dims(lore_rank=0), 16, 1)[0] == B.MOE_EUNSUPPORTED  # LORE needs factors
+    fl = dims(up_format="int2_g64", floe_keep=600)
+    assert ws_size(fl, 1, 3)[0] == B.MOE_EINVAL                        # keep > I
+    assert ws_size(dims(up_format="int2_g64", floe_keep=51), 1, 3)[0] == B.MOE_OK
+    assert ws_size(dims(up_format="int2_g64", floe_keep=51), 1, 0)[0] == B.MOE_EUNSUPPORTED
+    assert ws_size(dims(), 16, 7)[0] == B.MOE_EINVAL
+    assert ws_size(dims(), -1, 0)[0] == B.MOE_EINVAL
+
+
+def test_workspace_grows_with_tokens():
+    a = ws_size(dims(), 1, 0)[1]; b = ws_size(dims(), 64, 0)[1]
+    assert 0 < a < b and a % 256 == 0
+
+
+def _weights(**over):
+    w = {n: FAKE for n in B._WEIGHT_FIELDS}
+    w.update(over)
+    return B.MoeWeights(*[w[n] for n in B._WEIGHT_FIELDS])
+
+
+def fwd(d, T, w, resident, stride, mode, out, ws, ws_bytes, x=FAKE):
+    return L.moe_layer_forward(ctypes.byref(d), T, x, ctypes.byref(w), resident, stride, mode, out,
+                               None, ws, ws_bytes, None)
+
+
+def test_layer_forward_host_checks():
+    d = dims()
+    need = ws_size(d, 16, 1)[1]
+    w = _weights()
+    assert fwd(d, 16, w, FAKE, 0, 1, FAKE, FAKE, need - 1) == B.MOE_EWORKSPACE
+    assert fwd(d, 16, w, None, 0, 1, FAKE, FAKE, need) == B.MOE_EINVAL        # LORE needs a mask
+    assert fwd(d, 16, w, FAKE, 2, 1, FAKE, FAKE, need) == B.MOE_EINVAL        # stride 0 or 1
+    assert fwd(d, 16, _weights(lore_A=None), FAKE, 0, 1, FAKE, FAKE, need) == B.MOE_EINVAL
+    assert fwd(d, 16, _weights(w_up=None), FAKE, 0, 0, FAKE, FAKE, need) == B.MOE_EINVAL
+    assert fwd(d, 16, w, FAKE, 0, 1, FAKE + 2, FAKE, need) == B.MOE_EINVAL    # misaligned out
+    assert fwd(d, 16, w, FAKE, 0, 1, FAKE, FAKE, need, x=None) == B.MOE_EINVAL
+    assert fwd(d, 16, _weights(ws_gate=None), FAKE, 0, 0, FAKE, FAKE, need) == B.MOE_EINVAL
+    dg = dims(shared_gate=True)
+    assert fwd(dg, 16, _weights(w_shared_gate=None), FAKE, 0, 0, FAKE, FAKE, need) == B.MOE_EINVAL
+    # T = 0 with valid arguments enqueues nothing and succeeds (no GPU touched)
+    assert fwd(d, 0, w, FAKE, 0, 1, FAKE, FAKE, need) == B.MOE_OK
+
+
+def test_entry_point_null_checks():
+    d = dims()
+    P = ctypes.c_void_p
+    assert L.moe_route(ctypes.byref(d), 4, None, FAKE, None, 0, 0, FAKE, FAKE, FAKE, FAKE, None, None,
+                       None) == B.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(d), 4, FAKE, FAKE, None, 0, 2, FAKE, FAKE, FAKE, FAKE, None, None,
+                       None) == B.MOE_EINVAL                                   # stall-free needs masks
+    assert L.moe_route(ctypes.byref(d), 0, FAKE, FAKE, None, 0, 0, FAKE, FAKE, FAKE, FAKE, None, None,
+                       None) == B.MOE_OK
+    assert L.moe_permute(4, 9, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.MOE_EUNSUPPORTED
+    assert L.moe_permute(4, 2, 65, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.MOE_EUNSUPPORTED
+    assert L.moe_permute(4, 2, 8, None, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.MOE_EINVAL
+    assert L.moe_prefetch_mask(ctypes.byref(d), 4, FAKE, FAKE, None, FAKE, FAKE, None) == B.MOE_EINVAL
+    assert L.moe_lore_surrogate(ctypes.byref(dims(lore_rank=0)), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                None) == B.MOE_EUNSUPPORTED
+    assert L.moe_combine(ctypes.byref(d), 4, FAKE, FAKE, FAKE, FAKE, None, None, None, None,
+                         None) == B.MOE_EINVAL
+    w = _weights()
+    assert L.moe_expert_ffn(ctypes.byref(d), 4, FAKE, ctypes.byref(w), 0, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            None, None, FAKE, 0, None) == B.MOE_EWORKSPACE

@@ -210,11 +210,13 @@ class Layer:
     rows of one T_max-row draw, so smaller batches are row prefixes.
     """
 
-    def __init__(self, cfg: MoEConfig, seed: Optional[int] = None, threads: Optional[int] = None):
+    def __init__(self, cfg: MoEConfig, seed: Optional[int] = None, threads: Optional[int] = None,
+                 cache_bytes: int = 8 << 30):
         self.cfg = cfg
         self.seed = cfg.seed if seed is None else seed
         self.threads = threads or min(16, len(os.sched_getaffinity(0)))
         self._cache: Dict[Tuple[str, int], object] = {}
+        self._cache_left = cache_bytes
 
     # ---- scalars / small tensors -------------------------------------------------
     def _to_storage(self, a: np.ndarray) -> np.ndarray:
@@ -275,13 +277,19 @@ class Layer:
         if name in ("up_q", "up_scale", "up_zero"):
             w = _normal(_rng(self.seed, "w_up", e), self._shape("w_up"), c.weight_std)
             q, s, z = quantize_int2_g64(w)
-            self._cache[("up_q", e)], self._cache[("up_scale", e)], self._cache[("up_zero", e)] = q, s, z
-            return self._cache[key]
+            out = {"up_q": q, "up_scale": s, "up_zero": z}
+            nb = q.nbytes + s.nbytes + z.nbytes
+            if nb <= self._cache_left:
+                self._cache_left -= nb
+                for n, v in out.items():
+                    self._cache[(n, e)] = v
+            return out[name]
         std = c.lore_std if name.startswith("lore_") else c.weight_std
         a = self._to_storage(_normal(_rng(self.seed, name, e), self._shape(name), std))
-        # Large layers are drawn once per call site; only small ones are cached.
-        if a.nbytes <= (1 << 22):
+        # Kept until the cache budget is spent; later draws are regenerated.
+        if a.nbytes <= self._cache_left:
             self._cache[key] = a
+            self._cache_left -= a.nbytes
         return a
 
     def w_up_f32(self, e: int) -> np.ndarray:
