@@ -1,0 +1,306 @@
+"""MoE-layer forward throughput on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload dsv2_lite] [--tokens 64]
+                    [--mode lore] [--quick]
+
+One step = one moe_layer_forward over one batch of synthetic tokens (router,
+softmax/top-k, residency split, permutation, expert + shared FFNs, LoRE
+surrogate fused into the combine), eager launches on torch's current stream,
+inputs and weights resident in HBM.  The headline workload is the
+DeepSeek-V2-Lite-shaped decode layer (H=2048, 64 experts top-6, I=1408, two
+shared experts, 50% of experts resident, LoRE rank 16) at 64 tokens.  Steps
+cycle through enough copies of the layer's weights that the 256 MB Infinity
+Cache cannot serve one step's weights to the next.
+
+Prints ONE JSON line.  `roofline` is for the dominant kernel (the expert
+gate/up projection): algorithmic bytes (or flops) per launch divided by its
+average duration, timed live with HIP events recorded around that kernel on
+the launch stream.  `cpu_baseline` times the CPU oracle on a bounded sample of
+the same workload.  `also` lists the other token counts and workloads.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "MoE-layer tokens/s at 1 GPU; % HBM BW peak (decode) / % MFMA peak (prefill)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="dsv2_lite")
+    ap.add_argument("--tokens", type=int, default=64)
+    ap.add_argument("--mode", default="lore")
+    ap.add_argument("--quick", action="store_true", help="headline only (no other workloads)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t pairs from the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(ev)) == 0
+        return ev.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(ev)
+
+
+# ------------------------------------------------------ algorithmic bytes --
+def step_traffic(cfg, T, mode, ids, exact, keep_count=None):
+    """Algorithmic bytes and flops of one layer forward, from the routing the
+    GPU actually took: each touched weight byte once, activations once."""
+    H, I, E, k = cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k
+    eb = 4 if cfg.dtype == "f32" else 2
+    exact_experts = {int(e) for e, x in zip(ids.reshape(-1), exact.reshape(-1)) if x}
+    miss_experts = {int(e) for e, x in zip(ids.reshape(-1), exact.reshape(-1)) if not x}
+    P = int(exact.sum())
+    b = H * E * eb + 2 * T * H * eb                    # router, x in, out
+    f = 2 * T * H * E
+    up = {}
+    if mode == "floe":
+        nk = cfg.floe_keep
+        per_pair_rows = nk
+        for e in exact_experts:
+            b += I * H // 4 + 2 * I * (H // 64) * 2     # INT2 codes + fp16 scale/zero
+        b += P * 2 * per_pair_rows * H * eb            # kept gate and down rows
+        f += P * (2 * I * H + 2 * 2 * nk * H)
+        up = dict(bytes=len(exact_experts) * (I * H // 4 + 2 * I * (H // 64) * 2) + P * H * eb,
+                  flops=P * 2 * I * H)
+    else:
+        b += len(exact_experts) * 3 * I * H * eb
+        f += P * 2 * 3 * I * H
+        sh = cfg.n_shared * cfg.shared_inter
+        b += 3 * sh * H * eb + (H * eb if cfg.shared_gate else 0)
+        f += T * 2 * 3 * sh * H
+        b += len(miss_experts) * 2 * cfg.lore_rank * H * eb
+        f += int((1 - exact).sum()) * 2 * 2 * cfg.lore_rank * H
+        act_b = 4 if (eb == 4 or T <= 64) else 2       # bf16 hi+lo up to 64 tokens, else hi
+        n_miss = int((1 - exact).sum())
+        r = cfg.lore_rank
+        up = dict(bytes=(len(exact_experts) * 2 * I * H + 2 * sh * H + len(miss_experts) * r * H) * eb
+                  + T * H * eb + (P * I + T * sh + n_miss * r) * act_b,
+                  flops=P * 2 * 2 * I * H + T * 2 * 2 * sh * H + n_miss * 2 * r * H)
+    return dict(bytes=b, flops=f, up=up, distinct_experts=len(exact_experts),
+                lore_experts=len(miss_experts), pairs=P)
+
+
+# ------------------------------------------------------------- measurement --
+def measure(name, T, mode, steps, warmup, ev=None, want_roofline=False):
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from workloads.device import dims_dict, mask_tensor, tensor, upload
+    import sparse_moe_layer_route_amd as M
+
+    layer = W.make_layer(name)
+    cfg = layer.cfg
+    dims = M.Dims(**dims_dict(cfg)).c()
+    w0 = upload(layer, "cuda")
+    x = tensor(layer.x(T), cfg.dtype, "cuda")
+    stride = 0
+    res = None
+    if mode == "lore":
+        res = mask_tensor([layer.resident()], "cuda")
+    elif mode == "stall_free":
+        d = torch.from_numpy(layer.delta(T).astype(np.int32)).cuda()
+        res = torch.empty(T, dtype=torch.int64, device="cuda")
+        fl = torch.empty(T, dtype=torch.int32, device="cuda")
+        M.moe_prefetch_mask(dims, T, x, w0["w_prefetch"], d, res, fl)
+        stride = 1
+    ws = torch.empty(M.moe_workspace_size(dims, T, mode), dtype=torch.uint8, device="cuda")
+    odt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    out = torch.empty(T, cfg.hidden, dtype=odt, device="cuda")
+    k = cfg.top_k
+    ids = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    exact = torch.empty(T * k, dtype=torch.uint8, device="cuda")
+    M.moe_layer_forward(dims, T, x, w0, res, stride, mode, out, ws,
+                        debug={"topk_ids": ids, "exact": exact})
+    torch.cuda.synchronize()
+    tr = step_traffic(cfg, T, mode, ids.cpu().numpy(), exact.cpu().numpy())
+    # weight copies so consecutive steps stream different bytes
+    n_copies = max(1, min(16, math.ceil(1.0e9 / max(tr["bytes"], 1))))
+    copies = [w0] + [{n: t.clone() for n, t in w0.items()} for _ in range(n_copies - 1)]
+    wstructs = [M.weights_struct(c) for c in copies]
+    dom = "floe_up" if mode == "floe" else "expert_gate_up"
+    evs = []
+    dbgs = []
+    if ev is not None:
+        for _ in range(steps):
+            a, b = ev.create(), ev.create()
+            evs.append((a, b))
+            dbg = M.MoeDebug()
+            dbg.prof_start, dbg.prof_stop, dbg.prof_kernel = a, b, M.binding.KERNELS[dom]
+            dbgs.append(dbg)
+
+    def step(i, dbg=None):
+        M.moe_layer_forward(dims, T, x, wstructs[i % n_copies], res, stride, mode, out, ws,
+                            debug=dbg)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(steps):
+        step(i, dbgs[i] if dbgs else None)
+    t_stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t_start.elapsed_time(t_stop) / steps
+    r = dict(workload=name, tokens=T, mode=mode, ms_per_step=ms, tokens_per_s=T / (ms * 1e-3),
+             wall_ms_per_step=wall * 1e3 / steps, weight_copies=n_copies,
+             step_bytes=tr["bytes"], step_flops=tr["flops"],
+             step_gbs=tr["bytes"] / (ms * 1e-3) / 1e9,
+             distinct_experts=tr["distinct_experts"], lore_experts=tr["lore_experts"], pairs=tr["pairs"])
+    r["step_hbm_frac"] = r["step_gbs"] / HBM_PEAK_GBS
+    r["step_mfma_frac"] = tr["flops"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS
+    if evs:
+        kms = [ev.elapsed_ms(a, b) for a, b in evs]
+        avg_us = 1e3 * sum(kms) / len(kms)
+        up = tr["up"]
+        prefill = T >= 1024
+        if prefill:
+            achieved = up["flops"] / (avg_us * 1e-6) / 1e12
+            roof = dict(bound="mfma", achieved=achieved, peak=MFMA_BF16_PEAK_TFS, unit="TFLOP/s",
+                        frac=achieved / MFMA_BF16_PEAK_TFS)
+        else:
+            achieved = up["bytes"] / (avg_us * 1e-6) / 1e9
+            roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=achieved / HBM_PEAK_GBS)
+        roof.update(traffic=None, kernel=dom, avg_us=avg_us, bytes_per_launch=up["bytes"],
+                    flops_per_launch=up["flops"])
+        r["roofline"] = roof
+        for a, b in evs:
+            ev.destroy(a)
+            ev.destroy(b)
+    del copies, wstructs, w0
+    torch.cuda.empty_cache()
+    return r
+
+
+def cpu_baseline(name, T, mode, budget_s=12.0):
+    """The CPU oracle as it stands on a bounded sample: the first S tokens of
+    the same layer, S doubled until one call takes ~budget_s (or S = T)."""
+    import numpy as np
+
+    import oracle as O
+    import workloads as W
+    from workloads.device import dims_dict
+
+    layer = W.make_layer(name)
+    cfg = layer.cfg
+    d = dims_dict(cfg)
+    res = layer.resident() if mode == "lore" else None
+    if mode == "stall_free":
+        masks, _, _ = O.prefetch_masks(O.decode(layer.x(T), cfg.dtype),
+                                       O.decode(layer.w_prefetch(), cfg.dtype), layer.delta(T), cfg.top_k)
+        res = masks
+    S, dt = 1, 0.0
+    while True:
+        sub_res = res[:S] if isinstance(res, list) else res
+        t0 = time.perf_counter()
+        O.layer_forward(layer.x(T)[:S], layer, d, mode, resident=sub_res)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 2 or S >= T:
+            break
+        S = min(T, S * 2)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    return dict(value=S / dt, unit="tokens/s", cores=int(cores), kind="oracle",
+                sample=f"first {S} of the {T} tokens of the same {name} layer in mode {mode}, "
+                       f"one fp64 NumPy oracle call ({dt:.1f} s)")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ev = HipEvents()
+    head = measure(args.workload, args.tokens, args.mode, args.steps, args.warmup, ev=ev)
+    also = []
+    if not args.quick:
+        plan = [("dsv2_lite", 1, "standard"), ("dsv2_lite", 1, "lore"),
+                ("dsv2_lite", 8, "standard"), ("dsv2_lite", 8, "lore"),
+                ("dsv2_lite", 64, "standard"), ("dsv2_lite", 64, "lore"),
+                ("qwen2_57b", 1, "standard"), ("qwen2_57b", 1, "lore"),
+                ("qwen2_57b", 32, "standard"), ("qwen2_57b", 32, "lore"),
+                ("qwen2_57b", 256, "standard"), ("qwen2_57b", 256, "lore"),
+                ("mixtral_floe", 1, "floe"),
+                ("granite_prefill", 4096, "standard"), ("granite_prefill", 4096, "stall_free"),
+                ("tiny", 16, "standard"), ("tiny", 16, "lore")]
+        for name, T, mode in plan:
+            if (name, T, mode) == (args.workload, args.tokens, args.mode):
+                continue
+            steps = max(10, min(args.steps, 50)) if T >= 256 else args.steps
+            r = measure(name, T, mode, steps, min(args.warmup, 5), ev=ev)
+            also.append(r)
+            print(f"# {name} T={T} {mode}: {r['ms_per_step']*1e3:.1f} us/step "
+                  f"(wall {r['wall_ms_per_step']*1e3:.1f} us) "
+                  f"{r['tokens_per_s']:.0f} tok/s, {r['step_gbs']:.0f} GB/s"
+                  + (f", {r['roofline']['kernel']} {r['roofline']['frac']*100:.1f}% of {r['roofline']['bound']}"
+                     if 'roofline' in r else ""), file=sys.stderr, flush=True)
+    cpu = None if args.no_cpu else cpu_baseline(args.workload, args.tokens, args.mode)
+    line = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) hidden states, random 50% resident mask)",
+        "config": {"workload": f"{args.workload} MoE layer decode, T={args.tokens}, mode={args.mode}",
+                   "tokens": args.tokens, "mode": args.mode, "weight_copies": head["weight_copies"],
+                   "step_bytes": head["step_bytes"], "step_gbs": head["step_gbs"],
+                   "step_hbm_frac": head["step_hbm_frac"]},
+        "roofline": head.get("roofline"),
+        "cpu_baseline": cpu,
+        "also": also,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

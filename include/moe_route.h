@@ -88,7 +88,7 @@ typedef struct {
 
 /* Layer weights (host struct of device pointers; unused entries may be NULL). */
 typedef struct {
-  const void* w_router;       /* [H][E] dtype                                          */
+  const void* w_router;       /* [E][H] dtype: row e holds expert e's logit weights    */
   const void* w_gate;         /* [E][I][H] dtype: channel i's H inputs contiguous      */
   const void* w_up;           /* [E][I][H] dtype (MOE_UP_DENSE)                        */
   const void* w_down;         /* MOE_UP_DENSE: [E][H][I]; MOE_UP_INT2_G64: [E][I][H]   */
@@ -103,8 +103,25 @@ typedef struct {
   const void* lore_B;         /* [E][H][r] dtype                                       */
 } moe_weights_t;
 
+/* Kernels of moe_layer_forward that the debug hook can bracket with events. */
+typedef enum {
+  MOE_KERNEL_NONE = 0,
+  MOE_KERNEL_ROUTE = 1,
+  MOE_KERNEL_PERMUTE = 2,
+  MOE_KERNEL_EXPERT_GATE_UP = 3, /* routed + shared gate/up projections (+ SiLU product) */
+  MOE_KERNEL_EXPERT_DOWN = 4,    /* routed + shared down projections                     */
+  MOE_KERNEL_FLOE_UP = 5,        /* INT2 up projection                                   */
+  MOE_KERNEL_FLOE_SELECT = 6,    /* top-|u| channel selection                            */
+  MOE_KERNEL_FLOE_GATE = 7,      /* gate on kept channels                                */
+  MOE_KERNEL_FLOE_DOWN = 8,      /* down on kept channels                                */
+  MOE_KERNEL_COMBINE = 9         /* weighted combine (+ fused LoRE)                      */
+} moe_kernel_t;
+
 /* Optional copies of intermediate results from moe_layer_forward (host
- * struct of device pointers; each entry may be NULL). */
+ * struct of device pointers; each entry may be NULL).  prof_start/prof_stop
+ * are hipEvent_t handles owned by the caller: when prof_kernel names a
+ * kernel of this call, they are recorded on `stream` immediately before and
+ * after that kernel's launch (so hipEventElapsedTime gives its duration). */
 typedef struct {
   int32_t* topk_ids;     /* [T][k] final expert per slot, ordered by (-logit, id)  */
   float* topk_w;         /* [T][k] combine weight per slot                          */
@@ -115,6 +132,9 @@ typedef struct {
   int32_t* expert_offsets; /* [E+1]                                                 */
   int32_t* perm;         /* [T*k] (first offsets[E] entries meaningful)             */
   int32_t* floe_keep;    /* [T][k][floe_keep] kept channels, ascending (FLOE)       */
+  void* prof_start;      /* hipEvent_t or NULL                                      */
+  void* prof_stop;       /* hipEvent_t or NULL                                      */
+  int32_t prof_kernel;   /* moe_kernel_t                                            */
 } moe_debug_t;
 
 int moe_abi_version(void);
@@ -127,7 +147,7 @@ moe_status_t moe_workspace_size(const moe_dims_t* dims, int32_t T, moe_mode_t mo
 
 /* Router: logits l = x W_r, softmax p, top-k by (-l, id) [APEX page, Sec. 1;
  * SPICE page, "MoE inference I/O bottleneck"].
- *   x [T][H] dtype, w_router [H][E] dtype.
+ *   x [T][H] dtype, w_router [E][H] dtype.
  *   resident: uint64 expert bit masks; resident_stride 0 = one mask for all
  *     tokens, 1 = one mask per token.  LORE: exact[t][j] = bit of expert.
  *     STALL_FREE: the token's prefetched set; the final set is the routed set
@@ -144,7 +164,7 @@ moe_status_t moe_route(const moe_dims_t* dims, int32_t T, const void* x, const v
                        float* logits_opt, float* mass_opt, void* stream);
 
 /* APEX prefetch set: mask_out[t] = bit mask of the top-(k + delta[t]) experts
- * of x W_p (a linear prefetch router; softmax keeps the order) [APEX page,
+ * of x W_p^T, W_p [E][H] (a linear prefetch router; softmax keeps the order) [APEX page,
  * Sec. 4.1 and Sec. 4.2].  delta [T] int32 in 0..E-k.  flags [T] is
  * overwritten: bit 2 where the list's last member and the next expert differ
  * by less than dims.tie_margin in logits, else 0. */

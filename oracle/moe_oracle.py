@@ -43,6 +43,7 @@ notes):
   2*(h%4) of byte h/4 and fp16 s, z per group of 64 consecutive inputs.
 * Dense expert down weights are stored [H][I] (output row h holds the I inputs);
   FloE down weights are stored [I][H] (one channel's H-vector contiguous).
+  Router and prefetch-router weights are stored [E][H].
 
 Flag bits per token: 1 route near-tie, 2 prefetch near-tie, 4 substitution
 near-tie, 8 FloE mask near-tie.
@@ -97,9 +98,10 @@ def sigmoid(z):
 
 # ------------------------------------------------------------------ routing --
 def router_logits(x: np.ndarray, w_router: np.ndarray) -> np.ndarray:
-    """l[t, e] = sum_h x[t, h] W_r[h, e]: the router is a linear head over the
-    experts [APEX Sec. 1; SPICE "MoE inference I/O bottleneck"]."""
-    return x @ w_router
+    """l[t, e] = sum_h x[t, h] W_r[e, h]: the router is a linear head over the
+    experts [APEX Sec. 1; SPICE "MoE inference I/O bottleneck"].  W_r is stored
+    [E][H], one row of weights per expert."""
+    return x @ w_router.T
 
 
 def softmax(l: np.ndarray) -> np.ndarray:

@@ -51,8 +51,14 @@ _DEBUG_FIELDS = ["topk_ids", "topk_w", "exact", "flags", "logits", "mass", "expe
                  "perm", "floe_keep"]
 
 
+KERNELS = {"none": 0, "route": 1, "permute": 2, "expert_gate_up": 3, "expert_down": 4,
+           "floe_up": 5, "floe_select": 6, "floe_gate": 7, "floe_down": 8, "combine": 9}
+
+
 class MoeDebug(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in _DEBUG_FIELDS]
+    _fields_ = [(n, ctypes.c_void_p) for n in _DEBUG_FIELDS] + [
+        ("prof_start", ctypes.c_void_p), ("prof_stop", ctypes.c_void_p),
+        ("prof_kernel", ctypes.c_int32)]
 
 
 def _load():
@@ -206,8 +212,13 @@ def moe_layer_forward(dims, T, x, weights, resident, resident_stride, mode, out,
                       stream=None):
     ws_struct = weights if isinstance(weights, MoeWeights) else weights_struct(weights)
     dbg = None
-    if debug is not None:
-        dbg = ctypes.byref(MoeDebug(*[_ptr(debug.get(n)) for n in _DEBUG_FIELDS]))
+    if isinstance(debug, MoeDebug):
+        dbg = ctypes.byref(debug)
+    elif debug is not None:
+        prof = debug.get("prof")        # (start_event, stop_event, kernel name): raw hipEvent_t
+        dbg = ctypes.byref(MoeDebug(*[_ptr(debug.get(n)) for n in _DEBUG_FIELDS],
+                                    prof[0] if prof else None, prof[1] if prof else None,
+                                    KERNELS[prof[2]] if prof else 0))
     _check(_lib.moe_layer_forward(ctypes.byref(_dims(dims)), T, _ptr(x), ctypes.byref(ws_struct),
                                   _ptr(resident), resident_stride, _mode(mode), _ptr(out), dbg,
                                   _ptr(ws), ws.numel(), _stream(stream)), "moe_layer_forward")

@@ -9,23 +9,33 @@ namespace moe {
 hipError_t launch_route(const moe_dims_t& d, int T, const void* x, const void* w_router,
                         const uint64_t* resident, int64_t res_stride, int mode, int32_t* ids,
                         float* w, uint8_t* exact, uint32_t* flags, float* logits, float* mass,
-                        hipStream_t s);
+                        const void* w_sg, float* g_s, hipStream_t s);
 hipError_t launch_prefetch(const moe_dims_t& d, int T, const void* x, const void* w_p,
                            const int32_t* delta, uint64_t* mask_out, uint32_t* flags,
                            hipStream_t s);
 hipError_t launch_permute(int n_pairs, int E, const int32_t* ids, const uint8_t* exact,
-                          int32_t* offsets, int32_t* perm, int32_t* inv, hipStream_t s);
+                          int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* row_of,
+                          int32_t* miss_offsets, hipStream_t s);
 hipError_t launch_dense_ffn(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
                             const int32_t* offsets, const int32_t* perm, int n_pairs_max,
-                            float* act, float* y_perm, float* act_s, float* y_s, float* g_s,
+                            float* act, float* y_perm, float* act_s, float* y_s, const Prof& pf,
                             hipStream_t s);
+hipError_t launch_shared_gate(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
+                              float* g_s, hipStream_t s);
+hipError_t launch_ffn_mfma(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
+                           const int32_t* offsets, const int32_t* moffsets, const int32_t* perm,
+                           const FfnBuffers& b, int lore, hipStream_t s, int which);
 hipError_t launch_floe(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
                        const int32_t* offsets, const int32_t* perm, float* u, int32_t* keep,
-                       float* a, float* part, float* y_perm, uint32_t* flags, hipStream_t s);
+                       float* a, float* part, float* y_perm, uint32_t* flags, const Prof& pf,
+                       hipStream_t s);
 hipError_t launch_combine(const moe_dims_t& d, int T, const float* y_perm, const int32_t* inv,
                           const float* topk_w, const uint8_t* exact, const int32_t* ids,
                           const float* y_s, const float* g_s, const float* lore_out, const void* x,
                           const void* lore_A, const void* lore_B, void* out, hipStream_t s);
+hipError_t launch_combine_rows(const moe_dims_t& d, int T, const float* y_perm, const int32_t* row_of,
+                               const float* topk_w, const uint8_t* exact, const float* y_s,
+                               const float* g_s, void* out, hipStream_t s);
 hipError_t launch_lore(const moe_dims_t& d, int T, const void* x, const int32_t* ids,
                        const uint8_t* exact, const void* lore_A, const void* lore_B,
                        float* lore_out, hipStream_t s);
@@ -94,16 +104,23 @@ moe_status_t check_weights(const moe_dims_t* d, const moe_weights_t* w, moe_mode
 
 // Workspace plan for T tokens.
 struct Plan {
-  size_t ids, w, exact, flags, offsets, perm, inv;       // routing + permutation
-  size_t act, act_s, y_perm, y_s, g_s;                   // dense FFN
-  size_t u, keep, fa, part;                              // FloE
-  size_t ffn_begin, total;
+  size_t ids, w, exact, flags, offsets, moffsets, perm, inv, row_of;  // routing + permutation
+  size_t y_perm, y_s, g_s;                                            // FFN outputs
+  size_t act, act_s;                                                  // fp32 GEMV activations
+  size_t act_hi, act_lo, acts_hi, acts_lo, z_hi, z_lo;                // bf16 MFMA activations
+  size_t u, keep, fa, part;                                           // FloE
+  bool use_lo;
+  size_t total;
 };
+
+// bf16 hi + lo activations keep ~16 significant bits for the down projection
+// at decode sizes; beyond 64 tokens only hi is kept.
+inline bool split_act(int T) { return T <= 64; }
 
 Plan make_plan(const moe_dims_t& d, int T, moe_mode_t mode) {
   Plan p{};
   const size_t P = (size_t)T * d.top_k;
-  const size_t H = d.hidden, I = d.inter;
+  const size_t H = d.hidden, I = d.inter, S = (size_t)d.n_shared * d.shared_inter;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o = align256(o + bytes); return at; };
   p.ids = take(P * 4);
@@ -111,20 +128,33 @@ Plan make_plan(const moe_dims_t& d, int T, moe_mode_t mode) {
   p.exact = take(P);
   p.flags = take((size_t)T * 4);
   p.offsets = take((size_t)(d.n_experts + 1) * 4);
+  p.moffsets = take((size_t)(d.n_experts + 1) * 4);
   p.perm = take(P * 4);
   p.inv = take(P * 4);
-  p.ffn_begin = o;
+  p.row_of = take(P * 4);
   p.y_perm = take(P * H * 4);
+  p.use_lo = split_act(T);
   if (mode == MOE_MODE_FLOE) {
     p.u = take(P * I * 4);
     p.keep = take(P * (size_t)d.floe_keep * 4);
     p.fa = take(P * (size_t)d.floe_keep * 4);
     p.part = take((size_t)floe_slices(d.floe_keep) * P * H * 4);
+  } else if (d.dtype == MOE_BF16) {
+    p.act_hi = take(P * I * 2);
+    if (p.use_lo) p.act_lo = take(P * I * 2);
+    if (S) {
+      p.acts_hi = take((size_t)T * S * 2);
+      if (p.use_lo) p.acts_lo = take((size_t)T * S * 2);
+    }
+    if (mode == MOE_MODE_LORE) {
+      p.z_hi = take(P * (size_t)d.lore_rank * 2);
+      if (p.use_lo) p.z_lo = take(P * (size_t)d.lore_rank * 2);
+    }
   } else {
     p.act = take(P * I * 4);
+    if (S) p.act_s = take((size_t)T * S * 4);
   }
   if (d.n_shared > 0) {
-    p.act_s = take((size_t)T * d.n_shared * d.shared_inter * 4);
     p.y_s = take((size_t)T * H * 4);
     p.g_s = take((size_t)T * 4);
   }
@@ -137,16 +167,36 @@ inline T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<cha
 
 inline moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
-// Dense or FloE expert FFNs + shared experts into the plan's buffers.
+// Dense or FloE expert FFNs + shared experts (+ the LoRE products when
+// `lore`) into the plan's buffers.  bf16 layers run on the matrix cores; fp32
+// layers use the vector GEMV kernels.
 hipError_t run_ffn(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
-                   moe_mode_t mode, const int32_t* offsets, const int32_t* perm, float* y_perm,
-                   float* y_s, float* g_s, int32_t* keep, uint32_t* flags, void* ws, const Plan& p,
-                   hipStream_t s) {
+                   moe_mode_t mode, const int32_t* offsets, const int32_t* moffsets,
+                   const int32_t* perm, float* y_perm, float* y_s, int32_t* keep, uint32_t* flags,
+                   void* ws, const Plan& p, int lore, const Prof& pf, hipStream_t s) {
   if (mode == MOE_MODE_FLOE)
     return launch_floe(d, T, x, w, offsets, perm, at<float>(ws, p.u), keep, at<float>(ws, p.fa),
-                       at<float>(ws, p.part), y_perm, flags, s);
-  return launch_dense_ffn(d, T, x, w, offsets, perm, T * d.top_k, at<float>(ws, p.act), y_perm,
-                          d.n_shared > 0 ? at<float>(ws, p.act_s) : nullptr, y_s, g_s, s);
+                       at<float>(ws, p.part), y_perm, flags, pf, s);
+  if (d.dtype != MOE_BF16)
+    return launch_dense_ffn(d, T, x, w, offsets, perm, T * d.top_k, at<float>(ws, p.act), y_perm,
+                            d.n_shared > 0 ? at<float>(ws, p.act_s) : nullptr, y_s, pf, s);
+  const bool sh = d.n_shared > 0;
+  FfnBuffers b{};
+  b.act_hi = at<bf16>(ws, p.act_hi);
+  b.act_lo = p.use_lo ? at<bf16>(ws, p.act_lo) : nullptr;
+  b.acts_hi = sh ? at<bf16>(ws, p.acts_hi) : nullptr;
+  b.acts_lo = (sh && p.use_lo) ? at<bf16>(ws, p.acts_lo) : nullptr;
+  b.z_hi = lore ? at<bf16>(ws, p.z_hi) : nullptr;
+  b.z_lo = (lore && p.use_lo) ? at<bf16>(ws, p.z_lo) : nullptr;
+  b.y = y_perm;
+  b.ys = y_s;
+  hipError_t e = pf.begin(MOE_KERNEL_EXPERT_GATE_UP, s);
+  if (e == hipSuccess) e = launch_ffn_mfma(d, T, x, w, offsets, moffsets, perm, b, lore, s, 1);
+  if (e == hipSuccess) e = pf.end(MOE_KERNEL_EXPERT_GATE_UP, s);
+  if (e == hipSuccess) e = pf.begin(MOE_KERNEL_EXPERT_DOWN, s);
+  if (e == hipSuccess) e = launch_ffn_mfma(d, T, x, w, offsets, moffsets, perm, b, lore, s, 2);
+  if (e == hipSuccess) e = pf.end(MOE_KERNEL_EXPERT_DOWN, s);
+  return e;
 }
 
 }  // namespace
@@ -193,7 +243,8 @@ moe_status_t moe_route(const moe_dims_t* dims, int32_t T, const void* x, const v
     return MOE_EINVAL;
   if (T == 0) return MOE_OK;
   return hip_status(launch_route(*dims, T, x, w_router, resident, resident_stride, mode, topk_ids,
-                                 topk_w, exact, flags, logits_opt, mass_opt, (hipStream_t)stream));
+                                 topk_w, exact, flags, logits_opt, mass_opt, nullptr, nullptr,
+                                 (hipStream_t)stream));
 }
 
 moe_status_t moe_prefetch_mask(const moe_dims_t* dims, int32_t T, const void* x,
@@ -220,8 +271,8 @@ moe_status_t moe_permute(int32_t T, int32_t k, int32_t E, const int32_t* topk_id
   if (!ok_ptr(topk_ids) || !ok_ptr(exact) || !ok_ptr(expert_offsets) || !ok_ptr(perm) ||
       !ok_ptr(inv))
     return MOE_EINVAL;
-  return hip_status(launch_permute(T * k, E, topk_ids, exact, expert_offsets, perm, inv,
-                                   (hipStream_t)stream));
+  return hip_status(launch_permute(T * k, E, topk_ids, exact, expert_offsets, perm, inv, nullptr,
+                                   nullptr, (hipStream_t)stream));
 }
 
 moe_status_t moe_expert_ffn(const moe_dims_t* dims, int32_t T, const void* x,
@@ -244,8 +295,10 @@ moe_status_t moe_expert_ffn(const moe_dims_t* dims, int32_t T, const void* x,
   if (ws_bytes < p.total) return MOE_EWORKSPACE;
   if (T == 0) return MOE_OK;
   int32_t* keep = floe_keep_opt ? floe_keep_opt : at<int32_t>(ws, p.keep);
-  return hip_status(run_ffn(*dims, T, x, *w, mode, expert_offsets, perm, y_perm, y_shared,
-                            shared_gate, keep, flags_opt, ws, p, (hipStream_t)stream));
+  hipError_t e = run_ffn(*dims, T, x, *w, mode, expert_offsets, nullptr, perm, y_perm, y_shared, keep,
+                         flags_opt, ws, p, 0, Prof{}, (hipStream_t)stream);
+  if (e == hipSuccess) e = launch_shared_gate(*dims, T, x, *w, shared_gate, (hipStream_t)stream);
+  return hip_status(e);
 }
 
 moe_status_t moe_lore_surrogate(const moe_dims_t* dims, int32_t T, const void* x,
@@ -314,20 +367,44 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, int32_t T, const void* x,
   int32_t* offsets = at<int32_t>(ws, p.offsets);
   int32_t* perm = at<int32_t>(ws, p.perm);
   int32_t* inv = at<int32_t>(ws, p.inv);
+  int32_t* row_of = at<int32_t>(ws, p.row_of);
+  int32_t* moffsets = at<int32_t>(ws, p.moffsets);
   float* y_perm = at<float>(ws, p.y_perm);
   float* y_s = d.n_shared > 0 ? at<float>(ws, p.y_s) : nullptr;
   float* g_s = d.n_shared > 0 ? at<float>(ws, p.g_s) : nullptr;
   int32_t* keep = (mode == MOE_MODE_FLOE) ? at<int32_t>(ws, p.keep) : nullptr;
+  const bool lore = mode == MOE_MODE_LORE;
+  // bf16: LoRE products run as extra tiles of the FFN kernels and the combine
+  // reads rows; fp32: the combine computes LoRE itself.
+  const bool mfma = d.dtype == MOE_BF16 && mode != MOE_MODE_FLOE;
 
-  hipError_t e = launch_route(d, T, x, w->w_router, resident, resident_stride, mode, ids, wts, exact,
-                              flags, dbg ? dbg->logits : nullptr, dbg ? dbg->mass : nullptr, s);
-  if (e == hipSuccess) e = launch_permute(P, E, ids, exact, offsets, perm, inv, s);
+  Prof pf;
+  if (dbg) {
+    pf.id = dbg->prof_kernel;
+    pf.start = (hipEvent_t)dbg->prof_start;
+    pf.stop = (hipEvent_t)dbg->prof_stop;
+  }
+  hipError_t e = pf.begin(MOE_KERNEL_ROUTE, s);
   if (e == hipSuccess)
-    e = run_ffn(d, T, x, *w, mode, offsets, perm, y_perm, y_s, g_s, keep, flags, ws, p, s);
+    e = launch_route(d, T, x, w->w_router, resident, resident_stride, mode, ids, wts, exact, flags,
+                     dbg ? dbg->logits : nullptr, dbg ? dbg->mass : nullptr,
+                     d.shared_gate ? w->w_shared_gate : nullptr, g_s, s);
+  if (e == hipSuccess) e = pf.end(MOE_KERNEL_ROUTE, s);
+  if (e == hipSuccess) e = pf.begin(MOE_KERNEL_PERMUTE, s);
+  if (e == hipSuccess) e = launch_permute(P, E, ids, exact, offsets, perm, inv, row_of, moffsets, s);
+  if (e == hipSuccess) e = pf.end(MOE_KERNEL_PERMUTE, s);
   if (e == hipSuccess)
-    e = launch_combine(d, T, y_perm, inv, wts, exact, ids, y_s, g_s, nullptr, x,
-                       mode == MOE_MODE_LORE ? w->lore_A : nullptr,
-                       mode == MOE_MODE_LORE ? w->lore_B : nullptr, out, s);
+    e = run_ffn(d, T, x, *w, mode, offsets, moffsets, perm, y_perm, y_s, keep, flags, ws, p,
+                mfma && lore, pf, s);
+  if (e == hipSuccess) e = pf.begin(MOE_KERNEL_COMBINE, s);
+  if (e == hipSuccess) {
+    if (mfma || mode == MOE_MODE_FLOE)
+      e = launch_combine_rows(d, T, y_perm, row_of, wts, exact, y_s, g_s, out, s);
+    else
+      e = launch_combine(d, T, y_perm, inv, wts, exact, ids, y_s, g_s, nullptr, x,
+                         lore ? w->lore_A : nullptr, lore ? w->lore_B : nullptr, out, s);
+  }
+  if (e == hipSuccess) e = pf.end(MOE_KERNEL_COMBINE, s);
   if (e == hipSuccess && dbg) {
     auto cp = [&](void* dst, const void* src, size_t bytes) {
       if (dst && e == hipSuccess) e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);

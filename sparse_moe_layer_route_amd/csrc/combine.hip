@@ -120,6 +120,64 @@ lore_kernel(int H, int k, int r, const Tin* __restrict__ x, const int32_t* __res
   }
 }
 
+// Combine over y_perm rows: out[t] = g_s y_s + sum_j w_j (y_perm[row_of[f]] +
+// (exact ? 0 : y_s)), f = t*k + j.  Non-exact rows already hold B_e A_e x_t,
+// so a surrogate slot contributes w_j (y_s + B_e A_e x_t).  Each thread owns
+// four consecutive columns (16-byte loads).
+template <typename Tin>
+__global__ void __launch_bounds__(COMBINE_THREADS)
+combine_rows_kernel(int H, int k, const float* __restrict__ y_perm, const int32_t* __restrict__ row_of,
+                    const float* __restrict__ topk_w, const uint8_t* __restrict__ exact,
+                    const float* __restrict__ y_s, const float* __restrict__ g_s,
+                    Tin* __restrict__ out) {
+  __shared__ int s_row[MOE_MAX_TOPK], s_ex[MOE_MAX_TOPK];
+  __shared__ float s_w[MOE_MAX_TOPK];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (tid < k) {
+    const int64_t o = (int64_t)t * k + tid;
+    s_row[tid] = row_of[o];
+    s_ex[tid] = exact[o];
+    s_w[tid] = topk_w[o];
+  }
+  __syncthreads();
+  const float gs = g_s ? g_s[t] : 1.f;
+  for (int h = tid * 4; h < H; h += COMBINE_THREADS * 4) {
+    float4 ys = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (y_s) ys = *reinterpret_cast<const float4*>(y_s + (int64_t)t * H + h);
+    float a0 = gs * ys.x, a1 = gs * ys.y, a2 = gs * ys.z, a3 = gs * ys.w;
+    for (int j = 0; j < k; ++j) {
+      const int row = s_row[j];
+      if (row < 0) continue;
+      float4 v = *reinterpret_cast<const float4*>(y_perm + (int64_t)row * H + h);
+      if (!s_ex[j]) {
+        v.x += ys.x; v.y += ys.y; v.z += ys.z; v.w += ys.w;
+      }
+      const float wj = s_w[j];
+      a0 = fmaf(wj, v.x, a0);
+      a1 = fmaf(wj, v.y, a1);
+      a2 = fmaf(wj, v.z, a2);
+      a3 = fmaf(wj, v.w, a3);
+    }
+    const int64_t o = (int64_t)t * H + h;
+    elem<Tin>::store(out, o, a0);
+    elem<Tin>::store(out, o + 1, a1);
+    elem<Tin>::store(out, o + 2, a2);
+    elem<Tin>::store(out, o + 3, a3);
+  }
+}
+
+hipError_t launch_combine_rows(const moe_dims_t& d, int T, const float* y_perm, const int32_t* row_of,
+                               const float* topk_w, const uint8_t* exact, const float* y_s,
+                               const float* g_s, void* out, hipStream_t s) {
+  if (d.dtype == MOE_BF16)
+    combine_rows_kernel<bf16><<<T, COMBINE_THREADS, 0, s>>>(d.hidden, d.top_k, y_perm, row_of, topk_w,
+                                                            exact, y_s, g_s, (bf16*)out);
+  else
+    combine_rows_kernel<float><<<T, COMBINE_THREADS, 0, s>>>(d.hidden, d.top_k, y_perm, row_of, topk_w,
+                                                             exact, y_s, g_s, (float*)out);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const moe_dims_t& d, int T, const float* y_perm, const int32_t* inv,
                           const float* topk_w, const uint8_t* exact, const int32_t* ids,
                           const float* y_s, const float* g_s, const float* lore_out, const void* x,

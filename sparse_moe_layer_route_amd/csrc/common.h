@@ -92,4 +92,24 @@ __device__ __forceinline__ uint32_t float_order_key(float f) {
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
+// Activation buffers of the matrix-core FFN (bf16 hi + optional lo parts).
+struct FfnBuffers {
+  bf16 *act_hi, *act_lo;    // routed   [T*k][I]
+  bf16 *acts_hi, *acts_lo;  // shared   [T][n_shared*I_s]
+  bf16 *z_hi, *z_lo;        // LoRE A x [T*k][r]
+  float *y, *ys;            // y_perm [T*k][H], y_shared [T][H]
+};
+
+// Events recorded around one named kernel launch (see moe_kernel_t).
+struct Prof {
+  int id = MOE_KERNEL_NONE;
+  hipEvent_t start = nullptr, stop = nullptr;
+  hipError_t begin(int k, hipStream_t s) const {
+    return (id == k && start) ? hipEventRecord(start, s) : hipSuccess;
+  }
+  hipError_t end(int k, hipStream_t s) const {
+    return (id == k && stop) ? hipEventRecord(stop, s) : hipSuccess;
+  }
+};
+
 }  // namespace moe

@@ -185,19 +185,25 @@ shared_gate_kernel(const Tin* __restrict__ x, const Tin* __restrict__ wsg, int H
 template <typename Tin>
 static hipError_t launch_dense_ffn_t(const moe_dims_t& d, int T, const Tin* x, const moe_weights_t& w,
                                      const int32_t* offsets, const int32_t* perm, int n_pairs_max,
-                                     float* act, float* y_perm, float* act_s, float* y_s, float* g_s,
-                                     hipStream_t s) {
+                                     float* act, float* y_perm, float* act_s, float* y_s,
+                                     const Prof& pf, hipStream_t s) {
   constexpr int NT = 4;
   const int H = d.hidden, I = d.inter, E = d.n_experts, k = d.top_k;
   const int max_active = n_pairs_max < E ? n_pairs_max : E;
+  hipError_t e = hipSuccess;
   if (max_active > 0) {
     dim3 g1(I / GEMV_ROWS_PER_BLOCK, max_active);
+    e = pf.begin(MOE_KERNEL_EXPERT_GATE_UP, s);
     gate_up_kernel<Tin, NT><<<g1, 256, 0, s>>>(x, (const Tin*)w.w_gate, (const Tin*)w.w_up, H, I,
                                                (int64_t)I * H, 1, E, k, T, offsets, perm, act, I);
+    if (e == hipSuccess) e = pf.end(MOE_KERNEL_EXPERT_GATE_UP, s);
     dim3 g2(H / GEMV_ROWS_PER_BLOCK, max_active);
+    if (e == hipSuccess) e = pf.begin(MOE_KERNEL_EXPERT_DOWN, s);
     down_kernel<Tin, NT><<<g2, 256, 0, s>>>((const Tin*)w.w_down, H, I, (int64_t)H * I, 1, 0, 1, E,
                                             T, offsets, act, I, y_perm);
+    if (e == hipSuccess) e = pf.end(MOE_KERNEL_EXPERT_DOWN, s);
   }
+  if (e != hipSuccess) return e;
   if (d.n_shared > 0) {
     const int Is = d.shared_inter, ns = d.n_shared;
     dim3 g1(Is / GEMV_ROWS_PER_BLOCK, ns);
@@ -207,20 +213,31 @@ static hipError_t launch_dense_ffn_t(const moe_dims_t& d, int T, const Tin* x, c
     dim3 g2(H / GEMV_ROWS_PER_BLOCK, 1);
     down_kernel<Tin, NT><<<g2, 256, 0, s>>>((const Tin*)w.ws_down, H, Is, 0, ns, (int64_t)H * Is, 0,
                                             E, T, offsets, act_s, (int64_t)ns * Is, y_s);
-    shared_gate_kernel<Tin><<<T, 64, 0, s>>>(x, (const Tin*)w.w_shared_gate, H, d.shared_gate, g_s);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_shared_gate(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
+                              float* g_s, hipStream_t s) {
+  if (d.n_shared == 0) return hipSuccess;
+  if (d.dtype == MOE_BF16)
+    shared_gate_kernel<bf16><<<T, 64, 0, s>>>((const bf16*)x, (const bf16*)w.w_shared_gate, d.hidden,
+                                              d.shared_gate, g_s);
+  else
+    shared_gate_kernel<float><<<T, 64, 0, s>>>((const float*)x, (const float*)w.w_shared_gate,
+                                               d.hidden, d.shared_gate, g_s);
   return hipGetLastError();
 }
 
 hipError_t launch_dense_ffn(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
                             const int32_t* offsets, const int32_t* perm, int n_pairs_max,
-                            float* act, float* y_perm, float* act_s, float* y_s, float* g_s,
+                            float* act, float* y_perm, float* act_s, float* y_s, const Prof& pf,
                             hipStream_t s) {
   if (d.dtype == MOE_BF16)
     return launch_dense_ffn_t<bf16>(d, T, (const bf16*)x, w, offsets, perm, n_pairs_max, act, y_perm,
-                                    act_s, y_s, g_s, s);
+                                    act_s, y_s, pf, s);
   return launch_dense_ffn_t<float>(d, T, (const float*)x, w, offsets, perm, n_pairs_max, act, y_perm,
-                                   act_s, y_s, g_s, s);
+                                   act_s, y_s, pf, s);
 }
 
 }  // namespace moe

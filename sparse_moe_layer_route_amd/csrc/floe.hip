@@ -309,33 +309,42 @@ int floe_max_inter() { return FLOE_MAX_INTER; }
 
 template <typename Tin>
 static hipError_t launch_floe_t(const moe_dims_t& d, int T, const Tin* x, const moe_weights_t& w,
-                                const int32_t* offsets, const int32_t* perm, float* u, int32_t* keep, float* a, float* part, float* y_perm,
-                                uint32_t* flags, hipStream_t s) {
+                                const int32_t* offsets, const int32_t* perm, float* u,
+                                int32_t* keep, float* a, float* part, float* y_perm,
+                                uint32_t* flags, const Prof& pf, hipStream_t s) {
   const int H = d.hidden, I = d.inter, E = d.n_experts, k = d.top_k, nk = d.floe_keep;
   const int P = T * k;
   if (P == 0) return hipSuccess;
+  hipError_t e = pf.begin(MOE_KERNEL_FLOE_UP, s);
   floe_up_kernel<Tin><<<dim3(I / FLOE_ROWS_PER_BLOCK, P), 256, 0, s>>>(
       x, w.up_q, w.up_scale, w.up_zero, H, I, E, k, offsets, perm, u);
+  if (e == hipSuccess) e = pf.end(MOE_KERNEL_FLOE_UP, s);
+  if (e == hipSuccess) e = pf.begin(MOE_KERNEL_FLOE_SELECT, s);
   floe_select_kernel<<<P, FLOE_SELECT_THREADS, 0, s>>>(u, I, nk, d.tie_margin, E, k, offsets, perm,
                                                         keep, flags);
+  if (e == hipSuccess) e = pf.end(MOE_KERNEL_FLOE_SELECT, s);
+  if (e == hipSuccess) e = pf.begin(MOE_KERNEL_FLOE_GATE, s);
   floe_gate_kernel<Tin><<<dim3((nk + FLOE_ROWS_PER_BLOCK - 1) / FLOE_ROWS_PER_BLOCK, P), 256, 0, s>>>(
       x, (const Tin*)w.w_gate, u, H, I, nk, E, k, offsets, perm, keep, a);
+  if (e == hipSuccess) e = pf.end(MOE_KERNEL_FLOE_GATE, s);
   const int ns = floe_slices(nk);
+  if (e == hipSuccess) e = pf.begin(MOE_KERNEL_FLOE_DOWN, s);
   floe_down_kernel<Tin><<<dim3((H + 2047) / 2048, ns, P), 256, 0, s>>>(
       (const Tin*)w.w_down, a, H, I, nk, P, E, k, offsets, perm, keep, part);
+  if (e == hipSuccess) e = pf.end(MOE_KERNEL_FLOE_DOWN, s);
   floe_reduce_kernel<<<dim3((H + 255) / 256, P), 256, 0, s>>>(part, H, ns, P, E, offsets, y_perm);
-  return hipGetLastError();
+  return e == hipSuccess ? hipGetLastError() : e;
 }
 
 hipError_t launch_floe(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
                        const int32_t* offsets, const int32_t* perm, float* u,
                        int32_t* keep, float* a, float* part, float* y_perm, uint32_t* flags,
-                       hipStream_t s) {
+                       const Prof& pf, hipStream_t s) {
   if (d.dtype == MOE_BF16)
     return launch_floe_t<bf16>(d, T, (const bf16*)x, w, offsets, perm, u, keep, a, part, y_perm,
-                               flags, s);
+                               flags, pf, s);
   return launch_floe_t<float>(d, T, (const float*)x, w, offsets, perm, u, keep, a, part, y_perm,
-                              flags, s);
+                              flags, pf, s);
 }
 
 }  // namespace moe

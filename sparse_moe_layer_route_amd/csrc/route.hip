@@ -1,61 +1,148 @@
 // Router: logits -> softmax -> top-k, residency split, stall-free
-// substitution, and the APEX prefetch mask.
+// substitution, shared-expert gate, and the APEX prefetch mask.
 //
-// One 256-thread block per token.  The four waves each sum a quarter of the
-// hidden dimension with lane = expert (E <= 64), the partial logits meet in
-// LDS, and wave 0 does everything else with wave-wide shuffles:
-//   softmax            max / sum of exp over the 64 lanes;
-//   top-k              k rounds of a 64-bit arg-max whose key is
-//                      (order-preserving logit bits, 0xFFFFFFFF - id), so
-//                      equal logits go to the lower id;
-//   near-tie flag      one extra round reads the first rejected logit.
+// One 1024-thread block (16 waves) per tile of 16 tokens.
+//   logits  bf16: l = X W_r^T on the matrix cores (v_mfma_f32_16x16x32_bf16),
+//           A = 16 token rows, B = 16 expert rows of W_r [E][H] (both k
+//           contiguous).  The 16 waves are ceil(E/16) expert tiles times a
+//           K split; partial tiles meet in LDS and are summed in a fixed
+//           order, so logits are bitwise reproducible.
+//           fp32: each wave dots its token with every expert row.
+//   top-k   wave w finishes token w of the tile with lane = expert:
+//           softmax by wave max / sum of exp; k rounds of a 64-bit arg-max on
+//           (order-preserving logit bits, 0xFFFFFFFF - id), so equal logits go
+//           to the lower id; one more round reads the first rejected logit for
+//           the near-tie flag.
 // Stall-free substitution [APEX page, Sec. 4.3, Algorithm 1]: every routed
-// expert outranks every non-routed one, so "keep the prefetched routed experts
-// and fill each miss with the best remaining prefetched expert" is the top-k
-// of the router restricted to the prefetched set; the kernel takes that
-// masked top-k.
+// expert outranks every non-routed one, so keeping the prefetched routed
+// experts and filling each miss with the best remaining prefetched expert is
+// the top-k of the router restricted to the prefetched set; the kernel takes
+// that masked top-k.
 #include "common.h"
 
 namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int ROUTE_TOK = 16;
+constexpr int ROUTE_WAVES = 16;
 
 __device__ __forceinline__ uint64_t topk_key(float l, int e) {
   return ((uint64_t)float_order_key(l) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 __device__ __forceinline__ int key_id(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
 
-// Logits of token t for lanes 0..E-1, returned to every lane of wave 0 (-inf
-// beyond E).  Call from all 256 threads.
-template <typename Tin>
-__device__ __forceinline__ float block_logits(const Tin* __restrict__ xr, const Tin* __restrict__ w,
-                                              int H, int E, float (*part)[MOE_WAVE]) {
+struct RouteLds {
+  float part[ROUTE_WAVES][ROUTE_TOK][MOE_MAX_EXPERTS];
+  float logits[ROUTE_TOK][MOE_MAX_EXPERTS];
+};
+
+// Logits of tokens t0..t0+15 (rows past T are clamped, results unused) into
+// lds.logits.  Called by all 1024 threads.
+__device__ __forceinline__ void tile_logits(const bf16* __restrict__ x, const bf16* __restrict__ w,
+                                            int T, int H, int E, int t0, RouteLds& lds) {
   const int lane = lane_id(), wv = threadIdx.x >> 6;
-  float acc = 0.f;
-  if (lane < E) {
-    const int hq = H >> 2;
-    const int h0 = wv * hq;
-    for (int h = h0; h < h0 + hq; ++h)
-      acc = fmaf(elem<Tin>::load(xr, h), elem<Tin>::load(w, (int64_t)h * E + lane), acc);
+  const int n_et = (E + 15) >> 4;
+  const int n_sp = ROUTE_WAVES / n_et;
+  const int et = wv % n_et, sp = wv / n_et;
+  const int r16 = lane & 15, kg = lane >> 4;
+  if (sp < n_sp) {
+    const int t = min(t0 + r16, T - 1);
+    const int e = et * 16 + r16;
+    const bf16* xr = x + (int64_t)t * H + 8 * kg;
+    const bf16* wr = w + (int64_t)min(e, E - 1) * H + 8 * kg;
+    const bool live = e < E;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    const int ksteps = H >> 5;
+    int ks = sp;
+    for (; ks + 3 * n_sp < ksteps; ks += 4 * n_sp) {
+      bf16x8_t a[4], b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a[u] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(xr + ((ks + u * n_sp) << 5)));
+        b[u] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(wr + ((ks + u * n_sp) << 5)));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (!live) b[u] = __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u], acc, 0, 0, 0);
+      }
+    }
+    for (; ks < ksteps; ks += n_sp) {
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(xr + (ks << 5)));
+      bf16x8_t b = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(wr + (ks << 5)));
+      if (!live) b = __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+    // accumulator: rows (tokens) 4*kg+i, column (expert) r16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds.part[sp][4 * kg + i][et * 16 + r16] = acc[i];
   }
-  part[wv][lane] = acc;
   __syncthreads();
-  float l = -INFINITY;
-  if (lane < E) l = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
-  return l;
+  for (int idx = threadIdx.x; idx < ROUTE_TOK * MOE_MAX_EXPERTS; idx += ROUTE_TOK * MOE_WAVE) {
+    const int tt = idx / MOE_MAX_EXPERTS, e = idx % MOE_MAX_EXPERTS;
+    float s = 0.f;
+    for (int p = 0; p < n_sp; ++p) s += lds.part[p][tt][e];
+    lds.logits[tt][e] = s;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void tile_logits(const float* __restrict__ x, const float* __restrict__ w,
+                                            int T, int H, int E, int t0, RouteLds& lds) {
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  const int t = t0 + wv;
+  if (t < T) {
+    for (int e = 0; e < E; ++e) {
+      float acc = 0.f;
+      for (int h = lane * 8; h < H; h += 8 * MOE_WAVE) {
+        float a8[8], b8[8];
+        elem<float>::load8(x + (int64_t)t * H + h, a8);
+        elem<float>::load8(w + (int64_t)e * H + h, b8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc = fmaf(a8[j], b8[j], acc);
+      }
+      acc = wave_sum(acc);
+      if (lane == 0) lds.logits[wv][e] = acc;
+    }
+  }
+  __syncthreads();
 }
 
 template <typename Tin>
-__global__ void __launch_bounds__(256)
-route_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w_router, int H, int E, int k,
+__device__ __forceinline__ float wave_dot(const Tin* __restrict__ a, const Tin* __restrict__ b, int H) {
+  float acc = 0.f;
+  for (int h = lane_id() * 8; h < H; h += 8 * MOE_WAVE) {
+    float a8[8], b8[8];
+    elem<Tin>::load8(a + h, a8);
+    elem<Tin>::load8(b + h, b8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = fmaf(a8[j], b8[j], acc);
+  }
+  return wave_sum(acc);
+}
+
+template <typename Tin>
+__global__ void __launch_bounds__(1024)
+route_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w_router, int T, int H, int E, int k,
              int renorm, float margin, int mode, const uint64_t* __restrict__ resident,
              int64_t res_stride, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
              uint8_t* __restrict__ exact, uint32_t* __restrict__ flags,
-             float* __restrict__ logits_out, float* __restrict__ mass_out) {
-  __shared__ float part[4][MOE_WAVE];
-  const int t = blockIdx.x;
-  const float l = block_logits<Tin>(x + (int64_t)t * H, w_router, H, E, part);
-  if (threadIdx.x >= MOE_WAVE) return;
-  const int lane = threadIdx.x;
+             float* __restrict__ logits_out, float* __restrict__ mass_out,
+             const Tin* __restrict__ w_sg, float* __restrict__ g_s) {
+  __shared__ RouteLds lds;
+  const int t0 = blockIdx.x * ROUTE_TOK;
+  tile_logits(x, w_router, T, H, E, t0, lds);
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  const int t = t0 + wv;
+  if (t >= T) return;
+  const float l = lane < E ? lds.logits[wv][lane] : -INFINITY;
   if (logits_out && lane < E) logits_out[(int64_t)t * E + lane] = l;
+  if (g_s) {
+    const float gd = w_sg ? wave_dot<Tin>(x + (int64_t)t * H, w_sg, H) : 0.f;
+    if (lane == 0) g_s[t] = w_sg ? sigmoid_f(gd) : 1.f;
+  }
 
   // softmax numerator / denominator
   const float mx = wave_max(l);
@@ -125,17 +212,19 @@ route_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w_router, int H,
   }
 }
 
-// APEX prefetch set: top-(k + delta_t) of x W_p as a bit mask.
+// APEX prefetch set: top-(k + delta_t) of x W_p^T as a bit mask.
 template <typename Tin>
-__global__ void __launch_bounds__(256)
-prefetch_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w_p, int H, int E, int k,
+__global__ void __launch_bounds__(1024)
+prefetch_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w_p, int T, int H, int E, int k,
                 float margin, const int32_t* __restrict__ delta, uint64_t* __restrict__ mask_out,
                 uint32_t* __restrict__ flags) {
-  __shared__ float part[4][MOE_WAVE];
-  const int t = blockIdx.x;
-  const float l = block_logits<Tin>(x + (int64_t)t * H, w_p, H, E, part);
-  if (threadIdx.x >= MOE_WAVE) return;
-  const int lane = threadIdx.x;
+  __shared__ RouteLds lds;
+  const int t0 = blockIdx.x * ROUTE_TOK;
+  tile_logits(x, w_p, T, H, E, t0, lds);
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  const int t = t0 + wv;
+  if (t >= T) return;
+  const float l = lane < E ? lds.logits[wv][lane] : -INFINITY;
   int n = k + delta[t];
   n = n < 1 ? 1 : (n > E ? E : n);
   uint64_t key = lane < E ? topk_key(l, lane) : 0ull;
@@ -162,29 +251,33 @@ prefetch_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w_p, int H, i
 hipError_t launch_route(const moe_dims_t& d, int T, const void* x, const void* w_router,
                         const uint64_t* resident, int64_t res_stride, int mode, int32_t* ids,
                         float* w, uint8_t* exact, uint32_t* flags, float* logits, float* mass,
-                        hipStream_t s) {
+                        const void* w_sg, float* g_s, hipStream_t s) {
+  const int blocks = (T + ROUTE_TOK - 1) / ROUTE_TOK;
   if (d.dtype == MOE_BF16)
-    route_kernel<bf16><<<T, 256, 0, s>>>((const bf16*)x, (const bf16*)w_router, d.hidden,
-                                         d.n_experts, d.top_k, d.renormalize, d.tie_margin, mode,
-                                         resident, res_stride, ids, w, exact, flags, logits, mass);
+    route_kernel<bf16><<<blocks, 1024, 0, s>>>((const bf16*)x, (const bf16*)w_router, T, d.hidden,
+                                               d.n_experts, d.top_k, d.renormalize, d.tie_margin,
+                                               mode, resident, res_stride, ids, w, exact, flags,
+                                               logits, mass, (const bf16*)w_sg, g_s);
   else
-    route_kernel<float><<<T, 256, 0, s>>>((const float*)x, (const float*)w_router, d.hidden,
-                                          d.n_experts, d.top_k, d.renormalize, d.tie_margin, mode,
-                                          resident, res_stride, ids, w, exact, flags, logits, mass);
+    route_kernel<float><<<blocks, 1024, 0, s>>>((const float*)x, (const float*)w_router, T, d.hidden,
+                                                d.n_experts, d.top_k, d.renormalize, d.tie_margin,
+                                                mode, resident, res_stride, ids, w, exact, flags,
+                                                logits, mass, (const float*)w_sg, g_s);
   return hipGetLastError();
 }
 
 hipError_t launch_prefetch(const moe_dims_t& d, int T, const void* x, const void* w_p,
                            const int32_t* delta, uint64_t* mask_out, uint32_t* flags,
                            hipStream_t s) {
+  const int blocks = (T + ROUTE_TOK - 1) / ROUTE_TOK;
   if (d.dtype == MOE_BF16)
-    prefetch_kernel<bf16><<<T, 256, 0, s>>>((const bf16*)x, (const bf16*)w_p, d.hidden,
-                                            d.n_experts, d.top_k, d.tie_margin, delta, mask_out,
-                                            flags);
+    prefetch_kernel<bf16><<<blocks, 1024, 0, s>>>((const bf16*)x, (const bf16*)w_p, T, d.hidden,
+                                                  d.n_experts, d.top_k, d.tie_margin, delta,
+                                                  mask_out, flags);
   else
-    prefetch_kernel<float><<<T, 256, 0, s>>>((const float*)x, (const float*)w_p, d.hidden,
-                                             d.n_experts, d.top_k, d.tie_margin, delta, mask_out,
-                                             flags);
+    prefetch_kernel<float><<<blocks, 1024, 0, s>>>((const float*)x, (const float*)w_p, T, d.hidden,
+                                                   d.n_experts, d.top_k, d.tie_margin, delta,
+                                                   mask_out, flags);
   return hipGetLastError();
 }
 

@@ -208,7 +208,7 @@ def oracle_forward_forced(layer: W.Layer, T: int, mode: str, g: GpuRun, sample: 
 def check_floe_masks(layer: W.Layer, g: GpuRun, ref: dict, sample: Sequence[int]):
     """FloE kept channels: exact where the oracle sees no near-tie at the
     mask edge; admissible within the margin otherwise."""
-    n_keep = layer.cfg.floe_keep
+    n_keep = g.keep.shape[2]
     n_tie = 0
     for i, t in enumerate(sample):
         for j in range(layer.cfg.top_k):

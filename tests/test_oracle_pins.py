@@ -36,7 +36,7 @@ def _mask(ids):
 
 
 def _hand_expected():
-    """Worked by hand.  Logits are [2, 1, 0.5, 0] (x picks row 0 of W_r).
+    """Worked by hand.  Logits are [2, 1, 0.5, 0] (x picks column 0 of W_r).
     Expert outputs with x = [1, 0]: g = gate[0], u = up[0], y = SiLU(g) u down.
     SiLU(z) = z sigma(z)."""
     sig = lambda z: 1.0 / (1.0 + math.exp(-z))
@@ -151,11 +151,11 @@ def test_softmax_two_expert_closed_form():
 
 def test_router_logits_brute_force():
     rng = np.random.default_rng(4)
-    x = rng.standard_normal((3, 5)); wr = rng.standard_normal((5, 4))
+    x = rng.standard_normal((3, 5)); wr = rng.standard_normal((4, 5))     # [E][H]
     l = O.router_logits(x, wr)
     for t in range(3):
         for e in range(4):
-            assert math.isclose(l[t, e], sum(x[t, h] * wr[h, e] for h in range(5)), rel_tol=1e-12)
+            assert math.isclose(l[t, e], sum(x[t, h] * wr[e, h] for h in range(5)), rel_tol=1e-12)
 
 
 # ----------------------------------------------------- stall-free pins ----
@@ -404,7 +404,7 @@ def test_expert_relabelling_equivariance():
     lay = _small_layer(); cfg = lay.cfg; w = _weights(lay); x = lay.x(); d = _dims(cfg)
     pi = np.random.default_rng(14).permutation(cfg.n_experts)     # new id j holds old expert pi[j]
     w2 = dict(w)
-    w2["w_router"] = w["w_router"][:, pi]
+    w2["w_router"] = w["w_router"][pi]
     for n in ("w_gate", "w_up", "w_down", "lore_A", "lore_B"):
         w2[n] = w[n][pi]
     res = lay.resident()

@@ -29,7 +29,8 @@ Shapes follow the five MoE-layer workloads the pages study:
 Layouts (all row-major, C order):
 
 * ``x``             [T][H]
-* ``w_router``      [H][E]           ``w_prefetch`` [H][E]
+* ``w_router``      [E][H]           ``w_prefetch`` [E][H]  (expert e's row holds
+                    the H weights of its logit, so logits = x W^T)
 * ``w_gate``        [E][I][H]        (output channel i's H-vector contiguous)
 * ``w_up``          [E][I][H]        (dense up only)
 * ``w_down``        [E][H][I] dense; [E][I][H] for the FloE format, whose
@@ -231,10 +232,10 @@ class Layer:
         return full if T is None else full[:T]
 
     def w_router(self) -> np.ndarray:
-        return self._small("w_router", (self.cfg.hidden, self.cfg.n_experts), self.cfg.weight_std)
+        return self._small("w_router", (self.cfg.n_experts, self.cfg.hidden), self.cfg.weight_std)
 
     def w_prefetch(self) -> np.ndarray:
-        return self._small("w_prefetch", (self.cfg.hidden, self.cfg.n_experts), self.cfg.weight_std)
+        return self._small("w_prefetch", (self.cfg.n_experts, self.cfg.hidden), self.cfg.weight_std)
 
     def w_shared_gate(self) -> np.ndarray:
         return self._small("w_shared_gate", (self.cfg.hidden,), self.cfg.weight_std)
