@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "MoE-layer tokens/s at 1 GPU; % HBM BW peak (decode) / % MFMA peak (prefill)"
+PROF_EVERY = 8                 # timed steps between kernel-event samples
 
 
 def parse():
@@ -151,15 +152,18 @@ def measure(name, T, mode, steps, warmup, ev=None, want_roofline=False):
     copies = [w0] + [{n: t.clone() for n, t in w0.items()} for _ in range(n_copies - 1)]
     wstructs = [M.weights_struct(c) for c in copies]
     dom = "floe_up" if mode == "floe" else "expert_gate_up"
+    # events around the dominant kernel on every PROF_EVERY-th timed step:
+    # each record is a timestamp packet that would otherwise add a few
+    # microseconds to every step
     evs = []
-    dbgs = []
+    dbgs = {}
     if ev is not None:
-        for _ in range(steps):
+        for i in range(0, steps, PROF_EVERY):
             a, b = ev.create(), ev.create()
             evs.append((a, b))
             dbg = M.MoeDebug()
             dbg.prof_start, dbg.prof_stop, dbg.prof_kernel = a, b, M.binding.KERNELS[dom]
-            dbgs.append(dbg)
+            dbgs[i] = dbg
 
     def step(i, dbg=None):
         M.moe_layer_forward(dims, T, x, wstructs[i % n_copies], res, stride, mode, out, ws,
@@ -173,7 +177,7 @@ def measure(name, T, mode, steps, warmup, ev=None, want_roofline=False):
     wall0 = time.perf_counter()
     t_start.record()
     for i in range(steps):
-        step(i, dbgs[i] if dbgs else None)
+        step(i, dbgs.get(i))
     t_stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -199,7 +203,7 @@ def measure(name, T, mode, steps, warmup, ev=None, want_roofline=False):
             roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                         frac=achieved / HBM_PEAK_GBS)
         roof.update(traffic=None, kernel=dom, avg_us=avg_us, bytes_per_launch=up["bytes"],
-                    flops_per_launch=up["flops"])
+                    flops_per_launch=up["flops"], launches_timed=len(kms))
         r["roofline"] = roof
         for a, b in evs:
             ev.destroy(a)

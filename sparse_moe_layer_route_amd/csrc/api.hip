@@ -24,7 +24,11 @@ hipError_t launch_shared_gate(const moe_dims_t& d, int T, const void* x, const m
                               float* g_s, hipStream_t s);
 hipError_t launch_ffn_mfma(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
                            const int32_t* offsets, const int32_t* moffsets, const int32_t* perm,
-                           const FfnBuffers& b, int lore, hipStream_t s, int which);
+                           const FfnBuffers& b, int routed, int shared, int lore, hipStream_t s,
+                           int which);
+hipError_t launch_ffn_gemm(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
+                           const int32_t* offsets, const int32_t* perm, bool shared, bf16* act,
+                           float* y, hipStream_t s, int which);
 hipError_t launch_floe(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
                        const int32_t* offsets, const int32_t* perm, float* u, int32_t* keep,
                        float* a, float* part, float* y_perm, uint32_t* flags, const Prof& pf,
@@ -117,6 +121,16 @@ struct Plan {
 // at decode sizes; beyond 64 tokens only hi is kept.
 inline bool split_act(int T) { return T <= 64; }
 
+// The LDS-tiled grouped GEMM takes the routed experts once segments average
+// 64 tokens or more, and the shared experts from 128 tokens on; both need the
+// contraction lengths in whole 64-wide stages.
+inline bool gemm_routed(const moe_dims_t& d, int T) {
+  return (int64_t)T * d.top_k >= 64LL * d.n_experts && d.hidden % 64 == 0 && d.inter % 64 == 0;
+}
+inline bool gemm_shared(const moe_dims_t& d, int T) {
+  return d.n_shared > 0 && T >= 128 && d.hidden % 64 == 0 && d.shared_inter % 64 == 0;
+}
+
 Plan make_plan(const moe_dims_t& d, int T, moe_mode_t mode) {
   Plan p{};
   const size_t P = (size_t)T * d.top_k;
@@ -190,11 +204,20 @@ hipError_t run_ffn(const moe_dims_t& d, int T, const void* x, const moe_weights_
   b.z_lo = (lore && p.use_lo) ? at<bf16>(ws, p.z_lo) : nullptr;
   b.y = y_perm;
   b.ys = y_s;
+  const bool g_r = gemm_routed(d, T), g_s = gemm_shared(d, T);
+  auto stage = [&](int which) {
+    hipError_t r = launch_ffn_mfma(d, T, x, w, offsets, moffsets, perm, b, !g_r, !g_s, lore, s, which);
+    if (r == hipSuccess && g_r)
+      r = launch_ffn_gemm(d, T, x, w, offsets, perm, false, b.act_hi, y_perm, s, which);
+    if (r == hipSuccess && g_s)
+      r = launch_ffn_gemm(d, T, x, w, nullptr, nullptr, true, b.acts_hi, y_s, s, which);
+    return r;
+  };
   hipError_t e = pf.begin(MOE_KERNEL_EXPERT_GATE_UP, s);
-  if (e == hipSuccess) e = launch_ffn_mfma(d, T, x, w, offsets, moffsets, perm, b, lore, s, 1);
+  if (e == hipSuccess) e = stage(1);
   if (e == hipSuccess) e = pf.end(MOE_KERNEL_EXPERT_GATE_UP, s);
   if (e == hipSuccess) e = pf.begin(MOE_KERNEL_EXPERT_DOWN, s);
-  if (e == hipSuccess) e = launch_ffn_mfma(d, T, x, w, offsets, moffsets, perm, b, lore, s, 2);
+  if (e == hipSuccess) e = stage(2);
   if (e == hipSuccess) e = pf.end(MOE_KERNEL_EXPERT_DOWN, s);
   return e;
 }

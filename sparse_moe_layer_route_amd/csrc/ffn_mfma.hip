@@ -27,9 +27,11 @@
 // use_lo = 0 only hi is kept (large token counts, where the second MFMA would
 // make the kernel compute-bound).
 //
-// Work split: a block of 4 waves owns 16*WM rows of one segment; with WK > 1
-// the waves deal the k loop round-robin and reduce through LDS (few rows to
-// spread, e.g. one decode token), else WM = 4 row groups per block.
+// Work split: a block of 4 waves owns 16*WM rows of one segment and WK = 4/WM
+// k-splits: the waves deal the k loop round-robin and reduce through LDS,
+// which keeps the dependent k chain of each wave short.  Each block picks,
+// per chunk of tokens, the smallest instantiation covering its live token
+// tiles, so a 6-token routed segment does not pay for a 64-token shared one.
 #include <algorithm>
 
 #include "common.h"
@@ -103,7 +105,7 @@ __device__ __forceinline__ void nth_segment(const int32_t* __restrict__ offs, in
 }
 
 template <int WM>
-__device__ __forceinline__ TileInfo tile_of(const FfnMfmaArgs& a) {
+__device__ __forceinline__ TileInfo tile_of(const FfnMfmaArgs a) {
   __shared__ int s_e, s_seg0, s_n;
   TileInfo ti;
   int b = blockIdx.x;
@@ -148,7 +150,102 @@ __device__ __forceinline__ void store_hi_lo(bf16* hi, bf16* lo, int64_t off, con
         make_uint2((uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16));
 }
 
+// k-steps loaded together before their MFMAs: enough independent 16-byte
+// loads in flight per wave to cover HBM latency, bounded by registers.
+template <int NA>
+struct Unroll {
+  static constexpr int U = NA <= 2 ? 4 : (NA <= 4 ? 2 : 1);
+};
+
 // ---------------------------------------------------------------- gate+up --
+// One chunk of up to 16*NA tokens of a segment: k loop, LDS reduction over
+// the WK k-splits, epilogue.
+template <int NA, int NTT, int WM, int WK>
+__device__ __forceinline__ void up_chunk(const FfnMfmaArgs a, const TileInfo& ti, int c0,
+                                         const bf16* ag_row, const bf16* au_row, bool gated,
+                                         bool rows_ok, int row_base,
+                                         f32x4_t (*red)[(WK > 1) ? 2 * NTT : 1][MOE_WAVE]) {
+  constexpr int U = Unroll<NA>::U;
+  const int lane = lane_id(), wv = threadIdx.x >> 6, wk = wv / WM;
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int H = a.H, ksteps = H >> 5;
+  const bf16* xrow[NA];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) {
+    int r = c0 + 16 * j + r16;
+    if (r >= ti.n) r = c0;
+    const int tok = ti.kind == 1 ? r : a.perm[ti.seg0 + r] / a.k;
+    xrow[j] = a.x + (int64_t)tok * H + 8 * kg;
+  }
+  f32x4_t accg[NA], accu[NA];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) accg[j] = accu[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (rows_ok) {
+    for (int ks = wk; ks < ksteps; ks += U * WK) {
+      bf16x8_t fg[U], fu[U], fx[U][NA];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kk = ks + u * WK;
+        if (kk < ksteps) {
+          const int ko = kk << 5;
+          fg[u] = frag_load(ag_row + ko);
+          fu[u] = gated ? frag_load(au_row + ko) : fg[u];
+#pragma unroll
+          for (int j = 0; j < NA; ++j) fx[u][j] = frag_load(xrow[j] + ko);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (ks + u * WK < ksteps) {
+#pragma unroll
+          for (int j = 0; j < NA; ++j) {
+            accg[j] = mfma16(fg[u], fx[u][j], accg[j]);
+            if (gated) accu[j] = mfma16(fu[u], fx[u][j], accu[j]);
+          }
+        }
+      }
+    }
+  }
+  if (WK > 1) {
+    if (wk > 0 && rows_ok) {
+#pragma unroll
+      for (int j = 0; j < NA; ++j) {
+        red[wk - 1][2 * j][lane] = accg[j];
+        red[wk - 1][2 * j + 1][lane] = accu[j];
+      }
+    }
+    __syncthreads();
+    if (wk == 0 && rows_ok) {
+#pragma unroll
+      for (int w = 0; w < WK - 1; ++w)
+#pragma unroll
+        for (int j = 0; j < NA; ++j) {
+          accg[j] += red[w][2 * j][lane];
+          accu[j] += red[w][2 * j + 1][lane];
+        }
+    }
+    __syncthreads();
+  }
+  if (wk == 0 && rows_ok) {
+    const int i = row_base + 4 * kg;
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const int r = c0 + 16 * j + r16;
+      if (r < ti.n) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = gated ? silu_f(accg[j][q]) * accu[j][q] : accg[j][q];
+        if (ti.kind == 0)
+          store_hi_lo(a.o_hi, a.o_lo, (int64_t)(ti.seg0 + r) * a.I + i, v);
+        else if (ti.kind == 1)
+          store_hi_lo(a.os_hi, a.os_lo, (int64_t)r * ((int64_t)a.ns * a.Is) + (int64_t)ti.e * a.Is + i, v);
+        else
+          store_hi_lo(a.oz_hi, a.oz_lo, (int64_t)(ti.seg0 + r) * a.r + i, v);
+      }
+    }
+  }
+}
+
 template <int NTT, int WM, int WK>
 __global__ void __launch_bounds__(256) ffn_up_mfma_kernel(FfnMfmaArgs a) {
   static_assert(WM * WK == 4, "four waves per block");
@@ -156,7 +253,7 @@ __global__ void __launch_bounds__(256) ffn_up_mfma_kernel(FfnMfmaArgs a) {
   const TileInfo ti = tile_of<WM>(a);
   if (ti.kind < 0) return;
   const int lane = lane_id(), wv = threadIdx.x >> 6;
-  const int wm = wv % WM, wk = wv / WM;
+  const int wm = wv % WM;
   const int H = a.H;
   const bool gated = ti.kind != 2;
   const int R = ti.kind == 0 ? a.I : (ti.kind == 1 ? a.Is : a.r);
@@ -176,91 +273,21 @@ __global__ void __launch_bounds__(256) ffn_up_mfma_kernel(FfnMfmaArgs a) {
   const int r16 = lane & 15, kg = lane >> 4;
   const bf16* ag_row = wg + (int64_t)(row_base + r16) * H + 8 * kg;
   const bf16* au_row = wu + (int64_t)(row_base + r16) * H + 8 * kg;
-  const int ksteps = H >> 5;
-
   for (int c0 = 0; c0 < ti.n; c0 += 16 * NTT) {
-    const int nt = min(NTT, (ti.n - c0 + 15) >> 4);
-    const bf16* xrow[NTT];
-#pragma unroll
-    for (int j = 0; j < NTT; ++j) {
-      int r = c0 + 16 * j + r16;
-      if (r >= ti.n) r = c0;
-      const int tok = ti.kind == 1 ? r : a.perm[ti.seg0 + r] / a.k;
-      xrow[j] = a.x + (int64_t)tok * H + 8 * kg;
-    }
-    f32x4_t accg[NTT], accu[NTT];
-#pragma unroll
-    for (int j = 0; j < NTT; ++j) accg[j] = accu[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (rows_ok) {
-      int ks = wk;
-      for (; ks + 3 * WK < ksteps; ks += 4 * WK) {
-        bf16x8_t fg[4], fu[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          fg[u] = frag_load(ag_row + ((ks + u * WK) << 5));
-          fu[u] = gated ? frag_load(au_row + ((ks + u * WK) << 5)) : fg[u];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-#pragma unroll
-          for (int j = 0; j < NTT; ++j) {
-            if (j < nt) {
-              const bf16x8_t fx = frag_load(xrow[j] + ((ks + u * WK) << 5));
-              accg[j] = mfma16(fg[u], fx, accg[j]);
-              if (gated) accu[j] = mfma16(fu[u], fx, accu[j]);
-            }
-          }
-        }
-      }
-      for (; ks < ksteps; ks += WK) {
-        const int ko = ks << 5;
-        const bf16x8_t fg = frag_load(ag_row + ko);
-        const bf16x8_t fu = gated ? frag_load(au_row + ko) : fg;
-#pragma unroll
-        for (int j = 0; j < NTT; ++j) {
-          if (j < nt) {
-            const bf16x8_t fx = frag_load(xrow[j] + ko);
-            accg[j] = mfma16(fg, fx, accg[j]);
-            if (gated) accu[j] = mfma16(fu, fx, accu[j]);
-          }
-        }
-      }
-    }
-    if (WK > 1) {
-      if (wk > 0 && rows_ok) {
-#pragma unroll
-        for (int j = 0; j < NTT; ++j) {
-          red[wk - 1][2 * j][lane] = accg[j];
-          red[wk - 1][2 * j + 1][lane] = accu[j];
-        }
-      }
-      __syncthreads();
-      if (wk == 0 && rows_ok) {
-#pragma unroll
-        for (int w = 0; w < WK - 1; ++w)
-#pragma unroll
-          for (int j = 0; j < NTT; ++j) {
-            accg[j] += red[w][2 * j][lane];
-            accu[j] += red[w][2 * j + 1][lane];
-          }
-      }
-      __syncthreads();
-    }
-    if (wk == 0 && rows_ok) {
-      const int i = row_base + 4 * kg;
-#pragma unroll
-      for (int j = 0; j < NTT; ++j) {
-        const int r = c0 + 16 * j + r16;
-        if (j < nt && r < ti.n) {
-          float v[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = gated ? silu_f(accg[j][q]) * accu[j][q] : accg[j][q];
-          if (ti.kind == 0)
-            store_hi_lo(a.o_hi, a.o_lo, (int64_t)(ti.seg0 + r) * a.I + i, v);
-          else if (ti.kind == 1)
-            store_hi_lo(a.os_hi, a.os_lo, (int64_t)r * ((int64_t)a.ns * a.Is) + (int64_t)ti.e * a.Is + i, v);
-          else
-            store_hi_lo(a.oz_hi, a.oz_lo, (int64_t)(ti.seg0 + r) * a.r + i, v);
+    const int nt = min(NTT, (ti.n - c0 + 15) >> 4);  // block-uniform
+    if (nt <= 1) {
+      up_chunk<1, NTT, WM, WK>(a, ti, c0, ag_row, au_row, gated, rows_ok, row_base, red);
+    } else if constexpr (NTT >= 2) {
+      if (nt <= 2) {
+        up_chunk<2, NTT, WM, WK>(a, ti, c0, ag_row, au_row, gated, rows_ok, row_base, red);
+      } else if constexpr (NTT >= 4) {
+        if (nt <= 4) {
+          up_chunk<4, NTT, WM, WK>(a, ti, c0, ag_row, au_row, gated, rows_ok, row_base, red);
+        } else if constexpr (NTT >= 8) {
+          if (nt <= 8)
+            up_chunk<8, NTT, WM, WK>(a, ti, c0, ag_row, au_row, gated, rows_ok, row_base, red);
+          else if constexpr (NTT >= 16)
+            up_chunk<16, NTT, WM, WK>(a, ti, c0, ag_row, au_row, gated, rows_ok, row_base, red);
         }
       }
     }
@@ -268,115 +295,132 @@ __global__ void __launch_bounds__(256) ffn_up_mfma_kernel(FfnMfmaArgs a) {
 }
 
 // ------------------------------------------------------------------- down --
+template <int NA, int NTT, int WM, int WK>
+__device__ __forceinline__ void down_chunk(const FfnMfmaArgs a, const TileInfo& ti, int c0,
+                                           bool rows_ok, int row_base,
+                                           f32x4_t (*red)[(WK > 1) ? NTT : 1][MOE_WAVE]) {
+  constexpr int U = Unroll<NA>::U;
+  const int lane = lane_id(), wv = threadIdx.x >> 6, wk = wv / WM;
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int H = a.H;
+  const int K = ti.kind == 0 ? a.I : (ti.kind == 1 ? a.Is : a.r);
+  const int nsub = ti.kind == 1 ? a.ns : 1;
+  const int64_t ld = ti.kind == 0 ? a.I : (ti.kind == 1 ? (int64_t)a.ns * a.Is : a.r);
+  const bf16* bhi = ti.kind == 0 ? a.act_hi : (ti.kind == 1 ? a.acts_hi : a.z_hi);
+  const bf16* blo = ti.kind == 0 ? a.act_lo : (ti.kind == 1 ? a.acts_lo : a.z_lo);
+  const bool two = a.use_lo != 0;
+  const int kfull = K >> 5;  // full 32-wide steps; K % 8 == 0 may leave a partial one
+  int64_t brow[NA];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) {
+    int r = c0 + 16 * j + r16;
+    if (r >= ti.n) r = c0;
+    brow[j] = (int64_t)(ti.kind == 1 ? r : ti.seg0 + r) * ld + 8 * kg;
+  }
+  f32x4_t acc[NA];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (rows_ok) {
+    for (int s = 0; s < nsub; ++s) {
+      const bf16* wrow;
+      if (ti.kind == 0)
+        wrow = a.w0 + ((int64_t)ti.e * H + row_base + r16) * a.I + 8 * kg;
+      else if (ti.kind == 1)
+        wrow = a.ws0 + ((int64_t)s * H + row_base + r16) * a.Is + 8 * kg;
+      else
+        wrow = a.wl + ((int64_t)ti.e * H + row_base + r16) * a.r + 8 * kg;
+      const int64_t so = ti.kind == 1 ? (int64_t)s * a.Is : 0;
+      for (int ks = wk; ks < kfull; ks += U * WK) {
+        bf16x8_t fw[U], fh[U][NA], fl[U][NA];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int kk = ks + u * WK;
+          if (kk < kfull) {
+            const int ko = kk << 5;
+            fw[u] = frag_load(wrow + ko);
+#pragma unroll
+            for (int j = 0; j < NA; ++j) {
+              fh[u][j] = frag_load(bhi + brow[j] + so + ko);
+              fl[u][j] = two ? frag_load(blo + brow[j] + so + ko) : frag_zero();
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (ks + u * WK < kfull) {
+#pragma unroll
+            for (int j = 0; j < NA; ++j) {
+              acc[j] = mfma16(fw[u], fh[u][j], acc[j]);
+              if (two) acc[j] = mfma16(fw[u], fl[u][j], acc[j]);
+            }
+          }
+        }
+      }
+      // partial last step (K % 32 != 0): lanes whose 8 k values lie past K
+      // feed zeros to both operands
+      if ((K & 31) && wk == kfull % WK) {
+        const int ko = kfull << 5;
+        const bool live = ko + 8 * kg < K;
+        const bf16x8_t fw = live ? frag_load(wrow + ko) : frag_zero();
+#pragma unroll
+        for (int j = 0; j < NA; ++j) {
+          acc[j] = mfma16(fw, live ? frag_load(bhi + brow[j] + so + ko) : frag_zero(), acc[j]);
+          if (two) acc[j] = mfma16(fw, live ? frag_load(blo + brow[j] + so + ko) : frag_zero(), acc[j]);
+        }
+      }
+    }
+  }
+  if (WK > 1) {
+    if (wk > 0 && rows_ok) {
+#pragma unroll
+      for (int j = 0; j < NA; ++j) red[wk - 1][j][lane] = acc[j];
+    }
+    __syncthreads();
+    if (wk == 0 && rows_ok) {
+#pragma unroll
+      for (int w = 0; w < WK - 1; ++w)
+#pragma unroll
+        for (int j = 0; j < NA; ++j) acc[j] += red[w][j][lane];
+    }
+    __syncthreads();
+  }
+  if (wk == 0 && rows_ok) {
+    const int h = row_base + 4 * kg;
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const int r = c0 + 16 * j + r16;
+      if (r < ti.n) {
+        float* dst = ti.kind == 1 ? a.ys + (int64_t)r * H + h : a.y + (int64_t)(ti.seg0 + r) * H + h;
+        *reinterpret_cast<float4*>(dst) = float4{acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+      }
+    }
+  }
+}
+
 template <int NTT, int WM, int WK>
 __global__ void __launch_bounds__(256) ffn_down_mfma_kernel(FfnMfmaArgs a) {
   static_assert(WM * WK == 4, "four waves per block");
   __shared__ f32x4_t red[(WK > 1) ? (WK - 1) : 1][(WK > 1) ? NTT : 1][MOE_WAVE];
   const TileInfo ti = tile_of<WM>(a);
   if (ti.kind < 0) return;
-  const int lane = lane_id(), wv = threadIdx.x >> 6;
-  const int wm = wv % WM, wk = wv / WM;
-  const int H = a.H;
-  const int row_base = ti.row0 + 16 * wm;
-  const bool rows_ok = row_base < H;
-  const int K = ti.kind == 0 ? a.I : (ti.kind == 1 ? a.Is : a.r);
-  const int nsub = ti.kind == 1 ? a.ns : 1;
-  const int r16 = lane & 15, kg = lane >> 4;
-  const int64_t ld = ti.kind == 0 ? a.I : (ti.kind == 1 ? (int64_t)a.ns * a.Is : a.r);
-  const bf16* bhi = ti.kind == 0 ? a.act_hi : (ti.kind == 1 ? a.acts_hi : a.z_hi);
-  const bf16* blo = ti.kind == 0 ? a.act_lo : (ti.kind == 1 ? a.acts_lo : a.z_lo);
-  const bool two = a.use_lo != 0;
-  const int kfull = K >> 5;  // full 32-wide steps; K % 8 == 0 may leave a partial one
-
+  const int wv = threadIdx.x >> 6;
+  const int row_base = ti.row0 + 16 * (wv % WM);
+  const bool rows_ok = row_base < a.H;
   for (int c0 = 0; c0 < ti.n; c0 += 16 * NTT) {
-    const int nt = min(NTT, (ti.n - c0 + 15) >> 4);
-    int64_t brow[NTT];
-#pragma unroll
-    for (int j = 0; j < NTT; ++j) {
-      int r = c0 + 16 * j + r16;
-      if (r >= ti.n) r = c0;
-      brow[j] = (int64_t)(ti.kind == 1 ? r : ti.seg0 + r) * ld + 8 * kg;
-    }
-    f32x4_t acc[NTT];
-#pragma unroll
-    for (int j = 0; j < NTT; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (rows_ok) {
-      for (int s = 0; s < nsub; ++s) {
-        const bf16* wrow;
-        if (ti.kind == 0)
-          wrow = a.w0 + ((int64_t)ti.e * H + row_base + r16) * a.I + 8 * kg;
-        else if (ti.kind == 1)
-          wrow = a.ws0 + ((int64_t)s * H + row_base + r16) * a.Is + 8 * kg;
-        else
-          wrow = a.wl + ((int64_t)ti.e * H + row_base + r16) * a.r + 8 * kg;
-        const int64_t so = ti.kind == 1 ? (int64_t)s * a.Is : 0;
-        int ks = wk;
-        for (; ks + 3 * WK < kfull; ks += 4 * WK) {
-          bf16x8_t fw[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) fw[u] = frag_load(wrow + ((ks + u * WK) << 5));
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int ko = (ks + u * WK) << 5;
-#pragma unroll
-            for (int j = 0; j < NTT; ++j) {
-              if (j < nt) {
-                acc[j] = mfma16(fw[u], frag_load(bhi + brow[j] + so + ko), acc[j]);
-                if (two) acc[j] = mfma16(fw[u], frag_load(blo + brow[j] + so + ko), acc[j]);
-              }
-            }
-          }
-        }
-        for (; ks < kfull; ks += WK) {
-          const int ko = ks << 5;
-          const bf16x8_t fw = frag_load(wrow + ko);
-#pragma unroll
-          for (int j = 0; j < NTT; ++j) {
-            if (j < nt) {
-              acc[j] = mfma16(fw, frag_load(bhi + brow[j] + so + ko), acc[j]);
-              if (two) acc[j] = mfma16(fw, frag_load(blo + brow[j] + so + ko), acc[j]);
-            }
-          }
-        }
-        // partial last step (K % 32 != 0): lanes whose 8 k values lie past K
-        // feed zeros to both operands
-        if ((K & 31) && wk == kfull % WK) {
-          const int ko = kfull << 5;
-          const bool live = ko + 8 * kg < K;
-          const bf16x8_t fw = live ? frag_load(wrow + ko) : frag_zero();
-#pragma unroll
-          for (int j = 0; j < NTT; ++j) {
-            if (j < nt) {
-              acc[j] = mfma16(fw, live ? frag_load(bhi + brow[j] + so + ko) : frag_zero(), acc[j]);
-              if (two)
-                acc[j] = mfma16(fw, live ? frag_load(blo + brow[j] + so + ko) : frag_zero(), acc[j]);
-            }
-          }
-        }
-      }
-    }
-    if (WK > 1) {
-      if (wk > 0 && rows_ok) {
-#pragma unroll
-        for (int j = 0; j < NTT; ++j) red[wk - 1][j][lane] = acc[j];
-      }
-      __syncthreads();
-      if (wk == 0 && rows_ok) {
-#pragma unroll
-        for (int w = 0; w < WK - 1; ++w)
-#pragma unroll
-          for (int j = 0; j < NTT; ++j) acc[j] += red[w][j][lane];
-      }
-      __syncthreads();
-    }
-    if (wk == 0 && rows_ok) {
-      const int h = row_base + 4 * kg;
-#pragma unroll
-      for (int j = 0; j < NTT; ++j) {
-        const int r = c0 + 16 * j + r16;
-        if (j < nt && r < ti.n) {
-          float* dst = ti.kind == 1 ? a.ys + (int64_t)r * H + h : a.y + (int64_t)(ti.seg0 + r) * H + h;
-          *reinterpret_cast<float4*>(dst) = float4{acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+    const int nt = min(NTT, (ti.n - c0 + 15) >> 4);  // block-uniform
+    if (nt <= 1) {
+      down_chunk<1, NTT, WM, WK>(a, ti, c0, rows_ok, row_base, red);
+    } else if constexpr (NTT >= 2) {
+      if (nt <= 2) {
+        down_chunk<2, NTT, WM, WK>(a, ti, c0, rows_ok, row_base, red);
+      } else if constexpr (NTT >= 4) {
+        if (nt <= 4) {
+          down_chunk<4, NTT, WM, WK>(a, ti, c0, rows_ok, row_base, red);
+        } else if constexpr (NTT >= 8) {
+          if (nt <= 8)
+            down_chunk<8, NTT, WM, WK>(a, ti, c0, rows_ok, row_base, red);
+          else if constexpr (NTT >= 16)
+            down_chunk<16, NTT, WM, WK>(a, ti, c0, rows_ok, row_base, red);
         }
       }
     }
@@ -393,11 +437,12 @@ static void launch_kernels(const FfnMfmaArgs& up, const FfnMfmaArgs& dn, int n_u
 // which: bit 0 = gate/up kernel, bit 1 = down kernel.  lore: LoRE tiles on.
 hipError_t launch_ffn_mfma(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
                            const int32_t* offsets, const int32_t* moffsets, const int32_t* perm,
-                           const FfnBuffers& b, int lore, hipStream_t s, int which) {
+                           const FfnBuffers& b, int routed, int shared, int lore, hipStream_t s,
+                           int which) {
   const int ntiles_tok = (T + 15) / 16;  // the largest segment has at most T tokens
   int NTT = 1;
   while (NTT < ntiles_tok && NTT < 16) NTT <<= 1;
-  const int WM = NTT <= 2 ? 1 : 4;
+  const int WM = NTT <= 4 ? 1 : (NTT == 8 ? 2 : 4);
   const int rows = 16 * WM;
   const int slots = std::min(d.n_experts, T * d.top_k);
   FfnMfmaArgs up{};
@@ -433,9 +478,9 @@ hipError_t launch_ffn_mfma(const moe_dims_t& d, int T, const void* x, const moe_
   up.k = d.top_k;
   up.T = T;
   up.use_lo = b.act_lo != nullptr;
-  up.slots_r = slots;
+  up.slots_r = routed ? slots : 0;
   up.tiles_r = (d.inter + rows - 1) / rows;
-  up.n_shared_seg = d.n_shared;
+  up.n_shared_seg = shared ? d.n_shared : 0;
   up.tiles_s = d.n_shared > 0 ? (d.shared_inter + rows - 1) / rows : 0;
   up.slots_l = lore ? slots : 0;
   up.tiles_l = lore ? (d.lore_rank + rows - 1) / rows : 0;
@@ -446,7 +491,7 @@ hipError_t launch_ffn_mfma(const moe_dims_t& d, int T, const void* x, const moe_
   dn.ws1 = nullptr;
   dn.wl = (const bf16*)w.lore_B;
   dn.tiles_r = (d.hidden + rows - 1) / rows;
-  dn.n_shared_seg = d.n_shared > 0 ? 1 : 0;
+  dn.n_shared_seg = (shared && d.n_shared > 0) ? 1 : 0;
   dn.tiles_s = dn.tiles_r;
   dn.tiles_l = lore ? dn.tiles_r : 0;
   const int n_up = up.slots_r * up.tiles_r + up.n_shared_seg * up.tiles_s + up.slots_l * up.tiles_l;
@@ -454,8 +499,8 @@ hipError_t launch_ffn_mfma(const moe_dims_t& d, int T, const void* x, const moe_
   switch (NTT) {
     case 1: launch_kernels<1, 1, 4>(up, dn, n_up, n_dn, s, which); break;
     case 2: launch_kernels<2, 1, 4>(up, dn, n_up, n_dn, s, which); break;
-    case 4: launch_kernels<4, 4, 1>(up, dn, n_up, n_dn, s, which); break;
-    case 8: launch_kernels<8, 4, 1>(up, dn, n_up, n_dn, s, which); break;
+    case 4: launch_kernels<4, 1, 4>(up, dn, n_up, n_dn, s, which); break;
+    case 8: launch_kernels<8, 2, 2>(up, dn, n_up, n_dn, s, which); break;
     default: launch_kernels<16, 4, 1>(up, dn, n_up, n_dn, s, which); break;
   }
   return hipGetLastError();

@@ -9,10 +9,11 @@
 //           order, so logits are bitwise reproducible.
 //           fp32: each wave dots its token with every expert row.
 //   top-k   wave w finishes token w of the tile with lane = expert:
-//           softmax by wave max / sum of exp; k rounds of a 64-bit arg-max on
-//           (order-preserving logit bits, 0xFFFFFFFF - id), so equal logits go
-//           to the lower id; one more round reads the first rejected logit for
-//           the near-tie flag.
+//           softmax by wave max / sum of exp; each lane's rank is the number
+//           of lanes whose key (order-preserving logit bits, 0xFFFFFFFF - id)
+//           is larger, read with E scalar lane reads, so equal logits go to
+//           the lower id; the expert of rank j fills slot j, and the logits
+//           at ranks k-1 and k give the near-tie flag.
 // Stall-free substitution [APEX page, Sec. 4.3, Algorithm 1]: every routed
 // expert outranks every non-routed one, so keeping the prefetched routed
 // experts and filling each miss with the best remaining prefetched expert is
@@ -31,7 +32,25 @@ constexpr int ROUTE_WAVES = 16;
 __device__ __forceinline__ uint64_t topk_key(float l, int e) {
   return ((uint64_t)float_order_key(l) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
 }
-__device__ __forceinline__ int key_id(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
+// Rank of this lane's key among lanes 0..E-1 (0 = largest).  Keys of valid
+// lanes are distinct (the id is part of the key), so ranks are a permutation.
+__device__ __forceinline__ int key_rank(uint64_t key, int E) {
+  const int lo = (int)(uint32_t)key, hi = (int)(uint32_t)(key >> 32);
+  int rank = 0;
+  for (int j = 0; j < E; ++j) {
+    const uint64_t kj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, j) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane(lo, j);
+    rank += kj > key;
+  }
+  return rank;
+}
+
+// Logit of the lane holding rank r (lanes pass their own rank; r < E).
+__device__ __forceinline__ float lane_logit_at_rank(float l, int rank, int r, int E) {
+  const uint64_t hit = __ballot(lane_id() < E && rank == r);
+  const int src = __ffsll((unsigned long long)hit) - 1;
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), src));
+}
 
 struct RouteLds {
   float part[ROUTE_WAVES][ROUTE_TOK][MOE_MAX_EXPERTS];
@@ -149,62 +168,45 @@ route_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w_router, int T,
   const float ex = lane < E ? __expf(l - mx) : 0.f;
   const float denom = wave_sum(ex);
 
-  // routed top-k over all experts
-  uint64_t key = lane < E ? topk_key(l, lane) : 0ull;
-  uint64_t routed = 0ull;
-  float l_last = 0.f;
-  for (int r = 0; r < k; ++r) {
-    const uint64_t m = wave_max_u64(key);
-    const int e = key_id(m);
-    routed |= 1ull << e;
-    if (r == k - 1) l_last = __shfl(l, e, MOE_WAVE);
-    if (lane == e) key = 0ull;
-  }
+  // routed top-k: rank of each expert's key among all experts
+  const uint64_t key = lane < E ? topk_key(l, lane) : 0ull;
+  const int rank = key_rank(key, E);
+  const uint64_t routed = __ballot(lane < E && rank < k);
   uint32_t flag = 0;
-  if (k < E) {
-    const int e = key_id(wave_max_u64(key));
-    if (l_last - __shfl(l, e, MOE_WAVE) < margin) flag |= 1u;
-  }
-  const bool in_routed = lane < E && ((routed >> lane) & 1ull);
+  if (k < E && lane_logit_at_rank(l, rank, k - 1, E) - lane_logit_at_rank(l, rank, k, E) < margin)
+    flag |= 1u;
+  const bool in_routed = lane < E && rank < k;
   const float mass = wave_sum(in_routed ? ex : 0.f) / denom;
 
   uint64_t res_mask = ~0ull;
   if (mode == MOE_MODE_LORE || mode == MOE_MODE_STALL_FREE) res_mask = resident[res_stride * t];
+  const uint64_t all_e = (E == 64) ? ~0ull : ((1ull << E) - 1ull);
 
   // final set: routed, or the top-k inside the prefetched set (stall-free)
-  uint64_t final_set = routed;
+  bool in_final = in_routed;
+  int slot = rank;
   if (mode == MOE_MODE_STALL_FREE && (routed & ~res_mask) != 0ull) {
-    uint64_t allowed = res_mask;
+    uint64_t allowed = res_mask & all_e;
     // fewer than k prefetched experts: the remaining slots take the best
     // experts outside the set (callers pass sets of at least k experts)
-    if (__popcll(allowed & ((E == 64) ? ~0ull : ((1ull << E) - 1ull))) < k) allowed = ~0ull;
-    key = (lane < E && ((allowed >> lane) & 1ull)) ? topk_key(l, lane) : 0ull;
-    final_set = 0ull;
-    for (int r = 0; r < k; ++r) {
-      const uint64_t m = wave_max_u64(key);
-      const int e = key_id(m);
-      final_set |= 1ull << e;
-      if (r == k - 1) l_last = __shfl(l, e, MOE_WAVE);
-      if (lane == e) key = 0ull;
+    if (__popcll(allowed) < k) allowed = all_e;
+    const bool ok = (allowed >> lane) & 1ull;
+    const int mrank = key_rank(ok ? key : 0ull, E);
+    in_final = ok && mrank < k;
+    slot = mrank;
+    if (__popcll(allowed) > k) {
+      const int mr = ok ? mrank : E;
+      if (lane_logit_at_rank(l, mr, k - 1, E) - lane_logit_at_rank(l, mr, k, E) < margin) flag |= 4u;
     }
-    const uint64_t m = wave_max_u64(key);
-    if (m != 0ull && l_last - __shfl(l, key_id(m), MOE_WAVE) < margin) flag |= 4u;
   }
 
   // slots in (-logit, id) order, weights p_e (renormalised over the set)
-  const bool in_final = lane < E && ((final_set >> lane) & 1ull);
   const float fsum = wave_sum(in_final ? ex : 0.f);
-  key = in_final ? topk_key(l, lane) : 0ull;
-  for (int r = 0; r < k; ++r) {
-    const uint64_t m = wave_max_u64(key);
-    const int e = key_id(m);
-    if (lane == e) {
-      key = 0ull;
-      const int64_t o = (int64_t)t * k + r;
-      topk_ids[o] = e;
-      topk_w[o] = renorm ? ex / fsum : ex / denom;
-      exact[o] = (mode == MOE_MODE_LORE) ? (uint8_t)((res_mask >> e) & 1ull) : (uint8_t)1;
-    }
+  if (in_final) {
+    const int64_t o = (int64_t)t * k + slot;
+    topk_ids[o] = lane;
+    topk_w[o] = renorm ? ex / fsum : ex / denom;
+    exact[o] = (mode == MOE_MODE_LORE) ? (uint8_t)((res_mask >> lane) & 1ull) : (uint8_t)1;
   }
   if (lane == 0) {
     flags[t] = flag;
@@ -227,21 +229,11 @@ prefetch_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w_p, int T, i
   const float l = lane < E ? lds.logits[wv][lane] : -INFINITY;
   int n = k + delta[t];
   n = n < 1 ? 1 : (n > E ? E : n);
-  uint64_t key = lane < E ? topk_key(l, lane) : 0ull;
-  uint64_t mask = 0ull;
-  float l_last = 0.f;
-  for (int r = 0; r < n; ++r) {
-    const uint64_t m = wave_max_u64(key);
-    const int e = key_id(m);
-    mask |= 1ull << e;
-    if (r == n - 1) l_last = __shfl(l, e, MOE_WAVE);
-    if (lane == e) key = 0ull;
-  }
+  const int rank = key_rank(lane < E ? topk_key(l, lane) : 0ull, E);
+  const uint64_t mask = __ballot(lane < E && rank < n);
   uint32_t flag = 0;
-  if (n < E) {
-    const int e = key_id(wave_max_u64(key));
-    if (l_last - __shfl(l, e, MOE_WAVE) < margin) flag = 2u;
-  }
+  if (n < E && lane_logit_at_rank(l, rank, n - 1, E) - lane_logit_at_rank(l, rank, n, E) < margin)
+    flag = 2u;
   if (lane == 0) {
     mask_out[t] = mask;
     flags[t] = flag;

@@ -42,6 +42,11 @@ SMALL = {
                             seed=102),
     "granite_small": _variant("granite_prefill", name="granite_small", hidden=384, n_experts=40,
                               inter=144, token_counts=(203,), seed=103),
+    # prefill-sized segments (grouped GEMM path): ~150 tokens per expert,
+    # ragged m- and n-tiles, a shared expert of 320 channels over 300 tokens
+    "prefill_small": _variant("dsv2_lite", name="prefill_small", hidden=256, n_experts=4, top_k=2,
+                              inter=192, n_shared=1, shared_inter=320, token_counts=(300,),
+                              resident_count=2, seed=106),
 }
 FLOE_SMALL = {
     "floe_small": _variant("mixtral_floe", name="floe_small", hidden=1024, n_experts=4, inter=1040,
@@ -73,6 +78,7 @@ def _check_full(layer, T, mode, sample=None, dims_over=None):
     ("dsv2_small", "standard"), ("dsv2_small", "lore"),
     ("qwen2_small", "standard"), ("qwen2_small", "lore"),
     ("granite_small", "standard"), ("granite_small", "stall_free"),
+    ("prefill_small", "standard"), ("prefill_small", "lore"),
 ])
 def test_small_layer_parity(name, mode):
     layer = W.Layer(SMALL[name])
