@@ -28,7 +28,8 @@ hipError_t launch_ffn_mfma(const moe_dims_t& d, int T, const void* x, const moe_
                            int which);
 hipError_t launch_ffn_gemm(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
                            const int32_t* offsets, const int32_t* perm, bool shared, bf16* act,
-                           float* y, hipStream_t s, int which);
+                           float* y, float* part, hipStream_t s, int which);
+int gemm_shared_down_ksplit(const moe_dims_t& d, int T);
 hipError_t launch_floe(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
                        const int32_t* offsets, const int32_t* perm, float* u, int32_t* keep,
                        float* a, float* part, float* y_perm, uint32_t* flags, const Prof& pf,
@@ -113,6 +114,7 @@ struct Plan {
   size_t act, act_s;                                                  // fp32 GEMV activations
   size_t act_hi, act_lo, acts_hi, acts_lo, z_hi, z_lo;                // bf16 MFMA activations
   size_t u, keep, fa, part;                                           // FloE
+  size_t ys_part;                                                     // shared down k-split
   bool use_lo;
   size_t total;
 };
@@ -172,6 +174,10 @@ Plan make_plan(const moe_dims_t& d, int T, moe_mode_t mode) {
     p.y_s = take((size_t)T * H * 4);
     p.g_s = take((size_t)T * 4);
   }
+  if (mode != MOE_MODE_FLOE && d.dtype == MOE_BF16 && gemm_shared(d, T)) {
+    const int ks = gemm_shared_down_ksplit(d, T);
+    if (ks > 1) p.ys_part = take((size_t)ks * T * H * 4);
+  }
   p.total = o;
   return p;
 }
@@ -208,9 +214,10 @@ hipError_t run_ffn(const moe_dims_t& d, int T, const void* x, const moe_weights_
   auto stage = [&](int which) {
     hipError_t r = launch_ffn_mfma(d, T, x, w, offsets, moffsets, perm, b, !g_r, !g_s, lore, s, which);
     if (r == hipSuccess && g_r)
-      r = launch_ffn_gemm(d, T, x, w, offsets, perm, false, b.act_hi, y_perm, s, which);
+      r = launch_ffn_gemm(d, T, x, w, offsets, perm, false, b.act_hi, y_perm, nullptr, s, which);
     if (r == hipSuccess && g_s)
-      r = launch_ffn_gemm(d, T, x, w, nullptr, nullptr, true, b.acts_hi, y_s, s, which);
+      r = launch_ffn_gemm(d, T, x, w, nullptr, nullptr, true, b.acts_hi, y_s,
+                          p.ys_part ? at<float>(ws, p.ys_part) : nullptr, s, which);
     return r;
   };
   hipError_t e = pf.begin(MOE_KERNEL_EXPERT_GATE_UP, s);

@@ -6,13 +6,23 @@
 //   GEMM2 (down):     Y = W_d act^T                 stored fp32 [pair][H]
 // [FloE page, Sec. 1, forward a^S(x) with S_t = identity.]
 //
-// Block tile: 128 weight rows (M) x 128 tokens (N) x 64 k per stage, 4 waves
-// in a 2 x 2 grid, each wave 64 x 64 = 4 x 4 MFMA tiles (x2 for gate and up).
-// A (weights) and B (token rows, gathered through the permutation) are both
-// k-contiguous in HBM; each stage is copied global -> registers -> LDS with
-// 16-byte loads while the previous stage feeds the MFMAs (double-buffered
-// LDS, one barrier per stage).  LDS rows are padded to 72 elements so the
-// 16 lanes reading one fragment column hit distinct banks.
+// Block tile: 256 tokens (N) x 256 weight rows (M: 128 gate + 128 up, or 256
+// down) x 32 k per stage, 4 waves in a 2 x 2 grid, each wave 128 x 128
+// outputs = 8 x 8 MFMA tiles held in 256 accumulator registers.  Per stage a
+// wave reads 16 fragments (16 KiB) from LDS for 64 MFMAs; a block pulls
+// 32 KiB per stage from L2 for 4.2 MFLOP (128 flop/B).  A (weights) and B
+// (token rows, gathered through the permutation) are both k-contiguous in
+// HBM.  Stages move global -> LDS directly (16-byte LDS DMA loads, no
+// register staging) into a 4-deep ring, so three stages are in flight while
+// one feeds the MFMAs: the L2/HBM latency of a stage (microseconds under load)
+// is covered by three stages of math.  Each 64-byte LDS row holds four
+// 16-byte k chunks stored at chunk ^ ((row / 4) % 4), so the 16 lanes reading
+// one fragment column hit distinct banks.  Ordering is explicit: a thread
+// waits for its own DMA loads with a vmcnt wait, then a workgroup barrier
+// publishes the stage; a slot is refilled only after the barrier that ends
+// its last read.  A long contraction over few tiles (the shared experts' down
+// projection at a few hundred tokens) is split over grid.y into partial sums
+// that a small kernel adds up.
 //
 // Tiles are (segment m-tile, weight n-tile) pairs enumerated expert by expert;
 // block ids are remapped so each XCD (blocks are dealt to the 8 XCDs round-
@@ -27,10 +37,10 @@ namespace moe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int GM = 128;        // weight rows per block tile
-constexpr int GN = 128;        // tokens per block tile
-constexpr int GK = 64;         // k per stage
-constexpr int GLD = GK + 8;    // padded LDS row (elements)
+constexpr int GN = 256;        // tokens per block tile
+constexpr int GK = 32;         // k per stage
+constexpr int GSTAGES = 4;     // LDS ring depth (stages in flight: GSTAGES - 1)
+constexpr int GROWS = 512;     // LDS rows per stage: 256 weight + 256 token
 constexpr int GTHREADS = 256;
 constexpr int NXCD = 8;
 
@@ -54,12 +64,33 @@ struct GemmArgs {
   int R, K;             // weight rows (output width), contraction length
   int G;                // groups: experts (routed) or shared experts
   int T;
-  int tiles_n;          // R / GM (rounded up)
+  int tiles_n;          // weight-row tiles (128 gate+up rows or 256 down rows)
+  int ksplit;           // GEMM2: k-stage ranges (grid.y); partial sums to y_out + y * part_stride
+  int64_t part_stride;
   int n_blocks;         // grid size (upper bound of tiles)
 };
 
-__device__ __forceinline__ bf16x8_t lds_frag(const bf16* p) {
-  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte LDS read issued as an instruction the compiler's wait-count pass
+// does not track: the ring's DMA writes are ordered by explicit waits and
+// barriers instead (the pass would otherwise drain every DMA in flight before
+// each read).  Results are used only after lds_wait_all.
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+  return r;
+}
+
+// Wait for this wave's LDS reads; the fragments are in/out operands so no
+// use of them can be scheduled above the wait.
+template <int NA, int NB>
+__device__ __forceinline__ void lds_wait_all(u32x4 (&b)[NB], u32x4 (&a)[NA]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < NB; ++j) asm volatile("" : "+v"(b[j]));
+#pragma unroll
+  for (int i = 0; i < NA; ++i) asm volatile("" : "+v"(a[i]));
 }
 
 // Block id -> logical tile id with each XCD owning a contiguous range.
@@ -112,132 +143,134 @@ __device__ __forceinline__ bool find_mtile(const GemmArgs a, int m_idx, MTile& m
   return mt.g >= 0;
 }
 
-// GATED: GEMM1 (two weight matrices, SiLU product, bf16 out); else GEMM2.
+// Wait until at most N of this wave's vector-memory operations are pending
+// (LDS DMA loads complete in issue order).
+#define GEMM_VMCNT(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
+
+// GATED: GEMM1 (gate and up matrices, 128 rows each, SiLU product, bf16 out);
+// else GEMM2 (256 down rows, fp32 out).  Either way a block stages 256 weight
+// rows and 256 token rows per 32-wide k stage, and each wave owns a 128 x 128
+// output tile (8 x 8 MFMA tiles, 256 fp32 accumulators per lane).
 template <bool GATED>
 __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
-  constexpr int NW = GATED ? 2 : 1;
-  __shared__ bf16 lds_w[2][NW][GM][GLD];
-  __shared__ bf16 lds_x[2][GN][GLD];
+  constexpr int NW = GATED ? 2 : 1;          // weight matrices
+  constexpr int MW = GATED ? 128 : 256;      // weight rows per matrix per block
+  constexpr int WT = MW / 2 / 16;            // weight tiles per wave per matrix (4 or 8)
+  __shared__ __attribute__((aligned(16))) bf16 lds[GSTAGES][GROWS * GK];
   const int tile = xcd_tile(blockIdx.x, a.n_blocks);
   if (tile >= a.n_blocks) return;
   const int m_idx = tile / a.tiles_n, n_idx = tile % a.tiles_n;
   MTile mt;
   if (!find_mtile(a, m_idx, mt)) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv & 1, wn = wv >> 1;     // 2 x 2 waves
+  const int wm = wv & 1, wn = wv >> 1;       // 2 x 2 waves: weight half, token half
   const int r16 = lane & 15, kg = lane >> 4;
-  const int row_w0 = n_idx * GM;           // first weight row of the tile
+  const int row_w0 = n_idx * MW;             // first weight row of the tile
 
-  // global -> LDS copy plan: chunk c (16 B) = row c/8, k-chunk c%8; 1024
-  // chunks per 128x64 tile, 4 per thread per matrix
-  const bf16* wsrc[NW][4];
-  const bf16* xsrc[4];
-  int crow[4], ccol[4];
+  // DMA plan: a stage is 512 LDS rows x 64 B; one wave instruction writes 16
+  // rows (1 KiB, lane l -> row l/4, 16-byte slot l%4).  Wave w issues
+  // instructions 8w..8w+7: waves 0-1 the weight rows (GATED: 0-127 gate,
+  // 128-255 up), waves 2-3 the token rows.  Slot p of row r holds k chunk
+  // p ^ ((r/4) % 4), so the 16 rows of one fragment read hit distinct banks.
+  const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
+  const bf16* base_w0 = a.w0 + (int64_t)mt.g * a.w_stride;
+  const bf16* base_w1 = GATED ? a.w1 + (int64_t)mt.g * a.w_stride : base_w0;
+  const bf16* base_x = GATED ? a.x : a.act_in;
+  const bool is_w = wv < 2;
+  const bf16* dma_base = is_w ? ((GATED && wv == 1) ? base_w1 : base_w0) : base_x;
+  int off[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + GTHREADS * i;
-    crow[i] = c >> 3;
-    ccol[i] = (c & 7) * 8;
-    const int wr = min(row_w0 + crow[i], a.R - 1);
-#pragma unroll
-    for (int m = 0; m < NW; ++m) {
-      const bf16* base = (m == 0 ? a.w0 : a.w1) + (int64_t)mt.g * a.w_stride;
-      wsrc[m][i] = base + (int64_t)wr * a.K + ccol[i];
-    }
-    const int r = min(mt.row0 + crow[i], mt.n - 1);
-    if (GATED) {
-      const int tok = a.offsets ? a.perm[mt.seg0 + r] / a.k : r;
-      xsrc[i] = a.x + (int64_t)tok * a.K + ccol[i];
+  for (int q = 0; q < 8; ++q) {
+    const int row = 16 * (8 * wv + q) + (lane >> 2);   // LDS row 0..511
+    if (is_w) {
+      const int r = GATED ? (row & 127) : row;
+      off[q] = min(row_w0 + r, a.R - 1) * a.K + 8 * chunk;
     } else {
-      xsrc[i] = a.act_in + (int64_t)(mt.seg0 + r) * a.ld_in + ccol[i];
+      const int r = min(mt.row0 + (row - 256), mt.n - 1);
+      if (GATED) {
+        const int tok = a.offsets ? a.perm[mt.seg0 + r] / a.k : r;
+        off[q] = tok * a.K + 8 * chunk;
+      } else {
+        off[q] = (mt.seg0 + r) * (int)a.ld_in + 8 * chunk;
+      }
     }
   }
 
-  f32x4_t acc[NW][4][4];
+  f32x4_t acc[NW][WT][8];
 #pragma unroll
   for (int m = 0; m < NW; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WT; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[m][i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 8; ++j) acc[m][i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nsub = GATED ? 1 : a.n_sub;
-  const int kst = a.K / GK;          // K % 64 == 0 on this path
+  const int kst = a.K / GK;          // K % 32 == 0 on this path
   const int nst = nsub * kst;
-  // one stage in flight per thread: 4 chunks of gate (or down), up, token rows
-  uint4 w0a, w0b, w0c, w0d, w1a, w1b, w1c, w1d, xa, xb, xc, xd;
-  auto gload = [&](int st) __attribute__((always_inline)) {
-    const int s_ = st / kst, ko_ = (st % kst) * GK;
-    const int64_t wo = (int64_t)s_ * a.sub_stride + ko_;
-    const int64_t xo = (int64_t)s_ * a.sub_k_off + ko_;
-    w0a = *reinterpret_cast<const uint4*>(wsrc[0][0] + wo);
-    w0b = *reinterpret_cast<const uint4*>(wsrc[0][1] + wo);
-    w0c = *reinterpret_cast<const uint4*>(wsrc[0][2] + wo);
-    w0d = *reinterpret_cast<const uint4*>(wsrc[0][3] + wo);
-    if constexpr (GATED) {
-      w1a = *reinterpret_cast<const uint4*>(wsrc[NW - 1][0] + wo);
-      w1b = *reinterpret_cast<const uint4*>(wsrc[NW - 1][1] + wo);
-      w1c = *reinterpret_cast<const uint4*>(wsrc[NW - 1][2] + wo);
-      w1d = *reinterpret_cast<const uint4*>(wsrc[NW - 1][3] + wo);
-    }
-    xa = *reinterpret_cast<const uint4*>(xsrc[0] + xo);
-    xb = *reinterpret_cast<const uint4*>(xsrc[1] + xo);
-    xc = *reinterpret_cast<const uint4*>(xsrc[2] + xo);
-    xd = *reinterpret_cast<const uint4*>(xsrc[3] + xo);
-  };
-  auto lstore = [&](int buf) __attribute__((always_inline)) {
-    *reinterpret_cast<uint4*>(&lds_w[buf][0][crow[0]][ccol[0]]) = w0a;
-    *reinterpret_cast<uint4*>(&lds_w[buf][0][crow[1]][ccol[1]]) = w0b;
-    *reinterpret_cast<uint4*>(&lds_w[buf][0][crow[2]][ccol[2]]) = w0c;
-    *reinterpret_cast<uint4*>(&lds_w[buf][0][crow[3]][ccol[3]]) = w0d;
-    if constexpr (GATED) {
-      *reinterpret_cast<uint4*>(&lds_w[buf][NW - 1][crow[0]][ccol[0]]) = w1a;
-      *reinterpret_cast<uint4*>(&lds_w[buf][NW - 1][crow[1]][ccol[1]]) = w1b;
-      *reinterpret_cast<uint4*>(&lds_w[buf][NW - 1][crow[2]][ccol[2]]) = w1c;
-      *reinterpret_cast<uint4*>(&lds_w[buf][NW - 1][crow[3]][ccol[3]]) = w1d;
-    }
-    *reinterpret_cast<uint4*>(&lds_x[buf][crow[0]][ccol[0]]) = xa;
-    *reinterpret_cast<uint4*>(&lds_x[buf][crow[1]][ccol[1]]) = xb;
-    *reinterpret_cast<uint4*>(&lds_x[buf][crow[2]][ccol[2]]) = xc;
-    *reinterpret_cast<uint4*>(&lds_x[buf][crow[3]][ccol[3]]) = xd;
-  };
+  const int per = (nst + a.ksplit - 1) / a.ksplit;
+  const int k_lo = a.ksplit > 1 ? blockIdx.y * per : 0;
+  const int k_hi = a.ksplit > 1 ? min(nst, k_lo + per) : nst;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nst) gload(st + 1);
+  // Every step issues exactly 8 DMA loads per thread (stages past the range
+  // reload the last stage into a slot nobody reads again), so "stage s+1 has
+  // landed" is always "at most 16 of this thread's loads pending".
+  auto issue = [&](int st) __attribute__((always_inline)) {
+    bf16* dst = &lds[st % GSTAGES][(16 * 8 * wv) * GK];
+    st = min(st, k_hi - 1);
+    const int s_ = st / kst, ko = (st % kst) * GK;
+    const bf16* src = dma_base + (is_w ? (int64_t)s_ * a.sub_stride : (int64_t)s_ * a.sub_k_off) + ko;
 #pragma unroll
-    for (int kk = 0; kk < GK; kk += 32) {
-      bf16x8_t fa[NW][4], fb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int m = 0; m < NW; ++m)
-          fa[m][i] = lds_frag(&lds_w[buf][m][wm * 64 + 16 * i + r16][kk + 8 * kg]);
-        fb[i] = lds_frag(&lds_x[buf][wn * 64 + 16 * i + r16][kk + 8 * kg]);
-      }
-#pragma unroll
-      for (int m = 0; m < NW; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[m][i], fb[j], acc[m][i][j], 0, 0, 0);
-    }
-    if (st + 1 < nst) lstore(buf ^ 1);
-    __syncthreads();
+    for (int q = 0; q < 8; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(src + off[q]),
+                                       (__attribute__((address_space(3))) void*)(dst + q * 16 * GK),
+                                       16, 0, 0);
+  };
+  // byte address of this lane's fragment slot: logical chunk kg of row r
+  // lives at physical chunk kg ^ ((r/4) % 4); rows here are 16-aligned + r16
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)&lds[0][0];
+  const uint32_t lane_off = (uint32_t)(r16 * GK * 2 + ((kg ^ ((r16 >> 2) & 3)) * 16));
+
+  if (k_lo < k_hi) {
+    issue(k_lo);
+    issue(k_lo + 1);
+    issue(k_lo + 2);
+    GEMM_VMCNT(16);
   }
+  __builtin_amdgcn_s_barrier();
+  for (int st = k_lo; st < k_hi; ++st) {
+    issue(st + GSTAGES - 1);
+    const uint32_t sl = lds0 + (uint32_t)((st % GSTAGES) * GROWS * GK * 2) + lane_off;
+    u32x4 fb[8], fa[NW * WT];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fb[j] = lds_read16(sl + (uint32_t)((256 + wn * 128 + 16 * j) * GK * 2));
+#pragma unroll
+    for (int m = 0; m < NW; ++m)
+#pragma unroll
+      for (int i = 0; i < WT; ++i)
+        fa[m * WT + i] = lds_read16(sl + (uint32_t)((m * MW + wm * (MW / 2) + 16 * i) * GK * 2));
+    lds_wait_all(fb, fa);
+#pragma unroll
+    for (int m = 0; m < NW; ++m)
+#pragma unroll
+      for (int i = 0; i < WT; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, fa[m * WT + i]), __builtin_bit_cast(bf16x8_t, fb[j]),
+              acc[m][i][j], 0, 0, 0);
+    GEMM_VMCNT(16);   // this thread's loads for stage st+1 have landed
+    __builtin_amdgcn_s_barrier();
+  }
+  GEMM_VMCNT(0);      // no DMA may outlive the workgroup's LDS
 
   // epilogue: lane holds weight rows 4*kg..+3 of tile i, token r16 of tile j
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int tr = mt.row0 + wn * 64 + 16 * j + r16;   // token row within segment
+  for (int j = 0; j < 8; ++j) {
+    const int tr = mt.row0 + wn * 128 + 16 * j + r16;   // token row within segment
     if (tr >= mt.n) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int wr = row_w0 + wm * 64 + 16 * i + 4 * kg;
+    for (int i = 0; i < WT; ++i) {
+      const int wr = row_w0 + wm * (MW / 2) + 16 * i + 4 * kg;
       if (wr >= a.R) continue;
       if (GATED) {
         uint32_t h[4];
@@ -246,19 +279,45 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
         bf16* dst = a.act_out + (int64_t)(mt.seg0 + tr) * a.ld_out + (int64_t)mt.g * a.col_off + wr;
         *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
       } else {
-        float* dst = a.y_out + (int64_t)(mt.seg0 + tr) * a.R + wr;
+        float* dst = a.y_out + (int64_t)blockIdx.y * a.part_stride + (int64_t)(mt.seg0 + tr) * a.R + wr;
         *reinterpret_cast<float4*>(dst) =
             float4{acc[0][i][j][0], acc[0][i][j][1], acc[0][i][j][2], acc[0][i][j][3]};
       }
     }
   }
 }
+#undef GEMM_VMCNT
+
+// Sum of k-split partials: y[i] = sum_s part[s][i] (float4 per thread).
+__global__ void __launch_bounds__(256)
+ksplit_reduce_kernel(const float* __restrict__ part, int64_t n4, int64_t stride, int ns,
+                     float* __restrict__ y) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  float4 acc = reinterpret_cast<const float4*>(part)[i];
+  for (int s = 1; s < ns; ++s) {
+    const float4 v = reinterpret_cast<const float4*>(part + s * stride)[i];
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  reinterpret_cast<float4*>(y)[i] = acc;
+}
+
+// k-splits of the shared experts' down GEMM: enough blocks to cover the CUs
+// when there are few (token, row) tiles and a long contraction.
+int gemm_shared_down_ksplit(const moe_dims_t& d, int T) {
+  const int tiles = ((T + GN - 1) / GN) * ((d.hidden + 255) / 256);
+  const int nst = d.n_shared * (d.shared_inter / GK);
+  int ks = 256 / (tiles > 0 ? tiles : 1);
+  ks = ks < 1 ? 1 : (ks > nst ? nst : ks);
+  return ks;
+}
 
 // Routed experts (offsets != nullptr) or shared experts (offsets == nullptr).
-// GEMM1 writes bf16 act (routed [P][I], shared [T][ns*Is]); GEMM2 writes fp32 y.
+// GEMM1 writes bf16 act (routed [P][I], shared [T][ns*Is]); GEMM2 writes fp32
+// y (shared: through k-split partials in `part`, then summed).
 hipError_t launch_ffn_gemm(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
                            const int32_t* offsets, const int32_t* perm, bool shared, bf16* act,
-                           float* y, hipStream_t s, int which) {
+                           float* y, float* part, hipStream_t s, int which) {
   const int H = d.hidden, E = d.n_experts;
   const int R1 = shared ? d.shared_inter : d.inter;     // GEMM1 rows
   const int G = shared ? d.n_shared : E;
@@ -282,8 +341,9 @@ hipError_t launch_ffn_gemm(const moe_dims_t& d, int T, const void* x, const moe_
     a.K = H;
     a.G = G;
     a.T = T;
-    a.tiles_n = (R1 + GM - 1) / GM;
+    a.tiles_n = (R1 + 127) / 128;            // 128 gate + 128 up rows per block
     a.n_blocks = mt_max * a.tiles_n;
+    a.ksplit = 1;
     const int grid = ((a.n_blocks + NXCD - 1) / NXCD) * NXCD;
     if (a.n_blocks > 0) ffn_gemm_kernel<true><<<grid, GTHREADS, 0, s>>>(a);
   }
@@ -297,7 +357,6 @@ hipError_t launch_ffn_gemm(const moe_dims_t& d, int T, const void* x, const moe_
     a.n_sub = shared ? d.n_shared : 1;
     a.ld_in = shared ? (int64_t)d.n_shared * d.shared_inter : d.inter;
     a.sub_k_off = shared ? d.shared_inter : 0;
-    a.y_out = y;
     a.offsets = shared ? nullptr : offsets;
     a.perm = perm;
     a.k = d.top_k;
@@ -305,11 +364,19 @@ hipError_t launch_ffn_gemm(const moe_dims_t& d, int T, const void* x, const moe_
     a.K = R1;
     a.G = shared ? 1 : E;      // shared: one segment of T tokens, sub-matrices summed
     a.T = T;
-    a.tiles_n = (H + GM - 1) / GM;
+    a.tiles_n = (H + 255) / 256;             // 256 down rows per block
     const int mt2 = shared ? (T + GN - 1) / GN : mt_max;
     a.n_blocks = mt2 * a.tiles_n;
+    a.ksplit = shared ? gemm_shared_down_ksplit(d, T) : 1;
+    a.y_out = a.ksplit > 1 ? part : y;
+    a.part_stride = (int64_t)T * H;
     const int grid = ((a.n_blocks + NXCD - 1) / NXCD) * NXCD;
-    if (a.n_blocks > 0) ffn_gemm_kernel<false><<<grid, GTHREADS, 0, s>>>(a);
+    if (a.n_blocks > 0) ffn_gemm_kernel<false><<<dim3(grid, a.ksplit), GTHREADS, 0, s>>>(a);
+    if (a.ksplit > 1) {
+      const int64_t n4 = (int64_t)T * H / 4;
+      ksplit_reduce_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>(part, n4, a.part_stride,
+                                                                         a.ksplit, y);
+    }
   }
   return hipGetLastError();
 }
