@@ -152,7 +152,7 @@ def step_traffic(cfg, T, mode, ids, exact, keep_count=None):
         f += T * 2 * 3 * sh * H
         b += len(miss_experts) * 2 * cfg.lore_rank * H * eb
         f += int((1 - exact).sum()) * 2 * 2 * cfg.lore_rank * H
-        act_b = 4 if (eb == 4 or T <= 64) else 2       # bf16 hi+lo up to 64 tokens, else hi
+        act_b = eb                                     # activations in the layer's dtype
         n_miss = int((1 - exact).sum())
         r = cfg.lore_rank
         up = dict(bytes=(len(exact_experts) * 2 * I * H + 2 * sh * H + len(miss_experts) * r * H) * eb

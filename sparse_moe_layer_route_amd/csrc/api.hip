@@ -112,16 +112,11 @@ struct Plan {
   size_t ids, w, exact, flags, offsets, moffsets, perm, inv, row_of;  // routing + permutation
   size_t y_perm, y_s, g_s;                                            // FFN outputs
   size_t act, act_s;                                                  // fp32 GEMV activations
-  size_t act_hi, act_lo, acts_hi, acts_lo, z_hi, z_lo;                // bf16 MFMA activations
+  size_t act_b, acts_b, z_b;                                          // bf16 MFMA activations
   size_t u, keep, fa, part;                                           // FloE
   size_t ys_part;                                                     // shared down k-split
-  bool use_lo;
   size_t total;
 };
-
-// bf16 hi + lo activations keep ~16 significant bits for the down projection
-// at decode sizes; beyond 64 tokens only hi is kept.
-inline bool split_act(int T) { return T <= 64; }
 
 // The LDS-tiled grouped GEMM takes the routed experts once segments average
 // 64 tokens or more, and the shared experts from 128 tokens on; both need the
@@ -149,23 +144,15 @@ Plan make_plan(const moe_dims_t& d, int T, moe_mode_t mode) {
   p.inv = take(P * 4);
   p.row_of = take(P * 4);
   p.y_perm = take(P * H * 4);
-  p.use_lo = split_act(T);
   if (mode == MOE_MODE_FLOE) {
     p.u = take(P * I * 4);
     p.keep = take(P * (size_t)d.floe_keep * 4);
     p.fa = take(P * (size_t)d.floe_keep * 4);
     p.part = take((size_t)floe_slices(d.floe_keep) * P * H * 4);
   } else if (d.dtype == MOE_BF16) {
-    p.act_hi = take(P * I * 2);
-    if (p.use_lo) p.act_lo = take(P * I * 2);
-    if (S) {
-      p.acts_hi = take((size_t)T * S * 2);
-      if (p.use_lo) p.acts_lo = take((size_t)T * S * 2);
-    }
-    if (mode == MOE_MODE_LORE) {
-      p.z_hi = take(P * (size_t)d.lore_rank * 2);
-      if (p.use_lo) p.z_lo = take(P * (size_t)d.lore_rank * 2);
-    }
+    p.act_b = take(P * I * 2);
+    if (S) p.acts_b = take((size_t)T * S * 2);
+    if (mode == MOE_MODE_LORE) p.z_b = take(P * (size_t)d.lore_rank * 2);
   } else {
     p.act = take(P * I * 4);
     if (S) p.act_s = take((size_t)T * S * 4);
@@ -202,21 +189,18 @@ hipError_t run_ffn(const moe_dims_t& d, int T, const void* x, const moe_weights_
                             d.n_shared > 0 ? at<float>(ws, p.act_s) : nullptr, y_s, pf, s);
   const bool sh = d.n_shared > 0;
   FfnBuffers b{};
-  b.act_hi = at<bf16>(ws, p.act_hi);
-  b.act_lo = p.use_lo ? at<bf16>(ws, p.act_lo) : nullptr;
-  b.acts_hi = sh ? at<bf16>(ws, p.acts_hi) : nullptr;
-  b.acts_lo = (sh && p.use_lo) ? at<bf16>(ws, p.acts_lo) : nullptr;
-  b.z_hi = lore ? at<bf16>(ws, p.z_hi) : nullptr;
-  b.z_lo = (lore && p.use_lo) ? at<bf16>(ws, p.z_lo) : nullptr;
+  b.act = at<bf16>(ws, p.act_b);
+  b.acts = sh ? at<bf16>(ws, p.acts_b) : nullptr;
+  b.z = lore ? at<bf16>(ws, p.z_b) : nullptr;
   b.y = y_perm;
   b.ys = y_s;
   const bool g_r = gemm_routed(d, T), g_s = gemm_shared(d, T);
   auto stage = [&](int which) {
     hipError_t r = launch_ffn_mfma(d, T, x, w, offsets, moffsets, perm, b, !g_r, !g_s, lore, s, which);
     if (r == hipSuccess && g_r)
-      r = launch_ffn_gemm(d, T, x, w, offsets, perm, false, b.act_hi, y_perm, nullptr, s, which);
+      r = launch_ffn_gemm(d, T, x, w, offsets, perm, false, b.act, y_perm, nullptr, s, which);
     if (r == hipSuccess && g_s)
-      r = launch_ffn_gemm(d, T, x, w, nullptr, nullptr, true, b.acts_hi, y_s,
+      r = launch_ffn_gemm(d, T, x, w, nullptr, nullptr, true, b.acts, y_s,
                           p.ys_part ? at<float>(ws, p.ys_part) : nullptr, s, which);
     return r;
   };

@@ -94,10 +94,10 @@ __device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __ex
 
 // Activation buffers of the matrix-core FFN (bf16 hi + optional lo parts).
 struct FfnBuffers {
-  bf16 *act_hi, *act_lo;    // routed   [T*k][I]
-  bf16 *acts_hi, *acts_lo;  // shared   [T][n_shared*I_s]
-  bf16 *z_hi, *z_lo;        // LoRE A x [T*k][r]
-  float *y, *ys;            // y_perm [T*k][H], y_shared [T][H]
+  bf16* act;   // routed   [T*k][I]
+  bf16* acts;  // shared   [T][n_shared*I_s]
+  bf16* z;     // LoRE A x [T*k][r]
+  float *y, *ys;  // y_perm [T*k][H], y_shared [T][H]
 };
 
 // Events recorded around one named kernel launch (see moe_kernel_t).
