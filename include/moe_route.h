@@ -156,12 +156,13 @@ moe_status_t moe_workspace_size(const moe_dims_t* dims, int32_t T, moe_mode_t mo
  *     STANDARD / FLOE: ignored (may be NULL); every slot exact.
  *   Outputs: topk_ids [T][k] int32 ordered by (-l, id); topk_w [T][k] fp32
  *     (p_e, or p_e / sum over the set when dims.renormalize); exact [T][k];
- *     flags [T]; logits_opt [T][E] fp32 and mass_opt [T] fp32 (SPICE
- *     confidence: mass of the routed top-k) may be NULL. */
+ *     flags [T]; logits [T][E] fp32 (required: the first of the router's two
+ *     kernels writes the logits there and the second ranks them); mass_opt
+ *     [T] fp32 (SPICE confidence: mass of the routed top-k) may be NULL. */
 moe_status_t moe_route(const moe_dims_t* dims, int32_t T, const void* x, const void* w_router,
                        const uint64_t* resident, int64_t resident_stride, moe_mode_t mode,
                        int32_t* topk_ids, float* topk_w, uint8_t* exact, uint32_t* flags,
-                       float* logits_opt, float* mass_opt, void* stream);
+                       float* logits, float* mass_opt, void* stream);
 
 /* APEX prefetch set: mask_out[t] = bit mask of the top-(k + delta[t]) experts
  * of x W_p^T, W_p [E][H] (a linear prefetch router; softmax keeps the order) [APEX page,

@@ -164,7 +164,7 @@ def moe_workspace_size(dims, T: int, mode) -> int:
 
 
 def moe_route(dims, T, x, w_router, resident, resident_stride, mode, topk_ids, topk_w, exact,
-              flags, logits=None, mass=None, stream=None):
+              flags, logits, mass=None, stream=None):
     _check(_lib.moe_route(ctypes.byref(_dims(dims)), T, _ptr(x), _ptr(w_router), _ptr(resident),
                           resident_stride, _mode(mode), _ptr(topk_ids), _ptr(topk_w), _ptr(exact),
                           _ptr(flags), _ptr(logits), _ptr(mass), _stream(stream)), "moe_route")

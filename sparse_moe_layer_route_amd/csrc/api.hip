@@ -109,7 +109,7 @@ moe_status_t check_weights(const moe_dims_t* d, const moe_weights_t* w, moe_mode
 
 // Workspace plan for T tokens.
 struct Plan {
-  size_t ids, w, exact, flags, offsets, moffsets, perm, inv, row_of;  // routing + permutation
+  size_t ids, w, exact, flags, logits, offsets, moffsets, perm, inv, row_of;  // routing + permutation
   size_t y_perm, y_s, g_s;                                            // FFN outputs
   size_t act, act_s;                                                  // fp32 GEMV activations
   size_t act_b, acts_b, z_b;                                          // bf16 MFMA activations
@@ -138,6 +138,7 @@ Plan make_plan(const moe_dims_t& d, int T, moe_mode_t mode) {
   p.w = take(P * 4);
   p.exact = take(P);
   p.flags = take((size_t)T * 4);
+  p.logits = take((size_t)T * d.n_experts * 4);
   p.offsets = take((size_t)(d.n_experts + 1) * 4);
   p.moffsets = take((size_t)(d.n_experts + 1) * 4);
   p.perm = take(P * 4);
@@ -243,21 +244,21 @@ moe_status_t moe_workspace_size(const moe_dims_t* dims, int32_t T, moe_mode_t mo
 moe_status_t moe_route(const moe_dims_t* dims, int32_t T, const void* x, const void* w_router,
                        const uint64_t* resident, int64_t resident_stride, moe_mode_t mode,
                        int32_t* topk_ids, float* topk_w, uint8_t* exact, uint32_t* flags,
-                       float* logits_opt, float* mass_opt, void* stream) {
+                       float* logits, float* mass_opt, void* stream) {
   moe_status_t st = check_dims(dims);
   if (st != MOE_OK) return st;
   if (mode < MOE_MODE_STANDARD || mode > MOE_MODE_FLOE) return MOE_EINVAL;
   if (T < 0) return MOE_EINVAL;
   if (T > kMaxTokens) return MOE_EUNSUPPORTED;
   if (!ok_ptr(x) || !ok_ptr(w_router) || !ok_ptr(topk_ids) || !ok_ptr(topk_w) || !ok_ptr(exact) ||
-      !ok_ptr(flags) || !ok_opt(logits_opt) || !ok_opt(mass_opt))
+      !ok_ptr(flags) || !ok_ptr(logits) || !ok_opt(mass_opt))
     return MOE_EINVAL;
   const bool needs_mask = mode == MOE_MODE_LORE || mode == MOE_MODE_STALL_FREE;
   if (needs_mask && (!ok_ptr(resident) || (resident_stride != 0 && resident_stride != 1)))
     return MOE_EINVAL;
   if (T == 0) return MOE_OK;
   return hip_status(launch_route(*dims, T, x, w_router, resident, resident_stride, mode, topk_ids,
-                                 topk_w, exact, flags, logits_opt, mass_opt, nullptr, nullptr,
+                                 topk_w, exact, flags, logits, mass_opt, nullptr, nullptr,
                                  (hipStream_t)stream));
 }
 
@@ -378,6 +379,7 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, int32_t T, const void* x,
   float* wts = at<float>(ws, p.w);
   uint8_t* exact = at<uint8_t>(ws, p.exact);
   uint32_t* flags = at<uint32_t>(ws, p.flags);
+  float* logits = (dbg && dbg->logits) ? dbg->logits : at<float>(ws, p.logits);
   int32_t* offsets = at<int32_t>(ws, p.offsets);
   int32_t* perm = at<int32_t>(ws, p.perm);
   int32_t* inv = at<int32_t>(ws, p.inv);
@@ -401,7 +403,7 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, int32_t T, const void* x,
   hipError_t e = pf.begin(MOE_KERNEL_ROUTE, s);
   if (e == hipSuccess)
     e = launch_route(d, T, x, w->w_router, resident, resident_stride, mode, ids, wts, exact, flags,
-                     dbg ? dbg->logits : nullptr, dbg ? dbg->mass : nullptr,
+                     logits, dbg ? dbg->mass : nullptr,
                      d.shared_gate ? w->w_shared_gate : nullptr, g_s, s);
   if (e == hipSuccess) e = pf.end(MOE_KERNEL_ROUTE, s);
   if (e == hipSuccess) e = pf.begin(MOE_KERNEL_PERMUTE, s);

@@ -4,27 +4,36 @@
 //   g_i = x . W_gate[i] and a_i = SiLU(g_i) u_i only for kept channels;
 //   y = sum over kept i of a_i W_down[i, :]  (down stored channel-major).
 //
-// up:     one wave per up row; lane l owns the 64 inputs of quantisation
+// up:     each wave owns FLOE_UP_RPW up rows and issues all their loads
+//         before any arithmetic; lane l owns the 64 inputs of quantisation
 //         group l (16 bytes of codes = one 16-byte load), keeps its 64 x values
-//         and their sum in registers across rows, and forms
-//         s * (sum_h q_h x_h - z * sum_h x_h) -- the group's (q - z) * s dot
-//         product -- before one wave reduction.  Codes are unpacked four at a
-//         time: (word >> 2j) & 0x03030303 leaves code j of every byte in that
-//         byte, which converts to float with a single byte-to-float op.
-// select: one 1024-thread workgroup per pair, |u| bit patterns (monotone for
-//         non-negative floats) in LDS, MSB-first 8-bit radix select for the
-//         keep-th largest, then two block scans to list kept channels in
-//         ascending order, equal keys resolved toward lower channels.
-// gate:   one wave per kept channel row (contiguous H-vector).
+//         and their sum in registers, and forms s * (sum_h q_h x_h - z * sum_h
+//         x_h) -- the group's (q - z) * s dot product -- before one wave
+//         reduction per row.  Codes are unpacked four at a time:
+//         (word >> 2j) & 0x03030303 leaves code j of every byte in that byte,
+//         which converts to float with a single byte-to-float op.
+// select: one 1024-thread workgroup per pair; each thread holds the |u| bit
+//         patterns (monotone for non-negative floats) of up to 16 consecutive
+//         channels in registers; MSB-first 8-bit radix select for the keep-th
+//         largest with one LDS histogram per wave, then two block scans list
+//         the kept channels in ascending order, equal keys resolved toward
+//         lower channels.
+// gate:   each wave owns two kept channel rows (contiguous H-vectors) and
+//         loads both before reducing.
 // down:   each thread owns 8 output columns and sweeps a slice of the kept
-//         channel rows; slices are summed by a small reduction kernel.
+//         channel rows, eight rows in flight; slices are summed in a fixed
+//         order by a small reduction kernel.
 #include "common.h"
 
 namespace moe {
 
-constexpr int FLOE_ROWS_PER_BLOCK = 16;
+constexpr int FLOE_UP_RPW = 4;          // up rows per wave
+constexpr int FLOE_GATE_RPW = 2;        // gate rows per wave
+constexpr int FLOE_DOWN_COLS = 1024;    // output columns per down block (8 per thread)
 constexpr int FLOE_SELECT_THREADS = 1024;
+constexpr int FLOE_SELECT_CH = 16;      // channels per select thread (I <= 16384)
 constexpr int FLOE_MAX_INTER = 16384;
+static_assert(FLOE_MAX_INTER <= FLOE_SELECT_THREADS * FLOE_SELECT_CH, "select covers every channel");
 constexpr int FLOE_DOWN_SLICE = 32;
 
 // Pair position p -> (pair f, token t, expert e).  e is the segment of the
@@ -53,10 +62,23 @@ floe_up_kernel(const Tin* __restrict__ x, const uint8_t* __restrict__ up_q,
   if (!pair_of(blockIdx.y, E, k, offsets, perm, f, t, e)) return;
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   const int G = H >> 6;  // groups per row
+  const int i0 = (blockIdx.x * 4 + wv) * FLOE_UP_RPW;
+  if (i0 >= I) return;
   const Tin* xr = x + (int64_t)t * H;
   for (int g0 = 0; g0 < G; g0 += MOE_WAVE) {
     const int g = g0 + lane;
     const bool act = g < G;
+    uint4 cw[FLOE_UP_RPW];
+    float sc[FLOE_UP_RPW], zp[FLOE_UP_RPW];
+    if (act) {
+#pragma unroll
+      for (int q = 0; q < FLOE_UP_RPW; ++q) {
+        const int64_t row = (int64_t)e * I + min(i0 + q, I - 1);
+        cw[q] = *reinterpret_cast<const uint4*>(up_q + row * (H >> 2) + (int64_t)g * 16);
+        sc[q] = half_bits_to_f(up_s[row * G + g]);
+        zp[q] = half_bits_to_f(up_z[row * G + g]);
+      }
+    }
     float xv[64];
     float xs = 0.f;
     if (act) {
@@ -71,15 +93,12 @@ floe_up_kernel(const Tin* __restrict__ x, const uint8_t* __restrict__ up_q,
         }
       }
     }
-    for (int q = 0; q < FLOE_ROWS_PER_BLOCK / 4; ++q) {
-      const int i = blockIdx.x * FLOE_ROWS_PER_BLOCK + wv * (FLOE_ROWS_PER_BLOCK / 4) + q;
-      const int64_t row = (int64_t)e * I + i;
-      float part = 0.f;
+    float part[FLOE_UP_RPW];
+#pragma unroll
+    for (int q = 0; q < FLOE_UP_RPW; ++q) {
+      part[q] = 0.f;
       if (act) {
-        const uint4 cw = *reinterpret_cast<const uint4*>(up_q + row * (H >> 2) + (int64_t)g * 16);
-        const float s = half_bits_to_f(up_s[row * G + g]);
-        const float z = half_bits_to_f(up_z[row * G + g]);
-        const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
+        const uint32_t words[4] = {cw[q].x, cw[q].y, cw[q].z, cw[q].w};
         float acc = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -91,14 +110,16 @@ floe_up_kernel(const Tin* __restrict__ x, const uint8_t* __restrict__ up_q,
               acc = fmaf((float)((m >> (8 * b)) & 0xFFu), xv[w * 16 + 4 * b + j], acc);
           }
         }
-        part = s * (acc - z * xs);
+        part[q] = sc[q] * (acc - zp[q] * xs);
       }
-      const float uval = wave_sum(part);
-      if (lane == 0) {
-        if (g0 == 0)
-          u_out[(int64_t)blockIdx.y * I + i] = uval;
-        else
-          u_out[(int64_t)blockIdx.y * I + i] += uval;
+    }
+#pragma unroll
+    for (int q = 0; q < FLOE_UP_RPW; ++q) {
+      const float uval = wave_sum(part[q]);
+      if (lane == 0 && i0 + q < I) {
+        float* o = u_out + (int64_t)blockIdx.y * I + i0 + q;
+        if (g0 == 0) *o = uval;
+        else *o += uval;
       }
     }
   }
@@ -126,12 +147,17 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
   return base + s - v;
 }
 
+// Thread tid owns the CH consecutive channels [tid*ch, tid*ch + ch) (ch <=
+// FLOE_SELECT_CH) and keeps their |u| bit patterns in registers through all
+// radix passes, so a pass is CH histogram increments per thread and the final
+// ascending listing is one block scan over per-thread counts.
 __global__ void __launch_bounds__(FLOE_SELECT_THREADS)
 floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin, int E, int k,
                    const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
                    int32_t* __restrict__ keep_out,
                    uint32_t* __restrict__ flags) {
-  __shared__ uint32_t keys[FLOE_MAX_INTER];
+  constexpr int CH = FLOE_SELECT_CH;
+  __shared__ int whist[FLOE_SELECT_THREADS / MOE_WAVE][256];
   __shared__ int hist[256];
   __shared__ int wsum[FLOE_SELECT_THREADS / MOE_WAVE];
   __shared__ uint32_t s_prefix;
@@ -139,23 +165,37 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
   __shared__ uint32_t s_next;
   int f, t, e;
   if (!pair_of(blockIdx.x, E, k, offsets, perm, f, t, e)) return;
-  const int tid = threadIdx.x, lane = lane_id();
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
+  const int ch = (I + FLOE_SELECT_THREADS - 1) / FLOE_SELECT_THREADS;
+  const int i0 = tid * ch;
   const float* ur = u + (int64_t)blockIdx.x * I;
-  for (int i = tid; i < I; i += FLOE_SELECT_THREADS) keys[i] = __float_as_uint(fabsf(ur[i]));
+  uint32_t key[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int i = i0 + j;
+    key[j] = (j < ch && i < I) ? __float_as_uint(fabsf(ur[i])) : 0u;
+  }
   if (tid == 0) {
     s_prefix = 0u;
     s_need = n_keep;
     s_next = 0u;
   }
-  __syncthreads();
   uint32_t pmask = 0u;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0;
+    for (int j = lane; j < 256; j += MOE_WAVE) whist[wv][j] = 0;
     __syncthreads();
     const uint32_t prefix = s_prefix;
-    for (int i = tid; i < I; i += FLOE_SELECT_THREADS) {
-      const uint32_t kk = keys[i];
-      if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> shift) & 0xFFu], 1);
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      if (j < ch && i0 + j < I && (key[j] & pmask) == prefix)
+        atomicAdd(&whist[wv][(key[j] >> shift) & 0xFFu], 1);
+    }
+    __syncthreads();
+    if (tid < 256) {
+      int c = 0;
+#pragma unroll
+      for (int w = 0; w < FLOE_SELECT_THREADS / MOE_WAVE; ++w) c += whist[w][tid];
+      hist[tid] = c;
     }
     __syncthreads();
     if (tid < MOE_WAVE) {
@@ -188,39 +228,40 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
   }
   const uint32_t thr = s_prefix;
   const int need_eq = s_need;
-  // chunk of consecutive channels per thread
-  const int ch = (I + FLOE_SELECT_THREADS - 1) / FLOE_SELECT_THREADS;
-  const int i0 = tid * ch, i1 = min(I, i0 + ch);
   int n_eq = 0;
   uint32_t below_max = 0u;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t kk = keys[i];
-    n_eq += kk == thr;
-    if (kk < thr && kk > below_max) below_max = kk;
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    if (j < ch && i0 + j < I) {
+      n_eq += key[j] == thr;
+      if (key[j] < thr && key[j] > below_max) below_max = key[j];
+    }
   }
   int eq_total;
-  int eq_rank = block_excl_scan(n_eq, wsum, eq_total);
-  int n_kept = 0;
+  const int eq_rank = block_excl_scan(n_eq, wsum, eq_total);
+  // kept: above the threshold, or among the first need_eq equal keys in
+  // channel order
+  uint32_t kept = 0u;  // bit j: channel i0 + j kept
   {
     int r = eq_rank;
-    for (int i = i0; i < i1; ++i) {
-      const uint32_t kk = keys[i];
-      if (kk > thr) ++n_kept;
-      else if (kk == thr) { if (r < need_eq) ++n_kept; ++r; }
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      if (j < ch && i0 + j < I) {
+        bool kp = key[j] > thr;
+        if (key[j] == thr) {
+          kp = r < need_eq;
+          ++r;
+        }
+        if (kp) kept |= 1u << j;
+      }
     }
   }
   int kept_total;
-  int pos = block_excl_scan(n_kept, wsum, kept_total);
-  {
-    int r = eq_rank;
-    int32_t* ko = keep_out + (int64_t)f * n_keep;
-    for (int i = i0; i < i1; ++i) {
-      const uint32_t kk = keys[i];
-      bool kp = kk > thr;
-      if (kk == thr) { kp = r < need_eq; ++r; }
-      if (kp) ko[pos++] = i;
-    }
-  }
+  int pos = block_excl_scan(__popc(kept), wsum, kept_total);
+  int32_t* ko = keep_out + (int64_t)f * n_keep;
+#pragma unroll
+  for (int j = 0; j < CH; ++j)
+    if ((kept >> j) & 1u) ko[pos++] = i0 + j;
   // near-tie at the edge: next value below the threshold, or a tie at it
   if (n_keep < I) {
     uint32_t m = below_max;
@@ -238,69 +279,142 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
   }
 }
 
+// 8 consecutive inputs as raw bits, converted at use.
+template <typename Tin> struct Raw8;
+template <> struct Raw8<bf16> {
+  uint4 v;
+  __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void to_f(float (&o)[8]) const {
+    o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+    o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
+  }
+};
+template <> struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void to_f(float (&o)[8]) const {
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  }
+};
+
+// Kept channel c of pair p: a[p][c] = SiLU(x_t . W_gate[e][keep[c]]) * u[p][keep[c]].
+// Wave w of block b owns channels (4b + w) * FLOE_GATE_RPW + q; the H loop
+// takes 512 inputs per step (8 per lane) and loads both rows' chunks first.
 template <typename Tin>
 __global__ void __launch_bounds__(256)
 floe_gate_kernel(const Tin* __restrict__ x, const Tin* __restrict__ wg, const float* __restrict__ u,
                  int H, int I, int n_keep, int E, int k, const int32_t* __restrict__ offsets,
                  const int32_t* __restrict__ perm, const int32_t* __restrict__ keep,
                  float* __restrict__ a_out) {
+  constexpr int R = FLOE_GATE_RPW;
+  constexpr int NB = 8;  // 512-input chunks loaded together (4096 inputs)
   int f, t, e;
   if (!pair_of(blockIdx.y, E, k, offsets, perm, f, t, e)) return;
   const int lane = lane_id(), wv = threadIdx.x >> 6;
+  const int c0 = (blockIdx.x * 4 + wv) * R;
+  if (c0 >= n_keep) return;
   const Tin* xr = x + (int64_t)t * H;
-  for (int q = 0; q < FLOE_ROWS_PER_BLOCK / 4; ++q) {
-    const int c = blockIdx.x * FLOE_ROWS_PER_BLOCK + wv * (FLOE_ROWS_PER_BLOCK / 4) + q;
-    if (c >= n_keep) break;
-    const int i = keep[(int64_t)f * n_keep + c];
-    const Tin* row = wg + ((int64_t)e * I + i) * H;
-    float acc = 0.f;
-    for (int h = lane * 8; h < H; h += 8 * MOE_WAVE) {
-      float w8[8], x8[8];
-      elem<Tin>::load8(row + h, w8);
-      elem<Tin>::load8(xr + h, x8);
+  int ch[R];
+  const Tin* rows[R];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc = fmaf(w8[j], x8[j], acc);
+  for (int q = 0; q < R; ++q) {
+    ch[q] = keep[(int64_t)f * n_keep + min(c0 + q, n_keep - 1)];
+    rows[q] = wg + ((int64_t)e * I + ch[q]) * H;
+  }
+  float acc[R];
+#pragma unroll
+  for (int q = 0; q < R; ++q) acc[q] = 0.f;
+  for (int h0 = 0; h0 < H; h0 += NB * 512) {
+    Raw8<Tin> w[R][NB], xv[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int h = min(h0 + 512 * j + 8 * lane, H - 8);
+#pragma unroll
+      for (int q = 0; q < R; ++q) w[q][j].load(rows[q] + h);
+      xv[j].load(xr + h);
     }
-    const float g = wave_sum(acc);
-    if (lane == 0) a_out[(int64_t)blockIdx.y * n_keep + c] = silu_f(g) * u[(int64_t)blockIdx.y * I + i];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (h0 + 512 * j + 8 * lane >= H) continue;
+      float xf[8];
+      xv[j].to_f(xf);
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        float wf[8];
+        w[q][j].to_f(wf);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[q] = fmaf(wf[c], xf[c], acc[q]);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    const float g = wave_sum(acc[q]);
+    if (lane == 0 && c0 + q < n_keep)
+      a_out[(int64_t)blockIdx.y * n_keep + c0 + q] = silu_f(g) * u[(int64_t)blockIdx.y * I + ch[q]];
   }
 }
 
+// Partial y over one slice of FLOE_DOWN_SLICE kept channels; eight channel
+// rows are loaded before their multiply-adds.
 template <typename Tin>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(FLOE_DOWN_COLS / 8)
 floe_down_kernel(const Tin* __restrict__ wd, const float* __restrict__ a, int H, int I, int n_keep,
                  int P_max, int E, int k, const int32_t* __restrict__ offsets,
                  const int32_t* __restrict__ perm, const int32_t* __restrict__ keep,
                  float* __restrict__ part) {
+  constexpr int B = 8;
   int f, t, e;
   if (!pair_of(blockIdx.z, E, k, offsets, perm, f, t, e)) return;
-  const int h = (blockIdx.x * 256 + threadIdx.x) * 8;
+  const int h = (blockIdx.x * (FLOE_DOWN_COLS / 8) + threadIdx.x) * 8;
   if (h >= H) return;
   const int c0 = blockIdx.y * FLOE_DOWN_SLICE, c1 = min(n_keep, c0 + FLOE_DOWN_SLICE);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const float* ar = a + (int64_t)blockIdx.z * n_keep;
   const int32_t* kr = keep + (int64_t)f * n_keep;
-  for (int c = c0; c < c1; ++c) {
-    const float av = ar[c];
-    float w8[8];
-    elem<Tin>::load8(wd + ((int64_t)e * I + kr[c]) * H + h, w8);
+  for (int c = c0; c < c1; c += B) {
+    Raw8<Tin> w[B];
+    float av[B];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = fmaf(av, w8[j], acc[j]);
+    for (int u = 0; u < B; ++u) {
+      const int cc = min(c + u, c1 - 1);
+      av[u] = c + u < c1 ? ar[cc] : 0.f;
+      w[u].load(wd + ((int64_t)e * I + kr[cc]) * H + h);
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      float wf[8];
+      w[u].to_f(wf);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(av[u], wf[j], acc[j]);
+    }
   }
   float* o = part + ((int64_t)blockIdx.y * P_max + blockIdx.z) * H + h;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) o[j] = acc[j];
+  *reinterpret_cast<float4*>(o) = float4{acc[0], acc[1], acc[2], acc[3]};
+  *reinterpret_cast<float4*>(o + 4) = float4{acc[4], acc[5], acc[6], acc[7]};
 }
 
+// y[p] = sum of the slices' partials, added in slice order.
 __global__ void __launch_bounds__(256)
 floe_reduce_kernel(const float* __restrict__ part, int H, int n_slices, int P_max, int E,
                    const int32_t* __restrict__ offsets, float* __restrict__ y) {
+  constexpr int B = 8;
   const int p = blockIdx.y;
   if (p >= offsets[E]) return;
   const int h = blockIdx.x * 256 + threadIdx.x;
   if (h >= H) return;
   float s = 0.f;
-  for (int sl = 0; sl < n_slices; ++sl) s += part[((int64_t)sl * P_max + p) * H + h];
+  for (int sl = 0; sl < n_slices; sl += B) {
+    float v[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+      v[u] = sl + u < n_slices ? part[((int64_t)(sl + u) * P_max + p) * H + h] : 0.f;
+#pragma unroll
+    for (int u = 0; u < B; ++u) s += v[u];
+  }
   y[(int64_t)p * H + h] = s;
 }
 
@@ -316,7 +430,7 @@ static hipError_t launch_floe_t(const moe_dims_t& d, int T, const Tin* x, const 
   const int P = T * k;
   if (P == 0) return hipSuccess;
   hipError_t e = pf.begin(MOE_KERNEL_FLOE_UP, s);
-  floe_up_kernel<Tin><<<dim3(I / FLOE_ROWS_PER_BLOCK, P), 256, 0, s>>>(
+  floe_up_kernel<Tin><<<dim3((I + 4 * FLOE_UP_RPW - 1) / (4 * FLOE_UP_RPW), P), 256, 0, s>>>(
       x, w.up_q, w.up_scale, w.up_zero, H, I, E, k, offsets, perm, u);
   if (e == hipSuccess) e = pf.end(MOE_KERNEL_FLOE_UP, s);
   if (e == hipSuccess) e = pf.begin(MOE_KERNEL_FLOE_SELECT, s);
@@ -324,12 +438,12 @@ static hipError_t launch_floe_t(const moe_dims_t& d, int T, const Tin* x, const 
                                                         keep, flags);
   if (e == hipSuccess) e = pf.end(MOE_KERNEL_FLOE_SELECT, s);
   if (e == hipSuccess) e = pf.begin(MOE_KERNEL_FLOE_GATE, s);
-  floe_gate_kernel<Tin><<<dim3((nk + FLOE_ROWS_PER_BLOCK - 1) / FLOE_ROWS_PER_BLOCK, P), 256, 0, s>>>(
+  floe_gate_kernel<Tin><<<dim3((nk + 4 * FLOE_GATE_RPW - 1) / (4 * FLOE_GATE_RPW), P), 256, 0, s>>>(
       x, (const Tin*)w.w_gate, u, H, I, nk, E, k, offsets, perm, keep, a);
   if (e == hipSuccess) e = pf.end(MOE_KERNEL_FLOE_GATE, s);
   const int ns = floe_slices(nk);
   if (e == hipSuccess) e = pf.begin(MOE_KERNEL_FLOE_DOWN, s);
-  floe_down_kernel<Tin><<<dim3((H + 2047) / 2048, ns, P), 256, 0, s>>>(
+  floe_down_kernel<Tin><<<dim3((H + FLOE_DOWN_COLS - 1) / FLOE_DOWN_COLS, ns, P), FLOE_DOWN_COLS / 8, 0, s>>>(
       (const Tin*)w.w_down, a, H, I, nk, P, E, k, offsets, perm, keep, part);
   if (e == hipSuccess) e = pf.end(MOE_KERNEL_FLOE_DOWN, s);
   floe_reduce_kernel<<<dim3((H + 255) / 256, P), 256, 0, s>>>(part, H, ns, P, E, offsets, y_perm);

@@ -1,19 +1,23 @@
 // Router: logits -> softmax -> top-k, residency split, stall-free
 // substitution, shared-expert gate, and the APEX prefetch mask.
 //
-// One 1024-thread block (16 waves) per tile of 16 tokens.
-//   logits  bf16: l = X W_r^T on the matrix cores (v_mfma_f32_16x16x32_bf16),
+// Routing is two launches.
+//   logits  one 512-thread block per (16-token tile, 16-expert tile): bf16
+//           l = X W_r^T on the matrix cores (v_mfma_f32_16x16x32_bf16),
 //           A = 16 token rows, B = 16 expert rows of W_r [E][H] (both k
-//           contiguous).  The 16 waves are ceil(E/16) expert tiles times a
-//           K split; partial tiles meet in LDS and are summed in a fixed
-//           order, so logits are bitwise reproducible.
-//           fp32: each wave dots its token with every expert row.
-//   top-k   wave w finishes token w of the tile with lane = expert:
-//           softmax by wave max / sum of exp; each lane's rank is the number
-//           of lanes whose key (order-preserving logit bits, 0xFFFFFFFF - id)
-//           is larger, read with E scalar lane reads, so equal logits go to
-//           the lower id; the expert of rank j fills slot j, and the logits
-//           at ranks k-1 and k give the near-tie flag.
+//           contiguous); the 8 waves take contiguous eighths of K and their
+//           partial tiles meet in LDS, summed in a fixed order, so logits are
+//           bitwise reproducible.  Spreading the expert tiles over blocks
+//           keeps each CU's share of W_r small.  fp32: one thread per
+//           (token, expert) dot product.
+//   top-k   one wave per token, lane = expert: softmax by wave max / sum of
+//           exp; each lane's rank is the number of lanes whose key
+//           (order-preserving logit bits, 0xFFFFFFFF - id) is larger, read
+//           with E scalar lane reads, so equal logits go to the lower id; the
+//           expert of rank j fills slot j, and the logits at ranks k-1 and k
+//           give the near-tie flag.
+// The prefetch mask runs as one 1024-thread block per 16-token tile (logits
+// and ranking in one launch).
 // Stall-free substitution [APEX page, Sec. 4.3, Algorithm 1]: every routed
 // expert outranks every non-routed one, so keeping the prefetched routed
 // experts and filling each miss with the best remaining prefetched expert is
@@ -129,6 +133,76 @@ __device__ __forceinline__ void tile_logits(const float* __restrict__ x, const f
   __syncthreads();
 }
 
+constexpr int LOGIT_WAVES = 8;
+
+// Logits of tokens 16*blockIdx.x.. and experts 16*blockIdx.y.. into
+// logits [T][E].
+__global__ void __launch_bounds__(LOGIT_WAVES * MOE_WAVE)
+route_logits_kernel(const bf16* __restrict__ x, const bf16* __restrict__ w, int T, int H, int E,
+                    float* __restrict__ logits) {
+  __shared__ f32x4_t part[LOGIT_WAVES - 1][MOE_WAVE];
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
+  const bf16* xr = x + (int64_t)min(t0 + r16, T - 1) * H + 8 * kg;
+  const bf16* wr = w + (int64_t)min(e0 + r16, E - 1) * H + 8 * kg;
+  const bool live = e0 + r16 < E;
+  constexpr int U = 4;
+  const int ksteps = H >> 5;
+  const int per = (ksteps + LOGIT_WAVES - 1) / LOGIT_WAVES;
+  const int kb = wv * per, ke = min(ksteps, kb + per);
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = kb; k0 < ke; k0 += U) {
+    bf16x8_t a[U], b[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ko = min(k0 + u, ke - 1) << 5;
+      a[u] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(xr + ko));
+      b[u] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(wr + ko));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool on = live && k0 + u < ke;
+      const bf16x8_t bv = on ? b[u] : __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], bv, acc, 0, 0, 0);
+    }
+  }
+  if (wv > 0) part[wv - 1][lane] = acc;
+  __syncthreads();
+  if (wv == 0) {
+#pragma unroll
+    for (int p = 0; p < LOGIT_WAVES - 1; ++p) acc += part[p][lane];
+    // accumulator: rows (tokens) 4*kg+i, column (expert) r16
+    const int e = e0 + r16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 4 * kg + i;
+      if (t < T && e < E) logits[(int64_t)t * E + e] = acc[i];
+    }
+  }
+}
+
+__global__ void __launch_bounds__(LOGIT_WAVES * MOE_WAVE)
+route_logits_kernel(const float* __restrict__ x, const float* __restrict__ w, int T, int H, int E,
+                    float* __restrict__ logits) {
+  const int tid = threadIdx.x;
+  if (tid >= 256) return;
+  const int t = blockIdx.x * 16 + (tid >> 4), e = blockIdx.y * 16 + (tid & 15);
+  if (t >= T || e >= E) return;
+  const float* xr = x + (int64_t)t * H;
+  const float* wr = w + (int64_t)e * H;
+  float acc = 0.f;
+  for (int h = 0; h < H; h += 4) {
+    const float4 a = *reinterpret_cast<const float4*>(xr + h);
+    const float4 b = *reinterpret_cast<const float4*>(wr + h);
+    acc = fmaf(a.x, b.x, acc);
+    acc = fmaf(a.y, b.y, acc);
+    acc = fmaf(a.z, b.z, acc);
+    acc = fmaf(a.w, b.w, acc);
+  }
+  logits[(int64_t)t * E + e] = acc;
+}
+
 template <typename Tin>
 __device__ __forceinline__ float wave_dot(const Tin* __restrict__ a, const Tin* __restrict__ b, int H) {
   float acc = 0.f;
@@ -142,22 +216,19 @@ __device__ __forceinline__ float wave_dot(const Tin* __restrict__ a, const Tin* 
   return wave_sum(acc);
 }
 
+// One wave per token (4 per block) on logits [T][E] from route_logits_kernel.
 template <typename Tin>
-__global__ void __launch_bounds__(1024)
-route_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w_router, int T, int H, int E, int k,
-             int renorm, float margin, int mode, const uint64_t* __restrict__ resident,
-             int64_t res_stride, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
-             uint8_t* __restrict__ exact, uint32_t* __restrict__ flags,
-             float* __restrict__ logits_out, float* __restrict__ mass_out,
-             const Tin* __restrict__ w_sg, float* __restrict__ g_s) {
-  __shared__ RouteLds lds;
-  const int t0 = blockIdx.x * ROUTE_TOK;
-  tile_logits(x, w_router, T, H, E, t0, lds);
-  const int lane = lane_id(), wv = threadIdx.x >> 6;
-  const int t = t0 + wv;
+__global__ void __launch_bounds__(256)
+route_topk_kernel(const Tin* __restrict__ x, const float* __restrict__ logits, int T, int H, int E,
+                  int k, int renorm, float margin, int mode, const uint64_t* __restrict__ resident,
+                  int64_t res_stride, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+                  uint8_t* __restrict__ exact, uint32_t* __restrict__ flags,
+                  float* __restrict__ mass_out, const Tin* __restrict__ w_sg,
+                  float* __restrict__ g_s) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float l = lane < E ? lds.logits[wv][lane] : -INFINITY;
-  if (logits_out && lane < E) logits_out[(int64_t)t * E + lane] = l;
+  const float l = lane < E ? logits[(int64_t)t * E + lane] : -INFINITY;
   if (g_s) {
     const float gd = w_sg ? wave_dot<Tin>(x + (int64_t)t * H, w_sg, H) : 0.f;
     if (lane == 0) g_s[t] = w_sg ? sigmoid_f(gd) : 1.f;
@@ -244,17 +315,21 @@ hipError_t launch_route(const moe_dims_t& d, int T, const void* x, const void* w
                         const uint64_t* resident, int64_t res_stride, int mode, int32_t* ids,
                         float* w, uint8_t* exact, uint32_t* flags, float* logits, float* mass,
                         const void* w_sg, float* g_s, hipStream_t s) {
-  const int blocks = (T + ROUTE_TOK - 1) / ROUTE_TOK;
-  if (d.dtype == MOE_BF16)
-    route_kernel<bf16><<<blocks, 1024, 0, s>>>((const bf16*)x, (const bf16*)w_router, T, d.hidden,
-                                               d.n_experts, d.top_k, d.renormalize, d.tie_margin,
-                                               mode, resident, res_stride, ids, w, exact, flags,
-                                               logits, mass, (const bf16*)w_sg, g_s);
-  else
-    route_kernel<float><<<blocks, 1024, 0, s>>>((const float*)x, (const float*)w_router, T, d.hidden,
-                                                d.n_experts, d.top_k, d.renormalize, d.tie_margin,
-                                                mode, resident, res_stride, ids, w, exact, flags,
-                                                logits, mass, (const float*)w_sg, g_s);
+  const dim3 lgrid((T + 15) / 16, (d.n_experts + 15) / 16);
+  const int tblocks = (T + 3) / 4;
+  if (d.dtype == MOE_BF16) {
+    route_logits_kernel<<<lgrid, LOGIT_WAVES * MOE_WAVE, 0, s>>>(
+        (const bf16*)x, (const bf16*)w_router, T, d.hidden, d.n_experts, logits);
+    route_topk_kernel<bf16><<<tblocks, 256, 0, s>>>(
+        (const bf16*)x, logits, T, d.hidden, d.n_experts, d.top_k, d.renormalize, d.tie_margin, mode,
+        resident, res_stride, ids, w, exact, flags, mass, (const bf16*)w_sg, g_s);
+  } else {
+    route_logits_kernel<<<lgrid, LOGIT_WAVES * MOE_WAVE, 0, s>>>(
+        (const float*)x, (const float*)w_router, T, d.hidden, d.n_experts, logits);
+    route_topk_kernel<float><<<tblocks, 256, 0, s>>>(
+        (const float*)x, logits, T, d.hidden, d.n_experts, d.top_k, d.renormalize, d.tie_margin, mode,
+        resident, res_stride, ids, w, exact, flags, mass, (const float*)w_sg, g_s);
+  }
   return hipGetLastError();
 }
 

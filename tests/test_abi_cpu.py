@@ -112,7 +112,9 @@ def test_entry_point_null_checks():
                        None) == B.MOE_EINVAL
     assert L.moe_route(ctypes.byref(d), 4, FAKE, FAKE, None, 0, 2, FAKE, FAKE, FAKE, FAKE, None, None,
                        None) == B.MOE_EINVAL                                   # stall-free needs masks
-    assert L.moe_route(ctypes.byref(d), 0, FAKE, FAKE, None, 0, 0, FAKE, FAKE, FAKE, FAKE, None, None,
+    assert L.moe_route(ctypes.byref(d), 4, FAKE, FAKE, None, 0, 0, FAKE, FAKE, FAKE, FAKE, None, None,
+                       None) == B.MOE_EINVAL                                   # logits are required
+    assert L.moe_route(ctypes.byref(d), 0, FAKE, FAKE, None, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None,
                        None) == B.MOE_OK
     assert L.moe_permute(4, 9, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.MOE_EUNSUPPORTED
     assert L.moe_permute(4, 2, 65, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.MOE_EUNSUPPORTED

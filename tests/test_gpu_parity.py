@@ -291,7 +291,8 @@ def test_unfused_entry_points_match_fused():
     w = torch.empty(T * k, dtype=torch.float32, device="cuda")
     ex = torch.empty(T * k, dtype=torch.uint8, device="cuda")
     fl = torch.empty(T, dtype=torch.int32, device="cuda")
-    M.moe_route(dims, T, x, wdev["w_router"], res, 0, "lore", ids, w, ex, fl)
+    lg = torch.empty(T * E, dtype=torch.float32, device="cuda")
+    M.moe_route(dims, T, x, wdev["w_router"], res, 0, "lore", ids, w, ex, fl, lg)
     off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
     perm = torch.empty(T * k, dtype=torch.int32, device="cuda")
     inv = torch.empty(T * k, dtype=torch.int32, device="cuda")
