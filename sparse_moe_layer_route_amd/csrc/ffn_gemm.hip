@@ -7,14 +7,15 @@
 // [FloE page, Sec. 1, forward a^S(x) with S_t = identity.]
 //
 // Block tile: 256 tokens (N) x 256 weight rows (M: 128 gate + 128 up, or 256
-// down) x 32 k per stage, 4 waves in a 2 x 2 grid, each wave 128 x 128
-// outputs = 8 x 8 MFMA tiles held in 256 accumulator registers.  Per stage a
-// wave reads 16 fragments (16 KiB) from LDS for 64 MFMAs; a block pulls
-// 32 KiB per stage from L2 for 4.2 MFLOP (128 flop/B).  A (weights) and B
-// (token rows, gathered through the permutation) are both k-contiguous in
-// HBM.  Stages move global -> LDS directly (16-byte LDS DMA loads, no
-// register staging) into a 4-deep ring, so three stages are in flight while
-// one feeds the MFMAs: the L2/HBM latency of a stage (microseconds under load)
+// down) x 32 k per stage, 8 waves (two per SIMD) in a 2 x 4 grid, each wave
+// 128 weight rows x 64 tokens = 8 x 4 MFMA tiles in 128 accumulator
+// registers.  Per stage a wave reads 12 fragments (12 KiB) from LDS for 32
+// MFMAs, and while one wave of a SIMD waits on LDS the other issues MFMAs;
+// a block pulls 32 KiB per stage from L2 for 4.2 MFLOP (128 flop/B).  A
+// (weights) and B (token rows, gathered through the permutation) are both
+// k-contiguous in HBM.  Stages move global -> LDS directly (16-byte LDS DMA
+// loads, no register staging) into a 4-deep ring, so three stages are in
+// flight while one feeds the MFMAs: the L2/HBM latency of a stage (microseconds under load)
 // is covered by three stages of math.  Each 64-byte LDS row holds four
 // 16-byte k chunks stored at chunk ^ ((row / 4) % 4), so the 16 lanes reading
 // one fragment column hit distinct banks.  Ordering is explicit: a thread
@@ -41,7 +42,9 @@ constexpr int GN = 256;        // tokens per block tile
 constexpr int GK = 32;         // k per stage
 constexpr int GSTAGES = 4;     // LDS ring depth (stages in flight: GSTAGES - 1)
 constexpr int GROWS = 512;     // LDS rows per stage: 256 weight + 256 token
-constexpr int GTHREADS = 256;
+constexpr int GTHREADS = 512;  // 8 waves: two per SIMD
+constexpr int GWAVES = GTHREADS / 64;
+constexpr int GTT = 4;         // token tiles (16 each) per wave: 64 tokens
 constexpr int NXCD = 8;
 
 struct GemmArgs {
@@ -145,12 +148,14 @@ __device__ __forceinline__ bool find_mtile(const GemmArgs a, int m_idx, MTile& m
 
 // Wait until at most N of this wave's vector-memory operations are pending
 // (LDS DMA loads complete in issue order).
-#define GEMM_VMCNT(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
+#define GEMM_VMCNT(N) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory")
+// at most two later stages of this thread's DMA loads still pending
+#define GEMM_VMCNT_STAGES2() GEMM_VMCNT(2 * NQ)
 
 // GATED: GEMM1 (gate and up matrices, 128 rows each, SiLU product, bf16 out);
 // else GEMM2 (256 down rows, fp32 out).  Either way a block stages 256 weight
-// rows and 256 token rows per 32-wide k stage, and each wave owns a 128 x 128
-// output tile (8 x 8 MFMA tiles, 256 fp32 accumulators per lane).
+// rows and 256 token rows per 32-wide k stage, and each wave owns a 128 x 64
+// output tile (8 x 4 MFMA tiles, 128 fp32 accumulators per lane).
 template <bool GATED>
 __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   constexpr int NW = GATED ? 2 : 1;          // weight matrices
@@ -163,25 +168,27 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   MTile mt;
   if (!find_mtile(a, m_idx, mt)) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv & 1, wn = wv >> 1;       // 2 x 2 waves: weight half, token half
+  const int wm = wv & 1, wn = wv >> 1;       // 2 x 4 waves: weight half, token quarter
   const int r16 = lane & 15, kg = lane >> 4;
   const int row_w0 = n_idx * MW;             // first weight row of the tile
 
   // DMA plan: a stage is 512 LDS rows x 64 B; one wave instruction writes 16
   // rows (1 KiB, lane l -> row l/4, 16-byte slot l%4).  Wave w issues
-  // instructions 8w..8w+7: waves 0-1 the weight rows (GATED: 0-127 gate,
-  // 128-255 up), waves 2-3 the token rows.  Slot p of row r holds k chunk
+  // instructions NQ*w..NQ*w+NQ-1: waves 0-3 the weight rows (GATED: 0-127
+  // gate, 128-255 up), waves 4-7 the token rows.  Slot p of row r holds k chunk
   // p ^ ((r/4) % 4), so the 16 rows of one fragment read hit distinct banks.
   const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
   const bf16* base_w0 = a.w0 + (int64_t)mt.g * a.w_stride;
   const bf16* base_w1 = GATED ? a.w1 + (int64_t)mt.g * a.w_stride : base_w0;
   const bf16* base_x = GATED ? a.x : a.act_in;
-  const bool is_w = wv < 2;
-  const bf16* dma_base = is_w ? ((GATED && wv == 1) ? base_w1 : base_w0) : base_x;
-  int off[8];
+  const bool is_w = wv < GWAVES / 2;
+  // GATED: LDS rows 0-127 (waves 0-1) gate, 128-255 (waves 2-3) up
+  const bf16* dma_base = is_w ? ((GATED && wv >= GWAVES / 4) ? base_w1 : base_w0) : base_x;
+  constexpr int NQ = GROWS / 16 / GWAVES;   // DMA instructions per wave per stage
+  int off[NQ];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int row = 16 * (8 * wv + q) + (lane >> 2);   // LDS row 0..511
+  for (int q = 0; q < NQ; ++q) {
+    const int row = 16 * (NQ * wv + q) + (lane >> 2);   // LDS row 0..511
     if (is_w) {
       const int r = GATED ? (row & 127) : row;
       off[q] = min(row_w0 + r, a.R - 1) * a.K + 8 * chunk;
@@ -196,13 +203,13 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
     }
   }
 
-  f32x4_t acc[NW][WT][8];
+  f32x4_t acc[NW][WT][GTT];
 #pragma unroll
   for (int m = 0; m < NW; ++m)
 #pragma unroll
     for (int i = 0; i < WT; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[m][i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < GTT; ++j) acc[m][i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nsub = GATED ? 1 : a.n_sub;
   const int kst = a.K / GK;          // K % 32 == 0 on this path
@@ -211,16 +218,16 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   const int k_lo = a.ksplit > 1 ? blockIdx.y * per : 0;
   const int k_hi = a.ksplit > 1 ? min(nst, k_lo + per) : nst;
 
-  // Every step issues exactly 8 DMA loads per thread (stages past the range
+  // Every step issues exactly NQ DMA loads per thread (stages past the range
   // reload the last stage into a slot nobody reads again), so "stage s+1 has
-  // landed" is always "at most 16 of this thread's loads pending".
+  // landed" is always "at most 2 * NQ of this thread's loads pending".
   auto issue = [&](int st) __attribute__((always_inline)) {
-    bf16* dst = &lds[st % GSTAGES][(16 * 8 * wv) * GK];
+    bf16* dst = &lds[st % GSTAGES][(16 * NQ * wv) * GK];
     st = min(st, k_hi - 1);
     const int s_ = st / kst, ko = (st % kst) * GK;
     const bf16* src = dma_base + (is_w ? (int64_t)s_ * a.sub_stride : (int64_t)s_ * a.sub_k_off) + ko;
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
+    for (int q = 0; q < NQ; ++q)
       __builtin_amdgcn_global_load_lds((const void*)(src + off[q]),
                                        (__attribute__((address_space(3))) void*)(dst + q * 16 * GK),
                                        16, 0, 0);
@@ -234,15 +241,15 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
     issue(k_lo);
     issue(k_lo + 1);
     issue(k_lo + 2);
-    GEMM_VMCNT(16);
+    GEMM_VMCNT_STAGES2();
   }
   __builtin_amdgcn_s_barrier();
   for (int st = k_lo; st < k_hi; ++st) {
     issue(st + GSTAGES - 1);
     const uint32_t sl = lds0 + (uint32_t)((st % GSTAGES) * GROWS * GK * 2) + lane_off;
-    u32x4 fb[8], fa[NW * WT];
+    u32x4 fb[GTT], fa[NW * WT];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) fb[j] = lds_read16(sl + (uint32_t)((256 + wn * 128 + 16 * j) * GK * 2));
+    for (int j = 0; j < GTT; ++j) fb[j] = lds_read16(sl + (uint32_t)((256 + wn * 16 * GTT + 16 * j) * GK * 2));
 #pragma unroll
     for (int m = 0; m < NW; ++m)
 #pragma unroll
@@ -254,19 +261,19 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < WT; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < GTT; ++j)
           acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               __builtin_bit_cast(bf16x8_t, fa[m * WT + i]), __builtin_bit_cast(bf16x8_t, fb[j]),
               acc[m][i][j], 0, 0, 0);
-    GEMM_VMCNT(16);   // this thread's loads for stage st+1 have landed
+    GEMM_VMCNT_STAGES2();   // this thread's loads for stage st+1 have landed
     __builtin_amdgcn_s_barrier();
   }
   GEMM_VMCNT(0);      // no DMA may outlive the workgroup's LDS
 
   // epilogue: lane holds weight rows 4*kg..+3 of tile i, token r16 of tile j
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int tr = mt.row0 + wn * 128 + 16 * j + r16;   // token row within segment
+  for (int j = 0; j < GTT; ++j) {
+    const int tr = mt.row0 + wn * 16 * GTT + 16 * j + r16;   // token row within segment
     if (tr >= mt.n) continue;
 #pragma unroll
     for (int i = 0; i < WT; ++i) {
@@ -287,6 +294,7 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   }
 }
 #undef GEMM_VMCNT
+#undef GEMM_VMCNT_STAGES2
 
 // Sum of k-split partials: y[i] = sum_s part[s][i] (float4 per thread).
 __global__ void __launch_bounds__(256)
