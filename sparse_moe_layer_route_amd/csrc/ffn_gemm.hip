@@ -17,8 +17,9 @@
 // loads, no register staging) into a 4-deep ring, so three stages are in
 // flight while one feeds the MFMAs: the L2/HBM latency of a stage (microseconds under load)
 // is covered by three stages of math.  Each 64-byte LDS row holds four
-// 16-byte k chunks stored at chunk ^ ((row / 4) % 4), so the 16 lanes reading
-// one fragment column hit distinct banks.  Ordering is explicit: a thread
+// 16-byte k chunks stored at chunk ^ ((row / 2) % 4): a 16-byte LDS read is
+// served eight lanes at a time over 32 banks, and the eight rows of one such
+// group then cover all 32 banks once.  Ordering is explicit: a thread
 // waits for its own DMA loads with a vmcnt wait, then a workgroup barrier
 // publishes the stage; a slot is refilled only after the barrier that ends
 // its last read.  A long contraction over few tiles (the shared experts' down
@@ -82,6 +83,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
   u32x4 r;
   asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+  return r;
+}
+// Same, with a compile-time byte offset folded into the instruction.
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read16_at(uint32_t base) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(base), "n"(OFF) : "memory");
   return r;
 }
 
@@ -151,6 +160,25 @@ __device__ __forceinline__ bool find_mtile(const GemmArgs a, int m_idx, MTile& m
 #define GEMM_VMCNT(N) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory")
 // at most two later stages of this thread's DMA loads still pending
 #define GEMM_VMCNT_STAGES2() GEMM_VMCNT(2 * NQ)
+#define GEMM_VMCNT_STAGES1() GEMM_VMCNT(NQ)
+
+// The GTT token fragments (LDS rows sb + 16j) and NW*WT weight fragments (rows
+// sa + m*MW + 16i) of one stage; row offsets are instruction immediates.
+template <int J, int NJ>
+__device__ __forceinline__ void read_fb(u32x4 (&fb)[NJ], uint32_t sb) {
+  if constexpr (J < NJ) {
+    fb[J] = lds_read16_at<16 * J * GK * 2>(sb);
+    read_fb<J + 1, NJ>(fb, sb);
+  }
+}
+template <int NW, int WT, int MW, int Q>
+__device__ __forceinline__ void read_fa(u32x4 (&fa)[NW * WT], uint32_t sa) {
+  if constexpr (Q < NW * WT) {
+    constexpr int m = Q / WT, i = Q % WT;
+    fa[Q] = lds_read16_at<(m * MW + 16 * i) * GK * 2>(sa);
+    read_fa<NW, WT, MW, Q + 1>(fa, sa);
+  }
+}
 
 // GATED: GEMM1 (gate and up matrices, 128 rows each, SiLU product, bf16 out);
 // else GEMM2 (256 down rows, fp32 out).  Either way a block stages 256 weight
@@ -171,13 +199,17 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   const int wm = wv & 1, wn = wv >> 1;       // 2 x 4 waves: weight half, token quarter
   const int r16 = lane & 15, kg = lane >> 4;
   const int row_w0 = n_idx * MW;             // first weight row of the tile
+  // a wave whose 64 tokens all lie past the segment end (the last m-tile of a
+  // segment) still moves its share of the stages but skips the MFMAs
+  const bool tok_live = mt.row0 + wn * 16 * GTT < mt.n;
 
   // DMA plan: a stage is 512 LDS rows x 64 B; one wave instruction writes 16
   // rows (1 KiB, lane l -> row l/4, 16-byte slot l%4).  Wave w issues
   // instructions NQ*w..NQ*w+NQ-1: waves 0-3 the weight rows (GATED: 0-127
   // gate, 128-255 up), waves 4-7 the token rows.  Slot p of row r holds k chunk
-  // p ^ ((r/4) % 4), so the 16 rows of one fragment read hit distinct banks.
-  const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
+  // p ^ ((r/2) % 4), so each 8-row group of a fragment read hits 32 distinct
+  // banks.
+  const int chunk = (lane & 3) ^ ((lane >> 3) & 3);
   const bf16* base_w0 = a.w0 + (int64_t)mt.g * a.w_stride;
   const bf16* base_w1 = GATED ? a.w1 + (int64_t)mt.g * a.w_stride : base_w0;
   const bf16* base_x = GATED ? a.x : a.act_in;
@@ -185,6 +217,7 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   // GATED: LDS rows 0-127 (waves 0-1) gate, 128-255 (waves 2-3) up
   const bf16* dma_base = is_w ? ((GATED && wv >= GWAVES / 4) ? base_w1 : base_w0) : base_x;
   constexpr int NQ = GROWS / 16 / GWAVES;   // DMA instructions per wave per stage
+  constexpr int NMF = NW * WT * GTT;        // MFMAs per wave per stage
   int off[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
@@ -221,53 +254,86 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   // Every step issues exactly NQ DMA loads per thread (stages past the range
   // reload the last stage into a slot nobody reads again), so "stage s+1 has
   // landed" is always "at most 2 * NQ of this thread's loads pending".
-  auto issue = [&](int st) __attribute__((always_inline)) {
+  // DMA instruction q of stage st (each stage is NQ instructions per thread).
+  auto issue_one = [&](int st, int q) __attribute__((always_inline)) {
     bf16* dst = &lds[st % GSTAGES][(16 * NQ * wv) * GK];
     st = min(st, k_hi - 1);
     const int s_ = st / kst, ko = (st % kst) * GK;
     const bf16* src = dma_base + (is_w ? (int64_t)s_ * a.sub_stride : (int64_t)s_ * a.sub_k_off) + ko;
-#pragma unroll
-    for (int q = 0; q < NQ; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(src + off[q]),
-                                       (__attribute__((address_space(3))) void*)(dst + q * 16 * GK),
-                                       16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(src + off[q]),
+                                     (__attribute__((address_space(3))) void*)(dst + q * 16 * GK),
+                                     16, 0, 0);
   };
-  // byte address of this lane's fragment slot: logical chunk kg of row r
-  // lives at physical chunk kg ^ ((r/4) % 4); rows here are 16-aligned + r16
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)&lds[0][0];
-  const uint32_t lane_off = (uint32_t)(r16 * GK * 2 + ((kg ^ ((r16 >> 2) & 3)) * 16));
+  auto issue = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) issue_one(st, q);
+  };
 
+  // byte address of this lane's fragment slot: logical chunk kg of row r
+  // lives at physical chunk kg ^ ((r/2) % 4); rows here are 16-aligned + r16
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)&lds[0][0];
+  const uint32_t lane_off = (uint32_t)(r16 * GK * 2 + ((kg ^ ((r16 >> 1) & 3)) * 16));
+
+  // Stage st's fragments sit in one register set while the next stage's are
+  // read into the other: after the barrier that publishes stage st+1 a wave
+  // starts its LDS reads, runs stage st's MFMAs from registers, then waits for
+  // the reads.  The last stage reads a slot holding a duplicate stage, which
+  // is never multiplied.
+#define GEMM_READ(FB, FA, st_)                                                          \
+  {                                                                                     \
+    const uint32_t sl = lds0 + (uint32_t)(((st_) % GSTAGES) * GROWS * GK * 2) + lane_off; \
+    read_fb<0, GTT>(FB, sl + (uint32_t)((256 + wn * 16 * GTT) * GK * 2));              \
+    read_fa<NW, WT, MW, 0>(FA, sl + (uint32_t)(wm * (MW / 2) * GK * 2));               \
+  }
+#define GEMM_MFMA(FB, FA)                                                               \
+  _Pragma("unroll") for (int m = 0; m < NW; ++m)                                        \
+    _Pragma("unroll") for (int i = 0; i < WT; ++i)                                      \
+      _Pragma("unroll") for (int j = 0; j < GTT; ++j)                                   \
+        acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                         \
+            __builtin_bit_cast(bf16x8_t, FA[m * WT + i]), __builtin_bit_cast(bf16x8_t, FB[j]), \
+            acc[m][i][j], 0, 0, 0);
+#define GEMM_MFMA_PART(FB, FA, q)                                                       \
+  _Pragma("unroll") for (int t = 0; t < NMF / NQ; ++t) {                                \
+    const int L = (q) * (NMF / NQ) + t;                                                 \
+    const int m = L / (WT * GTT), i = (L / GTT) % WT, j = L % GTT;                      \
+    acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                             \
+        __builtin_bit_cast(bf16x8_t, FA[m * WT + i]), __builtin_bit_cast(bf16x8_t, FB[j]), \
+        acc[m][i][j], 0, 0, 0);                                                         \
+  }
+  // The refill of the slot freed two barriers ago is spread over the MFMAs so
+  // the waves do not queue their DMA instructions all at once.
+#define GEMM_STEP(FBc, FAc, FBn, FAn, st_)                                              \
+  {                                                                                     \
+    GEMM_VMCNT_STAGES1();                                                               \
+    __builtin_amdgcn_s_barrier();                                                       \
+    GEMM_READ(FBn, FAn, (st_) + 1);                                                     \
+    __builtin_amdgcn_sched_barrier(0); /* reads issue before the MFMAs */              \
+    _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                    \
+      issue_one((st_) + GSTAGES - 1, q);                                                \
+      __builtin_amdgcn_sched_barrier(0);                                                \
+      if (tok_live) { GEMM_MFMA_PART(FBc, FAc, q); }                                    \
+      __builtin_amdgcn_sched_barrier(0);                                                \
+    }                                                                                   \
+    lds_wait_all(FBn, FAn);                                                             \
+  }
   if (k_lo < k_hi) {
+    u32x4 fb0[GTT], fa0[NW * WT], fb1[GTT], fa1[NW * WT];
     issue(k_lo);
     issue(k_lo + 1);
     issue(k_lo + 2);
     GEMM_VMCNT_STAGES2();
-  }
-  __builtin_amdgcn_s_barrier();
-  for (int st = k_lo; st < k_hi; ++st) {
-    issue(st + GSTAGES - 1);
-    const uint32_t sl = lds0 + (uint32_t)((st % GSTAGES) * GROWS * GK * 2) + lane_off;
-    u32x4 fb[GTT], fa[NW * WT];
-#pragma unroll
-    for (int j = 0; j < GTT; ++j) fb[j] = lds_read16(sl + (uint32_t)((256 + wn * 16 * GTT + 16 * j) * GK * 2));
-#pragma unroll
-    for (int m = 0; m < NW; ++m)
-#pragma unroll
-      for (int i = 0; i < WT; ++i)
-        fa[m * WT + i] = lds_read16(sl + (uint32_t)((m * MW + wm * (MW / 2) + 16 * i) * GK * 2));
-    lds_wait_all(fb, fa);
-#pragma unroll
-    for (int m = 0; m < NW; ++m)
-#pragma unroll
-      for (int i = 0; i < WT; ++i)
-#pragma unroll
-        for (int j = 0; j < GTT; ++j)
-          acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, fa[m * WT + i]), __builtin_bit_cast(bf16x8_t, fb[j]),
-              acc[m][i][j], 0, 0, 0);
-    GEMM_VMCNT_STAGES2();   // this thread's loads for stage st+1 have landed
     __builtin_amdgcn_s_barrier();
+    GEMM_READ(fb0, fa0, k_lo);
+    lds_wait_all(fb0, fa0);
+    for (int st = k_lo; st < k_hi; st += 2) {
+      GEMM_STEP(fb0, fa0, fb1, fa1, st);
+      if (st + 1 < k_hi) GEMM_STEP(fb1, fa1, fb0, fa0, st + 1);
+    }
   }
+#undef GEMM_READ
+#undef GEMM_MFMA
+#undef GEMM_STEP
+#undef GEMM_MFMA_PART
   GEMM_VMCNT(0);      // no DMA may outlive the workgroup's LDS
 
   // epilogue: lane holds weight rows 4*kg..+3 of tile i, token r16 of tile j
@@ -295,6 +361,7 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
 }
 #undef GEMM_VMCNT
 #undef GEMM_VMCNT_STAGES2
+#undef GEMM_VMCNT_STAGES1
 
 // Sum of k-split partials: y[i] = sum_s part[s][i] (float4 per thread).
 __global__ void __launch_bounds__(256)
