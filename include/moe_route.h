@@ -177,7 +177,9 @@ moe_status_t moe_prefetch_mask(const moe_dims_t* dims, int32_t T, const void* x,
  * f = t*k + j.  expert_offsets [E+1]; perm [T*k] holds f, grouped by expert,
  * f increasing inside a group (first offsets[E] entries); inv [T*k] = position
  * of pair f in perm, or -1 when not exact.  ws: at least
- * moe_workspace_size(dims with these T, k, E, STANDARD) bytes. */
+ * moe_workspace_size(dims with these T, k, E, STANDARD) bytes; it holds the
+ * per-chunk bucket histograms when T*k > 1024 and may be NULL below that
+ * (MOE_EWORKSPACE when too small). */
 moe_status_t moe_permute(int32_t T, int32_t k, int32_t E, const int32_t* topk_ids,
                          const uint8_t* exact, int32_t* expert_offsets, int32_t* perm,
                          int32_t* inv, void* ws, size_t ws_bytes, void* stream);

@@ -15,7 +15,8 @@ hipError_t launch_prefetch(const moe_dims_t& d, int T, const void* x, const void
                            hipStream_t s);
 hipError_t launch_permute(int n_pairs, int E, const int32_t* ids, const uint8_t* exact,
                           int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* row_of,
-                          int32_t* miss_offsets, hipStream_t s);
+                          int32_t* miss_offsets, int32_t* scratch, hipStream_t s);
+int permute_scratch_bytes(int n_pairs, int E);
 hipError_t launch_dense_ffn(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
                             const int32_t* offsets, const int32_t* perm, int n_pairs_max,
                             float* act, float* y_perm, float* act_s, float* y_s, const Prof& pf,
@@ -109,7 +110,7 @@ moe_status_t check_weights(const moe_dims_t* d, const moe_weights_t* w, moe_mode
 
 // Workspace plan for T tokens.
 struct Plan {
-  size_t ids, w, exact, flags, logits, offsets, moffsets, perm, inv, row_of;  // routing + permutation
+  size_t ids, w, exact, flags, logits, offsets, moffsets, perm, inv, row_of, pscratch;  // routing + permutation
   size_t y_perm, y_s, g_s;                                            // FFN outputs
   size_t act, act_s;                                                  // fp32 GEMV activations
   size_t act_b, acts_b, z_b;                                          // bf16 MFMA activations
@@ -142,6 +143,7 @@ Plan make_plan(const moe_dims_t& d, int T, moe_mode_t mode) {
   p.offsets = take((size_t)(d.n_experts + 1) * 4);
   p.moffsets = take((size_t)(d.n_experts + 1) * 4);
   p.perm = take(P * 4);
+  p.pscratch = take((size_t)permute_scratch_bytes((int)P, d.n_experts));
   p.inv = take(P * 4);
   p.row_of = take(P * 4);
   p.y_perm = take(P * H * 4);
@@ -279,15 +281,16 @@ moe_status_t moe_prefetch_mask(const moe_dims_t* dims, int32_t T, const void* x,
 moe_status_t moe_permute(int32_t T, int32_t k, int32_t E, const int32_t* topk_ids,
                          const uint8_t* exact, int32_t* expert_offsets, int32_t* perm, int32_t* inv,
                          void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (T < 0 || k <= 0 || E <= 0) return MOE_EINVAL;
   if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || T > kMaxTokens) return MOE_EUNSUPPORTED;
   if (!ok_ptr(topk_ids) || !ok_ptr(exact) || !ok_ptr(expert_offsets) || !ok_ptr(perm) ||
       !ok_ptr(inv))
     return MOE_EINVAL;
+  const size_t need = (size_t)permute_scratch_bytes(T * k, E);
+  if (need > 0 && !ok_ptr(ws)) return MOE_EINVAL;
+  if (ws_bytes < need) return MOE_EWORKSPACE;
   return hip_status(launch_permute(T * k, E, topk_ids, exact, expert_offsets, perm, inv, nullptr,
-                                   nullptr, (hipStream_t)stream));
+                                   nullptr, need > 0 ? (int32_t*)ws : nullptr, (hipStream_t)stream));
 }
 
 moe_status_t moe_expert_ffn(const moe_dims_t* dims, int32_t T, const void* x,
@@ -407,7 +410,8 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, int32_t T, const void* x,
                      d.shared_gate ? w->w_shared_gate : nullptr, g_s, s);
   if (e == hipSuccess) e = pf.end(MOE_KERNEL_ROUTE, s);
   if (e == hipSuccess) e = pf.begin(MOE_KERNEL_PERMUTE, s);
-  if (e == hipSuccess) e = launch_permute(P, E, ids, exact, offsets, perm, inv, row_of, moffsets, s);
+  if (e == hipSuccess) e = launch_permute(P, E, ids, exact, offsets, perm, inv, row_of, moffsets,
+                                           at<int32_t>(ws, p.pscratch), s);
   if (e == hipSuccess) e = pf.end(MOE_KERNEL_PERMUTE, s);
   if (e == hipSuccess)
     e = run_ffn(d, T, x, *w, mode, offsets, moffsets, perm, y_perm, y_s, keep, flags, ws, p,

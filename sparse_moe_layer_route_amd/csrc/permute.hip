@@ -2,12 +2,16 @@
 // pairs f = t*k + j into 2E buckets -- exactly computed pairs by expert
 // first, then pairs left to the LoRE surrogate by expert.
 //
-// One 1024-thread workgroup: LDS histogram (order-free atomics on counts),
-// a shuffle scan for the bucket offsets, then a stable scatter in chunks of
-// 1024 pairs.  Inside a chunk a pair's rank among equal buckets is the
-// popcount of its wave's peer mask (eight ballots over the bits of
-// bucket+1) below its lane, plus the counts of the same bucket in the waves
-// before it -- no order-dependent atomics, so perm is deterministic.
+// Pairs are taken in chunks of 1024 (one 1024-thread workgroup per chunk).
+// A count kernel writes each chunk's bucket histogram (LDS atomics on
+// counts, whose order does not matter); the scatter kernel's block c then
+// sums the histograms -- all chunks for the bucket bases, chunks before c for
+// its own start in each bucket -- and places its chunk.  Inside a chunk a
+// pair's rank among equal buckets is the popcount of its wave's peer mask
+// (eight ballots over the bits of bucket+1) below its lane, plus the counts
+// of the same bucket in the waves before it, so the order is stable and
+// deterministic with no order-dependent atomics.  Up to 1024 pairs the
+// histogram is taken inside the single scatter block (one launch).
 #include "common.h"
 
 namespace moe {
@@ -25,27 +29,65 @@ __device__ __forceinline__ int bucket_of(int f, int E, const int32_t* __restrict
   return exact[f] ? e : E + e;
 }
 
+// Histogram of chunk blockIdx.x into counts[blockIdx.x][2E].
+__global__ void __launch_bounds__(PERM_THREADS)
+permute_count_kernel(int n_pairs, int E, const int32_t* __restrict__ ids,
+                     const uint8_t* __restrict__ exact, int32_t* __restrict__ counts) {
+  __shared__ int cnt[PERM_BUCKETS];
+  const int tid = threadIdx.x, NB = 2 * E;
+  if (tid < PERM_BUCKETS) cnt[tid] = 0;
+  __syncthreads();
+  const int f = blockIdx.x * PERM_THREADS + tid;
+  if (f < n_pairs) {
+    const int b = bucket_of(f, E, ids, exact);
+    if (b >= 0) atomicAdd(&cnt[b], 1);
+  }
+  __syncthreads();
+  if (tid < NB) counts[(int64_t)blockIdx.x * NB + tid] = cnt[tid];
+}
+
+// Block c places chunk c.  counts == nullptr: a single block histograms the
+// (at most one) chunk itself.
 __global__ void __launch_bounds__(PERM_THREADS)
 permute_kernel(int n_pairs, int E, const int32_t* __restrict__ ids, const uint8_t* __restrict__ exact,
-               int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
-               int32_t* __restrict__ row_of, int32_t* __restrict__ miss_offsets) {
-  __shared__ int cnt[PERM_BUCKETS];
+               const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+               int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ row_of,
+               int32_t* __restrict__ miss_offsets) {
+  __shared__ int tot[PERM_BUCKETS];     // pairs per bucket over all chunks
+  __shared__ int before[PERM_BUCKETS];  // pairs per bucket in earlier chunks
   __shared__ int cursor[PERM_BUCKETS];
   __shared__ int wcnt[PERM_WAVES][PERM_BUCKETS];
   __shared__ int s_total;
   const int tid = threadIdx.x, lane = tid & (MOE_WAVE - 1), wv = tid >> 6;
   const int NB = 2 * E;
-  if (tid < PERM_BUCKETS) cnt[tid] = 0;
-  __syncthreads();
-  for (int f = tid; f < n_pairs; f += PERM_THREADS) {
-    const int b = bucket_of(f, E, ids, exact);
-    if (b >= 0) atomicAdd(&cnt[b], 1);
+  const int chunk = blockIdx.x;
+  const int f = chunk * PERM_THREADS + tid;
+  const int b = f < n_pairs ? bucket_of(f, E, ids, exact) : -1;
+  if (counts) {
+    if (tid < NB) {
+      const int nchunks = gridDim.x;
+      int t = 0, bf = 0;
+      for (int c = 0; c < nchunks; ++c) {
+        const int v = counts[(int64_t)c * NB + tid];
+        t += v;
+        if (c < chunk) bf += v;
+      }
+      tot[tid] = t;
+      before[tid] = bf;
+    }
+  } else {
+    if (tid < PERM_BUCKETS) {
+      tot[tid] = 0;
+      before[tid] = 0;
+    }
+    __syncthreads();
+    if (b >= 0) atomicAdd(&tot[b], 1);
   }
   __syncthreads();
   if (tid < MOE_WAVE) {
     // two buckets per lane: 2*lane, 2*lane+1 (NB <= 128)
-    const int c0 = 2 * lane < NB ? cnt[2 * lane] : 0;
-    const int c1 = 2 * lane + 1 < NB ? cnt[2 * lane + 1] : 0;
+    const int c0 = 2 * lane < NB ? tot[2 * lane] : 0;
+    const int c1 = 2 * lane + 1 < NB ? tot[2 * lane + 1] : 0;
     const int c = c0 + c1;
     int s = c;
 #pragma unroll
@@ -53,59 +95,61 @@ permute_kernel(int n_pairs, int E, const int32_t* __restrict__ ids, const uint8_
       const int v = __shfl_up(s, o, MOE_WAVE);
       if (lane >= o) s += v;
     }
-    cursor[2 * lane] = s - c;
-    cursor[2 * lane + 1] = s - c + c0;
+    cursor[2 * lane] = s - c + (2 * lane < NB ? before[2 * lane] : 0);
+    cursor[2 * lane + 1] = s - c + c0 + (2 * lane + 1 < NB ? before[2 * lane + 1] : 0);
     if (lane == MOE_WAVE - 1) s_total = s;
+    if (chunk == 0) {
+      // bucket bases (chunk 0 has nothing before it)
+      if (2 * lane <= E) offsets[2 * lane] = s - c;
+      if (2 * lane + 1 <= E) offsets[2 * lane + 1] = s - c + c0;
+    }
   }
   __syncthreads();
-  if (tid <= E) {
-    offsets[tid] = cursor[tid];                       // cursor[E] = number of exact pairs
-    if (miss_offsets) miss_offsets[tid] = tid < E ? cursor[E + tid] : s_total;
-  }
-  __syncthreads();
+  if (chunk == 0 && miss_offsets && tid <= E) miss_offsets[tid] = tid < E ? cursor[E + tid] : s_total;
   const uint64_t below = (1ull << lane) - 1ull;
-  for (int base = 0; base < n_pairs; base += PERM_THREADS) {
-    const int f = base + tid;
-    const int b = f < n_pairs ? bucket_of(f, E, ids, exact) : -1;
-    const int v = b + 1;  // 0..128
-    uint64_t peers = __ballot(1);
+  const int v = b + 1;  // 0..128
+  uint64_t peers = __ballot(1);
 #pragma unroll
-    for (int bit = 0; bit < 8; ++bit) {
-      const bool on = (v >> bit) & 1;
-      const uint64_t bal = __ballot(on);
-      peers &= on ? bal : ~bal;
-    }
-    const int rank = __popcll(peers & below);
-    wcnt[wv][lane] = 0;
-    wcnt[wv][lane + MOE_WAVE] = 0;
-    __builtin_amdgcn_wave_barrier();
-    if (b >= 0 && rank == 0) wcnt[wv][b] = __popcll(peers);
-    __syncthreads();
-    if (b >= 0) {
-      int pos = cursor[b] + rank;
-      for (int w2 = 0; w2 < wv; ++w2) pos += wcnt[w2][b];
-      perm[pos] = f;
-      inv[f] = b < E ? pos : -1;
-      if (row_of) row_of[f] = pos;
-    } else if (f < n_pairs) {
-      inv[f] = -1;
-      if (row_of) row_of[f] = -1;
-    }
-    __syncthreads();
-    if (tid < NB) {
-      int s = 0;
-      for (int w2 = 0; w2 < PERM_WAVES; ++w2) s += wcnt[w2][tid];
-      cursor[tid] += s;
-    }
-    __syncthreads();
+  for (int bit = 0; bit < 8; ++bit) {
+    const bool on = (v >> bit) & 1;
+    const uint64_t bal = __ballot(on);
+    peers &= on ? bal : ~bal;
   }
+  const int rank = __popcll(peers & below);
+  wcnt[wv][lane] = 0;
+  wcnt[wv][lane + MOE_WAVE] = 0;
+  __builtin_amdgcn_wave_barrier();
+  if (b >= 0 && rank == 0) wcnt[wv][b] = __popcll(peers);
+  __syncthreads();
+  if (b >= 0) {
+    int pos = cursor[b] + rank;
+    for (int w2 = 0; w2 < wv; ++w2) pos += wcnt[w2][b];
+    perm[pos] = f;
+    inv[f] = b < E ? pos : -1;
+    if (row_of) row_of[f] = pos;
+  } else if (f < n_pairs) {
+    inv[f] = -1;
+    if (row_of) row_of[f] = -1;
+  }
+}
+
+int permute_scratch_bytes(int n_pairs, int E) {
+  const int nchunks = (n_pairs + PERM_THREADS - 1) / PERM_THREADS;
+  return nchunks > 1 ? nchunks * 2 * E * 4 : 0;
 }
 
 hipError_t launch_permute(int n_pairs, int E, const int32_t* ids, const uint8_t* exact,
                           int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* row_of,
-                          int32_t* miss_offsets, hipStream_t s) {
-  permute_kernel<<<1, PERM_THREADS, 0, s>>>(n_pairs, E, ids, exact, offsets, perm, inv, row_of,
-                                            miss_offsets);
+                          int32_t* miss_offsets, int32_t* scratch, hipStream_t s) {
+  const int nchunks = (n_pairs + PERM_THREADS - 1) / PERM_THREADS;
+  if (nchunks <= 1) {
+    permute_kernel<<<1, PERM_THREADS, 0, s>>>(n_pairs, E, ids, exact, nullptr, offsets, perm, inv,
+                                              row_of, miss_offsets);
+  } else {
+    permute_count_kernel<<<nchunks, PERM_THREADS, 0, s>>>(n_pairs, E, ids, exact, scratch);
+    permute_kernel<<<nchunks, PERM_THREADS, 0, s>>>(n_pairs, E, ids, exact, scratch, offsets, perm,
+                                                    inv, row_of, miss_offsets);
+  }
   return hipGetLastError();
 }
 

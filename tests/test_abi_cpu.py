@@ -119,6 +119,9 @@ def test_entry_point_null_checks():
     assert L.moe_permute(4, 9, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.MOE_EUNSUPPORTED
     assert L.moe_permute(4, 2, 65, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.MOE_EUNSUPPORTED
     assert L.moe_permute(4, 2, 8, None, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.MOE_EINVAL
+    # more than 1024 pairs: the per-chunk histograms need the workspace
+    assert L.moe_permute(600, 2, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.MOE_EINVAL
+    assert L.moe_permute(600, 2, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == B.MOE_EWORKSPACE
     assert L.moe_prefetch_mask(ctypes.byref(d), 4, FAKE, FAKE, None, FAKE, FAKE, None) == B.MOE_EINVAL
     assert L.moe_lore_surrogate(ctypes.byref(dims(lore_rank=0)), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                 None) == B.MOE_EUNSUPPORTED

@@ -192,7 +192,8 @@ def test_prefetch_delta_extremes(delta):
 def test_permute_parity_random():
     rng = np.random.default_rng(7)
     for T, k, E, p_exact in [(1, 1, 1, 1.0), (37, 6, 64, 0.5), (4096, 8, 40, 1.0), (300, 8, 64, 0.0),
-                             (1000, 2, 8, 0.7), (5, 8, 64, 1.0)]:
+                             (1000, 2, 8, 0.7), (5, 8, 64, 1.0), (128, 8, 16, 0.6), (129, 8, 16, 0.6),
+                             (2999, 7, 64, 0.5)]:
         ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
         exact = (rng.random((T, k)) < p_exact).astype(np.uint8)
         d_ids = torch.from_numpy(ids.reshape(-1)).cuda()
@@ -200,7 +201,9 @@ def test_permute_parity_random():
         off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
         perm = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
         inv = torch.empty(T * k, dtype=torch.int32, device="cuda")
-        M.moe_permute(T, k, E, d_ids, d_ex, off, perm, inv)
+        ws = torch.empty(M.moe_workspace_size(M.Dims(hidden=64, n_experts=E, top_k=k, inter=16), T,
+                                               "standard"), dtype=torch.uint8, device="cuda")
+        M.moe_permute(T, k, E, d_ids, d_ex, off, perm, inv, ws)
         torch.cuda.synchronize()
         o_off, o_perm, o_inv = O.permute(ids, exact, E)
         np.testing.assert_array_equal(off.cpu().numpy(), o_off)
