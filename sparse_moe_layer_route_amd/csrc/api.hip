@@ -29,7 +29,7 @@ hipError_t launch_ffn_mfma(const moe_dims_t& d, int T, const void* x, const moe_
                            int which);
 hipError_t launch_ffn_gemm(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
                            const int32_t* offsets, const int32_t* perm, bool shared, bf16* act,
-                           float* y, float* part, hipStream_t s, int which);
+                           float* y, bf16* yb, float* part, hipStream_t s, int which);
 int gemm_shared_down_ksplit(const moe_dims_t& d, int T);
 hipError_t launch_floe(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
                        const int32_t* offsets, const int32_t* perm, float* u, int32_t* keep,
@@ -39,9 +39,9 @@ hipError_t launch_combine(const moe_dims_t& d, int T, const float* y_perm, const
                           const float* topk_w, const uint8_t* exact, const int32_t* ids,
                           const float* y_s, const float* g_s, const float* lore_out, const void* x,
                           const void* lore_A, const void* lore_B, void* out, hipStream_t s);
-hipError_t launch_combine_rows(const moe_dims_t& d, int T, const float* y_perm, const int32_t* row_of,
-                               const float* topk_w, const uint8_t* exact, const float* y_s,
-                               const float* g_s, void* out, hipStream_t s);
+hipError_t launch_combine_rows(const moe_dims_t& d, int T, const void* y_perm, bool y_bf16,
+                               const int32_t* row_of, const float* topk_w, const uint8_t* exact,
+                               const float* y_s, const float* g_s, void* out, hipStream_t s);
 hipError_t launch_lore(const moe_dims_t& d, int T, const void* x, const int32_t* ids,
                        const uint8_t* exact, const void* lore_A, const void* lore_B,
                        float* lore_out, hipStream_t s);
@@ -183,7 +183,8 @@ inline moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK :
 hipError_t run_ffn(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
                    moe_mode_t mode, const int32_t* offsets, const int32_t* moffsets,
                    const int32_t* perm, float* y_perm, float* y_s, int32_t* keep, uint32_t* flags,
-                   void* ws, const Plan& p, int lore, const Prof& pf, hipStream_t s) {
+                   void* ws, const Plan& p, int lore, const Prof& pf, hipStream_t s,
+                   bool y_bf16 = false) {
   if (mode == MOE_MODE_FLOE)
     return launch_floe(d, T, x, w, offsets, perm, at<float>(ws, p.u), keep, at<float>(ws, p.fa),
                        at<float>(ws, p.part), y_perm, flags, pf, s);
@@ -201,9 +202,10 @@ hipError_t run_ffn(const moe_dims_t& d, int T, const void* x, const moe_weights_
   auto stage = [&](int which) {
     hipError_t r = launch_ffn_mfma(d, T, x, w, offsets, moffsets, perm, b, !g_r, !g_s, lore, s, which);
     if (r == hipSuccess && g_r)
-      r = launch_ffn_gemm(d, T, x, w, offsets, perm, false, b.act, y_perm, nullptr, s, which);
+      r = launch_ffn_gemm(d, T, x, w, offsets, perm, false, b.act, y_perm,
+                          y_bf16 ? (bf16*)y_perm : nullptr, nullptr, s, which);
     if (r == hipSuccess && g_s)
-      r = launch_ffn_gemm(d, T, x, w, nullptr, nullptr, true, b.acts, y_s,
+      r = launch_ffn_gemm(d, T, x, w, nullptr, nullptr, true, b.acts, y_s, nullptr,
                           p.ys_part ? at<float>(ws, p.ys_part) : nullptr, s, which);
     return r;
   };
@@ -413,13 +415,17 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, int32_t T, const void* x,
   if (e == hipSuccess) e = launch_permute(P, E, ids, exact, offsets, perm, inv, row_of, moffsets,
                                            at<int32_t>(ws, p.pscratch), s);
   if (e == hipSuccess) e = pf.end(MOE_KERNEL_PERMUTE, s);
+  // When every expert row comes from the grouped GEMM (no LoRE rows), the
+  // rows are kept as bf16: the combine sums them in fp32 and the bytes between
+  // the two launches halve.
+  const bool y_bf16 = mfma && !lore && gemm_routed(d, T);
   if (e == hipSuccess)
     e = run_ffn(d, T, x, *w, mode, offsets, moffsets, perm, y_perm, y_s, keep, flags, ws, p,
-                mfma && lore, pf, s);
+                mfma && lore, pf, s, y_bf16);
   if (e == hipSuccess) e = pf.begin(MOE_KERNEL_COMBINE, s);
   if (e == hipSuccess) {
     if (mfma || mode == MOE_MODE_FLOE)
-      e = launch_combine_rows(d, T, y_perm, row_of, wts, exact, y_s, g_s, out, s);
+      e = launch_combine_rows(d, T, y_perm, y_bf16, row_of, wts, exact, y_s, g_s, out, s);
     else
       e = launch_combine(d, T, y_perm, inv, wts, exact, ids, y_s, g_s, nullptr, x,
                          lore ? w->lore_A : nullptr, lore ? w->lore_B : nullptr, out, s);

@@ -123,10 +123,22 @@ lore_kernel(int H, int k, int r, const Tin* __restrict__ x, const int32_t* __res
 // Combine over y_perm rows: out[t] = g_s y_s + sum_j w_j (y_perm[row_of[f]] +
 // (exact ? 0 : y_s)), f = t*k + j.  Non-exact rows already hold B_e A_e x_t,
 // so a surrogate slot contributes w_j (y_s + B_e A_e x_t).  Each thread owns
-// four consecutive columns (16-byte loads).
-template <typename Tin>
+// four consecutive columns; y_perm rows are fp32 or bf16 (Ty), the sums fp32.
+template <typename Ty>
+__device__ __forceinline__ float4 load4(const Ty* p);
+template <>
+__device__ __forceinline__ float4 load4<float>(const float* p) {
+  return *reinterpret_cast<const float4*>(p);
+}
+template <>
+__device__ __forceinline__ float4 load4<bf16>(const bf16* p) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  return float4{bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
+}
+
+template <typename Tin, typename Ty>
 __global__ void __launch_bounds__(COMBINE_THREADS)
-combine_rows_kernel(int H, int k, const float* __restrict__ y_perm, const int32_t* __restrict__ row_of,
+combine_rows_kernel(int H, int k, const Ty* __restrict__ y_perm, const int32_t* __restrict__ row_of,
                     const float* __restrict__ topk_w, const uint8_t* __restrict__ exact,
                     const float* __restrict__ y_s, const float* __restrict__ g_s,
                     Tin* __restrict__ out) {
@@ -148,7 +160,7 @@ combine_rows_kernel(int H, int k, const float* __restrict__ y_perm, const int32_
     for (int j = 0; j < k; ++j) {
       const int row = s_row[j];
       if (row < 0) continue;
-      float4 v = *reinterpret_cast<const float4*>(y_perm + (int64_t)row * H + h);
+      float4 v = load4<Ty>(y_perm + (int64_t)row * H + h);
       if (!s_ex[j]) {
         v.x += ys.x; v.y += ys.y; v.z += ys.z; v.w += ys.w;
       }
@@ -166,15 +178,21 @@ combine_rows_kernel(int H, int k, const float* __restrict__ y_perm, const int32_
   }
 }
 
-hipError_t launch_combine_rows(const moe_dims_t& d, int T, const float* y_perm, const int32_t* row_of,
-                               const float* topk_w, const uint8_t* exact, const float* y_s,
-                               const float* g_s, void* out, hipStream_t s) {
-  if (d.dtype == MOE_BF16)
-    combine_rows_kernel<bf16><<<T, COMBINE_THREADS, 0, s>>>(d.hidden, d.top_k, y_perm, row_of, topk_w,
-                                                            exact, y_s, g_s, (bf16*)out);
-  else
-    combine_rows_kernel<float><<<T, COMBINE_THREADS, 0, s>>>(d.hidden, d.top_k, y_perm, row_of, topk_w,
-                                                             exact, y_s, g_s, (float*)out);
+// y_bf16: y_perm holds bf16 rows.
+hipError_t launch_combine_rows(const moe_dims_t& d, int T, const void* y_perm, bool y_bf16,
+                               const int32_t* row_of, const float* topk_w, const uint8_t* exact,
+                               const float* y_s, const float* g_s, void* out, hipStream_t s) {
+  if (d.dtype == MOE_BF16) {
+    if (y_bf16)
+      combine_rows_kernel<bf16, bf16><<<T, COMBINE_THREADS, 0, s>>>(
+          d.hidden, d.top_k, (const bf16*)y_perm, row_of, topk_w, exact, y_s, g_s, (bf16*)out);
+    else
+      combine_rows_kernel<bf16, float><<<T, COMBINE_THREADS, 0, s>>>(
+          d.hidden, d.top_k, (const float*)y_perm, row_of, topk_w, exact, y_s, g_s, (bf16*)out);
+  } else {
+    combine_rows_kernel<float, float><<<T, COMBINE_THREADS, 0, s>>>(
+        d.hidden, d.top_k, (const float*)y_perm, row_of, topk_w, exact, y_s, g_s, (float*)out);
+  }
   return hipGetLastError();
 }
 

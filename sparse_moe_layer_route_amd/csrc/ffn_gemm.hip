@@ -62,6 +62,7 @@ struct GemmArgs {
   int64_t ld_out;       // GEMM1 out row stride
   int64_t col_off;      // GEMM1 out column offset per group (shared: I_s)
   float* y_out;         // GEMM2 out [rows][R]
+  bf16* yb_out;         // GEMM2 out as bf16 [rows][R] instead (nullptr: y_out)
   const int32_t* offsets;  // routed segments [E+1]; nullptr = one segment of T rows per group
   const int32_t* perm;
   int k;                // top-k (pair -> token)
@@ -351,6 +352,12 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
         for (int q = 0; q < 4; ++q) h[q] = f_to_bf16(silu_f(acc[0][i][j][q]) * acc[NW - 1][i][j][q]);
         bf16* dst = a.act_out + (int64_t)(mt.seg0 + tr) * a.ld_out + (int64_t)mt.g * a.col_off + wr;
         *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      } else if (a.yb_out) {
+        uint32_t h[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) h[q] = f_to_bf16(acc[0][i][j][q]);
+        bf16* dst = a.yb_out + (int64_t)(mt.seg0 + tr) * a.R + wr;
+        *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
       } else {
         float* dst = a.y_out + (int64_t)blockIdx.y * a.part_stride + (int64_t)(mt.seg0 + tr) * a.R + wr;
         *reinterpret_cast<float4*>(dst) =
@@ -392,7 +399,7 @@ int gemm_shared_down_ksplit(const moe_dims_t& d, int T) {
 // y (shared: through k-split partials in `part`, then summed).
 hipError_t launch_ffn_gemm(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
                            const int32_t* offsets, const int32_t* perm, bool shared, bf16* act,
-                           float* y, float* part, hipStream_t s, int which) {
+                           float* y, bf16* yb, float* part, hipStream_t s, int which) {
   const int H = d.hidden, E = d.n_experts;
   const int R1 = shared ? d.shared_inter : d.inter;     // GEMM1 rows
   const int G = shared ? d.n_shared : E;
@@ -444,6 +451,7 @@ hipError_t launch_ffn_gemm(const moe_dims_t& d, int T, const void* x, const moe_
     a.n_blocks = mt2 * a.tiles_n;
     a.ksplit = shared ? gemm_shared_down_ksplit(d, T) : 1;
     a.y_out = a.ksplit > 1 ? part : y;
+    a.yb_out = a.ksplit > 1 ? nullptr : yb;
     a.part_stride = (int64_t)T * H;
     const int grid = ((a.n_blocks + NXCD - 1) / NXCD) * NXCD;
     if (a.n_blocks > 0) ffn_gemm_kernel<false><<<dim3(grid, a.ksplit), GTHREADS, 0, s>>>(a);

@@ -146,7 +146,7 @@ __device__ __forceinline__ void store_bf16x4(bf16* dst, int64_t off, const float
 // k-steps per batch of the pipelined loop: two register sets of U steps each.
 template <int NA>
 struct Unroll {
-  static constexpr int U = NA <= 1 ? 2 : 1;
+  static constexpr int U = NA <= 2 ? 2 : 1;
 };
 
 // Wave wk's contiguous share [beg, end) of nsteps k-steps, in nb batches of U.
@@ -178,7 +178,7 @@ __device__ __forceinline__ void up_chunk(const FfnMfmaArgs a, const TileInfo& ti
                                          bool rows_ok, int row_base, int R,
                                          f32x4_t (*red)[(WK > 1) ? 2 * NTT : 1][MOE_WAVE]) {
   constexpr int U = Unroll<NA>::U;
-  const int lane = lane_id(), wv = threadIdx.x >> 6, wk = wv / WM;
+  const int lane = lane_id(), wv = threadIdx.x >> 6, wk = wv / WM, wm = wv % WM;
   const int r16 = lane & 15, kg = lane >> 4;
   const int H = a.H, ksteps = H >> 5;
   const bf16* xrow[NA];
@@ -224,8 +224,8 @@ __device__ __forceinline__ void up_chunk(const FfnMfmaArgs a, const TileInfo& ti
     if (wk > 0 && rows_ok) {
 #pragma unroll
       for (int j = 0; j < NA; ++j) {
-        red[wk - 1][2 * j][lane] = accg[j];
-        red[wk - 1][2 * j + 1][lane] = accu[j];
+        red[(wk - 1) * WM + wm][2 * j][lane] = accg[j];
+        red[(wk - 1) * WM + wm][2 * j + 1][lane] = accu[j];
       }
     }
     __syncthreads();
@@ -234,8 +234,8 @@ __device__ __forceinline__ void up_chunk(const FfnMfmaArgs a, const TileInfo& ti
       for (int w = 0; w < WK - 1; ++w)
 #pragma unroll
         for (int j = 0; j < NA; ++j) {
-          accg[j] += red[w][2 * j][lane];
-          accu[j] += red[w][2 * j + 1][lane];
+          accg[j] += red[w * WM + wm][2 * j][lane];
+          accu[j] += red[w * WM + wm][2 * j + 1][lane];
         }
     }
     __syncthreads();
@@ -263,7 +263,8 @@ __device__ __forceinline__ void up_chunk(const FfnMfmaArgs a, const TileInfo& ti
 template <int NTT, int WM, int WK>
 __global__ void __launch_bounds__(256) FFN_OCCUPANCY ffn_up_mfma_kernel(FfnMfmaArgs a) {
   static_assert(WM * WK == 4, "four waves per block");
-  __shared__ f32x4_t red[(WK > 1) ? (WK - 1) : 1][(WK > 1) ? 2 * NTT : 1][MOE_WAVE];
+  // k-split partials, one slot per (k-split > 0, row strip)
+  __shared__ f32x4_t red[(WK > 1) ? (WK - 1) * WM : 1][(WK > 1) ? 2 * NTT : 1][MOE_WAVE];
   const TileInfo ti = tile_of<16 * WM>(a);
   if (ti.kind < 0) return;
   const int lane = lane_id(), wv = threadIdx.x >> 6;
@@ -319,7 +320,7 @@ __device__ __forceinline__ void down_chunk(const FfnMfmaArgs a, const TileInfo& 
                                            bool rows_ok, int row_base,
                                            f32x4_t (*red)[(WK > 1) ? NTT * RW : 1][MOE_WAVE]) {
   constexpr int U = Unroll<NA>::U;
-  const int lane = lane_id(), wv = threadIdx.x >> 6, wk = wv / WM;
+  const int lane = lane_id(), wv = threadIdx.x >> 6, wk = wv / WM, wm = wv % WM;
   const int r16 = lane & 15, kg = lane >> 4;
   const int H = a.H;
   const int K = ti.kind == 0 ? a.I : (ti.kind == 1 ? a.Is : a.r);
@@ -400,7 +401,7 @@ __device__ __forceinline__ void down_chunk(const FfnMfmaArgs a, const TileInfo& 
 #pragma unroll
       for (int j = 0; j < NA; ++j)
 #pragma unroll
-        for (int q = 0; q < RW; ++q) red[wk - 1][j * RW + q][lane] = acc[j][q];
+        for (int q = 0; q < RW; ++q) red[(wk - 1) * WM + wm][j * RW + q][lane] = acc[j][q];
     }
     __syncthreads();
     if (wk == 0 && rows_ok) {
@@ -409,7 +410,7 @@ __device__ __forceinline__ void down_chunk(const FfnMfmaArgs a, const TileInfo& 
 #pragma unroll
         for (int j = 0; j < NA; ++j)
 #pragma unroll
-          for (int q = 0; q < RW; ++q) acc[j][q] += red[w][j * RW + q][lane];
+          for (int q = 0; q < RW; ++q) acc[j][q] += red[w * WM + wm][j * RW + q][lane];
     }
     __syncthreads();
   }
@@ -433,7 +434,8 @@ __device__ __forceinline__ void down_chunk(const FfnMfmaArgs a, const TileInfo& 
 template <int NTT, int WM, int WK, int RW>
 __global__ void __launch_bounds__(256) FFN_OCCUPANCY ffn_down_mfma_kernel(FfnMfmaArgs a) {
   static_assert(WM * WK == 4, "four waves per block");
-  __shared__ f32x4_t red[(WK > 1) ? (WK - 1) : 1][(WK > 1) ? NTT * RW : 1][MOE_WAVE];
+  // k-split partials, one slot per (k-split > 0, row strip)
+  __shared__ f32x4_t red[(WK > 1) ? (WK - 1) * WM : 1][(WK > 1) ? NTT * RW : 1][MOE_WAVE];
   const TileInfo ti = tile_of<16 * RW * WM>(a);
   if (ti.kind < 0) return;
   const int wv = threadIdx.x >> 6;
@@ -485,7 +487,13 @@ hipError_t launch_ffn_mfma(const moe_dims_t& d, int T, const void* x, const moe_
                            const int32_t* offsets, const int32_t* moffsets, const int32_t* perm,
                            const FfnBuffers& b, int routed, int shared, int lore, hipStream_t s,
                            int which) {
-  const int ntiles_tok = (T + 15) / 16;  // the largest segment has at most T tokens
+  // Token tiles per pass: every token when shared tiles are in the launch;
+  // otherwise about twice the mean routed segment (a longer segment loops
+  // over chunks, rereading its weights from cache).
+  const bool shared_on = shared && d.n_shared > 0;
+  const int seg_est = std::max(16, (int)((2LL * T * d.top_k + d.n_experts - 1) / d.n_experts));
+  const int cover = shared_on ? T : std::min(T, seg_est);
+  const int ntiles_tok = (cover + 15) / 16;
   int NTT = 1;
   while (NTT < ntiles_tok && NTT < 16) NTT <<= 1;
   const int WM = NTT <= 4 ? 1 : (NTT == 8 ? 2 : 4);

@@ -47,6 +47,11 @@ SMALL = {
     "prefill_small": _variant("dsv2_lite", name="prefill_small", hidden=256, n_experts=4, top_k=2,
                               inter=192, n_shared=1, shared_inter=320, token_counts=(300,),
                               resident_count=2, seed=106),
+    # 65-128 tokens with the shared experts on the decode kernels: eight
+    # 16-token tiles, two row strips x two k-splits per block
+    "dsv2_t100": _variant("dsv2_lite", name="dsv2_t100", hidden=512, n_experts=16, top_k=4,
+                          inter=384, shared_inter=256, token_counts=(100,), resident_count=8,
+                          seed=107),
 }
 FLOE_SMALL = {
     "floe_small": _variant("mixtral_floe", name="floe_small", hidden=1024, n_experts=4, inter=1040,
@@ -79,6 +84,7 @@ def _check_full(layer, T, mode, sample=None, dims_over=None):
     ("qwen2_small", "standard"), ("qwen2_small", "lore"),
     ("granite_small", "standard"), ("granite_small", "stall_free"),
     ("prefill_small", "standard"), ("prefill_small", "lore"),
+    ("dsv2_t100", "standard"), ("dsv2_t100", "lore"),
 ])
 def test_small_layer_parity(name, mode):
     layer = W.Layer(SMALL[name])
