@@ -16,9 +16,10 @@
 //
 // Tile kinds, in the order blockIdx.x enumerates them:
 //   1 shared   up:   act_s = SiLU(W_sg x) * (W_su x)   down: y_s = sum_s W_sd act_s
+//   2 LoRE     up:   z = A_e x  (r rows)               down: y = B_e z (all H rows per block)
 //   0 routed   up:   act = SiLU(W_g x) * (W_u x)       down: y = W_d act
-//   2 LoRE     up:   z = A_e x  (r rows)               down: y = B_e z
-// Shared tiles carry every token of the batch, so they start first instead of
+// Shared tiles carry every token of the batch and LoRE tiles are short
+// latency-bound chains, so both start before the routed bulk instead of
 // running as a tail.  SPICE's surrogate for a non-resident slot is
 // y_shared + B_e A_e x [SPICE page, "LoRE low-rank surrogate"]; the B_e A_e x
 // part lands in the pair's y_perm row and the combine adds y_shared.
@@ -109,7 +110,6 @@ __device__ __forceinline__ TileInfo tile_of(const FfnMfmaArgs a) {
   __shared__ int s_e, s_seg0, s_n;
   TileInfo ti;
   int b = blockIdx.x;
-  const int nr = a.slots_r * a.tiles_r;
   const int nsh = a.n_shared_seg * a.tiles_s;
   if (b < nsh) {
     ti.kind = 1;
@@ -120,15 +120,16 @@ __device__ __forceinline__ TileInfo tile_of(const FfnMfmaArgs a) {
     return ti;
   }
   b -= nsh;
-  if (b < nr) {
-    ti.kind = 0;
-    ti.row0 = (b % a.tiles_r) * ROWS;
-    nth_segment(a.offsets, a.E, b / a.tiles_r, &s_e, &s_seg0, &s_n);
-  } else {
-    b -= nr;
+  const int nl = a.slots_l * a.tiles_l;
+  if (b < nl) {
     ti.kind = 2;
     ti.row0 = (b % a.tiles_l) * ROWS;
     nth_segment(a.moffsets, a.E, b / a.tiles_l, &s_e, &s_seg0, &s_n);
+  } else {
+    b -= nl;
+    ti.kind = 0;
+    ti.row0 = (b % a.tiles_r) * ROWS;
+    nth_segment(a.offsets, a.E, b / a.tiles_r, &s_e, &s_seg0, &s_n);
   }
   if (s_e < 0) ti.kind = -1;
   ti.e = s_e;
@@ -315,12 +316,16 @@ __global__ void __launch_bounds__(256) FFN_OCCUPANCY ffn_up_mfma_kernel(FfnMfmaA
 // ------------------------------------------------------------------- down --
 // Output rows are H for every kind; K is I (routed), Is per shared expert
 // (summed over the ns sub-matrices), or r (LoRE).  A wave owns RW row tiles.
+// solo (block-uniform): the wave covers the whole contraction itself and no
+// k-split reduction takes place (LoRE B_e tiles, where K = r is short).
 template <int NA, int NTT, int WM, int WK, int RW>
 __device__ __forceinline__ void down_chunk(const FfnMfmaArgs a, const TileInfo& ti, int c0,
                                            bool rows_ok, int row_base,
-                                           f32x4_t (*red)[(WK > 1) ? NTT * RW : 1][MOE_WAVE]) {
+                                           f32x4_t (*red)[(WK > 1) ? NTT * RW : 1][MOE_WAVE],
+                                           bool solo) {
   constexpr int U = Unroll<NA>::U;
-  const int lane = lane_id(), wv = threadIdx.x >> 6, wk = wv / WM, wm = wv % WM;
+  const int lane = lane_id(), wv = threadIdx.x >> 6, wm = wv % WM;
+  const int wk = solo ? 0 : wv / WM, nwk = solo ? 1 : WK;
   const int r16 = lane & 15, kg = lane >> 4;
   const int H = a.H;
   const int K = ti.kind == 0 ? a.I : (ti.kind == 1 ? a.Is : a.r);
@@ -354,7 +359,7 @@ __device__ __forceinline__ void down_chunk(const FfnMfmaArgs a, const TileInfo& 
           wrow[q] = a.wl + ((int64_t)ti.e * H + h) * a.r + 8 * kg;
       }
       const int64_t so = ti.kind == 1 ? (int64_t)s * a.Is : 0;
-      const KRange kr = k_range<U>(kfull, wk, WK);
+      const KRange kr = k_range<U>(kfull, wk, nwk);
       if (kr.nb > 0) {
         bf16x8_t w0[U][RW], b0[U][NA], w1[U][RW], b1[U][NA];
 #define DN_LOAD(W, B, b)                                                       \
@@ -383,7 +388,7 @@ __device__ __forceinline__ void down_chunk(const FfnMfmaArgs a, const TileInfo& 
       }
       // partial last step (K % 32 != 0): lanes whose 8 k values lie past K
       // feed zeros to both operands
-      if ((K & 31) && wk == WK - 1) {
+      if ((K & 31) && wk == nwk - 1) {
         const int ko = kfull << 5;
         const bool live = ko + 8 * kg < K;
 #pragma unroll
@@ -396,7 +401,7 @@ __device__ __forceinline__ void down_chunk(const FfnMfmaArgs a, const TileInfo& 
       }
     }
   }
-  if (WK > 1) {
+  if (WK > 1 && !solo) {
     if (wk > 0 && rows_ok) {
 #pragma unroll
       for (int j = 0; j < NA; ++j)
@@ -431,6 +436,31 @@ __device__ __forceinline__ void down_chunk(const FfnMfmaArgs a, const TileInfo& 
   }
 }
 
+// The smallest instantiation covering the live token tiles of chunk c0.
+template <int NTT, int WM, int WK, int RW>
+__device__ __forceinline__ void down_dispatch(const FfnMfmaArgs a, const TileInfo& ti, int c0,
+                                              bool rows_ok, int row_base,
+                                              f32x4_t (*red)[(WK > 1) ? NTT * RW : 1][MOE_WAVE],
+                                              bool solo) {
+  const int nt = min(NTT, (ti.n - c0 + 15) >> 4);  // block-uniform
+  if (nt <= 1) {
+    down_chunk<1, NTT, WM, WK, RW>(a, ti, c0, rows_ok, row_base, red, solo);
+  } else if constexpr (NTT >= 2) {
+    if (nt <= 2) {
+      down_chunk<2, NTT, WM, WK, RW>(a, ti, c0, rows_ok, row_base, red, solo);
+    } else if constexpr (NTT >= 4) {
+      if (nt <= 4) {
+        down_chunk<4, NTT, WM, WK, RW>(a, ti, c0, rows_ok, row_base, red, solo);
+      } else if constexpr (NTT >= 8) {
+        if (nt <= 8)
+          down_chunk<8, NTT, WM, WK, RW>(a, ti, c0, rows_ok, row_base, red, solo);
+        else if constexpr (NTT >= 16)
+          down_chunk<16, NTT, WM, WK, RW>(a, ti, c0, rows_ok, row_base, red, solo);
+      }
+    }
+  }
+}
+
 template <int NTT, int WM, int WK, int RW>
 __global__ void __launch_bounds__(256) FFN_OCCUPANCY ffn_down_mfma_kernel(FfnMfmaArgs a) {
   static_assert(WM * WK == 4, "four waves per block");
@@ -439,27 +469,16 @@ __global__ void __launch_bounds__(256) FFN_OCCUPANCY ffn_down_mfma_kernel(FfnMfm
   const TileInfo ti = tile_of<16 * RW * WM>(a);
   if (ti.kind < 0) return;
   const int wv = threadIdx.x >> 6;
+  if (ti.kind == 2) {
+    // LoRE B_e: one block per missed expert covers all H rows; each wave
+    // takes whole row strips with the full (short) contraction
+    for (int rb = 16 * RW * wv; rb < a.H; rb += 16 * RW * 4)
+      for (int c0 = 0; c0 < ti.n; c0 += 16 * NTT) down_dispatch<NTT, WM, WK, RW>(a, ti, c0, true, rb, red, true);
+    return;
+  }
   const int row_base = ti.row0 + 16 * RW * (wv % WM);
   const bool rows_ok = row_base < a.H;
-  for (int c0 = 0; c0 < ti.n; c0 += 16 * NTT) {
-    const int nt = min(NTT, (ti.n - c0 + 15) >> 4);  // block-uniform
-    if (nt <= 1) {
-      down_chunk<1, NTT, WM, WK, RW>(a, ti, c0, rows_ok, row_base, red);
-    } else if constexpr (NTT >= 2) {
-      if (nt <= 2) {
-        down_chunk<2, NTT, WM, WK, RW>(a, ti, c0, rows_ok, row_base, red);
-      } else if constexpr (NTT >= 4) {
-        if (nt <= 4) {
-          down_chunk<4, NTT, WM, WK, RW>(a, ti, c0, rows_ok, row_base, red);
-        } else if constexpr (NTT >= 8) {
-          if (nt <= 8)
-            down_chunk<8, NTT, WM, WK, RW>(a, ti, c0, rows_ok, row_base, red);
-          else if constexpr (NTT >= 16)
-            down_chunk<16, NTT, WM, WK, RW>(a, ti, c0, rows_ok, row_base, red);
-        }
-      }
-    }
-  }
+  for (int c0 = 0; c0 < ti.n; c0 += 16 * NTT) down_dispatch<NTT, WM, WK, RW>(a, ti, c0, rows_ok, row_base, red, false);
 }
 
 // Down row tiles per wave: 2 up to 4 token tiles (activation fragments reused
@@ -475,7 +494,7 @@ static void launch_kernels(FfnMfmaArgs up, FfnMfmaArgs dn, hipStream_t s, int wh
   const int H = up.H;
   dn.tiles_r = (H + 16 * RW * WM - 1) / (16 * RW * WM);
   dn.tiles_s = dn.tiles_r;
-  dn.tiles_l = dn.slots_l > 0 ? dn.tiles_r : 0;
+  dn.tiles_l = dn.slots_l > 0 ? 1 : 0;   // LoRE B_e: all H rows in one block
   const int n_up = up.slots_r * up.tiles_r + up.n_shared_seg * up.tiles_s + up.slots_l * up.tiles_l;
   const int n_dn = dn.slots_r * dn.tiles_r + dn.n_shared_seg * dn.tiles_s + dn.slots_l * dn.tiles_l;
   if ((which & 1) && n_up > 0) ffn_up_mfma_kernel<NTT, WM, WK><<<n_up, 256, 0, s>>>(up);
