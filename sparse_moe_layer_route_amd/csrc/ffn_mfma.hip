@@ -16,7 +16,7 @@
 //
 // Tile kinds, in the order blockIdx.x enumerates them:
 //   1 shared   up:   act_s = SiLU(W_sg x) * (W_su x)   down: y_s = sum_s W_sd act_s
-//   2 LoRE     up:   z = A_e x  (r rows)               down: y = B_e z (all H rows per block)
+//   2 LoRE     up:   z = A_e x  (r rows)               down: y = B_e z (128-row tiles)
 //   0 routed   up:   act = SiLU(W_g x) * (W_u x)       down: y = W_d act
 // Shared tiles carry every token of the batch and LoRE tiles are short
 // latency-bound chains, so both start before the routed bulk instead of
@@ -104,8 +104,8 @@ __device__ __forceinline__ void nth_segment(const int32_t* __restrict__ offs, in
   __syncthreads();
 }
 
-// ROWS = rows a block covers.
-template <int ROWS>
+// ROWS = rows a block covers (ROWS_L for LoRE tiles).
+template <int ROWS, int ROWS_L = ROWS>
 __device__ __forceinline__ TileInfo tile_of(const FfnMfmaArgs a) {
   __shared__ int s_e, s_seg0, s_n;
   TileInfo ti;
@@ -123,7 +123,7 @@ __device__ __forceinline__ TileInfo tile_of(const FfnMfmaArgs a) {
   const int nl = a.slots_l * a.tiles_l;
   if (b < nl) {
     ti.kind = 2;
-    ti.row0 = (b % a.tiles_l) * ROWS;
+    ti.row0 = (b % a.tiles_l) * ROWS_L;
     nth_segment(a.moffsets, a.E, b / a.tiles_l, &s_e, &s_seg0, &s_n);
   } else {
     b -= nl;
@@ -436,6 +436,14 @@ __device__ __forceinline__ void down_chunk(const FfnMfmaArgs a, const TileInfo& 
   }
 }
 
+// Rows of one LoRE down tile: one row strip per wave.  K = r is one short
+// step, so a LoRE tile is mostly fixed cost; this size gives ~48 blocks for
+// three missed experts and ~512 for thirty-two.
+template <int RW>
+struct LoreDownRows {
+  static constexpr int ROWS = 16 * RW * 4;
+};
+
 // The smallest instantiation covering the live token tiles of chunk c0.
 template <int NTT, int WM, int WK, int RW>
 __device__ __forceinline__ void down_dispatch(const FfnMfmaArgs a, const TileInfo& ti, int c0,
@@ -466,13 +474,14 @@ __global__ void __launch_bounds__(256) FFN_OCCUPANCY ffn_down_mfma_kernel(FfnMfm
   static_assert(WM * WK == 4, "four waves per block");
   // k-split partials, one slot per (k-split > 0, row strip)
   __shared__ f32x4_t red[(WK > 1) ? (WK - 1) * WM : 1][(WK > 1) ? NTT * RW : 1][MOE_WAVE];
-  const TileInfo ti = tile_of<16 * RW * WM>(a);
+  const TileInfo ti = tile_of<16 * RW * WM, LoreDownRows<RW>::ROWS>(a);
   if (ti.kind < 0) return;
   const int wv = threadIdx.x >> 6;
   if (ti.kind == 2) {
-    // LoRE B_e: one block per missed expert covers all H rows; each wave
-    // takes whole row strips with the full (short) contraction
-    for (int rb = 16 * RW * wv; rb < a.H; rb += 16 * RW * 4)
+    // LoRE B_e: a block covers LoreDownRows rows; each wave takes whole row
+    // strips with the full (short) contraction
+    const int r_end = min(a.H, ti.row0 + LoreDownRows<RW>::ROWS);
+    for (int rb = ti.row0 + 16 * RW * wv; rb < r_end; rb += 16 * RW * 4)
       for (int c0 = 0; c0 < ti.n; c0 += 16 * NTT) down_dispatch<NTT, WM, WK, RW>(a, ti, c0, true, rb, red, true);
     return;
   }
@@ -494,7 +503,7 @@ static void launch_kernels(FfnMfmaArgs up, FfnMfmaArgs dn, hipStream_t s, int wh
   const int H = up.H;
   dn.tiles_r = (H + 16 * RW * WM - 1) / (16 * RW * WM);
   dn.tiles_s = dn.tiles_r;
-  dn.tiles_l = dn.slots_l > 0 ? 1 : 0;   // LoRE B_e: all H rows in one block
+  dn.tiles_l = dn.slots_l > 0 ? (H + LoreDownRows<RW>::ROWS - 1) / LoreDownRows<RW>::ROWS : 0;
   const int n_up = up.slots_r * up.tiles_r + up.n_shared_seg * up.tiles_s + up.slots_l * up.tiles_l;
   const int n_dn = dn.slots_r * dn.tiles_r + dn.n_shared_seg * dn.tiles_s + dn.slots_l * dn.tiles_l;
   if ((which & 1) && n_up > 0) ffn_up_mfma_kernel<NTT, WM, WK><<<n_up, 256, 0, s>>>(up);
