@@ -47,6 +47,7 @@ hipError_t launch_lore(const moe_dims_t& d, int T, const void* x, const int32_t*
                        float* lore_out, hipStream_t s);
 int floe_slices(int n_keep);
 int floe_max_inter();
+int floe_max_hidden();
 }  // namespace moe
 
 using namespace moe;
@@ -86,7 +87,7 @@ moe_status_t check_mode(const moe_dims_t* d, moe_mode_t mode) {
     case MOE_MODE_FLOE:
       if (d->up_format != MOE_UP_INT2_G64) return MOE_EUNSUPPORTED;
       if (d->floe_keep < 1 || d->floe_keep > d->inter) return MOE_EINVAL;
-      if (d->inter > floe_max_inter()) return MOE_EUNSUPPORTED;
+      if (d->inter > floe_max_inter() || d->hidden > floe_max_hidden()) return MOE_EUNSUPPORTED;
       return MOE_OK;
   }
   return MOE_EINVAL;

@@ -4,25 +4,29 @@
 //   g_i = x . W_gate[i] and a_i = SiLU(g_i) u_i only for kept channels;
 //   y = sum over kept i of a_i W_down[i, :]  (down stored channel-major).
 //
-// up:     each wave owns FLOE_UP_RPW up rows and issues all their loads
-//         before any arithmetic; lane l owns the 64 inputs of quantisation
-//         group l (16 bytes of codes = one 16-byte load), keeps its 64 x values
-//         and their sum in registers, and forms s * (sum_h q_h x_h - z * sum_h
-//         x_h) -- the group's (q - z) * s dot product -- before one wave
-//         reduction per row.  Codes are unpacked four at a time:
-//         (word >> 2j) & 0x03030303 leaves code j of every byte in that byte,
-//         which converts to float with a single byte-to-float op.
-// select: one 1024-thread workgroup per pair; each thread holds the |u| bit
-//         patterns (monotone for non-negative floats) of up to 16 consecutive
-//         channels in registers; MSB-first 8-bit radix select for the keep-th
-//         largest with one LDS histogram per wave, then two block scans list
-//         the kept channels in ascending order, equal keys resolved toward
-//         lower channels.
+// up:     each wave owns a few consecutive up rows and issues all their
+//         loads before any arithmetic; lane l owns quantisation group l (16
+//         bytes of codes = one 16-byte load) and forms s * (sum_h q_h x_h -
+//         z * sum_h x_h), the group's (q - z) * s dot product, before one
+//         transposed wave reduction for all rows of the wave.  bf16 inputs
+//         decode codes straight into bf16 pairs for pair-dot instructions
+//         (see floe_up_bf16_kernel); fp32 inputs unpack four codes at a time,
+//         (word >> 2j) & 0x03030303 leaving code j of every byte in that
+//         byte, which converts to float with a single byte-to-float op.
+// select: one 1024-thread workgroup per pair; |u| is staged through LDS with
+//         coalesced reads, then each thread holds the bit patterns (monotone
+//         for non-negative floats) of up to 16 consecutive channels in
+//         registers; MSB-first 8-bit radix select for the keep-th largest
+//         with lane-interleaved LDS histograms; one block scan lists the kept
+//         channels in ascending order (a second one ranks equal keys when
+//         only some of them are kept: lower channels first).
 // gate:   each wave owns two kept channel rows (contiguous H-vectors) and
 //         loads both before reducing.
 // down:   each thread owns 8 output columns and sweeps a slice of the kept
 //         channel rows, eight rows in flight; slices are summed in a fixed
 //         order by a small reduction kernel.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -125,6 +129,178 @@ floe_up_kernel(const Tin* __restrict__ x, const uint8_t* __restrict__ up_q,
   }
 }
 
+// bf16 inputs: the group dot product runs on bf16 pair dot instructions.
+// Code word w of a group holds h = 16w + 4b + j at bits 8b + 2j, so the codes
+// of h and h + 8 sit 16 bits apart and one shift moves a pair of them under
+// a mask in both bf16 halves.  OR-ing the masked codes into 1.0 (0x3F80)
+// gives the exact bf16 values 1 + q/4 (codes at mantissa bits 5-6) or
+// 1 + q/16 (bits 3-4); one shift serves both, so a code word costs four
+// shifts, eight and-or and eight pair dots for its 16 codes.  With
+//   accH = sum over odd h of (1 + q_h/4) x_h,  accL = sum over even h of
+//   (1 + q_h/16) x_h,  xsH / xsL the odd / even sums of x,
+// the group term is s * (4 accH + 16 accL - (4 + z) xsH - (16 + z) xsL).
+// The block first stores x as (x_h, x_{h+8}) pairs in LDS (16-byte chunks
+// XOR-swizzled by group) with the odd / even sums of every group.
+// v + (value of the lane given by DPP control CTRL)
+template <int CTRL>
+__device__ __forceinline__ float dpp_take(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sums RPW per-lane values over the wave; lane r (r < RPW) returns the total
+// of value r.  The first log2(RPW) steps halve the values a lane carries:
+// step b keeps the values whose index bit 0 equals lane bit b and adds the
+// partner's copy of them.  Partners are lane ^ 1, lane ^ 2, then rotations by
+// 4 and 8 inside the 16-lane row (each pairs lanes of opposite bit 2 or 3 and
+// equal lower bits), then lanes 16 and 32 apart.
+template <int RPW>
+__device__ __forceinline__ float floe_wave_sum_rows(float (&v)[RPW], int lane) {
+  static_assert(RPW == 4 || RPW == 8, "rows per wave");
+#pragma unroll
+  for (int b = 0, n = RPW; n > 1; ++b, n >>= 1) {
+    const bool up = (lane >> b) & 1;
+#pragma unroll
+    for (int j = 0; j < n / 2; ++j) {
+      const float mine = up ? v[2 * j + 1] : v[2 * j];
+      const float other = up ? v[2 * j] : v[2 * j + 1];
+      float got;
+      if (b == 0) got = dpp_take<0xB1>(other);        // lane ^ 1
+      else if (b == 1) got = dpp_take<0x4E>(other);   // lane ^ 2
+      else got = dpp_take<0x124>(other);              // row rotate by 4
+      v[j] = mine + got;
+    }
+  }
+  float r = v[0];
+  if (RPW == 4) r += dpp_take<0x124>(r);  // row rotate by 4
+  r += dpp_take<0x128>(r);                // row rotate by 8
+  r += __shfl_xor(r, 16, MOE_WAVE);
+  r += __shfl_xor(r, 32, MOE_WAVE);
+  return r;
+}
+
+constexpr int FLOE_UP_BF16_RPW = 4;  // up rows per wave (bf16 path)
+constexpr int FLOE_MAX_HIDDEN = 16384;
+
+template <int RPW>
+__global__ void __launch_bounds__(256)
+floe_up_bf16_kernel(const bf16* __restrict__ x, const uint8_t* __restrict__ up_q,
+                    const uint16_t* __restrict__ up_s, const uint16_t* __restrict__ up_z, int H,
+                    int I, int E, int k, const int32_t* __restrict__ offsets,
+                    const int32_t* __restrict__ perm, float* __restrict__ u_out) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  // dynamic LDS: H / 8 chunks of x pairs (8 per group), then G (odd, even) sums
+  extern __shared__ uint4 xl[];
+  float2* xsl = reinterpret_cast<float2*>(xl + H / 8);
+  int f, t, e;
+  if (!pair_of(blockIdx.y, E, k, offsets, perm, f, t, e)) return;
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  const int G = H >> 6;  // groups per row
+  constexpr uint32_t ONES = 0x3F803F80u;  // bf16 pair (1, 1)
+  constexpr uint32_t ODD = 0x3F800000u;  // bf16 pair (0, 1): upper x of a raw pair (odd h)
+  // bf16 pair (1, 0): lower x (even h).  Kept in a VGPR: as an immediate the
+  // compiler encodes it as the inline constant 1.0, which the pair dot does
+  // not read as bf16 (1, 0).
+  uint32_t even = 0x00003F80u;
+  asm volatile("" : "+v"(even));
+  {
+    // item (g, w): the 16 x of code word w of group g -> eight pairs
+    const uint4* xg = reinterpret_cast<const uint4*>(x + (int64_t)t * H);
+    for (int it = threadIdx.x; it < H / 16; it += 256) {
+      const int g = it >> 2, w = it & 3;
+      const uint4 lo = xg[2 * it], hi = xg[2 * it + 1];  // h = 16w .. 16w+7, 16w+8 .. 16w+15
+      const uint32_t a[4] = {lo.x, lo.y, lo.z, lo.w}, c[4] = {hi.x, hi.y, hi.z, hi.w};
+      uint32_t pw[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pw[2 * i] = (a[i] & 0xFFFFu) | (c[i] << 16);
+        pw[2 * i + 1] = (a[i] >> 16) | (c[i] & 0xFFFF0000u);
+      }
+      float so = 0.f, se = 0.f;  // odd h are the upper halves of the raw pairs
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        so = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a[i]),
+                                             __builtin_bit_cast(bf16x2, ODD), so, false);
+        so = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, c[i]),
+                                             __builtin_bit_cast(bf16x2, ODD), so, false);
+        se = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a[i]),
+                                             __builtin_bit_cast(bf16x2, even), se, false);
+        se = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, c[i]),
+                                             __builtin_bit_cast(bf16x2, even), se, false);
+      }
+      xl[g * 8 + ((2 * w) ^ (g & 7))] = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+      xl[g * 8 + ((2 * w + 1) ^ (g & 7))] = make_uint4(pw[4], pw[5], pw[6], pw[7]);
+      // the four items of a group are adjacent lanes (H / 16 is a multiple of 4)
+      so += __shfl_xor(so, 1, MOE_WAVE);
+      so += __shfl_xor(so, 2, MOE_WAVE);
+      se += __shfl_xor(se, 1, MOE_WAVE);
+      se += __shfl_xor(se, 2, MOE_WAVE);
+      if (w == 0) xsl[g] = make_float2(so, se);
+    }
+  }
+  __syncthreads();
+  // wave-uniform row numbers, so the row addresses stay scalar
+  const int i0 = (blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(wv)) * RPW;
+  if (i0 >= I) return;
+  const int64_t rbase = (int64_t)e * I + i0;
+  uint32_t ones = ONES;  // opaque VGPR: (v & mask) | ones is one v_and_or_b32
+  asm volatile("" : "+v"(ones));
+  float part[RPW];
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) part[q] = 0.f;
+  for (int g0 = 0; g0 < G; g0 += MOE_WAVE) {
+    // lanes past the last group redo it and drop the result
+    const bool act = g0 + lane < G;
+    const int g = act ? g0 + lane : G - 1;
+    uint4 cw[RPW];
+    uint32_t sz[RPW];
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+      const int64_t row = rbase + min(q, I - 1 - i0);
+      const uint8_t* qr = up_q + row * (H >> 2);
+      const uint16_t* sr = up_s + row * G;
+      const uint16_t* zr = up_z + row * G;
+      cw[q] = *reinterpret_cast<const uint4*>(qr + g * 16);
+      sz[q] = (uint32_t)sr[g] | ((uint32_t)zr[g] << 16);
+    }
+    uint32_t xp[32];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint4 v = xl[g * 8 + (c ^ (g & 7))];
+      xp[4 * c] = v.x;
+      xp[4 * c + 1] = v.y;
+      xp[4 * c + 2] = v.z;
+      xp[4 * c + 3] = v.w;
+    }
+    const float2 xsg = xsl[g];
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+      const uint32_t words[4] = {cw[q].x, cw[q].y, cw[q].z, cw[q].w};
+      float accH = 0.f, accL = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          // codes 2m+1 and 2m (and their +8 partners) to bits 5-6 and 3-4
+          const int sh = 4 * m - 3;
+          const uint32_t v = sh >= 0 ? words[w] >> sh : words[w] << -sh;
+          const uint32_t ph = (v & 0x00600060u) | ones, pl = (v & 0x00180018u) | ones;
+          accH = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ph),
+                                                 __builtin_bit_cast(bf16x2, xp[8 * w + 2 * m + 1]),
+                                                 accH, false);
+          accL = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pl),
+                                                 __builtin_bit_cast(bf16x2, xp[8 * w + 2 * m]),
+                                                 accL, false);
+        }
+      }
+      const float sc = half_bits_to_f((uint16_t)(sz[q] & 0xFFFFu));
+      const float zp = half_bits_to_f((uint16_t)(sz[q] >> 16));
+      const float term = sc * (4.f * accH + 16.f * accL - (4.f + zp) * xsg.x - (16.f + zp) * xsg.y);
+      part[q] += act ? term : 0.f;
+    }
+  }
+  const float uval = floe_wave_sum_rows<RPW>(part, lane);
+  if (lane < RPW && i0 + lane < I) u_out[(int64_t)blockIdx.y * I + i0 + lane] = uval;
+}
+
 // Block-wide exclusive scan of one int per thread (1024 threads).
 __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
   const int lane = lane_id(), wv = threadIdx.x >> 6;
@@ -157,23 +333,30 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
                    int32_t* __restrict__ keep_out,
                    uint32_t* __restrict__ flags) {
   constexpr int CH = FLOE_SELECT_CH;
-  __shared__ int whist[FLOE_SELECT_THREADS / MOE_WAVE][256];
+  __shared__ uint32_t stage[FLOE_MAX_INTER];  // coalesced landing area for |u|
+  // 16 histogram copies picked by lane & 15, rows padded to 257 words: lanes
+  // of one wave that hit the same bin land on 16 banks, at most 4 per word
+  __shared__ int lhist[16][257];
   __shared__ int hist[256];
   __shared__ int wsum[FLOE_SELECT_THREADS / MOE_WAVE];
   __shared__ uint32_t s_prefix;
   __shared__ int s_need;
   __shared__ uint32_t s_next;
+  __shared__ int s_eqcnt;
   int f, t, e;
   if (!pair_of(blockIdx.x, E, k, offsets, perm, f, t, e)) return;
   const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
   const int ch = (I + FLOE_SELECT_THREADS - 1) / FLOE_SELECT_THREADS;
   const int i0 = tid * ch;
   const float* ur = u + (int64_t)blockIdx.x * I;
+  // coalesced global reads into LDS, then each thread takes its chunk
+  for (int i = tid; i < I; i += FLOE_SELECT_THREADS) stage[i] = __float_as_uint(fabsf(ur[i]));
+  __syncthreads();
   uint32_t key[CH];
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
     const int i = i0 + j;
-    key[j] = (j < ch && i < I) ? __float_as_uint(fabsf(ur[i])) : 0u;
+    key[j] = (j < ch && i < I) ? stage[i] : 0u;
   }
   if (tid == 0) {
     s_prefix = 0u;
@@ -182,19 +365,19 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
   }
   uint32_t pmask = 0u;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int j = lane; j < 256; j += MOE_WAVE) whist[wv][j] = 0;
+    for (int j = tid; j < 16 * 257; j += FLOE_SELECT_THREADS) (&lhist[0][0])[j] = 0;
     __syncthreads();
     const uint32_t prefix = s_prefix;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       if (j < ch && i0 + j < I && (key[j] & pmask) == prefix)
-        atomicAdd(&whist[wv][(key[j] >> shift) & 0xFFu], 1);
+        atomicAdd(&lhist[lane & 15][(key[j] >> shift) & 0xFFu], 1);
     }
     __syncthreads();
     if (tid < 256) {
       int c = 0;
 #pragma unroll
-      for (int w = 0; w < FLOE_SELECT_THREADS / MOE_WAVE; ++w) c += whist[w][tid];
+      for (int w = 0; w < 16; ++w) c += lhist[w][tid];
       hist[tid] = c;
     }
     __syncthreads();
@@ -221,6 +404,7 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
         }
         s_prefix = prefix | ((uint32_t)(4 * L + b) << shift);
         s_need = need - gt;
+        s_eqcnt = hb[b];  // after the last pass: keys equal to the threshold
       }
     }
     pmask |= 0xFFu << shift;
@@ -228,22 +412,24 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
   }
   const uint32_t thr = s_prefix;
   const int need_eq = s_need;
-  int n_eq = 0;
+  const int eq_total = s_eqcnt;
   uint32_t below_max = 0u;
 #pragma unroll
-  for (int j = 0; j < CH; ++j) {
-    if (j < ch && i0 + j < I) {
-      n_eq += key[j] == thr;
-      if (key[j] < thr && key[j] > below_max) below_max = key[j];
-    }
-  }
-  int eq_total;
-  const int eq_rank = block_excl_scan(n_eq, wsum, eq_total);
+  for (int j = 0; j < CH; ++j)
+    if (j < ch && i0 + j < I && key[j] < thr && key[j] > below_max) below_max = key[j];
   // kept: above the threshold, or among the first need_eq equal keys in
-  // channel order
+  // channel order (all of them when every equal key is kept)
   uint32_t kept = 0u;  // bit j: channel i0 + j kept
-  {
-    int r = eq_rank;
+  if (eq_total == need_eq) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+      if (j < ch && i0 + j < I && key[j] >= thr) kept |= 1u << j;
+  } else {
+    int n_eq = 0;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) n_eq += (j < ch && i0 + j < I && key[j] == thr) ? 1 : 0;
+    int eq_sum;
+    int r = block_excl_scan(n_eq, wsum, eq_sum);
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       if (j < ch && i0 + j < I) {
@@ -420,6 +606,7 @@ floe_reduce_kernel(const float* __restrict__ part, int H, int n_slices, int P_ma
 
 int floe_slices(int n_keep) { return (n_keep + FLOE_DOWN_SLICE - 1) / FLOE_DOWN_SLICE; }
 int floe_max_inter() { return FLOE_MAX_INTER; }
+int floe_max_hidden() { return FLOE_MAX_HIDDEN; }
 
 template <typename Tin>
 static hipError_t launch_floe_t(const moe_dims_t& d, int T, const Tin* x, const moe_weights_t& w,
@@ -430,8 +617,15 @@ static hipError_t launch_floe_t(const moe_dims_t& d, int T, const Tin* x, const 
   const int P = T * k;
   if (P == 0) return hipSuccess;
   hipError_t e = pf.begin(MOE_KERNEL_FLOE_UP, s);
-  floe_up_kernel<Tin><<<dim3((I + 4 * FLOE_UP_RPW - 1) / (4 * FLOE_UP_RPW), P), 256, 0, s>>>(
-      x, w.up_q, w.up_scale, w.up_zero, H, I, E, k, offsets, perm, u);
+  if constexpr (std::is_same<Tin, bf16>::value) {
+    constexpr int R = FLOE_UP_BF16_RPW;
+    const size_t lds = (size_t)H / 8 * 16 + (size_t)(H / 64) * 8;
+    floe_up_bf16_kernel<R><<<dim3((I + 4 * R - 1) / (4 * R), P), 256, lds, s>>>(
+        x, w.up_q, w.up_scale, w.up_zero, H, I, E, k, offsets, perm, u);
+  } else {
+    floe_up_kernel<Tin><<<dim3((I + 4 * FLOE_UP_RPW - 1) / (4 * FLOE_UP_RPW), P), 256, 0, s>>>(
+        x, w.up_q, w.up_scale, w.up_zero, H, I, E, k, offsets, perm, u);
+  }
   if (e == hipSuccess) e = pf.end(MOE_KERNEL_FLOE_UP, s);
   if (e == hipSuccess) e = pf.begin(MOE_KERNEL_FLOE_SELECT, s);
   floe_select_kernel<<<P, FLOE_SELECT_THREADS, 0, s>>>(u, I, nk, d.tie_margin, E, k, offsets, perm,
