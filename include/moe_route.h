@@ -49,6 +49,7 @@ extern "C" {
 #define MOE_MAX_EXPERTS 64
 #define MOE_MAX_TOPK 8
 #define MOE_MAX_LORE_RANK 64
+#define MOE_FLOE_MAX_DIM 16384 /* MOE_MODE_FLOE: inter and hidden at most this */
 
 typedef enum {
   MOE_OK = 0,

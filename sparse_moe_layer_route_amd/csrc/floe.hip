@@ -36,7 +36,7 @@ constexpr int FLOE_GATE_RPW = 2;        // gate rows per wave
 constexpr int FLOE_DOWN_COLS = 1024;    // output columns per down block (8 per thread)
 constexpr int FLOE_SELECT_THREADS = 1024;
 constexpr int FLOE_SELECT_CH = 16;      // channels per select thread (I <= 16384)
-constexpr int FLOE_MAX_INTER = 16384;
+constexpr int FLOE_MAX_INTER = MOE_FLOE_MAX_DIM;
 static_assert(FLOE_MAX_INTER <= FLOE_SELECT_THREADS * FLOE_SELECT_CH, "select covers every channel");
 constexpr int FLOE_DOWN_SLICE = 32;
 
@@ -178,7 +178,7 @@ __device__ __forceinline__ float floe_wave_sum_rows(float (&v)[RPW], int lane) {
 }
 
 constexpr int FLOE_UP_BF16_RPW = 4;  // up rows per wave (bf16 path)
-constexpr int FLOE_MAX_HIDDEN = 16384;
+constexpr int FLOE_MAX_HIDDEN = MOE_FLOE_MAX_DIM;
 
 template <int RPW>
 __global__ void __launch_bounds__(256)
