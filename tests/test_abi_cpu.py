@@ -67,6 +67,12 @@ def test_mode_validation():
     assert ws_size(fl, 1, 3)[0] == B.MOE_EINVAL                        # keep > I
     assert ws_size(dims(up_format="int2_g64", floe_keep=51), 1, 3)[0] == B.MOE_OK
     assert ws_size(dims(up_format="int2_g64", floe_keep=51), 1, 0)[0] == B.MOE_EUNSUPPORTED
+    # FloE keeps a whole |u| row and the packed x of a token in on-chip memory
+    big_i = dims(up_format="int2_g64", floe_keep=51, inter=16384 + 64)
+    big_h = dims(up_format="int2_g64", floe_keep=51, hidden=16384 + 64)
+    assert ws_size(big_i, 1, 3)[0] == B.MOE_EUNSUPPORTED
+    assert ws_size(big_h, 1, 3)[0] == B.MOE_EUNSUPPORTED
+    assert ws_size(dims(up_format="int2_g64", floe_keep=51, hidden=16384), 1, 3)[0] == B.MOE_OK
     assert ws_size(dims(), 16, 7)[0] == B.MOE_EINVAL
     assert ws_size(dims(), -1, 0)[0] == B.MOE_EINVAL
 
