@@ -20,11 +20,15 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_to_f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
 // fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
+// fp32 -> bf16, round to nearest even (NaN stays NaN): one hardware
+// conversion (v_cvt_pk_bf16_f32), two values per instruction when packed.
 __device__ __forceinline__ uint16_t f_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ __forceinline__ uint32_t f2_to_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+  typedef float f32x2_v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{lo, hi}, bf16x2_v));
 }
 
 __device__ __forceinline__ float half_bits_to_f(uint16_t b) {
@@ -89,8 +93,16 @@ __device__ __forceinline__ uint32_t float_order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
-__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// SiLU and sigmoid with the hardware reciprocal (1 ulp) instead of an IEEE
+// division: a division expands to about ten instructions, which dominates the
+// epilogue of the matrix-core kernels.  Large |z| still ends in 0 or z:
+// rcp(inf) = 0 and rcp(1) = 1.
+__device__ __forceinline__ float silu_f(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+__device__ __forceinline__ float sigmoid_f(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // Activation buffers of the matrix-core FFN (bf16 hi + optional lo parts).
 struct FfnBuffers {

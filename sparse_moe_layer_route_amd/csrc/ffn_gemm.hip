@@ -347,17 +347,15 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
       const int wr = row_w0 + wm * (MW / 2) + 16 * i + 4 * kg;
       if (wr >= a.R) continue;
       if (GATED) {
-        uint32_t h[4];
+        float h[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) h[q] = f_to_bf16(silu_f(acc[0][i][j][q]) * acc[NW - 1][i][j][q]);
+        for (int q = 0; q < 4; ++q) h[q] = silu_f(acc[0][i][j][q]) * acc[NW - 1][i][j][q];
         bf16* dst = a.act_out + (int64_t)(mt.seg0 + tr) * a.ld_out + (int64_t)mt.g * a.col_off + wr;
-        *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        *reinterpret_cast<uint2*>(dst) = make_uint2(f2_to_bf16x2(h[0], h[1]), f2_to_bf16x2(h[2], h[3]));
       } else if (a.yb_out) {
-        uint32_t h[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) h[q] = f_to_bf16(acc[0][i][j][q]);
+        const f32x4_t& v = acc[0][i][j];
         bf16* dst = a.yb_out + (int64_t)(mt.seg0 + tr) * a.R + wr;
-        *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        *reinterpret_cast<uint2*>(dst) = make_uint2(f2_to_bf16x2(v[0], v[1]), f2_to_bf16x2(v[2], v[3]));
       } else {
         float* dst = a.y_out + (int64_t)blockIdx.y * a.part_stride + (int64_t)(mt.seg0 + tr) * a.R + wr;
         *reinterpret_cast<float4*>(dst) =

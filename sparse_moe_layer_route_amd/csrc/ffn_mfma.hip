@@ -140,8 +140,7 @@ __device__ __forceinline__ TileInfo tile_of(const FfnMfmaArgs a) {
 
 __device__ __forceinline__ void store_bf16x4(bf16* dst, int64_t off, const float (&v)[4]) {
   *reinterpret_cast<uint2*>(dst + off) =
-      make_uint2((uint32_t)f_to_bf16(v[0]) | ((uint32_t)f_to_bf16(v[1]) << 16),
-                 (uint32_t)f_to_bf16(v[2]) | ((uint32_t)f_to_bf16(v[3]) << 16));
+      make_uint2(f2_to_bf16x2(v[0], v[1]), f2_to_bf16x2(v[2], v[3]));
 }
 
 // k-steps per batch of the pipelined loop: two register sets of U steps each.
