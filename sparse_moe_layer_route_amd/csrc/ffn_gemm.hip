@@ -106,54 +106,78 @@ __device__ __forceinline__ void lds_wait_all(u32x4 (&b)[NB], u32x4 (&a)[NA]) {
   for (int i = 0; i < NA; ++i) asm volatile("" : "+v"(a[i]));
 }
 
-// Block id -> logical tile id with each XCD owning a contiguous range.
-__device__ __forceinline__ int xcd_tile(int b, int n) {
-  const int per = (n + NXCD - 1) / NXCD;
-  const int xcd = b % NXCD, idx = b / NXCD;
-  return xcd * per + idx;   // may exceed n for the last XCD: caller checks
-}
-
-// Logical m-tile index -> (group, first row in segment, rows, segment start).
-struct MTile {
-  int g, row0, n, seg0;
+// Segment table in LDS, entry e for group e (expert, or shared expert):
+// start, rows, and the m-tiles of the groups before it.  Built by wave 0;
+// the caller publishes it with a barrier.  Returns the total m-tiles.
+struct SegTable {
+  int o0[MOE_WAVE], n[MOE_WAVE], excl[MOE_WAVE];
 };
 
-__device__ __forceinline__ bool find_mtile(const GemmArgs a, int m_idx, MTile& mt) {
-  __shared__ int s_g, s_row0, s_n, s_seg0;
-  if (threadIdx.x < MOE_WAVE) {
-    const int lane = threadIdx.x;
-    int n = 0, o0 = 0;
-    if (lane < a.G) {
-      if (a.offsets) {
-        o0 = a.offsets[lane];
-        n = a.offsets[lane + 1] - o0;
-      } else {
-        n = a.T;
-      }
-    }
-    const int tiles = (n + GN - 1) / GN;
-    int incl = tiles;
-#pragma unroll
-    for (int o = 1; o < MOE_WAVE; o <<= 1) {
-      const int v = __shfl_up(incl, o, MOE_WAVE);
-      if (lane >= o) incl += v;
-    }
-    const int excl = incl - tiles;
-    if (lane == 0) s_g = -1;
-    __builtin_amdgcn_wave_barrier();
-    if (lane < a.G && m_idx >= excl && m_idx < incl) {
-      s_g = lane;
-      s_row0 = (m_idx - excl) * GN;
-      s_n = n;
-      s_seg0 = o0;
+__device__ __forceinline__ int seg_table_build(const GemmArgs& a, SegTable& t) {
+  const int lane = lane_id();
+  int o0 = 0, n = 0;
+  if (lane < a.G) {
+    if (a.offsets) {
+      o0 = a.offsets[lane];
+      n = a.offsets[lane + 1] - o0;
+    } else {
+      n = a.T;
     }
   }
-  __syncthreads();
-  mt.g = s_g;
-  mt.row0 = s_row0;
-  mt.n = s_n;
-  mt.seg0 = s_seg0;
-  return mt.g >= 0;
+  const int tiles = (n + GN - 1) / GN;
+  int incl = tiles;
+#pragma unroll
+  for (int o = 1; o < MOE_WAVE; o <<= 1) {
+    const int v = __shfl_up(incl, o, MOE_WAVE);
+    if (lane >= o) incl += v;
+  }
+  if (threadIdx.x < MOE_WAVE) {
+    t.o0[lane] = o0;
+    t.n[lane] = n;
+    t.excl[lane] = incl - tiles;
+  }
+  return __builtin_amdgcn_readlane(incl, MOE_WAVE - 1);
+}
+
+// One (m-tile, weight-tile) pair: group, first row in the segment, segment
+// rows and start, weight-row tile.
+struct TileMeta {
+  int g, row0, n, seg0, n_idx;
+};
+constexpr int GEMM_MAX_TILES = 16;  // tiles per persistent block (the grid grows beyond)
+struct TileTable {
+  int g[GEMM_MAX_TILES], row0[GEMM_MAX_TILES], n[GEMM_MAX_TILES], seg0[GEMM_MAX_TILES],
+      n_idx[GEMM_MAX_TILES];
+};
+
+// Lane j of the calling wave fills entry j (tile t0 + j * stride) from the
+// published segment table.
+__device__ __forceinline__ void tile_table_build(const GemmArgs& a, const SegTable& sg, int t0,
+                                                 int stride, int count, TileTable& tt) {
+  const int j = lane_id();
+  if (j >= count) return;
+  const int t = t0 + j * stride;
+  const int m_idx = t / a.tiles_n;
+  int g = 0;
+  for (int e = 0; e < a.G; ++e) {
+    const int tiles = (sg.n[e] + GN - 1) / GN;
+    if (m_idx >= sg.excl[e] && m_idx < sg.excl[e] + tiles) g = e;
+  }
+  tt.g[j] = g;
+  tt.row0[j] = (m_idx - sg.excl[g]) * GN;
+  tt.n[j] = sg.n[g];
+  tt.seg0[j] = sg.o0[g];
+  tt.n_idx[j] = t % a.tiles_n;
+}
+
+__device__ __forceinline__ TileMeta tile_get(const TileTable& tt, int j) {
+  TileMeta m;
+  m.g = __builtin_amdgcn_readfirstlane(tt.g[j]);
+  m.row0 = __builtin_amdgcn_readfirstlane(tt.row0[j]);
+  m.n = __builtin_amdgcn_readfirstlane(tt.n[j]);
+  m.seg0 = __builtin_amdgcn_readfirstlane(tt.seg0[j]);
+  m.n_idx = __builtin_amdgcn_readfirstlane(tt.n_idx[j]);
+  return m;
 }
 
 // Wait until at most N of this wave's vector-memory operations are pending
@@ -182,27 +206,61 @@ __device__ __forceinline__ void read_fa(u32x4 (&fa)[NW * WT], uint32_t sa) {
 }
 
 // GATED: GEMM1 (gate and up matrices, 128 rows each, SiLU product, bf16 out);
-// else GEMM2 (256 down rows, fp32 out).  Either way a block stages 256 weight
-// rows and 256 token rows per 32-wide k stage, and each wave owns a 128 x 64
-// output tile (8 x 4 MFMA tiles, 128 fp32 accumulators per lane).
+// else GEMM2 (256 down rows, fp32 or bf16 out).  Either way a block stages
+// 256 weight rows and 256 token rows per 32-wide k stage, and each wave owns a
+// 128 x 64 output tile (8 x 4 MFMA tiles, 128 fp32 accumulators per lane).
+//
+// Blocks are persistent: block b works through its share of the tiles (those
+// of its XCD, strided by the XCD's blocks), and its k stages form one stream
+// through the LDS ring across tile boundaries, so the first stages of the
+// next tile load while the current tile finishes and writes its outputs.
 template <bool GATED>
 __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   constexpr int NW = GATED ? 2 : 1;          // weight matrices
   constexpr int MW = GATED ? 128 : 256;      // weight rows per matrix per block
   constexpr int WT = MW / 2 / 16;            // weight tiles per wave per matrix (4 or 8)
   __shared__ __attribute__((aligned(16))) bf16 lds[GSTAGES][GROWS * GK];
-  const int tile = xcd_tile(blockIdx.x, a.n_blocks);
-  if (tile >= a.n_blocks) return;
-  const int m_idx = tile / a.tiles_n, n_idx = tile % a.tiles_n;
-  MTile mt;
-  if (!find_mtile(a, m_idx, mt)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ SegTable seg;
+  const int n_tiles = seg_table_build(a, seg) * a.tiles_n;   // every wave: same total
+  __syncthreads();
+  // this block's tiles: XCD x owns a contiguous range, dealt to its blocks
+  const int nbx = gridDim.x / NXCD, xcd = blockIdx.x % NXCD, bi = blockIdx.x / NXCD;
+  const int per_x = (n_tiles + NXCD - 1) / NXCD;
+  const int t_lo = xcd * per_x + bi, t_hi = min(n_tiles, (xcd + 1) * per_x);
+  const int n_my = t_lo < t_hi ? (t_hi - t_lo + nbx - 1) / nbx : 0;
+  if (n_my == 0) return;
+  __shared__ TileTable tt;
+  if (threadIdx.x < MOE_WAVE) tile_table_build(a, seg, t_lo, nbx, n_my, tt);
+  __syncthreads();
+  // element offset of every token row of every tile of this block, gathered
+  // up front so the stream never waits on the permutation mid-flight
+  __shared__ int tok_base[GEMM_MAX_TILES][GN];
+  {
+    const int ld = GATED ? a.K : (int)a.ld_in;
+    for (int j = 0; j < n_my; ++j) {
+      const TileMeta m = tile_get(tt, j);
+      for (int r = threadIdx.x; r < GN; r += GTHREADS) {
+        const int rr = min(m.row0 + r, m.n - 1);
+        const int tok = GATED ? (a.offsets ? a.perm[m.seg0 + rr] / a.k : rr) : m.seg0 + rr;
+        tok_base[j][r] = tok * ld;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar
   const int wm = wv & 1, wn = wv >> 1;       // 2 x 4 waves: weight half, token quarter
   const int r16 = lane & 15, kg = lane >> 4;
-  const int row_w0 = n_idx * MW;             // first weight row of the tile
-  // a wave whose 64 tokens all lie past the segment end (the last m-tile of a
-  // segment) still moves its share of the stages but skips the MFMAs
-  const bool tok_live = mt.row0 + wn * 16 * GTT < mt.n;
+
+  const int nsub = GATED ? 1 : a.n_sub;
+  const int kst = a.K / GK;          // K % 32 == 0 on this path
+  const int nst_all = nsub * kst;
+  const int kper = (nst_all + a.ksplit - 1) / a.ksplit;
+  const int k_lo = a.ksplit > 1 ? blockIdx.y * kper : 0;
+  const int k_hi = a.ksplit > 1 ? min(nst_all, k_lo + kper) : nst_all;
+  const int nst = max(0, k_hi - k_lo);       // stages per tile
+  const int S = n_my * nst;                  // stages of this block's stream
 
   // DMA plan: a stage is 512 LDS rows x 64 B; one wave instruction writes 16
   // rows (1 KiB, lane l -> row l/4, 16-byte slot l%4).  Wave w issues
@@ -211,31 +269,65 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   // p ^ ((r/2) % 4), so each 8-row group of a fragment read hits 32 distinct
   // banks.
   const int chunk = (lane & 3) ^ ((lane >> 3) & 3);
-  const bf16* base_w0 = a.w0 + (int64_t)mt.g * a.w_stride;
-  const bf16* base_w1 = GATED ? a.w1 + (int64_t)mt.g * a.w_stride : base_w0;
-  const bf16* base_x = GATED ? a.x : a.act_in;
   const bool is_w = wv < GWAVES / 2;
-  // GATED: LDS rows 0-127 (waves 0-1) gate, 128-255 (waves 2-3) up
-  const bf16* dma_base = is_w ? ((GATED && wv >= GWAVES / 4) ? base_w1 : base_w0) : base_x;
   constexpr int NQ = GROWS / 16 / GWAVES;   // DMA instructions per wave per stage
   constexpr int NMF = NW * WT * GTT;        // MFMAs per wave per stage
+  // row of this lane's DMA instruction q within the token or weight half
+  auto dma_row = [&](int q) __attribute__((always_inline)) { return 16 * (NQ * wv + q) + (lane >> 2); };
+
+  // DMA state: the tile the stream is loading, its base and per-lane offsets
+  int dj = 0, dk = 0;   // stream position of the next DMA stage: tile, stage in tile
+  TileMeta dm = tile_get(tt, 0);
+  const bf16* dbase;
   int off[NQ];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int row = 16 * (NQ * wv + q) + (lane >> 2);   // LDS row 0..511
+  auto set_dma = [&](const TileMeta& m, int j) __attribute__((always_inline)) {
     if (is_w) {
-      const int r = GATED ? (row & 127) : row;
-      off[q] = min(row_w0 + r, a.R - 1) * a.K + 8 * chunk;
+      const bf16* w = (GATED && wv >= GWAVES / 4) ? a.w1 : a.w0;
+      dbase = w + (int64_t)m.g * a.w_stride;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int r = GATED ? (dma_row(q) & 127) : dma_row(q);
+        off[q] = min(m.n_idx * MW + r, a.R - 1) * a.K + 8 * chunk;
+      }
     } else {
-      const int r = min(mt.row0 + (row - 256), mt.n - 1);
-      if (GATED) {
-        const int tok = a.offsets ? a.perm[mt.seg0 + r] / a.k : r;
-        off[q] = tok * a.K + 8 * chunk;
+      dbase = GATED ? a.x : a.act_in;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) off[q] = tok_base[j][dma_row(q) - 256] + 8 * chunk;
+    }
+  };
+  set_dma(dm, 0);
+  // The DMA stream visits (tile, k stage) in order; dma_next() returns the k
+  // stage of the next stream stage.  Stages past the end reload the last one
+  // into a slot nobody reads again, so every step issues exactly NQ loads per
+  // thread and "stage s+1 has landed" is "at most 2 NQ pending".
+  auto dma_next = [&]() __attribute__((always_inline)) {
+    if (dk == nst) {            // the previous stage ended a tile
+      if (dj + 1 < n_my) {
+        dk = 0;
+        ++dj;
+        dm = tile_get(tt, dj);
+        set_dma(dm, dj);
       } else {
-        off[q] = (mt.seg0 + r) * (int)a.ld_in + 8 * chunk;
+        dk = nst - 1;           // past the end: the last stage again
       }
     }
-  }
+    return k_lo + dk++;
+  };
+  auto issue_one = [&](int s, int kstage, int q) __attribute__((always_inline)) {
+    bf16* dst = &lds[s % GSTAGES][(16 * NQ * wv) * GK];
+    const int s_ = kstage / kst, ko = (kstage % kst) * GK;
+    const bf16* src = dbase + (is_w ? (int64_t)s_ * a.sub_stride : (int64_t)s_ * a.sub_k_off) + ko;
+    __builtin_amdgcn_global_load_lds((const void*)(src + off[q]),
+                                     (__attribute__((address_space(3))) void*)(dst + q * 16 * GK),
+                                     16, 0, 0);
+  };
+
+  // compute state: the tile whose stages the MFMAs consume
+  int cj = 0, ck = 0;   // compute position: tile, stage in tile
+  TileMeta cm = dm;
+  // a wave whose 64 tokens all lie past the segment end (the last m-tile of a
+  // segment) still moves its share of the stages but skips the MFMAs
+  bool tok_live = cm.row0 + wn * 16 * GTT < cm.n;
 
   f32x4_t acc[NW][WT][GTT];
 #pragma unroll
@@ -245,54 +337,75 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < GTT; ++j) acc[m][i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nsub = GATED ? 1 : a.n_sub;
-  const int kst = a.K / GK;          // K % 32 == 0 on this path
-  const int nst = nsub * kst;
-  const int per = (nst + a.ksplit - 1) / a.ksplit;
-  const int k_lo = a.ksplit > 1 ? blockIdx.y * per : 0;
-  const int k_hi = a.ksplit > 1 ? min(nst, k_lo + per) : nst;
-
-  // Every step issues exactly NQ DMA loads per thread (stages past the range
-  // reload the last stage into a slot nobody reads again), so "stage s+1 has
-  // landed" is always "at most 2 * NQ of this thread's loads pending".
-  // DMA instruction q of stage st (each stage is NQ instructions per thread).
-  auto issue_one = [&](int st, int q) __attribute__((always_inline)) {
-    bf16* dst = &lds[st % GSTAGES][(16 * NQ * wv) * GK];
-    st = min(st, k_hi - 1);
-    const int s_ = st / kst, ko = (st % kst) * GK;
-    const bf16* src = dma_base + (is_w ? (int64_t)s_ * a.sub_stride : (int64_t)s_ * a.sub_k_off) + ko;
-    __builtin_amdgcn_global_load_lds((const void*)(src + off[q]),
-                                     (__attribute__((address_space(3))) void*)(dst + q * 16 * GK),
-                                     16, 0, 0);
-  };
-  auto issue = [&](int st) __attribute__((always_inline)) {
+  // epilogue of the compute tile: lane holds weight rows 4*kg..+3 of tile i,
+  // token r16 of tile j; then the accumulators restart for the next tile
+  auto epilogue = [&]() __attribute__((always_inline)) {
+    const int row_w0 = cm.n_idx * MW;
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) issue_one(st, q);
+    for (int j = 0; j < GTT; ++j) {
+      const int tr = cm.row0 + wn * 16 * GTT + 16 * j + r16;   // token row within segment
+      if (tr >= cm.n) continue;
+#pragma unroll
+      for (int i = 0; i < WT; ++i) {
+        const int wr = row_w0 + wm * (MW / 2) + 16 * i + 4 * kg;
+        if (wr >= a.R) continue;
+        if (GATED) {
+          float h[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) h[q] = silu_f(acc[0][i][j][q]) * acc[NW - 1][i][j][q];
+          bf16* dst = a.act_out + (int64_t)(cm.seg0 + tr) * a.ld_out + (int64_t)cm.g * a.col_off + wr;
+          *reinterpret_cast<uint2*>(dst) = make_uint2(f2_to_bf16x2(h[0], h[1]), f2_to_bf16x2(h[2], h[3]));
+        } else if (a.yb_out) {
+          const f32x4_t& v = acc[0][i][j];
+          bf16* dst = a.yb_out + (int64_t)(cm.seg0 + tr) * a.R + wr;
+          *reinterpret_cast<uint2*>(dst) = make_uint2(f2_to_bf16x2(v[0], v[1]), f2_to_bf16x2(v[2], v[3]));
+        } else {
+          float* dst = a.y_out + (int64_t)blockIdx.y * a.part_stride + (int64_t)(cm.seg0 + tr) * a.R + wr;
+          *reinterpret_cast<float4*>(dst) =
+              float4{acc[0][i][j][0], acc[0][i][j][1], acc[0][i][j][2], acc[0][i][j][3]};
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NW; ++m)
+#pragma unroll
+      for (int i = 0; i < WT; ++i)
+#pragma unroll
+        for (int j = 0; j < GTT; ++j) acc[m][i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   };
+  auto next_compute_tile = [&]() __attribute__((always_inline)) {
+    ++cj;
+    if (cj < n_my) {
+      cm = tile_get(tt, cj);
+      tok_live = cm.row0 + wn * 16 * GTT < cm.n;
+    }
+  };
+
+  if (nst == 0) {  // an empty k range (k split): the partial sums are zero
+    for (int j = 0; j < n_my; ++j) {
+      epilogue();
+      next_compute_tile();
+    }
+    return;
+  }
 
   // byte address of this lane's fragment slot: logical chunk kg of row r
   // lives at physical chunk kg ^ ((r/2) % 4); rows here are 16-aligned + r16
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)&lds[0][0];
-  const uint32_t lane_off = (uint32_t)(r16 * GK * 2 + ((kg ^ ((r16 >> 1) & 3)) * 16));
+  uint32_t lane_off = (uint32_t)(r16 * GK * 2 + ((kg ^ ((r16 >> 1) & 3)) * 16));
 
-  // Stage st's fragments sit in one register set while the next stage's are
-  // read into the other: after the barrier that publishes stage st+1 a wave
-  // starts its LDS reads, runs stage st's MFMAs from registers, then waits for
+  // Stage s's fragments sit in one register set while the next stage's are
+  // read into the other: after the barrier that publishes stage s+1 a wave
+  // starts its LDS reads, runs stage s's MFMAs from registers, then waits for
   // the reads.  The last stage reads a slot holding a duplicate stage, which
   // is never multiplied.
 #define GEMM_READ(FB, FA, st_)                                                          \
   {                                                                                     \
+    asm volatile("" : "+v"(lane_off)); /* addresses formed here, not kept live */       \
     const uint32_t sl = lds0 + (uint32_t)(((st_) % GSTAGES) * GROWS * GK * 2) + lane_off; \
     read_fb<0, GTT>(FB, sl + (uint32_t)((256 + wn * 16 * GTT) * GK * 2));              \
     read_fa<NW, WT, MW, 0>(FA, sl + (uint32_t)(wm * (MW / 2) * GK * 2));               \
   }
-#define GEMM_MFMA(FB, FA)                                                               \
-  _Pragma("unroll") for (int m = 0; m < NW; ++m)                                        \
-    _Pragma("unroll") for (int i = 0; i < WT; ++i)                                      \
-      _Pragma("unroll") for (int j = 0; j < GTT; ++j)                                   \
-        acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                         \
-            __builtin_bit_cast(bf16x8_t, FA[m * WT + i]), __builtin_bit_cast(bf16x8_t, FB[j]), \
-            acc[m][i][j], 0, 0, 0);
 #define GEMM_MFMA_PART(FB, FA, q)                                                       \
   _Pragma("unroll") for (int t = 0; t < NMF / NQ; ++t) {                                \
     const int L = (q) * (NMF / NQ) + t;                                                 \
@@ -302,67 +415,52 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
         acc[m][i][j], 0, 0, 0);                                                         \
   }
   // The refill of the slot freed two barriers ago is spread over the MFMAs so
-  // the waves do not queue their DMA instructions all at once.
+  // the waves do not queue their DMA instructions all at once.  A tile's
+  // last stage is followed by its epilogue, and the next stage's fragments
+  // are read only after it (they are not live while the outputs are formed).
 #define GEMM_STEP(FBc, FAc, FBn, FAn, st_)                                              \
   {                                                                                     \
+    const bool last = ++ck == nst;                                                      \
     GEMM_VMCNT_STAGES1();                                                               \
     __builtin_amdgcn_s_barrier();                                                       \
-    GEMM_READ(FBn, FAn, (st_) + 1);                                                     \
+    if (!last) GEMM_READ(FBn, FAn, (st_) + 1);                                          \
+    const int kref = dma_next();                                                        \
     __builtin_amdgcn_sched_barrier(0); /* reads issue before the MFMAs */              \
     _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                    \
-      issue_one((st_) + GSTAGES - 1, q);                                                \
+      issue_one((st_) + GSTAGES - 1, kref, q);                                          \
       __builtin_amdgcn_sched_barrier(0);                                                \
       if (tok_live) { GEMM_MFMA_PART(FBc, FAc, q); }                                    \
       __builtin_amdgcn_sched_barrier(0);                                                \
     }                                                                                   \
+    if (last) {                                                                         \
+      ck = 0;                                                                           \
+      epilogue();                                                                       \
+      next_compute_tile();                                                              \
+      GEMM_READ(FBn, FAn, (st_) + 1);                                                   \
+    }                                                                                   \
     lds_wait_all(FBn, FAn);                                                             \
   }
-  if (k_lo < k_hi) {
+  {
     u32x4 fb0[GTT], fa0[NW * WT], fb1[GTT], fa1[NW * WT];
-    issue(k_lo);
-    issue(k_lo + 1);
-    issue(k_lo + 2);
+#pragma unroll
+    for (int s0 = 0; s0 < GSTAGES - 1; ++s0) {
+      const int kref = dma_next();
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) issue_one(s0, kref, q);
+    }
     GEMM_VMCNT_STAGES2();
     __builtin_amdgcn_s_barrier();
-    GEMM_READ(fb0, fa0, k_lo);
+    GEMM_READ(fb0, fa0, 0);
     lds_wait_all(fb0, fa0);
-    for (int st = k_lo; st < k_hi; st += 2) {
+    for (int st = 0; st < S; st += 2) {
       GEMM_STEP(fb0, fa0, fb1, fa1, st);
-      if (st + 1 < k_hi) GEMM_STEP(fb1, fa1, fb0, fa0, st + 1);
+      if (st + 1 < S) GEMM_STEP(fb1, fa1, fb0, fa0, st + 1);
     }
   }
 #undef GEMM_READ
-#undef GEMM_MFMA
 #undef GEMM_STEP
 #undef GEMM_MFMA_PART
   GEMM_VMCNT(0);      // no DMA may outlive the workgroup's LDS
-
-  // epilogue: lane holds weight rows 4*kg..+3 of tile i, token r16 of tile j
-#pragma unroll
-  for (int j = 0; j < GTT; ++j) {
-    const int tr = mt.row0 + wn * 16 * GTT + 16 * j + r16;   // token row within segment
-    if (tr >= mt.n) continue;
-#pragma unroll
-    for (int i = 0; i < WT; ++i) {
-      const int wr = row_w0 + wm * (MW / 2) + 16 * i + 4 * kg;
-      if (wr >= a.R) continue;
-      if (GATED) {
-        float h[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) h[q] = silu_f(acc[0][i][j][q]) * acc[NW - 1][i][j][q];
-        bf16* dst = a.act_out + (int64_t)(mt.seg0 + tr) * a.ld_out + (int64_t)mt.g * a.col_off + wr;
-        *reinterpret_cast<uint2*>(dst) = make_uint2(f2_to_bf16x2(h[0], h[1]), f2_to_bf16x2(h[2], h[3]));
-      } else if (a.yb_out) {
-        const f32x4_t& v = acc[0][i][j];
-        bf16* dst = a.yb_out + (int64_t)(mt.seg0 + tr) * a.R + wr;
-        *reinterpret_cast<uint2*>(dst) = make_uint2(f2_to_bf16x2(v[0], v[1]), f2_to_bf16x2(v[2], v[3]));
-      } else {
-        float* dst = a.y_out + (int64_t)blockIdx.y * a.part_stride + (int64_t)(mt.seg0 + tr) * a.R + wr;
-        *reinterpret_cast<float4*>(dst) =
-            float4{acc[0][i][j][0], acc[0][i][j][1], acc[0][i][j][2], acc[0][i][j][3]};
-      }
-    }
-  }
 }
 #undef GEMM_VMCNT
 #undef GEMM_VMCNT_STAGES2
@@ -390,6 +488,18 @@ int gemm_shared_down_ksplit(const moe_dims_t& d, int T) {
   int ks = 256 / (tiles > 0 ? tiles : 1);
   ks = ks < 1 ? 1 : (ks > nst ? nst : ks);
   return ks;
+}
+
+// Persistent grid: one block per CU (a block's LDS ring fills a CU), shared
+// by the k splits, a multiple of the XCD count; fewer when there are fewer
+// tiles (an upper bound here: the routing decides the exact count).
+constexpr int GEMM_CUS = 256;
+static int gemm_grid(int tiles_upper, int ksplit) {
+  int g = std::min(tiles_upper, std::max(NXCD, GEMM_CUS / std::max(1, ksplit)));
+  // each XCD's range is dealt to its blocks: at most GEMM_MAX_TILES apiece
+  const int per_x = (tiles_upper + NXCD - 1) / NXCD;
+  g = std::max(g, NXCD * ((per_x + GEMM_MAX_TILES - 1) / GEMM_MAX_TILES));
+  return ((g + NXCD - 1) / NXCD) * NXCD;
 }
 
 // Routed experts (offsets != nullptr) or shared experts (offsets == nullptr).
@@ -424,7 +534,7 @@ hipError_t launch_ffn_gemm(const moe_dims_t& d, int T, const void* x, const moe_
     a.tiles_n = (R1 + 127) / 128;            // 128 gate + 128 up rows per block
     a.n_blocks = mt_max * a.tiles_n;
     a.ksplit = 1;
-    const int grid = ((a.n_blocks + NXCD - 1) / NXCD) * NXCD;
+    const int grid = gemm_grid(a.n_blocks, 1);
     if (a.n_blocks > 0) ffn_gemm_kernel<true><<<grid, GTHREADS, 0, s>>>(a);
   }
   if (which & 2) {
@@ -451,7 +561,7 @@ hipError_t launch_ffn_gemm(const moe_dims_t& d, int T, const void* x, const moe_
     a.y_out = a.ksplit > 1 ? part : y;
     a.yb_out = a.ksplit > 1 ? nullptr : yb;
     a.part_stride = (int64_t)T * H;
-    const int grid = ((a.n_blocks + NXCD - 1) / NXCD) * NXCD;
+    const int grid = gemm_grid(a.n_blocks, a.ksplit);
     if (a.n_blocks > 0) ffn_gemm_kernel<false><<<dim3(grid, a.ksplit), GTHREADS, 0, s>>>(a);
     if (a.ksplit > 1) {
       const int64_t n4 = (int64_t)T * H / 4;
