@@ -136,61 +136,71 @@ __device__ __forceinline__ float4 load4<bf16>(const bf16* p) {
   return float4{bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
 }
 
+template <typename Tin>
+__device__ __forceinline__ void store4(Tin* p, float a0, float a1, float a2, float a3);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float a0, float a1, float a2, float a3) {
+  *reinterpret_cast<float4*>(p) = float4{a0, a1, a2, a3};
+}
+template <>
+__device__ __forceinline__ void store4<bf16>(bf16* p, float a0, float a1, float a2, float a3) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(f2_to_bf16x2(a0, a1), f2_to_bf16x2(a2, a3));
+}
+
+// grid (T tokens, H / (4 * COMBINE_THREADS) column blocks): a thread owns four
+// consecutive columns of one token and issues the loads of all k slots
+// before summing them; the token's slot table is read with scalar loads.
 template <typename Tin, typename Ty>
 __global__ void __launch_bounds__(COMBINE_THREADS)
 combine_rows_kernel(int H, int k, const Ty* __restrict__ y_perm, const int32_t* __restrict__ row_of,
                     const float* __restrict__ topk_w, const uint8_t* __restrict__ exact,
                     const float* __restrict__ y_s, const float* __restrict__ g_s,
                     Tin* __restrict__ out) {
-  __shared__ int s_row[MOE_MAX_TOPK], s_ex[MOE_MAX_TOPK];
-  __shared__ float s_w[MOE_MAX_TOPK];
-  const int t = blockIdx.x, tid = threadIdx.x;
-  if (tid < k) {
-    const int64_t o = (int64_t)t * k + tid;
-    s_row[tid] = row_of[o];
-    s_ex[tid] = exact[o];
-    s_w[tid] = topk_w[o];
-  }
-  __syncthreads();
+  const int t = blockIdx.x;
+  const int h = (blockIdx.y * COMBINE_THREADS + threadIdx.x) * 4;
+  if (h >= H) return;
   const float gs = g_s ? g_s[t] : 1.f;
-  for (int h = tid * 4; h < H; h += COMBINE_THREADS * 4) {
-    float4 ys = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (y_s) ys = *reinterpret_cast<const float4*>(y_s + (int64_t)t * H + h);
-    float a0 = gs * ys.x, a1 = gs * ys.y, a2 = gs * ys.z, a3 = gs * ys.w;
-    for (int j = 0; j < k; ++j) {
-      const int row = s_row[j];
-      if (row < 0) continue;
-      float4 v = load4<Ty>(y_perm + (int64_t)row * H + h);
-      if (!s_ex[j]) {
-        v.x += ys.x; v.y += ys.y; v.z += ys.z; v.w += ys.w;
-      }
-      const float wj = s_w[j];
-      a0 = fmaf(wj, v.x, a0);
-      a1 = fmaf(wj, v.y, a1);
-      a2 = fmaf(wj, v.z, a2);
-      a3 = fmaf(wj, v.w, a3);
-    }
-    const int64_t o = (int64_t)t * H + h;
-    elem<Tin>::store(out, o, a0);
-    elem<Tin>::store(out, o + 1, a1);
-    elem<Tin>::store(out, o + 2, a2);
-    elem<Tin>::store(out, o + 3, a3);
+  float4 ys = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (y_s) ys = *reinterpret_cast<const float4*>(y_s + (int64_t)t * H + h);
+  int row[MOE_MAX_TOPK];
+  float4 v[MOE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    row[j] = j < k ? row_of[(int64_t)t * k + j] : -1;
+    v[j] = row[j] >= 0 ? load4<Ty>(y_perm + (int64_t)row[j] * H + h) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  float a0 = gs * ys.x, a1 = gs * ys.y, a2 = gs * ys.z, a3 = gs * ys.w;
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    if (row[j] < 0) continue;
+    const int64_t o = (int64_t)t * k + j;
+    float4 vj = v[j];
+    if (!exact[o]) {
+      vj.x += ys.x; vj.y += ys.y; vj.z += ys.z; vj.w += ys.w;
+    }
+    const float wj = topk_w[o];
+    a0 = fmaf(wj, vj.x, a0);
+    a1 = fmaf(wj, vj.y, a1);
+    a2 = fmaf(wj, vj.z, a2);
+    a3 = fmaf(wj, vj.w, a3);
+  }
+  store4<Tin>(out + (int64_t)t * H + h, a0, a1, a2, a3);
 }
 
 // y_bf16: y_perm holds bf16 rows.
 hipError_t launch_combine_rows(const moe_dims_t& d, int T, const void* y_perm, bool y_bf16,
                                const int32_t* row_of, const float* topk_w, const uint8_t* exact,
                                const float* y_s, const float* g_s, void* out, hipStream_t s) {
+  const dim3 grid(T, (d.hidden + 4 * COMBINE_THREADS - 1) / (4 * COMBINE_THREADS));
   if (d.dtype == MOE_BF16) {
     if (y_bf16)
-      combine_rows_kernel<bf16, bf16><<<T, COMBINE_THREADS, 0, s>>>(
+      combine_rows_kernel<bf16, bf16><<<grid, COMBINE_THREADS, 0, s>>>(
           d.hidden, d.top_k, (const bf16*)y_perm, row_of, topk_w, exact, y_s, g_s, (bf16*)out);
     else
-      combine_rows_kernel<bf16, float><<<T, COMBINE_THREADS, 0, s>>>(
+      combine_rows_kernel<bf16, float><<<grid, COMBINE_THREADS, 0, s>>>(
           d.hidden, d.top_k, (const float*)y_perm, row_of, topk_w, exact, y_s, g_s, (bf16*)out);
   } else {
-    combine_rows_kernel<float, float><<<T, COMBINE_THREADS, 0, s>>>(
+    combine_rows_kernel<float, float><<<grid, COMBINE_THREADS, 0, s>>>(
         d.hidden, d.top_k, (const float*)y_perm, row_of, topk_w, exact, y_s, g_s, (float*)out);
   }
   return hipGetLastError();

@@ -133,7 +133,10 @@ __device__ __forceinline__ void tile_logits(const float* __restrict__ x, const f
   __syncthreads();
 }
 
-constexpr int LOGIT_WAVES = 8;
+#ifndef ROUTE_LOGIT_WAVES
+#define ROUTE_LOGIT_WAVES 8
+#endif
+constexpr int LOGIT_WAVES = ROUTE_LOGIT_WAVES;
 
 // Logits of tokens 16*blockIdx.x.. and experts 16*blockIdx.y.. into
 // logits [T][E].
@@ -147,7 +150,10 @@ route_logits_kernel(const bf16* __restrict__ x, const bf16* __restrict__ w, int 
   const bf16* xr = x + (int64_t)min(t0 + r16, T - 1) * H + 8 * kg;
   const bf16* wr = w + (int64_t)min(e0 + r16, E - 1) * H + 8 * kg;
   const bool live = e0 + r16 < E;
-  constexpr int U = 4;
+#ifndef ROUTE_LOGIT_U
+#define ROUTE_LOGIT_U 4
+#endif
+  constexpr int U = ROUTE_LOGIT_U;
   const int ksteps = H >> 5;
   const int per = (ksteps + LOGIT_WAVES - 1) / LOGIT_WAVES;
   const int kb = wv * per, ke = min(ksteps, kb + per);
@@ -216,19 +222,17 @@ __device__ __forceinline__ float wave_dot(const Tin* __restrict__ a, const Tin* 
   return wave_sum(acc);
 }
 
-// One wave per token (4 per block) on logits [T][E] from route_logits_kernel.
+// Everything after the logits for token t, one wave, lane = expert: shared
+// gate, softmax, routed top-k, near-tie flag, mass, residency split or
+// stall-free substitution, weights.  l is this lane's logit (-inf past E).
 template <typename Tin>
-__global__ void __launch_bounds__(256)
-route_topk_kernel(const Tin* __restrict__ x, const float* __restrict__ logits, int T, int H, int E,
-                  int k, int renorm, float margin, int mode, const uint64_t* __restrict__ resident,
-                  int64_t res_stride, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
-                  uint8_t* __restrict__ exact, uint32_t* __restrict__ flags,
-                  float* __restrict__ mass_out, const Tin* __restrict__ w_sg,
-                  float* __restrict__ g_s) {
+__device__ __forceinline__ void route_topk_token(
+    int t, float l, const Tin* __restrict__ x, int H, int E, int k, int renorm, float margin,
+    int mode, const uint64_t* __restrict__ resident, int64_t res_stride,
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, uint8_t* __restrict__ exact,
+    uint32_t* __restrict__ flags, float* __restrict__ mass_out, const Tin* __restrict__ w_sg,
+    float* __restrict__ g_s) {
   const int lane = lane_id();
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float l = lane < E ? logits[(int64_t)t * E + lane] : -INFINITY;
   if (g_s) {
     const float gd = w_sg ? wave_dot<Tin>(x + (int64_t)t * H, w_sg, H) : 0.f;
     if (lane == 0) g_s[t] = w_sg ? sigmoid_f(gd) : 1.f;
@@ -285,6 +289,48 @@ route_topk_kernel(const Tin* __restrict__ x, const float* __restrict__ logits, i
   }
 }
 
+// One wave per token (4 per block) on logits [T][E] from route_logits_kernel.
+template <typename Tin>
+__global__ void __launch_bounds__(256)
+route_topk_kernel(const Tin* __restrict__ x, const float* __restrict__ logits, int T, int H, int E,
+                  int k, int renorm, float margin, int mode, const uint64_t* __restrict__ resident,
+                  int64_t res_stride, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+                  uint8_t* __restrict__ exact, uint32_t* __restrict__ flags,
+                  float* __restrict__ mass_out, const Tin* __restrict__ w_sg,
+                  float* __restrict__ g_s) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float l = lane < E ? logits[(int64_t)t * E + lane] : -INFINITY;
+  route_topk_token<Tin>(t, l, x, H, E, k, renorm, margin, mode, resident, res_stride, topk_ids,
+                        topk_w, exact, flags, mass_out, w_sg, g_s);
+}
+
+// Small batches: logits and top-k in one launch.  A 1024-thread block takes
+// tpb tokens (<= 16): its 16 waves form the logits of a 16-row token tile on
+// the matrix cores (rows past tpb belong to the next block and go unused),
+// then wave j ranks token t0 + j.
+template <typename Tin>
+__global__ void __launch_bounds__(1024)
+route_fused_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w_router, int T, int H,
+                   int E, int tpb, int k, int renorm, float margin, int mode,
+                   const uint64_t* __restrict__ resident, int64_t res_stride,
+                   int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+                   uint8_t* __restrict__ exact, uint32_t* __restrict__ flags,
+                   float* __restrict__ logits_out, float* __restrict__ mass_out,
+                   const Tin* __restrict__ w_sg, float* __restrict__ g_s) {
+  __shared__ RouteLds lds;
+  const int t0 = blockIdx.x * tpb;
+  tile_logits(x, w_router, T, H, E, t0, lds);
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  const int t = t0 + wv;
+  if (wv >= tpb || t >= T) return;
+  const float l = lane < E ? lds.logits[wv][lane] : -INFINITY;
+  if (lane < E) logits_out[(int64_t)t * E + lane] = l;
+  route_topk_token<Tin>(t, l, x, H, E, k, renorm, margin, mode, resident, res_stride, topk_ids,
+                        topk_w, exact, flags, mass_out, w_sg, g_s);
+}
+
 // APEX prefetch set: top-(k + delta_t) of x W_p^T as a bit mask.
 template <typename Tin>
 __global__ void __launch_bounds__(1024)
@@ -311,10 +357,41 @@ prefetch_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w_p, int T, i
   }
 }
 
+// Batches up to ROUTE_FUSED_MAX_T tokens route in one launch (logits and
+// top-k per block); larger ones spread the logits over (token, expert) tiles
+// first.  Tiny batches put fewer tokens in a block so more CUs share W_r.
+#ifndef ROUTE_FUSED_MAX_T
+#define ROUTE_FUSED_MAX_T 256
+#endif
+#ifndef ROUTE_FUSED_MAX_E
+#define ROUTE_FUSED_MAX_E 16
+#endif
+#ifndef ROUTE_FUSED_SMALL_T
+#define ROUTE_FUSED_SMALL_T 64
+#endif
+#ifndef ROUTE_FUSED_SMALL_TPB
+#define ROUTE_FUSED_SMALL_TPB 4
+#endif
+
 hipError_t launch_route(const moe_dims_t& d, int T, const void* x, const void* w_router,
                         const uint64_t* resident, int64_t res_stride, int mode, int32_t* ids,
                         float* w, uint8_t* exact, uint32_t* flags, float* logits, float* mass,
                         const void* w_sg, float* g_s, hipStream_t s) {
+  if (T <= ROUTE_FUSED_MAX_T && d.n_experts <= ROUTE_FUSED_MAX_E) {
+    const int tpb = T <= ROUTE_FUSED_SMALL_T ? ROUTE_FUSED_SMALL_TPB : ROUTE_TOK;
+    const int blocks = (T + tpb - 1) / tpb;
+    if (d.dtype == MOE_BF16)
+      route_fused_kernel<bf16><<<blocks, 1024, 0, s>>>(
+          (const bf16*)x, (const bf16*)w_router, T, d.hidden, d.n_experts, tpb, d.top_k,
+          d.renormalize, d.tie_margin, mode, resident, res_stride, ids, w, exact, flags, logits,
+          mass, (const bf16*)w_sg, g_s);
+    else
+      route_fused_kernel<float><<<blocks, 1024, 0, s>>>(
+          (const float*)x, (const float*)w_router, T, d.hidden, d.n_experts, tpb, d.top_k,
+          d.renormalize, d.tie_margin, mode, resident, res_stride, ids, w, exact, flags, logits,
+          mass, (const float*)w_sg, g_s);
+    return hipGetLastError();
+  }
   const dim3 lgrid((T + 15) / 16, (d.n_experts + 15) / 16);
   const int tblocks = (T + 3) / 4;
   if (d.dtype == MOE_BF16) {
