@@ -165,18 +165,24 @@ __device__ __forceinline__ KRange k_range(int nsteps, int wk, int WK) {
 }
 
 // Up to 4 token tiles the kernels are held to >= 3 waves per SIMD (at most
-// 168 registers per lane), which keeps enough weight loads in flight per CU.
-#define FFN_OCCUPANCY __attribute__((amdgpu_waves_per_eu(NTT <= 4 ? 3 : 1)))
+// 168 registers per lane), which keeps enough weight loads in flight per CU;
+// the wide-row forms for long segments (gate/up with 2 row tiles per wave,
+// down with 4) take 2 waves per SIMD and the registers they need.
+#define FFN_UP_OCCUPANCY __attribute__((amdgpu_waves_per_eu(NTT <= 4 ? (RW > 1 ? 2 : 3) : 1)))
+#define FFN_DOWN_OCCUPANCY __attribute__((amdgpu_waves_per_eu(NTT <= 4 ? (RW > 2 ? 2 : 3) : 1)))
 
 // ---------------------------------------------------------------- gate+up --
 // One chunk of up to 16*NA tokens of a segment: pipelined k loop, LDS
-// reduction over the WK k-splits, epilogue.  Steps past a wave's range in its
-// last batch load an in-range address and feed a zero token fragment.
-template <int NA, int NTT, int WM, int WK>
+// reduction over the WK k-splits, epilogue.  A wave owns RW row tiles of
+// gate and up, so each token fragment feeds 2*RW MFMAs.  Steps past a wave's
+// range in its last batch load an in-range address and feed a zero token
+// fragment.
+template <int NA, int NTT, int WM, int WK, int RW>
 __device__ __forceinline__ void up_chunk(const FfnMfmaArgs a, const TileInfo& ti, int c0,
-                                         const bf16* ag_row, const bf16* au_row, bool gated,
+                                         const bf16* const (&ag_row)[RW],
+                                         const bf16* const (&au_row)[RW], bool gated,
                                          bool rows_ok, int row_base, int R,
-                                         f32x4_t (*red)[(WK > 1) ? 2 * NTT : 1][MOE_WAVE]) {
+                                         f32x4_t (*red)[(WK > 1) ? 2 * NTT * RW : 1][MOE_WAVE]) {
   constexpr int U = Unroll<NA>::U;
   const int lane = lane_id(), wv = threadIdx.x >> 6, wk = wv / WM, wm = wv % WM;
   const int r16 = lane & 15, kg = lane >> 4;
@@ -189,17 +195,21 @@ __device__ __forceinline__ void up_chunk(const FfnMfmaArgs a, const TileInfo& ti
     const int tok = ti.kind == 1 ? r : a.perm[ti.seg0 + r] / a.k;
     xrow[j] = a.x + (int64_t)tok * H + 8 * kg;
   }
-  f32x4_t accg[NA], accu[NA];
+  f32x4_t accg[NA][RW], accu[NA][RW];
 #pragma unroll
-  for (int j = 0; j < NA; ++j) accg[j] = accu[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NA; ++j)
+#pragma unroll
+    for (int q = 0; q < RW; ++q) accg[j][q] = accu[j][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const KRange kr = k_range<U>(ksteps, wk, WK);
   if (rows_ok && kr.nb > 0) {
-    bf16x8_t g0[U], u0[U], x0[U][NA], g1[U], u1[U], x1[U][NA];
+    bf16x8_t g0[U][RW], u0[U][RW], x0[U][NA], g1[U][RW], u1[U][RW], x1[U][NA];
 #define UP_LOAD(G, UU, X, b)                                                   \
   _Pragma("unroll") for (int u = 0; u < U; ++u) {                              \
     const int ko = min(kr.beg + (b) * U + u, kr.end - 1) << 5;                 \
-    G[u] = frag_load(ag_row + ko);                                             \
-    UU[u] = frag_load(au_row + ko);                                            \
+    _Pragma("unroll") for (int q = 0; q < RW; ++q) {                           \
+      G[u][q] = frag_load(ag_row[q] + ko);                                     \
+      UU[u][q] = frag_load(au_row[q] + ko);                                    \
+    }                                                                          \
     _Pragma("unroll") for (int j = 0; j < NA; ++j) X[u][j] = frag_load(xrow[j] + ko); \
   }
 #define UP_MFMA(G, UU, X, b)                                                   \
@@ -207,8 +217,10 @@ __device__ __forceinline__ void up_chunk(const FfnMfmaArgs a, const TileInfo& ti
     _Pragma("unroll") for (int j = 0; j < NA; ++j) {                           \
       const bool live = kr.beg + (b) * U + u < kr.end;                         \
       const bf16x8_t xv = live ? X[u][j] : frag_zero();                        \
-      accg[j] = mfma16(G[u], xv, accg[j]);                                     \
-      accu[j] = mfma16(UU[u], xv, accu[j]);                                    \
+      _Pragma("unroll") for (int q = 0; q < RW; ++q) {                         \
+        accg[j][q] = mfma16(G[u][q], xv, accg[j][q]);                          \
+        accu[j][q] = mfma16(UU[u][q], xv, accu[j][q]);                         \
+      }                                                                        \
     }
     UP_LOAD(g0, u0, x0, 0);
     for (int bb = 0; bb < kr.nb; bb += 2) {
@@ -223,57 +235,90 @@ __device__ __forceinline__ void up_chunk(const FfnMfmaArgs a, const TileInfo& ti
   if (WK > 1) {
     if (wk > 0 && rows_ok) {
 #pragma unroll
-      for (int j = 0; j < NA; ++j) {
-        red[(wk - 1) * WM + wm][2 * j][lane] = accg[j];
-        red[(wk - 1) * WM + wm][2 * j + 1][lane] = accu[j];
-      }
+      for (int j = 0; j < NA; ++j)
+#pragma unroll
+        for (int q = 0; q < RW; ++q) {
+          red[(wk - 1) * WM + wm][2 * (j * RW + q)][lane] = accg[j][q];
+          red[(wk - 1) * WM + wm][2 * (j * RW + q) + 1][lane] = accu[j][q];
+        }
     }
     __syncthreads();
     if (wk == 0 && rows_ok) {
 #pragma unroll
       for (int w = 0; w < WK - 1; ++w)
 #pragma unroll
-        for (int j = 0; j < NA; ++j) {
-          accg[j] += red[w * WM + wm][2 * j][lane];
-          accu[j] += red[w * WM + wm][2 * j + 1][lane];
-        }
+        for (int j = 0; j < NA; ++j)
+#pragma unroll
+          for (int q = 0; q < RW; ++q) {
+            accg[j][q] += red[w * WM + wm][2 * (j * RW + q)][lane];
+            accu[j][q] += red[w * WM + wm][2 * (j * RW + q) + 1][lane];
+          }
     }
     __syncthreads();
   }
   if (wk == 0 && rows_ok) {
-    const int i = row_base + 4 * kg;
 #pragma unroll
-    for (int j = 0; j < NA; ++j) {
-      const int r = c0 + 16 * j + r16;
-      if (r < ti.n && i < R) {
-        float v[4];
+    for (int q = 0; q < RW; ++q) {
+      const int i = row_base + 16 * q + 4 * kg;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = gated ? silu_f(accg[j][q]) * accu[j][q] : accg[j][q];
-        if (ti.kind == 0)
-          store_bf16x4(a.act, (int64_t)(ti.seg0 + r) * a.I + i, v);
-        else if (ti.kind == 1)
-          store_bf16x4(a.acts, (int64_t)r * ((int64_t)a.ns * a.Is) + (int64_t)ti.e * a.Is + i, v);
-        else
-          store_bf16x4(a.z, (int64_t)(ti.seg0 + r) * a.r + i, v);
+      for (int j = 0; j < NA; ++j) {
+        const int r = c0 + 16 * j + r16;
+        if (r < ti.n && i < R) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = gated ? silu_f(accg[j][q][e]) * accu[j][q][e] : accg[j][q][e];
+          if (ti.kind == 0)
+            store_bf16x4(a.act, (int64_t)(ti.seg0 + r) * a.I + i, v);
+          else if (ti.kind == 1)
+            store_bf16x4(a.acts, (int64_t)r * ((int64_t)a.ns * a.Is) + (int64_t)ti.e * a.Is + i, v);
+          else
+            store_bf16x4(a.z, (int64_t)(ti.seg0 + r) * a.r + i, v);
+        }
       }
     }
   }
 }
 
-template <int NTT, int WM, int WK>
-__global__ void __launch_bounds__(256) FFN_OCCUPANCY ffn_up_mfma_kernel(FfnMfmaArgs a) {
+// The smallest instantiation covering the live token tiles of chunk c0.
+template <int NTT, int WM, int WK, int RW>
+__device__ __forceinline__ void up_dispatch(const FfnMfmaArgs a, const TileInfo& ti, int c0,
+                                            const bf16* const (&ag_row)[RW],
+                                            const bf16* const (&au_row)[RW], bool gated,
+                                            bool rows_ok, int row_base, int R,
+                                            f32x4_t (*red)[(WK > 1) ? 2 * NTT * RW : 1][MOE_WAVE]) {
+  const int nt = min(NTT, (ti.n - c0 + 15) >> 4);  // block-uniform
+  if (nt <= 1) {
+    up_chunk<1, NTT, WM, WK, RW>(a, ti, c0, ag_row, au_row, gated, rows_ok, row_base, R, red);
+  } else if constexpr (NTT >= 2) {
+    if (nt <= 2) {
+      up_chunk<2, NTT, WM, WK, RW>(a, ti, c0, ag_row, au_row, gated, rows_ok, row_base, R, red);
+    } else if constexpr (NTT >= 4) {
+      if (nt <= 4) {
+        up_chunk<4, NTT, WM, WK, RW>(a, ti, c0, ag_row, au_row, gated, rows_ok, row_base, R, red);
+      } else if constexpr (NTT >= 8) {
+        if (nt <= 8)
+          up_chunk<8, NTT, WM, WK, RW>(a, ti, c0, ag_row, au_row, gated, rows_ok, row_base, R, red);
+        else if constexpr (NTT >= 16)
+          up_chunk<16, NTT, WM, WK, RW>(a, ti, c0, ag_row, au_row, gated, rows_ok, row_base, R, red);
+      }
+    }
+  }
+}
+
+// RW: row tiles per wave for routed and shared tiles (LoRE tiles, with only
+// r rows, keep one).
+template <int NTT, int WM, int WK, int RW>
+__global__ void __launch_bounds__(256) FFN_UP_OCCUPANCY ffn_up_mfma_kernel(FfnMfmaArgs a) {
   static_assert(WM * WK == 4, "four waves per block");
   // k-split partials, one slot per (k-split > 0, row strip)
-  __shared__ f32x4_t red[(WK > 1) ? (WK - 1) * WM : 1][(WK > 1) ? 2 * NTT : 1][MOE_WAVE];
-  const TileInfo ti = tile_of<16 * WM>(a);
+  __shared__ f32x4_t red[(WK > 1) ? (WK - 1) * WM : 1][(WK > 1) ? 2 * NTT * RW : 1][MOE_WAVE];
+  const TileInfo ti = tile_of<16 * WM * RW, 16 * WM>(a);
   if (ti.kind < 0) return;
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   const int wm = wv % WM;
   const int H = a.H;
   const bool gated = ti.kind != 2;
   const int R = ti.kind == 0 ? a.I : (ti.kind == 1 ? a.Is : a.r);
-  const int row_base = ti.row0 + 16 * wm;
-  const bool rows_ok = row_base < R;  // wave-uniform
   const bf16 *wg, *wu;
   if (ti.kind == 0) {
     wg = a.w0 + (int64_t)ti.e * a.I * H;
@@ -288,28 +333,28 @@ __global__ void __launch_bounds__(256) FFN_OCCUPANCY ffn_up_mfma_kernel(FfnMfmaA
   const int r16 = lane & 15, kg = lane >> 4;
   // a 16-row tile can overhang R (a LoRE rank that is a multiple of 8 only):
   // overhanging lanes reread row R-1 and their outputs are not stored
-  const int wrow_i = min(row_base + r16, R - 1);
-  const bf16* ag_row = wg + (int64_t)wrow_i * H + 8 * kg;
-  const bf16* au_row = wu + (int64_t)wrow_i * H + 8 * kg;
-  for (int c0 = 0; c0 < ti.n; c0 += 16 * NTT) {
-    const int nt = min(NTT, (ti.n - c0 + 15) >> 4);  // block-uniform
-    if (nt <= 1) {
-      up_chunk<1, NTT, WM, WK>(a, ti, c0, ag_row, au_row, gated, rows_ok, row_base, R, red);
-    } else if constexpr (NTT >= 2) {
-      if (nt <= 2) {
-        up_chunk<2, NTT, WM, WK>(a, ti, c0, ag_row, au_row, gated, rows_ok, row_base, R, red);
-      } else if constexpr (NTT >= 4) {
-        if (nt <= 4) {
-          up_chunk<4, NTT, WM, WK>(a, ti, c0, ag_row, au_row, gated, rows_ok, row_base, R, red);
-        } else if constexpr (NTT >= 8) {
-          if (nt <= 8)
-            up_chunk<8, NTT, WM, WK>(a, ti, c0, ag_row, au_row, gated, rows_ok, row_base, R, red);
-          else if constexpr (NTT >= 16)
-            up_chunk<16, NTT, WM, WK>(a, ti, c0, ag_row, au_row, gated, rows_ok, row_base, R, red);
-        }
-      }
-    }
+  if (ti.kind == 2) {
+    const int row_base = ti.row0 + 16 * wm;
+    const bool rows_ok = row_base < R;  // wave-uniform
+    const int wrow_i = min(row_base + r16, R - 1);
+    const bf16* const ag[1] = {wg + (int64_t)wrow_i * H + 8 * kg};
+    for (int c0 = 0; c0 < ti.n; c0 += 16 * NTT)
+      up_dispatch<NTT, WM, WK, 1>(a, ti, c0, ag, ag, gated, rows_ok, row_base, R,
+                                  reinterpret_cast<f32x4_t(*)[(WK > 1) ? 2 * NTT : 1][MOE_WAVE]>(red));
+    return;
   }
+  const int row_base = ti.row0 + 16 * RW * wm;
+  const bool rows_ok = row_base < R;  // wave-uniform
+  const bf16* ag[RW];
+  const bf16* au[RW];
+#pragma unroll
+  for (int q = 0; q < RW; ++q) {
+    const int wrow_i = min(row_base + 16 * q + r16, R - 1);
+    ag[q] = wg + (int64_t)wrow_i * H + 8 * kg;
+    au[q] = wu + (int64_t)wrow_i * H + 8 * kg;
+  }
+  for (int c0 = 0; c0 < ti.n; c0 += 16 * NTT)
+    up_dispatch<NTT, WM, WK, RW>(a, ti, c0, ag, au, gated, rows_ok, row_base, R, red);
 }
 
 // ------------------------------------------------------------------- down --
@@ -469,7 +514,7 @@ __device__ __forceinline__ void down_dispatch(const FfnMfmaArgs a, const TileInf
 }
 
 template <int NTT, int WM, int WK, int RW>
-__global__ void __launch_bounds__(256) FFN_OCCUPANCY ffn_down_mfma_kernel(FfnMfmaArgs a) {
+__global__ void __launch_bounds__(256) FFN_DOWN_OCCUPANCY ffn_down_mfma_kernel(FfnMfmaArgs a) {
   static_assert(WM * WK == 4, "four waves per block");
   // k-split partials, one slot per (k-split > 0, row strip)
   __shared__ f32x4_t red[(WK > 1) ? (WK - 1) * WM : 1][(WK > 1) ? NTT * RW : 1][MOE_WAVE];
@@ -489,23 +534,34 @@ __global__ void __launch_bounds__(256) FFN_OCCUPANCY ffn_down_mfma_kernel(FfnMfm
   for (int c0 = 0; c0 < ti.n; c0 += 16 * NTT) down_dispatch<NTT, WM, WK, RW>(a, ti, c0, rows_ok, row_base, red, false);
 }
 
-// Down row tiles per wave: 2 up to 4 token tiles (activation fragments reused
-// twice), 1 beyond (the MFMA work per weight byte is already high).
-template <int NTT>
-struct DownRW {
-  static constexpr int RW = NTT <= 4 ? 2 : 1;
+#ifndef FFN_LONG_DOWN_RW
+#define FFN_LONG_DOWN_RW 4
+#endif
+
+// Row tiles per wave.  Short segments (the decode case, a few tokens per
+// expert): gate/up 1, down 2 up to 4 token tiles (activation fragments reused
+// twice), 1 beyond.  Long segments (more than one token tile per expert on
+// average): each token fragment is reused over more weight rows, gate/up 2
+// and down 4 up to 4 token tiles.
+template <int NTT, bool LONG>
+struct RowTiles {
+  static constexpr int UP = (LONG && NTT <= 4) ? 2 : 1;
+  static constexpr int DOWN = NTT <= 4 ? (LONG ? FFN_LONG_DOWN_RW : 2) : 1;
 };
 
-template <int NTT, int WM, int WK>
+template <int NTT, int WM, int WK, bool LONG>
 static void launch_kernels(FfnMfmaArgs up, FfnMfmaArgs dn, hipStream_t s, int which) {
-  constexpr int RW = DownRW<NTT>::RW;
+  constexpr int RW = RowTiles<NTT, LONG>::DOWN;
+  constexpr int RWU = RowTiles<NTT, LONG>::UP;
   const int H = up.H;
+  up.tiles_r = (up.I + 16 * WM * RWU - 1) / (16 * WM * RWU);
+  up.tiles_s = up.Is > 0 ? (up.Is + 16 * WM * RWU - 1) / (16 * WM * RWU) : 0;
   dn.tiles_r = (H + 16 * RW * WM - 1) / (16 * RW * WM);
   dn.tiles_s = dn.tiles_r;
   dn.tiles_l = dn.slots_l > 0 ? (H + LoreDownRows<RW>::ROWS - 1) / LoreDownRows<RW>::ROWS : 0;
   const int n_up = up.slots_r * up.tiles_r + up.n_shared_seg * up.tiles_s + up.slots_l * up.tiles_l;
   const int n_dn = dn.slots_r * dn.tiles_r + dn.n_shared_seg * dn.tiles_s + dn.slots_l * dn.tiles_l;
-  if ((which & 1) && n_up > 0) ffn_up_mfma_kernel<NTT, WM, WK><<<n_up, 256, 0, s>>>(up);
+  if ((which & 1) && n_up > 0) ffn_up_mfma_kernel<NTT, WM, WK, RWU><<<n_up, 256, 0, s>>>(up);
   if ((which & 2) && n_dn > 0) ffn_down_mfma_kernel<NTT, WM, WK, RW><<<n_dn, 256, 0, s>>>(dn);
 }
 
@@ -562,12 +618,24 @@ hipError_t launch_ffn_mfma(const moe_dims_t& d, int T, const void* x, const moe_
   dn.ws1 = nullptr;
   dn.wl = (const bf16*)w.lore_B;
   dn.n_shared_seg = (shared && d.n_shared > 0) ? 1 : 0;
-  switch (NTT) {
-    case 1: launch_kernels<1, 1, 4>(up, dn, s, which); break;
-    case 2: launch_kernels<2, 1, 4>(up, dn, s, which); break;
-    case 4: launch_kernels<4, 1, 4>(up, dn, s, which); break;
-    case 8: launch_kernels<8, 2, 2>(up, dn, s, which); break;
-    default: launch_kernels<16, 4, 1>(up, dn, s, which); break;
+  // long segments: more than one token tile per routed expert on average
+  const bool long_seg = routed && (int64_t)T * d.top_k > 16LL * d.n_experts;
+  if (long_seg) {
+    switch (NTT) {
+      case 1: launch_kernels<1, 1, 4, true>(up, dn, s, which); break;
+      case 2: launch_kernels<2, 1, 4, true>(up, dn, s, which); break;
+      case 4: launch_kernels<4, 1, 4, true>(up, dn, s, which); break;
+      case 8: launch_kernels<8, 2, 2, true>(up, dn, s, which); break;
+      default: launch_kernels<16, 4, 1, true>(up, dn, s, which); break;
+    }
+  } else {
+    switch (NTT) {
+      case 1: launch_kernels<1, 1, 4, false>(up, dn, s, which); break;
+      case 2: launch_kernels<2, 1, 4, false>(up, dn, s, which); break;
+      case 4: launch_kernels<4, 1, 4, false>(up, dn, s, which); break;
+      case 8: launch_kernels<8, 2, 2, false>(up, dn, s, which); break;
+      default: launch_kernels<16, 4, 1, false>(up, dn, s, which); break;
+    }
   }
   return hipGetLastError();
 }

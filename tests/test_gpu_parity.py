@@ -47,6 +47,12 @@ SMALL = {
     "prefill_small": _variant("dsv2_lite", name="prefill_small", hidden=256, n_experts=4, top_k=2,
                               inter=192, n_shared=1, shared_inter=320, token_counts=(300,),
                               resident_count=2, seed=106),
+    # long routed segments on the decode kernels (more than one 16-token
+    # tile per expert, at most four): gate/up waves with two row tiles,
+    # down waves with four; ragged intermediate sizes
+    "long_seg": _variant("qwen2_57b", name="long_seg", hidden=640, n_experts=8, top_k=4,
+                         inter=336, shared_inter=528, token_counts=(64,), resident_count=4,
+                         seed=108),
     # 65-128 tokens with the shared experts on the decode kernels: eight
     # 16-token tiles, two row strips x two k-splits per block
     "dsv2_t100": _variant("dsv2_lite", name="dsv2_t100", hidden=512, n_experts=16, top_k=4,
@@ -85,6 +91,7 @@ def _check_full(layer, T, mode, sample=None, dims_over=None):
     ("granite_small", "standard"), ("granite_small", "stall_free"),
     ("prefill_small", "standard"), ("prefill_small", "lore"),
     ("dsv2_t100", "standard"), ("dsv2_t100", "lore"),
+    ("long_seg", "standard"), ("long_seg", "lore"),
 ])
 def test_small_layer_parity(name, mode):
     layer = W.Layer(SMALL[name])
