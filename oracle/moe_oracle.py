@@ -45,8 +45,13 @@ notes):
   FloE down weights are stored [I][H] (one channel's H-vector contiguous).
   Router and prefetch-router weights are stored [E][H].
 
+* APEX's adaptive budget is the least delta with p_delta >= tau; when no
+  delta in 0..N-k qualifies the budget is N-k (everything is prefetched).  Its
+  near-tie is measured on the logit scale: |theta_d - s - logit(tau)| below
+  ``tie_margin`` at the chosen d or at d - 1.
+
 Flag bits per token: 1 route near-tie, 2 prefetch near-tie, 4 substitution
-near-tie, 8 FloE mask near-tie.
+near-tie, 8 FloE mask near-tie, 16 prefetch-budget near-tie.
 """
 from __future__ import annotations
 
@@ -60,11 +65,13 @@ __all__ = [
     "bf16_to_f64", "fp16_to_f64", "decode", "silu", "sigmoid",
     "router_logits", "softmax", "rank_experts", "route_token",
     "prefetch_set", "prefetch_masks", "delta_star", "stall_free_select",
+    "FLAG_BUDGET", "adaptive_budget", "prefetch_overlap", "adaptive_prefetch",
     "permute", "swiglu_expert", "dequant_int2", "floe_expert",
     "shared_experts", "lore_residual", "layer_forward", "WeightSource",
 ]
 
 FLAG_ROUTE, FLAG_PREFETCH, FLAG_SUBST, FLAG_FLOE = 1, 2, 4, 8
+FLAG_BUDGET = 16
 MODES = ("standard", "lore", "stall_free", "floe")
 
 
@@ -168,6 +175,56 @@ def delta_star(routed: Sequence[int], lp_row: np.ndarray, k: int) -> int:
         if set(routed) <= set(order[: k + d]):
             return d
     raise AssertionError("unreachable: delta = N-k lists every expert")
+
+
+def adaptive_budget(x_row: np.ndarray, w_delta: np.ndarray, theta: Sequence[float],
+                    tau: float, margin: float = 1e-4):
+    """APEX adaptive budget [Sec. 4.2]: an ordinal logistic CDF
+    p_delta(x) = Pr(delta >= delta* | x) = sigmoid(theta_delta - w^T x) over
+    delta = 0..N-k, and delta_hat(x) = the least delta with p_delta >= tau.
+    theta has N-k+1 entries (non-decreasing on the page; the least qualifying
+    delta is taken either way).  Returns (delta_hat, near-tie flag)."""
+    s = float(np.dot(np.asarray(w_delta, dtype=np.float64), np.asarray(x_row, dtype=np.float64)))
+    lt = math.log(tau / (1.0 - tau))
+    d_hat = len(theta) - 1
+    for d, th in enumerate(theta):
+        if sigmoid(float(th) - s) >= tau:
+            d_hat = d
+            break
+    near = abs(float(theta[d_hat]) - s - lt) < margin
+    if d_hat > 0:
+        near = near or abs(float(theta[d_hat - 1]) - s - lt) < margin
+    return d_hat, bool(near)
+
+
+def prefetch_overlap(routed: Sequence[int], mask: int) -> int:
+    """Routed experts inside the prefetch list: the page's expert overlap of a
+    token is this count over k [APEX Sec. 5.1]."""
+    return sum(1 for e in routed if (mask >> int(e)) & 1)
+
+
+def adaptive_prefetch(x: np.ndarray, w_prefetch: np.ndarray, w_delta: np.ndarray,
+                      theta: Sequence[float], tau: float, k: int,
+                      routed: Optional[np.ndarray] = None, margin: float = 1e-4):
+    """Per token: delta_hat [Sec. 4.2], the top-(k + delta_hat) prefetch mask
+    [Sec. 4.1], and, given the router's choices, delta* and the overlap.
+    Returns (delta_hat, masks, flags, delta_star or None, overlap or None)."""
+    lp = router_logits(x, w_prefetch)
+    T = x.shape[0]
+    d_hat = np.zeros(T, dtype=np.int32)
+    flags = np.zeros(T, dtype=np.uint32)
+    masks = []
+    for t in range(T):
+        d, fb = adaptive_budget(x[t], w_delta, theta, tau, margin)
+        m, fp = prefetch_set(lp[t], k + d, margin)
+        d_hat[t] = d
+        masks.append(m)
+        flags[t] = (FLAG_BUDGET if fb else 0) | (FLAG_PREFETCH if fp else 0)
+    if routed is None:
+        return d_hat, masks, flags, None, None
+    ds = np.array([delta_star(routed[t], lp[t], k) for t in range(T)], dtype=np.int32)
+    ov = np.array([prefetch_overlap(routed[t], masks[t]) for t in range(T)], dtype=np.int32)
+    return d_hat, masks, flags, ds, ov
 
 
 def stall_free_select(k_routed: Sequence[int], q_r: np.ndarray, k_prefetched: set,

@@ -499,3 +499,70 @@ def test_workload_generator_shapes_and_determinism():
     v = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, 1.0 + 2**-8 + 2**-20], dtype=np.float32)
     bits = W.bf16_bits_from_f32(v)
     np.testing.assert_array_equal(O.bf16_to_f64(bits), [1.0, 1.0, 1.0 + 4 * 2**-8, 1.0 + 2**-7])
+
+
+# ------------------------------------------------- APEX adaptive budget --
+def _sig(z):
+    return 1.0 / (1.0 + math.exp(-z))
+
+
+def test_adaptive_budget_closed_forms():
+    """delta_hat = min{d : sigmoid(theta_d - w.x) >= tau} [APEX Sec. 4.2], on
+    scores whose value is exact: w = a e_0, x = b e_0, so w.x = a*b."""
+    H = 8
+    for a, b in [(0.5, 1.0), (-1.25, 2.0), (3.0, 0.75), (0.0, 5.0)]:
+        w = np.zeros(H); w[0] = a
+        x = np.zeros(H); x[0] = b
+        s = a * b
+        for tau in (0.6, 0.9, 0.97):
+            lt = math.log(tau / (1 - tau))
+            # constant theta: the first delta qualifies or none does (then N-k)
+            for c in (-3.0, 0.0, 1.7, 6.0):
+                th = [c] * 5
+                d, _ = O.adaptive_budget(x, w, th, tau)
+                assert d == (0 if _sig(c - s) >= tau else 4)
+            # linear theta_d = a0 + g d: least integer d >= (s + logit(tau) - a0) / g
+            for a0, g in [(-2.0, 0.5), (0.3, 1.1), (-5.0, 0.7)]:
+                th = [a0 + g * d for d in range(33)]
+                want = min(32, max(0, math.ceil((s + lt - a0) / g)))
+                assert abs((s + lt - a0) / g - round((s + lt - a0) / g)) > 1e-6  # off a boundary
+                d, _ = O.adaptive_budget(x, w, th, tau)
+                assert d == want, (a, b, tau, a0, g)
+
+
+def test_adaptive_budget_monotone():
+    """A larger tau never lowers the budget; raising every threshold theta_d
+    (more confidence at each budget) never raises it."""
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        H = 16
+        x = rng.standard_normal(H)
+        w = rng.standard_normal(H) / 4
+        th = np.cumsum(rng.uniform(0, 1, 9)) - 3
+        ds = [O.adaptive_budget(x, w, th, tau)[0] for tau in (0.5, 0.7, 0.9, 0.99)]
+        assert ds == sorted(ds)
+        assert O.adaptive_budget(x, w, th + 0.8, 0.9)[0] <= ds[2]
+
+
+def test_overlap_full_exactly_when_budget_covers_delta_star():
+    """The page's overlap is |K_r & K_p| / k; with the list top-(k + delta) it
+    is complete exactly when delta >= delta* (the definition of delta*),
+    checked on random tiny layers against a set intersection."""
+    rng = np.random.default_rng(12)
+    E, k, H = 9, 3, 12
+    for _ in range(100):
+        x = rng.standard_normal((4, H))
+        wr = rng.standard_normal((E, H))
+        wp = wr + rng.standard_normal((E, H)) * 0.7
+        wd = rng.standard_normal(H) / 3
+        th = np.cumsum(rng.uniform(0.2, 1.0, E - k + 1)) - 2
+        routed = np.array([O.route_token(O.router_logits(x[t:t + 1], wr)[0], k, True, 1e-4)[0]
+                           for t in range(4)])
+        d_hat, masks, _, ds, ov = O.adaptive_prefetch(x, wp, wd, th, 0.9, k, routed=routed)
+        lp = O.router_logits(x, wp)
+        for t in range(4):
+            order = sorted(range(E), key=lambda e: (-lp[t][e], e))
+            kp = set(order[: k + int(d_hat[t])])
+            assert masks[t] == _mask(kp)
+            assert ov[t] == len(set(routed[t]) & kp)
+            assert (ov[t] == k) == (d_hat[t] >= ds[t])

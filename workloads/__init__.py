@@ -43,6 +43,7 @@ Layouts (all row-major, C order):
 * ``lore_A``        [E][r][H];  ``lore_B`` [E][H][r]
 * ``resident``      one uint64 bit mask of resident experts (bit e = expert e)
 * ``delta``         [T] int32 extra prefetch budget per token
+* ``w_delta``, ``theta``  APEX ordinal budget model: [H] and [N-k+1] fp32
 
 bf16 tensors are returned as uint16 bit patterns (round-to-nearest-even from
 the fp32 draw); fp32 tensors as float32.  Every tensor has its own seed stream
@@ -61,7 +62,7 @@ import numpy as np
 
 __all__ = [
     "MoEConfig", "CONFIGS", "Layer", "make_layer", "bf16_bits_from_f32",
-    "fp16_bits_from_f32", "quantize_int2_g64", "draw_delta", "draw_resident",
+    "fp16_bits_from_f32", "quantize_int2_g64", "draw_delta", "draw_resident", "draw_ordinal",
 ]
 
 
@@ -132,7 +133,7 @@ CONFIGS: Dict[str, MoEConfig] = {
 _TAG = {"x": 1, "w_router": 2, "w_gate": 3, "w_up": 4, "w_down": 5,
         "ws_gate": 6, "ws_up": 7, "ws_down": 8, "w_shared_gate": 9,
         "lore_A": 10, "lore_B": 11, "resident": 12, "w_prefetch": 13,
-        "delta": 14}
+        "delta": 14, "w_delta": 15, "theta": 16}
 
 
 def _rng(seed: int, tag: str, idx: int = 0) -> np.random.Generator:
@@ -203,6 +204,19 @@ def draw_delta(cfg: MoEConfig, seed: int, T: int) -> np.ndarray:
     return np.minimum(d, cfg.delta_cap).astype(np.int32)
 
 
+def draw_ordinal(cfg: MoEConfig, seed: int, tau: float = 0.9):
+    """Synthetic APEX ordinal budget model (the page trains it; no trained
+    values exist here): w [H] ~ N(0, 1/H), so w.x has unit spread for unit x;
+    theta [N-k+1] non-decreasing, theta_d = logit(tau) - 2 + sum of d steps
+    drawn from 0.5 * U(0.5, 1.5), which puts the mean budget near 4 at tau.
+    Returns (w fp32, theta fp32)."""
+    w = _normal(_rng(seed, "w_delta"), (cfg.hidden,), 1.0 / np.sqrt(cfg.hidden))
+    steps = _rng(seed, "theta").uniform(0.5, 1.5, size=cfg.delta_cap).astype(np.float32) * np.float32(0.5)
+    base = np.float32(np.log(tau / (1.0 - tau)) - 2.0)
+    theta = np.concatenate([[base], base + np.cumsum(steps, dtype=np.float32)]).astype(np.float32)
+    return w, theta
+
+
 class Layer:
     """Lazily drawn inputs of one MoE layer for a workload.
 
@@ -246,6 +260,14 @@ class Layer:
     def delta(self, T: Optional[int] = None) -> np.ndarray:
         d = draw_delta(self.cfg, self.seed, self.cfg.t_max)
         return d if T is None else d[:T]
+
+    def ordinal(self, tau: float = 0.9):
+        """(w_delta in storage dtype, theta fp32) of the APEX budget model."""
+        key = ("ordinal", 0)
+        if key not in self._cache:
+            w, th = draw_ordinal(self.cfg, self.seed, tau)
+            self._cache[key] = (self._to_storage(w), th)
+        return self._cache[key]
 
     def _small(self, name, shape, std):
         key = (name, 0)
