@@ -313,6 +313,63 @@ def cpu_baseline(name, T, mode, budget_s=10.0):
                        f"{calls} fp64 NumPy oracle call(s), {total:.1f} s in total")
 
 
+def measure_prefetch_adaptive(name, T, steps, warmup, tau=0.9):
+    """The APEX adaptive prefetch call (budget, list, delta* and overlap) on
+    its own: time per call, its HBM rate against the bytes it must move
+    (x, W_p, w_delta, theta, the router's ids in; budget, mask, flags,
+    delta*, overlap out), and the budget and overlap it reaches."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from workloads.device import dims_dict, tensor
+    import sparse_moe_layer_route_amd as M
+
+    layer = W.make_layer(name)
+    cfg = layer.cfg
+    k, E, H = cfg.top_k, cfg.n_experts, cfg.hidden
+    dims = M.Dims(**dims_dict(cfg)).c()
+    x = tensor(layer.x(T), cfg.dtype, "cuda")
+    wp = tensor(layer.w_prefetch(), cfg.dtype, "cuda")
+    w_delta, theta = layer.ordinal(tau)
+    wd = tensor(w_delta, cfg.dtype, "cuda")
+    th = torch.from_numpy(np.ascontiguousarray(theta, np.float32)).cuda()
+    # the router's choices from the layer's own router (moe_route)
+    wr = tensor(layer.w_router(), cfg.dtype, "cuda")
+    ids = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    tw = torch.empty(T * k, dtype=torch.float32, device="cuda")
+    ex = torch.empty(T * k, dtype=torch.uint8, device="cuda")
+    fl = torch.empty(T, dtype=torch.int32, device="cuda")
+    lg = torch.empty(T * E, dtype=torch.float32, device="cuda")
+    M.moe_route(dims, T, x, wr, None, 0, "standard", ids, tw, ex, fl, lg)
+    delta = torch.empty(T, dtype=torch.int32, device="cuda")
+    mask = torch.empty(T, dtype=torch.int64, device="cuda")
+    ds = torch.empty(T, dtype=torch.int32, device="cuda")
+    ov = torch.empty(T, dtype=torch.int32, device="cuda")
+
+    def call():
+        M.moe_prefetch_adaptive(dims, T, x, wp, wd, th, tau, delta, mask, fl, topk_ids=ids,
+                                delta_star=ds, overlap=ov)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / steps
+    esz = 4 if cfg.dtype == "f32" else 2
+    nbytes = (T * H + E * H + H) * esz + (E - k + 1) * 4 + T * k * 4 + T * (4 + 8 + 4 + 4 + 4)
+    d, o, st = delta.cpu().numpy(), ov.cpu().numpy(), ds.cpu().numpy()
+    return dict(workload=name, tokens=T, mode="prefetch_adaptive", us_per_call=us,
+                gbs=nbytes / (us * 1e-6) / 1e9, hbm_frac=nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                bytes=nbytes, tau=tau, mean_budget=float(d.mean()),
+                overlap=float(o.mean() / k), covered=float((d >= st).mean()))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -348,6 +405,11 @@ def main():
                   f"{r['tokens_per_s']:.0f} tok/s, {r['step_gbs']:.0f} GB/s"
                   + (f", {r['roofline']['kernel']} {r['roofline']['frac']*100:.1f}% of {r['roofline']['bound']}"
                      if 'roofline' in r else ""), file=sys.stderr, flush=True)
+        r = measure_prefetch_adaptive("granite_prefill", 4096, args.steps, min(args.warmup, 5))
+        also.append(r)
+        print(f"# granite_prefill T=4096 adaptive prefetch: {r['us_per_call']:.1f} us/call, "
+              f"{r['gbs']:.0f} GB/s, mean budget {r['mean_budget']:.2f}, overlap {r['overlap']:.3f}, "
+              f"covered {r['covered']:.3f}", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu else cpu_baseline(args.workload, args.tokens, args.mode)
     line = {
         "metric": METRIC,

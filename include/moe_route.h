@@ -174,6 +174,28 @@ moe_status_t moe_prefetch_mask(const moe_dims_t* dims, int32_t T, const void* x,
                                const void* w_prefetch, const int32_t* delta,
                                uint64_t* mask_out, uint32_t* flags, void* stream);
 
+/* APEX adaptive prefetch [APEX page, Sec. 4.2 (ordinal budget model) and
+ * Sec. 5.1 (expert overlap)]: per token, s = w_delta . x_t and
+ * p_d = sigmoid(theta[d] - s) for budgets d = 0..E-k; delta_out[t] = the least
+ * d with p_d >= tau, or E-k when none qualifies; then mask_out[t] = the
+ * top-(k + delta_out[t]) experts of x W_p^T exactly as moe_prefetch_mask.
+ *   x [T][H] dtype, w_prefetch [E][H] dtype, w_delta [H] dtype, theta
+ *   [E-k+1] fp32 (device), tau in (0, 1) (host value; MOE_EINVAL outside).
+ *   flags [T] is overwritten: bit 2 as in moe_prefetch_mask, bit 16 where
+ *   theta[d] - s sits within dims.tie_margin of logit(tau) at the chosen
+ *   budget or the one below it (the budget itself is then a near-tie).
+ *   topk_ids_opt [T][k] (the router's choices, moe_route's topk_ids) with
+ *   delta_star_opt [T] and overlap_opt [T] int32: delta* = the least budget
+ *   whose list holds every routed expert, overlap = how many routed experts
+ *   the chosen list holds.  These three are all NULL or all set
+ *   (MOE_EINVAL otherwise); routed ids outside 0..E-1 are skipped.
+ *   Everything is caller-owned device memory; nothing is allocated. */
+moe_status_t moe_prefetch_adaptive(const moe_dims_t* dims, int32_t T, const void* x,
+                                   const void* w_prefetch, const void* w_delta,
+                                   const float* theta, float tau, const int32_t* topk_ids_opt,
+                                   int32_t* delta_out, uint64_t* mask_out, uint32_t* flags,
+                                   int32_t* delta_star_opt, int32_t* overlap_opt, void* stream);
+
 /* Stable counting sort of the exact (token, slot) pairs by expert: pair
  * f = t*k + j.  expert_offsets [E+1]; perm [T*k] holds f, grouped by expert,
  * f increasing inside a group (first offsets[E] entries); inv [T*k] = position

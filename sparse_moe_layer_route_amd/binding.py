@@ -73,6 +73,8 @@ def _load():
         "moe_workspace_size": ([D, I32, ctypes.c_int, ctypes.POINTER(SZ)], ctypes.c_int),
         "moe_route": ([D, I32, P, P, P, I64, ctypes.c_int, P, P, P, P, P, P, P], ctypes.c_int),
         "moe_prefetch_mask": ([D, I32, P, P, P, P, P, P], ctypes.c_int),
+        "moe_prefetch_adaptive": ([D, I32, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, P],
+                                  ctypes.c_int),
         "moe_permute": ([I32, I32, I32, P, P, P, P, P, P, SZ, P], ctypes.c_int),
         "moe_expert_ffn": ([D, I32, P, Wp, ctypes.c_int, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
         "moe_lore_surrogate": ([D, I32, P, P, P, P, P, P, P], ctypes.c_int),
@@ -88,7 +90,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_route",
-            "moe_prefetch_mask", "moe_permute", "moe_expert_ffn", "moe_lore_surrogate",
+            "moe_prefetch_mask", "moe_prefetch_adaptive", "moe_permute", "moe_expert_ffn", "moe_lore_surrogate",
             "moe_combine", "moe_layer_forward")
 
 
@@ -174,6 +176,15 @@ def moe_prefetch_mask(dims, T, x, w_prefetch, delta, mask_out, flags, stream=Non
     _check(_lib.moe_prefetch_mask(ctypes.byref(_dims(dims)), T, _ptr(x), _ptr(w_prefetch),
                                   _ptr(delta), _ptr(mask_out), _ptr(flags), _stream(stream)),
            "moe_prefetch_mask")
+
+
+def moe_prefetch_adaptive(dims, T, x, w_prefetch, w_delta, theta, tau, delta_out, mask_out, flags,
+                          topk_ids=None, delta_star=None, overlap=None, stream=None):
+    _check(_lib.moe_prefetch_adaptive(ctypes.byref(_dims(dims)), T, _ptr(x), _ptr(w_prefetch),
+                                      _ptr(w_delta), _ptr(theta), float(tau), _ptr(topk_ids),
+                                      _ptr(delta_out), _ptr(mask_out), _ptr(flags),
+                                      _ptr(delta_star), _ptr(overlap), _stream(stream)),
+           "moe_prefetch_adaptive")
 
 
 def moe_permute(T, k, E, topk_ids, exact, expert_offsets, perm, inv, ws=None, stream=None):

@@ -3,6 +3,8 @@
 // synchronises; every check runs before the first enqueue.
 #include <string.h>
 
+#include <cmath>
+
 #include "common.h"
 
 namespace moe {
@@ -10,6 +12,11 @@ hipError_t launch_route(const moe_dims_t& d, int T, const void* x, const void* w
                         const uint64_t* resident, int64_t res_stride, int mode, int32_t* ids,
                         float* w, uint8_t* exact, uint32_t* flags, float* logits, float* mass,
                         const void* w_sg, float* g_s, hipStream_t s);
+hipError_t launch_prefetch_adaptive(const moe_dims_t& d, int T, const void* x, const void* w_p,
+                                    const void* w_delta, const float* theta, float logit_tau,
+                                    const int32_t* routed, int32_t* delta_out,
+                                    uint64_t* mask_out, uint32_t* flags, int32_t* delta_star,
+                                    int32_t* overlap, hipStream_t s);
 hipError_t launch_prefetch(const moe_dims_t& d, int T, const void* x, const void* w_p,
                            const int32_t* delta, uint64_t* mask_out, uint32_t* flags,
                            hipStream_t s);
@@ -279,6 +286,29 @@ moe_status_t moe_prefetch_mask(const moe_dims_t* dims, int32_t T, const void* x,
   if (T == 0) return MOE_OK;
   return hip_status(launch_prefetch(*dims, T, x, w_prefetch, delta, mask_out, flags,
                                     (hipStream_t)stream));
+}
+
+moe_status_t moe_prefetch_adaptive(const moe_dims_t* dims, int32_t T, const void* x,
+                                   const void* w_prefetch, const void* w_delta,
+                                   const float* theta, float tau, const int32_t* topk_ids_opt,
+                                   int32_t* delta_out, uint64_t* mask_out, uint32_t* flags,
+                                   int32_t* delta_star_opt, int32_t* overlap_opt, void* stream) {
+  moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (T < 0 || !(tau > 0.f && tau < 1.f)) return MOE_EINVAL;
+  if (T > kMaxTokens) return MOE_EUNSUPPORTED;
+  if (!ok_ptr(x) || !ok_ptr(w_prefetch) || !ok_ptr(w_delta) || !ok_ptr(theta) ||
+      !ok_ptr(delta_out) || !ok_ptr(mask_out) || !ok_ptr(flags))
+    return MOE_EINVAL;
+  if (!ok_opt(topk_ids_opt) || !ok_opt(delta_star_opt) || !ok_opt(overlap_opt)) return MOE_EINVAL;
+  // the diagnostics need the router's choices, and come together
+  if ((delta_star_opt != nullptr) != (overlap_opt != nullptr)) return MOE_EINVAL;
+  if ((delta_star_opt != nullptr) != (topk_ids_opt != nullptr)) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  const float lt = (float)std::log((double)tau / (1.0 - (double)tau));
+  return hip_status(launch_prefetch_adaptive(*dims, T, x, w_prefetch, w_delta, theta, lt,
+                                             topk_ids_opt, delta_out, mask_out, flags,
+                                             delta_star_opt, overlap_opt, (hipStream_t)stream));
 }
 
 moe_status_t moe_permute(int32_t T, int32_t k, int32_t E, const int32_t* topk_ids,

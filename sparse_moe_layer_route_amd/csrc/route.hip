@@ -331,12 +331,21 @@ route_fused_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w_router, 
                         topk_w, exact, flags, mass_out, w_sg, g_s);
 }
 
-// APEX prefetch set: top-(k + delta_t) of x W_p^T as a bit mask.
-template <typename Tin>
+// APEX prefetch set: top-(k + delta_t) of x W_p^T as a bit mask.  ADAPT:
+// delta_t is the adaptive budget [APEX page, Sec. 4.2]: with s = w . x_t,
+// p_d = sigmoid(theta_d - s) >= tau  <=>  theta_d - s >= logit(tau) (lt), so
+// lane d tests its own budget and the least qualifying lane is the budget
+// (N - k when none qualifies).  Given the router's choices, the kernel also
+// reports delta* (the least budget covering them: the largest prefetch rank
+// among them, minus k - 1) and how many of them the list covers.
+template <typename Tin, bool ADAPT>
 __global__ void __launch_bounds__(1024)
 prefetch_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w_p, int T, int H, int E, int k,
                 float margin, const int32_t* __restrict__ delta, uint64_t* __restrict__ mask_out,
-                uint32_t* __restrict__ flags) {
+                uint32_t* __restrict__ flags, const Tin* __restrict__ w_delta,
+                const float* __restrict__ theta, float lt, const int32_t* __restrict__ routed,
+                int32_t* __restrict__ delta_out, int32_t* __restrict__ delta_star_out,
+                int32_t* __restrict__ overlap_out) {
   __shared__ RouteLds lds;
   const int t0 = blockIdx.x * ROUTE_TOK;
   tile_logits(x, w_p, T, H, E, t0, lds);
@@ -344,13 +353,41 @@ prefetch_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w_p, int T, i
   const int t = t0 + wv;
   if (t >= T) return;
   const float l = lane < E ? lds.logits[wv][lane] : -INFINITY;
-  int n = k + delta[t];
+  uint32_t flag = 0;
+  int n;
+  if constexpr (ADAPT) {
+    const float sc = wave_dot<Tin>(x + (int64_t)t * H, w_delta, H);
+    const int nd = E - k + 1;  // budgets 0..N-k
+    const float g = lane < nd ? theta[lane] - sc - lt : -INFINITY;
+    const uint64_t ok = __ballot(lane < nd && g >= 0.f);
+    const int d = ok ? __ffsll((unsigned long long)ok) - 1 : nd - 1;
+    if (__ballot((lane == d || lane == d - 1) && fabsf(g) < margin)) flag |= 16u;
+    if (lane == 0) delta_out[t] = d;
+    n = k + d;
+  } else {
+    n = k + delta[t];
+  }
   n = n < 1 ? 1 : (n > E ? E : n);
   const int rank = key_rank(lane < E ? topk_key(l, lane) : 0ull, E);
   const uint64_t mask = __ballot(lane < E && rank < n);
-  uint32_t flag = 0;
   if (n < E && lane_logit_at_rank(l, rank, n - 1, E) - lane_logit_at_rank(l, rank, n, E) < margin)
-    flag = 2u;
+    flag |= 2u;
+  if constexpr (ADAPT) {
+    if (routed) {
+      int top = -1, cover = 0;
+      for (int j = 0; j < k; ++j) {
+        const int e = __builtin_amdgcn_readfirstlane(routed[(int64_t)t * k + j]);
+        if (e < 0 || e >= E) continue;
+        const int re = __builtin_amdgcn_readlane(rank, e);
+        top = re > top ? re : top;
+        cover += re < n ? 1 : 0;
+      }
+      if (lane == 0) {
+        delta_star_out[t] = top + 1 - k > 0 ? top + 1 - k : 0;
+        overlap_out[t] = cover;
+      }
+    }
+  }
   if (lane == 0) {
     mask_out[t] = mask;
     flags[t] = flag;
@@ -415,13 +452,32 @@ hipError_t launch_prefetch(const moe_dims_t& d, int T, const void* x, const void
                            hipStream_t s) {
   const int blocks = (T + ROUTE_TOK - 1) / ROUTE_TOK;
   if (d.dtype == MOE_BF16)
-    prefetch_kernel<bf16><<<blocks, 1024, 0, s>>>((const bf16*)x, (const bf16*)w_p, T, d.hidden,
-                                                  d.n_experts, d.top_k, d.tie_margin, delta,
-                                                  mask_out, flags);
+    prefetch_kernel<bf16, false><<<blocks, 1024, 0, s>>>(
+        (const bf16*)x, (const bf16*)w_p, T, d.hidden, d.n_experts, d.top_k, d.tie_margin, delta,
+        mask_out, flags, nullptr, nullptr, 0.f, nullptr, nullptr, nullptr, nullptr);
   else
-    prefetch_kernel<float><<<blocks, 1024, 0, s>>>((const float*)x, (const float*)w_p, T, d.hidden,
-                                                   d.n_experts, d.top_k, d.tie_margin, delta,
-                                                   mask_out, flags);
+    prefetch_kernel<float, false><<<blocks, 1024, 0, s>>>(
+        (const float*)x, (const float*)w_p, T, d.hidden, d.n_experts, d.top_k, d.tie_margin, delta,
+        mask_out, flags, nullptr, nullptr, 0.f, nullptr, nullptr, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefetch_adaptive(const moe_dims_t& d, int T, const void* x, const void* w_p,
+                                    const void* w_delta, const float* theta, float logit_tau,
+                                    const int32_t* routed, int32_t* delta_out,
+                                    uint64_t* mask_out, uint32_t* flags, int32_t* delta_star,
+                                    int32_t* overlap, hipStream_t s) {
+  const int blocks = (T + ROUTE_TOK - 1) / ROUTE_TOK;
+  if (d.dtype == MOE_BF16)
+    prefetch_kernel<bf16, true><<<blocks, 1024, 0, s>>>(
+        (const bf16*)x, (const bf16*)w_p, T, d.hidden, d.n_experts, d.top_k, d.tie_margin,
+        nullptr, mask_out, flags, (const bf16*)w_delta, theta, logit_tau, routed, delta_out,
+        delta_star, overlap);
+  else
+    prefetch_kernel<float, true><<<blocks, 1024, 0, s>>>(
+        (const float*)x, (const float*)w_p, T, d.hidden, d.n_experts, d.top_k, d.tie_margin,
+        nullptr, mask_out, flags, (const float*)w_delta, theta, logit_tau, routed, delta_out,
+        delta_star, overlap);
   return hipGetLastError();
 }
 

@@ -81,6 +81,34 @@ def prefetch_masks_gpu(layer: W.Layer, T: int, wdev, delta=None):
     return masks, flags.cpu().numpy().view(np.uint32), mask
 
 
+def prefetch_adaptive_gpu(layer: W.Layer, T: int, wdev, tau: float, theta=None, routed=None):
+    """moe_prefetch_adaptive on the first T rows; returns (delta, masks,
+    flags, delta_star or None, overlap or None) as numpy / int lists."""
+    cfg = layer.cfg
+    dims = M.Dims(**dims_dict(cfg))
+    w_delta, th = layer.ordinal(tau)
+    th = th if theta is None else np.asarray(theta, np.float32)
+    # buffers hold at least one row, so T = 0 still passes valid pointers
+    x = tensor(layer.x(max(T, 1)), cfg.dtype, "cuda")
+    wd = tensor(w_delta, cfg.dtype, "cuda")
+    th_d = torch.from_numpy(np.ascontiguousarray(th, np.float32)).cuda()
+    delta = torch.full((max(T, 1),), -7, dtype=torch.int32, device="cuda")
+    mask = torch.empty(max(T, 1), dtype=torch.int64, device="cuda")
+    flags = torch.empty(max(T, 1), dtype=torch.int32, device="cuda")
+    ids = ds = ov = None
+    if routed is not None:
+        ids = torch.zeros(max(T, 1) * cfg.top_k, dtype=torch.int32, device="cuda")
+        ids[:T * cfg.top_k] = torch.from_numpy(np.ascontiguousarray(routed, np.int32).reshape(-1))
+        ds = torch.full((max(T, 1),), -7, dtype=torch.int32, device="cuda")
+        ov = torch.full((max(T, 1),), -7, dtype=torch.int32, device="cuda")
+    M.moe_prefetch_adaptive(dims, T, x, wdev["w_prefetch"], wd, th_d, tau, delta, mask, flags,
+                            topk_ids=ids, delta_star=ds, overlap=ov)
+    torch.cuda.synchronize()
+    masks = [int(v) for v in mask[:T].cpu().numpy().view(np.uint64)]
+    return (delta[:T].cpu().numpy(), masks, flags[:T].cpu().numpy().view(np.uint32),
+            None if ds is None else ds[:T].cpu().numpy(), None if ov is None else ov[:T].cpu().numpy())
+
+
 def run_layer(layer: W.Layer, T: int, mode: str, wdev=None, dims_over=None,
               resident_masks=None, x_np=None) -> GpuRun:
     """moe_layer_forward on the first T rows of the layer's x."""

@@ -129,6 +129,18 @@ def test_entry_point_null_checks():
     assert L.moe_permute(600, 2, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.MOE_EINVAL
     assert L.moe_permute(600, 2, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == B.MOE_EWORKSPACE
     assert L.moe_prefetch_mask(ctypes.byref(d), 4, FAKE, FAKE, None, FAKE, FAKE, None) == B.MOE_EINVAL
+    pa = L.moe_prefetch_adaptive
+    for tau in (0.0, 1.0, -0.5, float("nan")):   # tau must lie in (0, 1)
+        assert pa(ctypes.byref(d), 4, FAKE, FAKE, FAKE, FAKE, tau, None, FAKE, FAKE, FAKE, None, None,
+                  None) == B.MOE_EINVAL
+    assert pa(ctypes.byref(d), 4, FAKE, FAKE, None, FAKE, 0.9, None, FAKE, FAKE, FAKE, None, None,
+              None) == B.MOE_EINVAL                                   # w_delta required
+    assert pa(ctypes.byref(d), 4, FAKE, FAKE, FAKE, FAKE, 0.9, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+              None) == B.MOE_EINVAL                                   # diagnostics need topk_ids
+    assert pa(ctypes.byref(d), 4, FAKE, FAKE, FAKE, FAKE, 0.9, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+              None) == B.MOE_EINVAL                                   # both diagnostics or neither
+    assert pa(ctypes.byref(d), 0, FAKE, FAKE, FAKE, FAKE, 0.9, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+              None) == B.MOE_OK
     assert L.moe_lore_surrogate(ctypes.byref(dims(lore_rank=0)), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                 None) == B.MOE_EUNSUPPORTED
     assert L.moe_combine(ctypes.byref(d), 4, FAKE, FAKE, FAKE, FAKE, None, None, None, None,

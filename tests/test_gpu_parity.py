@@ -23,8 +23,9 @@ if not torch.cuda.is_available():  # the -m gpu suite runs on the GPU machine
     pytest.skip("no GPU", allow_module_level=True)
 
 import sparse_moe_layer_route_amd as M  # noqa: E402
-from gpu_harness import (TOL, check_decisions, check_floe_masks, dev_weights,  # noqa: E402
-                         oracle_forward_forced, prefetch_masks_gpu, rel_fro, run_layer, say)
+from gpu_harness import (MARGIN, TOL, check_decisions, check_floe_masks, dev_weights,  # noqa: E402
+                         oracle_forward_forced, prefetch_adaptive_gpu, prefetch_masks_gpu, rel_fro,
+                         run_layer, say)
 
 
 def _variant(base, **kw):
@@ -200,6 +201,99 @@ def test_prefetch_delta_extremes(delta):
         st = run_layer(layer, T, "standard")
         np.testing.assert_array_equal(sf.ids, st.ids)
         np.testing.assert_array_equal(sf.out, st.out)
+
+
+def _oracle_routed(layer, X, k):
+    """The router's top-k by the oracle (inputs of the overlap diagnostics)."""
+    lr = O.router_logits(X, O.decode(layer.w_router(), layer.cfg.dtype))
+    return np.array([O.rank_experts(lr[t])[:k] for t in range(X.shape[0])], dtype=np.int32)
+
+
+@pytest.mark.parametrize("name,T", [("granite_prefill", 4096), ("granite_small", 203),
+                                    ("granite_small", 37)])
+def test_prefetch_adaptive_parity(name, T):
+    """Adaptive budget, list, delta* and overlap against the oracle, every
+    token: exact where neither side flags a near-tie; at a budget near-tie
+    (flag 16) the budgets differ by at most one and the list is still the
+    top-(k + budget) of the prefetch logits."""
+    layer = W.make_layer(name) if name in W.CONFIGS else W.Layer(SMALL[name])
+    cfg, tau = layer.cfg, 0.9
+    k, E = cfg.top_k, cfg.n_experts
+    wdev = dev_weights(layer)
+    X = O.decode(layer.x(T), cfg.dtype)
+    Wp = O.decode(layer.w_prefetch(), cfg.dtype)
+    w_delta, theta = layer.ordinal(tau)
+    routed = _oracle_routed(layer, X, k)
+    od, om, of, ods, oov = O.adaptive_prefetch(X, Wp, O.decode(w_delta, cfg.dtype), theta, tau, k,
+                                               routed, MARGIN)
+    gd, gm, gf, gds, gov = prefetch_adaptive_gpu(layer, T, wdev, tau, routed=routed)
+    lp = O.router_logits(X, Wp)
+    # theta_d - w.x - logit(tau) per token and budget: the oracle's budget
+    # test on the logit scale (for the flag-threshold check below)
+    g = (theta.astype(np.float64)[None, :] - (X @ O.decode(w_delta, cfg.dtype))[:, None]
+         - np.log(tau / (1 - tau)))
+    n_budget_tie = n_list_tie = 0
+    for t in range(T):
+        srt = np.sort(lp[t])[::-1]
+        if (of[t] | gf[t]) & O.FLAG_BUDGET:
+            n_budget_tie += 1
+        if gd[t] != od[t]:  # a budget near-tie, raised on both sides
+            assert gf[t] & O.FLAG_BUDGET and of[t] & O.FLAG_BUDGET, t
+            assert abs(int(gd[t]) - int(od[t])) == 1, t
+        if (gf[t] ^ of[t]) & O.FLAG_BUDGET:  # the flag itself sits on its threshold
+            d = int(od[t])
+            gap = min(abs(g[t, j]) for j in (d - 1, d) if j >= 0)
+            assert abs(gap - MARGIN) < 1e-2 * MARGIN, t
+        n = k + int(gd[t])
+        assert bin(gm[t]).count("1") == n, t
+        sel = [e for e in range(E) if (gm[t] >> e) & 1]
+        rest = [e for e in range(E) if not (gm[t] >> e) & 1]
+        if gd[t] == od[t] and not (of[t] & O.FLAG_PREFETCH):
+            assert gm[t] == om[t], t
+            assert gov[t] == oov[t], t
+        else:
+            n_list_tie += 1
+            assert not rest or min(lp[t][sel]) >= max(lp[t][rest]) - MARGIN, t
+            assert gov[t] == O.prefetch_overlap(routed[t], gm[t]), t
+        if gds[t] != ods[t]:  # only where the deepest routed expert ties its neighbour
+            lo = k - 1 + min(int(gds[t]), int(ods[t]))
+            assert abs(int(gds[t]) - int(ods[t])) == 1 and srt[lo] - srt[lo + 1] < MARGIN, t
+        # flag bits other than 2 and 16 are never set
+        assert gf[t] & ~np.uint32(O.FLAG_PREFETCH | O.FLAG_BUDGET) == 0, t
+    say(f"    {name} T={T}: mean budget {gd.mean():.2f}, overlap {gov.mean() / k:.3f}, "
+        f"budget near-ties {n_budget_tie}, list near-ties {n_list_tie}")
+    assert 0 < gd.mean() < E - k  # the synthetic model spreads the budget
+
+
+@pytest.mark.parametrize("fill,expect", [(-1e4, "all"), (1e4, "zero")])
+def test_prefetch_adaptive_extremes(fill, expect):
+    """theta far below logit(tau) everywhere: no budget qualifies, so the
+    budget is N - k and every expert is listed (every routed one covered);
+    far above: budget 0, the list is the prefetch router's own top-k."""
+    layer = W.Layer(SMALL["granite_small"])
+    cfg = layer.cfg
+    k, E, T = cfg.top_k, cfg.n_experts, 203
+    X = O.decode(layer.x(T), cfg.dtype)
+    routed = _oracle_routed(layer, X, k)
+    theta = np.full(E - k + 1, fill, np.float32)
+    gd, gm, gf, gds, gov = prefetch_adaptive_gpu(layer, T, dev_weights(layer), 0.9, theta=theta,
+                                                 routed=routed)
+    assert (gf & O.FLAG_BUDGET).sum() == 0
+    if expect == "all":
+        assert (gd == E - k).all() and all(m == (1 << E) - 1 for m in gm) and (gov == k).all()
+    else:
+        lp = O.router_logits(X, O.decode(layer.w_prefetch(), cfg.dtype))
+        om, of, _ = O.prefetch_masks(X, O.decode(layer.w_prefetch(), cfg.dtype),
+                                     np.zeros(T, np.int32), k)
+        assert (gd == 0).all()
+        for t in range(T):
+            assert gm[t] == om[t] or of[t], t
+        assert (gov <= k).all() and (gds >= 0).all()
+        # covered exactly when delta* is 0
+        assert ((gov == k) == (gds == 0)).all()
+    # T = 0 enqueues nothing and succeeds
+    out = prefetch_adaptive_gpu(layer, 0, dev_weights(layer), 0.9, routed=routed[:0])
+    assert len(out[0]) == 0 and len(out[1]) == 0
 
 
 def test_permute_parity_random():

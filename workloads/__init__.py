@@ -23,8 +23,10 @@ Shapes follow the five MoE-layer workloads the pages study:
                          of 64 with fp16 scale and zero, keep 10% of channels.
 * ``granite_prefill`` -- Granite-3B-A800M shape (APEX page, Sec. 1: 40 experts,
                          top-8): H=1536, I=512, 4096 tokens, separate linear
-                         prefetch router, per-token extra budget delta drawn
-                         from Geometric(0.4) on {0,1,...} capped at N-k.
+                         prefetch router correlated 0.97 with the router,
+                         per-token extra budget delta drawn from
+                         Geometric(0.4) on {0,1,...} capped at N-k, and an
+                         ordinal budget model (w_delta, theta).
 
 Layouts (all row-major, C order):
 
@@ -88,6 +90,7 @@ class MoEConfig:
     resident_count: Optional[int] = None
     prefetch: bool = False          # draws w_prefetch and delta
     delta_p: float = 0.4
+    prefetch_rho: float = 0.97      # correlation of the prefetch router with the router
     weight_std: float = 0.02
     hidden_std: float = 1.0
     lore_std: float = 0.01
@@ -249,7 +252,22 @@ class Layer:
         return self._small("w_router", (self.cfg.n_experts, self.cfg.hidden), self.cfg.weight_std)
 
     def w_prefetch(self) -> np.ndarray:
-        return self._small("w_prefetch", (self.cfg.n_experts, self.cfg.hidden), self.cfg.weight_std)
+        """A prefetch router distilled toward the router (APEX page, Sec. 4.1:
+        trained to match the router's distribution; no trained weights exist
+        here): rho * W_r + sqrt(1 - rho^2) * fresh noise of the same spread,
+        drawn in fp32 before rounding to the storage dtype.  rho = 0.97 gives
+        Granite-shaped inputs a long-tailed delta* (median 2, 98th
+        percentile about 9)."""
+        key = ("w_prefetch", 0)
+        if key not in self._cache:
+            c = self.cfg
+            shape = (c.n_experts, c.hidden)
+            wr = _normal(_rng(self.seed, "w_router"), shape, c.weight_std)
+            nz = _normal(_rng(self.seed, "w_prefetch"), shape, c.weight_std)
+            rho = np.float32(c.prefetch_rho)
+            w = (rho * wr + np.float32(np.sqrt(1.0 - c.prefetch_rho ** 2)) * nz).astype(np.float32)
+            self._cache[key] = self._to_storage(w)
+        return self._cache[key]
 
     def w_shared_gate(self) -> np.ndarray:
         return self._small("w_shared_gate", (self.cfg.hidden,), self.cfg.weight_std)
