@@ -22,6 +22,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import dataclasses
 import json
 import math
 import os
@@ -173,8 +174,13 @@ def measure(name, T, mode, steps, warmup, ev=None, want_roofline=False):
 
     layer = W.make_layer(name)
     cfg = layer.cfg
-    dims = M.Dims(**dims_dict(cfg)).c()
     w0 = upload(layer, "cuda")
+    dd = M.Dims(**dims_dict(cfg))
+    if cfg.dtype == "bf16" and cfg.up_format == "dense":
+        # expert matrices packed fragment-major once, as a deployment would
+        dd = dataclasses.replace(dd, weight_layout="mfma16")
+        w0 = M.pack_weights(dd, w0)
+    dims = dd.c()
     x = tensor(layer.x(T), cfg.dtype, "cuda")
     stride = 0
     res = None

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 #define MOE_MAX_EXPERTS 64
 #define MOE_MAX_TOPK 8
 #define MOE_MAX_LORE_RANK 64
@@ -70,6 +70,20 @@ typedef enum {
 
 typedef enum { MOE_UP_DENSE = 0, MOE_UP_INT2_G64 = 1 } moe_up_format_t;
 
+/* Storage of the routed and shared expert matrices (w_gate, w_up, w_down,
+ * ws_gate, ws_up, ws_down).  The router, prefetch router, shared gate, LoRE
+ * factors and FloE tensors are row-major in either case.
+ *   MOE_LAYOUT_ROWS:   row-major, the shapes listed in moe_weights_t.
+ *   MOE_LAYOUT_MFMA16: every [R][K] matrix (k contiguous in the row-major
+ *     form) packed fragment-major by moe_pack_weights: [ceil(R/16)]
+ *     [ceil(K/32)][64][8], fragment (t, s) = rows 16t..+15 by k 32s..+31 as the
+ *     16x16x32 matrix-core operand (lane l: row 16t + l%16, k from
+ *     32s + 8*(l/16), eight values), zero past R or K.  Each expert's (or
+ *     shared expert's) matrix is moe_pack_size(1, R, K) bytes, consecutive.
+ *     bf16 and MOE_UP_DENSE only.  The kernels then read every weight
+ *     fragment as one contiguous 1 KiB access. */
+typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_MFMA16 = 1 } moe_weight_layout_t;
+
 /* Layer shape (host struct). */
 typedef struct {
   int32_t hidden;        /* H                                                     */
@@ -85,6 +99,7 @@ typedef struct {
   moe_dtype_t dtype;
   moe_up_format_t up_format;
   float tie_margin;      /* near-tie threshold for the flags (1e-4)               */
+  moe_weight_layout_t weight_layout; /* storage of the expert matrices          */
 } moe_dims_t;
 
 /* Layer weights (host struct of device pointers; unused entries may be NULL). */
@@ -145,6 +160,18 @@ const char* moe_status_string(moe_status_t status);
  * moe_permute need for T tokens in `mode` (host output). */
 moe_status_t moe_workspace_size(const moe_dims_t* dims, int32_t T, moe_mode_t mode,
                                 size_t* bytes /* host */);
+
+/* Bytes of `groups` consecutive [rows][cols] matrices in MOE_LAYOUT_MFMA16
+ * (host output): groups * ceil(rows/16)*16 * ceil(cols/32)*32 * 2.
+ * MOE_EINVAL for a non-positive size or cols % 8 != 0. */
+moe_status_t moe_pack_size(int32_t groups, int32_t rows, int32_t cols, size_t* bytes /* host */);
+
+/* Packs `groups` consecutive row-major bf16 matrices src [groups][rows][cols]
+ * into dst (moe_pack_size bytes) in MOE_LAYOUT_MFMA16, padding with zeros.
+ * src and dst must not overlap.  Done once per set of weights: e.g.
+ * w_gate with (E, I, H), w_down with (E, H, I), ws_down with (n_s, H, I_s). */
+moe_status_t moe_pack_weights(int32_t groups, int32_t rows, int32_t cols, const void* src,
+                              void* dst, void* stream);
 
 /* Router: logits l = x W_r, softmax p, top-k by (-l, id) [APEX page, Sec. 1;
  * SPICE page, "MoE inference I/O bottleneck"].

@@ -21,6 +21,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 MODES = {"standard": 0, "lore": 1, "stall_free": 2, "floe": 3}
 MOE_UP_DENSE, MOE_UP_INT2_G64 = 0, 1
+LAYOUTS = {"rows": 0, "mfma16": 1}
 
 
 class MoEError(RuntimeError):
@@ -36,7 +37,7 @@ class MoeDims(ctypes.Structure):
                 ("lore_rank", ctypes.c_int32), ("renormalize", ctypes.c_int32),
                 ("shared_gate", ctypes.c_int32), ("floe_keep", ctypes.c_int32),
                 ("dtype", ctypes.c_int), ("up_format", ctypes.c_int),
-                ("tie_margin", ctypes.c_float)]
+                ("tie_margin", ctypes.c_float), ("weight_layout", ctypes.c_int)]
 
 
 _WEIGHT_FIELDS = ["w_router", "w_gate", "w_up", "w_down", "up_q", "up_scale", "up_zero",
@@ -73,6 +74,8 @@ def _load():
         "moe_workspace_size": ([D, I32, ctypes.c_int, ctypes.POINTER(SZ)], ctypes.c_int),
         "moe_route": ([D, I32, P, P, P, I64, ctypes.c_int, P, P, P, P, P, P, P], ctypes.c_int),
         "moe_prefetch_mask": ([D, I32, P, P, P, P, P, P], ctypes.c_int),
+        "moe_pack_size": ([I32, I32, I32, ctypes.POINTER(SZ)], ctypes.c_int),
+        "moe_pack_weights": ([I32, I32, I32, P, P, P], ctypes.c_int),
         "moe_prefetch_adaptive": ([D, I32, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, P],
                                   ctypes.c_int),
         "moe_permute": ([I32, I32, I32, P, P, P, P, P, P, SZ, P], ctypes.c_int),
@@ -90,7 +93,8 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_route",
-            "moe_prefetch_mask", "moe_prefetch_adaptive", "moe_permute", "moe_expert_ffn", "moe_lore_surrogate",
+            "moe_prefetch_mask", "moe_prefetch_adaptive", "moe_pack_size", "moe_pack_weights",
+            "moe_permute", "moe_expert_ffn", "moe_lore_surrogate",
             "moe_combine", "moe_layer_forward")
 
 
@@ -110,6 +114,7 @@ class Dims:
     dtype: str = "bf16"
     up_format: str = "dense"
     tie_margin: float = 1e-4
+    weight_layout: str = "rows"      # "rows" or "mfma16" (see pack_weights)
 
     def c(self) -> MoeDims:
         return MoeDims(self.hidden, self.n_experts, self.top_k, self.inter, self.n_shared,
@@ -117,7 +122,7 @@ class Dims:
                        int(self.shared_gate), self.floe_keep,
                        MOE_BF16 if self.dtype == "bf16" else MOE_F32,
                        MOE_UP_INT2_G64 if self.up_format == "int2_g64" else MOE_UP_DENSE,
-                       self.tie_margin)
+                       self.tie_margin, LAYOUTS[self.weight_layout])
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -185,6 +190,41 @@ def moe_prefetch_adaptive(dims, T, x, w_prefetch, w_delta, theta, tau, delta_out
                                       _ptr(delta_out), _ptr(mask_out), _ptr(flags),
                                       _ptr(delta_star), _ptr(overlap), _stream(stream)),
            "moe_prefetch_adaptive")
+
+
+def moe_pack_size(groups, rows, cols) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.moe_pack_size(groups, rows, cols, ctypes.byref(n)), "moe_pack_size")
+    return n.value
+
+
+def moe_pack_weights(groups, rows, cols, src, dst, stream=None):
+    _check(_lib.moe_pack_weights(groups, rows, cols, _ptr(src), _ptr(dst), _stream(stream)),
+           "moe_pack_weights")
+
+
+# (groups, rows, cols) of each expert matrix that MOE_LAYOUT_MFMA16 packs
+def _packed_shapes(d: "Dims"):
+    E, H, I, ns, Is = d.n_experts, d.hidden, d.inter, d.n_shared, d.shared_inter
+    shapes = {"w_gate": (E, I, H), "w_up": (E, I, H), "w_down": (E, H, I)}
+    if ns > 0:
+        shapes.update(ws_gate=(ns, Is, H), ws_up=(ns, Is, H), ws_down=(ns, H, Is))
+    return shapes
+
+
+def pack_weights(dims: "Dims", w: Dict[str, torch.Tensor], stream=None) -> Dict[str, torch.Tensor]:
+    """A copy of the weight dict with the routed and shared expert matrices
+    packed fragment-major (moe_pack_weights); use it with
+    dataclasses.replace(dims, weight_layout="mfma16")."""
+    out = dict(w)
+    for name, (g, r, c) in _packed_shapes(dims).items():
+        src = w[name]
+        if src.numel() != g * r * c:
+            raise ValueError(f"{name}: expected {g}x{r}x{c} elements, got {src.numel()}")
+        dst = torch.empty(moe_pack_size(g, r, c) // 2, dtype=src.dtype, device=src.device)
+        moe_pack_weights(g, r, c, src, dst, stream)
+        out[name] = dst
+    return out
 
 
 def moe_permute(T, k, E, topk_ids, exact, expert_offsets, perm, inv, ws=None, stream=None):

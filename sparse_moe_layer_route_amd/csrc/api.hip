@@ -12,6 +12,8 @@ hipError_t launch_route(const moe_dims_t& d, int T, const void* x, const void* w
                         const uint64_t* resident, int64_t res_stride, int mode, int32_t* ids,
                         float* w, uint8_t* exact, uint32_t* flags, float* logits, float* mass,
                         const void* w_sg, float* g_s, hipStream_t s);
+hipError_t launch_pack_mfma16(int G, int R, int K, const void* src, void* dst, hipStream_t s);
+int64_t packed_elems(int R, int K);
 hipError_t launch_prefetch_adaptive(const moe_dims_t& d, int T, const void* x, const void* w_p,
                                     const void* w_delta, const float* theta, float logit_tau,
                                     const int32_t* routed, int32_t* delta_out,
@@ -80,6 +82,11 @@ moe_status_t check_dims(const moe_dims_t* d) {
   if (d->hidden % 64 != 0 || d->inter % 16 != 0) return MOE_EUNSUPPORTED;
   if (d->n_shared > 0 && (d->shared_inter <= 0 || d->shared_inter % 16 != 0)) return MOE_EUNSUPPORTED;
   if (d->lore_rank > MOE_MAX_LORE_RANK || d->lore_rank % 8 != 0) return MOE_EUNSUPPORTED;
+  if (d->weight_layout != MOE_LAYOUT_ROWS && d->weight_layout != MOE_LAYOUT_MFMA16)
+    return MOE_EINVAL;
+  if (d->weight_layout == MOE_LAYOUT_MFMA16 &&
+      (d->dtype != MOE_BF16 || d->up_format != MOE_UP_DENSE))
+    return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
@@ -286,6 +293,23 @@ moe_status_t moe_prefetch_mask(const moe_dims_t* dims, int32_t T, const void* x,
   if (T == 0) return MOE_OK;
   return hip_status(launch_prefetch(*dims, T, x, w_prefetch, delta, mask_out, flags,
                                     (hipStream_t)stream));
+}
+
+moe_status_t moe_pack_size(int32_t groups, int32_t rows, int32_t cols, size_t* bytes) {
+  if (!bytes || groups <= 0 || rows <= 0 || cols <= 0 || cols % 8 != 0) return MOE_EINVAL;
+  *bytes = (size_t)groups * (size_t)packed_elems(rows, cols) * 2;
+  return MOE_OK;
+}
+
+moe_status_t moe_pack_weights(int32_t groups, int32_t rows, int32_t cols, const void* src,
+                              void* dst, void* stream) {
+  if (groups <= 0 || rows <= 0 || cols <= 0 || cols % 8 != 0) return MOE_EINVAL;
+  if (!ok_ptr(src) || !ok_ptr(dst)) return MOE_EINVAL;
+  const size_t sb = (size_t)groups * rows * cols * 2;
+  const size_t db = (size_t)groups * (size_t)packed_elems(rows, cols) * 2;
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  if (s0 < d0 + db && d0 < s0 + sb) return MOE_EINVAL;  // overlap
+  return hip_status(launch_pack_mfma16(groups, rows, cols, src, dst, (hipStream_t)stream));
 }
 
 moe_status_t moe_prefetch_adaptive(const moe_dims_t* dims, int32_t T, const void* x,

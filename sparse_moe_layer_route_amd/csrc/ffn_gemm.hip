@@ -73,6 +73,7 @@ struct GemmArgs {
   int ksplit;           // GEMM2: k-stage ranges (grid.y); partial sums to y_out + y * part_stride
   int64_t part_stride;
   int n_blocks;         // grid size (upper bound of tiles)
+  int packed;           // weights fragment-major [R/16][K/32][64][8] (R % 16 == K % 32 == 0 here)
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -270,6 +271,7 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   // banks.
   const int chunk = (lane & 3) ^ ((lane >> 3) & 3);
   const bool is_w = wv < GWAVES / 2;
+  const int wsh = a.packed ? 4 : 0;
   constexpr int NQ = GROWS / 16 / GWAVES;   // DMA instructions per wave per stage
   constexpr int NMF = NW * WT * GTT;        // MFMAs per wave per stage
   // row of this lane's DMA instruction q within the token or weight half
@@ -287,7 +289,11 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         const int r = GATED ? (dma_row(q) & 127) : dma_row(q);
-        off[q] = min(m.n_idx * MW + r, a.R - 1) * a.K + 8 * chunk;
+        const int row = min(m.n_idx * MW + r, a.R - 1);
+        // fragment-major: the 16 rows of one DMA instruction are one
+        // contiguous 1 KiB fragment, row r%16 chunk c at lane slot 16c + r%16
+        off[q] = a.packed ? (row >> 4) * (a.K >> 5) * 512 + (16 * chunk + (row & 15)) * 8
+                          : row * a.K + 8 * chunk;
       }
     } else {
       dbase = GATED ? a.x : a.act_in;
@@ -316,7 +322,9 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   auto issue_one = [&](int s, int kstage, int q) __attribute__((always_inline)) {
     bf16* dst = &lds[s % GSTAGES][(16 * NQ * wv) * GK];
     const int s_ = kstage / kst, ko = (kstage % kst) * GK;
-    const bf16* src = dbase + (is_w ? (int64_t)s_ * a.sub_stride : (int64_t)s_ * a.sub_k_off) + ko;
+    // weight k stage stride: 32 elements row-major, a 512-element fragment packed
+    const bf16* src = dbase + (is_w ? (int64_t)s_ * a.sub_stride + (ko << wsh)
+                                    : (int64_t)s_ * a.sub_k_off + ko);
     __builtin_amdgcn_global_load_lds((const void*)(src + off[q]),
                                      (__attribute__((address_space(3))) void*)(dst + q * 16 * GK),
                                      16, 0, 0);
@@ -534,6 +542,7 @@ hipError_t launch_ffn_gemm(const moe_dims_t& d, int T, const void* x, const moe_
     a.tiles_n = (R1 + 127) / 128;            // 128 gate + 128 up rows per block
     a.n_blocks = mt_max * a.tiles_n;
     a.ksplit = 1;
+    a.packed = d.weight_layout == MOE_LAYOUT_MFMA16;
     const int grid = gemm_grid(a.n_blocks, 1);
     if (a.n_blocks > 0) ffn_gemm_kernel<true><<<grid, GTHREADS, 0, s>>>(a);
   }
@@ -557,6 +566,7 @@ hipError_t launch_ffn_gemm(const moe_dims_t& d, int T, const void* x, const moe_
     a.tiles_n = (H + 255) / 256;             // 256 down rows per block
     const int mt2 = shared ? (T + GN - 1) / GN : mt_max;
     a.n_blocks = mt2 * a.tiles_n;
+    a.packed = d.weight_layout == MOE_LAYOUT_MFMA16;
     a.ksplit = shared ? gemm_shared_down_ksplit(d, T) : 1;
     a.y_out = a.ksplit > 1 ? part : y;
     a.yb_out = a.ksplit > 1 ? nullptr : yb;

@@ -71,6 +71,7 @@ struct FfnMfmaArgs {
   const int32_t* moffsets;  // LoRE segments [E+1] (positions after the exact ones)
   const int32_t* perm;
   int H, I, Is, ns, r, E, k, T;
+  int packed;             // routed and shared matrices fragment-major (LoRE row-major)
   int slots_r, tiles_r;       // routed slots x row tiles
   int n_shared_seg, tiles_s;  // shared segments (up: ns, down: 1) x row tiles
   int slots_l, tiles_l;       // LoRE slots x row tiles
@@ -187,6 +188,9 @@ __device__ __forceinline__ void up_chunk(const FfnMfmaArgs a, const TileInfo& ti
   const int lane = lane_id(), wv = threadIdx.x >> 6, wk = wv / WM, wm = wv % WM;
   const int r16 = lane & 15, kg = lane >> 4;
   const int H = a.H, ksteps = H >> 5;
+  // k-step stride of the weight pointers: 32 elements row-major, one 1 KiB
+  // fragment (512 elements) fragment-major
+  const int wsh = (a.packed && ti.kind != 2) ? 4 : 0;
   const bf16* xrow[NA];
 #pragma unroll
   for (int j = 0; j < NA; ++j) {
@@ -207,8 +211,8 @@ __device__ __forceinline__ void up_chunk(const FfnMfmaArgs a, const TileInfo& ti
   _Pragma("unroll") for (int u = 0; u < U; ++u) {                              \
     const int ko = min(kr.beg + (b) * U + u, kr.end - 1) << 5;                 \
     _Pragma("unroll") for (int q = 0; q < RW; ++q) {                           \
-      G[u][q] = frag_load(ag_row[q] + ko);                                     \
-      UU[u][q] = frag_load(au_row[q] + ko);                                    \
+      G[u][q] = frag_load(ag_row[q] + (ko << wsh));                            \
+      UU[u][q] = frag_load(au_row[q] + (ko << wsh));                           \
     }                                                                          \
     _Pragma("unroll") for (int j = 0; j < NA; ++j) X[u][j] = frag_load(xrow[j] + ko); \
   }
@@ -349,9 +353,15 @@ __global__ void __launch_bounds__(256) FFN_UP_OCCUPANCY ffn_up_mfma_kernel(FfnMf
   const bf16* au[RW];
 #pragma unroll
   for (int q = 0; q < RW; ++q) {
-    const int wrow_i = min(row_base + 16 * q + r16, R - 1);
-    ag[q] = wg + (int64_t)wrow_i * H + 8 * kg;
-    au[q] = wu + (int64_t)wrow_i * H + 8 * kg;
+    if (a.packed) {  // fragment (row tile, k step 0); R % 16 == 0, tiles past R reread the last
+      const int64_t f = (int64_t)min((row_base >> 4) + q, (R >> 4) - 1) * (H >> 5) * 512 + lane * 8;
+      ag[q] = wg + f;
+      au[q] = wu + f;
+    } else {
+      const int wrow_i = min(row_base + 16 * q + r16, R - 1);
+      ag[q] = wg + (int64_t)wrow_i * H + 8 * kg;
+      au[q] = wu + (int64_t)wrow_i * H + 8 * kg;
+    }
   }
   for (int c0 = 0; c0 < ti.n; c0 += 16 * NTT)
     up_dispatch<NTT, WM, WK, RW>(a, ti, c0, ag, au, gated, rows_ok, row_base, R, red);
@@ -377,6 +387,7 @@ __device__ __forceinline__ void down_chunk(const FfnMfmaArgs a, const TileInfo& 
   const int64_t ld = ti.kind == 0 ? a.I : (ti.kind == 1 ? (int64_t)a.ns * a.Is : a.r);
   const bf16* bsrc = ti.kind == 0 ? a.act : (ti.kind == 1 ? a.acts : a.z);
   const int kfull = K >> 5;  // full 32-wide steps; K % 8 == 0 may leave a partial one
+  const int wsh = (a.packed && ti.kind != 2) ? 4 : 0;  // weight k-step stride, as in up_chunk
   int64_t brow[NA];
 #pragma unroll
   for (int j = 0; j < NA; ++j) {
@@ -395,12 +406,18 @@ __device__ __forceinline__ void down_chunk(const FfnMfmaArgs a, const TileInfo& 
 #pragma unroll
       for (int q = 0; q < RW; ++q) {
         const int h = min(row_base + 16 * q + r16, H - 1);
-        if (ti.kind == 0)
+        if (wsh) {  // fragment-major [H/16][ceil(K/32)][64][8] per matrix
+          const int ks = (K + 31) >> 5;
+          const int64_t f = (int64_t)min((row_base >> 4) + q, (H >> 4) - 1) * ks * 512 + lane * 8;
+          wrow[q] = (ti.kind == 0 ? a.w0 + (int64_t)ti.e * H * (ks << 5)
+                                  : a.ws0 + (int64_t)s * H * (ks << 5)) + f;
+        } else if (ti.kind == 0) {
           wrow[q] = a.w0 + ((int64_t)ti.e * H + h) * a.I + 8 * kg;
-        else if (ti.kind == 1)
+        } else if (ti.kind == 1) {
           wrow[q] = a.ws0 + ((int64_t)s * H + h) * a.Is + 8 * kg;
-        else
+        } else {
           wrow[q] = a.wl + ((int64_t)ti.e * H + h) * a.r + 8 * kg;
+        }
       }
       const int64_t so = ti.kind == 1 ? (int64_t)s * a.Is : 0;
       const KRange kr = k_range<U>(kfull, wk, nwk);
@@ -409,7 +426,7 @@ __device__ __forceinline__ void down_chunk(const FfnMfmaArgs a, const TileInfo& 
 #define DN_LOAD(W, B, b)                                                       \
   _Pragma("unroll") for (int u = 0; u < U; ++u) {                              \
     const int ko = min(kr.beg + (b) * U + u, kr.end - 1) << 5;                 \
-    _Pragma("unroll") for (int q = 0; q < RW; ++q) W[u][q] = frag_load(wrow[q] + ko); \
+    _Pragma("unroll") for (int q = 0; q < RW; ++q) W[u][q] = frag_load(wrow[q] + (ko << wsh)); \
     _Pragma("unroll") for (int j = 0; j < NA; ++j) B[u][j] = frag_load(bsrc + brow[j] + so + ko); \
   }
 #define DN_MFMA(W, B, b)                                                       \
@@ -440,7 +457,7 @@ __device__ __forceinline__ void down_chunk(const FfnMfmaArgs a, const TileInfo& 
           const bf16x8_t bv = live ? frag_load(bsrc + brow[j] + so + ko) : frag_zero();
 #pragma unroll
           for (int q = 0; q < RW; ++q)
-            acc[j][q] = mfma16(live ? frag_load(wrow[q] + ko) : frag_zero(), bv, acc[j][q]);
+            acc[j][q] = mfma16(live ? frag_load(wrow[q] + (ko << wsh)) : frag_zero(), bv, acc[j][q]);
         }
       }
     }
@@ -605,6 +622,7 @@ hipError_t launch_ffn_mfma(const moe_dims_t& d, int T, const void* x, const moe_
   up.E = d.n_experts;
   up.k = d.top_k;
   up.T = T;
+  up.packed = d.weight_layout == MOE_LAYOUT_MFMA16;
   up.slots_r = routed ? slots : 0;
   up.tiles_r = (d.inter + rows - 1) / rows;
   up.n_shared_seg = shared ? d.n_shared : 0;

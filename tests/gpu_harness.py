@@ -36,10 +36,31 @@ def say(*a):
 def dev_weights(layer: W.Layer):
     key = (layer.cfg, layer.seed)
     if key not in _dev_cache:
-        _dev_cache.clear()
+        _dev_cache.clear()  # one layer's weights (and their packed copy) at a time
         torch.cuda.empty_cache()
         _dev_cache[key] = upload(layer, "cuda")
     return _dev_cache[key]
+
+
+def default_layout(cfg) -> str:
+    """The layout the bench runs: fragment-major expert matrices wherever the
+    matrix-core kernels run (bf16, dense up), row-major elsewhere."""
+    return "mfma16" if cfg.dtype == "bf16" and cfg.up_format == "dense" else "rows"
+
+
+def packed_weights(layer: W.Layer, wdev=None):
+    """The device weights with the expert matrices packed by moe_pack_weights
+    (cached beside dev_weights when wdev is the layer's own)."""
+    own = wdev is None
+    wdev = dev_weights(layer) if own else wdev
+    key = ("packed", layer.cfg, layer.seed)
+    if own and key in _dev_cache:
+        return _dev_cache[key]
+    packed = M.pack_weights(M.Dims(**dims_dict(layer.cfg)), wdev)
+    torch.cuda.synchronize()
+    if own:
+        _dev_cache[key] = packed
+    return packed
 
 
 def rel_fro(a, b) -> float:
@@ -110,12 +131,15 @@ def prefetch_adaptive_gpu(layer: W.Layer, T: int, wdev, tau: float, theta=None, 
 
 
 def run_layer(layer: W.Layer, T: int, mode: str, wdev=None, dims_over=None,
-              resident_masks=None, x_np=None) -> GpuRun:
-    """moe_layer_forward on the first T rows of the layer's x."""
+              resident_masks=None, x_np=None, layout="rows") -> GpuRun:
+    """moe_layer_forward on the first T rows of the layer's x; layout
+    "mfma16" packs the expert matrices (of wdev, or the layer's own) first."""
     cfg = layer.cfg
     dd = dims_dict(cfg, **(dims_over or {}))
-    dims = M.Dims(**dd)
+    dims = M.Dims(**dd, weight_layout=layout)
     wdev = wdev if wdev is not None else dev_weights(layer)
+    if layout == "mfma16":
+        wdev = packed_weights(layer, None if wdev is _dev_cache.get((cfg, layer.seed)) else wdev)
     x_np = layer.x(T) if x_np is None else x_np
     x = tensor(x_np, cfg.dtype, "cuda")
     k, E, H = dd["top_k"], dd["n_experts"], dd["hidden"]

@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert M.moe_abi_version() == 1
+    assert M.moe_abi_version() == 2
     for s in range(5):
         assert L.moe_status_string(s)
     assert L.moe_status_string(99) == b"unknown status"
@@ -55,6 +55,9 @@ def ws_size(d, T, mode):
     (dict(lore_rank=128), B.MOE_EUNSUPPORTED), (dict(hidden=0), B.MOE_EINVAL),
     (dict(top_k=0), B.MOE_EINVAL), (dict(shared_inter=100), B.MOE_EUNSUPPORTED),
     (dict(tie_margin=-1.0), B.MOE_EINVAL), ({}, B.MOE_OK),
+    (dict(weight_layout="mfma16"), B.MOE_EUNSUPPORTED),                  # fp32
+    (dict(weight_layout="mfma16", dtype="bf16"), B.MOE_OK),
+    (dict(weight_layout="mfma16", dtype="bf16", up_format="int2_g64"), B.MOE_EUNSUPPORTED),
 ])
 def test_dims_validation(kw, status):
     assert ws_size(dims(**kw), 16, 0)[0] == status
@@ -109,6 +112,26 @@ def test_layer_forward_host_checks():
     assert fwd(dg, 16, _weights(w_shared_gate=None), FAKE, 0, 0, FAKE, FAKE, need) == B.MOE_EINVAL
     # T = 0 with valid arguments enqueues nothing and succeeds (no GPU touched)
     assert fwd(d, 0, w, FAKE, 0, 1, FAKE, FAKE, need) == B.MOE_OK
+
+
+def test_layout_field_out_of_range():
+    d = dims(dtype="bf16")
+    d.weight_layout = 7
+    assert ws_size(d, 16, 0)[0] == B.MOE_EINVAL
+
+
+def test_pack_size_and_checks():
+    # rows padded to 16, cols to 32, 2 bytes each
+    assert M.moe_pack_size(1, 40, 72) == 48 * 96 * 2
+    assert M.moe_pack_size(3, 64, 2048) == 3 * 64 * 2048 * 2
+    n = ctypes.c_size_t(0)
+    for g, r, c in [(0, 16, 32), (1, 0, 32), (1, 16, 12), (1, 16, -8)]:
+        assert L.moe_pack_size(g, r, c, ctypes.byref(n)) == B.MOE_EINVAL
+    assert L.moe_pack_size(1, 16, 32, None) == B.MOE_EINVAL
+    assert L.moe_pack_weights(1, 16, 32, None, FAKE, None) == B.MOE_EINVAL
+    assert L.moe_pack_weights(1, 16, 32, FAKE, FAKE + 8, None) == B.MOE_EINVAL   # misaligned
+    assert L.moe_pack_weights(1, 16, 32, FAKE, FAKE + 512, None) == B.MOE_EINVAL  # overlap
+    assert L.moe_pack_weights(1, 16, 12, FAKE, FAKE + 4096, None) == B.MOE_EINVAL  # cols % 8
 
 
 def test_entry_point_null_checks():

@@ -23,8 +23,8 @@ if not torch.cuda.is_available():  # the -m gpu suite runs on the GPU machine
     pytest.skip("no GPU", allow_module_level=True)
 
 import sparse_moe_layer_route_amd as M  # noqa: E402
-from gpu_harness import (MARGIN, TOL, check_decisions, check_floe_masks, dev_weights,  # noqa: E402
-                         oracle_forward_forced, prefetch_adaptive_gpu, prefetch_masks_gpu, rel_fro,
+from gpu_harness import (MARGIN, TOL, check_decisions, check_floe_masks, default_layout,  # noqa: E402
+                         dev_weights, oracle_forward_forced, packed_weights, prefetch_adaptive_gpu, prefetch_masks_gpu, rel_fro,
                          run_layer, say)
 
 
@@ -68,9 +68,10 @@ FLOE_SMALL = {
 }
 
 
-def _check_full(layer, T, mode, sample=None, dims_over=None):
-    say(f"[parity] {layer.cfg.name} T={T} mode={mode}")
-    g = run_layer(layer, T, mode, dims_over=dims_over)
+def _check_full(layer, T, mode, sample=None, dims_over=None, layout=None):
+    layout = default_layout(layer.cfg) if layout is None else layout
+    say(f"[parity] {layer.cfg.name} T={T} mode={mode} layout={layout}")
+    g = run_layer(layer, T, mode, dims_over=dims_over, layout=layout)
     counts = check_decisions(layer, T, mode, g, dims_over=dims_over)
     sample = list(range(T)) if sample is None else sample
     ref = oracle_forward_forced(layer, T, mode, g, sample, dims_over=dims_over)
@@ -97,6 +98,8 @@ def _check_full(layer, T, mode, sample=None, dims_over=None):
 def test_small_layer_parity(name, mode):
     layer = W.Layer(SMALL[name])
     _check_full(layer, layer.cfg.t_max, mode)
+    if default_layout(layer.cfg) != "rows":  # the row-major expert matrices too
+        _check_full(layer, layer.cfg.t_max, mode, layout="rows")
 
 
 @pytest.mark.parametrize("name", ["floe_small", "floe_wide"])
@@ -294,6 +297,35 @@ def test_prefetch_adaptive_extremes(fill, expect):
     # T = 0 enqueues nothing and succeeds
     out = prefetch_adaptive_gpu(layer, 0, dev_weights(layer), 0.9, routed=routed[:0])
     assert len(out[0]) == 0 and len(out[1]) == 0
+
+
+def _pack_reference(src: np.ndarray) -> np.ndarray:
+    """Fragment-major packing written from its definition: fragment (t, s),
+    lane l, element j = W[16t + l%16][32s + 8(l/16) + j], zero outside."""
+    G, R, K = src.shape
+    RT, KS = -(-R // 16), -(-K // 32)
+    pad = np.zeros((G, RT * 16, KS * 32), dtype=src.dtype)
+    pad[:, :R, :K] = src
+    out = np.zeros((G, RT, KS, 64, 8), dtype=src.dtype)
+    for lane in range(64):
+        rows = np.arange(RT) * 16 + lane % 16
+        for s_ in range(KS):
+            k0 = 32 * s_ + 8 * (lane // 16)
+            out[:, :, s_, lane, :] = pad[:, rows, k0:k0 + 8]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("G,R,K", [(3, 40, 72), (2, 64, 64), (1, 16, 8), (5, 48, 2048)])
+def test_pack_weights_bit_exact(G, R, K):
+    rng = np.random.default_rng(G * 1000 + R + K)
+    src = rng.integers(0, 1 << 16, size=(G, R, K), dtype=np.uint16)
+    d_src = torch.from_numpy(src.view(np.int16)).cuda()
+    n = M.moe_pack_size(G, R, K)
+    assert n == G * (-(-R // 16)) * 16 * (-(-K // 32)) * 32 * 2
+    d_dst = torch.full((n // 2,), -1, dtype=torch.int16, device="cuda")
+    M.moe_pack_weights(G, R, K, d_src, d_dst)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(d_dst.cpu().numpy().view(np.uint16), _pack_reference(src))
 
 
 def test_permute_parity_random():
