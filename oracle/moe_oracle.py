@@ -50,6 +50,13 @@ notes):
   near-tie is measured on the logit scale: |theta_d - s - logit(tau)| below
   ``tie_margin`` at the chosen d or at d - 1.
 
+* FloE's intra-expert predictor applies the mask rule itself to h_l W_up^(l+1)
+  (the previous layer's hidden state and this layer's INT2 up weights) for the
+  experts this layer routes to; the inter-expert predictor that would guess
+  those experts is a trained MLP and not modelled, so the experts are given.
+  Recall is |predicted & true| / n_keep per (token, expert).  Compact packing
+  gathers the kept channels' gate and down rows in ascending channel order.
+
 Flag bits per token: 1 route near-tie, 2 prefetch near-tie, 4 substitution
 near-tie, 8 FloE mask near-tie, 16 prefetch-budget near-tie.
 """
@@ -67,6 +74,7 @@ __all__ = [
     "prefetch_set", "prefetch_masks", "delta_star", "stall_free_select",
     "FLAG_BUDGET", "adaptive_budget", "prefetch_overlap", "adaptive_prefetch",
     "permute", "swiglu_expert", "dequant_int2", "floe_expert",
+    "floe_channel_mask", "floe_predict_masks", "mask_recall", "floe_pack",
     "shared_experts", "lore_residual", "layer_forward", "WeightSource",
 ]
 
@@ -292,6 +300,57 @@ def dequant_int2(q_packed: np.ndarray, scale_bits: np.ndarray, zero_bits: np.nda
     s = np.repeat(fp16_to_f64(scale_bits), 64, axis=-1)
     z = np.repeat(fp16_to_f64(zero_bits), 64, axis=-1)
     return (codes - z) * s
+
+
+def floe_channel_mask(x_t: np.ndarray, up_q, up_scale, up_zero, n_keep: int, margin: float):
+    """FloE's channel mask S_t for one (token, expert) [FloE Sec. 1,
+    contextual sparsification]: u = x W_up with INT2 W_up; keep the n_keep
+    channels of largest |u|, ties to the lower channel.  Returns (keep
+    ascending int32, near-tie flag at the mask edge, u)."""
+    u = dequant_int2(up_q, up_scale, up_zero) @ x_t
+    I = u.shape[0]
+    order = sorted(range(I), key=lambda i: (-abs(u[i]), i))
+    flag = n_keep < I and (abs(u[order[n_keep - 1]]) - abs(u[order[n_keep]])) < margin
+    keep = np.sort(np.array(order[:n_keep], dtype=np.int64))
+    return keep.astype(np.int32), bool(flag), u
+
+
+def floe_predict_masks(h_prev: np.ndarray, ids: np.ndarray, up_q, up_scale, up_zero,
+                       n_keep: int, margin: float):
+    """FloE intra-expert predictor [FloE, "dual sparsity predictors",
+    intra-expert, reuse-based]: the mask of layer l+1 is estimated before its
+    input exists by applying the same top-|u| rule to h_l W_up^(l+1), the
+    current layer's hidden state times the next layer's own (INT2) up
+    projection -- no extra parameters.  ids [T][k] are the next layer's
+    experts per token; up_q etc. index [E][I][...].  Returns (keep [T][k][n_keep],
+    flags [T] with FLAG_FLOE at a near-tie)."""
+    T, k = ids.shape
+    keep = np.zeros((T, k, n_keep), dtype=np.int32)
+    flags = np.zeros(T, dtype=np.uint32)
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            kp, fl, _ = floe_channel_mask(h_prev[t], up_q[e], up_scale[e], up_zero[e], n_keep, margin)
+            keep[t, j] = kp
+            if fl:
+                flags[t] |= FLAG_FLOE
+    return keep, flags
+
+
+def mask_recall(pred: Sequence[int], true: Sequence[int]) -> float:
+    """Share of the true kept channels that the predicted set holds (the
+    page's recall of the intra-expert predictor)."""
+    t = set(int(c) for c in true)
+    return len(t & set(int(c) for c in pred)) / len(t) if t else 1.0
+
+
+def floe_pack(keep: np.ndarray, w_gate_e: np.ndarray, w_down_ih_e: np.ndarray):
+    """Compact column packing [FloE, "system co-optimisation": the gate and
+    down columns of the selected channels stored aligned so they move as one
+    compact block]: the kept channels' gate rows [n_keep][H] and down rows
+    [n_keep][H] (both stored channel-major), in the mask's ascending order."""
+    kp = np.asarray(keep, dtype=np.int64)
+    return np.asarray(w_gate_e)[kp].copy(), np.asarray(w_down_ih_e)[kp].copy()
 
 
 def floe_expert(x_t: np.ndarray, w_gate: np.ndarray, up_q, up_scale, up_zero,

@@ -340,6 +340,60 @@ def test_floe_keep_one_closed_form_and_mask_rule():
     assert set(keep5) == set(np.argsort(-np.abs(u5), kind="stable")[:5]) and list(keep5) == sorted(keep5)
 
 
+def test_floe_mask_brute_force_and_sign_scale_invariance():
+    """The kept set is the n-subset with the largest sum of |u| (brute force
+    over every 4-subset of 10 channels); it depends on |u| only, so x, -x and
+    3x keep the same channels."""
+    rng = np.random.default_rng(31)
+    q, s, z, _, _ = _floe_layer(rng, H=64, I=10)
+    x = rng.standard_normal(64)
+    keep, _, u = O.floe_channel_mask(x, q, s, z, 4, 1e-4)
+    best = max(itertools.combinations(range(10), 4), key=lambda c: sum(abs(u[i]) for i in c))
+    assert list(keep) == sorted(best)
+    for c in (-1.0, 3.0):
+        assert list(O.floe_channel_mask(c * x, q, s, z, 4, 1e-4)[0]) == list(keep)
+
+
+def test_floe_predictor_on_the_true_input_is_exact_and_recall_closed_forms():
+    """With h_prev equal to the layer's own input the predicted masks are the
+    layer's masks (recall 1); recall counts the shared channels over |true|."""
+    rng = np.random.default_rng(32)
+    E, I, H, keep = 3, 24, 128, 5
+    layers = [_floe_layer(rng, H=H, I=I) for _ in range(E)]
+    q = np.stack([l[0] for l in layers]); sc = np.stack([l[1] for l in layers])
+    z = np.stack([l[2] for l in layers])
+    x = rng.standard_normal((2, H))
+    ids = np.array([[2, 0], [1, 2]])
+    pk, fl = O.floe_predict_masks(x, ids, q, sc, z, keep, 1e-4)
+    for t in range(2):
+        for j in range(2):
+            e = ids[t, j]
+            _, _, kt, _ = O.floe_expert(x[t], layers[e][3], q[e], sc[e], z[e], layers[e][4], keep, 1e-4)
+            assert list(pk[t, j]) == list(kt) and O.mask_recall(pk[t, j], kt) == 1.0
+    assert O.mask_recall([1, 2, 3, 4], [5, 6, 7, 8]) == 0.0
+    assert O.mask_recall([1, 2, 9, 8], [1, 2, 3, 4]) == 0.5
+    # a far-off previous state predicts worse than a near one (same weights)
+    near = x + 0.01 * rng.standard_normal(x.shape)
+    r_near = np.mean([O.mask_recall(a, b) for a, b in
+                      zip(O.floe_predict_masks(near, ids, q, sc, z, keep, 1e-4)[0].reshape(-1, keep),
+                          pk.reshape(-1, keep))])
+    assert r_near == 1.0
+
+
+def test_floe_pack_reproduces_the_sparse_forward():
+    """The compact gate and down blocks of the kept channels, used as a dense
+    SwiGLU over n_keep channels, give FloE's output: a wrong, shuffled or
+    transposed row selection would not."""
+    rng = np.random.default_rng(33)
+    q, s, z, wg, wd = _floe_layer(rng, H=128, I=24)
+    x = rng.standard_normal(128)
+    y, u, keep, _ = O.floe_expert(x, wg, q, s, z, wd, 6, 1e-4)
+    gc, dc = O.floe_pack(keep, wg, wd)
+    assert gc.shape == (6, 128) and dc.shape == (6, 128)
+    y_c = (O.silu(gc @ x) * u[keep]) @ dc
+    np.testing.assert_allclose(y_c, y, rtol=1e-12, atol=1e-14)
+
+
 # ------------------------------------------------------- layer-level pins --
 def _small_layer(name="tiny", **kw):
     cfg = W.CONFIGS[name]

@@ -94,6 +94,7 @@ class MoEConfig:
     weight_std: float = 0.02
     hidden_std: float = 1.0
     lore_std: float = 0.01
+    prev_noise: float = 0.33        # x_prev = x + prev_noise * N(0, hidden_std): cosine ~0.95
 
     @property
     def t_max(self) -> int:
@@ -136,7 +137,7 @@ CONFIGS: Dict[str, MoEConfig] = {
 _TAG = {"x": 1, "w_router": 2, "w_gate": 3, "w_up": 4, "w_down": 5,
         "ws_gate": 6, "ws_up": 7, "ws_down": 8, "w_shared_gate": 9,
         "lore_A": 10, "lore_B": 11, "resident": 12, "w_prefetch": 13,
-        "delta": 14, "w_delta": 15, "theta": 16}
+        "delta": 14, "w_delta": 15, "theta": 16, "x_prev": 17}
 
 
 def _rng(seed: int, tag: str, idx: int = 0) -> np.random.Generator:
@@ -245,6 +246,22 @@ class Layer:
         if key not in self._cache:
             a = _normal(_rng(self.seed, "x"), (self.cfg.t_max, self.cfg.hidden), self.cfg.hidden_std)
             self._cache[key] = self._to_storage(a)
+        full = self._cache[key]
+        return full if T is None else full[:T]
+
+    def x_prev(self, T: Optional[int] = None) -> np.ndarray:
+        """The previous layer's hidden state for the FloE intra-expert
+        predictor: x + prev_noise * fresh N(0, hidden_std) noise, drawn in fp32
+        from the fp32 x draw, then rounded to the storage dtype.  0.33 puts the
+        cosine between the two near 0.95, the similarity of adjacent layers'
+        hidden states on the FloE page."""
+        key = ("x_prev", 0)
+        if key not in self._cache:
+            c = self.cfg
+            shape = (c.t_max, c.hidden)
+            x = _normal(_rng(self.seed, "x"), shape, c.hidden_std)
+            nz = _normal(_rng(self.seed, "x_prev"), shape, c.hidden_std)
+            self._cache[key] = self._to_storage((x + np.float32(c.prev_noise) * nz).astype(np.float32))
         full = self._cache[key]
         return full if T is None else full[:T]
 
