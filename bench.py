@@ -376,6 +376,71 @@ def measure_prefetch_adaptive(name, T, steps, warmup, tau=0.9):
                 overlap=float(o.mean() / k), covered=float((d >= st).mean()))
 
 
+def measure_floe_predict(steps, warmup, T=1, T_recall=8):
+    """FloE intra-expert predictor (previous hidden state through the INT2 up,
+    channel selection) and compact gate/down packing for Mixtral-8x7B-shaped
+    experts: time per call, HBM rate against the bytes each must move, and
+    the recall of the predicted masks against the true ones."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from workloads.device import dims_dict, tensor, upload
+    import sparse_moe_layer_route_amd as M
+
+    cfg = dataclasses.replace(W.CONFIGS["mixtral_floe"], token_counts=(1, T_recall))
+    layer = W.Layer(cfg)
+    dims = M.Dims(**dims_dict(cfg))
+    k, nk, H, I, E = cfg.top_k, cfg.floe_keep, cfg.hidden, cfg.inter, cfg.n_experts
+    w = upload(layer, "cuda")
+    Tm = max(T, T_recall)
+    ws = torch.empty(M.moe_workspace_size(dims, Tm, "floe"), dtype=torch.uint8, device="cuda")
+    # this layer's experts: the router on x (moe_route)
+    ids = torch.empty(Tm * k, dtype=torch.int32, device="cuda")
+    tw = torch.empty(Tm * k, dtype=torch.float32, device="cuda")
+    ex = torch.empty(Tm * k, dtype=torch.uint8, device="cuda")
+    fl = torch.zeros(Tm, dtype=torch.int32, device="cuda")
+    lg = torch.empty(Tm * E, dtype=torch.float32, device="cuda")
+    x = tensor(layer.x(Tm), cfg.dtype, "cuda")
+    xp = tensor(layer.x_prev(Tm), cfg.dtype, "cuda")
+    M.moe_route(dims, Tm, x, w["w_router"], None, 0, "standard", ids, tw, ex, fl, lg)
+    keep_p = torch.empty(Tm * k * nk, dtype=torch.int32, device="cuda")
+    keep_t = torch.empty(Tm * k * nk, dtype=torch.int32, device="cuda")
+    M.moe_floe_predict(dims, Tm, xp, w, ids, keep_p, fl, ws)
+    M.moe_floe_predict(dims, Tm, x, w, ids, keep_t, fl, ws)
+    torch.cuda.synchronize()
+    kp = keep_p.cpu().numpy().reshape(-1, nk)
+    kt = keep_t.cpu().numpy().reshape(-1, nk)
+    recall = float(np.mean([len(set(a) & set(b)) / nk for a, b in zip(kp, kt)]))
+    esz = 2 if cfg.dtype == "bf16" else 4
+    gate = torch.empty(T * k * nk * H * esz // 2, dtype=torch.int16, device="cuda")
+    down = torch.empty_like(gate)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(steps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e3 / steps
+
+    us_pred = timed(lambda: M.moe_floe_predict(dims, T, xp, w, ids, keep_p, fl, ws))
+    us_pack = timed(lambda: M.moe_floe_pack(dims, T, ids, keep_p, w["w_gate"], w["w_down"], gate, down))
+    # bytes: INT2 codes + fp16 scale and zero of each pair's expert, and h;
+    # packing reads and writes the kept gate and down rows
+    pred_bytes = T * k * (I * H // 4 + 2 * I * (H // 64) * 2) + T * H * esz
+    pack_bytes = T * k * nk * H * esz * 2 * 2
+    return dict(workload="mixtral_floe", tokens=T, mode="floe_predict_pack",
+                predict_us=us_pred, predict_gbs=pred_bytes / (us_pred * 1e-6) / 1e9,
+                pack_us=us_pack, pack_gbs=pack_bytes / (us_pack * 1e-6) / 1e9,
+                pack_hbm_frac=pack_bytes / (us_pack * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                recall=recall, recall_tokens=T_recall, prev_noise=cfg.prev_noise)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -416,6 +481,12 @@ def main():
         print(f"# granite_prefill T=4096 adaptive prefetch: {r['us_per_call']:.1f} us/call, "
               f"{r['gbs']:.0f} GB/s, mean budget {r['mean_budget']:.2f}, overlap {r['overlap']:.3f}, "
               f"covered {r['covered']:.3f}", file=sys.stderr, flush=True)
+        r = measure_floe_predict(args.steps, min(args.warmup, 5))
+        also.append(r)
+        print(f"# mixtral_floe T=1 FloE predictor: {r['predict_us']:.1f} us/call "
+              f"({r['predict_gbs']:.0f} GB/s); compact pack {r['pack_us']:.1f} us "
+              f"({r['pack_gbs']:.0f} GB/s); recall {r['recall']:.3f} over {r['recall_tokens']} tokens",
+              file=sys.stderr, flush=True)
     cpu = None if args.no_cpu else cpu_baseline(args.workload, args.tokens, args.mode)
     line = {
         "metric": METRIC,

@@ -241,7 +241,8 @@ moe_status_t moe_permute(int32_t T, int32_t k, int32_t E, const int32_t* topk_id
  *     of largest |u| (ties -> lower channel); y = sum over kept i of
  *     SiLU(g_i) u_i W_d[i,:] [FloE page, Sec. 1].  floe_keep_opt [T*k][keep]
  *     receives the kept channels of slot f = t*k + j (ascending); flags_opt [T] gets
- *     bit 8 OR-ed in for a near-tie at the mask edge (may be NULL).
+ *     bit 8 OR-ed in for a near-tie at the mask edge (required in MOE_MODE_FLOE,
+ *     ignored otherwise and may be NULL).  MOE_MODE_FLOE: T*k <= 65535.
  *   Shared: y_shared [T][H] fp32 = sum of the shared SwiGLU FFNs (ungated);
  *     shared_gate [T] fp32 = sigmoid(x . w_sg), or 1.  Both may be NULL when
  *     n_shared = 0.
@@ -252,6 +253,32 @@ moe_status_t moe_expert_ffn(const moe_dims_t* dims, int32_t T, const void* x,
                             float* y_perm, float* y_shared, float* shared_gate,
                             int32_t* floe_keep_opt, uint32_t* flags_opt,
                             void* ws, size_t ws_bytes, void* stream);
+
+/* FloE intra-expert predictor [FloE page, "dual sparsity predictors",
+ * intra-expert predictor]: the channel masks of this layer's (token, expert)
+ * pairs estimated from the previous layer's hidden state h_prev [T][H]
+ * (dtype) through this layer's INT2 up projection, by the same rule as the
+ * FloE forward (the dims.floe_keep channels of largest |h_prev W_up|, ties ->
+ * lower channel).  topk_ids [T][k] name this layer's experts (ids outside
+ * 0..E-1 leave their slot unwritten); keep_out [T][k][floe_keep] receives the
+ * kept channels of slot f = t*k + j, ascending; flags [T] gets bit 8 OR-ed in
+ * at a near-tie (the caller initialises it).  Reads w->up_q, up_scale,
+ * up_zero.  ws: at least moe_workspace_size(dims, T, MOE_MODE_FLOE) bytes.
+ * Needs the MOE_MODE_FLOE shape (INT2 up format), T*k <= 65535. */
+moe_status_t moe_floe_predict(const moe_dims_t* dims, int32_t T, const void* h_prev,
+                              const moe_weights_t* w, const int32_t* topk_ids, int32_t* keep_out,
+                              uint32_t* flags, void* ws, size_t ws_bytes, void* stream);
+
+/* FloE compact packing [FloE page, "system co-optimisation": the selected
+ * channels' gate and down columns stored aligned and moved as one block]:
+ * for slot f = t*k + j with expert e = topk_ids[f] and c < floe_keep,
+ * gate_out[f][c][:] = w_gate[e][keep[f][c]][:] and down_out[f][c][:] =
+ * w_down[e][keep[f][c]][:] (both weight tensors [E][I][H] dtype, the FloE
+ * format); out [T][k][floe_keep][H] dtype each.  A slot with an id outside
+ * 0..E-1, or a channel outside 0..I-1, gets zero rows.  T*k <= 65535. */
+moe_status_t moe_floe_pack(const moe_dims_t* dims, int32_t T, const int32_t* topk_ids,
+                           const int32_t* keep, const void* w_gate, const void* w_down,
+                           void* gate_out, void* down_out, void* stream);
 
 /* LoRE residual [SPICE page, "LoRE low-rank surrogate"]: for each slot with
  * exact[t][j] == 0, lore_out[t][j] = B_e (A_e x_t) with A_e [r][H] and

@@ -81,6 +81,8 @@ def _load():
         "moe_permute": ([I32, I32, I32, P, P, P, P, P, P, SZ, P], ctypes.c_int),
         "moe_expert_ffn": ([D, I32, P, Wp, ctypes.c_int, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
         "moe_lore_surrogate": ([D, I32, P, P, P, P, P, P, P], ctypes.c_int),
+        "moe_floe_predict": ([D, I32, P, Wp, P, P, P, P, SZ, P], ctypes.c_int),
+        "moe_floe_pack": ([D, I32, P, P, P, P, P, P, P], ctypes.c_int),
         "moe_combine": ([D, I32, P, P, P, P, P, P, P, P, P], ctypes.c_int),
         "moe_layer_forward": ([D, I32, P, Wp, P, I64, ctypes.c_int, P, Dbg, P, SZ, P], ctypes.c_int),
     }
@@ -94,7 +96,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_route",
             "moe_prefetch_mask", "moe_prefetch_adaptive", "moe_pack_size", "moe_pack_weights",
-            "moe_permute", "moe_expert_ffn", "moe_lore_surrogate",
+            "moe_permute", "moe_floe_predict", "moe_floe_pack", "moe_expert_ffn", "moe_lore_surrogate",
             "moe_combine", "moe_layer_forward")
 
 
@@ -225,6 +227,19 @@ def pack_weights(dims: "Dims", w: Dict[str, torch.Tensor], stream=None) -> Dict[
         moe_pack_weights(g, r, c, src, dst, stream)
         out[name] = dst
     return out
+
+
+def moe_floe_predict(dims, T, h_prev, w, topk_ids, keep_out, flags, ws, stream=None):
+    ws_ = weights_struct(w) if isinstance(w, dict) else w
+    _check(_lib.moe_floe_predict(ctypes.byref(_dims(dims)), T, _ptr(h_prev), ctypes.byref(ws_),
+                                 _ptr(topk_ids), _ptr(keep_out), _ptr(flags), _ptr(ws), ws.numel(),
+                                 _stream(stream)), "moe_floe_predict")
+
+
+def moe_floe_pack(dims, T, topk_ids, keep, w_gate, w_down, gate_out, down_out, stream=None):
+    _check(_lib.moe_floe_pack(ctypes.byref(_dims(dims)), T, _ptr(topk_ids), _ptr(keep), _ptr(w_gate),
+                              _ptr(w_down), _ptr(gate_out), _ptr(down_out), _stream(stream)),
+           "moe_floe_pack")
 
 
 def moe_permute(T, k, E, topk_ids, exact, expert_offsets, perm, inv, ws=None, stream=None):

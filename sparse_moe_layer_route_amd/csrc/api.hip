@@ -13,6 +13,12 @@ hipError_t launch_route(const moe_dims_t& d, int T, const void* x, const void* w
                         float* w, uint8_t* exact, uint32_t* flags, float* logits, float* mass,
                         const void* w_sg, float* g_s, hipStream_t s);
 hipError_t launch_pack_mfma16(int G, int R, int K, const void* src, void* dst, hipStream_t s);
+hipError_t launch_floe_predict(const moe_dims_t& d, int T, const void* h, const moe_weights_t& w,
+                               const int32_t* offsets, const int32_t* perm, float* u,
+                               int32_t* keep, uint32_t* flags, hipStream_t s);
+hipError_t launch_floe_pack(const moe_dims_t& d, int T, const int32_t* ids, const int32_t* keep,
+                            const void* w_gate, const void* w_down, void* gate_out,
+                            void* down_out, hipStream_t s);
 int64_t packed_elems(int R, int K);
 hipError_t launch_prefetch_adaptive(const moe_dims_t& d, int T, const void* x, const void* w_p,
                                     const void* w_delta, const float* theta, float logit_tau,
@@ -64,6 +70,8 @@ using namespace moe;
 namespace {
 
 constexpr int32_t kMaxTokens = 1 << 22;
+// FloE kernels index (token, expert) pairs on a grid dimension capped at 65535
+constexpr int64_t kFloeMaxPairs = 65535;
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
@@ -366,6 +374,7 @@ moe_status_t moe_expert_ffn(const moe_dims_t* dims, int32_t T, const void* x,
   if (dims->n_shared > 0 && (!ok_ptr(y_shared) || !ok_ptr(shared_gate))) return MOE_EINVAL;
   if (!ok_opt(floe_keep_opt) || !ok_opt(flags_opt)) return MOE_EINVAL;
   if (mode == MOE_MODE_FLOE && !flags_opt) return MOE_EINVAL;
+  if (mode == MOE_MODE_FLOE && (int64_t)T * dims->top_k > kFloeMaxPairs) return MOE_EUNSUPPORTED;
   const Plan p = make_plan(*dims, T, mode);
   if (ws_bytes < p.total) return MOE_EWORKSPACE;
   if (T == 0) return MOE_OK;
@@ -374,6 +383,49 @@ moe_status_t moe_expert_ffn(const moe_dims_t* dims, int32_t T, const void* x,
                          flags_opt, ws, p, 0, Prof{}, (hipStream_t)stream);
   if (e == hipSuccess) e = launch_shared_gate(*dims, T, x, *w, shared_gate, (hipStream_t)stream);
   return hip_status(e);
+}
+
+moe_status_t moe_floe_predict(const moe_dims_t* dims, int32_t T, const void* h_prev,
+                              const moe_weights_t* w, const int32_t* topk_ids, int32_t* keep_out,
+                              uint32_t* flags, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if ((st = check_mode(dims, MOE_MODE_FLOE)) != MOE_OK) return st;
+  if (!w || !ok_ptr(w->up_q) || !ok_ptr(w->up_scale) || !ok_ptr(w->up_zero)) return MOE_EINVAL;
+  if (T < 0) return MOE_EINVAL;
+  if ((int64_t)T * dims->top_k > kFloeMaxPairs) return MOE_EUNSUPPORTED;
+  if (!ok_ptr(h_prev) || !ok_ptr(topk_ids) || !ok_ptr(keep_out) || !ok_ptr(flags) || !ok_ptr(ws))
+    return MOE_EINVAL;
+  const Plan p = make_plan(*dims, T, MOE_MODE_FLOE);
+  if (ws_bytes < p.total) return MOE_EWORKSPACE;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const int P = T * dims->top_k;
+  int32_t* offsets = at<int32_t>(ws, p.offsets);
+  int32_t* perm = at<int32_t>(ws, p.perm);
+  hipError_t e = launch_permute(P, dims->n_experts, topk_ids, nullptr, offsets, perm,
+                                at<int32_t>(ws, p.inv), at<int32_t>(ws, p.row_of),
+                                at<int32_t>(ws, p.moffsets), at<int32_t>(ws, p.pscratch), s);
+  if (e == hipSuccess)
+    e = launch_floe_predict(*dims, T, h_prev, *w, offsets, perm, at<float>(ws, p.u), keep_out,
+                            flags, s);
+  return hip_status(e);
+}
+
+moe_status_t moe_floe_pack(const moe_dims_t* dims, int32_t T, const int32_t* topk_ids,
+                           const int32_t* keep, const void* w_gate, const void* w_down,
+                           void* gate_out, void* down_out, void* stream) {
+  moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if ((st = check_mode(dims, MOE_MODE_FLOE)) != MOE_OK) return st;
+  if (T < 0) return MOE_EINVAL;
+  if ((int64_t)T * dims->top_k > kFloeMaxPairs) return MOE_EUNSUPPORTED;
+  if (!ok_ptr(topk_ids) || !ok_ptr(keep) || !ok_ptr(w_gate) || !ok_ptr(w_down) ||
+      !ok_ptr(gate_out) || !ok_ptr(down_out))
+    return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  return hip_status(launch_floe_pack(*dims, T, topk_ids, keep, w_gate, w_down, gate_out, down_out,
+                                     (hipStream_t)stream));
 }
 
 moe_status_t moe_lore_surrogate(const moe_dims_t* dims, int32_t T, const void* x,
@@ -418,6 +470,7 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, int32_t T, const void* x,
   if ((st = check_weights(dims, w, mode)) != MOE_OK) return st;
   if (T < 0) return MOE_EINVAL;
   if (T > kMaxTokens) return MOE_EUNSUPPORTED;
+  if (mode == MOE_MODE_FLOE && (int64_t)T * dims->top_k > kFloeMaxPairs) return MOE_EUNSUPPORTED;
   if (!ok_ptr(x) || !ok_ptr(out) || !ok_ptr(ws)) return MOE_EINVAL;
   const bool needs_mask = mode == MOE_MODE_LORE || mode == MOE_MODE_STALL_FREE;
   if (needs_mask && (!ok_ptr(resident) || (resident_stride != 0 && resident_stride != 1)))

@@ -644,6 +644,67 @@ static hipError_t launch_floe_t(const moe_dims_t& d, int T, const Tin* x, const 
   return e == hipSuccess ? hipGetLastError() : e;
 }
 
+// FloE intra-expert predictor: the up projection and channel selection of the
+// FloE forward, run on another hidden state (the previous layer's) for the
+// pairs already permuted into `offsets` / `perm`.
+hipError_t launch_floe_predict(const moe_dims_t& d, int T, const void* h, const moe_weights_t& w,
+                               const int32_t* offsets, const int32_t* perm, float* u,
+                               int32_t* keep, uint32_t* flags, hipStream_t s) {
+  const int H = d.hidden, I = d.inter, E = d.n_experts, k = d.top_k, nk = d.floe_keep;
+  const int P = T * k;
+  if (P == 0) return hipSuccess;
+  if (d.dtype == MOE_BF16) {
+    constexpr int R = FLOE_UP_BF16_RPW;
+    const size_t lds = (size_t)H / 8 * 16 + (size_t)(H / 64) * 8;
+    floe_up_bf16_kernel<R><<<dim3((I + 4 * R - 1) / (4 * R), P), 256, lds, s>>>(
+        (const bf16*)h, w.up_q, w.up_scale, w.up_zero, H, I, E, k, offsets, perm, u);
+  } else {
+    floe_up_kernel<float><<<dim3((I + 4 * FLOE_UP_RPW - 1) / (4 * FLOE_UP_RPW), P), 256, 0, s>>>(
+        (const float*)h, w.up_q, w.up_scale, w.up_zero, H, I, E, k, offsets, perm, u);
+  }
+  floe_select_kernel<<<P, FLOE_SELECT_THREADS, 0, s>>>(u, I, nk, d.tie_margin, E, k, offsets, perm,
+                                                        keep, flags);
+  return hipGetLastError();
+}
+
+// Compact packing of the kept channels: for slot f = t*k + j with expert
+// e = ids[f], rows keep[f][c] of W_gate[e] and W_down[e] (both [I][H]) are
+// copied to gate_out[f][c] and down_out[f][c].  One block per (slot, group of
+// FLOE_PACK_ROWS kept channels), 16 bytes per thread per row.
+constexpr int FLOE_PACK_ROWS = 8;
+__global__ void __launch_bounds__(256)
+floe_pack_kernel(const int32_t* __restrict__ ids, const int32_t* __restrict__ keep,
+                 const uint4* __restrict__ wg, const uint4* __restrict__ wd, int I, int nk, int E,
+                 int row_u4, uint4* __restrict__ gate_out, uint4* __restrict__ down_out) {
+  const int f = blockIdx.x;
+  const int e = ids[f];
+  const int c0 = blockIdx.y * FLOE_PACK_ROWS, c1 = min(nk, c0 + FLOE_PACK_ROWS);
+  const bool valid = (unsigned)e < (unsigned)E;
+  for (int c = c0; c < c1; ++c) {
+    const int ch = keep[(int64_t)f * nk + c];
+    const bool ok = valid && (unsigned)ch < (unsigned)I;
+    const int64_t src = ((int64_t)(ok ? e : 0) * I + (ok ? ch : 0)) * row_u4;
+    const int64_t dst = ((int64_t)f * nk + c) * row_u4;
+    for (int i = threadIdx.x; i < row_u4; i += blockDim.x) {
+      gate_out[dst + i] = ok ? wg[src + i] : make_uint4(0u, 0u, 0u, 0u);
+      down_out[dst + i] = ok ? wd[src + i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+}
+
+hipError_t launch_floe_pack(const moe_dims_t& d, int T, const int32_t* ids, const int32_t* keep,
+                            const void* w_gate, const void* w_down, void* gate_out,
+                            void* down_out, hipStream_t s) {
+  const int P = T * d.top_k, nk = d.floe_keep;
+  if (P == 0) return hipSuccess;
+  const int esz = d.dtype == MOE_BF16 ? 2 : 4;
+  const int row_u4 = d.hidden * esz / 16;
+  floe_pack_kernel<<<dim3(P, (nk + FLOE_PACK_ROWS - 1) / FLOE_PACK_ROWS), 256, 0, s>>>(
+      ids, keep, (const uint4*)w_gate, (const uint4*)w_down, d.inter, nk, d.n_experts, row_u4,
+      (uint4*)gate_out, (uint4*)down_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_floe(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
                        const int32_t* offsets, const int32_t* perm, float* u,
                        int32_t* keep, float* a, float* part, float* y_perm, uint32_t* flags,

@@ -21,12 +21,12 @@ constexpr int PERM_WAVES = PERM_THREADS / MOE_WAVE;
 constexpr int PERM_BUCKETS = 2 * MOE_MAX_EXPERTS;
 
 // Bucket of pair f: expert for exact pairs, E + expert for the others, -1
-// for out-of-range ids (never placed).
+// for out-of-range ids (never placed).  exact == nullptr: every pair exact.
 __device__ __forceinline__ int bucket_of(int f, int E, const int32_t* __restrict__ ids,
                                          const uint8_t* __restrict__ exact) {
   const int e = ids[f];
   if ((unsigned)e >= (unsigned)E) return -1;
-  return exact[f] ? e : E + e;
+  return (!exact || exact[f]) ? e : E + e;
 }
 
 // Histogram of chunk blockIdx.x into counts[blockIdx.x][2E].

@@ -134,6 +134,28 @@ def test_pack_size_and_checks():
     assert L.moe_pack_weights(1, 16, 12, FAKE, FAKE + 4096, None) == B.MOE_EINVAL  # cols % 8
 
 
+def test_floe_predict_and_pack_host_checks():
+    fl = dims(dtype="bf16", up_format="int2_g64", floe_keep=16, n_shared=0, shared_inter=0)
+    w = _weights()
+    need = ws_size(fl, 16, 3)[1]
+    pr, pk = L.moe_floe_predict, L.moe_floe_pack
+    assert pr(ctypes.byref(fl), 16, FAKE, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, need - 256,
+              None) == B.MOE_EWORKSPACE
+    assert pr(ctypes.byref(fl), 16, None, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, need,
+              None) == B.MOE_EINVAL
+    assert pr(ctypes.byref(fl), 16, FAKE, ctypes.byref(w), FAKE, FAKE, None, FAKE, need,
+              None) == B.MOE_EINVAL                                    # flags required
+    assert pr(ctypes.byref(fl), 40000, FAKE, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, 1 << 40,
+              None) == B.MOE_EUNSUPPORTED                              # T*k > 65535
+    assert pr(ctypes.byref(dims(dtype="bf16")), 16, FAKE, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE,
+              need, None) == B.MOE_EUNSUPPORTED                        # not the INT2 format
+    assert pr(ctypes.byref(fl), 0, FAKE, ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, 1 << 20,
+              None) == B.MOE_OK
+    assert pk(ctypes.byref(fl), 16, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == B.MOE_EINVAL
+    assert pk(ctypes.byref(fl), 40000, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.MOE_EUNSUPPORTED
+    assert pk(ctypes.byref(fl), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.MOE_OK
+
+
 def test_entry_point_null_checks():
     d = dims()
     P = ctypes.c_void_p

@@ -328,6 +328,108 @@ def test_pack_weights_bit_exact(G, R, K):
     np.testing.assert_array_equal(d_dst.cpu().numpy().view(np.uint16), _pack_reference(src))
 
 
+# ----------------------------------------------- FloE predictor and packing --
+def _floe_layer_for(name):
+    if name == "mixtral":
+        return W.Layer(dataclasses.replace(W.CONFIGS["mixtral_floe"], token_counts=(1, 3)))
+    return W.Layer(FLOE_SMALL[name])
+
+
+def _floe_stack(layer, field):
+    return np.stack([layer.expert(field, e) for e in range(layer.cfg.n_experts)])
+
+
+def _floe_predict_gpu(layer, T, h_np, ids):
+    cfg = layer.cfg
+    dims = M.Dims(**dims_dict(cfg))
+    k, nk = cfg.top_k, cfg.floe_keep
+    ws = torch.empty(M.moe_workspace_size(dims, T, "floe"), dtype=torch.uint8, device="cuda")
+    keep = torch.full((T * k * nk,), -3, dtype=torch.int32, device="cuda")
+    flags = torch.zeros(T, dtype=torch.int32, device="cuda")
+    d_ids = torch.from_numpy(np.ascontiguousarray(ids, np.int32).reshape(-1)).cuda()
+    M.moe_floe_predict(dims, T, tensor(h_np, cfg.dtype, "cuda"), dev_weights(layer), d_ids, keep,
+                       flags, ws)
+    torch.cuda.synchronize()
+    return keep.cpu().numpy().reshape(T, k, nk), flags.cpu().numpy().view(np.uint32)
+
+
+@pytest.mark.parametrize("name,T", [("floe_small", 5), ("floe_wide", 3), ("mixtral", 2)])
+def test_floe_predict_parity(name, T):
+    """Predicted masks from the previous layer's hidden state: every pair
+    exact against the oracle's mask rule unless it flags a near-tie at the
+    mask edge, admissible within the margin there."""
+    layer = _floe_layer_for(name)
+    cfg = layer.cfg
+    k, nk = cfg.top_k, cfg.floe_keep
+    X = O.decode(layer.x(T), cfg.dtype)
+    Xp = O.decode(layer.x_prev(T), cfg.dtype)
+    ids = _oracle_routed(layer, X, k)
+    gk, gf = _floe_predict_gpu(layer, T, layer.x_prev(T), ids)
+    n_tie, rec = 0, []
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            ok, ofl, u = O.floe_channel_mask(Xp[t], layer.expert("up_q", e), layer.expert("up_scale", e),
+                                             layer.expert("up_zero", e), nk, MARGIN)
+            assert np.all(np.diff(gk[t, j]) > 0)
+            if ofl:
+                n_tie += 1
+                assert gf[t] & O.FLAG_FLOE
+                mask = np.zeros(cfg.inter, bool)
+                mask[gk[t, j]] = True
+                assert np.abs(u[mask]).min() >= np.abs(u[~mask]).max() - MARGIN
+            else:
+                np.testing.assert_array_equal(gk[t, j], ok)
+            tk, _, _ = O.floe_channel_mask(X[t], layer.expert("up_q", e), layer.expert("up_scale", e),
+                                           layer.expert("up_zero", e), nk, MARGIN)
+            rec.append(O.mask_recall(ok, tk))
+    assert (gf & ~np.uint32(O.FLAG_FLOE)).sum() == 0
+    say(f"    {name} T={T}: near-ties {n_tie}, oracle recall vs the true mask {np.mean(rec):.3f}")
+
+
+@pytest.mark.parametrize("name,T", [("floe_small", 5), ("mixtral", 3)])
+def test_floe_pack_bit_exact(name, T):
+    """Compact gate/down rows of the oracle's predicted channels, bit for bit
+    (a pure gather), including a slot with an invalid expert id and a channel
+    past I, which give zero rows."""
+    layer = _floe_layer_for(name)
+    cfg = layer.cfg
+    k, nk, H = cfg.top_k, cfg.floe_keep, cfg.hidden
+    X = O.decode(layer.x(T), cfg.dtype)
+    ids = _oracle_routed(layer, X, k)
+    keep, _ = O.floe_predict_masks(O.decode(layer.x_prev(T), cfg.dtype), ids,
+                                   _floe_stack(layer, "up_q"), _floe_stack(layer, "up_scale"),
+                                   _floe_stack(layer, "up_zero"), nk, MARGIN)
+    ids_in = ids.copy()
+    ids_in[T - 1, k - 1] = cfg.n_experts          # invalid expert -> zero rows
+    keep_in = keep.copy()
+    keep_in[0, 0, nk - 1] = cfg.inter             # channel past I -> a zero row
+    dims = M.Dims(**dims_dict(cfg))
+    wdev = dev_weights(layer)
+    gate = torch.full((T * k * nk * H,), 7, dtype=torch.int16, device="cuda")
+    down = torch.full((T * k * nk * H,), 7, dtype=torch.int16, device="cuda")
+    M.moe_floe_pack(dims, T, torch.from_numpy(ids_in.reshape(-1)).cuda(),
+                    torch.from_numpy(keep_in.reshape(-1)).cuda(), wdev["w_gate"], wdev["w_down"],
+                    gate, down)
+    torch.cuda.synchronize()
+    gg = gate.cpu().numpy().view(np.uint16).reshape(T, k, nk, H)
+    gd = down.cpu().numpy().view(np.uint16).reshape(T, k, nk, H)
+    for t in range(T):
+        for j in range(k):
+            if ids_in[t, j] >= cfg.n_experts:
+                assert not gg[t, j].any() and not gd[t, j].any()
+                continue
+            e = int(ids_in[t, j])
+            wg, wd = O.floe_pack(keep[t, j], layer.expert("w_gate", e), layer.expert("w_down", e))
+            if t == 0 and j == 0:
+                assert not gg[0, 0, nk - 1].any() and not gd[0, 0, nk - 1].any()
+                wg, wd, gg_, gd_ = wg[:-1], wd[:-1], gg[0, 0, :-1], gd[0, 0, :-1]
+            else:
+                gg_, gd_ = gg[t, j], gd[t, j]
+            np.testing.assert_array_equal(gg_, wg)
+            np.testing.assert_array_equal(gd_, wd)
+
+
 def test_permute_parity_random():
     rng = np.random.default_rng(7)
     for T, k, E, p_exact in [(1, 1, 1, 1.0), (37, 6, 64, 0.5), (4096, 8, 40, 1.0), (300, 8, 64, 0.0),
