@@ -57,6 +57,11 @@ notes):
   Recall is |predicted & true| / n_keep per (token, expert).  Compact packing
   gathers the kept channels' gate and down rows in ascending channel order.
 
+* LoRE fitting: the calibration inputs are an orthogonal design (blocks of
+  sqrt(H)-scaled random orthogonal matrices, so h^T h = N I before rounding to
+  the layer dtype); the least-squares map is then R^T h / N, and the rank-r
+  factors come from its truncated SVD, B = U_r S_r and A = V_r^T.
+
 Flag bits per token: 1 route near-tie, 2 prefetch near-tie, 4 substitution
 near-tie, 8 FloE mask near-tie, 16 prefetch-budget near-tie.
 """
@@ -75,6 +80,7 @@ __all__ = [
     "FLAG_BUDGET", "adaptive_budget", "prefetch_overlap", "adaptive_prefetch",
     "permute", "swiglu_expert", "dequant_int2", "floe_expert",
     "floe_channel_mask", "floe_predict_masks", "mask_recall", "floe_pack",
+    "lore_targets", "lore_fit",
     "shared_experts", "lore_residual", "layer_forward", "WeightSource",
 ]
 
@@ -385,6 +391,33 @@ def shared_experts(x: np.ndarray, ws_gate, ws_up, ws_down_hi, w_shared_gate=None
         y += swiglu_expert(x, ws_gate[s], ws_up[s], ws_down_hi[s])
     g = sigmoid(x @ w_shared_gate) if w_shared_gate is not None else np.ones(T)
     return y, g
+
+
+def lore_targets(h: np.ndarray, w_gate_e, w_up_e, w_down_e, ws_gate, ws_up, ws_down) -> np.ndarray:
+    """What LoRE must reproduce for expert e on calibration inputs h [N][H]
+    [SPICE "LoRE low-rank surrogate": collect each expert's inputs and
+    outputs and the shared experts' output]: y_e(h) - y_shared(h)."""
+    y_e = swiglu_expert(h, w_gate_e, w_up_e, w_down_e)
+    y_s, _ = shared_experts(h, ws_gate, ws_up, ws_down)
+    return y_e - y_s
+
+
+def lore_fit(h: np.ndarray, resid: np.ndarray, r: int):
+    """LoRE fitting [SPICE "LoRE low-rank surrogate": minimise
+    ||y_e - y_shared - B_e A_e h||^2 over the calibration set, solved by an
+    SVD].  With R = resid [N][H] and the calibration inputs an orthogonal
+    design (H^T H = N I), the least-squares map is M = R^T h / N, and its
+    rank-r truncated SVD U_r S_r V_r^T is the best rank-r map (Eckart-Young).
+    Returns (A = V_r^T [r][H], B = U_r S_r [H][r], the r singular values, and
+    the relative residual ||R - h (B A)^T||_F / ||R||_F on the calibration set)."""
+    N = h.shape[0]
+    M = np.asarray(resid, dtype=np.float64).T @ np.asarray(h, dtype=np.float64) / N
+    U, S, Vt = np.linalg.svd(M)
+    B = U[:, :r] * S[:r]
+    A = Vt[:r]
+    pred = h @ (B @ A).T
+    err = float(np.linalg.norm(resid - pred) / np.linalg.norm(resid))
+    return A, B, S[:r].copy(), err
 
 
 def lore_residual(x_t: np.ndarray, lore_a: np.ndarray, lore_b: np.ndarray) -> np.ndarray:

@@ -394,6 +394,61 @@ def test_floe_pack_reproduces_the_sparse_forward():
     np.testing.assert_allclose(y_c, y, rtol=1e-12, atol=1e-14)
 
 
+def _orthogonal_design(rng, N, H):
+    blocks = [np.linalg.qr(rng.standard_normal((H, H)))[0] * np.sqrt(H) for _ in range(N // H)]
+    return np.concatenate(blocks, axis=0)
+
+
+def test_lore_fit_map_is_least_squares_under_orthogonal_design():
+    """With h^T h = N I the map R^T h / N is lstsq's solution, and the rank-r
+    residual obeys Eckart-Young: ||R - h M_r^T||^2 = ||R - h M^T||^2 +
+    N * (sum of the dropped squared singular values)."""
+    rng = np.random.default_rng(41)
+    N, H, r = 64, 32, 5
+    h = _orthogonal_design(rng, N, H)
+    R = rng.standard_normal((N, H)) @ rng.standard_normal((H, H)) * 0.1 + rng.standard_normal((N, H)) * 0.05
+    A, B, sig, err = O.lore_fit(h, R, r)
+    M_ls = np.linalg.lstsq(h, R, rcond=None)[0].T
+    np.testing.assert_allclose(R.T @ h / N, M_ls, rtol=1e-10, atol=1e-12)
+    S = np.linalg.svd(M_ls, compute_uv=False)
+    np.testing.assert_allclose(sig, S[:r], rtol=1e-12)
+    full = np.linalg.norm(R - h @ M_ls.T) ** 2
+    want = math.sqrt(full + N * float(np.sum(S[r:] ** 2))) / np.linalg.norm(R)
+    assert abs(err - want) < 1e-10
+    # the error never grows with the rank, and rank H reproduces the LS fit
+    errs = [O.lore_fit(h, R, q)[3] for q in (1, 2, 5, 10, 32)]
+    assert all(a >= b - 1e-12 for a, b in zip(errs, errs[1:]))
+    assert abs(errs[-1] - math.sqrt(full) / np.linalg.norm(R)) < 1e-10
+
+
+def test_lore_fit_recovers_an_exact_low_rank_map():
+    rng = np.random.default_rng(42)
+    N, H, r = 96, 48, 4
+    h = _orthogonal_design(rng, N, H)
+    M_true = rng.standard_normal((H, r)) @ rng.standard_normal((r, H))
+    A, B, sig, err = O.lore_fit(h, h @ M_true.T, r)
+    assert err < 1e-12
+    np.testing.assert_allclose(B @ A, M_true, rtol=1e-10, atol=1e-10)
+    assert A.shape == (r, H) and B.shape == (H, r)
+    # A has orthonormal rows; B's columns carry the singular values
+    np.testing.assert_allclose(A @ A.T, np.eye(r), atol=1e-12)
+    np.testing.assert_allclose(np.linalg.norm(B, axis=0), sig, rtol=1e-12)
+
+
+def test_lore_targets_are_expert_minus_shared():
+    rng = np.random.default_rng(43)
+    H, I, Is = 16, 8, 12
+    wg, wu, wd = (rng.standard_normal(s) * 0.3 for s in ((I, H), (I, H), (H, I)))
+    sg, su, sd = (rng.standard_normal(s) * 0.3 for s in ((1, Is, H), (1, Is, H), (1, H, Is)))
+    h = rng.standard_normal((3, H))
+    got = O.lore_targets(h, wg, wu, wd, sg, su, sd)
+    for t in range(3):
+        ye = sum(wd[:, i] * (h[t] @ wg[i]) / (1 + math.exp(-(h[t] @ wg[i]))) * (h[t] @ wu[i]) for i in range(I))
+        ys = sum(sd[0][:, i] * (h[t] @ sg[0][i]) / (1 + math.exp(-(h[t] @ sg[0][i]))) * (h[t] @ su[0][i])
+                 for i in range(Is))
+        np.testing.assert_allclose(got[t], ye - ys, rtol=1e-12, atol=1e-14)
+
+
 # ------------------------------------------------------- layer-level pins --
 def _small_layer(name="tiny", **kw):
     cfg = W.CONFIGS[name]

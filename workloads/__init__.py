@@ -137,7 +137,7 @@ CONFIGS: Dict[str, MoEConfig] = {
 _TAG = {"x": 1, "w_router": 2, "w_gate": 3, "w_up": 4, "w_down": 5,
         "ws_gate": 6, "ws_up": 7, "ws_down": 8, "w_shared_gate": 9,
         "lore_A": 10, "lore_B": 11, "resident": 12, "w_prefetch": 13,
-        "delta": 14, "w_delta": 15, "theta": 16, "x_prev": 17}
+        "delta": 14, "w_delta": 15, "theta": 16, "x_prev": 17, "calib": 18, "omega": 19}
 
 
 def _rng(seed: int, tag: str, idx: int = 0) -> np.random.Generator:
@@ -264,6 +264,26 @@ class Layer:
             self._cache[key] = self._to_storage((x + np.float32(c.prev_noise) * nz).astype(np.float32))
         full = self._cache[key]
         return full if T is None else full[:T]
+
+    def calibration(self, N: int) -> np.ndarray:
+        """LoRE calibration inputs: an orthogonal design of N = m*H rows, m
+        blocks of sqrt(H) * Q with Q the Q factor of an H x H N(0,1) draw, so
+        the rows have the norm of unit-variance hidden states and
+        h^T h = N I in fp32 before rounding to the storage dtype."""
+        H = self.cfg.hidden
+        if N % H:
+            raise ValueError("calibration size must be a multiple of hidden")
+        rng = _rng(self.seed, "calib")
+        blocks = []
+        for _ in range(N // H):
+            q, _ = np.linalg.qr(rng.standard_normal((H, H)))
+            blocks.append((q * np.sqrt(H)).astype(np.float32))
+        return self._to_storage(np.concatenate(blocks, axis=0))
+
+    def omega(self, cols: int) -> np.ndarray:
+        """Gaussian start block [H][cols] fp32 for the LoRE fit's subspace
+        iteration (the random numbers the method draws)."""
+        return _normal(_rng(self.seed, "omega"), (self.cfg.hidden, cols), 1.0)
 
     def w_router(self) -> np.ndarray:
         return self._small("w_router", (self.cfg.n_experts, self.cfg.hidden), self.cfg.weight_std)
