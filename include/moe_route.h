@@ -123,7 +123,7 @@ typedef struct {
 typedef enum {
   MOE_KERNEL_NONE = 0,
   MOE_KERNEL_ROUTE = 1,
-  MOE_KERNEL_PERMUTE = 2,
+  MOE_KERNEL_PERMUTE = 2,        /* runs inside ROUTE when T*k <= 1024 and E > 16 */
   MOE_KERNEL_EXPERT_GATE_UP = 3, /* routed + shared gate/up projections (+ SiLU product) */
   MOE_KERNEL_EXPERT_DOWN = 4,    /* routed + shared down projections                     */
   MOE_KERNEL_FLOE_UP = 5,        /* INT2 up projection                                   */

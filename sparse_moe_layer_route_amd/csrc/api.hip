@@ -11,7 +11,8 @@ namespace moe {
 hipError_t launch_route(const moe_dims_t& d, int T, const void* x, const void* w_router,
                         const uint64_t* resident, int64_t res_stride, int mode, int32_t* ids,
                         float* w, uint8_t* exact, uint32_t* flags, float* logits, float* mass,
-                        const void* w_sg, float* g_s, hipStream_t s);
+                        const void* w_sg, float* g_s, hipStream_t s, const PermOut* po = nullptr,
+                        bool* permuted = nullptr);
 hipError_t launch_pack_mfma16(int G, int R, int K, const void* src, void* dst, hipStream_t s);
 hipError_t launch_floe_predict(const moe_dims_t& d, int T, const void* h, const moe_weights_t& w,
                                const int32_t* offsets, const int32_t* perm, float* u,
@@ -134,6 +135,7 @@ moe_status_t check_weights(const moe_dims_t* d, const moe_weights_t* w, moe_mode
 // Workspace plan for T tokens.
 struct Plan {
   size_t ids, w, exact, flags, logits, offsets, moffsets, perm, inv, row_of, pscratch;  // routing + permutation
+  size_t counter;                                                     // router -> permutation handoff
   size_t y_perm, y_s, g_s;                                            // FFN outputs
   size_t act, act_s;                                                  // fp32 GEMV activations
   size_t act_b, acts_b, z_b;                                          // bf16 MFMA activations
@@ -169,6 +171,7 @@ Plan make_plan(const moe_dims_t& d, int T, moe_mode_t mode) {
   p.pscratch = take((size_t)permute_scratch_bytes((int)P, d.n_experts));
   p.inv = take(P * 4);
   p.row_of = take(P * 4);
+  p.counter = take(4);
   p.y_perm = take(P * H * 4);
   if (mode == MOE_MODE_FLOE) {
     p.u = take(P * I * 4);
@@ -513,15 +516,19 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, int32_t T, const void* x,
     pf.start = (hipEvent_t)dbg->prof_start;
     pf.stop = (hipEvent_t)dbg->prof_stop;
   }
+  // small batches are permuted by the router's top-k launch itself
+  const PermOut po{at<int32_t>(ws, p.counter), offsets, perm, inv, row_of, moffsets};
+  bool permuted = false;
   hipError_t e = pf.begin(MOE_KERNEL_ROUTE, s);
   if (e == hipSuccess)
     e = launch_route(d, T, x, w->w_router, resident, resident_stride, mode, ids, wts, exact, flags,
                      logits, dbg ? dbg->mass : nullptr,
-                     d.shared_gate ? w->w_shared_gate : nullptr, g_s, s);
+                     d.shared_gate ? w->w_shared_gate : nullptr, g_s, s, &po, &permuted);
   if (e == hipSuccess) e = pf.end(MOE_KERNEL_ROUTE, s);
   if (e == hipSuccess) e = pf.begin(MOE_KERNEL_PERMUTE, s);
-  if (e == hipSuccess) e = launch_permute(P, E, ids, exact, offsets, perm, inv, row_of, moffsets,
-                                           at<int32_t>(ws, p.pscratch), s);
+  if (e == hipSuccess && !permuted)
+    e = launch_permute(P, E, ids, exact, offsets, perm, inv, row_of, moffsets,
+                       at<int32_t>(ws, p.pscratch), s);
   if (e == hipSuccess) e = pf.end(MOE_KERNEL_PERMUTE, s);
   // When every expert row comes from the grouped GEMM (no LoRE rows), the
   // rows are kept as bf16: the combine sums them in fp32 and the bytes between

@@ -124,4 +124,12 @@ struct Prof {
   }
 };
 
+// Where the router's top-k launch writes the permutation when it also sorts
+// the (token, slot) pairs; counter is a workspace word the logits launch
+// zeroes and the top-k blocks count themselves in.
+struct PermOut {
+  int32_t* counter;
+  int32_t *offsets, *perm, *inv, *row_of, *miss_offsets;
+};
+
 }  // namespace moe

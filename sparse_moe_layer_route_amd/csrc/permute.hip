@@ -12,22 +12,9 @@
 // of the same bucket in the waves before it, so the order is stable and
 // deterministic with no order-dependent atomics.  Up to 1024 pairs the
 // histogram is taken inside the single scatter block (one launch).
-#include "common.h"
+#include "permute_block.h"
 
 namespace moe {
-
-constexpr int PERM_THREADS = 1024;
-constexpr int PERM_WAVES = PERM_THREADS / MOE_WAVE;
-constexpr int PERM_BUCKETS = 2 * MOE_MAX_EXPERTS;
-
-// Bucket of pair f: expert for exact pairs, E + expert for the others, -1
-// for out-of-range ids (never placed).  exact == nullptr: every pair exact.
-__device__ __forceinline__ int bucket_of(int f, int E, const int32_t* __restrict__ ids,
-                                         const uint8_t* __restrict__ exact) {
-  const int e = ids[f];
-  if ((unsigned)e >= (unsigned)E) return -1;
-  return (!exact || exact[f]) ? e : E + e;
-}
 
 // Histogram of chunk blockIdx.x into counts[blockIdx.x][2E].
 __global__ void __launch_bounds__(PERM_THREADS)
@@ -53,84 +40,8 @@ permute_kernel(int n_pairs, int E, const int32_t* __restrict__ ids, const uint8_
                const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ row_of,
                int32_t* __restrict__ miss_offsets) {
-  __shared__ int tot[PERM_BUCKETS];     // pairs per bucket over all chunks
-  __shared__ int before[PERM_BUCKETS];  // pairs per bucket in earlier chunks
-  __shared__ int cursor[PERM_BUCKETS];
-  __shared__ int wcnt[PERM_WAVES][PERM_BUCKETS];
-  __shared__ int s_total;
-  const int tid = threadIdx.x, lane = tid & (MOE_WAVE - 1), wv = tid >> 6;
-  const int NB = 2 * E;
-  const int chunk = blockIdx.x;
-  const int f = chunk * PERM_THREADS + tid;
-  const int b = f < n_pairs ? bucket_of(f, E, ids, exact) : -1;
-  if (counts) {
-    if (tid < NB) {
-      const int nchunks = gridDim.x;
-      int t = 0, bf = 0;
-      for (int c = 0; c < nchunks; ++c) {
-        const int v = counts[(int64_t)c * NB + tid];
-        t += v;
-        if (c < chunk) bf += v;
-      }
-      tot[tid] = t;
-      before[tid] = bf;
-    }
-  } else {
-    if (tid < PERM_BUCKETS) {
-      tot[tid] = 0;
-      before[tid] = 0;
-    }
-    __syncthreads();
-    if (b >= 0) atomicAdd(&tot[b], 1);
-  }
-  __syncthreads();
-  if (tid < MOE_WAVE) {
-    // two buckets per lane: 2*lane, 2*lane+1 (NB <= 128)
-    const int c0 = 2 * lane < NB ? tot[2 * lane] : 0;
-    const int c1 = 2 * lane + 1 < NB ? tot[2 * lane + 1] : 0;
-    const int c = c0 + c1;
-    int s = c;
-#pragma unroll
-    for (int o = 1; o < MOE_WAVE; o <<= 1) {
-      const int v = __shfl_up(s, o, MOE_WAVE);
-      if (lane >= o) s += v;
-    }
-    cursor[2 * lane] = s - c + (2 * lane < NB ? before[2 * lane] : 0);
-    cursor[2 * lane + 1] = s - c + c0 + (2 * lane + 1 < NB ? before[2 * lane + 1] : 0);
-    if (lane == MOE_WAVE - 1) s_total = s;
-    if (chunk == 0) {
-      // bucket bases (chunk 0 has nothing before it)
-      if (2 * lane <= E) offsets[2 * lane] = s - c;
-      if (2 * lane + 1 <= E) offsets[2 * lane + 1] = s - c + c0;
-    }
-  }
-  __syncthreads();
-  if (chunk == 0 && miss_offsets && tid <= E) miss_offsets[tid] = tid < E ? cursor[E + tid] : s_total;
-  const uint64_t below = (1ull << lane) - 1ull;
-  const int v = b + 1;  // 0..128
-  uint64_t peers = __ballot(1);
-#pragma unroll
-  for (int bit = 0; bit < 8; ++bit) {
-    const bool on = (v >> bit) & 1;
-    const uint64_t bal = __ballot(on);
-    peers &= on ? bal : ~bal;
-  }
-  const int rank = __popcll(peers & below);
-  wcnt[wv][lane] = 0;
-  wcnt[wv][lane + MOE_WAVE] = 0;
-  __builtin_amdgcn_wave_barrier();
-  if (b >= 0 && rank == 0) wcnt[wv][b] = __popcll(peers);
-  __syncthreads();
-  if (b >= 0) {
-    int pos = cursor[b] + rank;
-    for (int w2 = 0; w2 < wv; ++w2) pos += wcnt[w2][b];
-    perm[pos] = f;
-    inv[f] = b < E ? pos : -1;
-    if (row_of) row_of[f] = pos;
-  } else if (f < n_pairs) {
-    inv[f] = -1;
-    if (row_of) row_of[f] = -1;
-  }
+  permute_chunk(blockIdx.x, gridDim.x, n_pairs, E, ids, exact, counts, offsets, perm, inv, row_of,
+                miss_offsets);
 }
 
 int permute_scratch_bytes(int n_pairs, int E) {

@@ -23,7 +23,7 @@
 // experts and filling each miss with the best remaining prefetched expert is
 // the top-k of the router restricted to the prefetched set; the kernel takes
 // that masked top-k.
-#include "common.h"
+#include "permute_block.h"
 
 namespace moe {
 
@@ -142,7 +142,9 @@ constexpr int LOGIT_WAVES = ROUTE_LOGIT_WAVES;
 // logits [T][E].
 __global__ void __launch_bounds__(LOGIT_WAVES * MOE_WAVE)
 route_logits_kernel(const bf16* __restrict__ x, const bf16* __restrict__ w, int T, int H, int E,
-                    float* __restrict__ logits) {
+                    float* __restrict__ logits, int32_t* __restrict__ zero_me) {
+  // the top-k kernel that follows counts its finished blocks here
+  if (zero_me && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *zero_me = 0;
   __shared__ f32x4_t part[LOGIT_WAVES - 1][MOE_WAVE];
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   const int r16 = lane & 15, kg = lane >> 4;
@@ -190,8 +192,9 @@ route_logits_kernel(const bf16* __restrict__ x, const bf16* __restrict__ w, int 
 
 __global__ void __launch_bounds__(LOGIT_WAVES * MOE_WAVE)
 route_logits_kernel(const float* __restrict__ x, const float* __restrict__ w, int T, int H, int E,
-                    float* __restrict__ logits) {
+                    float* __restrict__ logits, int32_t* __restrict__ zero_me) {
   const int tid = threadIdx.x;
+  if (zero_me && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *zero_me = 0;
   if (tid >= 256) return;
   const int t = blockIdx.x * 16 + (tid >> 4), e = blockIdx.y * 16 + (tid & 15);
   if (t >= T || e >= E) return;
@@ -289,21 +292,40 @@ __device__ __forceinline__ void route_topk_token(
   }
 }
 
-// One wave per token (4 per block) on logits [T][E] from route_logits_kernel.
-template <typename Tin>
-__global__ void __launch_bounds__(256)
+// On logits [T][E] from route_logits_kernel: top-k of TPB tokens per block (one wave each).  TPB == PERM_WAVES (1024
+// threads): the batch's (token, slot) pairs are also permuted in this launch.
+template <typename Tin, int TPB>
+__global__ void __launch_bounds__(TPB * MOE_WAVE)
 route_topk_kernel(const Tin* __restrict__ x, const float* __restrict__ logits, int T, int H, int E,
                   int k, int renorm, float margin, int mode, const uint64_t* __restrict__ resident,
                   int64_t res_stride, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
                   uint8_t* __restrict__ exact, uint32_t* __restrict__ flags,
                   float* __restrict__ mass_out, const Tin* __restrict__ w_sg,
-                  float* __restrict__ g_s) {
+                  float* __restrict__ g_s, PermOut po) {
   const int lane = lane_id();
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float l = lane < E ? logits[(int64_t)t * E + lane] : -INFINITY;
-  route_topk_token<Tin>(t, l, x, H, E, k, renorm, margin, mode, resident, res_stride, topk_ids,
-                        topk_w, exact, flags, mass_out, w_sg, g_s);
+  const int t = blockIdx.x * TPB + (threadIdx.x >> 6);
+  if (t < T) {
+    const float l = lane < E ? logits[(int64_t)t * E + lane] : -INFINITY;
+    route_topk_token<Tin>(t, l, x, H, E, k, renorm, margin, mode, resident, res_stride, topk_ids,
+                          topk_w, exact, flags, mass_out, w_sg, g_s);
+  }
+  if constexpr (TPB == PERM_WAVES) {
+    // fused permutation (at most one 1024-pair chunk): the last block to
+    // finish its tokens sorts every pair; the logits kernel zeroed the count
+    // (one wave fences: the barrier has put every wave's stores in L2, and
+    // a device-scope fence writes back / invalidates whole caches)
+    __shared__ int s_last;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __threadfence();
+      s_last = atomicAdd(po.counter, 1) == (int)gridDim.x - 1;
+      if (s_last) __threadfence();
+    }
+    __syncthreads();
+    if (s_last)
+      permute_chunk(0, 1, T * k, E, topk_ids, exact, nullptr, po.offsets, po.perm, po.inv,
+                    po.row_of, po.miss_offsets);
+  }
 }
 
 // Small batches: logits and top-k in one launch.  A 1024-thread block takes
@@ -413,7 +435,9 @@ prefetch_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w_p, int T, i
 hipError_t launch_route(const moe_dims_t& d, int T, const void* x, const void* w_router,
                         const uint64_t* resident, int64_t res_stride, int mode, int32_t* ids,
                         float* w, uint8_t* exact, uint32_t* flags, float* logits, float* mass,
-                        const void* w_sg, float* g_s, hipStream_t s) {
+                        const void* w_sg, float* g_s, hipStream_t s, const PermOut* po,
+                        bool* permuted) {
+  if (permuted) *permuted = false;
   if (T <= ROUTE_FUSED_MAX_T && d.n_experts <= ROUTE_FUSED_MAX_E) {
     const int tpb = T <= ROUTE_FUSED_SMALL_T ? ROUTE_FUSED_SMALL_TPB : ROUTE_TOK;
     const int blocks = (T + tpb - 1) / tpb;
@@ -429,21 +453,35 @@ hipError_t launch_route(const moe_dims_t& d, int T, const void* x, const void* w
           mass, (const float*)w_sg, g_s);
     return hipGetLastError();
   }
+  // a batch of at most one permutation chunk is sorted by the top-k launch
+  const bool fuse = po != nullptr && (int64_t)T * d.top_k <= PERM_THREADS;
   const dim3 lgrid((T + 15) / 16, (d.n_experts + 15) / 16);
-  const int tblocks = (T + 3) / 4;
+  int32_t* zero_me = fuse ? po->counter : nullptr;
+  const PermOut none{};
   if (d.dtype == MOE_BF16) {
     route_logits_kernel<<<lgrid, LOGIT_WAVES * MOE_WAVE, 0, s>>>(
-        (const bf16*)x, (const bf16*)w_router, T, d.hidden, d.n_experts, logits);
-    route_topk_kernel<bf16><<<tblocks, 256, 0, s>>>(
-        (const bf16*)x, logits, T, d.hidden, d.n_experts, d.top_k, d.renormalize, d.tie_margin, mode,
-        resident, res_stride, ids, w, exact, flags, mass, (const bf16*)w_sg, g_s);
+        (const bf16*)x, (const bf16*)w_router, T, d.hidden, d.n_experts, logits, zero_me);
+    if (fuse)
+      route_topk_kernel<bf16, PERM_WAVES><<<(T + PERM_WAVES - 1) / PERM_WAVES, PERM_THREADS, 0, s>>>(
+          (const bf16*)x, logits, T, d.hidden, d.n_experts, d.top_k, d.renormalize, d.tie_margin,
+          mode, resident, res_stride, ids, w, exact, flags, mass, (const bf16*)w_sg, g_s, *po);
+    else
+      route_topk_kernel<bf16, 4><<<(T + 3) / 4, 256, 0, s>>>(
+          (const bf16*)x, logits, T, d.hidden, d.n_experts, d.top_k, d.renormalize, d.tie_margin,
+          mode, resident, res_stride, ids, w, exact, flags, mass, (const bf16*)w_sg, g_s, none);
   } else {
     route_logits_kernel<<<lgrid, LOGIT_WAVES * MOE_WAVE, 0, s>>>(
-        (const float*)x, (const float*)w_router, T, d.hidden, d.n_experts, logits);
-    route_topk_kernel<float><<<tblocks, 256, 0, s>>>(
-        (const float*)x, logits, T, d.hidden, d.n_experts, d.top_k, d.renormalize, d.tie_margin, mode,
-        resident, res_stride, ids, w, exact, flags, mass, (const float*)w_sg, g_s);
+        (const float*)x, (const float*)w_router, T, d.hidden, d.n_experts, logits, zero_me);
+    if (fuse)
+      route_topk_kernel<float, PERM_WAVES><<<(T + PERM_WAVES - 1) / PERM_WAVES, PERM_THREADS, 0, s>>>(
+          (const float*)x, logits, T, d.hidden, d.n_experts, d.top_k, d.renormalize, d.tie_margin,
+          mode, resident, res_stride, ids, w, exact, flags, mass, (const float*)w_sg, g_s, *po);
+    else
+      route_topk_kernel<float, 4><<<(T + 3) / 4, 256, 0, s>>>(
+          (const float*)x, logits, T, d.hidden, d.n_experts, d.top_k, d.renormalize, d.tie_margin,
+          mode, resident, res_stride, ids, w, exact, flags, mass, (const float*)w_sg, g_s, none);
   }
+  if (permuted) *permuted = fuse;
   return hipGetLastError();
 }
 
