@@ -280,6 +280,43 @@ moe_status_t moe_floe_pack(const moe_dims_t* dims, int32_t T, const int32_t* top
                            const int32_t* keep, const void* w_gate, const void* w_down,
                            void* gate_out, void* down_out, void* stream);
 
+/* LoRE fitting, step 1 [SPICE page, "LoRE low-rank surrogate": for each
+ * expert, collect its inputs h and outputs y_e and the shared experts'
+ * output]: resid_out [N][H] fp32 = y_e(h) - y_shared(h) for the N calibration
+ * rows h_cal [N][H] (dtype) and expert `expert`, computed by this library's
+ * expert and shared FFN kernels (as in moe_expert_ffn, the SwiGLU product
+ * rounded to dtype between the projections; y_shared ungated; 0 when
+ * n_shared = 0).  Reads the routed and shared matrices of w (either
+ * weight_layout) and requires w->w_router like every dense mode.  ws: at least
+ * moe_workspace_size(dims with top_k = 1, N, MOE_MODE_STANDARD) bytes. */
+moe_status_t moe_lore_targets(const moe_dims_t* dims, int32_t N, const void* h_cal,
+                              const moe_weights_t* w, int32_t expert, float* resid_out, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* Bytes of workspace moe_lore_fit needs (host output); MOE_EINVAL unless
+ * 1 <= rank <= cols <= min(64, hidden) and N > 0. */
+moe_status_t moe_lore_fit_size(int32_t hidden, int32_t N, int32_t rank, int32_t cols,
+                               size_t* bytes /* host */);
+
+/* LoRE fitting, step 2 [SPICE page, "LoRE low-rank surrogate": minimise
+ * ||y_e - y_shared - B_e A_e h||^2, solved with an SVD]: with R = resid
+ * [N][H] fp32 (moe_lore_targets) and the calibration rows h_cal [N][H] dtype
+ * taken as an orthogonal design (h^T h = N I), the least-squares map is
+ * M = R^T h / N; its rank-`rank` truncated SVD gives lore_A_out [rank][H]
+ * = V_r^T and lore_B_out [H][rank] = U_r S_r (dtype; for rank = dims.lore_rank
+ * these are expert e's slices of moe_weights_t.lore_A / lore_B), sigma_out
+ * [rank] fp32 the singular values (descending), err_out [1] fp32 the relative
+ * residual ||R - h (B A)^T||_F / ||R||_F of the fp32 factors.  The SVD is a
+ * subspace iteration of `n_iter` rounds (Y <- M M^T Y, orthonormalised) on
+ * `cols` columns (rank <= cols <= 64) started from omega [H][cols] fp32
+ * (the caller's random draw), then a Rayleigh-Ritz step.  ws: at least
+ * moe_lore_fit_size(H, N, rank, cols) bytes.  All buffers device, caller-owned. */
+moe_status_t moe_lore_fit(const moe_dims_t* dims, int32_t N, const void* h_cal,
+                          const float* resid, int32_t rank, int32_t cols, int32_t n_iter,
+                          const float* omega, void* lore_A_out, void* lore_B_out,
+                          float* sigma_out, float* err_out, void* ws, size_t ws_bytes,
+                          void* stream);
+
 /* LoRE residual [SPICE page, "LoRE low-rank surrogate"]: for each slot with
  * exact[t][j] == 0, lore_out[t][j] = B_e (A_e x_t) with A_e [r][H] and
  * B_e [H][r]; slots with exact == 1 get 0.  lore_out [T][k][H] fp32. */

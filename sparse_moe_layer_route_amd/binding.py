@@ -83,6 +83,9 @@ def _load():
         "moe_lore_surrogate": ([D, I32, P, P, P, P, P, P, P], ctypes.c_int),
         "moe_floe_predict": ([D, I32, P, Wp, P, P, P, P, SZ, P], ctypes.c_int),
         "moe_floe_pack": ([D, I32, P, P, P, P, P, P, P], ctypes.c_int),
+        "moe_lore_targets": ([D, I32, P, Wp, I32, P, P, SZ, P], ctypes.c_int),
+        "moe_lore_fit_size": ([I32, I32, I32, I32, ctypes.POINTER(SZ)], ctypes.c_int),
+        "moe_lore_fit": ([D, I32, P, P, I32, I32, I32, P, P, P, P, P, P, SZ, P], ctypes.c_int),
         "moe_combine": ([D, I32, P, P, P, P, P, P, P, P, P], ctypes.c_int),
         "moe_layer_forward": ([D, I32, P, Wp, P, I64, ctypes.c_int, P, Dbg, P, SZ, P], ctypes.c_int),
     }
@@ -96,7 +99,8 @@ def _load():
 _lib = _load()
 EXPORTED = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_route",
             "moe_prefetch_mask", "moe_prefetch_adaptive", "moe_pack_size", "moe_pack_weights",
-            "moe_permute", "moe_floe_predict", "moe_floe_pack", "moe_expert_ffn", "moe_lore_surrogate",
+            "moe_permute", "moe_floe_predict", "moe_floe_pack", "moe_lore_targets",
+            "moe_lore_fit_size", "moe_lore_fit", "moe_expert_ffn", "moe_lore_surrogate",
             "moe_combine", "moe_layer_forward")
 
 
@@ -240,6 +244,27 @@ def moe_floe_pack(dims, T, topk_ids, keep, w_gate, w_down, gate_out, down_out, s
     _check(_lib.moe_floe_pack(ctypes.byref(_dims(dims)), T, _ptr(topk_ids), _ptr(keep), _ptr(w_gate),
                               _ptr(w_down), _ptr(gate_out), _ptr(down_out), _stream(stream)),
            "moe_floe_pack")
+
+
+def moe_lore_targets(dims, N, h_cal, w, expert, resid_out, ws, stream=None):
+    ws_ = weights_struct(w) if isinstance(w, dict) else w
+    _check(_lib.moe_lore_targets(ctypes.byref(_dims(dims)), N, _ptr(h_cal), ctypes.byref(ws_), expert,
+                                 _ptr(resid_out), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_lore_targets")
+
+
+def moe_lore_fit_size(hidden, N, rank, cols) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.moe_lore_fit_size(hidden, N, rank, cols, ctypes.byref(n)), "moe_lore_fit_size")
+    return n.value
+
+
+def moe_lore_fit(dims, N, h_cal, resid, rank, cols, n_iter, omega, lore_A_out, lore_B_out,
+                 sigma_out, err_out, ws, stream=None):
+    _check(_lib.moe_lore_fit(ctypes.byref(_dims(dims)), N, _ptr(h_cal), _ptr(resid), rank, cols,
+                             n_iter, _ptr(omega), _ptr(lore_A_out), _ptr(lore_B_out),
+                             _ptr(sigma_out), _ptr(err_out), _ptr(ws), ws.numel(),
+                             _stream(stream)), "moe_lore_fit")
 
 
 def moe_permute(T, k, E, topk_ids, exact, expert_offsets, perm, inv, ws=None, stream=None):

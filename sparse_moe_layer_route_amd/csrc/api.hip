@@ -14,6 +14,12 @@ hipError_t launch_route(const moe_dims_t& d, int T, const void* x, const void* w
                         const void* w_sg, float* g_s, hipStream_t s, const PermOut* po = nullptr,
                         bool* permuted = nullptr);
 hipError_t launch_pack_mfma16(int G, int R, int K, const void* src, void* dst, hipStream_t s);
+int64_t lore_fit_ws_elems(int H, int N, int r, int s);
+hipError_t launch_lore_fit(const moe_dims_t& d, int N, const void* h, const float* R, int r, int s,
+                           int n_iter, const float* omega, void* A_out, void* B_out, float* sigma,
+                           float* err, float* ws, hipStream_t st);
+hipError_t launch_fit_route(int N, int E, int e, int32_t* offsets, int32_t* perm, hipStream_t st);
+hipError_t launch_fit_resid(const float* ye, const float* ys, int64_t n, float* R, hipStream_t st);
 hipError_t launch_floe_predict(const moe_dims_t& d, int T, const void* h, const moe_weights_t& w,
                                const int32_t* offsets, const int32_t* perm, float* u,
                                int32_t* keep, uint32_t* flags, hipStream_t s);
@@ -429,6 +435,62 @@ moe_status_t moe_floe_pack(const moe_dims_t* dims, int32_t T, const int32_t* top
   if (T == 0) return MOE_OK;
   return hip_status(launch_floe_pack(*dims, T, topk_ids, keep, w_gate, w_down, gate_out, down_out,
                                      (hipStream_t)stream));
+}
+
+moe_status_t moe_lore_targets(const moe_dims_t* dims, int32_t N, const void* h_cal,
+                              const moe_weights_t* w, int32_t expert, float* resid_out, void* ws,
+                              size_t ws_bytes, void* stream) {
+  moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (dims->up_format != MOE_UP_DENSE) return MOE_EUNSUPPORTED;
+  moe_dims_t d1 = *dims;
+  d1.top_k = 1;  // every calibration row goes to the one expert
+  if ((st = check_weights(&d1, w, MOE_MODE_STANDARD)) != MOE_OK) return st;
+  if (N < 0 || expert < 0 || expert >= dims->n_experts) return MOE_EINVAL;
+  if (N > kMaxTokens) return MOE_EUNSUPPORTED;
+  if (!ok_ptr(h_cal) || !ok_ptr(resid_out) || !ok_ptr(ws)) return MOE_EINVAL;
+  const Plan p = make_plan(d1, N, MOE_MODE_STANDARD);
+  if (ws_bytes < p.total) return MOE_EWORKSPACE;
+  if (N == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* offsets = at<int32_t>(ws, p.offsets);
+  int32_t* perm = at<int32_t>(ws, p.perm);
+  float* ye = at<float>(ws, p.y_perm);
+  float* ys = d1.n_shared > 0 ? at<float>(ws, p.y_s) : nullptr;
+  hipError_t e = launch_fit_route(N, d1.n_experts, expert, offsets, perm, s);
+  if (e == hipSuccess)
+    e = run_ffn(d1, N, h_cal, *w, MOE_MODE_STANDARD, offsets, at<int32_t>(ws, p.moffsets), perm, ye,
+                ys, nullptr, nullptr, ws, p, 0, Prof{}, s);
+  if (e == hipSuccess) e = launch_fit_resid(ye, ys, (int64_t)N * d1.hidden, resid_out, s);
+  return hip_status(e);
+}
+
+moe_status_t moe_lore_fit_size(int32_t hidden, int32_t N, int32_t rank, int32_t cols,
+                               size_t* bytes) {
+  if (!bytes || hidden <= 0 || N <= 0 || rank < 1 || cols < rank || cols > 64 || cols > hidden)
+    return MOE_EINVAL;
+  *bytes = (size_t)lore_fit_ws_elems(hidden, N, rank, cols) * 4;
+  return MOE_OK;
+}
+
+moe_status_t moe_lore_fit(const moe_dims_t* dims, int32_t N, const void* h_cal,
+                          const float* resid, int32_t rank, int32_t cols, int32_t n_iter,
+                          const float* omega, void* lore_A_out, void* lore_B_out,
+                          float* sigma_out, float* err_out, void* ws, size_t ws_bytes,
+                          void* stream) {
+  moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (N <= 0 || rank < 1 || cols < rank || cols > 64 || cols > dims->hidden || n_iter < 0 ||
+      n_iter > 1000)
+    return MOE_EINVAL;
+  if (N > kMaxTokens) return MOE_EUNSUPPORTED;
+  if (!ok_ptr(h_cal) || !ok_ptr(resid) || !ok_ptr(omega) || !ok_ptr(lore_A_out) ||
+      !ok_ptr(lore_B_out) || !ok_ptr(sigma_out) || !ok_ptr(err_out) || !ok_ptr(ws))
+    return MOE_EINVAL;
+  if (ws_bytes < (size_t)lore_fit_ws_elems(dims->hidden, N, rank, cols) * 4) return MOE_EWORKSPACE;
+  return hip_status(launch_lore_fit(*dims, N, h_cal, resid, rank, cols, n_iter, omega, lore_A_out,
+                                    lore_B_out, sigma_out, err_out, (float*)ws,
+                                    (hipStream_t)stream));
 }
 
 moe_status_t moe_lore_surrogate(const moe_dims_t* dims, int32_t T, const void* x,

@@ -156,6 +156,27 @@ def test_floe_predict_and_pack_host_checks():
     assert pk(ctypes.byref(fl), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.MOE_OK
 
 
+def test_lore_fit_host_checks():
+    n = ctypes.c_size_t(0)
+    assert L.moe_lore_fit_size(256, 512, 8, 16, ctypes.byref(n)) == B.MOE_OK and n.value > 256 * 256 * 4
+    for args in [(256, 512, 0, 16), (256, 512, 17, 16), (256, 512, 8, 65), (32, 64, 8, 48),
+                 (256, 0, 8, 16)]:
+        assert L.moe_lore_fit_size(*args, ctypes.byref(n)) == B.MOE_EINVAL
+    d = dims(dtype="bf16")
+    fit = L.moe_lore_fit
+    assert fit(ctypes.byref(d), 512, FAKE, FAKE, 8, 16, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16,
+               None) == B.MOE_EWORKSPACE
+    assert fit(ctypes.byref(d), 512, FAKE, None, 8, 16, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+               None) == B.MOE_EINVAL
+    assert fit(ctypes.byref(d), 512, FAKE, FAKE, 8, 4, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+               None) == B.MOE_EINVAL                                    # cols < rank
+    w = _weights()
+    tg = L.moe_lore_targets
+    assert tg(ctypes.byref(d), 64, FAKE, ctypes.byref(w), 8, FAKE, FAKE, 1 << 30, None) == B.MOE_EINVAL
+    assert tg(ctypes.byref(d), 64, FAKE, ctypes.byref(w), 1, FAKE, FAKE, 16, None) == B.MOE_EWORKSPACE
+    assert tg(ctypes.byref(d), 0, FAKE, ctypes.byref(w), 1, FAKE, FAKE, 1 << 30, None) == B.MOE_OK
+
+
 def test_entry_point_null_checks():
     d = dims()
     P = ctypes.c_void_p

@@ -430,6 +430,89 @@ def test_floe_pack_bit_exact(name, T):
             np.testing.assert_array_equal(gd_, wd)
 
 
+# ------------------------------------------------------------ LoRE fitting --
+def _fit_gpu(dims, h_np, R_np, dtype, r, cols, n_iter, omega):
+    N, H = R_np.shape
+    h = tensor(h_np, dtype, "cuda")
+    R = torch.from_numpy(np.ascontiguousarray(R_np, np.float32)).cuda()
+    om = torch.from_numpy(np.ascontiguousarray(omega, np.float32)).cuda()
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    A = torch.empty(r * H, dtype=tdt, device="cuda")
+    B = torch.empty(H * r, dtype=tdt, device="cuda")
+    sig = torch.empty(r, dtype=torch.float32, device="cuda")
+    err = torch.empty(4, dtype=torch.float32, device="cuda")
+    ws = torch.empty(M.moe_lore_fit_size(H, N, r, cols), dtype=torch.uint8, device="cuda")
+    M.moe_lore_fit(dims, N, h, R, r, cols, n_iter, om, A, B, sig, err, ws)
+    torch.cuda.synchronize()
+    return (A.float().cpu().numpy().reshape(r, H), B.float().cpu().numpy().reshape(H, r),
+            sig.cpu().numpy(), float(err[0].cpu()))
+
+
+def _orthogonal_rows(rng, N, H):
+    return np.concatenate([np.linalg.qr(rng.standard_normal((H, H)))[0] * np.sqrt(H)
+                           for _ in range(N // H)], axis=0)
+
+
+@pytest.mark.parametrize("H,N,r,cols", [(256, 512, 8, 16), (192, 384, 5, 24)])
+def test_lore_fit_planted_map(H, N, r, cols):
+    """Targets from a planted rank-r map plus small noise (well separated
+    singular values): the fitted B A, the singular values and the
+    calibration error match the oracle's truncated SVD."""
+    rng = np.random.default_rng(H + r)
+    h = _orthogonal_rows(rng, N, H).astype(np.float32)
+    U = np.linalg.qr(rng.standard_normal((H, r)))[0]
+    V = np.linalg.qr(rng.standard_normal((H, r)))[0]
+    M_true = (U * np.linspace(2.0, 1.0, r)) @ V.T
+    R = (h.astype(np.float64) @ M_true.T + 0.01 * rng.standard_normal((N, H))).astype(np.float32)
+    dims = M.Dims(hidden=H, n_experts=1, top_k=1, inter=16, dtype="f32")
+    omega = rng.standard_normal((H, cols)).astype(np.float32)
+    A, B, sig, err = _fit_gpu(dims, h, R, "f32", r, cols, 12, omega)
+    oA, oB, osig, oerr = O.lore_fit(h.astype(np.float64), R.astype(np.float64), r)
+    np.testing.assert_allclose(sig, osig, rtol=1e-4)
+    assert abs(err - oerr) < 1e-4, (err, oerr)
+    assert rel_fro(B @ A, oB @ oA) < 1e-4
+    np.testing.assert_allclose(A @ A.T, np.eye(r), atol=1e-4)
+
+
+def test_lore_targets_and_fit_on_an_expert():
+    """The whole fit for one expert of a small DeepSeek-V2-Lite-shaped layer:
+    targets y_e - y_s from the FFN kernels against the oracle's (bf16
+    activation rounding on the GPU side), then singular values and the
+    calibration error of rank-8 and rank-16 fits against the oracle's exact
+    SVD (the spectrum of random experts is flat, so the factors themselves
+    are only determined up to rotations within near-equal singular values and
+    are not compared)."""
+    layer = W.Layer(SMALL["dsv2_small"])
+    cfg = layer.cfg
+    N, e = 2 * cfg.hidden, 5
+    dims = M.Dims(**dims_dict(cfg))
+    h_np = layer.calibration(N)
+    h = O.decode(h_np, cfg.dtype)
+    D = lambda a: O.decode(a, cfg.dtype)
+    R_o = O.lore_targets(h, D(layer.expert("w_gate", e)), D(layer.expert("w_up", e)),
+                         D(layer.expert("w_down", e)), D(layer.full("ws_gate")), D(layer.full("ws_up")),
+                         D(layer.full("ws_down")))
+    wdev = dev_weights(layer)
+    d1 = dataclasses.replace(dims, top_k=1)
+    for layout, wts in (("rows", wdev), ("mfma16", packed_weights(layer))):
+        dl = dataclasses.replace(d1, weight_layout=layout)
+        ws = torch.empty(M.moe_workspace_size(dl, N, "standard"), dtype=torch.uint8, device="cuda")
+        R = torch.empty(N * cfg.hidden, dtype=torch.float32, device="cuda")
+        M.moe_lore_targets(dataclasses.replace(dims, weight_layout=layout), N,
+                           tensor(h_np, cfg.dtype, "cuda"), wts, e, R, ws)
+        torch.cuda.synchronize()
+        R_g = R.cpu().numpy().reshape(N, cfg.hidden)
+        say(f"    targets ({layout}): rel_fro {rel_fro(R_g, R_o):.2e}")
+        assert rel_fro(R_g, R_o) < 1e-2
+    omega = layer.omega(64)
+    for r in (8, 16):
+        _, _, sig, err = _fit_gpu(dims, h_np, R_g, cfg.dtype, r, 64, 20, omega)
+        _, _, osig, oerr = O.lore_fit(h, R_o, r)
+        say(f"    rank {r}: error {err:.4f} (oracle {oerr:.4f}), top sigma {sig[0]:.5f} ({osig[0]:.5f})")
+        np.testing.assert_allclose(sig, osig, rtol=5e-3)
+        assert abs(err - oerr) < 5e-3
+
+
 def test_permute_parity_random():
     rng = np.random.default_rng(7)
     for T, k, E, p_exact in [(1, 1, 1, 1.0), (37, 6, 64, 0.5), (4096, 8, 40, 1.0), (300, 8, 64, 0.0),
