@@ -441,6 +441,54 @@ def measure_floe_predict(steps, warmup, T=1, T_recall=8):
                 recall=recall, recall_tokens=T_recall, prev_noise=cfg.prev_noise)
 
 
+def measure_lore_fit(name="dsv2_lite", expert=0, ranks=(8, 16, 32), cols=64, n_iter=20):
+    """LoRE fitting for one expert of the named layer: targets y_e - y_s on an
+    orthogonal calibration design of H rows, then the rank-r fit for each r;
+    time per step and the relative calibration error per rank."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from workloads.device import dims_dict, tensor, upload
+    import sparse_moe_layer_route_amd as M
+
+    layer = W.make_layer(name)
+    cfg = layer.cfg
+    H, N = cfg.hidden, cfg.hidden
+    dims = M.Dims(**dims_dict(cfg))
+    w = upload(layer, "cuda")
+    h = tensor(layer.calibration(N), cfg.dtype, "cuda")
+    d1 = dataclasses.replace(dims, top_k=1)
+    ws = torch.empty(M.moe_workspace_size(d1, N, "standard"), dtype=torch.uint8, device="cuda")
+    R = torch.empty(N * H, dtype=torch.float32, device="cuda")
+    om = torch.from_numpy(np.ascontiguousarray(layer.omega(cols))).cuda()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    M.moe_lore_targets(dims, N, h, w, expert, R, ws)   # warm-up
+    torch.cuda.synchronize()
+    ev[0].record()
+    M.moe_lore_targets(dims, N, h, w, expert, R, ws)
+    ev[1].record()
+    torch.cuda.synchronize()
+    out = dict(workload=name, tokens=N, mode="lore_fit", expert=expert, cols=cols, n_iter=n_iter,
+               targets_ms=ev[0].elapsed_time(ev[1]), fits=[])
+    tdt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    for r in ranks:
+        A = torch.empty(r * H, dtype=tdt, device="cuda")
+        B = torch.empty(H * r, dtype=tdt, device="cuda")
+        sig = torch.empty(r, dtype=torch.float32, device="cuda")
+        err = torch.empty(4, dtype=torch.float32, device="cuda")
+        fws = torch.empty(M.moe_lore_fit_size(H, N, r, cols), dtype=torch.uint8, device="cuda")
+        M.moe_lore_fit(dims, N, h, R, r, cols, n_iter, om, A, B, sig, err, fws)
+        torch.cuda.synchronize()
+        ev[0].record()
+        M.moe_lore_fit(dims, N, h, R, r, cols, n_iter, om, A, B, sig, err, fws)
+        ev[1].record()
+        torch.cuda.synchronize()
+        out["fits"].append(dict(rank=r, ms=ev[0].elapsed_time(ev[1]), rel_error=float(err[0]),
+                                sigma_max=float(sig[0]), sigma_r=float(sig[r - 1])))
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -486,6 +534,12 @@ def main():
         print(f"# mixtral_floe T=1 FloE predictor: {r['predict_us']:.1f} us/call "
               f"({r['predict_gbs']:.0f} GB/s); compact pack {r['pack_us']:.1f} us "
               f"({r['pack_gbs']:.0f} GB/s); recall {r['recall']:.3f} over {r['recall_tokens']} tokens",
+              file=sys.stderr, flush=True)
+        r = measure_lore_fit()
+        also.append(r)
+        print(f"# dsv2_lite LoRE fit (expert 0, {r['tokens']} calibration rows): targets "
+              f"{r['targets_ms']:.2f} ms; " + "; ".join(
+                  f"rank {f['rank']}: {f['ms']:.1f} ms, error {f['rel_error']:.3f}" for f in r["fits"]),
               file=sys.stderr, flush=True)
     cpu = None if args.no_cpu else cpu_baseline(args.workload, args.tokens, args.mode)
     line = {

@@ -103,8 +103,9 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
-// Orthonormalises the s columns of Y [H][s] (row-major) in place by classical
-// Gram-Schmidt with one re-orthogonalisation pass; one 1024-thread workgroup.
+// Orthonormalises the s columns of Y, stored column after column ([s][H],
+// each column contiguous), in place by classical Gram-Schmidt with one
+// re-orthogonalisation pass; one 1024-thread workgroup.
 // A column whose remaining norm falls below 1e-6 of its original norm is
 // zeroed (the block then has numerical rank below s).
 constexpr int FIT_MAX_S = 64;
@@ -114,39 +115,43 @@ __global__ void __launch_bounds__(1024) fit_orth_kernel(float* __restrict__ Y, i
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   for (int j = 0; j < s; ++j) {
     float n0 = 0.f;
-    for (int i = tid; i < H; i += 1024) n0 += Y[(int64_t)i * s + j] * Y[(int64_t)i * s + j];
+    float* yj = Y + (int64_t)j * H;
+    for (int i = tid; i < H; i += 1024) n0 += yj[i] * yj[i];
     n0 = block_sum(n0, red);
     for (int pass = 0; pass < 2; ++pass) {
       // c_p = <q_p, y_j>, one wave per previous column
       for (int p = wv; p < j; p += 16) {
         float d = 0.f;
-        for (int i = lane; i < H; i += 64) d += Y[(int64_t)i * s + p] * Y[(int64_t)i * s + j];
+        const float* yp = Y + (int64_t)p * H;
+        for (int i = lane; i < H; i += 64) d += yp[i] * yj[i];
         d = wave_sum(d);
         if (lane == 0) coef[p] = d;
       }
       __syncthreads();
       for (int i = tid; i < H; i += 1024) {
-        float v = Y[(int64_t)i * s + j];
-        for (int p = 0; p < j; ++p) v -= coef[p] * Y[(int64_t)i * s + p];
-        Y[(int64_t)i * s + j] = v;
+        float v = yj[i];
+        for (int p = 0; p < j; ++p) v -= coef[p] * Y[(int64_t)p * H + i];
+        yj[i] = v;
       }
       __syncthreads();
     }
     float nr = 0.f;
-    for (int i = tid; i < H; i += 1024) nr += Y[(int64_t)i * s + j] * Y[(int64_t)i * s + j];
+    for (int i = tid; i < H; i += 1024) nr += yj[i] * yj[i];
     nr = block_sum(nr, red);
     const float inv = (nr > 1e-12f * n0 && nr > 0.f) ? 1.f / sqrtf(nr) : 0.f;
-    for (int i = tid; i < H; i += 1024) Y[(int64_t)i * s + j] *= inv;
+    for (int i = tid; i < H; i += 1024) yj[i] *= inv;
     __syncthreads();
   }
 }
 
 // Symmetric eigen-decomposition of T [s][s] by cyclic Jacobi rotations (each
 // rotation zeroes one off-diagonal pair: Golub & Van Loan, "Matrix
-// Computations", the cyclic Jacobi method), one 1024-thread workgroup.
-// Writes the eigenvalues in descending order to lam and the matching unit
-// eigenvectors as the columns of W [s][s].
-__global__ void __launch_bounds__(1024)
+// Computations", the cyclic Jacobi method), one wave (thread i owns row and
+// column i, so the rotations need only wave-level barriers).  Sweeps stop once
+// the off-diagonal mass is below 1e-10 of the diagonal's (squared norms), or
+// after max_sweeps.  Writes the eigenvalues in descending order to lam and
+// the matching unit eigenvectors as the columns of W [s][s].
+__global__ void __launch_bounds__(64)
 fit_jacobi_kernel(const float* __restrict__ Tin, int s, int max_sweeps, float* __restrict__ lam,
                   float* __restrict__ W) {
   __shared__ float T[FIT_MAX_S][FIT_MAX_S + 1];
@@ -155,22 +160,26 @@ fit_jacobi_kernel(const float* __restrict__ Tin, int s, int max_sweeps, float* _
   __shared__ float s_off, s_diag;
   __shared__ int order[FIT_MAX_S];
   const int tid = threadIdx.x;
-  for (int i = tid; i < s * s; i += 1024) {
+  for (int i = tid; i < s * s; i += 64) {
     const int r = i / s, c = i % s;
     T[r][c] = 0.5f * (Tin[r * s + c] + Tin[c * s + r]);
     V[r][c] = r == c ? 1.f : 0.f;
   }
   __syncthreads();
   for (int sweep = 0; sweep < max_sweeps; ++sweep) {
-    if (tid == 0) {
+    {
       float off = 0.f, dg = 0.f;
-      for (int r = 0; r < s; ++r)
-        for (int c = 0; c < s; ++c) (r == c ? dg : off) += T[r][c] * T[r][c];
-      s_off = off;
-      s_diag = dg;
+      if (tid < s)
+        for (int c = 0; c < s; ++c) (tid == c ? dg : off) += T[tid][c] * T[tid][c];
+      off = wave_sum(off);
+      dg = wave_sum(dg);
+      if (tid == 0) {
+        s_off = off;
+        s_diag = dg;
+      }
     }
     __syncthreads();
-    if (!(s_off > 1e-12f * s_diag)) break;
+    if (!(s_off > 1e-10f * s_diag)) break;
     for (int p = 0; p < s - 1; ++p) {
       for (int q = p + 1; q < s; ++q) {
         if (tid == 0) {
@@ -221,13 +230,14 @@ fit_jacobi_kernel(const float* __restrict__ Tin, int s, int max_sweeps, float* _
   }
   __syncthreads();
   if (tid < s) lam[tid] = T[order[tid]][order[tid]];
-  for (int i = tid; i < s * s; i += 1024) {
+  for (int i = tid; i < s * s; i += 64) {
     const int r = i / s, c = i % s;
     W[r * s + c] = V[r][order[c]];
   }
 }
 
-// B = U_r S_r as dtype [H][r] and fp32; sigma = sqrt(max(lam, 0)).
+// B = U_r S_r as dtype [H][r] and fp32 from U stored by columns ([s][H]);
+// sigma = sqrt(max(lam, 0)).
 template <typename Tout>
 __global__ void __launch_bounds__(256)
 fit_b_kernel(const float* __restrict__ U, int H, int s, int r, const float* __restrict__ lam,
@@ -236,7 +246,7 @@ fit_b_kernel(const float* __restrict__ U, int H, int s, int r, const float* __re
   if (blockIdx.x == 0 && threadIdx.x < r) sigma[threadIdx.x] = sqrtf(fmaxf(lam[threadIdx.x], 0.f));
   if (i >= (int64_t)H * r) return;
   const int h = (int)(i / r), j = (int)(i % r);
-  const float v = U[(int64_t)h * s + j] * sqrtf(fmaxf(lam[j], 0.f));
+  const float v = U[(int64_t)j * H + h] * sqrtf(fmaxf(lam[j], 0.f));
   Bf[i] = v;
   elem<Tout>::store(Bout, i, v);
 }
@@ -339,22 +349,22 @@ static hipError_t launch_lore_fit_t(int H, int N, const Tin* h, const float* R, 
   float* part = P + al((int64_t)N * H);
   // M = R^T h / N: M(a, b) = sum_n R[n][a] h[n][b]
   fit_gemm<float, Tin>(H, H, N, 1.f / (float)N, R, 1, H, h, H, 1, M, H, 1, st);
-  // Y = M omega
-  fit_gemm<float, float>(H, s, H, 1.f, M, H, 1, omega, s, 1, Y, s, 1, st);
+  // Y = M omega (Y, Z and U are stored by columns: element (h, j) at j*H + h)
+  fit_gemm<float, float>(H, s, H, 1.f, M, H, 1, omega, s, 1, Y, 1, H, st);
   fit_orth_kernel<<<1, 1024, 0, st>>>(Y, H, s);
   for (int it = 0; it < n_iter; ++it) {
     // Z = M^T Y, orthonormalised; Y = M Z, orthonormalised
-    fit_gemm<float, float>(H, s, H, 1.f, M, 1, H, Y, s, 1, Z, s, 1, st);
+    fit_gemm<float, float>(H, s, H, 1.f, M, 1, H, Y, 1, H, Z, 1, H, st);
     fit_orth_kernel<<<1, 1024, 0, st>>>(Z, H, s);
-    fit_gemm<float, float>(H, s, H, 1.f, M, H, 1, Z, s, 1, Y, s, 1, st);
+    fit_gemm<float, float>(H, s, H, 1.f, M, H, 1, Z, 1, H, Y, 1, H, st);
     fit_orth_kernel<<<1, 1024, 0, st>>>(Y, H, s);
   }
   // Rayleigh-Ritz: Bs = Y^T M [s][H], Tm = Bs Bs^T, eigenpairs (lam, Wv)
-  fit_gemm<float, float>(s, H, H, 1.f, Y, 1, s, M, H, 1, Bs, H, 1, st);
+  fit_gemm<float, float>(s, H, H, 1.f, Y, H, 1, M, H, 1, Bs, H, 1, st);
   fit_gemm<float, float>(s, s, H, 1.f, Bs, H, 1, Bs, 1, H, Tm, s, 1, st);
-  fit_jacobi_kernel<<<1, 1024, 0, st>>>(Tm, s, 60, lam, Wv);
+  fit_jacobi_kernel<<<1, 64, 0, st>>>(Tm, s, 30, lam, Wv);
   // U = Y Wv (into Z), B = U_r S_r; G = Wv^T Bs, A = S_r^-1 G_r
-  fit_gemm<float, float>(H, s, s, 1.f, Y, s, 1, Wv, s, 1, Z, s, 1, st);
+  fit_gemm<float, float>(H, s, s, 1.f, Y, 1, H, Wv, s, 1, Z, 1, H, st);
   fit_b_kernel<Tin><<<(unsigned)(((int64_t)H * r + 255) / 256), 256, 0, st>>>(Z, H, s, r, lam, Bf,
                                                                                 B_out, sigma);
   fit_gemm<float, float>(r, H, s, 1.f, Wv, 1, s, Bs, H, 1, G, H, 1, st);
