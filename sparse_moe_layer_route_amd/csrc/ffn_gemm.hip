@@ -334,7 +334,8 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   int cj = 0, ck = 0;   // compute position: tile, stage in tile
   TileMeta cm = dm;
   // a wave whose 64 tokens all lie past the segment end (the last m-tile of a
-  // segment) still moves its share of the stages but skips the MFMAs
+  // segment) still moves its share of the stages but skips its fragment reads
+  // and MFMAs
   bool tok_live = cm.row0 + wn * 16 * GTT < cm.n;
 
   f32x4_t acc[NW][WT][GTT];
@@ -431,7 +432,7 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
     const bool last = ++ck == nst;                                                      \
     GEMM_VMCNT_STAGES1();                                                               \
     __builtin_amdgcn_s_barrier();                                                       \
-    if (!last) GEMM_READ(FBn, FAn, (st_) + 1);                                          \
+    if (!last && tok_live) GEMM_READ(FBn, FAn, (st_) + 1);                              \
     const int kref = dma_next();                                                        \
     __builtin_amdgcn_sched_barrier(0); /* reads issue before the MFMAs */              \
     _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                    \
@@ -444,7 +445,7 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
       ck = 0;                                                                           \
       epilogue();                                                                       \
       next_compute_tile();                                                              \
-      GEMM_READ(FBn, FAn, (st_) + 1);                                                   \
+      if (tok_live) GEMM_READ(FBn, FAn, (st_) + 1);                                     \
     }                                                                                   \
     lds_wait_all(FBn, FAn);                                                             \
   }
@@ -458,7 +459,7 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
     }
     GEMM_VMCNT_STAGES2();
     __builtin_amdgcn_s_barrier();
-    GEMM_READ(fb0, fa0, 0);
+    if (tok_live) GEMM_READ(fb0, fa0, 0);
     lds_wait_all(fb0, fa0);
     for (int st = 0; st < S; st += 2) {
       GEMM_STEP(fb0, fa0, fb1, fa1, st);

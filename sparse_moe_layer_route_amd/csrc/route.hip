@@ -416,14 +416,20 @@ prefetch_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w_p, int T, i
   }
 }
 
-// Batches up to ROUTE_FUSED_MAX_T tokens route in one launch (logits and
-// top-k per block); larger ones spread the logits over (token, expert) tiles
-// first.  Tiny batches put fewer tokens in a block so more CUs share W_r.
+// Batches up to ROUTE_FUSED_MAX_T tokens with at most ROUTE_FUSED_MAX_E
+// experts route in one launch (logits and top-k per block); so do batches of
+// ROUTE_FUSED_BIG_T tokens or more, whose many blocks share the cost of
+// streaming W_r through each CU.  The rest spread the logits over (token,
+// expert) tiles first.  Tiny batches put fewer tokens in a block so more CUs
+// share W_r.
 #ifndef ROUTE_FUSED_MAX_T
 #define ROUTE_FUSED_MAX_T 256
 #endif
 #ifndef ROUTE_FUSED_MAX_E
 #define ROUTE_FUSED_MAX_E 16
+#endif
+#ifndef ROUTE_FUSED_BIG_T
+#define ROUTE_FUSED_BIG_T 2048
 #endif
 #ifndef ROUTE_FUSED_SMALL_T
 #define ROUTE_FUSED_SMALL_T 64
@@ -438,7 +444,7 @@ hipError_t launch_route(const moe_dims_t& d, int T, const void* x, const void* w
                         const void* w_sg, float* g_s, hipStream_t s, const PermOut* po,
                         bool* permuted) {
   if (permuted) *permuted = false;
-  if (T <= ROUTE_FUSED_MAX_T && d.n_experts <= ROUTE_FUSED_MAX_E) {
+  if ((T <= ROUTE_FUSED_MAX_T && d.n_experts <= ROUTE_FUSED_MAX_E) || T >= ROUTE_FUSED_BIG_T) {
     const int tpb = T <= ROUTE_FUSED_SMALL_T ? ROUTE_FUSED_SMALL_TPB : ROUTE_TOK;
     const int blocks = (T + tpb - 1) / tpb;
     if (d.dtype == MOE_BF16)
