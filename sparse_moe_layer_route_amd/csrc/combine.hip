@@ -187,16 +187,61 @@ combine_rows_kernel(int H, int k, const Ty* __restrict__ y_perm, const int32_t* 
   store4<Tin>(out + (int64_t)t * H + h, a0, a1, a2, a3);
 }
 
+// The same sums over bf16 rows with eight columns per thread (one 16-byte
+// load per slot row, one 16-byte store), in the same order and rounding as
+// combine_rows_kernel.
+template <typename Tin>
+__global__ void __launch_bounds__(COMBINE_THREADS)
+combine_rows8_kernel(int H, int k, const bf16* __restrict__ y_perm, const int32_t* __restrict__ row_of,
+                     const float* __restrict__ topk_w, const uint8_t* __restrict__ exact,
+                     const float* __restrict__ y_s, const float* __restrict__ g_s,
+                     Tin* __restrict__ out) {
+  const int t = blockIdx.x;
+  const int h = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
+  if (h >= H) return;
+  const float gs = g_s ? g_s[t] : 1.f;
+  float ys[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (y_s) elem<float>::load8(y_s + (int64_t)t * H + h, ys);
+  int row[MOE_MAX_TOPK];
+  uint4 v[MOE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    row[j] = j < k ? row_of[(int64_t)t * k + j] : -1;
+    v[j] = row[j] >= 0 ? *reinterpret_cast<const uint4*>(y_perm + (int64_t)row[j] * H + h)
+                       : make_uint4(0u, 0u, 0u, 0u);
+  }
+  float a[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) a[c] = gs * ys[c];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    if (row[j] < 0) continue;
+    const int64_t o = (int64_t)t * k + j;
+    const float wj = topk_w[o];
+    const float sj = exact[o] ? 0.f : 1.f;
+    const float f[8] = {bf16_lo(v[j].x), bf16_hi(v[j].x), bf16_lo(v[j].y), bf16_hi(v[j].y),
+                        bf16_lo(v[j].z), bf16_hi(v[j].z), bf16_lo(v[j].w), bf16_hi(v[j].w)};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) a[c] = fmaf(wj, fmaf(sj, ys[c], f[c]), a[c]);
+  }
+  store4<Tin>(out + (int64_t)t * H + h, a[0], a[1], a[2], a[3]);
+  store4<Tin>(out + (int64_t)t * H + h + 4, a[4], a[5], a[6], a[7]);
+}
+
 // y_bf16: y_perm holds bf16 rows.
 hipError_t launch_combine_rows(const moe_dims_t& d, int T, const void* y_perm, bool y_bf16,
                                const int32_t* row_of, const float* topk_w, const uint8_t* exact,
                                const float* y_s, const float* g_s, void* out, hipStream_t s) {
   const dim3 grid(T, (d.hidden + 4 * COMBINE_THREADS - 1) / (4 * COMBINE_THREADS));
   if (d.dtype == MOE_BF16) {
-    if (y_bf16)
-      combine_rows_kernel<bf16, bf16><<<grid, COMBINE_THREADS, 0, s>>>(
+    if (y_bf16) {
+      // eight columns per thread; blocks sized to the row (H % 64 == 0)
+      const int need = d.hidden / 8;
+      const int thr = need >= COMBINE_THREADS ? COMBINE_THREADS : ((need + 63) / 64) * 64;
+      const dim3 grid8(T, (need + thr - 1) / thr);
+      combine_rows8_kernel<bf16><<<grid8, thr, 0, s>>>(
           d.hidden, d.top_k, (const bf16*)y_perm, row_of, topk_w, exact, y_s, g_s, (bf16*)out);
-    else
+    } else
       combine_rows_kernel<bf16, float><<<grid, COMBINE_THREADS, 0, s>>>(
           d.hidden, d.top_k, (const float*)y_perm, row_of, topk_w, exact, y_s, g_s, (bf16*)out);
   } else {
