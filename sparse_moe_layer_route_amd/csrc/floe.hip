@@ -341,8 +341,8 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
   __shared__ int wsum[FLOE_SELECT_THREADS / MOE_WAVE];
   __shared__ uint32_t s_prefix;
   __shared__ int s_need;
-  __shared__ uint32_t s_next;
-  __shared__ int s_eqcnt;
+  __shared__ uint32_t s_next, s_kmin;
+  __shared__ int s_eqcnt, s_done;
   int f, t, e;
   if (!pair_of(blockIdx.x, E, k, offsets, perm, f, t, e)) return;
   const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
@@ -362,6 +362,8 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
     s_prefix = 0u;
     s_need = n_keep;
     s_next = 0u;
+    s_kmin = 0xFFFFFFFFu;
+    s_done = 0;
   }
   uint32_t pmask = 0u;
   for (int shift = 24; shift >= 0; shift -= 8) {
@@ -405,10 +407,14 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
         s_prefix = prefix | ((uint32_t)(4 * L + b) << shift);
         s_need = need - gt;
         s_eqcnt = hb[b];  // after the last pass: keys equal to the threshold
+        // every key of the chosen bin is kept: the bin's lower bound already
+        // separates kept from dropped keys, and the remaining passes can go
+        s_done = hb[b] == need - gt;
       }
     }
     pmask |= 0xFFu << shift;
     __syncthreads();
+    if (s_done) break;
   }
   const uint32_t thr = s_prefix;
   const int need_eq = s_need;
@@ -442,6 +448,19 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
       }
     }
   }
+  // smallest kept key (the threshold itself unless the passes stopped early)
+  {
+    uint32_t mn = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+      if (((kept >> j) & 1u) && key[j] < mn) mn = key[j];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint32_t v = __shfl_xor(mn, o, MOE_WAVE);
+      mn = v < mn ? v : mn;
+    }
+    if (lane == 0) atomicMin(&s_kmin, mn);
+  }
   int kept_total;
   int pos = block_excl_scan(__popc(kept), wsum, kept_total);
   int32_t* ko = keep_out + (int64_t)f * n_keep;
@@ -459,7 +478,7 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
     if (lane == 0) atomicMax(&s_next, m);
     __syncthreads();
     if (tid == 0) {
-      const bool tie = eq_total > need_eq || (__uint_as_float(thr) - __uint_as_float(s_next)) < margin;
+      const bool tie = eq_total > need_eq || (__uint_as_float(s_kmin) - __uint_as_float(s_next)) < margin;
       if (tie) atomicOr(&flags[t], 8u);
     }
   }

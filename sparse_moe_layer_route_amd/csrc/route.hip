@@ -331,7 +331,8 @@ route_topk_kernel(const Tin* __restrict__ x, const float* __restrict__ logits, i
 // Small batches: logits and top-k in one launch.  A 1024-thread block takes
 // tpb tokens (<= 16): its 16 waves form the logits of a 16-row token tile on
 // the matrix cores (rows past tpb belong to the next block and go unused),
-// then wave j ranks token t0 + j.
+// then wave j ranks token t0 + j.  po.perm != nullptr (a single block and at
+// most 1024 pairs): the block then permutes the batch's pairs itself.
 template <typename Tin>
 __global__ void __launch_bounds__(1024)
 route_fused_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w_router, int T, int H,
@@ -340,17 +341,23 @@ route_fused_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w_router, 
                    int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
                    uint8_t* __restrict__ exact, uint32_t* __restrict__ flags,
                    float* __restrict__ logits_out, float* __restrict__ mass_out,
-                   const Tin* __restrict__ w_sg, float* __restrict__ g_s) {
+                   const Tin* __restrict__ w_sg, float* __restrict__ g_s, PermOut po) {
   __shared__ RouteLds lds;
   const int t0 = blockIdx.x * tpb;
   tile_logits(x, w_router, T, H, E, t0, lds);
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   const int t = t0 + wv;
-  if (wv >= tpb || t >= T) return;
-  const float l = lane < E ? lds.logits[wv][lane] : -INFINITY;
-  if (lane < E) logits_out[(int64_t)t * E + lane] = l;
-  route_topk_token<Tin>(t, l, x, H, E, k, renorm, margin, mode, resident, res_stride, topk_ids,
-                        topk_w, exact, flags, mass_out, w_sg, g_s);
+  if (wv < tpb && t < T) {
+    const float l = lane < E ? lds.logits[wv][lane] : -INFINITY;
+    if (lane < E) logits_out[(int64_t)t * E + lane] = l;
+    route_topk_token<Tin>(t, l, x, H, E, k, renorm, margin, mode, resident, res_stride, topk_ids,
+                          topk_w, exact, flags, mass_out, w_sg, g_s);
+  }
+  if (po.perm) {  // block-uniform; the barrier orders the waves' writes within the workgroup
+    __syncthreads();
+    permute_chunk(0, 1, T * k, E, topk_ids, exact, nullptr, po.offsets, po.perm, po.inv,
+                  po.row_of, po.miss_offsets);
+  }
 }
 
 // APEX prefetch set: top-(k + delta_t) of x W_p^T as a bit mask.  ADAPT:
@@ -447,16 +454,21 @@ hipError_t launch_route(const moe_dims_t& d, int T, const void* x, const void* w
   if ((T <= ROUTE_FUSED_MAX_T && d.n_experts <= ROUTE_FUSED_MAX_E) || T >= ROUTE_FUSED_BIG_T) {
     const int tpb = T <= ROUTE_FUSED_SMALL_T ? ROUTE_FUSED_SMALL_TPB : ROUTE_TOK;
     const int blocks = (T + tpb - 1) / tpb;
+    // one block holding every token also permutes the (<= 1024) pairs
+    const bool fuse = po != nullptr && blocks == 1 && (int64_t)T * d.top_k <= PERM_THREADS;
+    PermOut pp{};
+    if (fuse) pp = *po;
     if (d.dtype == MOE_BF16)
       route_fused_kernel<bf16><<<blocks, 1024, 0, s>>>(
           (const bf16*)x, (const bf16*)w_router, T, d.hidden, d.n_experts, tpb, d.top_k,
           d.renormalize, d.tie_margin, mode, resident, res_stride, ids, w, exact, flags, logits,
-          mass, (const bf16*)w_sg, g_s);
+          mass, (const bf16*)w_sg, g_s, pp);
     else
       route_fused_kernel<float><<<blocks, 1024, 0, s>>>(
           (const float*)x, (const float*)w_router, T, d.hidden, d.n_experts, tpb, d.top_k,
           d.renormalize, d.tie_margin, mode, resident, res_stride, ids, w, exact, flags, logits,
-          mass, (const float*)w_sg, g_s);
+          mass, (const float*)w_sg, g_s, pp);
+    if (permuted) *permuted = fuse;
     return hipGetLastError();
   }
   // a batch of at most one permutation chunk is sorted by the top-k launch
