@@ -56,6 +56,12 @@ SMALL = {
                          seed=108),
     # 65-128 tokens with the shared experts on the decode kernels: eight
     # 16-token tiles, two row strips x two k-splits per block
+    # prefetch router and budget model on an fp32 layer, and on the full
+    # DeepSeek-V2-Lite shape (64 experts: every lane of the ranking wave live)
+    "f32_prefetch": _variant("tiny", name="f32_prefetch", n_experts=16, prefetch=True,
+                             token_counts=(23,), seed=109),
+    "dsv2_prefetch": _variant("dsv2_lite", name="dsv2_prefetch", prefetch=True,
+                              token_counts=(64,), seed=110),
     "dsv2_t100": _variant("dsv2_lite", name="dsv2_t100", hidden=512, n_experts=16, top_k=4,
                           inter=384, shared_inter=256, token_counts=(100,), resident_count=8,
                           seed=107),
@@ -213,7 +219,8 @@ def _oracle_routed(layer, X, k):
 
 
 @pytest.mark.parametrize("name,T", [("granite_prefill", 4096), ("granite_small", 203),
-                                    ("granite_small", 37)])
+                                    ("granite_small", 37), ("f32_prefetch", 23),
+                                    ("dsv2_prefetch", 64)])
 def test_prefetch_adaptive_parity(name, T):
     """Adaptive budget, list, delta* and overlap against the oracle, every
     token: exact where neither side flags a near-tie; at a budget near-tie
