@@ -237,7 +237,40 @@ def measure(name, T, mode, steps, warmup, ev=None, want_roofline=False):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = t_start.elapsed_time(t_stop) / steps
+    # eager step-time distribution: a second pass with events around every step
+    se = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        se[i][0].record()
+        step(i)
+        se[i][1].record()
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) * 1e3 for a, b in se)
+    pick = lambda q: per[min(len(per) - 1, int(q * (len(per) - 1) + 0.5))]
+    # HIP graph replay: one graph holding one step per weight copy, replayed
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(n_copies):
+            step(i)
+    reps = max(1, steps // n_copies)
+    g.replay()
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(reps):
+        g.replay()
+    t_stop.record()
+    torch.cuda.synchronize()
+    g_ms = t_start.elapsed_time(t_stop) / (reps * n_copies)
+    del g
     r = dict(workload=name, tokens=T, mode=mode, ms_per_step=ms, tokens_per_s=T / (ms * 1e-3),
+             step_us=dict(p10=pick(0.1), p50=pick(0.5), p90=pick(0.9)),
+             graph=dict(ms_per_step=g_ms, tokens_per_s=T / (g_ms * 1e-3)),
              wall_ms_per_step=wall * 1e3 / steps, weight_copies=n_copies,
              step_bytes=tr["bytes"], step_flops=tr["flops"],
              step_gbs=tr["bytes"] / (ms * 1e-3) / 1e9,
@@ -520,7 +553,8 @@ def main():
             r = measure(name, T, mode, steps, min(args.warmup, 5), ev=ev)
             also.append(r)
             print(f"# {name} T={T} {mode}: {r['ms_per_step']*1e3:.1f} us/step "
-                  f"(wall {r['wall_ms_per_step']*1e3:.1f} us) "
+                  f"(wall {r['wall_ms_per_step']*1e3:.1f} us, graph {r['graph']['ms_per_step']*1e3:.1f} us, "
+                  f"p50 {r['step_us']['p50']:.1f} us) "
                   f"{r['tokens_per_s']:.0f} tok/s, {r['step_gbs']:.0f} GB/s"
                   + (f", {r['roofline']['kernel']} {r['roofline']['frac']*100:.1f}% of {r['roofline']['bound']}"
                      if 'roofline' in r else ""), file=sys.stderr, flush=True)
@@ -560,6 +594,8 @@ def main():
                    "step_bytes": head["step_bytes"], "step_gbs": head["step_gbs"],
                    "step_hbm_frac": head["step_hbm_frac"]},
         "roofline": head.get("roofline"),
+        "step_us": head["step_us"],
+        "graph": head["graph"],
         "cpu_baseline": cpu,
         "also": also,
     }

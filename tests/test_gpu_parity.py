@@ -520,6 +520,57 @@ def test_lore_targets_and_fit_on_an_expert():
         assert abs(err - oerr) < 5e-3
 
 
+# --------------------------------------------------------- graph capture --
+@pytest.mark.parametrize("name,mode,layout", [("dsv2_small", "lore", "mfma16"),
+                                              ("dsv2_prefetch", "standard", "mfma16"),
+                                              ("granite_small", "stall_free", "rows"),
+                                              ("tiny", "lore", "rows")])
+def test_graph_replay_matches_eager(name, mode, layout):
+    """One moe_layer_forward captured in a HIP graph (torch.cuda.CUDAGraph on
+    the library's stream argument) and replayed three times, with eager work
+    and synchronisations in between: every replay's output equals the eager
+    call's bit for bit (the forward records kernels and no memset nodes)."""
+    layer = W.make_layer(name) if name in W.CONFIGS else W.Layer(SMALL[name])
+    cfg = layer.cfg
+    T = cfg.t_max
+    dd = dims_dict(cfg)
+    dims = M.Dims(**dd, weight_layout=layout)
+    wdev = packed_weights(layer) if layout == "mfma16" else dev_weights(layer)
+    x = tensor(layer.x(T), cfg.dtype, "cuda")
+    if mode == "lore":
+        res, stride = mask_tensor([layer.resident()], "cuda"), 0
+    elif mode == "stall_free":
+        _, _, res = prefetch_masks_gpu(layer, T, dev_weights(layer))
+        stride = 1
+    else:
+        res, stride = None, 0
+    ws = torch.empty(M.moe_workspace_size(dims, T, mode), dtype=torch.uint8, device="cuda")
+    odt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    eager = torch.empty(T, cfg.hidden, dtype=odt, device="cuda")
+    M.moe_layer_forward(dims, T, x, wdev, res, stride, mode, eager, ws)
+    torch.cuda.synchronize()
+    ref = eager.clone()
+    out = torch.zeros_like(eager)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        M.moe_layer_forward(dims, T, x, wdev, res, stride, mode, out, ws)  # warm-up on the side
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        M.moe_layer_forward(dims, T, x, wdev, res, stride, mode, out, ws)
+    for rep in range(3):
+        out.zero_()
+        eager.zero_()
+        M.moe_layer_forward(dims, T, x, wdev, res, stride, mode, eager, ws)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), (name, mode, rep)
+        assert torch.equal(eager, ref), (name, mode, rep)
+
+
 def test_permute_parity_random():
     rng = np.random.default_rng(7)
     for T, k, E, p_exact in [(1, 1, 1, 1.0), (37, 6, 64, 0.5), (4096, 8, 40, 1.0), (300, 8, 64, 0.0),
