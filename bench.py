@@ -347,9 +347,17 @@ def cpu_baseline(name, T, mode, budget_s=10.0):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")),
+                         model)
+    except OSError:
+        pass
     return dict(value=S * calls / total, unit="tokens/s", cores=int(cores), kind="oracle",
                 sample=f"first {S} of the {T} tokens of the same {name} layer in mode {mode}, "
-                       f"{calls} fp64 NumPy oracle call(s), {total:.1f} s in total")
+                       f"{calls} fp64 NumPy oracle call(s), {total:.1f} s in total",
+                cpu_model=model, host_cpus=len(os.sched_getaffinity(0)))
 
 
 def measure_prefetch_adaptive(name, T, steps, warmup, tau=0.9):
