@@ -222,9 +222,13 @@ def pack_weights(dims: "Dims", w: Dict[str, torch.Tensor], stream=None) -> Dict[
     """A copy of the weight dict with the routed and shared expert matrices
     packed fragment-major (moe_pack_weights); use it with
     dataclasses.replace(dims, weight_layout="mfma16")."""
+    if dims.dtype != "bf16":
+        raise ValueError("the fragment-major layout holds bf16 weights only")
     out = dict(w)
     for name, (g, r, c) in _packed_shapes(dims).items():
         src = w[name]
+        if src.element_size() != 2:
+            raise ValueError(f"{name}: expected 2-byte (bf16) elements")
         if src.numel() != g * r * c:
             raise ValueError(f"{name}: expected {g}x{r}x{c} elements, got {src.numel()}")
         dst = torch.empty(moe_pack_size(g, r, c) // 2, dtype=src.dtype, device=src.device)

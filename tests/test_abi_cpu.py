@@ -134,6 +134,17 @@ def test_pack_size_and_checks():
     assert L.moe_pack_weights(1, 16, 12, FAKE, FAKE + 4096, None) == B.MOE_EINVAL  # cols % 8
 
 
+def test_pack_weights_binding_rejects_non_bf16():
+    import torch
+    d32 = M.Dims(hidden=256, n_experts=8, top_k=2, inter=512, dtype="f32")
+    with pytest.raises(ValueError):
+        M.pack_weights(d32, {})
+    d16 = M.Dims(hidden=256, n_experts=8, top_k=2, inter=512, dtype="bf16")
+    w = {"w_gate": torch.zeros(8 * 512 * 256, dtype=torch.float32)}
+    with pytest.raises(ValueError):
+        M.pack_weights(d16, w)
+
+
 def test_floe_predict_and_pack_host_checks():
     fl = dims(dtype="bf16", up_format="int2_g64", floe_keep=16, n_shared=0, shared_inter=0)
     w = _weights()
