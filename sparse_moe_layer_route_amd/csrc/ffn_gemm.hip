@@ -490,11 +490,15 @@ ksplit_reduce_kernel(const float* __restrict__ part, int64_t n4, int64_t stride,
 }
 
 // k-splits of the shared experts' down GEMM: enough blocks to cover the CUs
-// when there are few (token, row) tiles and a long contraction.
+// when there are few (token, row) tiles and a long contraction, but no more
+// than one block per CU: the grid's x extent is the tile count rounded up to
+// the XCD count, and a block fills its CU, so a grid past 256 blocks runs a
+// second round (14 tiles split 18 ways took two rounds; split 16 ways, one).
 int gemm_shared_down_ksplit(const moe_dims_t& d, int T) {
   const int tiles = ((T + GN - 1) / GN) * ((d.hidden + 255) / 256);
   const int nst = d.n_shared * (d.shared_inter / GK);
-  int ks = 256 / (tiles > 0 ? tiles : 1);
+  const int gx = ((std::max(tiles, 1) + NXCD - 1) / NXCD) * NXCD;
+  int ks = 256 / gx;
   ks = ks < 1 ? 1 : (ks > nst ? nst : ks);
   return ks;
 }
