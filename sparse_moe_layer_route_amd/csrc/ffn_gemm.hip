@@ -140,33 +140,69 @@ __device__ __forceinline__ int seg_table_build(const GemmArgs& a, SegTable& t) {
   return __builtin_amdgcn_readlane(incl, MOE_WAVE - 1);
 }
 
-// One (m-tile, weight-tile) pair: group, first row in the segment, segment
-// rows and start, weight-row tile.
+// One (m-tile, weight-tile) pair, or half of one: group, first row in the
+// segment, the end of its live rows (segment rows, capped at the tile's
+// span), segment start, weight-row tile.
 struct TileMeta {
-  int g, row0, n, seg0, n_idx;
+  int g, row0, lim, seg0, n_idx;
 };
 constexpr int GEMM_MAX_TILES = 16;  // tiles per persistent block (the grid grows beyond)
 struct TileTable {
-  int g[GEMM_MAX_TILES], row0[GEMM_MAX_TILES], n[GEMM_MAX_TILES], seg0[GEMM_MAX_TILES],
+  int g[GEMM_MAX_TILES], row0[GEMM_MAX_TILES], lim[GEMM_MAX_TILES], seg0[GEMM_MAX_TILES],
       n_idx[GEMM_MAX_TILES];
 };
 
-// Lane j of the calling wave fills entry j (tile t0 + j * stride) from the
+// How an XCD's tiles are dealt to its blocks.  The `cnt` tiles from `base`
+// go round-robin to the `nbx` blocks, `full` whole rounds and then `rem`
+// tiles.  When that last, partial round holds at most half as many tiles as
+// there are blocks, each of its tiles is split into two 128-token halves, a
+// block apiece: a half keeps only the waves of its 128 tokens (one per SIMD)
+// busy and takes a little over half a tile's time, so the round no longer
+// costs a whole tile while half the CUs idle.  Either way every output
+// element is formed by the same MFMA sequence, so results do not change.
+struct TileDeal {
+  int base, full, rem;
+  bool split;
+};
+__device__ __forceinline__ TileDeal tile_deal(int n_tiles, int per_x, int xcd, int nbx) {
+  TileDeal d;
+  d.base = xcd * per_x;
+  const int cnt = max(0, min(n_tiles, d.base + per_x) - d.base);
+  d.full = cnt / nbx;
+  d.rem = cnt % nbx;
+  d.split = d.rem > 0 && 2 * d.rem <= nbx;
+  return d;
+}
+__device__ __forceinline__ int tile_count(const TileDeal& d, int bi, int nbx) {
+  if (d.split) return d.full + (bi < 2 * d.rem ? 1 : 0);
+  const int cnt = d.full * nbx + d.rem;
+  return bi < cnt ? (cnt - bi + nbx - 1) / nbx : 0;
+}
+
+// Lane j of the calling wave fills entry j of block bi's tiles from the
 // published segment table.
-__device__ __forceinline__ void tile_table_build(const GemmArgs& a, const SegTable& sg, int t0,
-                                                 int stride, int count, TileTable& tt) {
+__device__ __forceinline__ void tile_table_build(const GemmArgs& a, const SegTable& sg,
+                                                 const TileDeal& d, int bi, int nbx, int count,
+                                                 TileTable& tt) {
   const int j = lane_id();
   if (j >= count) return;
-  const int t = t0 + j * stride;
+  int t, half = -1;
+  if (d.split && j == d.full) {
+    t = d.base + d.full * nbx + bi / 2;
+    half = bi & 1;
+  } else {
+    t = d.base + bi + j * nbx;
+  }
   const int m_idx = t / a.tiles_n;
   int g = 0;
   for (int e = 0; e < a.G; ++e) {
     const int tiles = (sg.n[e] + GN - 1) / GN;
     if (m_idx >= sg.excl[e] && m_idx < sg.excl[e] + tiles) g = e;
   }
+  const int row0 = (m_idx - sg.excl[g]) * GN + (half > 0 ? GN / 2 : 0);
   tt.g[j] = g;
-  tt.row0[j] = (m_idx - sg.excl[g]) * GN;
-  tt.n[j] = sg.n[g];
+  tt.row0[j] = row0;
+  tt.lim[j] = min(sg.n[g], row0 + (half >= 0 ? GN / 2 : GN));
   tt.seg0[j] = sg.o0[g];
   tt.n_idx[j] = t % a.tiles_n;
 }
@@ -175,7 +211,7 @@ __device__ __forceinline__ TileMeta tile_get(const TileTable& tt, int j) {
   TileMeta m;
   m.g = __builtin_amdgcn_readfirstlane(tt.g[j]);
   m.row0 = __builtin_amdgcn_readfirstlane(tt.row0[j]);
-  m.n = __builtin_amdgcn_readfirstlane(tt.n[j]);
+  m.lim = __builtin_amdgcn_readfirstlane(tt.lim[j]);
   m.seg0 = __builtin_amdgcn_readfirstlane(tt.seg0[j]);
   m.n_idx = __builtin_amdgcn_readfirstlane(tt.n_idx[j]);
   return m;
@@ -227,11 +263,11 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   // this block's tiles: XCD x owns a contiguous range, dealt to its blocks
   const int nbx = gridDim.x / NXCD, xcd = blockIdx.x % NXCD, bi = blockIdx.x / NXCD;
   const int per_x = (n_tiles + NXCD - 1) / NXCD;
-  const int t_lo = xcd * per_x + bi, t_hi = min(n_tiles, (xcd + 1) * per_x);
-  const int n_my = t_lo < t_hi ? (t_hi - t_lo + nbx - 1) / nbx : 0;
+  const TileDeal deal = tile_deal(n_tiles, per_x, xcd, nbx);
+  const int n_my = tile_count(deal, bi, nbx);
   if (n_my == 0) return;
   __shared__ TileTable tt;
-  if (threadIdx.x < MOE_WAVE) tile_table_build(a, seg, t_lo, nbx, n_my, tt);
+  if (threadIdx.x < MOE_WAVE) tile_table_build(a, seg, deal, bi, nbx, n_my, tt);
   __syncthreads();
   // element offset of every token row of every tile of this block, gathered
   // up front so the stream never waits on the permutation mid-flight
@@ -241,7 +277,7 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
     for (int j = 0; j < n_my; ++j) {
       const TileMeta m = tile_get(tt, j);
       for (int r = threadIdx.x; r < GN; r += GTHREADS) {
-        const int rr = min(m.row0 + r, m.n - 1);
+        const int rr = min(m.row0 + r, m.lim - 1);   // rows past the live ones repeat the last
         const int tok = GATED ? (a.offsets ? a.perm[m.seg0 + rr] / a.k : rr) : m.seg0 + rr;
         tok_base[j][r] = tok * ld;
       }
@@ -333,10 +369,10 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   // compute state: the tile whose stages the MFMAs consume
   int cj = 0, ck = 0;   // compute position: tile, stage in tile
   TileMeta cm = dm;
-  // a wave whose 64 tokens all lie past the segment end (the last m-tile of a
-  // segment) still moves its share of the stages but skips its fragment reads
-  // and MFMAs
-  bool tok_live = cm.row0 + wn * 16 * GTT < cm.n;
+  // a wave whose 64 tokens all lie past the tile's live rows (the last m-tile
+  // of a segment, the upper half of a tile split in two) still moves its
+  // share of the stages but skips its fragment reads and MFMAs
+  bool tok_live = cm.row0 + wn * 16 * GTT < cm.lim;
 
   f32x4_t acc[NW][WT][GTT];
 #pragma unroll
@@ -353,7 +389,7 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < GTT; ++j) {
       const int tr = cm.row0 + wn * 16 * GTT + 16 * j + r16;   // token row within segment
-      if (tr >= cm.n) continue;
+      if (tr >= cm.lim) continue;
 #pragma unroll
       for (int i = 0; i < WT; ++i) {
         const int wr = row_w0 + wm * (MW / 2) + 16 * i + 4 * kg;
@@ -386,7 +422,7 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
     ++cj;
     if (cj < n_my) {
       cm = tile_get(tt, cj);
-      tok_live = cm.row0 + wn * 16 * GTT < cm.n;
+      tok_live = cm.row0 + wn * 16 * GTT < cm.lim;
     }
   };
 

@@ -46,15 +46,33 @@ __device__ __forceinline__ void permute_chunk(int chunk, int nchunks, int n_pair
   const int f = chunk * PERM_THREADS + tid;
   const int b = f < n_pairs ? bucket_of(f, E, ids, exact) : -1;
   if (counts) {
-    if (tid < NB) {
-      int t = 0, bf = 0;
-      for (int c = 0; c < nchunks; ++c) {
-        const int v = counts[(int64_t)c * NB + tid];
+    // bucket sums over the chunks' histograms: thread (g, bucket) adds
+    // chunks g, g + 8, ... with its loads in flight together, then the
+    // eight partial sums of a bucket are added (integers: any order is exact)
+    constexpr int NG = PERM_THREADS / PERM_BUCKETS;
+    __shared__ int ptot[NG][PERM_BUCKETS], pbef[NG][PERM_BUCKETS];
+    const int bk = tid % PERM_BUCKETS, g = tid / PERM_BUCKETS;
+    int t = 0, bf = 0;
+    if (bk < NB) {
+#pragma unroll 4
+      for (int c = g; c < nchunks; c += NG) {
+        const int v = counts[(int64_t)c * NB + bk];
         t += v;
-        if (c < chunk) bf += v;
+        bf += c < chunk ? v : 0;
       }
-      tot[tid] = t;
-      before[tid] = bf;
+    }
+    ptot[g][bk] = t;
+    pbef[g][bk] = bf;
+    __syncthreads();
+    if (tid < NB) {
+      int st = 0, sb = 0;
+#pragma unroll
+      for (int q = 0; q < NG; ++q) {
+        st += ptot[q][tid];
+        sb += pbef[q][tid];
+      }
+      tot[tid] = st;
+      before[tid] = sb;
     }
   } else {
     if (tid < PERM_BUCKETS) {
