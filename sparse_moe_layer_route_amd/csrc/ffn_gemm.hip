@@ -272,15 +272,21 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   // element offset of every token row of every tile of this block, gathered
   // up front so the stream never waits on the permutation mid-flight
   __shared__ int tok_base[GEMM_MAX_TILES][GN];
-  {
+  static_assert(GN <= GTHREADS, "one token row per thread");
+  if (threadIdx.x < GN) {
     const int ld = GATED ? a.K : (int)a.ld_in;
-    for (int j = 0; j < n_my; ++j) {
-      const TileMeta m = tile_get(tt, j);
-      for (int r = threadIdx.x; r < GN; r += GTHREADS) {
+    const int r = threadIdx.x;
+    for (int j0 = 0; j0 < n_my; j0 += 4) {   // four tiles' permutation loads in flight
+      int tok[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const TileMeta m = tile_get(tt, min(j0 + u, n_my - 1));
         const int rr = min(m.row0 + r, m.lim - 1);   // rows past the live ones repeat the last
-        const int tok = GATED ? (a.offsets ? a.perm[m.seg0 + rr] / a.k : rr) : m.seg0 + rr;
-        tok_base[j][r] = tok * ld;
+        tok[u] = GATED ? (a.offsets ? a.perm[m.seg0 + rr] / a.k : rr) : m.seg0 + rr;
       }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (j0 + u < n_my) tok_base[j0 + u][r] = tok[u] * ld;
     }
   }
   __syncthreads();

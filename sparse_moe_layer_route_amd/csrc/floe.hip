@@ -349,8 +349,21 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
   const int ch = (I + FLOE_SELECT_THREADS - 1) / FLOE_SELECT_THREADS;
   const int i0 = tid * ch;
   const float* ur = u + (int64_t)blockIdx.x * I;
-  // coalesced global reads into LDS, then each thread takes its chunk
-  for (int i = tid; i < I; i += FLOE_SELECT_THREADS) stage[i] = __float_as_uint(fabsf(ur[i]));
+  // coalesced global reads into LDS (all of a thread's loads in flight
+  // together), then each thread takes its chunk
+  {
+    float v[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int i = tid + j * FLOE_SELECT_THREADS;
+      v[j] = i < I ? ur[i] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int i = tid + j * FLOE_SELECT_THREADS;
+      if (i < I) stage[i] = __float_as_uint(fabsf(v[j]));
+    }
+  }
   __syncthreads();
   uint32_t key[CH];
 #pragma unroll

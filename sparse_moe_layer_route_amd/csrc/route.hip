@@ -78,25 +78,21 @@ __device__ __forceinline__ void tile_logits(const bf16* __restrict__ x, const bf
     const bool live = e < E;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     const int ksteps = H >> 5;
-    int ks = sp;
-    for (; ks + 3 * n_sp < ksteps; ks += 4 * n_sp) {
+    // k steps sp, sp + n_sp, ... in batches of four loads in flight; steps
+    // past the end load the last step again and multiply zeros
+    for (int ks = sp; ks < ksteps; ks += 4 * n_sp) {
       bf16x8_t a[4], b[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        a[u] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(xr + ((ks + u * n_sp) << 5)));
-        b[u] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(wr + ((ks + u * n_sp) << 5)));
+        const int kk = min(ks + u * n_sp, ksteps - 1) << 5;
+        a[u] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(xr + kk));
+        b[u] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(wr + kk));
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (!live) b[u] = __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
+        if (!live || ks + u * n_sp >= ksteps) b[u] = __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u], acc, 0, 0, 0);
       }
-    }
-    for (; ks < ksteps; ks += n_sp) {
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(xr + (ks << 5)));
-      bf16x8_t b = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(wr + (ks << 5)));
-      if (!live) b = __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
     }
     // accumulator: rows (tokens) 4*kg+i, column (expert) r16
 #pragma unroll
@@ -214,13 +210,26 @@ route_logits_kernel(const float* __restrict__ x, const float* __restrict__ w, in
 
 template <typename Tin>
 __device__ __forceinline__ float wave_dot(const Tin* __restrict__ a, const Tin* __restrict__ b, int H) {
+  // a lane's 8-element chunks in ascending order, four loads in flight at a
+  // time (chunks past H are neither loaded nor added)
+  constexpr int STEP = 8 * MOE_WAVE;
   float acc = 0.f;
-  for (int h = lane_id() * 8; h < H; h += 8 * MOE_WAVE) {
-    float a8[8], b8[8];
-    elem<Tin>::load8(a + h, a8);
-    elem<Tin>::load8(b + h, b8);
+  for (int h0 = lane_id() * 8; h0 < H; h0 += 4 * STEP) {
+    float a8[4][8], b8[4][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc = fmaf(a8[j], b8[j], acc);
+    for (int u = 0; u < 4; ++u) {
+      if (h0 + u * STEP < H) {
+        elem<Tin>::load8(a + h0 + u * STEP, a8[u]);
+        elem<Tin>::load8(b + h0 + u * STEP, b8[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (h0 + u * STEP < H) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc = fmaf(a8[u][j], b8[u][j], acc);
+      }
+    }
   }
   return wave_sum(acc);
 }
