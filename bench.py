@@ -60,6 +60,11 @@ COPY_BYTES = 256 << 20         # copy-probe size: 256 MiB read + 256 MiB written
 # sources the counted kernel was built from; a digest mismatch means the kernel
 # changed since the counters were taken and the figure no longer applies.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_expert_gate_up_dsv2_lite_T64_lore.md")
+TRAFFIC_FILES = {
+    ("dsv2_lite", 64, "lore"): TRAFFIC_FILE,
+    ("granite_prefill", 4096, "standard"): os.path.join(
+        ROOT, "profiles", "traffic_expert_gate_up_granite_prefill_T4096.md"),
+}
 
 
 def kernel_digest(files):
@@ -291,7 +296,8 @@ def measure(name, T, mode, steps, warmup, ev=None, want_roofline=False):
             roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                         frac=achieved / HBM_PEAK_GBS)
         traffic = None
-        rec = recorded_traffic() if (name, T, mode) == ("dsv2_lite", 64, "lore") else None
+        tf = TRAFFIC_FILES.get((name, T, mode))
+        rec = recorded_traffic(tf) if tf else None
         if rec is not None and kernel_digest(rec[1]) == rec[2]:
             traffic = rec[0]
         roof.update(traffic=traffic, kernel=dom, avg_us=avg_us, bytes_per_launch=up["bytes"],
