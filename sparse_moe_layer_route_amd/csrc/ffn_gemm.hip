@@ -156,8 +156,9 @@ struct TileTable {
 // go round-robin to the `nbx` blocks, `full` whole rounds and then `rem`
 // tiles.  When that last, partial round holds at most half as many tiles as
 // there are blocks, each of its tiles is split into two 128-token halves, a
-// block apiece: a half keeps only the waves of its 128 tokens (one per SIMD)
-// busy and takes a little over half a tile's time, so the round no longer
+// block apiece: a half keeps only the four waves of its 128 tokens busy
+// (waves 0-3, one per SIMD when waves are dealt to the SIMDs in turn) and
+// measured a little over half a tile's time, so the round no longer
 // costs a whole tile while half the CUs idle.  Either way every output
 // element is formed by the same MFMA sequence, so results do not change.
 struct TileDeal {
