@@ -19,7 +19,7 @@ from workloads.device import dims_dict, mask_tensor, tensor
 
 pytestmark = pytest.mark.gpu
 
-if not torch.cuda.is_available():  # the -m gpu suite runs on the GPU machine
+if not torch.cuda.is_available():  # the -m gpu suite needs a GPU
     pytest.skip("no GPU", allow_module_level=True)
 
 import sparse_moe_layer_route_amd as M  # noqa: E402
