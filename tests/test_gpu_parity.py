@@ -662,41 +662,52 @@ def test_exact_ties_go_to_lower_id():
         assert 7 not in g.ids[t] or 0 in g.ids[t]
 
 
-def test_unfused_entry_points_match_fused():
+@pytest.mark.parametrize("name,mode", [("qwen2_small", "lore"), ("prefill_small", "standard"),
+                                       ("prefill_small", "lore")])
+def test_unfused_entry_points_match_fused(name, mode):
     """route -> permute -> expert_ffn -> lore_surrogate -> combine matches
-    moe_layer_forward."""
-    layer = W.Layer(SMALL["qwen2_small"])
+    moe_layer_forward: on the decode kernels (qwen2_small) and on the grouped
+    GEMM with the shared experts' k-split (prefill_small), where the unfused
+    expert_ffn writes fp32 rows and the fused standard forward bf16 rows."""
+    layer = W.Layer(SMALL[name])
+    say(f"[unfused] {name} {mode}")
     cfg = layer.cfg
     T, k, E, H = cfg.t_max, cfg.top_k, cfg.n_experts, cfg.hidden
     dims = M.Dims(**dims_dict(cfg))
     wdev = dev_weights(layer)
     x = tensor(layer.x(T), "bf16", "cuda")
-    res = mask_tensor([layer.resident()], "cuda")
+    res = mask_tensor([layer.resident()], "cuda") if mode == "lore" else None
     ids = torch.empty(T * k, dtype=torch.int32, device="cuda")
     w = torch.empty(T * k, dtype=torch.float32, device="cuda")
     ex = torch.empty(T * k, dtype=torch.uint8, device="cuda")
     fl = torch.empty(T, dtype=torch.int32, device="cuda")
     lg = torch.empty(T * E, dtype=torch.float32, device="cuda")
-    M.moe_route(dims, T, x, wdev["w_router"], res, 0, "lore", ids, w, ex, fl, lg)
+    M.moe_route(dims, T, x, wdev["w_router"], res, 0, mode, ids, w, ex, fl, lg)
     off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
     perm = torch.empty(T * k, dtype=torch.int32, device="cuda")
     inv = torch.empty(T * k, dtype=torch.int32, device="cuda")
     M.moe_permute(T, k, E, ids, ex, off, perm, inv)
-    ws = torch.empty(M.moe_workspace_size(dims, T, "lore"), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(M.moe_workspace_size(dims, T, mode), dtype=torch.uint8, device="cuda")
     y = torch.empty(T * k, H, dtype=torch.float32, device="cuda")
     ys = torch.empty(T, H, dtype=torch.float32, device="cuda")
     gs = torch.empty(T, dtype=torch.float32, device="cuda")
-    M.moe_expert_ffn(dims, T, x, wdev, "lore", off, perm, y, ys, gs, ws)
+    M.moe_expert_ffn(dims, T, x, wdev, mode, off, perm, y, ys, gs, ws)
     lo = torch.empty(T, k, H, dtype=torch.float32, device="cuda")
     M.moe_lore_surrogate(dims, T, x, ids, ex, wdev["lore_A"], wdev["lore_B"], lo)
     out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
     M.moe_combine(dims, T, y, inv, w, ex, ys, gs, lo, out)
     torch.cuda.synchronize()
-    fused = run_layer(layer, T, "lore", wdev=wdev)
+    fused = run_layer(layer, T, mode, wdev=wdev)
     # same decisions; the fused path computes B_e A_e x on the matrix cores
-    # and the unfused one with vector FMAs, so outputs agree to rounding
+    # and the unfused one with vector FMAs, and rounds GEMM rows to bf16 when
+    # no surrogate row follows, so outputs agree to rounding
     np.testing.assert_array_equal(ids.cpu().numpy().reshape(T, k), fused.ids)
-    assert rel_fro(out.float().cpu().numpy(), fused.out) <= 2e-3
+    err = rel_fro(out.float().cpu().numpy(), fused.out)
+    say(f"    rel_fro={err:.3e}")
+    # bf16 GEMM rows in the fused forward: one more rounding of each routed
+    # row, at most 2^-9 relative per element, on top of the output's own
+    tol = 2.0 ** -8 if (name, mode) == ("prefill_small", "standard") else 2e-3
+    assert err <= tol
 
 
 def test_zero_tokens_enqueue_nothing():
