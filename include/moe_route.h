@@ -29,6 +29,9 @@
  *     MOE_BF16) applies to x, every dense weight, LoRE factors and out.
  *   - Limits: E <= 64, 1 <= k <= min(8, E), H % 64 == 0, I % 16 == 0,
  *     lore_rank <= 64, T >= 0 (T = 0 enqueues nothing and returns MOE_OK).
+ *     Element offsets on the GPU are 32-bit: T * k * max(H, I, n_shared * I_s)
+ *     and each expert matrix (I * H, I_s * H) must stay below 2^31, and
+ *     T <= 2^22; larger batches are split by the caller (MOE_EUNSUPPORTED).
  *
  * Decisions.  Every ranking orders experts by (-logit, id) -- ties go to the
  * lower expert id -- and FloE channels by (-|u|, channel).  A token whose

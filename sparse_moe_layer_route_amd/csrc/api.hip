@@ -3,6 +3,7 @@
 // synchronises; every check runs before the first enqueue.
 #include <string.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "common.h"
@@ -77,6 +78,15 @@ using namespace moe;
 namespace {
 
 constexpr int32_t kMaxTokens = 1 << 22;
+
+// Kernels form element offsets into token-major buffers (x, the routed and
+// shared activations, y_perm) in 32 bits, so each such buffer must hold fewer
+// than 2^31 elements: T * top_k * max(hidden, inter, n_shared * shared_inter).
+inline bool tokens_fit(const moe_dims_t& d, int64_t T) {
+  const int64_t wide = std::max<int64_t>(
+      {(int64_t)d.hidden, (int64_t)d.inter, (int64_t)d.n_shared * d.shared_inter});
+  return T <= kMaxTokens && T * d.top_k * wide < (int64_t(1) << 31);
+}
 // FloE kernels index (token, expert) pairs on a grid dimension capped at 65535
 constexpr int64_t kFloeMaxPairs = 65535;
 
@@ -95,6 +105,10 @@ moe_status_t check_dims(const moe_dims_t* d) {
   if (d->n_experts > MOE_MAX_EXPERTS || d->top_k > MOE_MAX_TOPK || d->top_k > d->n_experts)
     return MOE_EUNSUPPORTED;
   if (d->hidden % 64 != 0 || d->inter % 16 != 0) return MOE_EUNSUPPORTED;
+  // one expert matrix is indexed with 32-bit element offsets
+  if ((int64_t)d->inter * d->hidden >= (int64_t(1) << 31) ||
+      (int64_t)d->shared_inter * d->hidden >= (int64_t(1) << 31))
+    return MOE_EUNSUPPORTED;
   if (d->n_shared > 0 && (d->shared_inter <= 0 || d->shared_inter % 16 != 0)) return MOE_EUNSUPPORTED;
   if (d->lore_rank > MOE_MAX_LORE_RANK || d->lore_rank % 8 != 0) return MOE_EUNSUPPORTED;
   if (d->weight_layout != MOE_LAYOUT_ROWS && d->weight_layout != MOE_LAYOUT_MFMA16)
@@ -272,7 +286,7 @@ moe_status_t moe_workspace_size(const moe_dims_t* dims, int32_t T, moe_mode_t mo
   if (st != MOE_OK) return st;
   if ((st = check_mode(dims, mode)) != MOE_OK) return st;
   if (!bytes || T < 0) return MOE_EINVAL;
-  if (T > kMaxTokens) return MOE_EUNSUPPORTED;
+  if (!tokens_fit(*dims, T)) return MOE_EUNSUPPORTED;
   *bytes = make_plan(*dims, T, mode).total;
   return MOE_OK;
 }
@@ -285,7 +299,7 @@ moe_status_t moe_route(const moe_dims_t* dims, int32_t T, const void* x, const v
   if (st != MOE_OK) return st;
   if (mode < MOE_MODE_STANDARD || mode > MOE_MODE_FLOE) return MOE_EINVAL;
   if (T < 0) return MOE_EINVAL;
-  if (T > kMaxTokens) return MOE_EUNSUPPORTED;
+  if (!tokens_fit(*dims, T)) return MOE_EUNSUPPORTED;
   if (!ok_ptr(x) || !ok_ptr(w_router) || !ok_ptr(topk_ids) || !ok_ptr(topk_w) || !ok_ptr(exact) ||
       !ok_ptr(flags) || !ok_ptr(logits) || !ok_opt(mass_opt))
     return MOE_EINVAL;
@@ -304,7 +318,7 @@ moe_status_t moe_prefetch_mask(const moe_dims_t* dims, int32_t T, const void* x,
   moe_status_t st = check_dims(dims);
   if (st != MOE_OK) return st;
   if (T < 0) return MOE_EINVAL;
-  if (T > kMaxTokens) return MOE_EUNSUPPORTED;
+  if (!tokens_fit(*dims, T)) return MOE_EUNSUPPORTED;
   if (!ok_ptr(x) || !ok_ptr(w_prefetch) || !ok_ptr(delta) || !ok_ptr(mask_out) || !ok_ptr(flags))
     return MOE_EINVAL;
   if (T == 0) return MOE_OK;
@@ -337,7 +351,7 @@ moe_status_t moe_prefetch_adaptive(const moe_dims_t* dims, int32_t T, const void
   moe_status_t st = check_dims(dims);
   if (st != MOE_OK) return st;
   if (T < 0 || !(tau > 0.f && tau < 1.f)) return MOE_EINVAL;
-  if (T > kMaxTokens) return MOE_EUNSUPPORTED;
+  if (!tokens_fit(*dims, T)) return MOE_EUNSUPPORTED;
   if (!ok_ptr(x) || !ok_ptr(w_prefetch) || !ok_ptr(w_delta) || !ok_ptr(theta) ||
       !ok_ptr(delta_out) || !ok_ptr(mask_out) || !ok_ptr(flags))
     return MOE_EINVAL;
@@ -377,7 +391,7 @@ moe_status_t moe_expert_ffn(const moe_dims_t* dims, int32_t T, const void* x,
   if ((st = check_mode(dims, mode)) != MOE_OK) return st;
   if ((st = check_weights(dims, w, mode)) != MOE_OK) return st;
   if (T < 0) return MOE_EINVAL;
-  if (T > kMaxTokens) return MOE_EUNSUPPORTED;
+  if (!tokens_fit(*dims, T)) return MOE_EUNSUPPORTED;
   if (!ok_ptr(x) || !ok_ptr(expert_offsets) || !ok_ptr(perm) || !ok_ptr(y_perm) || !ok_ptr(ws))
     return MOE_EINVAL;
   if (dims->n_shared > 0 && (!ok_ptr(y_shared) || !ok_ptr(shared_gate))) return MOE_EINVAL;
@@ -447,7 +461,7 @@ moe_status_t moe_lore_targets(const moe_dims_t* dims, int32_t N, const void* h_c
   d1.top_k = 1;  // every calibration row goes to the one expert
   if ((st = check_weights(&d1, w, MOE_MODE_STANDARD)) != MOE_OK) return st;
   if (N < 0 || expert < 0 || expert >= dims->n_experts) return MOE_EINVAL;
-  if (N > kMaxTokens) return MOE_EUNSUPPORTED;
+  if (!tokens_fit(*dims, N)) return MOE_EUNSUPPORTED;
   if (!ok_ptr(h_cal) || !ok_ptr(resid_out) || !ok_ptr(ws)) return MOE_EINVAL;
   const Plan p = make_plan(d1, N, MOE_MODE_STANDARD);
   if (ws_bytes < p.total) return MOE_EWORKSPACE;
@@ -483,7 +497,7 @@ moe_status_t moe_lore_fit(const moe_dims_t* dims, int32_t N, const void* h_cal,
   if (N <= 0 || rank < 1 || cols < rank || cols > 64 || cols > dims->hidden || n_iter < 0 ||
       n_iter > 1000)
     return MOE_EINVAL;
-  if (N > kMaxTokens) return MOE_EUNSUPPORTED;
+  if (!tokens_fit(*dims, N)) return MOE_EUNSUPPORTED;
   if (!ok_ptr(h_cal) || !ok_ptr(resid) || !ok_ptr(omega) || !ok_ptr(lore_A_out) ||
       !ok_ptr(lore_B_out) || !ok_ptr(sigma_out) || !ok_ptr(err_out) || !ok_ptr(ws))
     return MOE_EINVAL;
@@ -500,7 +514,7 @@ moe_status_t moe_lore_surrogate(const moe_dims_t* dims, int32_t T, const void* x
   if (st != MOE_OK) return st;
   if (dims->lore_rank == 0) return MOE_EUNSUPPORTED;
   if (T < 0) return MOE_EINVAL;
-  if (T > kMaxTokens) return MOE_EUNSUPPORTED;
+  if (!tokens_fit(*dims, T)) return MOE_EUNSUPPORTED;
   if (!ok_ptr(x) || !ok_ptr(topk_ids) || !ok_ptr(exact) || !ok_ptr(lore_A) || !ok_ptr(lore_B) ||
       !ok_ptr(lore_out))
     return MOE_EINVAL;
@@ -515,7 +529,7 @@ moe_status_t moe_combine(const moe_dims_t* dims, int32_t T, const float* y_perm,
   moe_status_t st = check_dims(dims);
   if (st != MOE_OK) return st;
   if (T < 0) return MOE_EINVAL;
-  if (T > kMaxTokens) return MOE_EUNSUPPORTED;
+  if (!tokens_fit(*dims, T)) return MOE_EUNSUPPORTED;
   if (!ok_ptr(y_perm) || !ok_ptr(inv) || !ok_ptr(topk_w) || !ok_ptr(exact) || !ok_ptr(out) ||
       !ok_opt(y_shared) || !ok_opt(shared_gate) || !ok_opt(lore_out))
     return MOE_EINVAL;
@@ -534,7 +548,7 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, int32_t T, const void* x,
   if ((st = check_mode(dims, mode)) != MOE_OK) return st;
   if ((st = check_weights(dims, w, mode)) != MOE_OK) return st;
   if (T < 0) return MOE_EINVAL;
-  if (T > kMaxTokens) return MOE_EUNSUPPORTED;
+  if (!tokens_fit(*dims, T)) return MOE_EUNSUPPORTED;
   if (mode == MOE_MODE_FLOE && (int64_t)T * dims->top_k > kFloeMaxPairs) return MOE_EUNSUPPORTED;
   if (!ok_ptr(x) || !ok_ptr(out) || !ok_ptr(ws)) return MOE_EINVAL;
   const bool needs_mask = mode == MOE_MODE_LORE || mode == MOE_MODE_STALL_FREE;

@@ -114,6 +114,20 @@ def test_layer_forward_host_checks():
     assert fwd(d, 0, w, FAKE, 0, 1, FAKE, FAKE, need) == B.MOE_OK
 
 
+def test_32bit_offset_limits():
+    # T * k * max(H, I, n_s * I_s) must stay below 2^31
+    d = dims(hidden=4096, inter=512, n_shared=0, shared_inter=0)
+    big = (1 << 31) // (2 * 4096)          # k = 2
+    assert ws_size(d, big - 1, 0)[0] == B.MOE_OK
+    assert ws_size(d, big, 0)[0] == B.MOE_EUNSUPPORTED
+    d = dims(hidden=256, inter=512, n_shared=2, shared_inter=1 << 20)   # wide shared block
+    assert ws_size(d, 1 << 9, 0)[0] == B.MOE_EUNSUPPORTED
+    assert ws_size(d, (1 << 9) - 1, 0)[0] == B.MOE_OK
+    # one expert matrix past 2^31 elements
+    assert ws_size(dims(hidden=1 << 16, inter=1 << 15), 1, 0)[0] == B.MOE_EUNSUPPORTED
+    assert ws_size(dims(hidden=1 << 16, inter=(1 << 15) - 16), 1, 0)[0] == B.MOE_OK
+
+
 def test_layout_field_out_of_range():
     d = dims(dtype="bf16")
     d.weight_layout = 7
