@@ -57,13 +57,22 @@ notes):
   Recall is |predicted & true| / n_keep per (token, expert).  Compact packing
   gathers the kept channels' gate and down rows in ascending channel order.
 
-* LoRE fitting: the calibration inputs are an orthogonal design (blocks of
-  sqrt(H)-scaled random orthogonal matrices, so h^T h = N I before rounding to
-  the layer dtype); the least-squares map is then R^T h / N, and the rank-r
-  factors come from its truncated SVD, B = U_r S_r and A = V_r^T.
+* LoRE fitting minimises ||R - h (B A)^T||_F over rank-r maps on the rows it
+  is given (R = y_e - y_shared): with G = h^T h / N and M = R^T h / N, the
+  minimiser is B A = [M G^-1/2]_r G^-1/2 (reduced-rank regression: whiten the
+  inputs, truncate the SVD, map back), B = U_r S_r and A = V_r^T G^-1/2 from
+  the SVD U S V^T of M G^-1/2.  For an orthogonal design (G = I) this is the
+  truncated SVD of M itself.
+
+* Stall-free with fewer than k prefetched experts (outside the page's domain:
+  its lists hold k + delta >= k experts): Algorithm 1 then returns the whole
+  prefetched set; the remaining slots take the best experts outside it by
+  the original router's score (these would stall), and the token gets flag
+  bit 32.
 
 Flag bits per token: 1 route near-tie, 2 prefetch near-tie, 4 substitution
-near-tie, 8 FloE mask near-tie, 16 prefetch-budget near-tie.
+near-tie, 8 FloE mask near-tie, 16 prefetch-budget near-tie, 32 prefetched
+set smaller than k (stall-free).
 """
 from __future__ import annotations
 
@@ -73,10 +82,10 @@ from typing import Callable, Dict, List, Optional, Sequence
 import numpy as np
 
 __all__ = [
-    "FLAG_ROUTE", "FLAG_PREFETCH", "FLAG_SUBST", "FLAG_FLOE",
+    "FLAG_ROUTE", "FLAG_PREFETCH", "FLAG_SUBST", "FLAG_FLOE", "FLAG_SHORT",
     "bf16_to_f64", "fp16_to_f64", "decode", "silu", "sigmoid",
     "router_logits", "softmax", "rank_experts", "route_token",
-    "prefetch_set", "prefetch_masks", "delta_star", "stall_free_select",
+    "prefetch_set", "prefetch_masks", "delta_star", "stall_free_select", "stall_free_fill",
     "FLAG_BUDGET", "adaptive_budget", "prefetch_overlap", "adaptive_prefetch",
     "permute", "swiglu_expert", "dequant_int2", "floe_expert",
     "floe_channel_mask", "floe_predict_masks", "mask_recall", "floe_pack",
@@ -86,6 +95,7 @@ __all__ = [
 
 FLAG_ROUTE, FLAG_PREFETCH, FLAG_SUBST, FLAG_FLOE = 1, 2, 4, 8
 FLAG_BUDGET = 16
+FLAG_SHORT = 32
 MODES = ("standard", "lore", "stall_free", "floe")
 
 
@@ -265,6 +275,22 @@ def stall_free_select(k_routed: Sequence[int], q_r: np.ndarray, k_prefetched: se
     return keep | set(subs), bool(flag)
 
 
+def stall_free_fill(S: set, q_r: np.ndarray, k: int, margin: float):
+    """Completes a stall-free set that Algorithm 1 left short: with fewer
+    than k prefetched experts [APEX Sec. 4.3 assumes k + delta >= k] it
+    returns the whole prefetched set; the missing k - |S| slots take the
+    experts outside S with the highest original-router score (ties -> lower
+    id).  Returns (set of k, near-tie flag between the last one taken and the
+    next candidate)."""
+    S = set(S)
+    n = k - len(S)
+    if n <= 0:
+        return S, False
+    rest = sorted((e for e in range(len(q_r)) if e not in S), key=lambda e: (-q_r[e], e))
+    flag = len(rest) > n and (q_r[rest[n - 1]] - q_r[rest[n]]) < margin
+    return S | set(rest[:n]), bool(flag)
+
+
 # -------------------------------------------------------------- permutation --
 def permute(ids: np.ndarray, exact: np.ndarray, n_experts: int):
     """Token->expert permutation: the exactly computed (token, slot) pairs,
@@ -405,18 +431,28 @@ def lore_targets(h: np.ndarray, w_gate_e, w_up_e, w_down_e, ws_gate, ws_up, ws_d
 def lore_fit(h: np.ndarray, resid: np.ndarray, r: int):
     """LoRE fitting [SPICE "LoRE low-rank surrogate": minimise
     ||y_e - y_shared - B_e A_e h||^2 over the calibration set, solved by an
-    SVD].  With R = resid [N][H] and the calibration inputs an orthogonal
-    design (H^T H = N I), the least-squares map is M = R^T h / N, and its
-    rank-r truncated SVD U_r S_r V_r^T is the best rank-r map (Eckart-Young).
-    Returns (A = V_r^T [r][H], B = U_r S_r [H][r], the r singular values, and
-    the relative residual ||R - h (B A)^T||_F / ||R||_F on the calibration set)."""
+    SVD].  With R = resid [N][H_out] and the calibration inputs h [N][H_in]
+    (full column rank), the objective is ||R - h W^T||_F^2 over maps W of
+    rank <= r.  Writing G = h^T h / N and M = R^T h / N (the least-squares
+    map is M G^-1), the objective equals N ||(W - M G^-1) G^1/2||_F^2 plus a
+    constant, so the minimiser truncates the SVD of the whitened map
+    M G^-1/2 = U S V^T (Eckart-Young) and maps back: W = U_r S_r V_r^T G^-1/2.
+    G^-1/2 comes from the symmetric eigendecomposition of G.
+    Returns (A = V_r^T G^-1/2 [r][H_in], B = U_r S_r [H_out][r], the r
+    singular values of M G^-1/2, and the relative residual
+    ||R - h (B A)^T||_F / ||R||_F on the calibration set)."""
+    h = np.asarray(h, dtype=np.float64)
+    R = np.asarray(resid, dtype=np.float64)
     N = h.shape[0]
-    M = np.asarray(resid, dtype=np.float64).T @ np.asarray(h, dtype=np.float64) / N
-    U, S, Vt = np.linalg.svd(M)
+    G = h.T @ h / N
+    lam, Q = np.linalg.eigh(G)
+    G_mhalf = (Q / np.sqrt(lam)) @ Q.T
+    M = R.T @ h / N
+    U, S, Vt = np.linalg.svd(M @ G_mhalf)
     B = U[:, :r] * S[:r]
-    A = Vt[:r]
+    A = Vt[:r] @ G_mhalf
     pred = h @ (B @ A).T
-    err = float(np.linalg.norm(resid - pred) / np.linalg.norm(resid))
+    err = float(np.linalg.norm(R - pred) / np.linalg.norm(R))
     return A, B, S[:r].copy(), err
 
 
@@ -433,9 +469,10 @@ class WeightSource:
     ``src`` is either a mapping name -> stacked array, or an object with
     ``expert(name, e)`` (per-expert draw) plus ``w_router()`` etc."""
 
-    def __init__(self, src, dtype: str):
+    def __init__(self, src, dtype: str, compute=np.float64):
         self.src = src
         self.dtype = dtype
+        self.compute = compute
         self._memo: Dict = {}
 
     def small(self, name: str):
@@ -456,7 +493,7 @@ class WeightSource:
         key = (name, e)
         if key in self._memo:
             return self._memo[key]
-        v = decode(self.expert(name, e), self.dtype)
+        v = decode(self.expert(name, e), self.dtype).astype(self.compute, copy=False)
         if v.nbytes <= (1 << 22):
             self._memo[key] = v
         return v
@@ -464,8 +501,11 @@ class WeightSource:
 
 # ------------------------------------------------------------- layer forward --
 def layer_forward(x, weights, dims: dict, mode: str, resident=None,
-                  force: Optional[dict] = None, tie_margin: float = 1e-4) -> dict:
-    """One MoE layer forward, every step in fp64.
+                  force: Optional[dict] = None, tie_margin: float = 1e-4,
+                  precision: str = "f64") -> dict:
+    """One MoE layer forward, every step in fp64 (``precision="f32"`` runs
+    the same steps on float32 copies of the decoded inputs: the timed CPU
+    baseline, never a parity reference).
 
     x: [T][H] storage (bf16 bits or fp32); weights: mapping or per-expert source;
     dims: hidden, n_experts, top_k, inter, n_shared, shared_inter, lore_rank,
@@ -485,10 +525,11 @@ def layer_forward(x, weights, dims: dict, mode: str, resident=None,
     force = force or {}
     dt = dims["dtype"]
     H, E, k = dims["hidden"], dims["n_experts"], dims["top_k"]
-    src = weights if isinstance(weights, WeightSource) else WeightSource(weights, dt)
-    X = decode(x, dt)
+    cdt = {"f64": np.float64, "f32": np.float32}[precision]
+    src = weights if isinstance(weights, WeightSource) else WeightSource(weights, dt, cdt)
+    X = decode(x, dt).astype(cdt, copy=False)
     T = X.shape[0]
-    w_router = decode(src.small("w_router"), dt)
+    w_router = decode(src.small("w_router"), dt).astype(cdt, copy=False)
     logits = router_logits(X, w_router)
     probs = softmax(logits)
 
@@ -513,6 +554,9 @@ def layer_forward(x, weights, dims: dict, mode: str, resident=None,
             kp = {e for e in range(E) if (res[t] >> e) & 1}
             S, fs = stall_free_select(r_ids, logits[t], kp, tie_margin)
             flags[t] |= FLAG_SUBST if fs else 0
+            if len(S) < k:
+                S, ff = stall_free_fill(S, logits[t], k, tie_margin)
+                flags[t] |= FLAG_SHORT | (FLAG_SUBST if ff else 0)
             final = sorted(S, key=lambda e: (-logits[t][e], e))
             n_subst[t] = len(set(final) - set(r_ids))
         if t in force.get("ids", {}):
@@ -560,7 +604,7 @@ def layer_forward(x, weights, dims: dict, mode: str, resident=None,
         ws_g = [src.f64("ws_gate", s) for s in range(dims["n_shared"])]
         ws_u = [src.f64("ws_up", s) for s in range(dims["n_shared"])]
         ws_d = [src.f64("ws_down", s) for s in range(dims["n_shared"])]
-        wsg = decode(src.small("w_shared_gate"), dt) if dims["shared_gate"] else None
+        wsg = decode(src.small("w_shared_gate"), dt).astype(cdt, copy=False) if dims["shared_gate"] else None
         y_shared, g_shared = shared_experts(X, ws_g, ws_u, ws_d, wsg)
     else:
         y_shared, g_shared = np.zeros((T, H)), np.zeros(T)

@@ -675,3 +675,193 @@ def test_overlap_full_exactly_when_budget_covers_delta_star():
             assert masks[t] == _mask(kp)
             assert ov[t] == len(set(routed[t]) & kp)
             assert (ov[t] == k) == (d_hat[t] >= ds[t])
+
+
+# ------------------------------------------- flag thresholds (bits 2, 8, 16) --
+MARGIN = 1e-4
+
+
+@pytest.mark.parametrize("gap,want", [(0.99e-4, True), (1.01e-4, False)])
+def test_prefetch_edge_flag_sits_at_the_list_edge(gap, want):
+    """Bit 2 is raised exactly when the list's last member and the first
+    expert left out differ by less than the margin in prefetch logits; the
+    same gap one place deeper or shallower in the ranking never raises it."""
+    base = np.array([5.0, 4.0, 3.0, 2.0, 1.0, 0.0])
+    n = 3
+    lp = base.copy(); lp[3] = lp[2] - gap          # ranks n-1 and n
+    m, f = O.prefetch_set(lp, n, MARGIN)
+    assert m == 0b000111 and f is want
+    lp = base.copy(); lp[4] = lp[3] - gap          # ranks n and n+1
+    assert O.prefetch_set(lp, n, MARGIN) == (0b000111, False)
+    lp = base.copy(); lp[2] = lp[1] - gap          # ranks n-2 and n-1
+    assert O.prefetch_set(lp, n, MARGIN) == (0b000111, False)
+    # through the per-token entry: x = [1] makes the logits the router column
+    lp = base.copy(); lp[3] = lp[2] - gap
+    masks, flags, _ = O.prefetch_masks(np.ones((1, 1)), lp[:, None], np.array([1]), 2, MARGIN)
+    assert masks == [0b000111] and flags[0] == (O.FLAG_PREFETCH if want else 0)
+    # a list of every expert has no edge
+    assert O.prefetch_set(np.zeros(4), 4, MARGIN) == (0b1111, False)
+
+
+def test_budget_flag_on_the_logit_scale_at_the_chosen_budget_and_the_one_below():
+    """Bit 16: |theta_d - w.x - logit(tau)| below the margin at the chosen
+    budget d or at d - 1; not at d + 1, and judged on the logit scale, not on
+    the probability sigmoid(theta_d - w.x) (whose slope at tau = 0.9 is 0.09,
+    so a logit gap of 5e-4 is a probability gap of 4.5e-5)."""
+    tau = 0.9
+    lt = math.log(tau / (1 - tau))
+    w, x = np.array([0.75]), np.array([1.0])
+    s = 0.75
+
+    def budget(gaps):
+        return O.adaptive_budget(x, w, [lt + s + g for g in gaps], tau, MARGIN)
+
+    # the chosen budget (d = 1) sits just above the threshold
+    assert budget([-1.0, 0.99e-4, 1.0]) == (1, True)
+    assert budget([-1.0, 1.01e-4, 1.0]) == (1, False)
+    # the budget below it (d - 1 = 0) sits just under the threshold
+    assert budget([-0.99e-4, 1.0, 2.0]) == (1, True)
+    assert budget([-1.01e-4, 1.0, 2.0]) == (1, False)
+    # a near-threshold budget above the chosen one does not count
+    assert budget([-1.0, 1.0, 0.5e-4]) == (1, False)
+    # logit scale: a logit gap of 5e-4 is no near-tie although p moves by 4.5e-5
+    d, f = budget([-1.0, 5e-4, 1.0])
+    assert d == 1 and not f
+    assert abs(O.sigmoid(lt + 5e-4) - tau) < MARGIN
+    # no budget qualifies: N - k, flagged only if the last one is within the margin
+    assert budget([-1.0, -2.0, -3.0]) == (2, False)
+    assert budget([-1.0, -2.0, -0.5e-4]) == (2, True)
+
+
+def _int2_group(q0, q1):
+    """Codes of one 64-input group: input 0 -> q0, input 1 -> q1, the other
+    62 inputs -> code 1 (weight 0 with zero point 1)."""
+    b = np.full(16, 0b01010101, dtype=np.uint8)
+    b[0] = q0 | (q1 << 2) | (1 << 4) | (1 << 6)
+    return b
+
+
+@pytest.mark.parametrize("eps,want", [(0.99e-4, True), (1.01e-4, False)])
+def test_floe_mask_edge_flag_threshold(eps, want):
+    """Bit 8: the n_keep-th and (n_keep+1)-th |u| differ by less than the
+    margin.  Scale s = 1, zero z = 1 give weights q - 1 in {-1, 0, 1, 2};
+    x = [1, eps, 0, ...] then gives u = [2, 1, -(1 - eps), 0]: |u| ranks
+    channels 0, 1, 2, 3 and the gap at the edge of a 2-channel mask is eps."""
+    one = np.float16(1.0).view(np.uint16)
+    q = np.stack([_int2_group(3, 1), _int2_group(2, 1), _int2_group(0, 2), _int2_group(1, 1)])
+    s = np.full((4, 1), one, dtype=np.uint16)
+    z = np.full((4, 1), one, dtype=np.uint16)
+    x = np.zeros(64); x[0] = 1.0; x[1] = eps
+    keep, flag, u = O.floe_channel_mask(x, q, s, z, 2, MARGIN)
+    np.testing.assert_allclose(u, [2.0, 1.0, -(1.0 - eps), 0.0], rtol=0, atol=1e-15)
+    assert list(keep) == [0, 1] and flag is want
+    # the same gap elsewhere in the ranking is no near-tie
+    assert O.floe_channel_mask(x, q, s, z, 1, MARGIN)[1] is False
+    assert O.floe_channel_mask(x, q, s, z, 3, MARGIN)[1] is False
+    # the forward raises the same flag
+    rng = np.random.default_rng(3)
+    y, _, keep2, flag2 = O.floe_expert(x, rng.standard_normal((4, 64)), q, s, z,
+                                       rng.standard_normal((4, 64)), 2, MARGIN)
+    assert list(keep2) == [0, 1] and flag2 is want
+
+
+# ----------------------------------------------- LoRE fit: exact least squares --
+def _skewed_design(rng, N, H):
+    """Correlated, unequally scaled inputs: far from an orthogonal design."""
+    mix = rng.standard_normal((H, H)) * 0.3 + np.diag(np.linspace(0.5, 3.0, H))
+    return rng.standard_normal((N, H)) @ mix
+
+
+def test_lore_fit_full_rank_is_lstsq_on_a_non_orthogonal_design():
+    rng = np.random.default_rng(44)
+    N, H = 80, 24
+    h = _skewed_design(rng, N, H)
+    R = rng.standard_normal((N, H))
+    A, B, sig, err = O.lore_fit(h, R, H)
+    W_ls = np.linalg.lstsq(h, R, rcond=None)[0].T
+    np.testing.assert_allclose(B @ A, W_ls, rtol=1e-8, atol=1e-10)
+    want = np.linalg.norm(R - h @ W_ls.T) / np.linalg.norm(R)
+    assert abs(err - want) < 1e-10
+
+
+@pytest.mark.parametrize("r", [1, 3, 7])
+def test_lore_fit_rank_r_matches_the_qr_route_and_is_optimal(r):
+    """Rank-r least squares by a second route: with the thin QR h = Q_h R_h,
+    ||R - h W^T|| = ||Q_h^T R - R_h W^T|| + const, so R_h W^T is the rank-r
+    truncated SVD of C = Q_h^T R and W^T = R_h^-1 [C]_r.  Random rank-r
+    perturbations of the result never lower the residual, and it beats the
+    truncated SVD of the unwhitened map R^T h / N on this skewed design."""
+    rng = np.random.default_rng(45 + r)
+    N, H = 90, 20
+    h = _skewed_design(rng, N, H)
+    R = h @ rng.standard_normal((H, H)) * 0.2 + rng.standard_normal((N, H))
+    A, B, sig, err = O.lore_fit(h, R, r)
+    Qh, Rh = np.linalg.qr(h)
+    Uc, Sc, Vct = np.linalg.svd(Qh.T @ R)
+    Cr = (Uc[:, :r] * Sc[:r]) @ Vct[:r]
+    W_qr = np.linalg.solve(Rh, Cr).T
+    np.testing.assert_allclose(B @ A, W_qr, rtol=1e-8, atol=1e-10)
+    np.testing.assert_allclose(sig, Sc[:r] / math.sqrt(N), rtol=1e-10)
+    loss = lambda W: np.linalg.norm(R - h @ W.T)
+    base = loss(B @ A)
+    for _ in range(20):
+        dB = rng.standard_normal(B.shape) * 1e-3
+        dA = rng.standard_normal(A.shape) * 1e-3
+        assert loss((B + dB) @ (A + dA)) >= base - 1e-12
+    U, S, Vt = np.linalg.svd(R.T @ h / N)
+    naive = (U[:, :r] * S[:r]) @ Vt[:r]
+    assert base < loss(naive)
+
+
+# ------------------------------------- stall-free with a short prefetched set --
+def test_stall_free_short_prefetched_set_literal_and_fill():
+    """Fewer than k prefetched experts: Algorithm 1's sets give back the whole
+    prefetched set (every prefetched expert is kept or substitutes), and the
+    fill takes the best remaining experts by the original router's score."""
+    l = np.array([5.0, 4.0, 3.0, 2.0, 1.0, 0.0])
+    # routed {0, 1, 2}, prefetched {4, 5}: keep {}, missing {0, 1, 2}, subs {4, 5}
+    S, _ = O.stall_free_select([0, 1, 2], l, {4, 5}, MARGIN)
+    assert S == {4, 5}
+    full, f = O.stall_free_fill(S, l, 3, MARGIN)
+    assert full == {0, 4, 5} and not f
+    # prefetched {1}: keep {1}; fill 0 and 2
+    S, _ = O.stall_free_select([0, 1, 2], l, {1}, MARGIN)
+    assert S == {1} and O.stall_free_fill(S, l, 3, MARGIN) == ({0, 1, 2}, False)
+    # a near-tie between the last filled expert and the next one is flagged
+    l2 = np.array([5.0, 4.0, 3.0, 3.0 - 0.5e-4, 1.0])
+    assert O.stall_free_fill({4}, l2, 3, MARGIN) == ({0, 1, 4}, False)
+    assert O.stall_free_fill({4}, l2, 4, MARGIN)[1] is True
+    # a full set is returned unchanged
+    assert O.stall_free_fill({1, 2, 3}, l, 3, MARGIN) == ({1, 2, 3}, False)
+
+
+def test_stall_free_short_sets_brute_force_through_the_layer():
+    """On random tiny layers and prefetched sets of every size: the layer's
+    final set is the prefetched set plus the best outside it when the set is
+    short (flag 32), else Algorithm 1's set; slots ordered by (-logit, id)."""
+    rng = np.random.default_rng(46)
+    H, I = 8, 4
+    for trial in range(60):
+        E = int(rng.integers(3, 9)); k = int(rng.integers(1, E + 1))
+        w = {"w_router": rng.standard_normal((E, H)).astype(np.float32),
+             "w_gate": rng.standard_normal((E, I, H)).astype(np.float32),
+             "w_up": rng.standard_normal((E, I, H)).astype(np.float32),
+             "w_down": rng.standard_normal((E, H, I)).astype(np.float32)}
+        dims = dict(hidden=H, n_experts=E, top_k=k, inter=I, n_shared=0, shared_inter=0,
+                    lore_rank=0, renormalize=True, shared_gate=False, dtype="f32",
+                    up_format="dense", floe_keep=0)
+        x = rng.standard_normal((3, H)).astype(np.float32)
+        masks = [_mask(rng.permutation(E)[: int(rng.integers(0, E + 1))].tolist()) for _ in range(3)]
+        r = O.layer_forward(x, w, dims, "stall_free", resident=masks)
+        l = O.router_logits(x.astype(np.float64), w["w_router"].astype(np.float64))
+        for t in range(3):
+            kp = [e for e in range(E) if (masks[t] >> e) & 1]
+            order = O.rank_experts(l[t])
+            if len(kp) < k:
+                want = set(kp) | set([e for e in order if e not in kp][: k - len(kp)])
+                assert r["flags"][t] & O.FLAG_SHORT
+            else:
+                want = set(sorted(kp, key=lambda e: (-l[t][e], e))[:k])
+                assert not r["flags"][t] & O.FLAG_SHORT
+            assert set(r["ids"][t]) == want
+            assert list(r["ids"][t]) == [e for e in order if e in want]

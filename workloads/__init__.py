@@ -22,11 +22,17 @@ Shapes follow the five MoE-layer workloads the pages study:
                          projection stored as 2-bit asymmetric codes in groups
                          of 64 with fp16 scale and zero, keep 10% of channels.
 * ``granite_prefill`` -- Granite-3B-A800M shape (APEX page, Sec. 1: 40 experts,
-                         top-8): H=1536, I=512, 4096 tokens, separate linear
-                         prefetch router correlated 0.97 with the router,
-                         per-token extra budget delta drawn from
+                         top-8): H=1536, I=512, 4096 tokens, a separate linear
+                         prefetch router drawn N(0, 0.02) independently of the
+                         router, per-token extra budget delta drawn from
                          Geometric(0.4) on {0,1,...} capped at N-k, and an
                          ordinal budget model (w_delta, theta).
+* ``granite_prefill_distilled`` -- the same layer with the prefetch router
+                         drawn correlated 0.97 with the router (APEX page,
+                         Sec. 4.1 trains the prefetch router toward the
+                         router's choices); used for the adaptive-budget
+                         statistics, whose overlap is meaningless for an
+                         unrelated router.
 
 Layouts (all row-major, C order):
 
@@ -90,7 +96,7 @@ class MoEConfig:
     resident_count: Optional[int] = None
     prefetch: bool = False          # draws w_prefetch and delta
     delta_p: float = 0.4
-    prefetch_rho: float = 0.97      # correlation of the prefetch router with the router
+    prefetch_rho: float = 0.0       # correlation of the prefetch router with the router
     weight_std: float = 0.02
     hidden_std: float = 1.0
     lore_std: float = 0.01
@@ -131,6 +137,11 @@ CONFIGS: Dict[str, MoEConfig] = {
         n_shared=0, shared_inter=0, lore_rank=0, renormalize=True,
         shared_gate=False, dtype="bf16", token_counts=(4096,),
         modes=("standard", "stall_free"), seed=4, prefetch=True),
+    "granite_prefill_distilled": MoEConfig(
+        name="granite_prefill_distilled", hidden=1536, n_experts=40, top_k=8, inter=512,
+        n_shared=0, shared_inter=0, lore_rank=0, renormalize=True,
+        shared_gate=False, dtype="bf16", token_counts=(4096,),
+        modes=("standard", "stall_free"), seed=4, prefetch=True, prefetch_rho=0.97),
 }
 
 # Seed-stream tags, one per tensor.
@@ -289,11 +300,12 @@ class Layer:
         return self._small("w_router", (self.cfg.n_experts, self.cfg.hidden), self.cfg.weight_std)
 
     def w_prefetch(self) -> np.ndarray:
-        """A prefetch router distilled toward the router (APEX page, Sec. 4.1:
-        trained to match the router's distribution; no trained weights exist
-        here): rho * W_r + sqrt(1 - rho^2) * fresh noise of the same spread,
-        drawn in fp32 before rounding to the storage dtype.  rho = 0.97 gives
-        Granite-shaped inputs a long-tailed delta* (median 2, 98th
+        """The separate linear prefetch router (APEX page, Sec. 4.1):
+        rho * W_r + sqrt(1 - rho^2) * fresh N(0, weight_std) noise, drawn in
+        fp32 before rounding to the storage dtype.  rho = 0 (the default) is
+        an independent N(0, weight_std) router; rho = 0.97 stands in for one
+        trained toward the router's choices (no trained weights exist here)
+        and gives Granite-shaped inputs a long-tailed delta* (median 2, 98th
         percentile about 9)."""
         key = ("w_prefetch", 0)
         if key not in self._cache:
