@@ -311,18 +311,21 @@ def measure(name, T, mode, steps, warmup, ev=None, want_roofline=False):
     return r
 
 
-def cpu_baseline(name, T, mode, budget_s=10.0):
-    """The CPU oracle as it stands on a bounded sample of the same workload:
-    the first S tokens (S doubled from 1 until one call takes about budget_s/2
-    or covers all T tokens), then that call repeated until about budget_s of
-    CPU work has been timed."""
+def cpu_baseline(name, T, mode, budget_s=8.0, layer=None):
+    """The CPU oracle as it stands, timed on the host cores on a bounded
+    sample of the same workload: the fp32 variant (the same steps on float32
+    copies, BLAS matmuls) with every host thread and with one thread, and the
+    fp64 parity oracle for information.  Each leg takes the first S tokens (S
+    doubled from 1 until one call takes about budget_s/2 or covers all T
+    tokens) and repeats that call until about budget_s has been timed."""
     import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle as O
     import workloads as W
     from workloads.device import dims_dict
 
-    layer = W.make_layer(name)
+    layer = layer if layer is not None else W.make_layer(name)
     cfg = layer.cfg
     d = dims_dict(cfg)
     res = layer.resident() if mode == "lore" else None
@@ -331,28 +334,33 @@ def cpu_baseline(name, T, mode, budget_s=10.0):
                                        O.decode(layer.w_prefetch(), cfg.dtype), layer.delta(T), cfg.top_k)
         res = masks
 
-    def call(S):
+    def call(S, precision):
         sub_res = res[:S] if isinstance(res, list) else res
         t0 = time.perf_counter()
-        O.layer_forward(layer.x(T)[:S], layer, d, mode, resident=sub_res)
+        O.layer_forward(layer.x(T)[:S], layer, d, mode, resident=sub_res, precision=precision)
         return time.perf_counter() - t0
 
-    call(1)                      # untimed: first-call set-up (weight generation caches)
-    S = 1
-    while True:
-        dt = call(S)
-        if dt >= budget_s / 2 or S >= T:
-            break
-        S = min(T, S * 2)
-    total, calls = dt, 1
-    while total < budget_s:
-        total += call(S)
-        calls += 1
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = 1
+    def leg(precision, threads, budget):
+        with threadpool_limits(limits=threads):
+            call(1, precision)       # untimed: first-call set-up (weight draws cached)
+            S = 1
+            while True:
+                dt = call(S, precision)
+                if dt >= budget / 2 or S >= T:
+                    break
+                S = min(T, S * 2)
+            total, calls = dt, 1
+            while total < budget:
+                total += call(S, precision)
+                calls += 1
+            used = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return dict(value=S * calls / total, unit="tokens/s", cores=int(used), tokens=S,
+                    calls=calls, seconds=total)
+
+    host = len(os.sched_getaffinity(0))
+    f32_all = leg("f32", host, budget_s)
+    f32_one = leg("f32", 1, budget_s)
+    f64_all = leg("f64", host, budget_s / 2)
     model = "unknown"
     try:
         with open("/proc/cpuinfo") as fh:
@@ -360,10 +368,12 @@ def cpu_baseline(name, T, mode, budget_s=10.0):
                          model)
     except OSError:
         pass
-    return dict(value=S * calls / total, unit="tokens/s", cores=int(cores), kind="oracle",
-                sample=f"first {S} of the {T} tokens of the same {name} layer in mode {mode}, "
-                       f"{calls} fp64 NumPy oracle call(s), {total:.1f} s in total",
-                cpu_model=model, host_cpus=len(os.sched_getaffinity(0)))
+    return dict(value=f32_all["value"], unit="tokens/s", cores=f32_all["cores"], kind="oracle",
+                sample=f"first {f32_all['tokens']} of the {T} tokens of the same {name} layer in mode "
+                       f"{mode}, {f32_all['calls']} fp32 NumPy oracle call(s) with BLAS on "
+                       f"{f32_all['cores']} threads, {f32_all['seconds']:.1f} s in total",
+                one_thread=f32_one, fp64_parity_oracle=f64_all,
+                cpu_model=model, host_cpus=host)
 
 
 def measure_prefetch_adaptive(name, T, steps, warmup, tau=0.9):

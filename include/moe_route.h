@@ -36,7 +36,9 @@
  * Decisions.  Every ranking orders experts by (-logit, id) -- ties go to the
  * lower expert id -- and FloE channels by (-|u|, channel).  A token whose
  * deciding gap is below dims.tie_margin gets a flag bit (several answers are
- * correct there): 1 route, 2 prefetch, 4 substitution, 8 FloE mask.
+ * correct there): 1 route, 2 prefetch, 4 substitution, 8 FloE mask, 16
+ * prefetch budget.  Bit 32 marks a stall-free token whose prefetched set held
+ * fewer than k experts (see moe_route).
  */
 #ifndef MOE_ROUTE_H
 #define MOE_ROUTE_H
@@ -183,7 +185,10 @@ moe_status_t moe_pack_weights(int32_t groups, int32_t rows, int32_t cols, const 
  *     tokens, 1 = one mask per token.  LORE: exact[t][j] = bit of expert.
  *     STALL_FREE: the token's prefetched set; the final set is the routed set
  *     with each non-prefetched expert replaced by the best-scoring prefetched
- *     one under the original router [APEX page, Sec. 4.3, Algorithm 1].
+ *     one under the original router [APEX page, Sec. 4.3, Algorithm 1].  The
+ *     page's prefetched sets hold k + delta >= k experts; a set of fewer than
+ *     k is kept whole and the remaining slots take the best experts outside
+ *     it by router score (they stall), with flag bit 32.
  *     STANDARD / FLOE: ignored (may be NULL); every slot exact.
  *   Outputs: topk_ids [T][k] int32 ordered by (-l, id); topk_w [T][k] fp32
  *     (p_e, or p_e / sum over the set when dims.renormalize); exact [T][k];
@@ -302,18 +307,24 @@ moe_status_t moe_lore_fit_size(int32_t hidden, int32_t N, int32_t rank, int32_t 
                                size_t* bytes /* host */);
 
 /* LoRE fitting, step 2 [SPICE page, "LoRE low-rank surrogate": minimise
- * ||y_e - y_shared - B_e A_e h||^2, solved with an SVD]: with R = resid
- * [N][H] fp32 (moe_lore_targets) and the calibration rows h_cal [N][H] dtype
- * taken as an orthogonal design (h^T h = N I), the least-squares map is
- * M = R^T h / N; its rank-`rank` truncated SVD gives lore_A_out [rank][H]
- * = V_r^T and lore_B_out [H][rank] = U_r S_r (dtype; for rank = dims.lore_rank
- * these are expert e's slices of moe_weights_t.lore_A / lore_B), sigma_out
- * [rank] fp32 the singular values (descending), err_out [1] fp32 the relative
- * residual ||R - h (B A)^T||_F / ||R||_F of the fp32 factors.  The SVD is a
- * subspace iteration of `n_iter` rounds (Y <- M M^T Y, orthonormalised) on
- * `cols` columns (rank <= cols <= 64) started from omega [H][cols] fp32
- * (the caller's random draw), then a Rayleigh-Ritz step.  ws: at least
- * moe_lore_fit_size(H, N, rank, cols) bytes.  All buffers device, caller-owned. */
+ * ||y_e - y_shared - B_e A_e h||^2, solved with an SVD]: the rank-`rank` map
+ * W = B A minimising ||R - h W^T||_F on the N calibration rows h_cal [N][H]
+ * dtype (full column rank, N >= H) for targets R = resid [N][H] fp32
+ * (moe_lore_targets).  With G = h^T h / N and M = R^T h / N the minimiser is
+ * W = [M G^-1/2]_r G^-1/2: G^-1/2 by 20 rounds of the coupled Newton-Schulz
+ * iteration from a Gershgorin-scaled start (converged to fp32 accuracy for
+ * cond(G) up to about 1e2; an orthogonal design, G = I, takes 3), then the
+ * truncated SVD U_r S_r V_r^T of M G^-1/2.  Outputs: lore_A_out [rank][H] =
+ * V_r^T G^-1/2 and lore_B_out [H][rank] = U_r S_r (dtype; for rank =
+ * dims.lore_rank these are expert e's slices of moe_weights_t.lore_A /
+ * lore_B), sigma_out [rank] fp32 the singular values of M G^-1/2
+ * (descending), err_out [1] fp32 the relative residual
+ * ||R - h (B A)^T||_F / ||R||_F of the fp32 factors.  The SVD is a subspace
+ * iteration of `n_iter` rounds (Y <- M M^T Y, orthonormalised) on `cols`
+ * columns (rank <= cols <= 64) started from omega [H][cols] fp32 (the
+ * caller's random draw), then a Rayleigh-Ritz step.  ws: at least
+ * moe_lore_fit_size(H, N, rank, cols) bytes.  All buffers device,
+ * caller-owned. */
 moe_status_t moe_lore_fit(const moe_dims_t* dims, int32_t N, const void* h_cal,
                           const float* resid, int32_t rank, int32_t cols, int32_t n_iter,
                           const float* omega, void* lore_A_out, void* lore_B_out,

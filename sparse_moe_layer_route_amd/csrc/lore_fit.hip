@@ -4,9 +4,18 @@
 //
 //   targets:  R = y_e(h) - y_s(h) for the calibration rows, from the layer's
 //             own expert and shared FFN kernels (one routed expert, k = 1).
-//   map:      M = R^T h / N  [H][H] fp32 -- the least-squares map when the
-//             calibration design is orthogonal (h^T h = N I).
-//   factors:  the rank-r truncated SVD of M, B = U_r S_r, A = V_r^T, by
+//   whitening: G = h^T h / N and Z = G^-1/2 by the coupled Newton-Schulz
+//             iteration (Higham, "Functions of Matrices", the Newton-Schulz
+//             iteration for the matrix square root): Y0 = G / c, Z0 = I,
+//             P = 3I - Z Y, Y <- Y P / 2, Z <- P Z / 2, so Y -> (G/c)^1/2 and
+//             Z -> (G/c)^-1/2; c = the largest absolute row sum of G (a
+//             Gershgorin bound on its largest eigenvalue) keeps the spectrum
+//             of G / c in (0, 1], where the iteration converges.
+//   map:      M = (R^T h / N) Z [H][H] fp32 -- the least-squares map in
+//             whitened inputs; the rank-r minimiser of ||R - h W^T|| is
+//             W = [M]_r Z (reduced-rank regression).  For an orthogonal
+//             design (h^T h = N I) Z = I and M is the plain map.
+//   factors:  the rank-r truncated SVD of M, B = U_r S_r, A = V_r^T Z, by
 //             subspace iteration (Y <- M M^T Y, re-orthonormalised each half
 //             step) from a caller-supplied Gaussian block, then a
 //             Rayleigh-Ritz step: Bs = Q^T M, eigen-decomposition of
@@ -251,18 +260,68 @@ fit_b_kernel(const float* __restrict__ U, int H, int s, int r, const float* __re
   elem<Tout>::store(Bout, i, v);
 }
 
-// A = S_r^-1 W_r^T Bs as dtype [r][H] and fp32, from G = W^T Bs [s][H].
-template <typename Tout>
+// V_r^T = S_r^-1 W_r^T Bs [r][H] fp32, from G = W^T Bs [s][H].
 __global__ void __launch_bounds__(256)
-fit_a_kernel(const float* __restrict__ G, int H, int r, const float* __restrict__ lam,
-             float* __restrict__ Af, Tout* __restrict__ Aout) {
+fit_vt_kernel(const float* __restrict__ G, int H, int r, const float* __restrict__ lam,
+              float* __restrict__ Vt) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)r * H) return;
   const int j = (int)(i / H);
   const float sg = sqrtf(fmaxf(lam[j], 0.f));
-  const float v = sg > 0.f ? G[i] / sg : 0.f;
-  Af[i] = v;
-  elem<Tout>::store(Aout, i, v);
+  Vt[i] = sg > 0.f ? G[i] / sg : 0.f;
+}
+
+// c[0] = max_i sum_j |G[i][j]| over the H x H matrix G (one workgroup; a
+// wave per row, rows in a fixed order per wave, then the waves' maxima).
+__global__ void __launch_bounds__(1024)
+fit_gersh_kernel(const float* __restrict__ G, int H, float* __restrict__ c) {
+  __shared__ float red[16];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  float m = 0.f;
+  for (int i = wv; i < H; i += 16) {
+    float r = 0.f;
+    for (int j = lane; j < H; j += 64) r += fabsf(G[(int64_t)i * H + j]);
+    m = fmaxf(m, wave_sum(r));
+  }
+  if (lane == 0) red[wv] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+    for (int w = 0; w < 16; ++w) t = fmaxf(t, red[w]);
+    c[0] = t;
+  }
+}
+
+// Newton-Schulz start: Y = G / c (in place), Z = I.
+__global__ void __launch_bounds__(256)
+fit_ns_init_kernel(float* __restrict__ Y, float* __restrict__ Z, int H, const float* __restrict__ c) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)H * H) return;
+  const float inv = c[0] > 0.f ? 1.f / c[0] : 0.f;
+  Y[i] = Y[i] * inv;
+  Z[i] = (i / H == i % H) ? 1.f : 0.f;
+}
+
+// P = 3I - P (in place).
+__global__ void __launch_bounds__(256) fit_ns_sub_kernel(float* __restrict__ P, int H) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)H * H) return;
+  P[i] = ((i / H == i % H) ? 3.f : 0.f) - P[i];
+}
+
+// Z = Z / sqrt(c): (G/c)^-1/2 -> G^-1/2.
+__global__ void __launch_bounds__(256)
+fit_ns_final_kernel(float* __restrict__ Z, int H, const float* __restrict__ c) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)H * H) return;
+  Z[i] = c[0] > 0.f ? Z[i] / sqrtf(c[0]) : 0.f;
+}
+
+template <typename Tout>
+__global__ void __launch_bounds__(256)
+fit_store_kernel(const float* __restrict__ src, int64_t n, Tout* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) elem<Tout>::store(dst, i, src[i]);
 }
 
 // Partial sums of (R - P)^2 and R^2 per block, in a fixed order.
@@ -321,12 +380,16 @@ fit_route_kernel(int N, int E, int e, int32_t* __restrict__ offsets, int32_t* __
 }
 
 constexpr int FIT_ERR_BLOCKS = 256;
+// Newton-Schulz rounds: a Gershgorin-scaled start converges to fp32 accuracy
+// in about 3 rounds for a nearly orthogonal design and in 10-12 rounds for
+// cond(h^T h) near 35 (a Gaussian design of 2H rows); 20 leave room beyond.
+constexpr int FIT_NS_ITERS = 20;
 
 int64_t lore_fit_ws_elems(int H, int N, int r, int s) {
   auto al = [](int64_t v) { return (v + 63) & ~(int64_t)63; };
-  return al((int64_t)H * H) + 2 * al((int64_t)H * s) + al((int64_t)s * H) + 2 * al((int64_t)s * s) +
-         al(s) + al((int64_t)s * H) + al((int64_t)r * H) + al((int64_t)H * r) + al((int64_t)N * r) +
-         al((int64_t)N * H) + al(2 * FIT_ERR_BLOCKS);
+  return 6 * al((int64_t)H * H) + 2 * al((int64_t)H * s) + al((int64_t)s * H) + 2 * al((int64_t)s * s) +
+         al(s) + al((int64_t)s * H) + 2 * al((int64_t)r * H) + al((int64_t)H * r) + al((int64_t)N * r) +
+         al((int64_t)N * H) + al(2 * FIT_ERR_BLOCKS) + al(1);
 }
 
 template <typename Tin>
@@ -334,21 +397,46 @@ static hipError_t launch_lore_fit_t(int H, int N, const Tin* h, const float* R, 
                                     int n_iter, const float* omega, Tin* A_out, Tin* B_out,
                                     float* sigma, float* err, float* ws, hipStream_t st) {
   auto al = [](int64_t v) { return (v + 63) & ~(int64_t)63; };
+  const int64_t HH = al((int64_t)H * H);
   float* M = ws;
-  float* Y = M + al((int64_t)H * H);
+  float* Ya = M + HH;  // Newton-Schulz buffers; Ya starts as G
+  float* Yb = Ya + HH;
+  float* Za = Yb + HH;
+  float* Zb = Za + HH;
+  float* Pm = Zb + HH;
+  float* Y = Pm + HH;
   float* Z = Y + al((int64_t)H * s);
   float* Bs = Z + al((int64_t)H * s);
   float* Tm = Bs + al((int64_t)s * H);
   float* Wv = Tm + al((int64_t)s * s);
   float* lam = Wv + al((int64_t)s * s);
   float* G = lam + al(s);
-  float* Af = G + al((int64_t)s * H);
+  float* Vt = G + al((int64_t)s * H);
+  float* Af = Vt + al((int64_t)r * H);
   float* Bf = Af + al((int64_t)r * H);
   float* P1 = Bf + al((int64_t)H * r);
   float* P = P1 + al((int64_t)N * r);
   float* part = P + al((int64_t)N * H);
-  // M = R^T h / N: M(a, b) = sum_n R[n][a] h[n][b]
-  fit_gemm<float, Tin>(H, H, N, 1.f / (float)N, R, 1, H, h, H, 1, M, H, 1, st);
+  float* cscale = part + al(2 * FIT_ERR_BLOCKS);
+  const unsigned ew = (unsigned)(((int64_t)H * H + 255) / 256);
+  // whitening Z = (h^T h / N)^-1/2: G(a, b) = sum_n h[n][a] h[n][b] / N
+  fit_gemm<Tin, Tin>(H, H, N, 1.f / (float)N, h, 1, H, h, H, 1, Ya, H, 1, st);
+  fit_gersh_kernel<<<1, 1024, 0, st>>>(Ya, H, cscale);
+  fit_ns_init_kernel<<<ew, 256, 0, st>>>(Ya, Za, H, cscale);
+  for (int it = 0; it < FIT_NS_ITERS; ++it) {
+    // P = 3I - Z Y;  Y <- Y P / 2;  Z <- P Z / 2
+    fit_gemm<float, float>(H, H, H, 1.f, Za, H, 1, Ya, H, 1, Pm, H, 1, st);
+    fit_ns_sub_kernel<<<ew, 256, 0, st>>>(Pm, H);
+    fit_gemm<float, float>(H, H, H, 0.5f, Ya, H, 1, Pm, H, 1, Yb, H, 1, st);
+    fit_gemm<float, float>(H, H, H, 0.5f, Pm, H, 1, Za, H, 1, Zb, H, 1, st);
+    std::swap(Ya, Yb);
+    std::swap(Za, Zb);
+  }
+  fit_ns_final_kernel<<<ew, 256, 0, st>>>(Za, H, cscale);
+  const float* Wh = Za;  // G^-1/2
+  // M = (R^T h / N) G^-1/2: M0(a, b) = sum_n R[n][a] h[n][b] / N into Ya
+  fit_gemm<float, Tin>(H, H, N, 1.f / (float)N, R, 1, H, h, H, 1, Ya, H, 1, st);
+  fit_gemm<float, float>(H, H, H, 1.f, Ya, H, 1, Wh, H, 1, M, H, 1, st);
   // Y = M omega (Y, Z and U are stored by columns: element (h, j) at j*H + h)
   fit_gemm<float, float>(H, s, H, 1.f, M, H, 1, omega, s, 1, Y, 1, H, st);
   fit_orth_kernel<<<1, 1024, 0, st>>>(Y, H, s);
@@ -363,13 +451,15 @@ static hipError_t launch_lore_fit_t(int H, int N, const Tin* h, const float* R, 
   fit_gemm<float, float>(s, H, H, 1.f, Y, H, 1, M, H, 1, Bs, H, 1, st);
   fit_gemm<float, float>(s, s, H, 1.f, Bs, H, 1, Bs, 1, H, Tm, s, 1, st);
   fit_jacobi_kernel<<<1, 64, 0, st>>>(Tm, s, 30, lam, Wv);
-  // U = Y Wv (into Z), B = U_r S_r; G = Wv^T Bs, A = S_r^-1 G_r
+  // U = Y Wv (into Z), B = U_r S_r; G = Wv^T Bs, V_r^T = S_r^-1 G_r, A = V_r^T G^-1/2
   fit_gemm<float, float>(H, s, s, 1.f, Y, 1, H, Wv, s, 1, Z, 1, H, st);
   fit_b_kernel<Tin><<<(unsigned)(((int64_t)H * r + 255) / 256), 256, 0, st>>>(Z, H, s, r, lam, Bf,
                                                                                 B_out, sigma);
   fit_gemm<float, float>(r, H, s, 1.f, Wv, 1, s, Bs, H, 1, G, H, 1, st);
-  fit_a_kernel<Tin><<<(unsigned)(((int64_t)r * H + 255) / 256), 256, 0, st>>>(G, H, r, lam, Af,
-                                                                               A_out);
+  fit_vt_kernel<<<(unsigned)(((int64_t)r * H + 255) / 256), 256, 0, st>>>(G, H, r, lam, Vt);
+  fit_gemm<float, float>(r, H, H, 1.f, Vt, H, 1, Wh, H, 1, Af, H, 1, st);
+  fit_store_kernel<Tin><<<(unsigned)(((int64_t)r * H + 255) / 256), 256, 0, st>>>(
+      Af, (int64_t)r * H, A_out);
   // error of the fitted map on the calibration rows: P = (h A^T) B^T
   fit_gemm<Tin, float>(N, r, H, 1.f, h, H, 1, Af, 1, H, P1, r, 1, st);
   fit_gemm<float, float>(N, H, r, 1.f, P1, r, 1, Bf, 1, r, P, H, 1, st);

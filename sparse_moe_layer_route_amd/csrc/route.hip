@@ -279,17 +279,31 @@ __device__ __forceinline__ void route_topk_token(
   bool in_final = in_routed;
   int slot = rank;
   if (mode == MOE_MODE_STALL_FREE && (routed & ~res_mask) != 0ull) {
-    uint64_t allowed = res_mask & all_e;
-    // fewer than k prefetched experts: the remaining slots take the best
-    // experts outside the set (callers pass sets of at least k experts)
-    if (__popcll(allowed) < k) allowed = all_e;
+    const uint64_t allowed = res_mask & all_e;
+    const int na = __popcll(allowed);
     const bool ok = (allowed >> lane) & 1ull;
-    const int mrank = key_rank(ok ? key : 0ull, E);
-    in_final = ok && mrank < k;
-    slot = mrank;
-    if (__popcll(allowed) > k) {
-      const int mr = ok ? mrank : E;
-      if (lane_logit_at_rank(l, mr, k - 1, E) - lane_logit_at_rank(l, mr, k, E) < margin) flag |= 4u;
+    if (na >= k) {
+      const int mrank = key_rank(ok ? key : 0ull, E);
+      in_final = ok && mrank < k;
+      slot = mrank;
+      if (na > k) {
+        const int mr = ok ? mrank : E;
+        if (lane_logit_at_rank(l, mr, k - 1, E) - lane_logit_at_rank(l, mr, k, E) < margin) flag |= 4u;
+      }
+    } else {
+      // fewer than k prefetched experts (lists of k + delta >= k never are):
+      // all of them are kept and the remaining k - na slots take the best
+      // experts outside the set by router score (flag 32)
+      const bool out = lane < E && !ok;
+      const int nrank = key_rank(out ? key : 0ull, E);  // rank among the experts outside
+      const int need = k - na;
+      in_final = lane < E && (ok || nrank < need);
+      flag |= 32u;
+      if (E > k) {
+        const int nr = out ? nrank : E;
+        if (lane_logit_at_rank(l, nr, need - 1, E) - lane_logit_at_rank(l, nr, need, E) < margin) flag |= 4u;
+      }
+      slot = key_rank(in_final ? key : 0ull, E);
     }
   }
 

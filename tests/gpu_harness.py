@@ -188,38 +188,76 @@ def admissible_topk(l: np.ndarray, chosen: Sequence[int], allowed: Sequence[int]
     return min(l[e] for e in chosen) >= max(l[e] for e in rest) - margin
 
 
+def _flag_gap_ok(gap: float) -> bool:
+    """A flag that one side raises and the other does not must sit on its own
+    threshold: the oracle's fp64 gap within 1% of the margin (fp32 logits
+    carry about 1e-7 of rounding)."""
+    return abs(gap - MARGIN) < 1e-2 * MARGIN
+
+
 def check_decisions(layer: W.Layer, T: int, mode: str, g: GpuRun, dims_over=None,
                     x_np=None) -> dict:
     """Routing decisions for all T tokens: bit-exact unless the oracle flags a
-    near-tie; admissible otherwise.  Returns counts."""
+    near-tie; admissible otherwise.  The GPU's flag bits 1 (route near-tie),
+    4 (substitution near-tie) and 32 (short prefetched set) match the
+    oracle's, except where the deciding gap sits on the margin itself.
+    Returns counts."""
     cfg = layer.cfg
     dd = dims_dict(cfg, **(dims_over or {}))
     k, E = dd["top_k"], dd["n_experts"]
     X = O.decode(layer.x(T) if x_np is None else x_np, dd["dtype"])
     l = O.router_logits(X, O.decode(layer.w_router(), dd["dtype"]))
     np.testing.assert_allclose(g.logits, l, rtol=1e-4, atol=2e-5 * max(1.0, np.abs(l).max()))
-    n_flag = n_exact = 0
+    n_flag = n_exact = n_sub = n_short = 0
     res = layer.resident()
     for t in range(T):
         ids, w, mass, fl = O.route_token(l[t], k, dd["renormalize"], MARGIN)
-        final, allowed, f2 = list(ids), list(range(E)), False
+        order = O.rank_experts(l[t])
+        final, f2, short = list(ids), False, False
+        gaps = {1: l[t][order[k - 1]] - l[t][order[k]] if k < E else np.inf}
         if mode == "stall_free":
             kp = {e for e in range(E) if (g.masks[t] >> e) & 1}
             S, f2 = O.stall_free_select(ids, l[t], kp, MARGIN)
+            if len(S) < k:
+                short = True
+                n_short += 1
+                S, f2 = O.stall_free_fill(S, l[t], k, MARGIN)
+                rest = [e for e in order if e not in kp]
+                need = k - len(kp)
+                gaps[4] = l[t][rest[need - 1]] - l[t][rest[need]] if len(rest) > need else np.inf
+            elif not set(ids) <= kp:
+                cand = [e for e in order if e in kp]
+                gaps[4] = l[t][cand[k - 1]] - l[t][cand[k]] if len(cand) > k else np.inf
             final = sorted(S, key=lambda e: (-l[t][e], e))
-            if not set(ids) <= kp:
-                allowed = sorted(kp)
+            n_sub += len(set(final) - set(ids))
         gids = [int(e) for e in g.ids[t]]
         if fl or f2:
             n_flag += 1
-            if mode == "stall_free":
+            if mode == "stall_free" and short:
+                # every prefetched expert kept, the rest a top set of the others
+                assert kp <= set(gids), (t, gids, final)
+                assert admissible_topk(l[t], [e for e in gids if e not in kp],
+                                       [e for e in range(E) if e not in kp], MARGIN), (t, gids, final)
+            elif mode == "stall_free" and not set(ids) <= kp:
+                assert admissible_topk(l[t], gids, sorted(kp), MARGIN), (t, gids, final)
+            elif mode == "stall_free":
+                # a route near-tie decides whether a substitution happens at all
                 assert admissible_topk(l[t], gids, sorted(kp), MARGIN) or \
                     admissible_topk(l[t], gids, list(range(E)), MARGIN), (t, gids, final)
             else:
-                assert admissible_topk(l[t], gids, allowed, MARGIN), (t, gids, final)
+                assert admissible_topk(l[t], gids, list(range(E)), MARGIN), (t, gids, final)
         else:
             n_exact += 1
             assert gids == final, (t, gids, final)
+        # flag bits against the oracle's
+        want = (O.FLAG_ROUTE if fl else 0) | (O.FLAG_SUBST if f2 else 0) | (O.FLAG_SHORT if short else 0)
+        got = int(g.flags[t]) & (O.FLAG_ROUTE | O.FLAG_SUBST | O.FLAG_SHORT)
+        for bit in (O.FLAG_ROUTE, O.FLAG_SUBST):
+            if (got ^ want) & bit:
+                if bit == O.FLAG_SUBST and fl:
+                    continue  # a route near-tie decides whether anything is substituted
+                assert bit in gaps and _flag_gap_ok(gaps[bit]), (t, bit, got, want, gaps)
+        assert bool(got & O.FLAG_SHORT) == short, t
         # slots are ordered by (-logit, id)
         assert all((l[t][gids[j]], -gids[j]) >= (l[t][gids[j + 1]], -gids[j + 1]) for j in range(k - 1)) \
             or (fl or f2)
@@ -237,7 +275,7 @@ def check_decisions(layer: W.Layer, T: int, mode: str, g: GpuRun, dims_over=None
     off, perm, inv = O.permute(g.ids, g.exact, E)
     np.testing.assert_array_equal(g.offsets, off)
     np.testing.assert_array_equal(g.perm, perm)
-    return dict(flagged=n_flag, exact=n_exact)
+    return dict(flagged=n_flag, exact=n_exact, substituted_slots=n_sub, short_sets=n_short)
 
 
 def oracle_forward_forced(layer: W.Layer, T: int, mode: str, g: GpuRun, sample: Sequence[int],
@@ -259,16 +297,22 @@ def oracle_forward_forced(layer: W.Layer, T: int, mode: str, g: GpuRun, sample: 
 
 def check_floe_masks(layer: W.Layer, g: GpuRun, ref: dict, sample: Sequence[int]):
     """FloE kept channels: exact where the oracle sees no near-tie at the
-    mask edge; admissible within the margin otherwise."""
+    mask edge; admissible within the margin otherwise.  Flag bit 8 of a token
+    matches the oracle's (some pair of the token at a near-tie), except where
+    that pair's gap sits on the margin itself."""
     n_keep = g.keep.shape[2]
     n_tie = 0
     for i, t in enumerate(sample):
+        any_edge, gaps = False, []
         for j in range(layer.cfg.top_k):
             u = ref["floe_u"][(i, j)]
             gk = np.asarray(g.keep[t, j])
             order = sorted(range(len(u)), key=lambda c: (-abs(u[c]), c))
             want = np.sort(order[:n_keep])
-            edge = n_keep < len(u) and abs(u[order[n_keep - 1]]) - abs(u[order[n_keep]]) < MARGIN
+            gap = abs(u[order[n_keep - 1]]) - abs(u[order[n_keep]]) if n_keep < len(u) else np.inf
+            edge = gap < MARGIN
+            gaps.append(gap)
+            any_edge |= edge
             assert np.all(np.diff(gk) > 0), "kept channels ascending and distinct"
             if edge:
                 n_tie += 1
@@ -276,4 +320,6 @@ def check_floe_masks(layer: W.Layer, g: GpuRun, ref: dict, sample: Sequence[int]
                 assert np.abs(u[mask]).min() >= np.abs(u[~mask]).max() - MARGIN
             else:
                 np.testing.assert_array_equal(gk, want)
+        if bool(g.flags[t] & O.FLAG_FLOE) != any_edge:
+            assert any(abs(gp - MARGIN) < 1e-2 * MARGIN for gp in gaps), (t, gaps)
     return n_tie
