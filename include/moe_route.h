@@ -55,6 +55,8 @@ extern "C" {
 #define MOE_MAX_TOPK 8
 #define MOE_MAX_LORE_RANK 64
 #define MOE_FLOE_MAX_DIM 16384 /* MOE_MODE_FLOE: inter and hidden at most this */
+/* Scratch bytes per GPU of moe_layer_forward_noalloc (128 MiB). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 
 typedef enum {
   MOE_OK = 0,
@@ -358,6 +360,26 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, int32_t T, const void* x,
                                int64_t resident_stride, moe_mode_t mode, void* out,
                                const moe_debug_t* dbg_opt, void* ws, size_t ws_bytes,
                                void* stream);
+
+/* moe_layer_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the workspace taken from a
+ * scratch array of MOE_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on, from that GPU's first call until the process ends.  The
+ * call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); the caller still owns x, out, the weights and the masks.
+ * MOE_EWORKSPACE when moe_workspace_size(dims, T, mode) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES (e.g. 4096 Granite-shaped prefill tokens need
+ * 225 MiB; every decode batch of the five workloads fits); MOE_EHIP when the
+ * scratch array's device address cannot be obtained.  All calls on one GPU
+ * share its array, which keeps the last call's contents: calls on one
+ * stream are ordered, but calls that overlap on one GPU (other streams,
+ * other host threads) race and must be serialised by the caller.  No
+ * debug copies. */
+moe_status_t moe_layer_forward_noalloc(const moe_dims_t* dims, int32_t T, const void* x,
+                                       const moe_weights_t* w, const uint64_t* resident,
+                                       int64_t resident_stride, moe_mode_t mode, void* out,
+                                       void* stream);
 
 #ifdef __cplusplus
 }

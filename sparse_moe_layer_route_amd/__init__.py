@@ -6,4 +6,5 @@ from .binding import (  # noqa: F401
     moe_pack_size, moe_pack_weights, pack_weights, LAYOUTS, moe_permute,
     moe_floe_predict, moe_floe_pack, moe_lore_targets, moe_lore_fit_size, moe_lore_fit,
     moe_expert_ffn, moe_lore_surrogate, moe_combine, moe_layer_forward, weights_struct,
+    moe_layer_forward_noalloc, NOALLOC_SCRATCH_BYTES,
 )

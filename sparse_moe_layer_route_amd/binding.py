@@ -88,6 +88,7 @@ def _load():
         "moe_lore_fit": ([D, I32, P, P, I32, I32, I32, P, P, P, P, P, P, SZ, P], ctypes.c_int),
         "moe_combine": ([D, I32, P, P, P, P, P, P, P, P, P], ctypes.c_int),
         "moe_layer_forward": ([D, I32, P, Wp, P, I64, ctypes.c_int, P, Dbg, P, SZ, P], ctypes.c_int),
+        "moe_layer_forward_noalloc": ([D, I32, P, Wp, P, I64, ctypes.c_int, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -101,7 +102,7 @@ EXPORTED = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_r
             "moe_prefetch_mask", "moe_prefetch_adaptive", "moe_pack_size", "moe_pack_weights",
             "moe_permute", "moe_floe_predict", "moe_floe_pack", "moe_lore_targets",
             "moe_lore_fit_size", "moe_lore_fit", "moe_expert_ffn", "moe_lore_surrogate",
-            "moe_combine", "moe_layer_forward")
+            "moe_combine", "moe_layer_forward", "moe_layer_forward_noalloc")
 
 
 # ------------------------------------------------------------------ helpers --
@@ -317,3 +318,15 @@ def moe_layer_forward(dims, T, x, weights, resident, resident_stride, mode, out,
     _check(_lib.moe_layer_forward(ctypes.byref(_dims(dims)), T, _ptr(x), ctypes.byref(ws_struct),
                                   _ptr(resident), resident_stride, _mode(mode), _ptr(out), dbg,
                                   _ptr(ws), ws.numel(), _stream(stream)), "moe_layer_forward")
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20   # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def moe_layer_forward_noalloc(dims, T, x, weights, resident, resident_stride, mode, out,
+                              stream=None):
+    ws_struct = weights if isinstance(weights, MoeWeights) else weights_struct(weights)
+    _check(_lib.moe_layer_forward_noalloc(ctypes.byref(_dims(dims)), T, _ptr(x),
+                                          ctypes.byref(ws_struct), _ptr(resident), resident_stride,
+                                          _mode(mode), _ptr(out), _stream(stream)),
+           "moe_layer_forward_noalloc")

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "common.h"
 
@@ -539,10 +540,16 @@ moe_status_t moe_combine(const moe_dims_t* dims, int32_t T, const float* y_perm,
                                    (hipStream_t)stream));
 }
 
-moe_status_t moe_layer_forward(const moe_dims_t* dims, int32_t T, const void* x,
-                               const moe_weights_t* w, const uint64_t* resident,
-                               int64_t resident_stride, moe_mode_t mode, void* out,
-                               const moe_debug_t* dbg, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by moe_layer_forward and its allocation-free
+// variant (everything except the workspace).
+moe_status_t check_forward(const moe_dims_t* dims, int32_t T, const void* x,
+                           const moe_weights_t* w, const uint64_t* resident,
+                           int64_t resident_stride, moe_mode_t mode, const void* out,
+                           const moe_debug_t* dbg) {
   moe_status_t st = check_dims(dims);
   if (st != MOE_OK) return st;
   if ((st = check_mode(dims, mode)) != MOE_OK) return st;
@@ -550,7 +557,7 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, int32_t T, const void* x,
   if (T < 0) return MOE_EINVAL;
   if (!tokens_fit(*dims, T)) return MOE_EUNSUPPORTED;
   if (mode == MOE_MODE_FLOE && (int64_t)T * dims->top_k > kFloeMaxPairs) return MOE_EUNSUPPORTED;
-  if (!ok_ptr(x) || !ok_ptr(out) || !ok_ptr(ws)) return MOE_EINVAL;
+  if (!ok_ptr(x) || !ok_ptr(out)) return MOE_EINVAL;
   const bool needs_mask = mode == MOE_MODE_LORE || mode == MOE_MODE_STALL_FREE;
   if (needs_mask && (!ok_ptr(resident) || (resident_stride != 0 && resident_stride != 1)))
     return MOE_EINVAL;
@@ -560,10 +567,14 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, int32_t T, const void* x,
         !ok_opt(dbg->expert_offsets) || !ok_opt(dbg->perm) || !ok_opt(dbg->floe_keep))
       return MOE_EINVAL;
   }
-  const Plan p = make_plan(*dims, T, mode);
-  if (ws_bytes < p.total) return MOE_EWORKSPACE;
-  if (T == 0) return MOE_OK;
+  return MOE_OK;
+}
 
+// The forward after its checks, on the workspace `ws` laid out by plan p.
+moe_status_t layer_forward_impl(const moe_dims_t* dims, int32_t T, const void* x,
+                                const moe_weights_t* w, const uint64_t* resident,
+                                int64_t resident_stride, moe_mode_t mode, void* out,
+                                const moe_debug_t* dbg, void* ws, const Plan& p, void* stream) {
   const moe_dims_t& d = *dims;
   hipStream_t s = (hipStream_t)stream;
   const int k = d.top_k, E = d.n_experts, P = T * k;
@@ -635,6 +646,66 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, int32_t T, const void* x,
     if (keep) cp(dbg->floe_keep, keep, (size_t)P * d.floe_keep * 4);
   }
   return hip_status(e);
+}
+
+// Scratch memory of moe_layer_forward_noalloc: one array per GPU the library
+// runs on, held until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol); it
+// uses the device address that hipGetSymbolAddress returns, looked up once
+// per device on that device's first call and kept here.
+constexpr size_t kNoallocBytes = MOE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kNoallocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, or nullptr on a HIP error.
+void* noalloc_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_layer_forward(const moe_dims_t* dims, int32_t T, const void* x,
+                               const moe_weights_t* w, const uint64_t* resident,
+                               int64_t resident_stride, moe_mode_t mode, void* out,
+                               const moe_debug_t* dbg, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_forward(dims, T, x, w, resident, resident_stride, mode, out, dbg);
+  if (st != MOE_OK) return st;
+  if (!ok_ptr(ws)) return MOE_EINVAL;
+  const Plan p = make_plan(*dims, T, mode);
+  if (ws_bytes < p.total) return MOE_EWORKSPACE;
+  if (T == 0) return MOE_OK;
+  return layer_forward_impl(dims, T, x, w, resident, resident_stride, mode, out, dbg, ws, p,
+                            stream);
+}
+
+moe_status_t moe_layer_forward_noalloc(const moe_dims_t* dims, int32_t T, const void* x,
+                                       const moe_weights_t* w, const uint64_t* resident,
+                                       int64_t resident_stride, moe_mode_t mode, void* out,
+                                       void* stream) {
+  moe_status_t st = check_forward(dims, T, x, w, resident, resident_stride, mode, out, nullptr);
+  if (st != MOE_OK) return st;
+  const Plan p = make_plan(*dims, T, mode);
+  if (p.total > kNoallocBytes) return MOE_EWORKSPACE;
+  if (T == 0) return MOE_OK;
+  // No workspace region has to start at zero: the one counter the router's
+  // launches share is zeroed by the first of them on every call.
+  void* ws = noalloc_scratch();
+  if (!ws) return MOE_EHIP;
+  return layer_forward_impl(dims, T, x, w, resident, resident_stride, mode, out, nullptr, ws, p,
+                            stream);
 }
 
 }  // extern "C"

@@ -239,3 +239,19 @@ def test_entry_point_null_checks():
     w = _weights()
     assert L.moe_expert_ffn(ctypes.byref(d), 4, FAKE, ctypes.byref(w), 0, FAKE, FAKE, FAKE, FAKE, FAKE,
                             None, None, FAKE, 0, None) == B.MOE_EWORKSPACE
+
+
+def test_noalloc_forward_host_checks():
+    """The allocation-free forward validates like moe_layer_forward and
+    refuses a batch whose workspace exceeds its scratch array before
+    touching the GPU (T = 0 returns at once)."""
+    f = L.moe_layer_forward_noalloc
+    d = dims()
+    w = _weights()
+    assert f(ctypes.byref(d), 16, FAKE, ctypes.byref(w), None, 0, 1, FAKE, None) == B.MOE_EINVAL
+    assert f(ctypes.byref(d), 16, FAKE, ctypes.byref(w), FAKE, 0, 1, FAKE + 2, None) == B.MOE_EINVAL
+    assert f(ctypes.byref(d), 0, FAKE, ctypes.byref(w), FAKE, 0, 1, FAKE, None) == B.MOE_OK
+    big = dims(hidden=4096, inter=4096, n_shared=0, shared_inter=0)
+    T = 8192
+    assert ws_size(big, T, 0)[1] > M.NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), T, FAKE, ctypes.byref(_weights()), None, 0, 0, FAKE, None) == B.MOE_EWORKSPACE
