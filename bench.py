@@ -6,11 +6,12 @@
 One step = one moe_layer_forward over one batch of synthetic tokens (router,
 softmax/top-k, residency split, permutation, expert + shared FFNs, LoRE
 surrogate fused into the combine), eager launches on torch's current stream,
-inputs and weights resident in HBM.  The headline workload is the
-DeepSeek-V2-Lite-shaped decode layer (H=2048, 64 experts top-6, I=1408, two
-shared experts, 50% of experts resident, LoRE rank 16) at 64 tokens.  Steps
-cycle through enough copies of the layer's weights that the 256 MB Infinity
-Cache cannot serve one step's weights to the next.
+inputs and weights resident in HBM.  The headline workload is the largest
+layer: the Qwen2-57B-A14B-shaped decode layer (H=3584, 64 experts top-8,
+I=2560, one shared expert of 20480 channels with a sigmoid gate,
+renormalised weights) at 256 tokens, every routed expert computed exactly.
+Steps cycle through enough copies of the layer's weights that the 256 MB
+Infinity Cache cannot serve one step's weights to the next.
 
 Prints ONE JSON line.  `roofline` is for the dominant kernel (the expert
 gate/up projection): algorithmic bytes (or flops) per launch divided by its
@@ -43,9 +44,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="dsv2_lite")
-    ap.add_argument("--tokens", type=int, default=64)
-    ap.add_argument("--mode", default="lore")
+    ap.add_argument("--workload", default="qwen2_57b")
+    ap.add_argument("--tokens", type=int, default=256)
+    ap.add_argument("--mode", default="standard")
     ap.add_argument("--quick", action="store_true", help="headline only (no other workloads)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--copy-probe", action="store_true",
@@ -62,6 +63,8 @@ COPY_BYTES = 256 << 20         # copy-probe size: 256 MiB read + 256 MiB written
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_expert_gate_up_dsv2_lite_T64_lore.md")
 TRAFFIC_FILES = {
     ("dsv2_lite", 64, "lore"): TRAFFIC_FILE,
+    ("qwen2_57b", 256, "standard"): os.path.join(
+        ROOT, "profiles", "traffic_expert_gate_up_qwen2_57b_T256.md"),
     ("granite_prefill", 4096, "standard"): os.path.join(
         ROOT, "profiles", "traffic_expert_gate_up_granite_prefill_T4096.md"),
 }
@@ -169,7 +172,7 @@ def step_traffic(cfg, T, mode, ids, exact, keep_count=None):
 
 
 # ------------------------------------------------------------- measurement --
-def measure(name, T, mode, steps, warmup, ev=None, want_roofline=False):
+def measure(name, T, mode, steps, warmup, ev=None, want_roofline=False, layer=None):
     import numpy as np
     import torch
 
@@ -177,7 +180,7 @@ def measure(name, T, mode, steps, warmup, ev=None, want_roofline=False):
     from workloads.device import dims_dict, mask_tensor, tensor, upload
     import sparse_moe_layer_route_amd as M
 
-    layer = W.make_layer(name)
+    layer = layer if layer is not None else W.make_layer(name)
     cfg = layer.cfg
     w0 = upload(layer, "cuda")
     dd = M.Dims(**dims_dict(cfg))
@@ -558,7 +561,10 @@ def main():
         copy_probe()
         return
     ev = HipEvents()
-    head = measure(args.workload, args.tokens, args.mode, args.steps, args.warmup, ev=ev)
+    import workloads as W
+    head_layer = W.make_layer(args.workload)
+    head = measure(args.workload, args.tokens, args.mode, args.steps, args.warmup, ev=ev,
+                   layer=head_layer)
     also = []
     if not args.quick:
         plan = [("dsv2_lite", 1, "standard"), ("dsv2_lite", 1, "lore"),
@@ -582,9 +588,9 @@ def main():
                   f"{r['tokens_per_s']:.0f} tok/s, {r['step_gbs']:.0f} GB/s"
                   + (f", {r['roofline']['kernel']} {r['roofline']['frac']*100:.1f}% of {r['roofline']['bound']}"
                      if 'roofline' in r else ""), file=sys.stderr, flush=True)
-        r = measure_prefetch_adaptive("granite_prefill", 4096, args.steps, min(args.warmup, 5))
+        r = measure_prefetch_adaptive("granite_prefill_distilled", 4096, args.steps, min(args.warmup, 5))
         also.append(r)
-        print(f"# granite_prefill T=4096 adaptive prefetch: {r['us_per_call']:.1f} us/call, "
+        print(f"# granite_prefill_distilled T=4096 adaptive prefetch: {r['us_per_call']:.1f} us/call, "
               f"{r['gbs']:.0f} GB/s, mean budget {r['mean_budget']:.2f}, overlap {r['overlap']:.3f}, "
               f"covered {r['covered']:.3f}", file=sys.stderr, flush=True)
         r = measure_floe_predict(args.steps, min(args.warmup, 5))
@@ -599,7 +605,8 @@ def main():
               f"{r['targets_ms']:.2f} ms; " + "; ".join(
                   f"rank {f['rank']}: {f['ms']:.1f} ms, error {f['rel_error']:.3f}" for f in r["fits"]),
               file=sys.stderr, flush=True)
-    cpu = None if args.no_cpu else cpu_baseline(args.workload, args.tokens, args.mode)
+    cpu = None if args.no_cpu else cpu_baseline(args.workload, args.tokens, args.mode,
+                                                layer=head_layer)
     line = {
         "metric": METRIC,
         "value": head["tokens_per_s"],
@@ -612,8 +619,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) hidden states, random 50% resident mask)",
-        "config": {"workload": f"{args.workload} MoE layer decode, T={args.tokens}, mode={args.mode}",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) hidden states)",
+        "config": {"workload": f"{args.workload} MoE layer, T={args.tokens}, mode={args.mode}",
                    "tokens": args.tokens, "mode": args.mode, "weight_copies": head["weight_copies"],
                    "step_bytes": head["step_bytes"], "step_gbs": head["step_gbs"],
                    "step_hbm_frac": head["step_hbm_frac"]},
