@@ -14,17 +14,20 @@
 // a block pulls 32 KiB per stage from L2 for 4.2 MFLOP (128 flop/B).  A
 // (weights) and B (token rows, gathered through the permutation) are both
 // k-contiguous in HBM.  Stages move global -> LDS directly (16-byte LDS DMA
-// loads, no register staging) into a 4-deep ring, so three stages are in
-// flight while one feeds the MFMAs: the L2/HBM latency of a stage (microseconds under load)
-// is covered by three stages of math.  Each 64-byte LDS row holds four
-// 16-byte k chunks stored at chunk ^ ((row / 2) % 4): a 16-byte LDS read is
-// served eight lanes at a time over 32 banks, and the eight rows of one such
-// group then cover all 32 banks once.  Ordering is explicit: a thread
-// waits for its own DMA loads with a vmcnt wait, then a workgroup barrier
-// publishes the stage; a slot is refilled only after the barrier that ends
-// its last read.  A long contraction over few tiles (the shared experts' down
-// projection at a few hundred tokens) is split over grid.y into partial sums
-// that a small kernel adds up.
+// loads, no register staging) into two rings: weight rows 5 deep (four
+// stages in flight: an expert's first tiles fetch its weights from HBM) and
+// token rows 4 deep (three in flight; they are mostly cache hits).  The
+// loop is bound by the latency of these loads rather than by LDS bandwidth
+// (the LDS is busy about an eighth of the time): three stages in flight
+// instead of two made the gate/up GEMM a fifth faster.  Each 64-byte LDS row
+// holds four 16-byte k chunks stored at chunk ^ ((row / 2) % 4): a 16-byte
+// LDS read is served eight lanes at a time over 32 banks, and the eight rows
+// of one such group then cover all 32 banks once.  Ordering is explicit: a
+// thread waits for its own DMA loads with a vmcnt wait, then a workgroup
+// barrier publishes the stage; a slot is refilled only after the barrier
+// that ends its last read.  A long contraction over few tiles (the shared
+// experts' down projection at a few hundred tokens) is split over grid.y
+// into partial sums that a small kernel adds up.
 //
 // Tiles are (segment m-tile, weight n-tile) pairs enumerated expert by expert;
 // block ids are remapped so each XCD (blocks are dealt to the 8 XCDs round-
@@ -41,7 +44,14 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int GN = 256;        // tokens per block tile
 constexpr int GK = 32;         // k per stage
-constexpr int GSTAGES = 4;     // LDS ring depth (stages in flight: GSTAGES - 1)
+#ifndef GEMM_WSTAGES
+#define GEMM_WSTAGES 4
+#endif
+#ifndef GEMM_TSTAGES
+#define GEMM_TSTAGES 5
+#endif
+constexpr int GWST = GEMM_WSTAGES;  // weight-row LDS ring depth (stages in flight: GWST - 1)
+constexpr int GTST = GEMM_TSTAGES;  // token-row LDS ring depth (stages in flight: GTST - 1)
 constexpr int GROWS = 512;     // LDS rows per stage: 256 weight + 256 token
 constexpr int GTHREADS = 512;  // 8 waves: two per SIMD
 constexpr int GWAVES = GTHREADS / 64;
@@ -96,6 +106,14 @@ __device__ __forceinline__ u32x4 lds_read16_at(uint32_t base) {
   return r;
 }
 
+// 8-byte LDS store issued outside the compiler's wait-count tracking, like
+// the reads above (stores have no result register).
+__device__ __forceinline__ void lds_write8(uint32_t addr, uint32_t lo, uint32_t hi) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = {lo, hi};
+  asm volatile("ds_write_b64 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
 // Wait for this wave's LDS reads; the fragments are in/out operands so no
 // use of them can be scheduled above the wait.
 template <int NA, int NB>
@@ -146,7 +164,7 @@ __device__ __forceinline__ int seg_table_build(const GemmArgs& a, SegTable& t) {
 struct TileMeta {
   int g, row0, lim, seg0, n_idx;
 };
-constexpr int GEMM_MAX_TILES = 16;  // tiles per persistent block (the grid grows beyond)
+constexpr int GEMM_MAX_TILES = 14;  // tiles per persistent block (the grid grows beyond)
 struct TileTable {
   int g[GEMM_MAX_TILES], row0[GEMM_MAX_TILES], lim[GEMM_MAX_TILES], seg0[GEMM_MAX_TILES],
       n_idx[GEMM_MAX_TILES];
@@ -222,8 +240,6 @@ __device__ __forceinline__ TileMeta tile_get(const TileTable& tt, int j) {
 // (LDS DMA loads complete in issue order).
 #define GEMM_VMCNT(N) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory")
 // at most two later stages of this thread's DMA loads still pending
-#define GEMM_VMCNT_STAGES2() GEMM_VMCNT(2 * NQ)
-#define GEMM_VMCNT_STAGES1() GEMM_VMCNT(NQ)
 
 // The GTT token fragments (LDS rows sb + 16j) and NW*WT weight fragments (rows
 // sa + m*MW + 16i) of one stage; row offsets are instruction immediates.
@@ -252,12 +268,14 @@ __device__ __forceinline__ void read_fa(u32x4 (&fa)[NW * WT], uint32_t sa) {
 // of its XCD, strided by the XCD's blocks), and its k stages form one stream
 // through the LDS ring across tile boundaries, so the first stages of the
 // next tile load while the current tile finishes and writes its outputs.
-template <bool GATED>
+// YB (GEMM2 only): the outputs are bf16 rows (a.yb_out), else fp32 (a.y_out).
+template <bool GATED, bool YB = false>
 __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   constexpr int NW = GATED ? 2 : 1;          // weight matrices
   constexpr int MW = GATED ? 128 : 256;      // weight rows per matrix per block
   constexpr int WT = MW / 2 / 16;            // weight tiles per wave per matrix (4 or 8)
-  __shared__ __attribute__((aligned(16))) bf16 lds[GSTAGES][GROWS * GK];
+  __shared__ __attribute__((aligned(16))) bf16 lds_w[GWST][GN * GK];   // 256 weight rows per stage
+  __shared__ __attribute__((aligned(16))) bf16 lds_t[GTST][GN * GK];   // 256 token rows per stage
   __shared__ SegTable seg;
   const int n_tiles = seg_table_build(a, seg) * a.tiles_n;   // every wave: same total
   __syncthreads();
@@ -314,6 +332,13 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   // banks.
   const int chunk = (lane & 3) ^ ((lane >> 3) & 3);
   const bool is_w = wv < GWAVES / 2;
+  // a weight wave issues stage s + GWST - 1 at step s, a token wave stage
+  // s + GTST - 1 (the weights come from HBM on an expert's first tiles and
+  // need the longer lead); before the barrier of step s each thread's own
+  // loads of stage s + 1 must have landed: at most GWST - 3 (GTST - 3) later
+  // stages of its loads may still be pending
+  const int lead = is_w ? GWST - 1 : GTST - 1;
+  static_assert(GWST >= 3 && GTST >= 3 && GWST + GTST <= 9, "ring depths");
   const int wsh = a.packed ? 4 : 0;
   constexpr int NQ = GROWS / 16 / GWAVES;   // DMA instructions per wave per stage
   constexpr int NMF = NW * WT * GTT;        // MFMAs per wave per stage
@@ -363,7 +388,8 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
     return k_lo + dk++;
   };
   auto issue_one = [&](int s, int kstage, int q) __attribute__((always_inline)) {
-    bf16* dst = &lds[s % GSTAGES][(16 * NQ * wv) * GK];
+    bf16* dst = is_w ? &lds_w[s % GWST][(16 * NQ * wv) * GK]
+                     : &lds_t[s % GTST][(16 * NQ * (wv - GWAVES / 2)) * GK];
     const int s_ = kstage / kst, ko = (kstage % kst) * GK;
     // weight k stage stride: 32 elements row-major, a 512-element fragment packed
     const bf16* src = dbase + (is_w ? (int64_t)s_ * a.sub_stride + (ko << wsh)
@@ -391,30 +417,64 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
 
   // epilogue of the compute tile: lane holds weight rows 4*kg..+3 of tile i,
   // token r16 of tile j; then the accumulators restart for the next tile
-  auto epilogue = [&]() __attribute__((always_inline)) {
+  // GEMM2's bf16 rows go through LDS (staged): the wave's 4 KiB region of a
+  // ring slot that the tile's last stage has finished with (nothing refills
+  // it before the next barrier), written in the accumulator layout and read
+  // back row by row, so each global store writes whole 256-byte row
+  // segments instead of 32-byte pieces of 16 rows (the Granite-shaped down
+  // GEMM: 95 -> 85 us).  16-byte chunk c of row r sits at chunk c ^ (r % 16),
+  // so the row reads are free of bank conflicts.  The gate/up epilogue keeps
+  // its direct stores: staging it measured no faster there (the extra
+  // registers spill) and slower on the shared experts' GEMM.
+  auto epilogue = [&](uint32_t ebase, bool staged) __attribute__((always_inline)) {
     const int row_w0 = cm.n_idx * MW;
+    if (YB && staged) {
+      // bf16 rows: columns col0..col0+127, four passes of 16 tokens
+      const int col0 = row_w0 + wm * (MW / 2);
 #pragma unroll
-    for (int j = 0; j < GTT; ++j) {
-      const int tr = cm.row0 + wn * 16 * GTT + 16 * j + r16;   // token row within segment
-      if (tr >= cm.lim) continue;
+      for (int j = 0; j < GTT; ++j) {
+        __builtin_amdgcn_sched_barrier(0);   // one pass at a time (register pressure)
 #pragma unroll
-      for (int i = 0; i < WT; ++i) {
-        const int wr = row_w0 + wm * (MW / 2) + 16 * i + 4 * kg;
-        if (wr >= a.R) continue;
-        if (GATED) {
-          float h[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) h[q] = silu_f(acc[0][i][j][q]) * acc[NW - 1][i][j][q];
-          bf16* dst = a.act_out + (int64_t)(cm.seg0 + tr) * a.ld_out + (int64_t)cm.g * a.col_off + wr;
-          *reinterpret_cast<uint2*>(dst) = make_uint2(f2_to_bf16x2(h[0], h[1]), f2_to_bf16x2(h[2], h[3]));
-        } else if (a.yb_out) {
+        for (int i = 0; i < WT; ++i) {
           const f32x4_t& v = acc[0][i][j];
-          bf16* dst = a.yb_out + (int64_t)(cm.seg0 + tr) * a.R + wr;
-          *reinterpret_cast<uint2*>(dst) = make_uint2(f2_to_bf16x2(v[0], v[1]), f2_to_bf16x2(v[2], v[3]));
-        } else {
-          float* dst = a.y_out + (int64_t)blockIdx.y * a.part_stride + (int64_t)(cm.seg0 + tr) * a.R + wr;
-          *reinterpret_cast<float4*>(dst) =
-              float4{acc[0][i][j][0], acc[0][i][j][1], acc[0][i][j][2], acc[0][i][j][3]};
+          const int c16 = 2 * i + (kg >> 1);
+          lds_write8(ebase + r16 * 256 + ((c16 ^ r16) << 4) + ((kg & 1) << 3),
+                     f2_to_bf16x2(v[0], v[1]), f2_to_bf16x2(v[2], v[3]));
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {   // one 4-row group at a time (register pressure)
+          const int row = (lane >> 4) + 4 * q, c = lane & 15;
+          u32x4 v[1] = {lds_read16(ebase + row * 256 + ((c ^ row) << 4))};
+          lds_wait_all(v, v);
+          const int tr = cm.row0 + wn * 16 * GTT + 16 * j + row;
+          const int col = col0 + 8 * c;
+          if (tr < cm.lim && col < a.R) {
+            bf16* dst = a.yb_out + (int64_t)(cm.seg0 + tr) * a.R + col;
+            *reinterpret_cast<u32x4*>(dst) = v[0];
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < GTT; ++j) {
+        const int tr = cm.row0 + wn * 16 * GTT + 16 * j + r16;   // token row within segment
+        if (tr >= cm.lim) continue;
+#pragma unroll
+        for (int i = 0; i < WT; ++i) {
+          const int wr = row_w0 + wm * (MW / 2) + 16 * i + 4 * kg;
+          if (wr >= a.R) continue;
+          if (GATED) {
+            float h[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) h[q] = silu_f(acc[0][i][j][q]) * acc[NW - 1][i][j][q];
+            bf16* dst = a.act_out + (int64_t)(cm.seg0 + tr) * a.ld_out + (int64_t)cm.g * a.col_off + wr;
+            *reinterpret_cast<uint2*>(dst) = make_uint2(f2_to_bf16x2(h[0], h[1]), f2_to_bf16x2(h[2], h[3]));
+          } else {   // fp32 rows (bf16 rows are always staged: they come with k-split 1)
+            float* dst = a.y_out + (int64_t)blockIdx.y * a.part_stride + (int64_t)(cm.seg0 + tr) * a.R + wr;
+            *reinterpret_cast<float4*>(dst) =
+                float4{acc[0][i][j][0], acc[0][i][j][1], acc[0][i][j][2], acc[0][i][j][3]};
+          }
         }
       }
     }
@@ -435,7 +495,7 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
 
   if (nst == 0) {  // an empty k range (k split): the partial sums are zero
     for (int j = 0; j < n_my; ++j) {
-      epilogue();
+      epilogue(0u, false);
       next_compute_tile();
     }
     return;
@@ -443,7 +503,8 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
 
   // byte address of this lane's fragment slot: logical chunk kg of row r
   // lives at physical chunk kg ^ ((r/2) % 4); rows here are 16-aligned + r16
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)&lds[0][0];
+  const uint32_t ldsw0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)&lds_w[0][0];
+  const uint32_t ldst0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)&lds_t[0][0];
   uint32_t lane_off = (uint32_t)(r16 * GK * 2 + ((kg ^ ((r16 >> 1) & 3)) * 16));
 
   // Stage s's fragments sit in one register set while the next stage's are
@@ -454,9 +515,10 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
 #define GEMM_READ(FB, FA, st_)                                                          \
   {                                                                                     \
     asm volatile("" : "+v"(lane_off)); /* addresses formed here, not kept live */       \
-    const uint32_t sl = lds0 + (uint32_t)(((st_) % GSTAGES) * GROWS * GK * 2) + lane_off; \
-    read_fb<0, GTT>(FB, sl + (uint32_t)((256 + wn * 16 * GTT) * GK * 2));              \
-    read_fa<NW, WT, MW, 0>(FA, sl + (uint32_t)(wm * (MW / 2) * GK * 2));               \
+    const uint32_t slt = ldst0 + (uint32_t)(((st_) % GTST) * GN * GK * 2) + lane_off;    \
+    const uint32_t slw = ldsw0 + (uint32_t)(((st_) % GWST) * GN * GK * 2) + lane_off;    \
+    read_fb<0, GTT>(FB, slt + (uint32_t)(wn * 16 * GTT * GK * 2));                      \
+    read_fa<NW, WT, MW, 0>(FA, slw + (uint32_t)(wm * (MW / 2) * GK * 2));               \
   }
 #define GEMM_MFMA_PART(FB, FA, q)                                                       \
   _Pragma("unroll") for (int t = 0; t < NMF / NQ; ++t) {                                \
@@ -473,34 +535,36 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
 #define GEMM_STEP(FBc, FAc, FBn, FAn, st_)                                              \
   {                                                                                     \
     const bool last = ++ck == nst;                                                      \
-    GEMM_VMCNT_STAGES1();                                                               \
+    if (is_w) GEMM_VMCNT((GWST - 3) * NQ); else GEMM_VMCNT((GTST - 3) * NQ);          \
     __builtin_amdgcn_s_barrier();                                                       \
     if (!last && tok_live) GEMM_READ(FBn, FAn, (st_) + 1);                              \
     const int kref = dma_next();                                                        \
     __builtin_amdgcn_sched_barrier(0); /* reads issue before the MFMAs */              \
     _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                    \
-      issue_one((st_) + GSTAGES - 1, kref, q);                                          \
+      issue_one((st_) + lead, kref, q);                                                 \
       __builtin_amdgcn_sched_barrier(0);                                                \
       if (tok_live) { GEMM_MFMA_PART(FBc, FAc, q); }                                    \
       __builtin_amdgcn_sched_barrier(0);                                                \
     }                                                                                   \
     if (last) {                                                                         \
       ck = 0;                                                                           \
-      epilogue();                                                                       \
+      epilogue(is_w ? ldsw0 + (uint32_t)(((st_) % GWST) * GN * GK * 2 + wv * 4096)        \
+                    : ldst0 + (uint32_t)(((st_) % GTST) * GN * GK * 2 + (wv - 4) * 4096), \
+               true);                                                                   \
       next_compute_tile();                                                              \
-      if (tok_live) GEMM_READ(FBn, FAn, (st_) + 1);                                     \
+      /* unconditional, so the fragment sets are not live across the epilogue */       \
+      GEMM_READ(FBn, FAn, (st_) + 1);                                                   \
     }                                                                                   \
     lds_wait_all(FBn, FAn);                                                             \
   }
   {
     u32x4 fb0[GTT], fa0[NW * WT], fb1[GTT], fa1[NW * WT];
-#pragma unroll
-    for (int s0 = 0; s0 < GSTAGES - 1; ++s0) {
+    for (int s0 = 0; s0 < lead; ++s0) {
       const int kref = dma_next();
 #pragma unroll
       for (int q = 0; q < NQ; ++q) issue_one(s0, kref, q);
     }
-    GEMM_VMCNT_STAGES2();
+    if (is_w) GEMM_VMCNT((GWST - 2) * NQ); else GEMM_VMCNT((GTST - 2) * NQ);   // stage 0 landed
     __builtin_amdgcn_s_barrier();
     if (tok_live) GEMM_READ(fb0, fa0, 0);
     lds_wait_all(fb0, fa0);
@@ -515,8 +579,6 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   GEMM_VMCNT(0);      // no DMA may outlive the workgroup's LDS
 }
 #undef GEMM_VMCNT
-#undef GEMM_VMCNT_STAGES2
-#undef GEMM_VMCNT_STAGES1
 
 // Sum of k-split partials: y[i] = sum_s part[s][i] (float4 per thread).
 __global__ void __launch_bounds__(256)
@@ -620,7 +682,12 @@ hipError_t launch_ffn_gemm(const moe_dims_t& d, int T, const void* x, const moe_
     a.yb_out = a.ksplit > 1 ? nullptr : yb;
     a.part_stride = (int64_t)T * H;
     const int grid = gemm_grid(a.n_blocks, a.ksplit);
-    if (a.n_blocks > 0) ffn_gemm_kernel<false><<<dim3(grid, a.ksplit), GTHREADS, 0, s>>>(a);
+    if (a.n_blocks > 0) {
+      if (a.yb_out)
+        ffn_gemm_kernel<false, true><<<dim3(grid, a.ksplit), GTHREADS, 0, s>>>(a);
+      else
+        ffn_gemm_kernel<false, false><<<dim3(grid, a.ksplit), GTHREADS, 0, s>>>(a);
+    }
     if (a.ksplit > 1) {
       const int64_t n4 = (int64_t)T * H / 4;
       ksplit_reduce_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>(part, n4, a.part_stride,

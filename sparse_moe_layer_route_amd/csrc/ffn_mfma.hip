@@ -48,6 +48,19 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bf16x8_t frag_load(const bf16* p) {
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
 }
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+#ifndef FFN_NT_WEIGHTS
+#define FFN_NT_WEIGHTS 0
+#endif
+// Weight fragments are read once per launch; FFN_NT_WEIGHTS = 1 marks their
+// loads non-temporal (streamed past the caches).
+__device__ __forceinline__ bf16x8_t wfrag_load(const bf16* p) {
+#if FFN_NT_WEIGHTS
+  return __builtin_bit_cast(bf16x8_t, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+#else
+  return frag_load(p);
+#endif
+}
 __device__ __forceinline__ bf16x8_t frag_zero() {
   return __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
 }
@@ -145,9 +158,12 @@ __device__ __forceinline__ void store_bf16x4(bf16* dst, int64_t off, const float
 }
 
 // k-steps per batch of the pipelined loop: two register sets of U steps each.
+#ifndef FFN_UNROLL_SMALL
+#define FFN_UNROLL_SMALL 2
+#endif
 template <int NA>
 struct Unroll {
-  static constexpr int U = NA <= 2 ? 2 : 1;
+  static constexpr int U = NA <= 2 ? FFN_UNROLL_SMALL : 1;
 };
 
 // Wave wk's contiguous share [beg, end) of nsteps k-steps, in nb batches of U.
@@ -211,8 +227,8 @@ __device__ __forceinline__ void up_chunk(const FfnMfmaArgs a, const TileInfo& ti
   _Pragma("unroll") for (int u = 0; u < U; ++u) {                              \
     const int ko = min(kr.beg + (b) * U + u, kr.end - 1) << 5;                 \
     _Pragma("unroll") for (int q = 0; q < RW; ++q) {                           \
-      G[u][q] = frag_load(ag_row[q] + (ko << wsh));                            \
-      UU[u][q] = frag_load(au_row[q] + (ko << wsh));                           \
+      G[u][q] = wfrag_load(ag_row[q] + (ko << wsh));                           \
+      UU[u][q] = wfrag_load(au_row[q] + (ko << wsh));                          \
     }                                                                          \
     _Pragma("unroll") for (int j = 0; j < NA; ++j) X[u][j] = frag_load(xrow[j] + ko); \
   }
@@ -426,7 +442,7 @@ __device__ __forceinline__ void down_chunk(const FfnMfmaArgs a, const TileInfo& 
 #define DN_LOAD(W, B, b)                                                       \
   _Pragma("unroll") for (int u = 0; u < U; ++u) {                              \
     const int ko = min(kr.beg + (b) * U + u, kr.end - 1) << 5;                 \
-    _Pragma("unroll") for (int q = 0; q < RW; ++q) W[u][q] = frag_load(wrow[q] + (ko << wsh)); \
+    _Pragma("unroll") for (int q = 0; q < RW; ++q) W[u][q] = wfrag_load(wrow[q] + (ko << wsh)); \
     _Pragma("unroll") for (int j = 0; j < NA; ++j) B[u][j] = frag_load(bsrc + brow[j] + so + ko); \
   }
 #define DN_MFMA(W, B, b)                                                       \
@@ -554,6 +570,9 @@ __global__ void __launch_bounds__(256) FFN_DOWN_OCCUPANCY ffn_down_mfma_kernel(F
 #ifndef FFN_LONG_DOWN_RW
 #define FFN_LONG_DOWN_RW 4
 #endif
+#ifndef FFN_LONG_UP_RW
+#define FFN_LONG_UP_RW 2
+#endif
 
 // Row tiles per wave.  Short segments (the decode case, a few tokens per
 // expert): gate/up 1, down 2 up to 4 token tiles (activation fragments reused
@@ -562,7 +581,7 @@ __global__ void __launch_bounds__(256) FFN_DOWN_OCCUPANCY ffn_down_mfma_kernel(F
 // and down 4 up to 4 token tiles.
 template <int NTT, bool LONG>
 struct RowTiles {
-  static constexpr int UP = (LONG && NTT <= 4) ? 2 : 1;
+  static constexpr int UP = (LONG && NTT <= 4) ? FFN_LONG_UP_RW : 1;
   static constexpr int DOWN = NTT <= 4 ? (LONG ? FFN_LONG_DOWN_RW : 2) : 1;
 };
 
@@ -582,6 +601,12 @@ static void launch_kernels(FfnMfmaArgs up, FfnMfmaArgs dn, hipStream_t s, int wh
   if ((which & 2) && n_dn > 0) ffn_down_mfma_kernel<NTT, WM, WK, RW><<<n_dn, 256, 0, s>>>(dn);
 }
 
+// Row strips per block for long segments up to 4 token tiles (the rest of
+// the 4 waves split K).
+#ifndef FFN_LONG_WM
+#define FFN_LONG_WM 1
+#endif
+
 // which: bit 0 = gate/up kernel, bit 1 = down kernel.  lore: LoRE tiles on.
 hipError_t launch_ffn_mfma(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
                            const int32_t* offsets, const int32_t* moffsets, const int32_t* perm,
@@ -596,7 +621,8 @@ hipError_t launch_ffn_mfma(const moe_dims_t& d, int T, const void* x, const moe_
   const int ntiles_tok = (cover + 15) / 16;
   int NTT = 1;
   while (NTT < ntiles_tok && NTT < 16) NTT <<= 1;
-  const int WM = NTT <= 4 ? 1 : (NTT == 8 ? 2 : 4);
+  const bool long_seg = routed && (int64_t)T * d.top_k > 16LL * d.n_experts;
+  const int WM = NTT <= 4 ? (long_seg ? FFN_LONG_WM : 1) : (NTT == 8 ? 2 : 4);
   const int rows = 16 * WM;
   const int slots = std::min(d.n_experts, T * d.top_k);
   FfnMfmaArgs up{};
@@ -637,12 +663,12 @@ hipError_t launch_ffn_mfma(const moe_dims_t& d, int T, const void* x, const moe_
   dn.wl = (const bf16*)w.lore_B;
   dn.n_shared_seg = (shared && d.n_shared > 0) ? 1 : 0;
   // long segments: more than one token tile per routed expert on average
-  const bool long_seg = routed && (int64_t)T * d.top_k > 16LL * d.n_experts;
   if (long_seg) {
+    constexpr int LWM = FFN_LONG_WM, LWK = 4 / FFN_LONG_WM;
     switch (NTT) {
-      case 1: launch_kernels<1, 1, 4, true>(up, dn, s, which); break;
-      case 2: launch_kernels<2, 1, 4, true>(up, dn, s, which); break;
-      case 4: launch_kernels<4, 1, 4, true>(up, dn, s, which); break;
+      case 1: launch_kernels<1, LWM, LWK, true>(up, dn, s, which); break;
+      case 2: launch_kernels<2, LWM, LWK, true>(up, dn, s, which); break;
+      case 4: launch_kernels<4, LWM, LWK, true>(up, dn, s, which); break;
       case 8: launch_kernels<8, 2, 2, true>(up, dn, s, which); break;
       default: launch_kernels<16, 4, 1, true>(up, dn, s, which); break;
     }
