@@ -549,6 +549,145 @@ def measure_lore_fit(name="dsv2_lite", expert=0, ranks=(8, 16, 32), cols=64, n_i
     return out
 
 
+def measure_offload(ev, name="dsv2_lite", tokens=(1, 8), steps=20):
+    """Exact execution of missed experts (moe_layer_forward_offload) with the
+    layer's resident mask: the cost table is calibrated here (host -> GPU
+    copy rate of one expert, the host FFN on one expert with one and four
+    pairs, the GPU forward per active expert), then each batch runs under
+    four plans: fetch every missed expert, run every one on the host, the
+    cost rule, and the cost rule with the link and the host as queues.  Wall time per call (through a final synchronisation),
+    with the LoRE-mode forward (misses -> surrogate, no transfers) and the
+    all-resident STANDARD forward of the same batch as context."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from workloads.device import dims_dict, mask_tensor, tensor, upload
+    import sparse_moe_layer_route_amd as M
+
+    layer = W.make_layer(name)
+    cfg = layer.cfg
+    dims = M.Dims(**dims_dict(cfg))
+    threads = min(16, os.cpu_count() or 1)
+    wdev = upload(layer, "cuda")
+    names = ("w_gate", "w_up", "w_down")
+
+    def pinned(a):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if cfg.dtype == "bf16" \
+            else torch.from_numpy(a)
+        return t.pin_memory()
+
+    host = {n: pinned(layer.full(n)) for n in names}
+    res = layer.resident()
+    elem = 2 if cfg.dtype == "bf16" else 4
+    w_bytes = 3 * cfg.inter * cfg.hidden * elem
+
+    # calibration: link rate, host FFN per expert and per pair, GPU per expert
+    e_miss = next(e for e in range(cfg.n_experts) if not (res >> e) & 1)
+    dst = [torch.empty_like(host[n][e_miss], device="cuda") for n in names]
+    for _ in range(3):
+        for d_, n in zip(dst, names):
+            d_.copy_(host[n][e_miss], non_blocking=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    reps = 8
+    for _ in range(reps):
+        for d_, n in zip(dst, names):
+            d_.copy_(host[n][e_miss], non_blocking=True)
+    torch.cuda.synchronize()
+    pcie = reps * w_bytes / (time.perf_counter() - t0)
+    # host throughput per expert and per pair, from a batch of eight missed
+    # experts with one and with four pairs each (a lone expert leaves most
+    # of the host's memory bandwidth idle)
+    x_np = layer.x(max(tokens))
+    cal = [e for e in range(cfg.n_experts) if not (res >> e) & 1][:8]
+    hws = np.zeros(M.moe_host_ffn_workspace_size(dims, 4 * len(cal)), np.uint8)
+    y = np.zeros((4 * len(cal), cfg.hidden), np.float32)
+    hw = {n: host[n] for n in names}
+
+    def host_time(n):
+        best = float("inf")
+        ex = [e for e in cal for _ in range(n)]
+        for _ in range(5):
+            t = time.perf_counter()
+            M.moe_host_expert_ffn(dims, max(tokens), x_np, hw, [i % max(tokens) for i in range(len(ex))],
+                                  ex, threads, y, hws)
+            best = min(best, time.perf_counter() - t)
+        return best / len(cal)
+    t1, t4 = host_time(1), host_time(4)
+    cpu_pair = max(0.0, (t4 - t1) / 3)
+    cpu_expert = max(0.0, t1 - cpu_pair)
+
+    def forward_ms(T, mode):
+        x = tensor(layer.x(T), cfg.dtype, "cuda")
+        out = torch.empty(T, cfg.hidden, dtype=torch.bfloat16 if cfg.dtype == "bf16" else torch.float32,
+                          device="cuda")
+        ws = torch.empty(M.moe_workspace_size(dims, T, mode), dtype=torch.uint8, device="cuda")
+        rm = mask_tensor([res], "cuda")
+        for _ in range(3):
+            M.moe_layer_forward(dims, T, x, wdev, rm, 0, mode, out, ws)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(steps):
+            M.moe_layer_forward(dims, T, x, wdev, rm, 0, mode, out, ws)
+            torch.cuda.synchronize()
+        return (time.perf_counter() - t) / steps * 1e3
+
+    out = dict(workload=f"{name} MoE layer, exact miss execution", mode="offload",
+               resident_experts=bin(res).count("1"), host_threads=threads,
+               calibration=dict(pcie_gbs=pcie / 1e9, expert_bytes=w_bytes,
+                                host_expert_us=cpu_expert * 1e6, host_pair_us=cpu_pair * 1e6),
+               batches=[])
+    dev_b, host_b = M.moe_offload_workspace_size(dims, max(tokens))
+    ws = torch.empty(dev_b, dtype=torch.uint8, device="cuda")
+    hws_p = torch.empty(host_b, dtype=torch.uint8).pin_memory()
+    g0, g1 = ev.create(), ev.create()
+    for T in tokens:
+        x = tensor(layer.x(T), cfg.dtype, "cuda")
+        o = torch.empty(T, cfg.hidden, dtype=torch.bfloat16 if cfg.dtype == "bf16" else torch.float32,
+                        device="cuda")
+        std_ms = forward_ms(T, "standard")
+        lore_ms = forward_ms(T, "lore")
+        # GPU time per active expert: the all-resident forward over its experts
+        dbg_ids = torch.empty(T * cfg.top_k, dtype=torch.int32, device="cuda")
+        wsr = torch.empty(M.moe_workspace_size(dims, T, "standard"), dtype=torch.uint8, device="cuda")
+        M.moe_layer_forward(dims, T, x, wdev, None, 0, "standard", o, wsr, debug={"topk_ids": dbg_ids})
+        torch.cuda.synchronize()
+        ids = dbg_ids.cpu().numpy()
+        active = len(set(ids.tolist()))
+        gpu_expert = std_ms * 1e-3 / max(1, active)
+        plans = {"fetch_all": M.offload_cost(pcie, 0.0, 1.0, threads),
+                 "host_all": M.offload_cost(pcie, 1.0, 0.0, threads),
+                 "cost_rule": M.offload_cost(pcie, gpu_expert, cpu_pair, threads, cpu_expert),
+                 "cost_rule_queued": M.offload_cost(pcie, gpu_expert, cpu_pair, threads,
+                                                    cpu_expert, queue_aware=True)}
+        row = dict(tokens=T, standard_all_resident_ms=std_ms, lore_surrogate_ms=lore_ms,
+                   gpu_expert_us=gpu_expert * 1e6, plans={})
+        for pname, cost in plans.items():
+            for _ in range(2):
+                M.moe_layer_forward_offload(dims, T, x, wdev, host, res, cost, o, ws, hws_p)
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            for _ in range(steps):
+                M.moe_layer_forward_offload(dims, T, x, wdev, host, res, cost, o, ws, hws_p)
+                torch.cuda.synchronize()
+            ms = (time.perf_counter() - t) / steps * 1e3
+            st = M.MoeOffloadStats()
+            st.gpu_start, st.gpu_stop = g0, g1
+            M.moe_layer_forward_offload(dims, T, x, wdev, host, res, cost, o, ws, hws_p, stats=st)
+            gpu_ms = ev.elapsed_ms(g0, g1)
+            row["plans"][pname] = dict(
+                ms=ms, missed=st.missed_experts, fetched=st.fetched_experts,
+                host_experts=st.host_experts, host_pairs=st.host_pairs, route_ms=st.route_ms,
+                host_ms=st.host_ms, gpu_ms=gpu_ms, parallel_ms=st.parallel_ms,
+                hidden_ms=max(0.0, st.host_ms + gpu_ms - st.parallel_ms))
+        out["batches"].append(row)
+    ev.destroy(g0)
+    ev.destroy(g1)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -599,6 +738,15 @@ def main():
               f"({r['predict_gbs']:.0f} GB/s); compact pack {r['pack_us']:.1f} us "
               f"({r['pack_gbs']:.0f} GB/s); recall {r['recall']:.3f} over {r['recall_tokens']} tokens",
               file=sys.stderr, flush=True)
+        r = measure_offload(ev)
+        also.append(r)
+        for b in r["batches"]:
+            print(f"# dsv2_lite T={b['tokens']} exact miss execution (resident "
+                  f"{r['resident_experts']}/64): " + "; ".join(
+                      f"{k} {v['ms']:.2f} ms (fetch {v['fetched']}, host {v['host_experts']})"
+                      for k, v in b["plans"].items())
+                  + f"; LoRE {b['lore_surrogate_ms']:.3f} ms, all resident "
+                  f"{b['standard_all_resident_ms']:.3f} ms", file=sys.stderr, flush=True)
         r = measure_lore_fit()
         also.append(r)
         print(f"# dsv2_lite LoRE fit (expert 0, {r['tokens']} calibration rows): targets "

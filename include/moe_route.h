@@ -18,7 +18,10 @@
  *     device pointers.  Every device pointer must be 16-byte aligned.
  *   - The caller owns every buffer.  The library allocates nothing, frees
  *     nothing, never synchronises, and keeps no state between calls; scratch
- *     memory comes from the caller's workspace (moe_workspace_size()).
+ *     memory comes from the caller's workspace (moe_workspace_size()).  The
+ *     exceptions are named where they are declared: moe_layer_forward_noalloc
+ *     (a library-held scratch array), moe_layer_forward_offload (waits for
+ *     the routed ids and runs host threads) and moe_host_expert_ffn (host).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     the call returns without waiting.  Calls on one stream are ordered.
  *   - Errors are return codes.  All argument checks run on the host before
@@ -380,6 +383,128 @@ moe_status_t moe_layer_forward_noalloc(const moe_dims_t* dims, int32_t T, const 
                                        const moe_weights_t* w, const uint64_t* resident,
                                        int64_t resident_stride, moe_mode_t mode, void* out,
                                        void* stream);
+
+/* ---- Exact execution of missed experts on the host or after a fetch ------
+ * [SPICE page, "CPU-GPU collaboration: handling prefetch misses", cost rule
+ * and the three-step execution of its Fig. 6]
+ *
+ * The routed expert matrices live in host memory (host_w) and the GPU holds
+ * a slot per expert in w->w_gate / w_up / w_down, of which only the experts
+ * set in the `resident` mask hold valid weights.  A routed expert that is not
+ * resident is missed; each missed expert is either fetched (its three
+ * matrices copied host -> slot, then run on the GPU with the resident ones)
+ * or run on the host from host_w, by the cost rule below.  Both are exact:
+ * the output equals moe_layer_forward in MOE_MODE_STANDARD up to fp32
+ * summation order. */
+
+typedef struct {
+  double pcie_bytes_per_s; /* B_pcie: host -> GPU copy rate, bytes/s (> 0)          */
+  double gpu_expert_s;     /* T_gpu_e: one expert's FFN on the GPU, seconds (>= 0)  */
+  double cpu_expert_s;     /* host FFN time per expert run (its weight reads), s   */
+  double cpu_pair_s;       /* host FFN time per (token, expert) pair, s (>= 0)     */
+  int32_t cpu_threads;     /* host FFN threads; <= 0: min(16, hardware threads)   */
+  int32_t queue_aware;     /* 0: each missed expert on its own; 1: with the load
+                              already committed (see moe_offload_plan)         */
+} moe_offload_cost_t;
+
+/* Decisions of moe_offload_plan, one byte per expert. */
+#define MOE_OFFLOAD_NONE 0  /* resident, or routed by no token        */
+#define MOE_OFFLOAD_FETCH 1 /* copied to its GPU slot and run there   */
+#define MOE_OFFLOAD_HOST 2  /* run on the host from host_w            */
+
+/* The cost rule, per missed expert e with n_e routed (token, expert) pairs:
+ *   fetch cost = W_e / B_pcie + T_gpu_e, W_e = 3 * I * H * sizeof(dtype)
+ *   host cost  = T_cpu_e + 2 * n_e * H * sizeof(dtype) / B_pcie,
+ *   T_cpu_e    = cpu_expert_s + n_e * cpu_pair_s
+ * (the hidden state goes down and the expert's output comes back once per
+ * pair); the expert is fetched when the fetch cost is strictly lower, else
+ * run on the host.  With cost->queue_aware = 1 the link and the host are
+ * treated as queues (the page's "PCIe pressure"): the missed experts are
+ * decided in order of decreasing n_e (then id), and each fetch cost also
+ * counts the fetch time (W_e / B_pcie + T_gpu_e) of the experts already
+ * sent to the GPU, each host cost the host time of those already sent to
+ * the host, so the two sides fill up evenly; the first decision is the
+ * plain rule.  tokens [E] (host): n_e for every expert.  resident
+ * (host): one uint64 mask word, bit e set = expert e is in its GPU slot.
+ * decision_out [E] (host): MOE_OFFLOAD_*.  Host-only: no GPU needed, nothing
+ * enqueued.  MOE_EINVAL on NULL pointers, negative counts or a cost with
+ * B_pcie <= 0 (or infinite) or negative (or NaN) times. */
+moe_status_t moe_offload_plan(const moe_dims_t* dims, const int32_t* tokens,
+                              const uint64_t* resident, const moe_offload_cost_t* cost,
+                              uint8_t* decision_out);
+
+/* Device and host workspace bytes of moe_layer_forward_offload for T tokens.
+ * The host workspace must be pinned (hipHostMalloc, or a torch tensor made
+ * with pin_memory=True) so that its copies run asynchronously. */
+moe_status_t moe_offload_workspace_size(const moe_dims_t* dims, int32_t T,
+                                        size_t* device_bytes, size_t* host_bytes);
+
+/* The host half of moe_layer_forward_offload on its own, all buffers in
+ * host memory: for n (token, expert) pairs i, y_out[i] = W_d[e] a with
+ * a = SiLU(W_g[e] x_t) * (W_u[e] x_t), t = tok[i], e = expert[i], sums in
+ * fp32 and a rounded to dtype (bf16 layers) as on the GPU.  x [T][H] dtype;
+ * host_w: w_gate, w_up, w_down as in moe_layer_forward_offload; y_out
+ * [n][H] fp32.  threads <= 0: min(16, hardware threads).  host_ws: at least
+ * moe_host_ffn_workspace_size(dims, n) bytes (pinning not needed).  Each
+ * output element is one thread's fixed-order sum, so results do not depend
+ * on the thread count.  Requires MOE_UP_DENSE; MOE_EINVAL on a token or
+ * expert id out of range.  Runs on the calling thread (and the threads it
+ * starts) and returns when done; no GPU needed. */
+moe_status_t moe_host_ffn_workspace_size(const moe_dims_t* dims, int32_t n, size_t* bytes);
+moe_status_t moe_host_expert_ffn(const moe_dims_t* dims, int32_t T, const void* x,
+                                 const moe_weights_t* host_w, int32_t n, const int32_t* tok,
+                                 const int32_t* expert, int32_t threads, float* y_out,
+                                 void* host_ws, size_t host_ws_bytes);
+
+/* Per-call figures of moe_layer_forward_offload (host struct, optional). */
+typedef struct {
+  int32_t missed_experts;   /* out: routed experts not resident              */
+  int32_t fetched_experts;  /* out: of those, fetched                        */
+  int32_t host_experts;     /* out: of those, run on the host                */
+  int32_t host_pairs;       /* out: (token, expert) pairs run on the host    */
+  double route_ms;          /* out: call start -> routed ids on the host     */
+  double host_ms;           /* out: host FFN                                 */
+  double parallel_ms;       /* out: GPU work dispatched -> host FFN and GPU
+                               expert FFNs both done                         */
+  double wall_ms;           /* out: whole call, through its last kernel      */
+  uint8_t* decision;        /* in, optional host [E]: receives the plan      */
+  void* gpu_start;          /* in, optional hipEvent_t: recorded before the
+                               weight fetches                               */
+  void* gpu_stop;           /* in, optional hipEvent_t: recorded after the
+                               GPU expert FFNs                               */
+} moe_offload_stats_t;
+
+/* One layer forward with missed experts executed exactly, in three steps:
+ *   1. route (MOE_MODE_STANDARD semantics) and stage the token rows and the
+ *      routed ids in the pinned host workspace; plan every missed expert
+ *      with moe_offload_plan;
+ *   2. enqueue the fetched experts' copies host_w -> GPU slots and the GPU
+ *      FFNs of the resident and fetched experts and the shared experts; the
+ *      host FFN of the remaining missed pairs runs meanwhile on
+ *      cost->cpu_threads threads (fp32 sums, the SwiGLU product rounded to
+ *      dtype as on the GPU);
+ *   3. copy the host rows to the GPU and combine them with the GPU rows.
+ * x, out [T][H] dtype and ws (device bytes of moe_offload_workspace_size)
+ * are device buffers; w holds device pointers, and the call writes fetched
+ * experts into their slots of w->w_gate / w_up / w_down (it does not set
+ * their resident bits: that is the caller's cache policy).  host_w: host
+ * pointers w_gate, w_up, w_down, [E][I][H], [E][I][H], [E][H][I] dtype,
+ * pinned for asynchronous fetches (its other members are ignored).
+ * resident (host): one mask word.  host_ws: pinned host workspace.  Requires
+ * MOE_LAYOUT_ROWS and MOE_UP_DENSE.
+ *
+ * Unlike the other entry points this call waits on `stream`, once, for the
+ * routed ids (step 1), and with stats != NULL once more before returning.
+ * It returns with steps 2 and 3 still enqueued: host_ws must stay untouched
+ * until `stream` has finished them (a later call on the same stream is
+ * ordered after them).  MOE_EINVAL / MOE_EUNSUPPORTED / MOE_EWORKSPACE as
+ * for moe_layer_forward; MOE_EHIP on a failed launch or copy. */
+moe_status_t moe_layer_forward_offload(const moe_dims_t* dims, int32_t T, const void* x,
+                                       const moe_weights_t* w, const moe_weights_t* host_w,
+                                       const uint64_t* resident,
+                                       const moe_offload_cost_t* cost, void* out, void* ws,
+                                       size_t ws_bytes, void* host_ws, size_t host_ws_bytes,
+                                       moe_offload_stats_t* stats, void* stream);
 
 #ifdef __cplusplus
 }

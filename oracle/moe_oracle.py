@@ -64,6 +64,19 @@ notes):
   the SVD U S V^T of M G^-1/2.  For an orthogonal design (G = I) this is the
   truncated SVD of M itself.
 
+* SPICE's cost rule for a missed expert compares fetching it (W_e / B_pcie +
+  T_gpu_e) with running it on the host (T_cpu_e + 2H / B_pcie).  W_e counts
+  the expert's three matrices (gate, up, down) in the layer dtype; T_cpu_e
+  and the 2H transfer scale with the expert's routed (token, expert) pairs
+  (each pair's hidden state goes down and its output comes back), and
+  T_cpu_e may also hold a fixed per-expert term (the weight reads); the fetch
+  is taken only when strictly cheaper.  A resident expert, or one no token
+  routes to, needs neither.  The page also ties the choice to the current
+  PCIe pressure; the queue-aware form reads that as queues: experts are
+  decided by decreasing pair count, each cost counting the time earlier
+  decisions already put on the link or the host (the plain rule is the
+  default and the first decision of either form).
+
 * Stall-free with fewer than k prefetched experts (outside the page's domain:
   its lists hold k + delta >= k experts): Algorithm 1 then returns the whole
   prefetched set; the remaining slots take the best experts outside it by
@@ -91,6 +104,7 @@ __all__ = [
     "floe_channel_mask", "floe_predict_masks", "mask_recall", "floe_pack",
     "lore_targets", "lore_fit",
     "shared_experts", "lore_residual", "layer_forward", "WeightSource",
+    "OFFLOAD_NONE", "OFFLOAD_FETCH", "OFFLOAD_HOST", "offload_costs", "offload_plan",
 ]
 
 FLAG_ROUTE, FLAG_PREFETCH, FLAG_SUBST, FLAG_FLOE = 1, 2, 4, 8
@@ -460,6 +474,60 @@ def lore_residual(x_t: np.ndarray, lore_a: np.ndarray, lore_b: np.ndarray) -> np
     """LoRE low-rank residual B_e (A_e h) with A_e [r][H], B_e [H][r] [SPICE
     "LoRE low-rank surrogate"]."""
     return lore_b @ (lore_a @ x_t)
+
+
+# ------------------------------------------- missed experts: fetch or host --
+OFFLOAD_NONE, OFFLOAD_FETCH, OFFLOAD_HOST = 0, 1, 2
+
+
+def offload_costs(weight_bytes: float, hidden_bytes: float, n_pairs: int,
+                  pcie_bytes_per_s: float, gpu_expert_s: float, cpu_pair_s: float,
+                  cpu_expert_s: float = 0.0):
+    """(fetch cost, host cost) in seconds of one missed expert [SPICE
+    "CPU-GPU collaboration: handling prefetch misses", the per-expert cost
+    comparison]: fetching moves the weights over the link and then runs the
+    expert on the GPU; host execution runs it on the CPU (a fixed time per
+    expert plus a time per routed pair) and moves each routed token's hidden
+    state down and its output back."""
+    fetch = weight_bytes / pcie_bytes_per_s + gpu_expert_s
+    t_cpu = cpu_expert_s + n_pairs * cpu_pair_s
+    host = t_cpu + 2 * n_pairs * hidden_bytes / pcie_bytes_per_s
+    return fetch, host
+
+
+def offload_plan(dims: dict, tokens: Sequence[int], resident: int, pcie_bytes_per_s: float,
+                 gpu_expert_s: float, cpu_pair_s: float, cpu_expert_s: float = 0.0,
+                 queue_aware: bool = False) -> List[int]:
+    """Decision per expert: OFFLOAD_NONE (resident or not routed),
+    OFFLOAD_FETCH when the fetch cost is strictly below the host cost, else
+    OFFLOAD_HOST [SPICE "CPU-GPU collaboration: handling prefetch misses"].
+    tokens[e] = routed (token, expert) pairs of expert e.
+
+    queue_aware: the link and the host are queues ("PCIe pressure", Fig. 6
+    of the same section): missed experts are taken by decreasing pair count
+    (then id) and each side's cost includes what earlier decisions already
+    put on that side."""
+    elem = 2 if dims["dtype"] == "bf16" else 4
+    w_bytes = 3 * dims["inter"] * dims["hidden"] * elem
+    h_bytes = dims["hidden"] * elem
+    out = [OFFLOAD_NONE] * len(tokens)
+    missed = [e for e, n in enumerate(tokens) if n > 0 and not (resident >> e) & 1]
+    if queue_aware:
+        missed.sort(key=lambda e: (-tokens[e], e))
+    link_busy = host_busy = 0.0
+    for e in missed:
+        fetch, host = offload_costs(w_bytes, h_bytes, tokens[e], pcie_bytes_per_s, gpu_expert_s,
+                                    cpu_pair_s, cpu_expert_s)
+        if queue_aware:
+            fetch += link_busy
+            host += host_busy
+        if fetch < host:
+            out[e] = OFFLOAD_FETCH
+            link_busy = fetch
+        else:
+            out[e] = OFFLOAD_HOST
+            host_busy = host
+    return out
 
 
 # ---------------------------------------------------------- weight access --

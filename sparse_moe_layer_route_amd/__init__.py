@@ -7,4 +7,7 @@ from .binding import (  # noqa: F401
     moe_floe_predict, moe_floe_pack, moe_lore_targets, moe_lore_fit_size, moe_lore_fit,
     moe_expert_ffn, moe_lore_surrogate, moe_combine, moe_layer_forward, weights_struct,
     moe_layer_forward_noalloc, NOALLOC_SCRATCH_BYTES,
+    MoeOffloadCost, MoeOffloadStats, OFFLOAD_NONE, OFFLOAD_FETCH, OFFLOAD_HOST, offload_cost,
+    moe_offload_plan, moe_offload_workspace_size, moe_host_ffn_workspace_size,
+    moe_host_expert_ffn, moe_layer_forward_offload,
 )

@@ -62,6 +62,24 @@ class MoeDebug(ctypes.Structure):
         ("prof_kernel", ctypes.c_int32)]
 
 
+class MoeOffloadCost(ctypes.Structure):
+    _fields_ = [("pcie_bytes_per_s", ctypes.c_double), ("gpu_expert_s", ctypes.c_double),
+                ("cpu_expert_s", ctypes.c_double), ("cpu_pair_s", ctypes.c_double),
+                ("cpu_threads", ctypes.c_int32), ("queue_aware", ctypes.c_int32)]
+
+
+class MoeOffloadStats(ctypes.Structure):
+    _fields_ = [("missed_experts", ctypes.c_int32), ("fetched_experts", ctypes.c_int32),
+                ("host_experts", ctypes.c_int32), ("host_pairs", ctypes.c_int32),
+                ("route_ms", ctypes.c_double), ("host_ms", ctypes.c_double),
+                ("parallel_ms", ctypes.c_double), ("wall_ms", ctypes.c_double),
+                ("decision", ctypes.c_void_p), ("gpu_start", ctypes.c_void_p),
+                ("gpu_stop", ctypes.c_void_p)]
+
+
+OFFLOAD_NONE, OFFLOAD_FETCH, OFFLOAD_HOST = 0, 1, 2
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run sparse_moe_layer_route_amd.build.build()")
@@ -89,6 +107,14 @@ def _load():
         "moe_combine": ([D, I32, P, P, P, P, P, P, P, P, P], ctypes.c_int),
         "moe_layer_forward": ([D, I32, P, Wp, P, I64, ctypes.c_int, P, Dbg, P, SZ, P], ctypes.c_int),
         "moe_layer_forward_noalloc": ([D, I32, P, Wp, P, I64, ctypes.c_int, P, P], ctypes.c_int),
+        "moe_offload_plan": ([D, P, P, ctypes.POINTER(MoeOffloadCost), P], ctypes.c_int),
+        "moe_offload_workspace_size": ([D, I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ)],
+                                       ctypes.c_int),
+        "moe_host_ffn_workspace_size": ([D, I32, ctypes.POINTER(SZ)], ctypes.c_int),
+        "moe_host_expert_ffn": ([D, I32, P, Wp, I32, P, P, I32, P, P, SZ], ctypes.c_int),
+        "moe_layer_forward_offload": ([D, I32, P, Wp, Wp, P, ctypes.POINTER(MoeOffloadCost), P, P,
+                                       SZ, P, SZ, ctypes.POINTER(MoeOffloadStats), P],
+                                      ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -102,7 +128,9 @@ EXPORTED = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_r
             "moe_prefetch_mask", "moe_prefetch_adaptive", "moe_pack_size", "moe_pack_weights",
             "moe_permute", "moe_floe_predict", "moe_floe_pack", "moe_lore_targets",
             "moe_lore_fit_size", "moe_lore_fit", "moe_expert_ffn", "moe_lore_surrogate",
-            "moe_combine", "moe_layer_forward", "moe_layer_forward_noalloc")
+            "moe_combine", "moe_layer_forward", "moe_layer_forward_noalloc", "moe_offload_plan",
+            "moe_offload_workspace_size", "moe_host_ffn_workspace_size", "moe_host_expert_ffn",
+            "moe_layer_forward_offload")
 
 
 # ------------------------------------------------------------------ helpers --
@@ -330,3 +358,99 @@ def moe_layer_forward_noalloc(dims, T, x, weights, resident, resident_stride, mo
                                           ctypes.byref(ws_struct), _ptr(resident), resident_stride,
                                           _mode(mode), _ptr(out), _stream(stream)),
            "moe_layer_forward_noalloc")
+
+
+# ------------------------------------------------- exact miss execution --
+def _hptr(t):
+    """Address of a host buffer: a contiguous CPU tensor or numpy array."""
+    if t is None:
+        return None
+    if isinstance(t, torch.Tensor):
+        if t.is_cuda:
+            raise ValueError("tensor must live in host memory")
+        if not t.is_contiguous():
+            raise ValueError("tensor must be contiguous")
+        return t.data_ptr()
+    import numpy as np
+    if isinstance(t, np.ndarray):
+        if not t.flags["C_CONTIGUOUS"]:
+            raise ValueError("array must be C-contiguous")
+        return t.ctypes.data
+    raise TypeError("expected a CPU torch.Tensor or a numpy array")
+
+
+def offload_cost(pcie_bytes_per_s, gpu_expert_s, cpu_pair_s, cpu_threads=0,
+                 cpu_expert_s=0.0, queue_aware=False) -> MoeOffloadCost:
+    return MoeOffloadCost(float(pcie_bytes_per_s), float(gpu_expert_s), float(cpu_expert_s),
+                          float(cpu_pair_s), int(cpu_threads), int(bool(queue_aware)))
+
+
+def moe_offload_plan(dims, tokens, resident: int, cost: MoeOffloadCost):
+    """Cost-rule decision per expert (OFFLOAD_NONE / FETCH / HOST), host only."""
+    import numpy as np
+    d = _dims(dims)
+    tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+    if tok.shape != (d.n_experts,):
+        raise ValueError("tokens must hold one count per expert")
+    res = (ctypes.c_uint64 * 1)(int(resident) & (2**64 - 1))
+    dec = np.zeros(d.n_experts, dtype=np.uint8)
+    _check(_lib.moe_offload_plan(ctypes.byref(d), tok.ctypes.data, ctypes.addressof(res),
+                                 ctypes.byref(cost), dec.ctypes.data), "moe_offload_plan")
+    return dec
+
+
+def moe_offload_workspace_size(dims, T: int):
+    dev, host = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(_lib.moe_offload_workspace_size(ctypes.byref(_dims(dims)), T, ctypes.byref(dev),
+                                           ctypes.byref(host)), "moe_offload_workspace_size")
+    return dev.value, host.value
+
+
+def moe_host_ffn_workspace_size(dims, n: int) -> int:
+    b = ctypes.c_size_t(0)
+    _check(_lib.moe_host_ffn_workspace_size(ctypes.byref(_dims(dims)), n, ctypes.byref(b)),
+           "moe_host_ffn_workspace_size")
+    return b.value
+
+
+def _host_weights(w) -> MoeWeights:
+    if isinstance(w, MoeWeights):
+        return w
+    st = MoeWeights()
+    for n in ("w_gate", "w_up", "w_down"):
+        setattr(st, n, _hptr(w[n]))
+    return st
+
+
+def moe_host_expert_ffn(dims, T, x, host_weights, tok, expert, threads, y_out, host_ws):
+    """Host SwiGLU FFN of (token, expert) pairs; every buffer in host memory."""
+    import numpy as np
+    t = np.ascontiguousarray(np.asarray(tok, dtype=np.int32))
+    e = np.ascontiguousarray(np.asarray(expert, dtype=np.int32))
+    if t.shape != e.shape or t.ndim != 1:
+        raise ValueError("tok and expert must be 1-D of the same length")
+    hw = _host_weights(host_weights)
+    nbytes = host_ws.numel() * host_ws.element_size() if isinstance(host_ws, torch.Tensor) \
+        else host_ws.nbytes
+    _check(_lib.moe_host_expert_ffn(ctypes.byref(_dims(dims)), T, _hptr(x), ctypes.byref(hw),
+                                    len(t), t.ctypes.data, e.ctypes.data, int(threads),
+                                    _hptr(y_out), _hptr(host_ws), nbytes),
+           "moe_host_expert_ffn")
+
+
+def moe_layer_forward_offload(dims, T, x, weights, host_weights, resident: int,
+                              cost: MoeOffloadCost, out, ws, host_ws, stats=None, stream=None):
+    """Layer forward with missed experts fetched or run on the host (exact).
+
+    weights: device tensors (the expert slots are written for fetched
+    experts); host_weights: pinned CPU tensors w_gate / w_up / w_down;
+    host_ws: pinned CPU uint8 tensor; stats: a MoeOffloadStats or None."""
+    ws_struct = weights if isinstance(weights, MoeWeights) else weights_struct(weights)
+    hw = _host_weights(host_weights)
+    res = (ctypes.c_uint64 * 1)(int(resident) & (2**64 - 1))
+    _check(_lib.moe_layer_forward_offload(
+        ctypes.byref(_dims(dims)), T, _ptr(x), ctypes.byref(ws_struct), ctypes.byref(hw),
+        ctypes.addressof(res), ctypes.byref(cost), _ptr(out), _ptr(ws),
+        ws.numel() * ws.element_size(), _hptr(host_ws), host_ws.numel() * host_ws.element_size(),
+        ctypes.byref(stats) if stats is not None else None, _stream(stream)),
+        "moe_layer_forward_offload")

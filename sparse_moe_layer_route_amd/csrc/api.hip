@@ -1,11 +1,15 @@
 // Host side of the C ABI declared in include/moe_route.h: argument checks,
-// workspace carving and kernel enqueueing.  Nothing here allocates, frees or
-// synchronises; every check runs before the first enqueue.
+// workspace carving and kernel enqueueing.  Nothing here allocates device
+// memory, frees or synchronises, and every check runs before the first
+// enqueue -- except moe_layer_forward_offload, which waits for the routed ids
+// before it can plan the missed experts and runs the host FFN.
 #include <string.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cmath>
 #include <mutex>
+#include <thread>
 
 #include "common.h"
 
@@ -72,6 +76,14 @@ hipError_t launch_lore(const moe_dims_t& d, int T, const void* x, const int32_t*
 int floe_slices(int n_keep);
 int floe_max_inter();
 int floe_max_hidden();
+void offload_costs(double weight_bytes, double hidden_bytes, int tokens, double pcie_bytes_per_s,
+                   double gpu_expert_s, double cpu_expert_s, double cpu_pair_s, double* fetch,
+                   double* host);
+void host_expert_ffn(const HostFfnArgs& a, bool bf16_weights, const void* x, const void* wg,
+                     const void* wu, const void* wd);
+hipError_t launch_offload_scatter(int n, int H, const int32_t* pairs, const float* y_host,
+                                  const int32_t* row_of, float* y_perm, uint8_t* exact,
+                                  hipStream_t s);
 }  // namespace moe
 
 using namespace moe;
@@ -706,6 +718,373 @@ moe_status_t moe_layer_forward_noalloc(const moe_dims_t* dims, int32_t T, const 
   if (!ws) return MOE_EHIP;
   return layer_forward_impl(dims, T, x, w, resident, resident_stride, mode, out, nullptr, ws, p,
                             stream);
+}
+
+}  // extern "C"
+
+// ---- exact execution of missed experts: fetch or host FFN -------------------
+
+namespace {
+
+inline size_t elem_bytes(const moe_dims_t& d) { return d.dtype == MOE_BF16 ? 2 : 4; }
+
+moe_status_t check_cost(const moe_offload_cost_t* c) {
+  if (!c) return MOE_EINVAL;
+  if (!(c->pcie_bytes_per_s > 0.0) || !(c->gpu_expert_s >= 0.0) || !(c->cpu_expert_s >= 0.0) ||
+      !(c->cpu_pair_s >= 0.0) || std::isinf(c->pcie_bytes_per_s))
+    return MOE_EINVAL;
+  return MOE_OK;
+}
+
+// The cost rule over every expert (tokens, resident and cost checked).
+// Queue-aware: experts by decreasing pair count, each side's cost raised by
+// the time already committed to it.
+void offload_decide(const moe_dims_t& d, const int32_t* tokens, uint64_t resident,
+                    const moe_offload_cost_t& c, uint8_t* decision) {
+  const double eb = (double)elem_bytes(d);
+  const double w_bytes = 3.0 * d.inter * (double)d.hidden * eb, h_bytes = d.hidden * eb;
+  int order[MOE_MAX_EXPERTS];
+  int m = 0;
+  for (int e = 0; e < d.n_experts; ++e) {
+    decision[e] = MOE_OFFLOAD_NONE;
+    if (tokens[e] > 0 && !((resident >> e) & 1ull)) order[m++] = e;
+  }
+  if (c.queue_aware)
+    std::stable_sort(order, order + m, [&](int a, int b) { return tokens[a] > tokens[b]; });
+  double link = 0.0, cpu = 0.0;
+  for (int i = 0; i < m; ++i) {
+    const int e = order[i];
+    double fetch, host;
+    offload_costs(w_bytes, h_bytes, tokens[e], c.pcie_bytes_per_s, c.gpu_expert_s, c.cpu_expert_s,
+                  c.cpu_pair_s, &fetch, &host);
+    if (c.queue_aware) {
+      fetch += link;
+      host += cpu;
+    }
+    if (fetch < host) {
+      decision[e] = MOE_OFFLOAD_FETCH;
+      link = fetch;
+    } else {
+      decision[e] = MOE_OFFLOAD_HOST;
+      cpu = host;
+    }
+  }
+}
+
+// Extra device buffers (after the standard plan) and the host workspace.
+struct OffloadPlan {
+  Plan dev;
+  size_t d_y, d_pairs, d_total;
+  size_t ids, x, exact, pairs, tok, gexp, gstart, done, tokens, dec, xf, act, y, h_total;
+};
+
+OffloadPlan make_offload_plan(const moe_dims_t& d, int T) {
+  OffloadPlan p{};
+  p.dev = make_plan(d, T, MOE_MODE_STANDARD);
+  const size_t P = (size_t)T * d.top_k, H = d.hidden, I = d.inter, E = d.n_experts;
+  size_t o = p.dev.total;
+  auto take = [&](size_t bytes) { const size_t at = o; o = align256(o + bytes); return at; };
+  p.d_y = take(P * H * 4);
+  p.d_pairs = take(P * 4);
+  p.d_total = o;
+  o = 0;
+  p.ids = take(P * 4);
+  p.x = take((size_t)T * H * elem_bytes(d));
+  p.exact = take(P);
+  p.pairs = take(P * 4);
+  p.tok = take(P * 4);
+  p.gexp = take(E * 4);
+  p.gstart = take((E + 1) * 4);
+  p.done = take(E * 4);
+  p.tokens = take(E * 4);
+  p.dec = take(E);
+  p.xf = take(P * H * 4);
+  p.act = take(P * I * 4);
+  p.y = take(P * H * 4);
+  p.h_total = o;
+  return p;
+}
+
+double ms_since(std::chrono::steady_clock::time_point t0) {
+  return std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_offload_plan(const moe_dims_t* dims, const int32_t* tokens,
+                              const uint64_t* resident, const moe_offload_cost_t* cost,
+                              uint8_t* decision_out) {
+  moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if ((st = check_cost(cost)) != MOE_OK) return st;
+  if (!tokens || !resident || !decision_out) return MOE_EINVAL;
+  for (int e = 0; e < dims->n_experts; ++e)
+    if (tokens[e] < 0) return MOE_EINVAL;
+  offload_decide(*dims, tokens, *resident, *cost, decision_out);
+  return MOE_OK;
+}
+
+moe_status_t moe_offload_workspace_size(const moe_dims_t* dims, int32_t T, size_t* device_bytes,
+                                        size_t* host_bytes) {
+  moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (T < 0 || !device_bytes || !host_bytes) return MOE_EINVAL;
+  if (!tokens_fit(*dims, T)) return MOE_EUNSUPPORTED;
+  const OffloadPlan p = make_offload_plan(*dims, T);
+  *device_bytes = p.d_total;
+  *host_bytes = p.h_total;
+  return MOE_OK;
+}
+
+// host workspace of moe_host_expert_ffn: grouped pairs, counters, scratch
+struct HostFfnPlan {
+  size_t order, tok, gexp, gstart, done, cnt, xf, act, y, total;
+};
+
+HostFfnPlan make_host_ffn_plan(const moe_dims_t& d, int n) {
+  HostFfnPlan p{};
+  const size_t N = (size_t)std::max(n, 0), E = d.n_experts;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o = align256(o + bytes); return at; };
+  p.order = take(N * 4);
+  p.tok = take(N * 4);
+  p.gexp = take(E * 4);
+  p.gstart = take((E + 1) * 4);
+  p.done = take(E * 4);
+  p.cnt = take(E * 4);
+  p.xf = take(N * d.hidden * 4);
+  p.act = take(N * d.inter * 4);
+  p.y = take(N * d.hidden * 4);
+  p.total = o;
+  return p;
+}
+
+inline int host_threads(int32_t t) {
+  return t > 0 ? t : (int)std::min(16u, std::max(1u, std::thread::hardware_concurrency()));
+}
+
+moe_status_t moe_host_ffn_workspace_size(const moe_dims_t* dims, int32_t n, size_t* bytes) {
+  moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (n < 0 || !bytes) return MOE_EINVAL;
+  *bytes = make_host_ffn_plan(*dims, n).total;
+  return MOE_OK;
+}
+
+moe_status_t moe_host_expert_ffn(const moe_dims_t* dims, int32_t T, const void* x,
+                                 const moe_weights_t* host_w, int32_t n, const int32_t* tok,
+                                 const int32_t* expert, int32_t threads, float* y_out,
+                                 void* host_ws, size_t host_ws_bytes) {
+  moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (dims->up_format != MOE_UP_DENSE || dims->weight_layout != MOE_LAYOUT_ROWS)
+    return MOE_EUNSUPPORTED;
+  if (T < 0 || n < 0) return MOE_EINVAL;
+  if (n == 0) return MOE_OK;
+  if (!x || !host_w || !host_w->w_gate || !host_w->w_up || !host_w->w_down || !tok || !expert ||
+      !y_out || !host_ws || !aligned16(host_ws))
+    return MOE_EINVAL;
+  const moe_dims_t& d = *dims;
+  const HostFfnPlan p = make_host_ffn_plan(d, n);
+  if (host_ws_bytes < p.total) return MOE_EWORKSPACE;
+  for (int i = 0; i < n; ++i)
+    if (tok[i] < 0 || tok[i] >= T || expert[i] < 0 || expert[i] >= d.n_experts) return MOE_EINVAL;
+  // stable grouping of the pairs by expert
+  int32_t* cnt = at<int32_t>(host_ws, p.cnt);
+  int32_t* gexp = at<int32_t>(host_ws, p.gexp);
+  int32_t* gstart = at<int32_t>(host_ws, p.gstart);
+  int32_t* order = at<int32_t>(host_ws, p.order);
+  int32_t* gtok = at<int32_t>(host_ws, p.tok);
+  for (int e = 0; e < d.n_experts; ++e) cnt[e] = 0;
+  for (int i = 0; i < n; ++i) ++cnt[expert[i]];
+  int ng = 0, q = 0;
+  for (int e = 0; e < d.n_experts; ++e) {
+    if (!cnt[e]) continue;
+    gexp[ng] = e;
+    gstart[ng++] = q;
+    for (int i = 0; i < n; ++i)
+      if (expert[i] == e) order[q++] = i;
+  }
+  gstart[ng] = q;
+  for (int j = 0; j < n; ++j) gtok[j] = tok[order[j]];
+  HostFfnArgs a{};
+  a.H = d.hidden;
+  a.I = d.inter;
+  a.n_pairs = n;
+  a.n_groups = ng;
+  a.threads = host_threads(threads);
+  a.tok = gtok;
+  a.gexp = gexp;
+  a.gstart = gstart;
+  a.done = at<int32_t>(host_ws, p.done);
+  a.xf = at<float>(host_ws, p.xf);
+  a.act = at<float>(host_ws, p.act);
+  a.y = at<float>(host_ws, p.y);
+  host_expert_ffn(a, d.dtype == MOE_BF16, x, host_w->w_gate, host_w->w_up, host_w->w_down);
+  for (int j = 0; j < n; ++j)
+    memcpy(y_out + (int64_t)order[j] * d.hidden, a.y + (int64_t)j * d.hidden,
+           (size_t)d.hidden * 4);
+  return MOE_OK;
+}
+
+moe_status_t moe_layer_forward_offload(const moe_dims_t* dims, int32_t T, const void* x,
+                                       const moe_weights_t* w, const moe_weights_t* host_w,
+                                       const uint64_t* resident,
+                                       const moe_offload_cost_t* cost, void* out, void* ws,
+                                       size_t ws_bytes, void* host_ws, size_t host_ws_bytes,
+                                       moe_offload_stats_t* stats, void* stream) {
+  const auto t0 = std::chrono::steady_clock::now();
+  moe_status_t st = check_forward(dims, T, x, w, nullptr, 0, MOE_MODE_STANDARD, out, nullptr);
+  if (st != MOE_OK) return st;
+  if (dims->weight_layout != MOE_LAYOUT_ROWS || dims->up_format != MOE_UP_DENSE)
+    return MOE_EUNSUPPORTED;
+  if ((st = check_cost(cost)) != MOE_OK) return st;
+  if (!host_w || !host_w->w_gate || !host_w->w_up || !host_w->w_down || !resident)
+    return MOE_EINVAL;
+  if (!ok_ptr(ws) || !ok_ptr(host_ws)) return MOE_EINVAL;
+  const OffloadPlan op = make_offload_plan(*dims, T);
+  if (ws_bytes < op.d_total || host_ws_bytes < op.h_total) return MOE_EWORKSPACE;
+  if (T == 0) return MOE_OK;
+
+  const moe_dims_t& d = *dims;
+  const Plan& p = op.dev;
+  hipStream_t s = (hipStream_t)stream;
+  const int k = d.top_k, E = d.n_experts, P = T * k, H = d.hidden, I = d.inter;
+  const size_t eb = elem_bytes(d);
+  int32_t* ids = at<int32_t>(ws, p.ids);
+  float* wts = at<float>(ws, p.w);
+  uint8_t* exact = at<uint8_t>(ws, p.exact);
+  int32_t* offsets = at<int32_t>(ws, p.offsets);
+  int32_t* perm = at<int32_t>(ws, p.perm);
+  int32_t* row_of = at<int32_t>(ws, p.row_of);
+  int32_t* moffsets = at<int32_t>(ws, p.moffsets);
+  float* y_perm = at<float>(ws, p.y_perm);
+  float* y_s = d.n_shared > 0 ? at<float>(ws, p.y_s) : nullptr;
+  float* g_s = d.n_shared > 0 ? at<float>(ws, p.g_s) : nullptr;
+  int32_t* h_ids = at<int32_t>(host_ws, op.ids);
+  uint8_t* h_exact = at<uint8_t>(host_ws, op.exact);
+  int32_t* h_pairs = at<int32_t>(host_ws, op.pairs);
+  int32_t* h_tok = at<int32_t>(host_ws, op.tok);
+  int32_t* h_gexp = at<int32_t>(host_ws, op.gexp);
+  int32_t* h_gstart = at<int32_t>(host_ws, op.gstart);
+  int32_t* h_tokens = at<int32_t>(host_ws, op.tokens);
+  uint8_t* h_dec = at<uint8_t>(host_ws, op.dec);
+  float* h_y = at<float>(host_ws, op.y);
+
+  // 1. route, then stage the routed ids and the token rows on the host
+  hipError_t e = launch_route(d, T, x, w->w_router, nullptr, 0, MOE_MODE_STANDARD, ids, wts, exact,
+                              at<uint32_t>(ws, p.flags), at<float>(ws, p.logits), nullptr,
+                              d.shared_gate ? w->w_shared_gate : nullptr, g_s, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(h_ids, ids, (size_t)P * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(at<void>(host_ws, op.x), x, (size_t)T * H * eb, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return MOE_EHIP;
+  const double route_ms = ms_since(t0);
+
+  for (int i = 0; i < E; ++i) h_tokens[i] = 0;
+  for (int f = 0; f < P; ++f) {
+    const int ex = h_ids[f];
+    if (ex < 0 || ex >= E) return MOE_EHIP;  // the router never writes such an id
+    ++h_tokens[ex];
+  }
+  offload_decide(d, h_tokens, *resident, *cost, h_dec);
+  int missed = 0, fetched = 0, n_groups = 0, n_host = 0;
+  for (int i = 0; i < E; ++i) {
+    missed += h_dec[i] != MOE_OFFLOAD_NONE;
+    fetched += h_dec[i] == MOE_OFFLOAD_FETCH;
+    if (h_dec[i] == MOE_OFFLOAD_HOST) {
+      h_gexp[n_groups] = i;
+      h_gstart[n_groups] = n_host;
+      for (int f = 0; f < P; ++f)
+        if (h_ids[f] == i) {
+          h_pairs[n_host] = f;
+          h_tok[n_host] = f / k;
+          ++n_host;
+        }
+      ++n_groups;
+    }
+  }
+  h_gstart[n_groups] = n_host;
+  for (int f = 0; f < P; ++f) h_exact[f] = h_dec[h_ids[f]] != MOE_OFFLOAD_HOST;
+
+  // 2. fetches and the GPU's experts on the stream, the host FFN meanwhile
+  if (stats && stats->gpu_start) e = hipEventRecord((hipEvent_t)stats->gpu_start, s);
+  const size_t mat = (size_t)I * H * eb;
+  for (int i = 0; i < E && e == hipSuccess; ++i) {
+    if (h_dec[i] != MOE_OFFLOAD_FETCH) continue;
+    const size_t o = (size_t)i * mat;
+    e = hipMemcpyAsync((char*)w->w_gate + o, (const char*)host_w->w_gate + o, mat,
+                       hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync((char*)w->w_up + o, (const char*)host_w->w_up + o, mat,
+                         hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync((char*)w->w_down + o, (const char*)host_w->w_down + o, mat,
+                         hipMemcpyHostToDevice, s);
+  }
+  if (e == hipSuccess) e = hipMemcpyAsync(exact, h_exact, (size_t)P, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = launch_permute(P, E, ids, exact, offsets, perm, at<int32_t>(ws, p.inv), row_of, moffsets,
+                       at<int32_t>(ws, p.pscratch), s);
+  if (e == hipSuccess)
+    e = run_ffn(d, T, x, *w, MOE_MODE_STANDARD, offsets, moffsets, perm, y_perm, y_s, nullptr,
+                at<uint32_t>(ws, p.flags), ws, p, 0, Prof{}, s, false);
+  if (e == hipSuccess && stats && stats->gpu_stop) e = hipEventRecord((hipEvent_t)stats->gpu_stop, s);
+  if (e != hipSuccess) return MOE_EHIP;
+  const auto t1 = std::chrono::steady_clock::now();
+  double host_ms = 0.0, parallel_ms = 0.0;
+  if (n_host > 0) {
+    HostFfnArgs a{};
+    a.H = H;
+    a.I = I;
+    a.n_pairs = n_host;
+    a.n_groups = n_groups;
+    a.threads = host_threads(cost->cpu_threads);
+    a.tok = h_tok;
+    a.gexp = h_gexp;
+    a.gstart = h_gstart;
+    a.done = at<int32_t>(host_ws, op.done);
+    a.xf = at<float>(host_ws, op.xf);
+    a.act = at<float>(host_ws, op.act);
+    a.y = h_y;
+    host_expert_ffn(a, d.dtype == MOE_BF16, at<void>(host_ws, op.x), host_w->w_gate,
+                    host_w->w_up, host_w->w_down);
+    host_ms = ms_since(t1);
+  }
+  if (stats) {
+    e = stats->gpu_stop ? hipEventSynchronize((hipEvent_t)stats->gpu_stop) : hipStreamSynchronize(s);
+    if (e != hipSuccess) return MOE_EHIP;
+    parallel_ms = ms_since(t1);
+  }
+
+  // 3. host rows to the GPU, into the expert-output rows, then the combine
+  if (n_host > 0) {
+    float* d_y = at<float>(ws, op.d_y);
+    int32_t* d_pairs = at<int32_t>(ws, op.d_pairs);
+    e = hipMemcpyAsync(d_y, h_y, (size_t)n_host * H * 4, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(d_pairs, h_pairs, (size_t)n_host * 4, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = launch_offload_scatter(n_host, H, d_pairs, d_y, row_of, y_perm, exact, s);
+  }
+  if (e == hipSuccess) e = launch_combine_rows(d, T, y_perm, false, row_of, wts, exact, y_s, g_s, out, s);
+  if (e != hipSuccess) return MOE_EHIP;
+  if (stats) {
+    if (hipStreamSynchronize(s) != hipSuccess) return MOE_EHIP;
+    stats->missed_experts = missed;
+    stats->fetched_experts = fetched;
+    stats->host_experts = n_groups;
+    stats->host_pairs = n_host;
+    stats->route_ms = route_ms;
+    stats->host_ms = host_ms;
+    stats->parallel_ms = parallel_ms;
+    stats->wall_ms = ms_since(t0);
+    if (stats->decision) memcpy(stats->decision, h_dec, (size_t)E);
+  }
+  return MOE_OK;
 }
 
 }  // extern "C"

@@ -132,4 +132,15 @@ struct PermOut {
   int32_t *offsets, *perm, *inv, *row_of, *miss_offsets;
 };
 
+// Host FFN of the pairs run on the host (host memory throughout): n_groups
+// experts gexp[g], whose pairs are q in [gstart[g], gstart[g+1]) with token
+// tok[q]; xf [n_pairs][H] and act [n_pairs][I] are scratch, y [n_pairs][H]
+// the fp32 expert outputs; done [n_groups] are work counters.
+struct HostFfnArgs {
+  int H, I, n_pairs, n_groups, threads;
+  const int32_t *tok, *gexp, *gstart;
+  int32_t* done;
+  float *xf, *act, *y;
+};
+
 }  // namespace moe

@@ -865,3 +865,89 @@ def test_stall_free_short_sets_brute_force_through_the_layer():
                 assert not r["flags"][t] & O.FLAG_SHORT
             assert set(r["ids"][t]) == want
             assert list(r["ids"][t]) == [e for e in order if e in want]
+
+
+# ---- SPICE cost rule for missed experts ------------------------------------
+# SPICE page, "CPU-GPU collaboration: handling prefetch misses": fetch when
+# W_e / B_pcie + T_gpu_e is below T_cpu_e + 2H / B_pcie.
+
+def test_offload_rule_hand_worked_boundary():
+    # H = 64, I = 16, bf16: W_e = 3 * 16 * 64 * 2 = 6144 bytes, each pair moves
+    # 2 * 64 * 2 = 256 bytes.  With no compute time on either side the rule
+    # compares 6144 with 256 n: equal at n = 24 (not strictly cheaper: host),
+    # fetch from n = 25.  A dropped factor 2 would move the edge to 48 and a
+    # W_e of two matrices to 16.
+    d = {"dtype": "bf16", "inter": 16, "hidden": 64}
+    dec = O.offload_plan(d, [23, 24, 25, 48, 49], 0, 1.0e9, 0.0, 0.0)
+    assert dec == [O.OFFLOAD_HOST, O.OFFLOAD_HOST, O.OFFLOAD_FETCH, O.OFFLOAD_FETCH,
+                   O.OFFLOAD_FETCH]
+    f, h = O.offload_costs(6144, 128, 24, 1.0e9, 0.0, 0.0)
+    assert f == h == 6144 / 1.0e9
+
+
+def test_offload_rule_compute_terms():
+    # W_e / B = 4 s (4e9 bytes at 1e9 B/s), T_gpu = 0.5 s, host 1.5 s per pair
+    # and negligible transfers: fetch 4.5 s against 1.5 n s -> host for n <= 3
+    # (n = 3 ties at 4.5 s: host), fetch for n >= 4.
+    d = {"dtype": "f32", "inter": 1, "hidden": 1}
+    for n, want in ((1, O.OFFLOAD_HOST), (3, O.OFFLOAD_HOST), (4, O.OFFLOAD_FETCH)):
+        f, h = O.offload_costs(4.0e9, 0.0, n, 1.0e9, 0.5, 1.5)
+        assert f == 4.5 and h == 1.5 * n
+        assert (O.OFFLOAD_FETCH if f < h else O.OFFLOAD_HOST) == want
+    # through the plan: W_e there is 3 * 1 * 1 * 4 = 12 bytes, so fetching is
+    # cheap unless the GPU time dominates
+    assert O.offload_plan(d, [1], 0, 12.0, 2.0, 2.5) == [O.OFFLOAD_FETCH]   # 3.0 < 2.5 + 8/12
+    assert O.offload_plan(d, [1], 0, 12.0, 2.5, 2.5) == [O.OFFLOAD_HOST]    # 3.5 > 3.1667
+
+
+def test_offload_rule_fixed_host_term():
+    # a fixed host time per expert (its weight reads) counts once, not per
+    # pair: fetch 1.05 s against 0.6 + 0.1 n s (+ 8n bytes over the link) ->
+    # host up to n = 4, fetch at n = 5.  Counted per pair (0.7 n s) it would
+    # fetch from n = 2.
+    d = {"dtype": "f32", "inter": 1, "hidden": 1}
+    B = 12.0e9                                    # W_e = 12 bytes: 1 ns to fetch
+    dec = O.offload_plan(d, [1, 3, 4, 5], 0, B, 1.05 - 1e-9, 0.1, cpu_expert_s=0.6)
+    assert dec == [O.OFFLOAD_HOST, O.OFFLOAD_HOST, O.OFFLOAD_HOST, O.OFFLOAD_FETCH]
+    f, h = O.offload_costs(12, 4, 4, B, 0.5, 0.1, 0.6)
+    assert abs(h - (0.6 + 0.4 + 32 / B)) < 1e-15 and f == 12 / B + 0.5
+
+
+def test_offload_rule_resident_and_unrouted_need_nothing():
+    d = {"dtype": "bf16", "inter": 1408, "hidden": 2048}
+    dec = O.offload_plan(d, [0, 5, 5, 0], 0b0010, 50e9, 1e-5, 1e-3)
+    assert dec[0] == O.OFFLOAD_NONE and dec[1] == O.OFFLOAD_NONE and dec[3] == O.OFFLOAD_NONE
+    assert dec[2] in (O.OFFLOAD_FETCH, O.OFFLOAD_HOST)
+
+
+def test_offload_rule_switches_once_with_more_pairs():
+    # the host cost grows with the expert's pairs, the fetch cost does not: as
+    # pairs increase the decision can only move from host to fetch
+    rng = np.random.default_rng(11)
+    d = {"dtype": "bf16", "inter": 1408, "hidden": 2048}
+    for _ in range(200):
+        B = 10 ** rng.uniform(9, 11)
+        g = 10 ** rng.uniform(-6, -3)
+        c = 10 ** rng.uniform(-6, -2)
+        dec = O.offload_plan(d, list(range(1, 65)), 0, B, g, c)
+        first = next((i for i, v in enumerate(dec) if v == O.OFFLOAD_FETCH), len(dec))
+        assert all(v == O.OFFLOAD_HOST for v in dec[:first])
+        assert all(v == O.OFFLOAD_FETCH for v in dec[first:])
+
+
+def test_offload_queue_aware_balances_link_and_host():
+    # f32, H = I = 1000: W_e = 12e6 bytes at 12e6 B/s = 1 s per fetch; host
+    # 0.9 s per pair plus 8e3 / 12e6 s of transfers per pair.  On its own
+    # every single-pair expert goes to the host (0.9007 < 1); as queues:
+    # e0 host (0.9007), e1 fetch (1 < 1.8013), e2 host (1.8013 < 2),
+    # e3 fetch (2 < 2.702).
+    d = {"dtype": "f32", "inter": 1000, "hidden": 1000}
+    args = (0, 12e6, 0.0, 0.9)
+    assert O.offload_plan(d, [1, 1, 1, 1], *args) == [O.OFFLOAD_HOST] * 4
+    assert O.offload_plan(d, [1, 1, 1, 1], *args, queue_aware=True) == \
+        [O.OFFLOAD_HOST, O.OFFLOAD_FETCH, O.OFFLOAD_HOST, O.OFFLOAD_FETCH]
+    # order by decreasing pairs, then id: e1 (3 pairs: 2.7 s host) fetches,
+    # e3 (2 pairs) then faces 2 s of fetches against 1.8013 s on the host,
+    # e0 faces 2 s against 1.8013 + 0.9007, e2 then 3 s against 2.702
+    assert O.offload_plan(d, [1, 3, 1, 2], *args, queue_aware=True) == \
+        [O.OFFLOAD_FETCH, O.OFFLOAD_FETCH, O.OFFLOAD_HOST, O.OFFLOAD_HOST]
