@@ -22,6 +22,12 @@
  *     exceptions are named where they are declared: moe_layer_forward_noalloc
  *     (a library-held scratch array), moe_layer_forward_offload (waits for
  *     the routed ids and runs host threads) and moe_host_expert_ffn (host).
+ *     moe_layer_forward runs the shared experts of bf16 batches of 128 or
+ *     more tokens on a side stream (one non-blocking stream at the default
+ *     priority and two events per GPU, created by that GPU's first such call
+ *     and kept until the process ends), forked from and joined back into
+ *     `stream` inside the call, so the caller still sees one ordered stream
+ *     (and a graph captured on it holds both branches).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     the call returns without waiting.  Calls on one stream are ordered.
  *   - Errors are return codes.  All argument checks run on the host before
@@ -134,20 +140,25 @@ typedef enum {
   MOE_KERNEL_NONE = 0,
   MOE_KERNEL_ROUTE = 1,
   MOE_KERNEL_PERMUTE = 2,        /* runs inside ROUTE when T*k <= 1024 and E > 16 */
-  MOE_KERNEL_EXPERT_GATE_UP = 3, /* routed + shared gate/up projections (+ SiLU product) */
-  MOE_KERNEL_EXPERT_DOWN = 4,    /* routed + shared down projections                     */
+  MOE_KERNEL_EXPERT_GATE_UP = 3, /* routed (+ shared, unless SHARED_FFN runs apart) gate/up */
+  MOE_KERNEL_EXPERT_DOWN = 4,    /* routed (+ shared, unless SHARED_FFN runs apart) down  */
   MOE_KERNEL_FLOE_UP = 5,        /* INT2 up projection                                   */
   MOE_KERNEL_FLOE_SELECT = 6,    /* top-|u| channel selection                            */
   MOE_KERNEL_FLOE_GATE = 7,      /* gate on kept channels                                */
   MOE_KERNEL_FLOE_DOWN = 8,      /* down on kept channels                                */
-  MOE_KERNEL_COMBINE = 9         /* weighted combine (+ fused LoRE)                      */
+  MOE_KERNEL_COMBINE = 9,        /* weighted combine (+ fused LoRE)                      */
+  MOE_KERNEL_SHARED_FFN = 10     /* shared experts' own launches (bf16, T >= 128), run
+                                    on a side stream alongside the routing and the routed
+                                    experts; elapsed time 0 when the shared experts run
+                                    inside the routed launches                          */
 } moe_kernel_t;
 
 /* Optional copies of intermediate results from moe_layer_forward (host
  * struct of device pointers; each entry may be NULL).  prof_start/prof_stop
  * are hipEvent_t handles owned by the caller: when prof_kernel names a
  * kernel of this call, they are recorded on `stream` immediately before and
- * after that kernel's launch (so hipEventElapsedTime gives its duration). */
+ * after that kernel's launch (so hipEventElapsedTime gives its duration);
+ * for MOE_KERNEL_SHARED_FFN on the side stream that runs it. */
 typedef struct {
   int32_t* topk_ids;     /* [T][k] final expert per slot, ordered by (-logit, id)  */
   float* topk_w;         /* [T][k] combine weight per slot                          */

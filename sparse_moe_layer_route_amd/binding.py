@@ -53,7 +53,8 @@ _DEBUG_FIELDS = ["topk_ids", "topk_w", "exact", "flags", "logits", "mass", "expe
 
 
 KERNELS = {"none": 0, "route": 1, "permute": 2, "expert_gate_up": 3, "expert_down": 4,
-           "floe_up": 5, "floe_select": 6, "floe_gate": 7, "floe_down": 8, "combine": 9}
+           "floe_up": 5, "floe_select": 6, "floe_gate": 7, "floe_down": 8, "combine": 9,
+           "shared_ffn": 10}
 
 
 class MoeDebug(ctypes.Structure):

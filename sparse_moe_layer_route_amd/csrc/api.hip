@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <chrono>
 #include <cmath>
+#include <functional>
 #include <mutex>
 #include <thread>
 
@@ -243,7 +244,8 @@ hipError_t run_ffn(const moe_dims_t& d, int T, const void* x, const moe_weights_
                    moe_mode_t mode, const int32_t* offsets, const int32_t* moffsets,
                    const int32_t* perm, float* y_perm, float* y_s, int32_t* keep, uint32_t* flags,
                    void* ws, const Plan& p, int lore, const Prof& pf, hipStream_t s,
-                   bool y_bf16 = false) {
+                   bool y_bf16 = false, bool shared_apart = false,
+                   const std::function<hipError_t()>* after_up = nullptr) {
   if (mode == MOE_MODE_FLOE)
     return launch_floe(d, T, x, w, offsets, perm, at<float>(ws, p.u), keep, at<float>(ws, p.fa),
                        at<float>(ws, p.part), y_perm, flags, pf, s);
@@ -263,7 +265,7 @@ hipError_t run_ffn(const moe_dims_t& d, int T, const void* x, const moe_weights_
     if (r == hipSuccess && g_r)
       r = launch_ffn_gemm(d, T, x, w, offsets, perm, false, b.act, y_perm,
                           y_bf16 ? (bf16*)y_perm : nullptr, nullptr, s, which);
-    if (r == hipSuccess && g_s)
+    if (r == hipSuccess && g_s && !shared_apart)
       r = launch_ffn_gemm(d, T, x, w, nullptr, nullptr, true, b.acts, y_s, nullptr,
                           p.ys_part ? at<float>(ws, p.ys_part) : nullptr, s, which);
     return r;
@@ -271,6 +273,7 @@ hipError_t run_ffn(const moe_dims_t& d, int T, const void* x, const moe_weights_
   hipError_t e = pf.begin(MOE_KERNEL_EXPERT_GATE_UP, s);
   if (e == hipSuccess) e = stage(1);
   if (e == hipSuccess) e = pf.end(MOE_KERNEL_EXPERT_GATE_UP, s);
+  if (e == hipSuccess && after_up) e = (*after_up)();
   if (e == hipSuccess) e = pf.begin(MOE_KERNEL_EXPERT_DOWN, s);
   if (e == hipSuccess) e = stage(2);
   if (e == hipSuccess) e = pf.end(MOE_KERNEL_EXPERT_DOWN, s);
@@ -556,6 +559,40 @@ moe_status_t moe_combine(const moe_dims_t* dims, int32_t T, const float* y_perm,
 
 namespace {
 
+constexpr int kMaxDevices = 64;
+
+// Side stream of the shared experts' separate launches: one non-blocking
+// stream at the default priority and two events per GPU, made on that GPU's
+// first call that needs them and kept until the process ends.  `mu`
+// serialises the fork and join of concurrent calls on one GPU: each call's
+// side-stream wait must see its own fork record.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+SideStream g_side[kMaxDevices];
+std::mutex g_side_mu;
+
+SideStream* side_stream() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream& sd = g_side[dev];
+  if (!sd.s) {
+    hipStream_t st = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess)
+      return nullptr;
+    sd.fork = f;
+    sd.join = j;
+    sd.s = st;
+  }
+  return &sd;
+}
+
 // Argument checks shared by moe_layer_forward and its allocation-free
 // variant (everything except the workspace).
 moe_status_t check_forward(const moe_dims_t* dims, int32_t T, const void* x,
@@ -586,7 +623,8 @@ moe_status_t check_forward(const moe_dims_t* dims, int32_t T, const void* x,
 moe_status_t layer_forward_impl(const moe_dims_t* dims, int32_t T, const void* x,
                                 const moe_weights_t* w, const uint64_t* resident,
                                 int64_t resident_stride, moe_mode_t mode, void* out,
-                                const moe_debug_t* dbg, void* ws, const Plan& p, void* stream) {
+                                const moe_debug_t* dbg, void* ws, const Plan& p, void* stream,
+                                bool allow_side) {
   const moe_dims_t& d = *dims;
   hipStream_t s = (hipStream_t)stream;
   const int k = d.top_k, E = d.n_experts, P = T * k;
@@ -615,10 +653,41 @@ moe_status_t layer_forward_impl(const moe_dims_t* dims, int32_t T, const void* x
     pf.start = (hipEvent_t)dbg->prof_start;
     pf.stop = (hipEvent_t)dbg->prof_stop;
   }
+  // Shared experts with launches of their own depend on x alone: they run on
+  // the side stream from the start of the call, beside the routing and the
+  // routed experts, and join before the combine.
+#ifndef MOE_SIDE_AT
+#define MOE_SIDE_AT 1
+#endif
+  const bool apart = mfma && gemm_shared(d, T);
+  SideStream* sd = (apart && allow_side && MOE_SIDE_AT) ? side_stream() : nullptr;
+  std::unique_lock<std::mutex> side_lock;
+  hipError_t e = hipSuccess;
+  std::function<hipError_t()> side_launch = [&]() {
+    FfnBuffers sb{};
+    sb.acts = at<bf16>(ws, p.acts_b);
+    hipError_t r = hipStreamWaitEvent(sd->s, sd->fork, 0);
+    if (r == hipSuccess) r = pf.begin(MOE_KERNEL_SHARED_FFN, sd->s);
+    for (int which = 1; which <= 2 && r == hipSuccess; ++which)
+      r = launch_ffn_gemm(d, T, x, *w, nullptr, nullptr, true, sb.acts, y_s, nullptr,
+                          p.ys_part ? at<float>(ws, p.ys_part) : nullptr, sd->s, which);
+    if (r == hipSuccess) r = pf.end(MOE_KERNEL_SHARED_FFN, sd->s);
+    if (r == hipSuccess) r = hipEventRecord(sd->join, sd->s);
+    return r;
+  };
+  if (sd) {
+    side_lock = std::unique_lock<std::mutex>(sd->mu);
+    e = hipEventRecord(sd->fork, s);
+    if (e == hipSuccess && MOE_SIDE_AT == 1) e = side_launch();
+  } else {
+    // no separate shared launches: the bracket is empty
+    e = pf.begin(MOE_KERNEL_SHARED_FFN, s);
+    if (e == hipSuccess) e = pf.end(MOE_KERNEL_SHARED_FFN, s);
+  }
   // small batches are permuted by the router's top-k launch itself
   const PermOut po{at<int32_t>(ws, p.counter), offsets, perm, inv, row_of, moffsets};
   bool permuted = false;
-  hipError_t e = pf.begin(MOE_KERNEL_ROUTE, s);
+  if (e == hipSuccess) e = pf.begin(MOE_KERNEL_ROUTE, s);
   if (e == hipSuccess)
     e = launch_route(d, T, x, w->w_router, resident, resident_stride, mode, ids, wts, exact, flags,
                      logits, dbg ? dbg->mass : nullptr,
@@ -635,7 +704,9 @@ moe_status_t layer_forward_impl(const moe_dims_t* dims, int32_t T, const void* x
   const bool y_bf16 = mfma && !lore && gemm_routed(d, T);
   if (e == hipSuccess)
     e = run_ffn(d, T, x, *w, mode, offsets, moffsets, perm, y_perm, y_s, keep, flags, ws, p,
-                mfma && lore, pf, s, y_bf16);
+                mfma && lore, pf, s, y_bf16, sd != nullptr,
+                (sd && MOE_SIDE_AT == 2) ? &side_launch : nullptr);
+  if (e == hipSuccess && sd) e = hipStreamWaitEvent(s, sd->join, 0);
   if (e == hipSuccess) e = pf.begin(MOE_KERNEL_COMBINE, s);
   if (e == hipSuccess) {
     if (mfma || mode == MOE_MODE_FLOE)
@@ -668,7 +739,6 @@ moe_status_t layer_forward_impl(const moe_dims_t* dims, int32_t T, const void* x
 constexpr size_t kNoallocBytes = MOE_NOALLOC_SCRATCH_BYTES;
 __device__ __align__(256) uint8_t scratch[kNoallocBytes];
 
-constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
 
@@ -700,7 +770,7 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, int32_t T, const void* x,
   if (ws_bytes < p.total) return MOE_EWORKSPACE;
   if (T == 0) return MOE_OK;
   return layer_forward_impl(dims, T, x, w, resident, resident_stride, mode, out, dbg, ws, p,
-                            stream);
+                            stream, true);
 }
 
 moe_status_t moe_layer_forward_noalloc(const moe_dims_t* dims, int32_t T, const void* x,
@@ -717,7 +787,7 @@ moe_status_t moe_layer_forward_noalloc(const moe_dims_t* dims, int32_t T, const 
   void* ws = noalloc_scratch();
   if (!ws) return MOE_EHIP;
   return layer_forward_impl(dims, T, x, w, resident, resident_stride, mode, out, nullptr, ws, p,
-                            stream);
+                            stream, false);
 }
 
 }  // extern "C"

@@ -3,31 +3,30 @@
 //
 // Every weight matrix is stored with the contraction index contiguous
 // (gate/up [I][H], down [H][I]), so each output channel is one coalesced
-// 16-byte-per-lane sweep of a weight row by a wave64, dotted with up to NT
-// token rows at once, then a wave reduction.  A 256-thread block owns 16
-// consecutive rows of one expert (4 per wave).  Grid.y walks the experts
-// that received pairs: block y finds the y-th non-empty segment from the
-// offsets with one ballot, so no host round trip is needed.  Shared experts
-// use the same kernels with the identity token map.
+// 16-byte-per-lane sweep of a weight row by a wave64, dotted with several
+// token rows at once, then a wave reduction.  One launch per projection covers the routed and the shared experts: each
+// wave owns one output row and dots it with up to eight token rows per pass,
+// so a small layer puts many short, independent row sweeps in flight instead
+// of a few long chains.  Grid.y walks the experts that received pairs: block
+// y finds the y-th non-empty segment from the offsets with one ballot, so no
+// host round trip is needed; the shared experts follow with the identity
+// token map.
 #include "common.h"
 
 namespace moe {
 
-constexpr int GEMV_ROWS_PER_BLOCK = 16;
-constexpr int GEMV_ROWS_PER_WAVE = 4;
+constexpr int GEMV_WAVES = 4;   // rows per block: one output row per wave
+constexpr int GEMV_NT = 8;      // token rows dotted per pass over a weight row
 
+// Routed segment blockIdx.y of the pair permutation: the blockIdx.y-th
+// expert with a non-empty segment (e < 0: none).  Called by every thread.
 struct SegInfo {
-  int e;      // expert (routed) or shared-expert index
-  int seg0;   // first pair position of the segment (routed) or 0
-  int n;      // rows of the segment
+  int e;      // expert
+  int seg0;   // first pair position of the segment
+  int n;      // pairs in the segment
 };
-
-// Routed: the blockIdx.y-th expert with a non-empty segment.  Shared: expert
-// blockIdx.y over all T tokens.
-__device__ __forceinline__ SegInfo find_segment(int routed, int E, int T,
-                                                const int32_t* __restrict__ offsets) {
+__device__ __forceinline__ SegInfo find_segment(int E, const int32_t* __restrict__ offsets) {
   __shared__ int s_e, s_seg0, s_n;
-  if (!routed) return SegInfo{(int)blockIdx.y, 0, T};
   if (threadIdx.x < MOE_WAVE) {
     const int lane = threadIdx.x;
     int o0 = 0, n = 0;
@@ -48,113 +47,123 @@ __device__ __forceinline__ SegInfo find_segment(int routed, int E, int T,
   return SegInfo{s_e, s_seg0, s_n};
 }
 
-// gate+up: act[row(p)][col0 + i] = SiLU(x_t . W_g[i]) * (x_t . W_u[i])
-template <typename Tin, int NT>
-__global__ void __launch_bounds__(256)
-gate_up_kernel(const Tin* __restrict__ x, const Tin* __restrict__ wg, const Tin* __restrict__ wu,
-               int H, int I, int64_t e_stride, int routed, int E, int k, int T,
-               const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
-               float* __restrict__ act, int64_t act_ld) {
-  const SegInfo sg = find_segment(routed, E, T, offsets);
+// One launch for the gate/up projections of the routed experts and the
+// shared experts.  Grid.y: the first n_routed rows walk the experts that
+// received pairs (act[pos][i]); the next n_shared rows are shared expert s
+// over all T tokens (act_s[t][s * Is + i]).  Each wave owns one channel row
+// i and sweeps it once per pass of GEMV_NT tokens:
+//   act = SiLU(x_t . W_g[i]) * (x_t . W_u[i]).
+template <typename Tin>
+__global__ void __launch_bounds__(GEMV_WAVES * MOE_WAVE)
+gemv_gate_up_kernel(const Tin* __restrict__ x, const Tin* __restrict__ wg,
+                    const Tin* __restrict__ wu, const Tin* __restrict__ wsg,
+                    const Tin* __restrict__ wsu, int H, int I, int Is, int n_routed, int n_shared,
+                    int E, int k, int T, const int32_t* __restrict__ offsets,
+                    const int32_t* __restrict__ perm, float* __restrict__ act,
+                    float* __restrict__ act_s) {
+  const bool routed = (int)blockIdx.y < n_routed;
+  SegInfo sg{(int)blockIdx.y - n_routed, 0, T};
+  if (routed) sg = find_segment(E, offsets);   // block-uniform branch
   if (sg.e < 0) return;
-  const int lane = lane_id(), wv = threadIdx.x >> 6;
-  const Tin* wg_e = wg + (int64_t)sg.e * e_stride;
-  const Tin* wu_e = wu + (int64_t)sg.e * e_stride;
-  const int64_t col0 = routed ? 0 : (int64_t)sg.e * I;
-  const int r0 = blockIdx.x * GEMV_ROWS_PER_BLOCK + wv * GEMV_ROWS_PER_WAVE;
-  for (int tk = 0; tk < sg.n; tk += NT) {
-    const int nv = min(NT, sg.n - tk);
-    const Tin* xr[NT];
+  const int rows = routed ? I : Is;
+  const int i = blockIdx.x * GEMV_WAVES + (threadIdx.x >> 6);
+  if (i >= rows) return;
+  const int lane = lane_id();
+  const Tin* grow = (routed ? wg : wsg) + ((int64_t)sg.e * rows + i) * H;
+  const Tin* urow = (routed ? wu : wsu) + ((int64_t)sg.e * rows + i) * H;
+  for (int tk = 0; tk < sg.n; tk += GEMV_NT) {
+    const int nv = min(GEMV_NT, sg.n - tk);
+    const Tin* xr[GEMV_NT];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
+    for (int n = 0; n < GEMV_NT; ++n) {
       const int r = tk + (n < nv ? n : 0);
       const int tok = routed ? perm[sg.seg0 + r] / k : r;
       xr[n] = x + (int64_t)tok * H;
     }
-    for (int q = 0; q < GEMV_ROWS_PER_WAVE; ++q) {
-      const int i = r0 + q;
-      const Tin* grow = wg_e + (int64_t)i * H;
-      const Tin* urow = wu_e + (int64_t)i * H;
-      float ag[NT], au[NT];
+    float ag[GEMV_NT], au[GEMV_NT];
 #pragma unroll
-      for (int n = 0; n < NT; ++n) ag[n] = au[n] = 0.f;
-      for (int c = lane * 8; c < H; c += 8 * MOE_WAVE) {
-        float g8[8], u8[8];
-        elem<Tin>::load8(grow + c, g8);
-        elem<Tin>::load8(urow + c, u8);
+    for (int n = 0; n < GEMV_NT; ++n) ag[n] = au[n] = 0.f;
+    for (int c = lane * 8; c < H; c += 8 * MOE_WAVE) {
+      float g8[8], u8[8];
+      elem<Tin>::load8(grow + c, g8);
+      elem<Tin>::load8(urow + c, u8);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          if (n < nv) {
-            float x8[8];
-            elem<Tin>::load8(xr[n] + c, x8);
+      for (int n = 0; n < GEMV_NT; ++n) {
+        if (n < nv) {
+          float x8[8];
+          elem<Tin>::load8(xr[n] + c, x8);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              ag[n] = fmaf(g8[j], x8[j], ag[n]);
-              au[n] = fmaf(u8[j], x8[j], au[n]);
-            }
+          for (int j = 0; j < 8; ++j) {
+            ag[n] = fmaf(g8[j], x8[j], ag[n]);
+            au[n] = fmaf(u8[j], x8[j], au[n]);
           }
         }
       }
+    }
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        if (n < nv) {
-          const float g = wave_sum(ag[n]);
-          const float u = wave_sum(au[n]);
-          if (lane == 0) {
-            const int64_t row = routed ? (int64_t)sg.seg0 + tk + n : (int64_t)tk + n;
-            act[row * act_ld + col0 + i] = silu_f(g) * u;
-          }
+    for (int n = 0; n < GEMV_NT; ++n) {
+      if (n < nv) {
+        const float g = wave_sum(ag[n]);
+        const float u = wave_sum(au[n]);
+        if (lane == 0) {
+          const float v = silu_f(g) * u;
+          if (routed) act[((int64_t)sg.seg0 + tk + n) * I + i] = v;
+          else act_s[((int64_t)tk + n) * ((int64_t)n_shared * Is) + (int64_t)sg.e * Is + i] = v;
         }
       }
     }
   }
 }
 
-// down: out[row(p)][h] = sum over sub-matrices s of W_d[s][h][:] . act[row][s*K..]
-// (routed: one sub-matrix per expert; shared: all n_sub shared experts summed).
-template <typename Tin, int NT>
-__global__ void __launch_bounds__(256)
-down_kernel(const Tin* __restrict__ wd, int H, int K, int64_t e_stride, int n_sub,
-            int64_t sub_stride, int routed, int E, int T, const int32_t* __restrict__ offsets,
-            const float* __restrict__ act, int64_t act_ld, float* __restrict__ out) {
-  const SegInfo sg = find_segment(routed, E, T, offsets);
+// One launch for the down projections: grid.y rows below n_routed walk the
+// routed segments (y_perm[pos][h] = W_d[e][h] . act[pos]); row n_routed is
+// the shared experts, summed over the n_shared sub-matrices in order
+// (y_s[t][h] = sum_s W_ds[s][h] . act_s[t][s * Is ..]).  One output row h
+// per wave, GEMV_NT tokens per pass.
+template <typename Tin>
+__global__ void __launch_bounds__(GEMV_WAVES * MOE_WAVE)
+gemv_down_kernel(const Tin* __restrict__ wd, const Tin* __restrict__ wsd, int H, int I, int Is,
+                 int n_routed, int n_shared, int E, int T, const int32_t* __restrict__ offsets,
+                 const float* __restrict__ act, const float* __restrict__ act_s,
+                 float* __restrict__ y_perm, float* __restrict__ y_s) {
+  const bool routed = (int)blockIdx.y < n_routed;
+  SegInfo sg{0, 0, T};
+  if (routed) sg = find_segment(E, offsets);   // block-uniform branch
   if (sg.e < 0) return;
-  const int lane = lane_id(), wv = threadIdx.x >> 6;
-  const Tin* wd_e = wd + (routed ? (int64_t)sg.e * e_stride : 0);
-  const int r0 = blockIdx.x * GEMV_ROWS_PER_BLOCK + wv * GEMV_ROWS_PER_WAVE;
-  for (int tk = 0; tk < sg.n; tk += NT) {
-    const int nv = min(NT, sg.n - tk);
-    for (int q = 0; q < GEMV_ROWS_PER_WAVE; ++q) {
-      const int h = r0 + q;
-      float acc[NT];
+  const int h = blockIdx.x * GEMV_WAVES + (threadIdx.x >> 6);
+  if (h >= H) return;
+  const int lane = lane_id();
+  const int K = routed ? I : Is, n_sub = routed ? 1 : n_shared;
+  const int64_t ld = routed ? (int64_t)I : (int64_t)n_shared * Is;
+  const Tin* wrow0 = routed ? wd + ((int64_t)sg.e * H + h) * I : wsd + (int64_t)h * Is;
+  const float* a0 = routed ? act + (int64_t)sg.seg0 * ld : act_s;
+  float* out = routed ? y_perm + (int64_t)sg.seg0 * H : y_s;
+  for (int tk = 0; tk < sg.n; tk += GEMV_NT) {
+    const int nv = min(GEMV_NT, sg.n - tk);
+    float acc[GEMV_NT];
 #pragma unroll
-      for (int n = 0; n < NT; ++n) acc[n] = 0.f;
-      for (int s = 0; s < n_sub; ++s) {
-        const Tin* wrow = wd_e + (int64_t)s * sub_stride + (int64_t)h * K;
-        for (int c = lane * 8; c < K; c += 8 * MOE_WAVE) {
-          float w8[8];
-          elem<Tin>::load8(wrow + c, w8);
+    for (int n = 0; n < GEMV_NT; ++n) acc[n] = 0.f;
+    for (int sub = 0; sub < n_sub; ++sub) {
+      const Tin* wrow = wrow0 + (int64_t)sub * H * Is;
+      for (int c = lane * 8; c < K; c += 8 * MOE_WAVE) {
+        float w8[8];
+        elem<Tin>::load8(wrow + c, w8);
 #pragma unroll
-          for (int n = 0; n < NT; ++n) {
-            if (n < nv) {
-              const int64_t row = (routed ? (int64_t)sg.seg0 : 0) + tk + n;
-              float a8[8];
-              elem<float>::load8(act + row * act_ld + (int64_t)s * K + c, a8);
+        for (int n = 0; n < GEMV_NT; ++n) {
+          if (n < nv) {
+            float a8[8];
+            elem<float>::load8(a0 + (int64_t)(tk + n) * ld + (int64_t)sub * K + c, a8);
 #pragma unroll
-              for (int j = 0; j < 8; ++j) acc[n] = fmaf(w8[j], a8[j], acc[n]);
-            }
+            for (int j = 0; j < 8; ++j) acc[n] = fmaf(w8[j], a8[j], acc[n]);
           }
         }
       }
+    }
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        if (n < nv) {
-          const float v = wave_sum(acc[n]);
-          if (lane == 0) {
-            const int64_t row = (routed ? (int64_t)sg.seg0 : 0) + tk + n;
-            out[row * H + h] = v;
-          }
-        }
+    for (int n = 0; n < GEMV_NT; ++n) {
+      if (n < nv) {
+        const float v = wave_sum(acc[n]);
+        if (lane == 0) out[(int64_t)(tk + n) * H + h] = v;
       }
     }
   }
@@ -187,34 +196,24 @@ static hipError_t launch_dense_ffn_t(const moe_dims_t& d, int T, const Tin* x, c
                                      const int32_t* offsets, const int32_t* perm, int n_pairs_max,
                                      float* act, float* y_perm, float* act_s, float* y_s,
                                      const Prof& pf, hipStream_t s) {
-  constexpr int NT = 4;
   const int H = d.hidden, I = d.inter, E = d.n_experts, k = d.top_k;
-  const int max_active = n_pairs_max < E ? n_pairs_max : E;
-  hipError_t e = hipSuccess;
-  if (max_active > 0) {
-    dim3 g1(I / GEMV_ROWS_PER_BLOCK, max_active);
-    e = pf.begin(MOE_KERNEL_EXPERT_GATE_UP, s);
-    gate_up_kernel<Tin, NT><<<g1, 256, 0, s>>>(x, (const Tin*)w.w_gate, (const Tin*)w.w_up, H, I,
-                                               (int64_t)I * H, 1, E, k, T, offsets, perm, act, I);
-    if (e == hipSuccess) e = pf.end(MOE_KERNEL_EXPERT_GATE_UP, s);
-    dim3 g2(H / GEMV_ROWS_PER_BLOCK, max_active);
-    if (e == hipSuccess) e = pf.begin(MOE_KERNEL_EXPERT_DOWN, s);
-    down_kernel<Tin, NT><<<g2, 256, 0, s>>>((const Tin*)w.w_down, H, I, (int64_t)H * I, 1, 0, 1, E,
-                                            T, offsets, act, I, y_perm);
-    if (e == hipSuccess) e = pf.end(MOE_KERNEL_EXPERT_DOWN, s);
-  }
-  if (e != hipSuccess) return e;
-  if (d.n_shared > 0) {
-    const int Is = d.shared_inter, ns = d.n_shared;
-    dim3 g1(Is / GEMV_ROWS_PER_BLOCK, ns);
-    gate_up_kernel<Tin, NT><<<g1, 256, 0, s>>>(x, (const Tin*)w.ws_gate, (const Tin*)w.ws_up, H, Is,
-                                               (int64_t)Is * H, 0, E, k, T, offsets, perm, act_s,
-                                               (int64_t)ns * Is);
-    dim3 g2(H / GEMV_ROWS_PER_BLOCK, 1);
-    down_kernel<Tin, NT><<<g2, 256, 0, s>>>((const Tin*)w.ws_down, H, Is, 0, ns, (int64_t)H * Is, 0,
-                                            E, T, offsets, act_s, (int64_t)ns * Is, y_s);
-  }
-  return hipGetLastError();
+  const int Is = d.shared_inter, ns = d.n_shared;
+  const int n_routed = n_pairs_max < E ? n_pairs_max : E;
+  if (n_routed + ns == 0) return hipSuccess;
+  const int rows = I > Is ? I : Is;
+  hipError_t e = pf.begin(MOE_KERNEL_EXPERT_GATE_UP, s);
+  gemv_gate_up_kernel<Tin><<<dim3((rows + GEMV_WAVES - 1) / GEMV_WAVES, n_routed + ns),
+                             GEMV_WAVES * MOE_WAVE, 0, s>>>(
+      x, (const Tin*)w.w_gate, (const Tin*)w.w_up, (const Tin*)w.ws_gate, (const Tin*)w.ws_up, H, I,
+      Is, n_routed, ns, E, k, T, offsets, perm, act, act_s);
+  if (e == hipSuccess) e = pf.end(MOE_KERNEL_EXPERT_GATE_UP, s);
+  if (e == hipSuccess) e = pf.begin(MOE_KERNEL_EXPERT_DOWN, s);
+  gemv_down_kernel<Tin><<<dim3((H + GEMV_WAVES - 1) / GEMV_WAVES, n_routed + (ns > 0 ? 1 : 0)),
+                          GEMV_WAVES * MOE_WAVE, 0, s>>>(
+      (const Tin*)w.w_down, (const Tin*)w.ws_down, H, I, Is, n_routed, ns, E, T, offsets, act, act_s,
+      y_perm, y_s);
+  if (e == hipSuccess) e = pf.end(MOE_KERNEL_EXPERT_DOWN, s);
+  return e == hipSuccess ? hipGetLastError() : e;
 }
 
 hipError_t launch_shared_gate(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
