@@ -133,9 +133,11 @@ class HipEvents:
 
 
 # ------------------------------------------------------ algorithmic bytes --
-def step_traffic(cfg, T, mode, ids, exact, keep_count=None):
+def step_traffic(cfg, T, mode, ids, exact, keep_count=None, shared_apart=False):
     """Algorithmic bytes and flops of one layer forward, from the routing the
-    GPU actually took: each touched weight byte once, activations once."""
+    GPU actually took: each touched weight byte once, activations once.
+    `up` is the gate/up launch: routed experts, plus the shared experts
+    unless they run in launches of their own (shared_apart)."""
     H, I, E, k = cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k
     eb = 4 if cfg.dtype == "f32" else 2
     exact_experts = {int(e) for e, x in zip(ids.reshape(-1), exact.reshape(-1)) if x}
@@ -164,9 +166,10 @@ def step_traffic(cfg, T, mode, ids, exact, keep_count=None):
         act_b = eb                                     # activations in the layer's dtype
         n_miss = int((1 - exact).sum())
         r = cfg.lore_rank
-        up = dict(bytes=(len(exact_experts) * 2 * I * H + 2 * sh * H + len(miss_experts) * r * H) * eb
-                  + T * H * eb + (P * I + T * sh + n_miss * r) * act_b,
-                  flops=P * 2 * 2 * I * H + T * 2 * 2 * sh * H + n_miss * 2 * r * H)
+        sh_up = 0 if shared_apart else sh
+        up = dict(bytes=(len(exact_experts) * 2 * I * H + 2 * sh_up * H + len(miss_experts) * r * H) * eb
+                  + T * H * eb + (P * I + T * sh_up + n_miss * r) * act_b,
+                  flops=P * 2 * 2 * I * H + T * 2 * 2 * sh_up * H + n_miss * 2 * r * H)
     return dict(bytes=b, flops=f, up=up, distinct_experts=len(exact_experts),
                 lore_experts=len(miss_experts), pairs=P)
 
@@ -209,7 +212,19 @@ def measure(name, T, mode, steps, warmup, ev=None, want_roofline=False, layer=No
     M.moe_layer_forward(dims, T, x, w0, res, stride, mode, out, ws,
                         debug={"topk_ids": ids, "exact": exact})
     torch.cuda.synchronize()
-    tr = step_traffic(cfg, T, mode, ids.cpu().numpy(), exact.cpu().numpy())
+    # do the shared experts run in launches of their own (a non-empty bracket)?
+    shared_apart = False
+    if ev is not None and cfg.n_shared > 0:
+        a, b = ev.create(), ev.create()
+        dbg = M.MoeDebug()
+        dbg.prof_start, dbg.prof_stop, dbg.prof_kernel = a, b, M.binding.KERNELS["shared_ffn"]
+        M.moe_layer_forward(dims, T, x, w0, res, stride, mode, out, ws, debug=dbg)
+        torch.cuda.synchronize()
+        shared_apart = ev.elapsed_ms(a, b) > 0.02   # an empty bracket reads ~0
+        ev.destroy(a)
+        ev.destroy(b)
+    tr = step_traffic(cfg, T, mode, ids.cpu().numpy(), exact.cpu().numpy(),
+                      shared_apart=shared_apart)
     # weight copies so consecutive steps stream different bytes
     n_copies = max(1, min(16, math.ceil(1.0e9 / max(tr["bytes"], 1))))
     copies = [w0] + [{n: t.clone() for n, t in w0.items()} for _ in range(n_copies - 1)]
@@ -303,7 +318,8 @@ def measure(name, T, mode, steps, warmup, ev=None, want_roofline=False, layer=No
         rec = recorded_traffic(tf) if tf else None
         if rec is not None and kernel_digest(rec[1]) == rec[2]:
             traffic = rec[0]
-        roof.update(traffic=traffic, kernel=dom, avg_us=avg_us, bytes_per_launch=up["bytes"],
+        roof.update(traffic=traffic, kernel=dom + (" (routed)" if shared_apart else ""),
+                    avg_us=avg_us, bytes_per_launch=up["bytes"],
                     flops_per_launch=up["flops"], launches_timed=len(kms))
         r["roofline"] = roof
         for a, b in evs:

@@ -63,7 +63,7 @@ int gemm_shared_down_ksplit(const moe_dims_t& d, int T);
 hipError_t launch_floe(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
                        const int32_t* offsets, const int32_t* perm, float* u, int32_t* keep,
                        float* a, float* part, float* y_perm, uint32_t* flags, const Prof& pf,
-                       hipStream_t s);
+                       hipStream_t s, const FloeCombine* cb);
 hipError_t launch_combine(const moe_dims_t& d, int T, const float* y_perm, const int32_t* inv,
                           const float* topk_w, const uint8_t* exact, const int32_t* ids,
                           const float* y_s, const float* g_s, const float* lore_out, const void* x,
@@ -212,6 +212,9 @@ Plan make_plan(const moe_dims_t& d, int T, moe_mode_t mode) {
     p.keep = take(P * (size_t)d.floe_keep * 4);
     p.fa = take(P * (size_t)d.floe_keep * 4);
     p.part = take((size_t)floe_slices(d.floe_keep) * P * H * 4);
+    // dense shared experts beside the FloE routed experts
+    if (S && d.dtype == MOE_BF16) p.acts_b = take((size_t)T * S * 2);
+    if (S && d.dtype != MOE_BF16) p.act_s = take((size_t)T * S * 4);
   } else if (d.dtype == MOE_BF16) {
     p.act_b = take(P * I * 2);
     if (S) p.acts_b = take((size_t)T * S * 2);
@@ -245,10 +248,29 @@ hipError_t run_ffn(const moe_dims_t& d, int T, const void* x, const moe_weights_
                    const int32_t* perm, float* y_perm, float* y_s, int32_t* keep, uint32_t* flags,
                    void* ws, const Plan& p, int lore, const Prof& pf, hipStream_t s,
                    bool y_bf16 = false, bool shared_apart = false,
-                   const std::function<hipError_t()>* after_up = nullptr) {
-  if (mode == MOE_MODE_FLOE)
-    return launch_floe(d, T, x, w, offsets, perm, at<float>(ws, p.u), keep, at<float>(ws, p.fa),
-                       at<float>(ws, p.part), y_perm, flags, pf, s);
+                   const std::function<hipError_t()>* after_up = nullptr,
+                   const FloeCombine* floe_cb = nullptr) {
+  if (mode == MOE_MODE_FLOE) {
+    hipError_t e = hipSuccess;
+    if (d.n_shared > 0) {
+      // the shared experts are dense: the same kernels as the other modes,
+      // shared segments only
+      if (d.dtype == MOE_BF16) {
+        FfnBuffers sb{};
+        sb.acts = at<bf16>(ws, p.acts_b);
+        sb.ys = y_s;
+        e = launch_ffn_mfma(d, T, x, w, offsets, moffsets, perm, sb, 0, 1, 0, s, 1);
+        if (e == hipSuccess) e = launch_ffn_mfma(d, T, x, w, offsets, moffsets, perm, sb, 0, 1, 0, s, 2);
+      } else {
+        e = launch_dense_ffn(d, T, x, w, offsets, perm, 0, nullptr, y_perm, at<float>(ws, p.act_s),
+                             y_s, Prof{}, s);
+      }
+    }
+    if (e == hipSuccess)
+      e = launch_floe(d, T, x, w, offsets, perm, at<float>(ws, p.u), keep, at<float>(ws, p.fa),
+                      at<float>(ws, p.part), y_perm, flags, pf, s, floe_cb);
+    return e;
+  }
   if (d.dtype != MOE_BF16)
     return launch_dense_ffn(d, T, x, w, offsets, perm, T * d.top_k, at<float>(ws, p.act), y_perm,
                             d.n_shared > 0 ? at<float>(ws, p.act_s) : nullptr, y_s, pf, s);
@@ -702,20 +724,23 @@ moe_status_t layer_forward_impl(const moe_dims_t* dims, int32_t T, const void* x
   // rows are kept as bf16: the combine sums them in fp32 and the bytes between
   // the two launches halve.
   const bool y_bf16 = mfma && !lore && gemm_routed(d, T);
+  // FloE: the weighted combine is the last step of the FloE launches
+  const FloeCombine fcb{row_of, wts, exact, y_s, g_s, out};
+  const bool floe = mode == MOE_MODE_FLOE;
   if (e == hipSuccess)
     e = run_ffn(d, T, x, *w, mode, offsets, moffsets, perm, y_perm, y_s, keep, flags, ws, p,
                 mfma && lore, pf, s, y_bf16, sd != nullptr,
-                (sd && MOE_SIDE_AT == 2) ? &side_launch : nullptr);
+                (sd && MOE_SIDE_AT == 2) ? &side_launch : nullptr, floe ? &fcb : nullptr);
   if (e == hipSuccess && sd) e = hipStreamWaitEvent(s, sd->join, 0);
-  if (e == hipSuccess) e = pf.begin(MOE_KERNEL_COMBINE, s);
-  if (e == hipSuccess) {
-    if (mfma || mode == MOE_MODE_FLOE)
+  if (e == hipSuccess && !floe) e = pf.begin(MOE_KERNEL_COMBINE, s);
+  if (e == hipSuccess && !floe) {
+    if (mfma)
       e = launch_combine_rows(d, T, y_perm, y_bf16, row_of, wts, exact, y_s, g_s, out, s);
     else
       e = launch_combine(d, T, y_perm, inv, wts, exact, ids, y_s, g_s, nullptr, x,
                          lore ? w->lore_A : nullptr, lore ? w->lore_B : nullptr, out, s);
   }
-  if (e == hipSuccess) e = pf.end(MOE_KERNEL_COMBINE, s);
+  if (e == hipSuccess && !floe) e = pf.end(MOE_KERNEL_COMBINE, s);
   if (e == hipSuccess && dbg) {
     auto cp = [&](void* dst, const void* src, size_t bytes) {
       if (dst && e == hipSuccess) e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);

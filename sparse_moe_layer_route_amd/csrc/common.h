@@ -132,6 +132,18 @@ struct PermOut {
   int32_t *offsets, *perm, *inv, *row_of, *miss_offsets;
 };
 
+// Weighted combine fused into the last FloE launch: out [T][H] in the layer
+// dtype, from the slot -> row map, the slot weights and exact flags, and the
+// shared experts' output and gate (y_s / g_s may be null).
+struct FloeCombine {
+  const int32_t* row_of;
+  const float* topk_w;
+  const uint8_t* exact;
+  const float* y_s;
+  const float* g_s;
+  void* out;
+};
+
 // Host FFN of the pairs run on the host (host memory throughout): n_groups
 // experts gexp[g], whose pairs are q in [gstart[g], gstart[g+1]) with token
 // tok[q]; xf [n_pairs][H] and act [n_pairs][I] are scratch, y [n_pairs][H]

@@ -16,15 +16,19 @@
 // select: one 1024-thread workgroup per pair; |u| is staged through LDS with
 //         coalesced reads, then each thread holds the bit patterns (monotone
 //         for non-negative floats) of up to 16 consecutive channels in
-//         registers; MSB-first 8-bit radix select for the keep-th largest
-//         with lane-interleaved LDS histograms; one block scan lists the kept
+//         registers; MSB-first radix select (12 + 12 + 8 bits) for the
+//         keep-th largest with LDS histograms; one block scan lists the kept
 //         channels in ascending order (a second one ranks equal keys when
 //         only some of them are kept: lower channels first).
-// gate:   each wave owns two kept channel rows (contiguous H-vectors) and
-//         loads both before reducing.
-// down:   each thread owns 8 output columns and sweeps a slice of the kept
-//         channel rows, eight rows in flight; slices are summed in a fixed
-//         order by a small reduction kernel.
+// gate+down (layer forward): one block per slice of 16 kept channels of a
+//         pair forms their activations and their contribution to all H
+//         outputs (down rows prefetched during the gate sweep) into a slice
+//         partial; one more launch sums the slices in a fixed order and
+//         applies the combine weights, writing the layer output.
+// gate, down, reduce (the unfused expert-FFN entry point, which returns the
+//         per-pair rows): each gate wave owns two kept channel rows; each
+//         down thread owns 8 output columns of a 32-channel slice, eight rows
+//         in flight; the slices are summed in a fixed order.
 #include <type_traits>
 
 #include "common.h"
@@ -334,10 +338,7 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
                    uint32_t* __restrict__ flags) {
   constexpr int CH = FLOE_SELECT_CH;
   __shared__ uint32_t stage[FLOE_MAX_INTER];  // coalesced landing area for |u|
-  // 16 histogram copies picked by lane & 15, rows padded to 257 words: lanes
-  // of one wave that hit the same bin land on 16 banks, at most 4 per word
-  __shared__ int lhist[16][257];
-  __shared__ int hist[256];
+  __shared__ int hist[4096];
   __shared__ int wsum[FLOE_SELECT_THREADS / MOE_WAVE];
   __shared__ uint32_t s_prefix;
   __shared__ int s_need;
@@ -378,54 +379,59 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
     s_kmin = 0xFFFFFFFFu;
     s_done = 0;
   }
+  // MSB-first radix select on 12 + 12 + 8 bits: the 12-bit first digit
+  // (exponent and three mantissa bits) spreads |u| over tens of bins, so the
+  // histogram increments of the first pass, which every key makes, rarely
+  // collide on one LDS word.  (Merging a thread's increments in registers
+  // first costs more VALU issue than the atomics it saves: a wave64
+  // instruction takes four cycles on a 16-lane SIMD, and the whole select
+  // runs on one CU per pair.)
   uint32_t pmask = 0u;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int j = tid; j < 16 * 257; j += FLOE_SELECT_THREADS) (&lhist[0][0])[j] = 0;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
+    const int nb = pass == 2 ? 256 : 4096;
+    for (int j = tid; j < nb; j += FLOE_SELECT_THREADS) hist[j] = 0;
     __syncthreads();
     const uint32_t prefix = s_prefix;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       if (j < ch && i0 + j < I && (key[j] & pmask) == prefix)
-        atomicAdd(&lhist[lane & 15][(key[j] >> shift) & 0xFFu], 1);
+        atomicAdd(&hist[(key[j] >> shift) & (uint32_t)(nb - 1)], 1);
     }
     __syncthreads();
-    if (tid < 256) {
-      int c = 0;
+    // thread tid owns bins [bpt*tid, bpt*tid + bpt); suffix sums over threads
+    const int bpt = nb >= FLOE_SELECT_THREADS ? nb / FLOE_SELECT_THREADS : 1;
+    const bool owns = tid * bpt < nb;
+    int tsum = 0;
+    if (owns)
+      for (int b = 0; b < bpt; ++b) tsum += hist[tid * bpt + b];
+    int suf = tsum;  // inclusive suffix sum within the wave
 #pragma unroll
-      for (int w = 0; w < 16; ++w) c += lhist[w][tid];
-      hist[tid] = c;
+    for (int o = 1; o < MOE_WAVE; o <<= 1) {
+      const int n = __shfl_down(suf, o, MOE_WAVE);
+      if (lane + o < MOE_WAVE) suf += n;
     }
+    if (lane == 0) wsum[wv] = suf;
     __syncthreads();
-    if (tid < MOE_WAVE) {
-      const int need = s_need;
-      const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
-                h3 = hist[4 * lane + 3];
-      const int c4 = h0 + h1 + h2 + h3;
-      int suf = c4;  // inclusive suffix sum over lanes >= lane
-#pragma unroll
-      for (int o = 1; o < MOE_WAVE; o <<= 1) {
-        const int n = __shfl_down(suf, o, MOE_WAVE);
-        if (lane + o < MOE_WAVE) suf += n;
+    for (int w = wv + 1; w < FLOE_SELECT_THREADS / MOE_WAVE; ++w) suf += wsum[w];
+    const int need = s_need;
+    if (owns && suf >= need && suf - tsum < need) {
+      int gt = suf - tsum;
+      int b = bpt - 1;
+      for (; b > 0; --b) {
+        const int hb = hist[tid * bpt + b];
+        if (gt + hb >= need) break;
+        gt += hb;
       }
-      const uint64_t bal = __ballot(suf >= need);
-      const int L = 63 - __clzll(bal);  // highest lane whose suffix reaches need
-      if (lane == L) {
-        int gt = suf - c4;
-        const int hb[4] = {h0, h1, h2, h3};
-        int b = 3;
-        for (; b > 0; --b) {
-          if (gt + hb[b] >= need) break;
-          gt += hb[b];
-        }
-        s_prefix = prefix | ((uint32_t)(4 * L + b) << shift);
-        s_need = need - gt;
-        s_eqcnt = hb[b];  // after the last pass: keys equal to the threshold
-        // every key of the chosen bin is kept: the bin's lower bound already
-        // separates kept from dropped keys, and the remaining passes can go
-        s_done = hb[b] == need - gt;
-      }
+      const int hb = hist[tid * bpt + b];
+      s_prefix = prefix | ((uint32_t)(tid * bpt + b) << shift);
+      s_need = need - gt;
+      s_eqcnt = hb;  // after the last pass: keys equal to the threshold
+      // every key of the chosen bin is kept: the bin's lower bound already
+      // separates kept from dropped keys, and the remaining passes can go
+      s_done = hb == need - gt;
     }
-    pmask |= 0xFFu << shift;
+    pmask |= (uint32_t)(nb - 1) << shift;
     __syncthreads();
     if (s_done) break;
   }
@@ -636,7 +642,171 @@ floe_reduce_kernel(const float* __restrict__ part, int H, int n_slices, int P_ma
   y[(int64_t)p * H + h] = s;
 }
 
-int floe_slices(int n_keep) { return (n_keep + FLOE_DOWN_SLICE - 1) / FLOE_DOWN_SLICE; }
+// Gate and down of one slice of FLOE_GD_SLICE kept channels of one pair, in
+// one block: the four waves form the slice's a_c = SiLU(x . W_gate[ch_c]) u_ch
+// (four channel rows each, the H sweep loading every row's chunks before the
+// multiply-adds), then every thread sums a_c W_down[ch_c][h] over the slice
+// for its columns (eight at a time, the slice's down rows loaded first) into
+// the slice's partial row part[slice][p][:].  One launch instead of a gate and
+// a down launch, and the activations never leave the block.
+#ifndef FLOE_GD_SLICE_N
+#define FLOE_GD_SLICE_N 16
+#endif
+constexpr int FLOE_GD_SLICE = FLOE_GD_SLICE_N;
+constexpr int FLOE_GD_RPW = FLOE_GD_SLICE / 4;   // gate rows per wave
+constexpr int FLOE_GD_PRE = 2;                   // column chunks whose down rows load first
+
+template <typename Tin>
+__global__ void __launch_bounds__(256)
+floe_gate_down_kernel(const Tin* __restrict__ x, const Tin* __restrict__ wg,
+                      const Tin* __restrict__ wd, const float* __restrict__ u, int H, int I,
+                      int n_keep, int P_max, int E, int k, const int32_t* __restrict__ offsets,
+                      const int32_t* __restrict__ perm, const int32_t* __restrict__ keep,
+                      float* __restrict__ part) {
+  constexpr int S = FLOE_GD_SLICE, R = FLOE_GD_RPW, NB = 4;
+  __shared__ int s_ch[S];
+  __shared__ float s_a[S];
+  int f, t, e;
+  if (!pair_of(blockIdx.y, E, k, offsets, perm, f, t, e)) return;
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
+  const int c0 = blockIdx.x * S, nc = min(S, n_keep - c0);
+  if (tid < S) s_ch[tid] = keep[(int64_t)f * n_keep + c0 + min(tid, nc - 1)];
+  __syncthreads();
+  // the first FLOE_GD_PRE column chunks' down rows are in flight during the
+  // gate sweep (columns 8*tid + 2048*m)
+  Raw8<Tin> wpre[FLOE_GD_PRE][S];
+#pragma unroll
+  for (int m = 0; m < FLOE_GD_PRE; ++m) {
+    const int h = min(8 * tid + 2048 * m, H - 8);
+#pragma unroll
+    for (int c = 0; c < S; ++c) wpre[m][c].load(wd + ((int64_t)e * I + s_ch[c]) * H + h);
+  }
+  // gate: wave wv owns slice channels wv*R .. wv*R + R - 1
+  {
+    const Tin* xr = x + (int64_t)t * H;
+    const Tin* rows[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q) rows[q] = wg + ((int64_t)e * I + s_ch[wv * R + q]) * H;
+    float acc[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q) acc[q] = 0.f;
+    for (int h0 = 0; h0 < H; h0 += NB * 512) {
+      Raw8<Tin> w[R][NB], xv[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int h = min(h0 + 512 * j + 8 * lane, H - 8);
+#pragma unroll
+        for (int q = 0; q < R; ++q) w[q][j].load(rows[q] + h);
+        xv[j].load(xr + h);
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if (h0 + 512 * j + 8 * lane >= H) continue;
+        float xf[8];
+        xv[j].to_f(xf);
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+          float wf[8];
+          w[q][j].to_f(wf);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) acc[q] = fmaf(wf[c], xf[c], acc[q]);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const float g = wave_sum(acc[q]);
+      const int c = wv * R + q;
+      if (lane == 0) s_a[c] = c < nc ? silu_f(g) * u[(int64_t)blockIdx.y * I + s_ch[c]] : 0.f;
+    }
+  }
+  __syncthreads();
+  // down: columns 8*tid + 2048*m; channels past the slice's end carry a = 0
+  float a[S];
+#pragma unroll
+  for (int c = 0; c < S; ++c) a[c] = s_a[c];
+  float* prow = part + ((int64_t)blockIdx.x * P_max + blockIdx.y) * H;
+  auto sum_store = [&](const Raw8<Tin> (&w)[S], int h) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < S; ++c) {
+      float wf[8];
+      w[c].to_f(wf);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(a[c], wf[j], acc[j]);
+    }
+    *reinterpret_cast<float4*>(prow + h) = float4{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<float4*>(prow + h + 4) = float4{acc[4], acc[5], acc[6], acc[7]};
+  };
+#pragma unroll
+  for (int m = 0; m < FLOE_GD_PRE; ++m)
+    if (8 * tid + 2048 * m < H) sum_store(wpre[m], 8 * tid + 2048 * m);
+  for (int h = 8 * tid + 2048 * FLOE_GD_PRE; h < H; h += 2048) {
+    Raw8<Tin> w[S];
+#pragma unroll
+    for (int c = 0; c < S; ++c) w[c].load(wd + ((int64_t)e * I + s_ch[c]) * H + h);
+    sum_store(w, h);
+  }
+}
+
+// The slices' partials summed per pair and weighted per token in one launch:
+// out[t][h] = g_s(t) y_s(t)[h] + sum_j w_tj y_{p(t,j)}[h], y_p the sum of the
+// pair's slice partials.  A block takes 64 columns of one token; its
+// FLOE_RC_WAVES waves sum interleaved shares of the slices (each in slice
+// order, eight loads in flight), the shares are added in wave order, then
+// the k pairs in slot order as the combine does.
+constexpr int FLOE_RC_WAVES = 16;
+
+template <typename Tout>
+__global__ void __launch_bounds__(FLOE_RC_WAVES * 64)
+floe_reduce_combine_kernel(const float* __restrict__ part, int H, int k, int n_slices, int P_max,
+                           const int32_t* __restrict__ row_of, const float* __restrict__ topk_w,
+                           const uint8_t* __restrict__ exact, const float* __restrict__ y_s,
+                           const float* __restrict__ g_s, Tout* __restrict__ out) {
+  constexpr int B = 8, Q = FLOE_RC_WAVES;
+  __shared__ float red[MOE_MAX_TOPK][Q][64];
+  const int t = blockIdx.y, c = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int h = blockIdx.x * 64 + c;
+  for (int j = 0; j < k; ++j) {
+    const int p = row_of[(int64_t)t * k + j];
+    float s = 0.f;
+    if (p >= 0) {
+      for (int sl = q; sl < n_slices; sl += Q * B) {
+        float v[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const int ss = sl + Q * b;
+          v[b] = ss < n_slices ? part[((int64_t)ss * P_max + p) * H + h] : 0.f;
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) s += v[b];
+      }
+    }
+    red[j][q][c] = s;
+  }
+  __syncthreads();
+  if (q == 0) {
+    const float gs = g_s ? g_s[t] : 1.f;
+    const float ys = y_s ? y_s[(int64_t)t * H + h] : 0.f;
+    float acc = gs * ys;
+    for (int j = 0; j < k; ++j) {
+      const int64_t o = (int64_t)t * k + j;
+      if (row_of[o] < 0) continue;
+      float y = 0.f;
+#pragma unroll
+      for (int w = 0; w < Q; ++w) y += red[j][w][c];
+      if (!exact[o]) y += ys;
+      acc = fmaf(topk_w[o], y, acc);
+    }
+    elem<Tout>::store(out, (int64_t)t * H + h, acc);
+  }
+}
+
+int floe_slices(int n_keep) {
+  const int a = (n_keep + FLOE_DOWN_SLICE - 1) / FLOE_DOWN_SLICE;
+  const int b = (n_keep + FLOE_GD_SLICE - 1) / FLOE_GD_SLICE;
+  return a > b ? a : b;
+}
 int floe_max_inter() { return FLOE_MAX_INTER; }
 int floe_max_hidden() { return FLOE_MAX_HIDDEN; }
 
@@ -644,7 +814,8 @@ template <typename Tin>
 static hipError_t launch_floe_t(const moe_dims_t& d, int T, const Tin* x, const moe_weights_t& w,
                                 const int32_t* offsets, const int32_t* perm, float* u,
                                 int32_t* keep, float* a, float* part, float* y_perm,
-                                uint32_t* flags, const Prof& pf, hipStream_t s) {
+                                uint32_t* flags, const Prof& pf, hipStream_t s,
+                                const FloeCombine* cb) {
   const int H = d.hidden, I = d.inter, E = d.n_experts, k = d.top_k, nk = d.floe_keep;
   const int P = T * k;
   if (P == 0) return hipSuccess;
@@ -663,11 +834,28 @@ static hipError_t launch_floe_t(const moe_dims_t& d, int T, const Tin* x, const 
   floe_select_kernel<<<P, FLOE_SELECT_THREADS, 0, s>>>(u, I, nk, d.tie_margin, E, k, offsets, perm,
                                                         keep, flags);
   if (e == hipSuccess) e = pf.end(MOE_KERNEL_FLOE_SELECT, s);
+  if (cb) {
+    // in the layer forward: gate + down per slice, then the slices' sum and
+    // the weighted combine straight into the output
+    const int ns = (nk + FLOE_GD_SLICE - 1) / FLOE_GD_SLICE;
+    if (e == hipSuccess) e = pf.begin(MOE_KERNEL_FLOE_GATE, s);
+    floe_gate_down_kernel<Tin><<<dim3(ns, P), 256, 0, s>>>(
+        x, (const Tin*)w.w_gate, (const Tin*)w.w_down, u, H, I, nk, P, E, k, offsets, perm, keep,
+        part);
+    if (e == hipSuccess) e = pf.end(MOE_KERNEL_FLOE_GATE, s);
+    if (e == hipSuccess) e = pf.begin(MOE_KERNEL_FLOE_DOWN, s);
+    if (e == hipSuccess) e = pf.end(MOE_KERNEL_FLOE_DOWN, s);
+    if (e == hipSuccess) e = pf.begin(MOE_KERNEL_COMBINE, s);
+    floe_reduce_combine_kernel<Tin><<<dim3(H / 64, T), FLOE_RC_WAVES * 64, 0, s>>>(
+        part, H, k, ns, P, cb->row_of, cb->topk_w, cb->exact, cb->y_s, cb->g_s, (Tin*)cb->out);
+    if (e == hipSuccess) e = pf.end(MOE_KERNEL_COMBINE, s);
+    return e == hipSuccess ? hipGetLastError() : e;
+  }
   if (e == hipSuccess) e = pf.begin(MOE_KERNEL_FLOE_GATE, s);
   floe_gate_kernel<Tin><<<dim3((nk + 4 * FLOE_GATE_RPW - 1) / (4 * FLOE_GATE_RPW), P), 256, 0, s>>>(
       x, (const Tin*)w.w_gate, u, H, I, nk, E, k, offsets, perm, keep, a);
   if (e == hipSuccess) e = pf.end(MOE_KERNEL_FLOE_GATE, s);
-  const int ns = floe_slices(nk);
+  const int ns = (nk + FLOE_DOWN_SLICE - 1) / FLOE_DOWN_SLICE;
   if (e == hipSuccess) e = pf.begin(MOE_KERNEL_FLOE_DOWN, s);
   floe_down_kernel<Tin><<<dim3((H + FLOE_DOWN_COLS - 1) / FLOE_DOWN_COLS, ns, P), FLOE_DOWN_COLS / 8, 0, s>>>(
       (const Tin*)w.w_down, a, H, I, nk, P, E, k, offsets, perm, keep, part);
@@ -740,12 +928,12 @@ hipError_t launch_floe_pack(const moe_dims_t& d, int T, const int32_t* ids, cons
 hipError_t launch_floe(const moe_dims_t& d, int T, const void* x, const moe_weights_t& w,
                        const int32_t* offsets, const int32_t* perm, float* u,
                        int32_t* keep, float* a, float* part, float* y_perm, uint32_t* flags,
-                       const Prof& pf, hipStream_t s) {
+                       const Prof& pf, hipStream_t s, const FloeCombine* cb) {
   if (d.dtype == MOE_BF16)
     return launch_floe_t<bf16>(d, T, (const bf16*)x, w, offsets, perm, u, keep, a, part, y_perm,
-                               flags, pf, s);
+                               flags, pf, s, cb);
   return launch_floe_t<float>(d, T, (const float*)x, w, offsets, perm, u, keep, a, part, y_perm,
-                              flags, pf, s);
+                              flags, pf, s, cb);
 }
 
 }  // namespace moe

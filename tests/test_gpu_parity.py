@@ -70,6 +70,13 @@ FLOE_SMALL = {
                            floe_keep=104, token_counts=(5,), seed=104),
     "floe_wide": _variant("mixtral_floe", name="floe_wide", hidden=8192, n_experts=4, inter=512,
                           floe_keep=51, token_counts=(3,), seed=105),
+    # FloE routed experts beside dense gated shared experts, bf16 and fp32
+    "floe_shared": _variant("mixtral_floe", name="floe_shared", hidden=1024, n_experts=4,
+                            inter=1040, floe_keep=104, n_shared=2, shared_inter=256,
+                            shared_gate=True, token_counts=(7,), seed=111),
+    "floe_shared_f32": _variant("mixtral_floe", name="floe_shared_f32", hidden=512, n_experts=4,
+                                inter=528, floe_keep=53, n_shared=1, shared_inter=256,
+                                dtype="f32", token_counts=(6,), seed=112),
 }
 
 
@@ -110,7 +117,7 @@ def test_small_layer_parity(name, mode):
         _check_full(layer, layer.cfg.t_max, mode, layout="rows")
 
 
-@pytest.mark.parametrize("name", ["floe_small", "floe_wide"])
+@pytest.mark.parametrize("name", ["floe_small", "floe_wide", "floe_shared", "floe_shared_f32"])
 def test_floe_small_parity(name):
     layer = W.Layer(FLOE_SMALL[name])
     _check_full(layer, layer.cfg.t_max, "floe")
