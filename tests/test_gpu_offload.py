@@ -177,3 +177,36 @@ def test_offload_host_checks():
         M.moe_layer_forward_offload(rig.dims, 4, x, rig.wdev, rig.host, rig.res,
                                     M.offload_cost(0.0, 0.0, 0.0), out, rig.ws, rig.hws)
     assert ei.value.status == M.binding.MOE_EINVAL
+
+
+def test_offload_without_misses_is_the_standard_forward():
+    """All experts resident: nothing to fetch or run on the host, and the
+    output is the STANDARD forward's bit for bit; T = 0 enqueues nothing."""
+    layer = W.make_layer("dsv2_lite")
+    cfg = layer.cfg
+    T = 8
+    g = run_layer(layer, T, "standard")
+    rig = Rig(layer, T)
+    rig.res = (1 << cfg.n_experts) - 1
+    rig.wdev = dict(dev_weights(layer))          # every slot valid
+    out, st, dec = rig.run(T, M.offload_cost(50e9, 0.0, 0.0, 4))
+    assert st.missed_experts == 0 and st.fetched_experts == 0 and st.host_pairs == 0
+    assert not dec.any()
+    assert np.array_equal(out, g.out)
+    x = tensor(layer.x(1), cfg.dtype, "cuda")
+    o = torch.empty(1, cfg.hidden, dtype=torch.bfloat16, device="cuda")
+    M.moe_layer_forward_offload(rig.dims, 0, x, rig.wdev, rig.host, rig.res,
+                                M.offload_cost(50e9, 0.0, 0.0), o, rig.ws, rig.hws)
+
+
+def test_offload_single_host_thread_matches_many():
+    """The host FFN's thread count does not change a bit of the output."""
+    layer = W.make_layer("dsv2_lite")
+    T = 5
+    rig = Rig(layer, T)
+    outs = []
+    for threads in (1, 16):
+        out, st, _ = rig.run(T, M.offload_cost(50e9, 1.0, 0.0, threads))
+        assert st.host_pairs > 0 and st.fetched_experts == 0
+        outs.append(out)
+    assert np.array_equal(outs[0], outs[1])

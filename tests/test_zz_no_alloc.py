@@ -45,12 +45,19 @@ def _both(layer, T, mode, layout):
     ("dsv2_lite", "standard", "mfma16", 64, 1),
     ("granite_small", "stall_free", "rows", 203, 37),
     ("tiny", "lore", "rows", 16, 5),
+    ("floe_small", "floe", "rows", 6, 2),
 ])
 def test_noalloc_matches_workspace_forward(name, mode, layout, T1, T2):
+    import dataclasses
     if name == "granite_small":
-        import dataclasses
         cfg = dataclasses.replace(W.CONFIGS["granite_prefill"], name="granite_small", hidden=384,
                                   inter=144, token_counts=(203,), seed=103)
+        layer = W.Layer(cfg)
+    elif name == "floe_small":
+        # FloE with gated shared experts: the fused slice-sum + combine launch
+        cfg = dataclasses.replace(W.CONFIGS["mixtral_floe"], name="floe_small_sh", hidden=1024,
+                                  n_experts=4, inter=1040, floe_keep=104, n_shared=1,
+                                  shared_inter=256, shared_gate=True, token_counts=(6,), seed=113)
         layer = W.Layer(cfg)
     else:
         layer = W.make_layer(name)
