@@ -77,6 +77,12 @@ FLOE_SMALL = {
     "floe_shared_f32": _variant("mixtral_floe", name="floe_shared_f32", hidden=512, n_experts=4,
                                 inter=528, floe_keep=53, n_shared=1, shared_inter=256,
                                 dtype="f32", token_counts=(6,), seed=112),
+    # the FloE limits: I = 16384 (16 channels per select thread, |u| row filling its LDS
+    # stage) and H = 16384 (the packed x row of the up kernel)
+    "floe_max_inter": _variant("mixtral_floe", name="floe_max_inter", hidden=512, n_experts=4,
+                               inter=16384, floe_keep=1639, token_counts=(2,), seed=114),
+    "floe_max_hidden": _variant("mixtral_floe", name="floe_max_hidden", hidden=16384, n_experts=4,
+                                inter=256, floe_keep=26, token_counts=(2,), seed=115),
 }
 
 
@@ -117,7 +123,8 @@ def test_small_layer_parity(name, mode):
         _check_full(layer, layer.cfg.t_max, mode, layout="rows")
 
 
-@pytest.mark.parametrize("name", ["floe_small", "floe_wide", "floe_shared", "floe_shared_f32"])
+@pytest.mark.parametrize("name", ["floe_small", "floe_wide", "floe_shared", "floe_shared_f32",
+                                  "floe_max_inter", "floe_max_hidden"])
 def test_floe_small_parity(name):
     layer = W.Layer(FLOE_SMALL[name])
     _check_full(layer, layer.cfg.t_max, "floe")
