@@ -395,6 +395,78 @@ def cpu_baseline(name, T, mode, budget_s=8.0, layer=None):
                 cpu_model=model, host_cpus=host)
 
 
+def measure_library_gemm(ev, name="granite_prefill", T=4096, reps=30):
+    """Context for the grouped GEMM: its gate/up and down launches at the
+    prefill layer beside the vendor GEMM (torch.matmul / torch.bmm, bf16) on
+    the same flops without the token gather: one dense product over all
+    (token, slot) pairs, and a batched product with every expert given an
+    equal segment.  Timed with events; inputs are random bf16 tensors."""
+    import torch
+
+    import workloads as W
+    from workloads.device import dims_dict, tensor, upload
+    import sparse_moe_layer_route_amd as M
+
+    layer = W.make_layer(name)
+    cfg = layer.cfg
+    w0 = upload(layer, "cuda")
+    dd = dataclasses.replace(M.Dims(**dims_dict(cfg)), weight_layout="mfma16")
+    w0 = M.pack_weights(dd, w0)
+    dims = dd.c()
+    x = tensor(layer.x(T), cfg.dtype, "cuda")
+    ws = torch.empty(M.moe_workspace_size(dims, T, "standard"), dtype=torch.uint8, device="cuda")
+    out = torch.empty(T, cfg.hidden, dtype=torch.bfloat16, device="cuda")
+    ours = {}
+    for kern in ("expert_gate_up", "expert_down"):
+        times = []
+        for i in range(reps + 3):
+            a, b = ev.create(), ev.create()
+            dbg = M.MoeDebug()
+            dbg.prof_start, dbg.prof_stop, dbg.prof_kernel = a, b, M.binding.KERNELS[kern]
+            M.moe_layer_forward(dims, T, x, w0, None, 0, "standard", out, ws, debug=dbg)
+            torch.cuda.synchronize()
+            if i >= 3:
+                times.append(ev.elapsed_ms(a, b) * 1e3)
+            ev.destroy(a)
+            ev.destroy(b)
+        ours[kern] = sorted(times)[len(times) // 2]
+    del w0, ws
+    P, H, I, E = T * cfg.top_k, cfg.hidden, cfg.inter, cfg.n_experts
+    seg = P // E
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    g = torch.Generator(device="cuda").manual_seed(0)
+    rnd = lambda *shape: torch.randn(*shape, device="cuda", generator=g).to(torch.bfloat16)
+    res = {}
+    for part, K, N in (("gate_up", H, 2 * I), ("down", I, H)):
+        flops = 2.0 * P * K * N
+        a2, b2 = rnd(P, K), rnd(K, N)
+        dense = timed(lambda: torch.matmul(a2, b2))
+        del a2, b2
+        a3, b3 = rnd(E, seg, K), rnd(E, K, N)   # both contiguous
+        batched = timed(lambda: torch.bmm(a3, b3))
+        del a3, b3
+        mine = ours["expert_gate_up" if part == "gate_up" else "expert_down"]
+        res[part] = dict(ours_us=mine, ours_tflops=flops / (mine * 1e-6) / 1e12,
+                         dense_us=dense, dense_tflops=flops / (dense * 1e-6) / 1e12,
+                         batched_us=batched, batched_tflops=2.0 * E * seg * K * N / (batched * 1e-6) / 1e12)
+    torch.cuda.empty_cache()
+    return dict(kind="library_gemm_context", workload=name, tokens=T, pairs=P,
+                dense=f"[{P} x K] @ [K x N]", batched=f"{E} x [{seg} x K] @ [K x N]", **res)
+
+
 def measure_prefetch_adaptive(name, T, steps, warmup, tau=0.9):
     """The APEX adaptive prefetch call (budget, list, delta* and overlap) on
     its own: time per call, its HBM rate against the bytes it must move
@@ -743,6 +815,12 @@ def main():
                   f"{r['tokens_per_s']:.0f} tok/s, {r['step_gbs']:.0f} GB/s"
                   + (f", {r['roofline']['kernel']} {r['roofline']['frac']*100:.1f}% of {r['roofline']['bound']}"
                      if 'roofline' in r else ""), file=sys.stderr, flush=True)
+        r = measure_library_gemm(ev)
+        also.append(r)
+        print("# granite_prefill T=4096 grouped GEMM vs vendor GEMM on the same flops (no gather): " +
+              "; ".join(f"{k}: ours {r[k]['ours_us']:.1f} us ({r[k]['ours_tflops']:.0f} TFLOP/s), "
+                        f"dense {r[k]['dense_us']:.1f} us, batched {r[k]['batched_us']:.1f} us"
+                        for k in ("gate_up", "down")), file=sys.stderr, flush=True)
         r = measure_prefetch_adaptive("granite_prefill_distilled", 4096, args.steps, min(args.warmup, 5))
         also.append(r)
         print(f"# granite_prefill_distilled T=4096 adaptive prefetch: {r['us_per_call']:.1f} us/call, "

@@ -14,12 +14,11 @@
 // a block pulls 32 KiB per stage from L2 for 4.2 MFLOP (128 flop/B).  A
 // (weights) and B (token rows, gathered through the permutation) are both
 // k-contiguous in HBM.  Stages move global -> LDS directly (16-byte LDS DMA
-// loads, no register staging) into two rings: weight rows 5 deep (four
-// stages in flight: an expert's first tiles fetch its weights from HBM) and
-// token rows 4 deep (three in flight; they are mostly cache hits).  The
-// loop is bound by the latency of these loads rather than by LDS bandwidth
-// (the LDS is busy about an eighth of the time): three stages in flight
-// instead of two made the gate/up GEMM a fifth faster.  Each 64-byte LDS row
+// loads, no register staging) into two rings: weight rows 4 deep (three
+// stages in flight) and the gathered token rows 5 deep (four in flight).
+// The loop is bound by the latency of these loads rather than by LDS
+// bandwidth (the LDS is busy about an eighth of the time): three stages in
+// flight instead of two made the gate/up GEMM a fifth faster.  Each 64-byte LDS row
 // holds four 16-byte k chunks stored at chunk ^ ((row / 2) % 4): a 16-byte
 // LDS read is served eight lanes at a time over 32 banks, and the eight rows
 // of one such group then cover all 32 banks once.  Ordering is explicit: a
@@ -330,27 +329,33 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   // gate, 128-255 up), waves 4-7 the token rows.  Slot p of row r holds k chunk
   // p ^ ((r/2) % 4), so each 8-row group of a fragment read hits 32 distinct
   // banks.
-  const int chunk = (lane & 3) ^ ((lane >> 3) & 3);
   const bool is_w = wv < GWAVES / 2;
   // a weight wave issues stage s + GWST - 1 at step s, a token wave stage
-  // s + GTST - 1 (the weights come from HBM on an expert's first tiles and
-  // need the longer lead); before the barrier of step s each thread's own
-  // loads of stage s + 1 must have landed: at most GWST - 3 (GTST - 3) later
-  // stages of its loads may still be pending
+  // s + GTST - 1 (a sweep of the two depths at the Granite shape put the
+  // longer lead on the gathered token rows); before the barrier of step s
+  // each thread's own loads of stage s + 1 must have landed: at most
+  // GWST - 3 (GTST - 3) later stages of its loads may still be pending
   const int lead = is_w ? GWST - 1 : GTST - 1;
   static_assert(GWST >= 3 && GTST >= 3 && GWST + GTST <= 9, "ring depths");
   const int wsh = a.packed ? 4 : 0;
   constexpr int NQ = GROWS / 16 / GWAVES;   // DMA instructions per wave per stage
   constexpr int NMF = NW * WT * GTT;        // MFMAs per wave per stage
-  // row of this lane's DMA instruction q within the token or weight half
-  auto dma_row = [&](int q) __attribute__((always_inline)) { return 16 * (NQ * wv + q) + (lane >> 2); };
 
   // DMA state: the tile the stream is loading, its base and per-lane offsets
   int dj = 0, dk = 0;   // stream position of the next DMA stage: tile, stage in tile
   TileMeta dm = tile_get(tt, 0);
   const bf16* dbase;
   int off[NQ];
+  // Only at tile switches: the lane index is formed afresh (an opaque copy),
+  // so nothing lane-derived stays live across the stage loop for it (a value
+  // spilled there would be reloaded behind a full vmcnt wait, draining the
+  // ring).  The row of DMA instruction q within the token or weight half is
+  // 16 (NQ w + q) + lane / 4, its k chunk slot (lane % 4) ^ ((row / 2) % 4).
   auto set_dma = [&](const TileMeta& m, int j) __attribute__((always_inline)) {
+    int ln = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(ln));
+    const int chunk = (ln & 3) ^ ((ln >> 3) & 3);
+    auto dma_row = [&](int q) __attribute__((always_inline)) { return 16 * (NQ * wv + q) + (ln >> 2); };
     if (is_w) {
       const bf16* w = (GATED && wv >= GWAVES / 4) ? a.w1 : a.w0;
       dbase = w + (int64_t)m.g * a.w_stride;
@@ -428,6 +433,12 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   // registers spill) and slower on the shared experts' GEMM.
   auto epilogue = [&](uint32_t ebase, bool staged) __attribute__((always_inline)) {
     const int row_w0 = cm.n_idx * MW;
+    // Lane-derived values are formed here from an opaque copy of the lane
+    // index, not kept in registers across the stage loop: one spilled there
+    // would be reloaded here behind a full vmcnt wait, draining the ring.
+    int eln = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(eln));
+    const int r16 = eln & 15, kg = eln >> 4;
     if (YB && staged) {
       // bf16 rows: columns col0..col0+127, four passes of 16 tokens
       const int col0 = row_w0 + wm * (MW / 2);
@@ -444,7 +455,7 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
         for (int q = 0; q < 4; ++q) {   // one 4-row group at a time (register pressure)
-          const int row = (lane >> 4) + 4 * q, c = lane & 15;
+          const int row = kg + 4 * q, c = r16;
           u32x4 v[1] = {lds_read16(ebase + row * 256 + ((c ^ row) << 4))};
           lds_wait_all(v, v);
           const int tr = cm.row0 + wn * 16 * GTT + 16 * j + row;
