@@ -35,6 +35,23 @@
 
 namespace moe {
 
+// Expert weights (INT2 codes, kept gate and down rows) are read once per
+// call, so their loads are non-temporal: streamed without displacing x and
+// the small per-pair arrays the blocks share in L2.  FLOE_NT_WEIGHTS = 0
+// restores ordinary loads.
+#ifndef FLOE_NT_WEIGHTS
+#define FLOE_NT_WEIGHTS 1
+#endif
+typedef unsigned int floe_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 weight_load16(const void* p) {
+#if FLOE_NT_WEIGHTS
+  const floe_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const floe_u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *reinterpret_cast<const uint4*>(p);
+#endif
+}
+
 constexpr int FLOE_UP_RPW = 4;          // up rows per wave
 constexpr int FLOE_GATE_RPW = 2;        // gate rows per wave
 constexpr int FLOE_DOWN_COLS = 1024;    // output columns per down block (8 per thread)
@@ -82,7 +99,7 @@ floe_up_kernel(const Tin* __restrict__ x, const uint8_t* __restrict__ up_q,
 #pragma unroll
       for (int q = 0; q < FLOE_UP_RPW; ++q) {
         const int64_t row = (int64_t)e * I + min(i0 + q, I - 1);
-        cw[q] = *reinterpret_cast<const uint4*>(up_q + row * (H >> 2) + (int64_t)g * 16);
+        cw[q] = weight_load16(up_q + row * (H >> 2) + (int64_t)g * 16);
         sc[q] = half_bits_to_f(up_s[row * G + g]);
         zp[q] = half_bits_to_f(up_z[row * G + g]);
       }
@@ -262,7 +279,7 @@ floe_up_bf16_kernel(const bf16* __restrict__ x, const uint8_t* __restrict__ up_q
       const uint8_t* qr = up_q + row * (H >> 2);
       const uint16_t* sr = up_s + row * G;
       const uint16_t* zr = up_z + row * G;
-      cw[q] = *reinterpret_cast<const uint4*>(qr + g * 16);
+      cw[q] = weight_load16(qr + g * 16);
       sz[q] = (uint32_t)sr[g] | ((uint32_t)zr[g] << 16);
     }
     uint32_t xp[32];
@@ -508,6 +525,7 @@ template <typename Tin> struct Raw8;
 template <> struct Raw8<bf16> {
   uint4 v;
   __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void load_w(const bf16* p) { v = weight_load16(p); }
   __device__ __forceinline__ void to_f(float (&o)[8]) const {
     o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
     o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
@@ -518,6 +536,11 @@ template <> struct Raw8<float> {
   __device__ __forceinline__ void load(const float* p) {
     a = *reinterpret_cast<const float4*>(p);
     b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void load_w(const float* p) {
+    const uint4 u = weight_load16(p), v = weight_load16(p + 4);
+    a = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+    b = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
   }
   __device__ __forceinline__ void to_f(float (&o)[8]) const {
     o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
@@ -557,7 +580,7 @@ floe_gate_kernel(const Tin* __restrict__ x, const Tin* __restrict__ wg, const fl
     for (int j = 0; j < NB; ++j) {
       const int h = min(h0 + 512 * j + 8 * lane, H - 8);
 #pragma unroll
-      for (int q = 0; q < R; ++q) w[q][j].load(rows[q] + h);
+      for (int q = 0; q < R; ++q) w[q][j].load_w(rows[q] + h);
       xv[j].load(xr + h);
     }
 #pragma unroll
@@ -606,7 +629,7 @@ floe_down_kernel(const Tin* __restrict__ wd, const float* __restrict__ a, int H,
     for (int u = 0; u < B; ++u) {
       const int cc = min(c + u, c1 - 1);
       av[u] = c + u < c1 ? ar[cc] : 0.f;
-      w[u].load(wd + ((int64_t)e * I + kr[cc]) * H + h);
+      w[u].load_w(wd + ((int64_t)e * I + kr[cc]) * H + h);
     }
 #pragma unroll
     for (int u = 0; u < B; ++u) {
@@ -679,7 +702,7 @@ floe_gate_down_kernel(const Tin* __restrict__ x, const Tin* __restrict__ wg,
   for (int m = 0; m < FLOE_GD_PRE; ++m) {
     const int h = min(8 * tid + 2048 * m, H - 8);
 #pragma unroll
-    for (int c = 0; c < S; ++c) wpre[m][c].load(wd + ((int64_t)e * I + s_ch[c]) * H + h);
+    for (int c = 0; c < S; ++c) wpre[m][c].load_w(wd + ((int64_t)e * I + s_ch[c]) * H + h);
   }
   // gate: wave wv owns slice channels wv*R .. wv*R + R - 1
   {
@@ -696,7 +719,7 @@ floe_gate_down_kernel(const Tin* __restrict__ x, const Tin* __restrict__ wg,
       for (int j = 0; j < NB; ++j) {
         const int h = min(h0 + 512 * j + 8 * lane, H - 8);
 #pragma unroll
-        for (int q = 0; q < R; ++q) w[q][j].load(rows[q] + h);
+        for (int q = 0; q < R; ++q) w[q][j].load_w(rows[q] + h);
         xv[j].load(xr + h);
       }
 #pragma unroll
@@ -744,7 +767,7 @@ floe_gate_down_kernel(const Tin* __restrict__ x, const Tin* __restrict__ wg,
   for (int h = 8 * tid + 2048 * FLOE_GD_PRE; h < H; h += 2048) {
     Raw8<Tin> w[S];
 #pragma unroll
-    for (int c = 0; c < S; ++c) w[c].load(wd + ((int64_t)e * I + s_ch[c]) * H + h);
+    for (int c = 0; c < S; ++c) w[c].load_w(wd + ((int64_t)e * I + s_ch[c]) * H + h);
     sum_store(w, h);
   }
 }
