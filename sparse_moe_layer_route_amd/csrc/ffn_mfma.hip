@@ -521,9 +521,9 @@ __device__ __forceinline__ void down_chunk(const FfnMfmaArgs a, const TileInfo& 
   }
 }
 
-// Rows of one LoRE down tile: one row strip per wave.  K = r is one short
-// step, so a LoRE tile is mostly fixed cost; this size gives ~48 blocks for
-// three missed experts and ~512 for thirty-two.
+// Rows of one LoRE down tile: one row strip of RW row tiles per wave.  K = r
+// is one short step, so a LoRE tile is mostly fixed cost; at H = 2048 and
+// two row tiles per wave this gives 16 blocks per missed expert.
 template <int RW>
 struct LoreDownRows {
   static constexpr int ROWS = 16 * RW * 4;
@@ -583,14 +583,17 @@ __global__ void __launch_bounds__(256) FFN_DOWN_OCCUPANCY ffn_down_mfma_kernel(F
 #endif
 
 // Row tiles per wave.  Short segments (the decode case, a few tokens per
-// expert): gate/up 1, down 2 up to 4 token tiles (activation fragments reused
-// twice), 1 beyond.  Long segments (more than one token tile per expert on
-// average): each token fragment is reused over more weight rows, gate/up 2
-// and down 4 up to 4 token tiles.
+// expert): gate/up 1; down 1 with one token tile, 2 with two to four
+// (activation fragments reused twice), 1 beyond.  With one token tile the
+// single row tile doubles the blocks, so no tail of CUs holding two blocks
+// remains (one-token Qwen2-57B-shaped step 158 -> 153 us); with two to four
+// token tiles one row tile measured 9-20 us slower.  Long segments (more
+// than one token tile per expert on average): each token fragment is reused
+// over more weight rows, gate/up 2 and down 4 up to 4 token tiles.
 template <int NTT, bool LONG>
 struct RowTiles {
   static constexpr int UP = (LONG && NTT <= 4) ? FFN_LONG_UP_RW : 1;
-  static constexpr int DOWN = NTT <= 4 ? (LONG ? FFN_LONG_DOWN_RW : 2) : 1;
+  static constexpr int DOWN = NTT == 1 ? 1 : (NTT <= 4 ? (LONG ? FFN_LONG_DOWN_RW : 2) : 1);
 };
 
 template <int NTT, int WM, int WK, bool LONG>
