@@ -613,9 +613,11 @@ static void launch_kernels(FfnMfmaArgs up, FfnMfmaArgs dn, hipStream_t s, int wh
 }
 
 // Row strips per block for long segments up to 4 token tiles (the rest of
-// the 4 waves split K).
+// the 4 waves split K): two strips, each wave streaming half of K (the
+// Qwen2-57B-shaped 256-token step about 885 -> 875 us against one strip
+// with a four-way k split).
 #ifndef FFN_LONG_WM
-#define FFN_LONG_WM 1
+#define FFN_LONG_WM 2
 #endif
 
 // which: bit 0 = gate/up kernel, bit 1 = down kernel.  lore: LoRE tiles on.
