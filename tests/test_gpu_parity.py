@@ -151,6 +151,15 @@ def test_dsv2_lite(T, mode):
     _check_full(layer, T, mode)
 
 
+@pytest.mark.parametrize("mode", ["standard", "lore"])
+def test_dsv2_lite_long_segments(mode):
+    """256 tokens: 24 pairs per routed expert on average, so the decode
+    kernels take their long-segment form (two row strips per block, each
+    wave over half of K), and the shared experts run on the grouped GEMM."""
+    cfg = dataclasses.replace(W.CONFIGS["dsv2_lite"], token_counts=(256,))
+    _check_full(W.Layer(cfg), 256, mode)
+
+
 @pytest.mark.parametrize("T", [1, 32, 256])
 @pytest.mark.parametrize("mode", ["standard", "lore"])
 def test_qwen2_57b(T, mode):
