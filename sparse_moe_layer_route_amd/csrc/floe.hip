@@ -666,27 +666,38 @@ floe_reduce_kernel(const float* __restrict__ part, int H, int n_slices, int P_ma
 }
 
 // Gate and down of one slice of FLOE_GD_SLICE kept channels of one pair, in
-// one block: the four waves form the slice's a_c = SiLU(x . W_gate[ch_c]) u_ch
-// (four channel rows each, the H sweep loading every row's chunks before the
-// multiply-adds), then every thread sums a_c W_down[ch_c][h] over the slice
-// for its columns (eight at a time, the slice's down rows loaded first) into
-// the slice's partial row part[slice][p][:].  One launch instead of a gate and
-// a down launch, and the activations never leave the block.
+// one block of NWV waves: the waves form the slice's a_c = SiLU(x . W_gate[ch_c])
+// u_ch (S / NWV channel rows each), then every thread sums a_c W_down[ch_c][h]
+// over the slice for its columns (eight at a time) into the slice's partial
+// row part[slice][p][:].  One launch instead of a gate and a down launch, and
+// the activations never leave the block.  Loads are issued as: the first
+// batch of gate chunks (every row's chunks and x's), then the first columns'
+// down rows, then the gate multiply-adds, which wait only for their own batch
+// (a wave's loads complete in issue order), while the down rows arrive.  With
+// eight waves (bf16) a 4096-wide layer's gate and down rows are all in one
+// batch each, a single round trip to memory per block.
 #ifndef FLOE_GD_SLICE_N
 #define FLOE_GD_SLICE_N 16
 #endif
+#ifndef FLOE_GD_WAVES_BF16
+#define FLOE_GD_WAVES_BF16 8
+#endif
 constexpr int FLOE_GD_SLICE = FLOE_GD_SLICE_N;
-constexpr int FLOE_GD_RPW = FLOE_GD_SLICE / 4;   // gate rows per wave
-constexpr int FLOE_GD_PRE = 2;                   // column chunks whose down rows load first
-
 template <typename Tin>
-__global__ void __launch_bounds__(256)
+constexpr int floe_gd_waves() { return std::is_same<Tin, float>::value ? 4 : FLOE_GD_WAVES_BF16; }
+
+template <typename Tin, int NWV>
+__global__ void __launch_bounds__(NWV * 64)
 floe_gate_down_kernel(const Tin* __restrict__ x, const Tin* __restrict__ wg,
                       const Tin* __restrict__ wd, const float* __restrict__ u, int H, int I,
                       int n_keep, int P_max, int E, int k, const int32_t* __restrict__ offsets,
                       const int32_t* __restrict__ perm, const int32_t* __restrict__ keep,
                       float* __restrict__ part) {
-  constexpr int S = FLOE_GD_SLICE, R = FLOE_GD_RPW, NB = 4;
+  constexpr int TH = NWV * 64, S = FLOE_GD_SLICE, R = S / NWV;
+  constexpr int NB = NWV >= 8 ? 8 : 4;     // 512-input gate chunks per batch
+  constexpr int CS = 8 * TH;               // columns per down pass
+  constexpr int PRE = CS >= 4096 ? 1 : 4096 / CS;   // down passes whose rows load first
+  static_assert(S % NWV == 0, "slice channels per wave");
   __shared__ int s_ch[S];
   __shared__ float s_a[S];
   int f, t, e;
@@ -695,80 +706,85 @@ floe_gate_down_kernel(const Tin* __restrict__ x, const Tin* __restrict__ wg,
   const int c0 = blockIdx.x * S, nc = min(S, n_keep - c0);
   if (tid < S) s_ch[tid] = keep[(int64_t)f * n_keep + c0 + min(tid, nc - 1)];
   __syncthreads();
-  // the first FLOE_GD_PRE column chunks' down rows are in flight during the
-  // gate sweep (columns 8*tid + 2048*m)
-  Raw8<Tin> wpre[FLOE_GD_PRE][S];
+  // gate: wave wv owns slice channels wv*R .. wv*R + R - 1
+  const Tin* xr = x + (int64_t)t * H;
+  const Tin* rows[R];
 #pragma unroll
-  for (int m = 0; m < FLOE_GD_PRE; ++m) {
-    const int h = min(8 * tid + 2048 * m, H - 8);
+  for (int q = 0; q < R; ++q) rows[q] = wg + ((int64_t)e * I + s_ch[wv * R + q]) * H;
+  float acc[R];
+#pragma unroll
+  for (int q = 0; q < R; ++q) acc[q] = 0.f;
+  Raw8<Tin> w[R][NB], xv[NB];
+  auto gate_load = [&](int h0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int h = min(h0 + 512 * j + 8 * lane, H - 8);
+#pragma unroll
+      for (int q = 0; q < R; ++q) w[q][j].load_w(rows[q] + h);
+      xv[j].load(xr + h);
+    }
+  };
+  auto gate_fma = [&](int h0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (h0 + 512 * j + 8 * lane >= H) continue;
+      float xf[8];
+      xv[j].to_f(xf);
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        float wf[8];
+        w[q][j].to_f(wf);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[q] = fmaf(wf[c], xf[c], acc[q]);
+      }
+    }
+  };
+  gate_load(0);
+  // the first PRE passes' down rows (columns 8*tid + CS*m) load behind it
+  Raw8<Tin> wpre[PRE][S];
+#pragma unroll
+  for (int m = 0; m < PRE; ++m) {
+    const int h = min(8 * tid + CS * m, H - 8);
 #pragma unroll
     for (int c = 0; c < S; ++c) wpre[m][c].load_w(wd + ((int64_t)e * I + s_ch[c]) * H + h);
   }
-  // gate: wave wv owns slice channels wv*R .. wv*R + R - 1
-  {
-    const Tin* xr = x + (int64_t)t * H;
-    const Tin* rows[R];
+  gate_fma(0);
+  for (int h0 = NB * 512; h0 < H; h0 += NB * 512) {
+    gate_load(h0);
+    gate_fma(h0);
+  }
 #pragma unroll
-    for (int q = 0; q < R; ++q) rows[q] = wg + ((int64_t)e * I + s_ch[wv * R + q]) * H;
-    float acc[R];
-#pragma unroll
-    for (int q = 0; q < R; ++q) acc[q] = 0.f;
-    for (int h0 = 0; h0 < H; h0 += NB * 512) {
-      Raw8<Tin> w[R][NB], xv[NB];
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int h = min(h0 + 512 * j + 8 * lane, H - 8);
-#pragma unroll
-        for (int q = 0; q < R; ++q) w[q][j].load_w(rows[q] + h);
-        xv[j].load(xr + h);
-      }
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        if (h0 + 512 * j + 8 * lane >= H) continue;
-        float xf[8];
-        xv[j].to_f(xf);
-#pragma unroll
-        for (int q = 0; q < R; ++q) {
-          float wf[8];
-          w[q][j].to_f(wf);
-#pragma unroll
-          for (int c = 0; c < 8; ++c) acc[q] = fmaf(wf[c], xf[c], acc[q]);
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < R; ++q) {
-      const float g = wave_sum(acc[q]);
-      const int c = wv * R + q;
-      if (lane == 0) s_a[c] = c < nc ? silu_f(g) * u[(int64_t)blockIdx.y * I + s_ch[c]] : 0.f;
-    }
+  for (int q = 0; q < R; ++q) {
+    const float g = wave_sum(acc[q]);
+    const int c = wv * R + q;
+    if (lane == 0) s_a[c] = c < nc ? silu_f(g) * u[(int64_t)blockIdx.y * I + s_ch[c]] : 0.f;
   }
   __syncthreads();
-  // down: columns 8*tid + 2048*m; channels past the slice's end carry a = 0
+  // down: columns 8*tid + CS*m; channels past the slice's end carry a = 0
   float a[S];
 #pragma unroll
   for (int c = 0; c < S; ++c) a[c] = s_a[c];
   float* prow = part + ((int64_t)blockIdx.x * P_max + blockIdx.y) * H;
-  auto sum_store = [&](const Raw8<Tin> (&w)[S], int h) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto sum_store = [&](const Raw8<Tin> (&wr)[S], int h) {
+    float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < S; ++c) {
       float wf[8];
-      w[c].to_f(wf);
+      wr[c].to_f(wf);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = fmaf(a[c], wf[j], acc[j]);
+      for (int j = 0; j < 8; ++j) acc8[j] = fmaf(a[c], wf[j], acc8[j]);
     }
-    *reinterpret_cast<float4*>(prow + h) = float4{acc[0], acc[1], acc[2], acc[3]};
-    *reinterpret_cast<float4*>(prow + h + 4) = float4{acc[4], acc[5], acc[6], acc[7]};
+    *reinterpret_cast<float4*>(prow + h) = float4{acc8[0], acc8[1], acc8[2], acc8[3]};
+    *reinterpret_cast<float4*>(prow + h + 4) = float4{acc8[4], acc8[5], acc8[6], acc8[7]};
   };
 #pragma unroll
-  for (int m = 0; m < FLOE_GD_PRE; ++m)
-    if (8 * tid + 2048 * m < H) sum_store(wpre[m], 8 * tid + 2048 * m);
-  for (int h = 8 * tid + 2048 * FLOE_GD_PRE; h < H; h += 2048) {
-    Raw8<Tin> w[S];
+  for (int m = 0; m < PRE; ++m)
+    if (8 * tid + CS * m < H) sum_store(wpre[m], 8 * tid + CS * m);
+  for (int h = 8 * tid + CS * PRE; h < H; h += CS) {
+    Raw8<Tin> wr[S];
 #pragma unroll
-    for (int c = 0; c < S; ++c) w[c].load_w(wd + ((int64_t)e * I + s_ch[c]) * H + h);
-    sum_store(w, h);
+    for (int c = 0; c < S; ++c) wr[c].load_w(wd + ((int64_t)e * I + s_ch[c]) * H + h);
+    sum_store(wr, h);
   }
 }
 
@@ -862,7 +878,8 @@ static hipError_t launch_floe_t(const moe_dims_t& d, int T, const Tin* x, const 
     // the weighted combine straight into the output
     const int ns = (nk + FLOE_GD_SLICE - 1) / FLOE_GD_SLICE;
     if (e == hipSuccess) e = pf.begin(MOE_KERNEL_FLOE_GATE, s);
-    floe_gate_down_kernel<Tin><<<dim3(ns, P), 256, 0, s>>>(
+    constexpr int gdw = floe_gd_waves<Tin>();
+    floe_gate_down_kernel<Tin, gdw><<<dim3(ns, P), gdw * 64, 0, s>>>(
         x, (const Tin*)w.w_gate, (const Tin*)w.w_down, u, H, I, nk, P, E, k, offsets, perm, keep,
         part);
     if (e == hipSuccess) e = pf.end(MOE_KERNEL_FLOE_GATE, s);

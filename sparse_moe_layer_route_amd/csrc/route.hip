@@ -441,6 +441,9 @@ route_topk_small_kernel(const Tin* __restrict__ x, const float* __restrict__ log
 // the matrix cores (rows past tpb belong to the next block and go unused),
 // then wave j ranks token t0 + j.  po.perm != nullptr (a single block and at
 // most 1024 pairs): the block then permutes the batch's pairs itself.
+#ifndef ROUTE_FUSED_WAVE_PERM
+#define ROUTE_FUSED_WAVE_PERM 1
+#endif
 template <typename Tin>
 __global__ void __launch_bounds__(1024)
 route_fused_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w_router, int T, int H,
@@ -463,6 +466,13 @@ route_fused_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w_router, 
   }
   if (po.perm) {  // block-uniform; the barrier orders the waves' writes within the workgroup
     __syncthreads();
+#if ROUTE_FUSED_WAVE_PERM
+    if (T * k <= MOE_WAVE) {   // a few pairs: one wave sorts them, no block barriers
+      __shared__ int cnt[PERM_BUCKETS];
+      if (wv == 0) permute_one_wave(T * k, E, topk_ids, exact, cnt, po);
+      return;
+    }
+#endif
     permute_chunk(0, 1, T * k, E, topk_ids, exact, nullptr, po.offsets, po.perm, po.inv,
                   po.row_of, po.miss_offsets);
   }
