@@ -15,11 +15,16 @@
 // (weights) and B (token rows, gathered through the permutation) are both
 // k-contiguous in HBM.  Stages move global -> LDS directly (16-byte LDS DMA
 // loads, no register staging) into two rings: weight rows 4 deep (three
-// stages in flight) and the gathered token rows 5 deep (four in flight).
-// The loop is bound by the latency of these loads rather than by LDS
-// bandwidth (the LDS is busy about an eighth of the time): three stages in
-// flight instead of two made the gate/up GEMM a fifth faster.  Each 64-byte LDS row
-// holds four 16-byte k chunks stored at chunk ^ ((row / 2) % 4): a 16-byte
+// stages in flight) and the gathered token rows 5 deep.  Weight rows are read
+// 64 bytes (32 k) per stage; token rows 128 bytes (64 k, one whole cache
+// line) per load, so a token slot holds half the rows of a pair of stages
+// (rows 0-127 or 128-255, 64 k each): fetching each line's two halves in two
+// stages had made the L2 -> LDS stream 15% slower (with the arithmetic left
+// out, 131 -> 114 us for the Granite-shaped gate/up launch).  With both the
+// stream and the arithmetic measured apart (114 and 105 us there) the
+// whole launch takes about 133 us: the two overlap only in part.  Each
+// 64-byte weight row holds four 16-byte k chunks stored at chunk ^ ((row / 2)
+// % 4), each 128-byte token row eight stored at chunk ^ (row % 8): a 16-byte
 // LDS read is served eight lanes at a time over 32 banks, and the eight rows
 // of one such group then cover all 32 banks once.  Ordering is explicit: a
 // thread waits for its own DMA loads with a vmcnt wait, then a workgroup
@@ -242,11 +247,11 @@ __device__ __forceinline__ TileMeta tile_get(const TileTable& tt, int j) {
 
 // The GTT token fragments (LDS rows sb + 16j) and NW*WT weight fragments (rows
 // sa + m*MW + 16i) of one stage; row offsets are instruction immediates.
-template <int J, int NJ>
+template <int J, int NJ, int RS>
 __device__ __forceinline__ void read_fb(u32x4 (&fb)[NJ], uint32_t sb) {
   if constexpr (J < NJ) {
-    fb[J] = lds_read16_at<16 * J * GK * 2>(sb);
-    read_fb<J + 1, NJ>(fb, sb);
+    fb[J] = lds_read16_at<16 * J * RS>(sb);
+    read_fb<J + 1, NJ, RS>(fb, sb);
   }
 }
 template <int NW, int WT, int MW, int Q>
@@ -317,26 +322,33 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   const int nsub = GATED ? 1 : a.n_sub;
   const int kst = a.K / GK;          // K % 32 == 0 on this path
   const int nst_all = nsub * kst;
-  const int kper = (nst_all + a.ksplit - 1) / a.ksplit;
+  // every k range even, so a pair of stages never straddles two
+  const int kper = 2 * ((nst_all + 2 * a.ksplit - 1) / (2 * a.ksplit));
   const int k_lo = a.ksplit > 1 ? blockIdx.y * kper : 0;
   const int k_hi = a.ksplit > 1 ? min(nst_all, k_lo + kper) : nst_all;
   const int nst = max(0, k_hi - k_lo);       // stages per tile
   const int S = n_my * nst;                  // stages of this block's stream
 
-  // DMA plan: a stage is 512 LDS rows x 64 B; one wave instruction writes 16
-  // rows (1 KiB, lane l -> row l/4, 16-byte slot l%4).  Wave w issues
-  // instructions NQ*w..NQ*w+NQ-1: waves 0-3 the weight rows (GATED: 0-127
-  // gate, 128-255 up), waves 4-7 the token rows.  Slot p of row r holds k chunk
-  // p ^ ((r/2) % 4), so each 8-row group of a fragment read hits 32 distinct
-  // banks.
+  // DMA plan: one wave instruction writes 1 KiB of LDS (16 B per lane, lane
+  // l at byte 16 l).  Waves 0-3 load the weight rows of stage s (256 rows x
+  // 64 B, GATED: rows 0-127 gate, 128-255 up; instruction q of wave w: rows
+  // 16 (NQ w + q) + l / 4, slot l % 4 holding k chunk (l % 4) ^ ((row / 2) % 4)).
+  // Waves 4-7 load, at stream stage s, half s % 2 of the token rows of the
+  // stage pair (s & ~1, s | 1): 128 rows x 128 B (instruction q of wave w:
+  // rows 128 (s % 2) + 32 (w - 4) + 8 q + l / 8, slot l % 8 holding k chunk
+  // (l % 8) ^ (row % 8) of the pair's 64 k) into token slot s % GTST.
   const bool is_w = wv < GWAVES / 2;
-  // a weight wave issues stage s + GWST - 1 at step s, a token wave stage
-  // s + GTST - 1 (a sweep of the two depths at the Granite shape put the
-  // longer lead on the gathered token rows); before the barrier of step s
-  // each thread's own loads of stage s + 1 must have landed: at most
-  // GWST - 3 (GTST - 3) later stages of its loads may still be pending
+  // A weight wave issues stage s + GWST - 1 at step s, a token wave stream
+  // stage s + GTST - 1 (the sweep of the two depths at the Granite shape put
+  // the longer lead on the gathered token rows).  Before the barrier of step
+  // s each thread's own loads for the reads of stage s + 1 must have landed:
+  // for weights stage s + 1 (at most GWST - 3 later stages pending), for
+  // tokens both halves of its pair, the later being stream stage s + 1 (s
+  // even: GTST - 3 pending) or s + 2 (s odd: GTST - 4).  A token slot is
+  // refilled GTST stream stages later, after the last read of its pair (the
+  // reads of stage 2v + 1 at step 2v), which lead <= GTST - 1 guarantees.
   const int lead = is_w ? GWST - 1 : GTST - 1;
-  static_assert(GWST >= 3 && GTST >= 3 && GWST + GTST <= 9, "ring depths");
+  static_assert(GWST >= 3 && GTST >= 4 && GWST + GTST <= 9, "ring depths");
   const int wsh = a.packed ? 4 : 0;
   constexpr int NQ = GROWS / 16 / GWAVES;   // DMA instructions per wave per stage
   constexpr int NMF = NW * WT * GTT;        // MFMAs per wave per stage
@@ -345,12 +357,11 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   int dj = 0, dk = 0;   // stream position of the next DMA stage: tile, stage in tile
   TileMeta dm = tile_get(tt, 0);
   const bf16* dbase;
-  int off[NQ];
+  int off[2][NQ];   // [token half][instruction]; weight waves use off[0]
   // Only at tile switches: the lane index is formed afresh (an opaque copy),
   // so nothing lane-derived stays live across the stage loop for it (a value
   // spilled there would be reloaded behind a full vmcnt wait, draining the
-  // ring).  The row of DMA instruction q within the token or weight half is
-  // 16 (NQ w + q) + lane / 4, its k chunk slot (lane % 4) ^ ((row / 2) % 4).
+  // ring).
   auto set_dma = [&](const TileMeta& m, int j) __attribute__((always_inline)) {
     int ln = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     asm volatile("" : "+v"(ln));
@@ -365,20 +376,27 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
         const int row = min(m.n_idx * MW + r, a.R - 1);
         // fragment-major: the 16 rows of one DMA instruction are one
         // contiguous 1 KiB fragment, row r%16 chunk c at lane slot 16c + r%16
-        off[q] = a.packed ? (row >> 4) * (a.K >> 5) * 512 + (16 * chunk + (row & 15)) * 8
-                          : row * a.K + 8 * chunk;
+        off[0][q] = a.packed ? (row >> 4) * (a.K >> 5) * 512 + (16 * chunk + (row & 15)) * 8
+                             : row * a.K + 8 * chunk;
       }
     } else {
       dbase = GATED ? a.x : a.act_in;
+      // half h of a stage pair: token row 128 h + 32 (w - 4) + 8 q + lane / 8,
+      // 16-byte slot lane % 8 holding k chunk (lane % 8) ^ (row % 8) of the
+      // pair's 64 k: eight lanes read one whole 128-byte line of a row
+      const int c8 = (ln & 7) ^ ((ln >> 3) & 7);
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) off[q] = tok_base[j][dma_row(q) - 256] + 8 * chunk;
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+          off[h][q] = tok_base[j][128 * h + 32 * (wv - GWAVES / 2) + 8 * q + (ln >> 3)] + 8 * c8;
     }
   };
   set_dma(dm, 0);
   // The DMA stream visits (tile, k stage) in order; dma_next() returns the k
   // stage of the next stream stage.  Stages past the end reload the last one
   // into a slot nobody reads again, so every step issues exactly NQ loads per
-  // thread and "stage s+1 has landed" is "at most 2 NQ pending".
+  // thread and "stream stage x has landed" is a fixed count of pending loads.
   auto dma_next = [&]() __attribute__((always_inline)) {
     if (dk == nst) {            // the previous stage ended a tile
       if (dj + 1 < n_my) {
@@ -395,11 +413,15 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   auto issue_one = [&](int s, int kstage, int q) __attribute__((always_inline)) {
     bf16* dst = is_w ? &lds_w[s % GWST][(16 * NQ * wv) * GK]
                      : &lds_t[s % GTST][(16 * NQ * (wv - GWAVES / 2)) * GK];
-    const int s_ = kstage / kst, ko = (kstage % kst) * GK;
+    const int s_ = kstage / kst;
+    // token pairs: stream stage s is half s % 2 of the pair starting at the
+    // even k stage (stage and stream parities agree: every k range is even)
+    const int th = is_w ? 0 : (kstage & 1);
+    const int ko = ((kstage % kst) - th) * GK;
     // weight k stage stride: 32 elements row-major, a 512-element fragment packed
     const bf16* src = dbase + (is_w ? (int64_t)s_ * a.sub_stride + (ko << wsh)
                                     : (int64_t)s_ * a.sub_k_off + ko);
-    __builtin_amdgcn_global_load_lds((const void*)(src + off[q]),
+    __builtin_amdgcn_global_load_lds((const void*)(src + (th ? off[1][q] : off[0][q])),
                                      (__attribute__((address_space(3))) void*)(dst + q * 16 * GK),
                                      16, 0, 0);
   };
@@ -512,11 +534,14 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
     return;
   }
 
-  // byte address of this lane's fragment slot: logical chunk kg of row r
-  // lives at physical chunk kg ^ ((r/2) % 4); rows here are 16-aligned + r16
+  // byte address of this lane's weight fragment slot: logical chunk kg of row
+  // r lives at physical chunk kg ^ ((r/2) % 4); rows here are 16-aligned + r16
   const uint32_t ldsw0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)&lds_w[0][0];
   const uint32_t ldst0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)&lds_t[0][0];
   uint32_t lane_off = (uint32_t)(r16 * GK * 2 + ((kg ^ ((r16 >> 1) & 3)) * 16));
+  // token pairs: 128-byte rows, chunk c of row r at slot c ^ (r % 8); the
+  // odd stage of a pair reads chunks 4..7 (byte offset bit 6 toggled)
+  uint32_t lane_off_t = (uint32_t)(r16 * 128 + ((kg ^ (r16 & 7)) * 16));
 
   // Stage s's fragments sit in one register set while the next stage's are
   // read into the other: after the barrier that publishes stage s+1 a wave
@@ -526,9 +551,12 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
 #define GEMM_READ(FB, FA, st_)                                                          \
   {                                                                                     \
     asm volatile("" : "+v"(lane_off)); /* addresses formed here, not kept live */       \
-    const uint32_t slt = ldst0 + (uint32_t)(((st_) % GTST) * GN * GK * 2) + lane_off;    \
+    asm volatile("" : "+v"(lane_off_t));                                                \
     const uint32_t slw = ldsw0 + (uint32_t)(((st_) % GWST) * GN * GK * 2) + lane_off;    \
-    read_fb<0, GTT>(FB, slt + (uint32_t)(wn * 16 * GTT * GK * 2));                      \
+    /* the wave's 64 token rows lie in half wn / 2 of the pair of stage st_ */         \
+    const uint32_t slt = ldst0 + (uint32_t)(((((st_) & ~1) + (wn >> 1)) % GTST) * GN * GK * 2) \
+                         + (uint32_t)((wn & 1) * 64 * 128) + (lane_off_t ^ (((st_) & 1) << 6)); \
+    read_fb<0, GTT, 128>(FB, slt);                                                      \
     read_fa<NW, WT, MW, 0>(FA, slw + (uint32_t)(wm * (MW / 2) * GK * 2));               \
   }
 #define GEMM_MFMA_PART(FB, FA, q)                                                       \
@@ -543,10 +571,13 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   // the waves do not queue their DMA instructions all at once.  A tile's
   // last stage is followed by its epilogue, and the next stage's fragments
   // are read only after it (they are not live while the outputs are formed).
-#define GEMM_STEP(FBc, FAc, FBn, FAn, st_)                                              \
+// PAR: parity of st_.  Token pairs: the reads of stage st_ + 1 need both
+// halves of its pair, the later of which is stream stage st_ + 2 (st_ odd) or
+// st_ + 1 (st_ even); stages up to st_ + GTST - 2 have been issued.
+#define GEMM_STEP(FBc, FAc, FBn, FAn, st_, PAR)                                         \
   {                                                                                     \
     const bool last = ++ck == nst;                                                      \
-    if (is_w) GEMM_VMCNT((GWST - 3) * NQ); else GEMM_VMCNT((GTST - 3) * NQ);          \
+    if (is_w) GEMM_VMCNT((GWST - 3) * NQ); else GEMM_VMCNT((GTST - 3 - (PAR)) * NQ);  \
     __builtin_amdgcn_s_barrier();                                                       \
     if (!last && tok_live) GEMM_READ(FBn, FAn, (st_) + 1);                              \
     const int kref = dma_next();                                                        \
@@ -575,13 +606,14 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int q = 0; q < NQ; ++q) issue_one(s0, kref, q);
     }
-    if (is_w) GEMM_VMCNT((GWST - 2) * NQ); else GEMM_VMCNT((GTST - 2) * NQ);   // stage 0 landed
+    // stage 0 landed (token pairs: both halves of pair 0, stream stages 0 and 1)
+    if (is_w) GEMM_VMCNT((GWST - 2) * NQ); else GEMM_VMCNT((GTST - 3) * NQ);
     __builtin_amdgcn_s_barrier();
     if (tok_live) GEMM_READ(fb0, fa0, 0);
     lds_wait_all(fb0, fa0);
     for (int st = 0; st < S; st += 2) {
-      GEMM_STEP(fb0, fa0, fb1, fa1, st);
-      if (st + 1 < S) GEMM_STEP(fb1, fa1, fb0, fa0, st + 1);
+      GEMM_STEP(fb0, fa0, fb1, fa1, st, 0);
+      if (st + 1 < S) GEMM_STEP(fb1, fa1, fb0, fa0, st + 1, 1);
     }
   }
 #undef GEMM_READ
@@ -643,6 +675,8 @@ hipError_t launch_ffn_gemm(const moe_dims_t& d, int T, const void* x, const moe_
   const int P = T * d.top_k;
   // upper bound of m-tiles over all segments
   const int mt_max = shared ? G * ((T + GN - 1) / GN) : (P + GN - 1) / GN + std::min(E, P);
+  // token pairs take the contraction 64 at a time
+  if (H % 64 != 0 || R1 % 64 != 0) return hipErrorInvalidValue;
   if (which & 1) {
     GemmArgs a{};
     a.x = (const bf16*)x;
