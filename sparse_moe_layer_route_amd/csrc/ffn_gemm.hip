@@ -254,6 +254,21 @@ __device__ __forceinline__ void read_fb(u32x4 (&fb)[NJ], uint32_t sb) {
     read_fb<J + 1, NJ, RS>(fb, sb);
   }
 }
+// Entries LO..HI-1 of the stage's read list: the NJ token fragments (128-byte
+// token rows), then the weight fragments.
+template <int L, int HI, int NJ, int NW, int WT, int MW>
+__device__ __forceinline__ void read_range(u32x4 (&fb)[NJ], u32x4 (&fa)[NW * WT], uint32_t sb,
+                                           uint32_t sa) {
+  if constexpr (L < HI) {
+    if constexpr (L < NJ) {
+      fb[L] = lds_read16_at<16 * L * 128>(sb);
+    } else {
+      constexpr int Q = L - NJ, m = Q / WT, i = Q % WT;
+      fa[Q] = lds_read16_at<(m * MW + 16 * i) * GK * 2>(sa);
+    }
+    read_range<L + 1, HI, NJ, NW, WT, MW>(fb, fa, sb, sa);
+  }
+}
 template <int NW, int WT, int MW, int Q>
 __device__ __forceinline__ void read_fa(u32x4 (&fa)[NW * WT], uint32_t sa) {
   if constexpr (Q < NW * WT) {
@@ -548,16 +563,28 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
   // starts its LDS reads, runs stage s's MFMAs from registers, then waits for
   // the reads.  The last stage reads a slot holding a duplicate stage, which
   // is never multiplied.
-#define GEMM_READ(FB, FA, st_)                                                          \
-  {                                                                                     \
+#define GEMM_ADDR(st_)                                                                  \
     asm volatile("" : "+v"(lane_off)); /* addresses formed here, not kept live */       \
     asm volatile("" : "+v"(lane_off_t));                                                \
-    const uint32_t slw = ldsw0 + (uint32_t)(((st_) % GWST) * GN * GK * 2) + lane_off;    \
+    const uint32_t slw = ldsw0 + (uint32_t)(((st_) % GWST) * GN * GK * 2) + lane_off     \
+                         + (uint32_t)(wm * (MW / 2) * GK * 2);                          \
     /* the wave's 64 token rows lie in half wn / 2 of the pair of stage st_ */         \
     const uint32_t slt = ldst0 + (uint32_t)(((((st_) & ~1) + (wn >> 1)) % GTST) * GN * GK * 2) \
-                         + (uint32_t)((wn & 1) * 64 * 128) + (lane_off_t ^ (((st_) & 1) << 6)); \
+                         + (uint32_t)((wn & 1) * 64 * 128) + (lane_off_t ^ (((st_) & 1) << 6));
+#define GEMM_READ(FB, FA, st_)                                                          \
+  {                                                                                     \
+    GEMM_ADDR(st_)                                                                      \
     read_fb<0, GTT, 128>(FB, slt);                                                      \
-    read_fa<NW, WT, MW, 0>(FA, slw + (uint32_t)(wm * (MW / 2) * GK * 2));               \
+    read_fa<NW, WT, MW, 0>(FA, slw);                                                    \
+  }
+  constexpr int NRD = (GTT + NW * WT) / NQ;   // fragment reads per MFMA part
+  static_assert((GTT + NW * WT) % NQ == 0, "reads split evenly over the parts");
+#define GEMM_READ_PART(FB, FA, q)                                                       \
+  {                                                                                     \
+    if ((q) == 0) read_range<0, NRD, GTT, NW, WT, MW>(FB, FA, slt, slw);                \
+    else if ((q) == 1) read_range<NRD, 2 * NRD, GTT, NW, WT, MW>(FB, FA, slt, slw);     \
+    else if ((q) == 2) read_range<2 * NRD, 3 * NRD, GTT, NW, WT, MW>(FB, FA, slt, slw); \
+    else read_range<3 * NRD, 4 * NRD, GTT, NW, WT, MW>(FB, FA, slt, slw);               \
   }
 #define GEMM_MFMA_PART(FB, FA, q)                                                       \
   _Pragma("unroll") for (int t = 0; t < NMF / NQ; ++t) {                                \
@@ -567,10 +594,13 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
         __builtin_bit_cast(bf16x8_t, FA[m * WT + i]), __builtin_bit_cast(bf16x8_t, FB[j]), \
         acc[m][i][j], 0, 0, 0);                                                         \
   }
-  // The refill of the slot freed two barriers ago is spread over the MFMAs so
-  // the waves do not queue their DMA instructions all at once.  A tile's
-  // last stage is followed by its epilogue, and the next stage's fragments
-  // are read only after it (they are not live while the outputs are formed).
+  // The next stage's fragment reads and the refill of the slot freed two
+  // barriers ago are spread over the MFMA parts (three reads and one DMA
+  // load before each eight MFMAs), so the eight waves leaving a barrier do
+  // not queue their LDS reads all at once (1-2% off the Granite-shaped
+  // launches against issuing the twelve reads first).  A tile's last stage is
+  // followed by its epilogue, and the next stage's fragments are read only
+  // after it (they are not live while the outputs are formed).
 // PAR: parity of st_.  Token pairs: the reads of stage st_ + 1 need both
 // halves of its pair, the later of which is stream stage st_ + 2 (st_ odd) or
 // st_ + 1 (st_ even); stages up to st_ + GTST - 2 have been issued.
@@ -579,14 +609,18 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
     const bool last = ++ck == nst;                                                      \
     if (is_w) GEMM_VMCNT((GWST - 3) * NQ); else GEMM_VMCNT((GTST - 3 - (PAR)) * NQ);  \
     __builtin_amdgcn_s_barrier();                                                       \
-    if (!last && tok_live) GEMM_READ(FBn, FAn, (st_) + 1);                              \
-    const int kref = dma_next();                                                        \
-    __builtin_amdgcn_sched_barrier(0); /* reads issue before the MFMAs */              \
-    _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                    \
-      issue_one((st_) + lead, kref, q);                                                 \
-      __builtin_amdgcn_sched_barrier(0);                                                \
-      if (tok_live) { GEMM_MFMA_PART(FBc, FAc, q); }                                    \
-      __builtin_amdgcn_sched_barrier(0);                                                \
+    {                                                                                   \
+      const bool rd = !last && tok_live;                                                \
+      GEMM_ADDR((st_) + 1)                                                              \
+      const int kref = dma_next();                                                      \
+      _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                  \
+        if (rd) GEMM_READ_PART(FBn, FAn, q);                                            \
+        __builtin_amdgcn_sched_barrier(0);                                              \
+        issue_one((st_) + lead, kref, q);                                               \
+        __builtin_amdgcn_sched_barrier(0);                                              \
+        if (tok_live) { GEMM_MFMA_PART(FBc, FAc, q); }                                  \
+        __builtin_amdgcn_sched_barrier(0);                                              \
+      }                                                                                 \
     }                                                                                   \
     if (last) {                                                                         \
       ck = 0;                                                                           \
@@ -617,6 +651,8 @@ __global__ void __launch_bounds__(GTHREADS) ffn_gemm_kernel(GemmArgs a) {
     }
   }
 #undef GEMM_READ
+#undef GEMM_READ_PART
+#undef GEMM_ADDR
 #undef GEMM_STEP
 #undef GEMM_MFMA_PART
   GEMM_VMCNT(0);      // no DMA may outlive the workgroup's LDS
