@@ -322,21 +322,46 @@ floe_up_bf16_kernel(const bf16* __restrict__ x, const uint8_t* __restrict__ up_q
   if (lane < RPW && i0 + lane < I) u_out[(int64_t)blockIdx.y * I + i0 + lane] = uval;
 }
 
+// Wave-wide inclusive prefix sum on the DPP lane network (no LDS round
+// trips): shifts by 1, 2, 4 and 8 lanes within each row of 16 (lanes with no
+// source add 0), then the rows add the totals of the rows before them (lane
+// 15 of each row broadcast into rows 1 and 3, lane 31 into rows 2 and 3).
+__device__ __forceinline__ int dpp_scan_add(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);    // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);    // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);    // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);    // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return x;
+}
+// Wave-wide maximum (MAX) or minimum of unsigned values, in every lane: the
+// same network, lanes with no source keeping their own value.
+template <bool MAX>
+__device__ __forceinline__ uint32_t dpp_reduce_u32(uint32_t x) {
+  auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x111, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x112, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x114, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x118, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x142, 0xa, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, MOE_WAVE - 1);
+}
+
+constexpr int FLOE_SELECT_WAVES = FLOE_SELECT_THREADS / MOE_WAVE;
+
 // Block-wide exclusive scan of one int per thread (1024 threads).
 __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
   const int lane = lane_id(), wv = threadIdx.x >> 6;
-  int s = v;
-#pragma unroll
-  for (int o = 1; o < MOE_WAVE; o <<= 1) {
-    const int n = __shfl_up(s, o, MOE_WAVE);
-    if (lane >= o) s += n;
-  }
+  const int s = dpp_scan_add(v);
   if (lane == MOE_WAVE - 1) wsum[wv] = s;
   __syncthreads();
   int base = 0, tot = 0;
-  for (int w = 0; w < FLOE_SELECT_THREADS / MOE_WAVE; ++w) {
+#pragma unroll
+  for (int w = 0; w < FLOE_SELECT_WAVES; ++w) {
     const int c = wsum[w];
-    if (w < wv) base += c;
+    base += w < wv ? c : 0;
     tot += c;
   }
   __syncthreads();
@@ -347,7 +372,12 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
 // Thread tid owns the CH consecutive channels [tid*ch, tid*ch + ch) (ch <=
 // FLOE_SELECT_CH) and keeps their |u| bit patterns in registers through all
 // radix passes, so a pass is CH histogram increments per thread and the final
-// ascending listing is one block scan over per-thread counts.
+// ascending listing is one block scan over per-thread counts.  The select
+// runs on one CU per pair as a chain of block-wide steps, so each step is
+// kept short: scans and reductions on the DPP lane network, the histogram of
+// the next pass cleared while this one fills (two buffers), the bin sums read
+// 16 bytes at a time, and the mask-edge flag settled at the listing's
+// barrier (measured in stages: about 14 us before these changes).
 __global__ void __launch_bounds__(FLOE_SELECT_THREADS)
 floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin, int E, int k,
                    const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
@@ -355,8 +385,8 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
                    uint32_t* __restrict__ flags) {
   constexpr int CH = FLOE_SELECT_CH;
   __shared__ uint32_t stage[FLOE_MAX_INTER];  // coalesced landing area for |u|
-  __shared__ int hist[4096];
-  __shared__ int wsum[FLOE_SELECT_THREADS / MOE_WAVE];
+  __shared__ __attribute__((aligned(16))) int hist[2][4096];
+  __shared__ int wsum[FLOE_SELECT_WAVES];
   __shared__ uint32_t s_prefix;
   __shared__ int s_need;
   __shared__ uint32_t s_next, s_kmin;
@@ -368,7 +398,8 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
   const int i0 = tid * ch;
   const float* ur = u + (int64_t)blockIdx.x * I;
   // coalesced global reads into LDS (all of a thread's loads in flight
-  // together), then each thread takes its chunk
+  // together), then each thread takes its chunk; the first pass's
+  // histogram is cleared meanwhile
   {
     float v[CH];
 #pragma unroll
@@ -377,17 +408,12 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
       v[j] = i < I ? ur[i] : 0.f;
     }
 #pragma unroll
+    for (int j = 0; j < 4; ++j) hist[0][tid + j * FLOE_SELECT_THREADS] = 0;
+#pragma unroll
     for (int j = 0; j < CH; ++j) {
       const int i = tid + j * FLOE_SELECT_THREADS;
       if (i < I) stage[i] = __float_as_uint(fabsf(v[j]));
     }
-  }
-  __syncthreads();
-  uint32_t key[CH];
-#pragma unroll
-  for (int j = 0; j < CH; ++j) {
-    const int i = i0 + j;
-    key[j] = (j < ch && i < I) ? stage[i] : 0u;
   }
   if (tid == 0) {
     s_prefix = 0u;
@@ -395,6 +421,13 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
     s_next = 0u;
     s_kmin = 0xFFFFFFFFu;
     s_done = 0;
+  }
+  __syncthreads();
+  uint32_t key[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int i = i0 + j;
+    key[j] = (j < ch && i < I) ? stage[i] : 0u;
   }
   // MSB-first radix select on 12 + 12 + 8 bits: the 12-bit first digit
   // (exponent and three mantissa bits) spreads |u| over tens of bins, so the
@@ -407,46 +440,66 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
     const int nb = pass == 2 ? 256 : 4096;
-    for (int j = tid; j < nb; j += FLOE_SELECT_THREADS) hist[j] = 0;
-    __syncthreads();
+    int* h = hist[pass & 1];
+    // this pass's prefix and count, read before the barriers of the pass:
+    // the thread that finds the bin rewrites both after the second one
     const uint32_t prefix = s_prefix;
+    const int need = s_need;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       if (j < ch && i0 + j < I && (key[j] & pmask) == prefix)
-        atomicAdd(&hist[(key[j] >> shift) & (uint32_t)(nb - 1)], 1);
+        atomicAdd(&h[(key[j] >> shift) & (uint32_t)(nb - 1)], 1);
+    }
+    if (pass < 2) {   // the next pass's bins (4096, then 256)
+      int* hn = hist[(pass + 1) & 1];
+      for (int j = tid; j < (pass == 0 ? 4096 : 256); j += FLOE_SELECT_THREADS) hn[j] = 0;
     }
     __syncthreads();
     // thread tid owns bins [bpt*tid, bpt*tid + bpt); suffix sums over threads
     const int bpt = nb >= FLOE_SELECT_THREADS ? nb / FLOE_SELECT_THREADS : 1;
     const bool owns = tid * bpt < nb;
-    int tsum = 0;
-    if (owns)
-      for (int b = 0; b < bpt; ++b) tsum += hist[tid * bpt + b];
-    int suf = tsum;  // inclusive suffix sum within the wave
-#pragma unroll
-    for (int o = 1; o < MOE_WAVE; o <<= 1) {
-      const int n = __shfl_down(suf, o, MOE_WAVE);
-      if (lane + o < MOE_WAVE) suf += n;
+    int hb[4] = {0, 0, 0, 0};
+    if (bpt == 4) {
+      const int4 v4 = reinterpret_cast<const int4*>(h)[tid];
+      hb[0] = v4.x; hb[1] = v4.y; hb[2] = v4.z; hb[3] = v4.w;
+    } else if (owns) {
+      hb[0] = h[tid];
     }
-    if (lane == 0) wsum[wv] = suf;
+    const int tsum = hb[0] + hb[1] + hb[2] + hb[3];
+    const int pre = dpp_scan_add(tsum);
+    if (lane == MOE_WAVE - 1) wsum[wv] = pre;
     __syncthreads();
-    for (int w = wv + 1; w < FLOE_SELECT_THREADS / MOE_WAVE; ++w) suf += wsum[w];
-    const int need = s_need;
+    int after = 0;   // the waves after this one
+#pragma unroll
+    for (int w = 0; w < FLOE_SELECT_WAVES; ++w) {
+      const int c = wsum[w];
+      after += w > wv ? c : 0;
+    }
+    // inclusive suffix sum: the keys in this thread's bins and above
+    const int suf = __builtin_amdgcn_readlane(pre, MOE_WAVE - 1) - pre + tsum + after;
     if (owns && suf >= need && suf - tsum < need) {
-      int gt = suf - tsum;
-      int b = bpt - 1;
-      for (; b > 0; --b) {
-        const int hb = hist[tid * bpt + b];
-        if (gt + hb >= need) break;
-        gt += hb;
+      // the bin holding the need-th largest key: walk down from the top bin
+      int gt = suf - tsum, sel = 0, gsel = 0, hsel = 0;
+      bool found = false;
+#pragma unroll
+      for (int b = 3; b >= 0; --b) {
+        if (b < bpt && !found) {
+          if (gt + hb[b] >= need) {
+            found = true;
+            sel = b;
+            gsel = gt;
+            hsel = hb[b];
+          } else {
+            gt += hb[b];
+          }
+        }
       }
-      const int hb = hist[tid * bpt + b];
-      s_prefix = prefix | ((uint32_t)(tid * bpt + b) << shift);
-      s_need = need - gt;
-      s_eqcnt = hb;  // after the last pass: keys equal to the threshold
+      s_prefix = prefix | ((uint32_t)(tid * bpt + sel) << shift);
+      s_need = need - gsel;
+      s_eqcnt = hsel;  // after the last pass: keys equal to the threshold
       // every key of the chosen bin is kept: the bin's lower bound already
       // separates kept from dropped keys, and the remaining passes can go
-      s_done = hb == need - gt;
+      s_done = hsel == need - gsel;
     }
     pmask |= (uint32_t)(nb - 1) << shift;
     __syncthreads();
@@ -485,38 +538,38 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
     }
   }
   // smallest kept key (the threshold itself unless the passes stopped early)
+  // and largest dropped key, per wave into LDS before the listing's barrier
   {
     uint32_t mn = 0xFFFFFFFFu;
 #pragma unroll
     for (int j = 0; j < CH; ++j)
       if (((kept >> j) & 1u) && key[j] < mn) mn = key[j];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const uint32_t v = __shfl_xor(mn, o, MOE_WAVE);
-      mn = v < mn ? v : mn;
+    mn = dpp_reduce_u32<false>(mn);
+    const uint32_t bm = dpp_reduce_u32<true>(below_max);
+    if (lane == 0) {
+      atomicMin(&s_kmin, mn);
+      atomicMax(&s_next, bm);
     }
-    if (lane == 0) atomicMin(&s_kmin, mn);
   }
-  int kept_total;
-  int pos = block_excl_scan(__popc(kept), wsum, kept_total);
+  // ascending listing: exclusive scan of the per-thread kept counts
+  const int cnt = __popc(kept);
+  const int pre = dpp_scan_add(cnt);
+  if (lane == MOE_WAVE - 1) wsum[wv] = pre;
+  __syncthreads();
+  int pos = pre - cnt;
+#pragma unroll
+  for (int w = 0; w < FLOE_SELECT_WAVES; ++w) {
+    const int c = wsum[w];
+    pos += w < wv ? c : 0;
+  }
   int32_t* ko = keep_out + (int64_t)f * n_keep;
 #pragma unroll
   for (int j = 0; j < CH; ++j)
-    if ((kept >> j) & 1u) ko[pos++] = i0 + j;
+    if (((kept >> j) & 1u) && pos < n_keep) ko[pos++] = i0 + j;
   // near-tie at the edge: next value below the threshold, or a tie at it
-  if (n_keep < I) {
-    uint32_t m = below_max;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const uint32_t v = __shfl_xor(m, o, MOE_WAVE);
-      m = v > m ? v : m;
-    }
-    if (lane == 0) atomicMax(&s_next, m);
-    __syncthreads();
-    if (tid == 0) {
-      const bool tie = eq_total > need_eq || (__uint_as_float(s_kmin) - __uint_as_float(s_next)) < margin;
-      if (tie) atomicOr(&flags[t], 8u);
-    }
+  if (n_keep < I && tid == 0) {
+    const bool tie = eq_total > need_eq || (__uint_as_float(s_kmin) - __uint_as_float(s_next)) < margin;
+    if (tie) atomicOr(&flags[t], 8u);
   }
 }
 
@@ -547,6 +600,11 @@ template <> struct Raw8<float> {
   }
 };
 
+// A kept channel read from the keep list, held inside [0, I): the select
+// writes exactly n_keep valid channels, and this keeps a weight-row address
+// in bounds whatever the list holds.
+__device__ __forceinline__ int keep_channel(int v, int I) { return (unsigned)v < (unsigned)I ? v : 0; }
+
 // Kept channel c of pair p: a[p][c] = SiLU(x_t . W_gate[e][keep[c]]) * u[p][keep[c]].
 // Wave w of block b owns channels (4b + w) * FLOE_GATE_RPW + q; the H loop
 // takes 512 inputs per step (8 per lane) and loads both rows' chunks first.
@@ -568,7 +626,7 @@ floe_gate_kernel(const Tin* __restrict__ x, const Tin* __restrict__ wg, const fl
   const Tin* rows[R];
 #pragma unroll
   for (int q = 0; q < R; ++q) {
-    ch[q] = keep[(int64_t)f * n_keep + min(c0 + q, n_keep - 1)];
+    ch[q] = keep_channel(keep[(int64_t)f * n_keep + min(c0 + q, n_keep - 1)], I);
     rows[q] = wg + ((int64_t)e * I + ch[q]) * H;
   }
   float acc[R];
@@ -629,7 +687,7 @@ floe_down_kernel(const Tin* __restrict__ wd, const float* __restrict__ a, int H,
     for (int u = 0; u < B; ++u) {
       const int cc = min(c + u, c1 - 1);
       av[u] = c + u < c1 ? ar[cc] : 0.f;
-      w[u].load_w(wd + ((int64_t)e * I + kr[cc]) * H + h);
+      w[u].load_w(wd + ((int64_t)e * I + keep_channel(kr[cc], I)) * H + h);
     }
 #pragma unroll
     for (int u = 0; u < B; ++u) {
@@ -704,7 +762,7 @@ floe_gate_down_kernel(const Tin* __restrict__ x, const Tin* __restrict__ wg,
   if (!pair_of(blockIdx.y, E, k, offsets, perm, f, t, e)) return;
   const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
   const int c0 = blockIdx.x * S, nc = min(S, n_keep - c0);
-  if (tid < S) s_ch[tid] = keep[(int64_t)f * n_keep + c0 + min(tid, nc - 1)];
+  if (tid < S) s_ch[tid] = keep_channel(keep[(int64_t)f * n_keep + c0 + min(tid, nc - 1)], I);
   __syncthreads();
   // gate: wave wv owns slice channels wv*R .. wv*R + R - 1
   const Tin* xr = x + (int64_t)t * H;
