@@ -62,28 +62,48 @@ template <> struct elem<bf16> {
 };
 
 // --------------------------------------------------------- wave64 ops -----
+// Reductions and scans run on the DPP lane network rather than through LDS
+// permutes (each of which is an LDS round trip): values move by 1, 2, 4 and
+// 8 lanes within each row of 16, then the rows take the totals of the rows
+// before them (lane 15 of each row broadcast into rows 1 and 3, lane 31 into
+// rows 2 and 3), so lane l ends with the result over lanes 0..l.  Called by
+// whole waves.  dpp_move: lanes with no source lane get 0 (BOUND_ZERO) or
+// `old`; lanes of rows outside ROWS get `old`.
+template <int CTRL, int ROWS = 0xf, bool BOUND_ZERO = true>
+__device__ __forceinline__ int dpp_move(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xf, BOUND_ZERO);
+}
+// Inclusive prefix sum of one int per lane.
+__device__ __forceinline__ int wave_incl_scan_i(int x) {
+  x += dpp_move<0x111>(0, x);             // row_shr:1 (no source: 0)
+  x += dpp_move<0x112>(0, x);             // row_shr:2
+  x += dpp_move<0x114>(0, x);             // row_shr:4
+  x += dpp_move<0x118>(0, x);             // row_shr:8
+  x += dpp_move<0x142, 0xa, false>(0, x); // row_bcast:15 into rows 1, 3
+  x += dpp_move<0x143, 0xc, false>(0, x); // row_bcast:31 into rows 2, 3
+  return x;
+}
+// Sum over the wave, in every lane (a fixed order: deterministic).
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
-  return v;
+  int x = __float_as_int(v);
+  x = __float_as_int(__int_as_float(x) + __int_as_float(dpp_move<0x111>(0, x)));
+  x = __float_as_int(__int_as_float(x) + __int_as_float(dpp_move<0x112>(0, x)));
+  x = __float_as_int(__int_as_float(x) + __int_as_float(dpp_move<0x114>(0, x)));
+  x = __float_as_int(__int_as_float(x) + __int_as_float(dpp_move<0x118>(0, x)));
+  x = __float_as_int(__int_as_float(x) + __int_as_float(dpp_move<0x142, 0xa, false>(0, x)));
+  x = __float_as_int(__int_as_float(x) + __int_as_float(dpp_move<0x143, 0xc, false>(0, x)));
+  return __int_as_float(__builtin_amdgcn_readlane(x, 63));
 }
+// Maximum over the wave, in every lane (lanes with no source keep their own).
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, MOE_WAVE));
-  return v;
-}
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o, MOE_WAVE);
-    v = w > v ? w : v;
-  }
-  return v;
-}
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
-  return v;
+  int x = __float_as_int(v);
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp_move<0x111, 0xf, false>(x, x))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp_move<0x112, 0xf, false>(x, x))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp_move<0x114, 0xf, false>(x, x))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp_move<0x118, 0xf, false>(x, x))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp_move<0x142, 0xa, false>(x, x))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp_move<0x143, 0xc, false>(x, x))));
+  return __int_as_float(__builtin_amdgcn_readlane(x, 63));
 }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (MOE_WAVE - 1); }
 

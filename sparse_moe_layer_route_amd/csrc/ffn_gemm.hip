@@ -148,12 +148,7 @@ __device__ __forceinline__ int seg_table_build(const GemmArgs& a, SegTable& t) {
     }
   }
   const int tiles = (n + GN - 1) / GN;
-  int incl = tiles;
-#pragma unroll
-  for (int o = 1; o < MOE_WAVE; o <<= 1) {
-    const int v = __shfl_up(incl, o, MOE_WAVE);
-    if (lane >= o) incl += v;
-  }
+  const int incl = wave_incl_scan_i(tiles);
   if (threadIdx.x < MOE_WAVE) {
     t.o0[lane] = o0;
     t.n[lane] = n;

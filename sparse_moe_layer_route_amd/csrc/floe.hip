@@ -322,31 +322,19 @@ floe_up_bf16_kernel(const bf16* __restrict__ x, const uint8_t* __restrict__ up_q
   if (lane < RPW && i0 + lane < I) u_out[(int64_t)blockIdx.y * I + i0 + lane] = uval;
 }
 
-// Wave-wide inclusive prefix sum on the DPP lane network (no LDS round
-// trips): shifts by 1, 2, 4 and 8 lanes within each row of 16 (lanes with no
-// source add 0), then the rows add the totals of the rows before them (lane
-// 15 of each row broadcast into rows 1 and 3, lane 31 into rows 2 and 3).
-__device__ __forceinline__ int dpp_scan_add(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);    // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);    // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);    // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);    // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
-  return x;
-}
-// Wave-wide maximum (MAX) or minimum of unsigned values, in every lane: the
-// same network, lanes with no source keeping their own value.
+// Wave-wide maximum (MAX) or minimum of unsigned values, in every lane, on
+// the DPP network (lanes with no source keep their own value).
 template <bool MAX>
-__device__ __forceinline__ uint32_t dpp_reduce_u32(uint32_t x) {
+__device__ __forceinline__ uint32_t dpp_reduce_u32(uint32_t v) {
   auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x111, 0xf, 0xf, false));
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x112, 0xf, 0xf, false));
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x114, 0xf, 0xf, false));
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x118, 0xf, 0xf, false));
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x142, 0xa, 0xf, false));
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x143, 0xc, 0xf, false));
-  return (uint32_t)__builtin_amdgcn_readlane((int)x, MOE_WAVE - 1);
+  int x = (int)v;
+  x = (int)op((uint32_t)x, (uint32_t)dpp_move<0x111, 0xf, false>(x, x));
+  x = (int)op((uint32_t)x, (uint32_t)dpp_move<0x112, 0xf, false>(x, x));
+  x = (int)op((uint32_t)x, (uint32_t)dpp_move<0x114, 0xf, false>(x, x));
+  x = (int)op((uint32_t)x, (uint32_t)dpp_move<0x118, 0xf, false>(x, x));
+  x = (int)op((uint32_t)x, (uint32_t)dpp_move<0x142, 0xa, false>(x, x));
+  x = (int)op((uint32_t)x, (uint32_t)dpp_move<0x143, 0xc, false>(x, x));
+  return (uint32_t)__builtin_amdgcn_readlane(x, MOE_WAVE - 1);
 }
 
 constexpr int FLOE_SELECT_WAVES = FLOE_SELECT_THREADS / MOE_WAVE;
@@ -354,7 +342,7 @@ constexpr int FLOE_SELECT_WAVES = FLOE_SELECT_THREADS / MOE_WAVE;
 // Block-wide exclusive scan of one int per thread (1024 threads).
 __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
   const int lane = lane_id(), wv = threadIdx.x >> 6;
-  const int s = dpp_scan_add(v);
+  const int s = wave_incl_scan_i(v);
   if (lane == MOE_WAVE - 1) wsum[wv] = s;
   __syncthreads();
   int base = 0, tot = 0;
@@ -466,7 +454,7 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
       hb[0] = h[tid];
     }
     const int tsum = hb[0] + hb[1] + hb[2] + hb[3];
-    const int pre = dpp_scan_add(tsum);
+    const int pre = wave_incl_scan_i(tsum);
     if (lane == MOE_WAVE - 1) wsum[wv] = pre;
     __syncthreads();
     int after = 0;   // the waves after this one
@@ -553,7 +541,7 @@ floe_select_kernel(const float* __restrict__ u, int I, int n_keep, float margin,
   }
   // ascending listing: exclusive scan of the per-thread kept counts
   const int cnt = __popc(kept);
-  const int pre = dpp_scan_add(cnt);
+  const int pre = wave_incl_scan_i(cnt);
   if (lane == MOE_WAVE - 1) wsum[wv] = pre;
   __syncthreads();
   int pos = pre - cnt;

@@ -88,12 +88,7 @@ __device__ __forceinline__ void permute_chunk(int chunk, int nchunks, int n_pair
     const int c0 = 2 * lane < NB ? tot[2 * lane] : 0;
     const int c1 = 2 * lane + 1 < NB ? tot[2 * lane + 1] : 0;
     const int c = c0 + c1;
-    int s = c;
-#pragma unroll
-    for (int o = 1; o < MOE_WAVE; o <<= 1) {
-      const int v = __shfl_up(s, o, MOE_WAVE);
-      if (lane >= o) s += v;
-    }
+    const int s = wave_incl_scan_i(c);
     cursor[2 * lane] = s - c + (2 * lane < NB ? before[2 * lane] : 0);
     cursor[2 * lane + 1] = s - c + c0 + (2 * lane + 1 < NB ? before[2 * lane + 1] : 0);
     if (lane == MOE_WAVE - 1) s_total = s;
