@@ -65,15 +65,8 @@ struct RouteLds {
 #ifndef ROUTE_TILE_U
 #define ROUTE_TILE_U 4
 #endif
-// Grids of at most this many blocks load the logits' operands 8 k steps at a time.
-#ifndef ROUTE_FEW_BLOCKS
-#define ROUTE_FEW_BLOCKS 32
-#endif
 // Logits of tokens t0..t0+15 (rows past T are clamped, results unused) into
-// lds.logits.  Called by all 1024 threads.  U: k steps per batch of loads in
-// flight (a grid of a few blocks takes 8, so a 4096-wide router row is one
-// batch per wave: one round trip to memory instead of two).
-template <int U = ROUTE_TILE_U>
+// lds.logits.  Called by all 1024 threads.
 __device__ __forceinline__ void tile_logits(const bf16* __restrict__ x, const bf16* __restrict__ w,
                                             int T, int H, int E, int t0, RouteLds& lds) {
   const int lane = lane_id(), wv = threadIdx.x >> 6;
@@ -89,10 +82,11 @@ __device__ __forceinline__ void tile_logits(const bf16* __restrict__ x, const bf
     const bool live = e < E;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     const int ksteps = H >> 5;
-    // k steps sp, sp + n_sp, ... in batches of U loads in flight; steps past
-    // the end load the last step again and multiply zeros.  Over a full grid
-    // batches of 8 or 12 (one batch per wave at 1536 x 40 experts) measured
+    // k steps sp, sp + n_sp, ... in batches of ROUTE_TILE_U loads in flight;
+    // steps past the end load the last step again and multiply zeros.
+    // Batches of 8 or 12 (one batch per wave at 1536 x 40 experts) measured
     // slower than 4 (4096 tokens: 15.3 us at 4, 18.3 at 8, 15.7 at 12)
+    constexpr int U = ROUTE_TILE_U;
     for (int ks = sp; ks < ksteps; ks += U * n_sp) {
       bf16x8_t a[U], b[U];
 #pragma unroll
@@ -121,7 +115,6 @@ __device__ __forceinline__ void tile_logits(const bf16* __restrict__ x, const bf
   __syncthreads();
 }
 
-template <int U = ROUTE_TILE_U>
 __device__ __forceinline__ void tile_logits(const float* __restrict__ x, const float* __restrict__ w,
                                             int T, int H, int E, int t0, RouteLds& lds) {
   const int lane = lane_id(), wv = threadIdx.x >> 6;
@@ -149,13 +142,7 @@ __device__ __forceinline__ void tile_logits(const float* __restrict__ x, const f
 constexpr int LOGIT_WAVES = ROUTE_LOGIT_WAVES;
 
 // Logits of tokens 16*blockIdx.x.. and experts 16*blockIdx.y.. into
-// logits [T][E].  U: k steps per batch of loads in flight (a grid of a few
-// blocks takes all of a wave's steps in one or two batches: one-token layers
-// wait on one or two memory round trips instead of two to four).
-#ifndef ROUTE_LOGIT_U
-#define ROUTE_LOGIT_U 4
-#endif
-template <int U>
+// logits [T][E].
 __global__ void __launch_bounds__(LOGIT_WAVES * MOE_WAVE)
 route_logits_kernel(const bf16* __restrict__ x, const bf16* __restrict__ w, int T, int H, int E,
                     float* __restrict__ logits, int32_t* __restrict__ zero_me) {
@@ -168,6 +155,10 @@ route_logits_kernel(const bf16* __restrict__ x, const bf16* __restrict__ w, int 
   const bf16* xr = x + (int64_t)min(t0 + r16, T - 1) * H + 8 * kg;
   const bf16* wr = w + (int64_t)min(e0 + r16, E - 1) * H + 8 * kg;
   const bool live = e0 + r16 < E;
+#ifndef ROUTE_LOGIT_U
+#define ROUTE_LOGIT_U 4
+#endif
+  constexpr int U = ROUTE_LOGIT_U;
   const int ksteps = H >> 5;
   const int per = (ksteps + LOGIT_WAVES - 1) / LOGIT_WAVES;
   const int kb = wv * per, ke = min(ksteps, kb + per);
@@ -202,7 +193,6 @@ route_logits_kernel(const bf16* __restrict__ x, const bf16* __restrict__ w, int 
   }
 }
 
-template <int U>
 __global__ void __launch_bounds__(LOGIT_WAVES * MOE_WAVE)
 route_logits_kernel(const float* __restrict__ x, const float* __restrict__ w, int T, int H, int E,
                     float* __restrict__ logits, int32_t* __restrict__ zero_me) {
@@ -460,8 +450,7 @@ route_fused_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w_router, 
                    const Tin* __restrict__ w_sg, float* __restrict__ g_s, PermOut po) {
   __shared__ RouteLds lds;
   const int t0 = blockIdx.x * tpb;
-  if (gridDim.x <= ROUTE_FEW_BLOCKS) tile_logits<8>(x, w_router, T, H, E, t0, lds);
-  else tile_logits<ROUTE_TILE_U>(x, w_router, T, H, E, t0, lds);
+  tile_logits(x, w_router, T, H, E, t0, lds);
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   const int t = t0 + wv;
   if (wv < tpb && t < T) {
@@ -501,8 +490,7 @@ prefetch_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w_p, int T, i
                 int32_t* __restrict__ overlap_out) {
   __shared__ RouteLds lds;
   const int t0 = blockIdx.x * ROUTE_TOK;
-  if (gridDim.x <= ROUTE_FEW_BLOCKS) tile_logits<8>(x, w_p, T, H, E, t0, lds);
-  else tile_logits<ROUTE_TILE_U>(x, w_p, T, H, E, t0, lds);
+  tile_logits(x, w_p, T, H, E, t0, lds);
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   const int t = t0 + wv;
   if (t >= T) return;
@@ -604,19 +592,9 @@ hipError_t launch_route(const moe_dims_t& d, int T, const void* x, const void* w
   const bool small = fuse && T <= ROUTE_TOPK_SMALL_T;
   int32_t* zero_me = (fuse && !small) ? po->counter : nullptr;
   const PermOut none{};
-  // a wave's share of the k steps in one or two batches when the grid is small
-  const int per = ((d.hidden >> 5) + LOGIT_WAVES - 1) / LOGIT_WAVES;
-  const bool few = (int)(lgrid.x * lgrid.y) <= ROUTE_FEW_BLOCKS;
   if (d.dtype == MOE_BF16) {
-    if (few && per > 8)
-      route_logits_kernel<16><<<lgrid, LOGIT_WAVES * MOE_WAVE, 0, s>>>(
-          (const bf16*)x, (const bf16*)w_router, T, d.hidden, d.n_experts, logits, zero_me);
-    else if (few)
-      route_logits_kernel<8><<<lgrid, LOGIT_WAVES * MOE_WAVE, 0, s>>>(
-          (const bf16*)x, (const bf16*)w_router, T, d.hidden, d.n_experts, logits, zero_me);
-    else
-      route_logits_kernel<ROUTE_LOGIT_U><<<lgrid, LOGIT_WAVES * MOE_WAVE, 0, s>>>(
-          (const bf16*)x, (const bf16*)w_router, T, d.hidden, d.n_experts, logits, zero_me);
+    route_logits_kernel<<<lgrid, LOGIT_WAVES * MOE_WAVE, 0, s>>>(
+        (const bf16*)x, (const bf16*)w_router, T, d.hidden, d.n_experts, logits, zero_me);
     if (small)
       route_topk_small_kernel<bf16><<<1, T * MOE_WAVE, 0, s>>>(
           (const bf16*)x, logits, T, d.hidden, d.n_experts, d.top_k, d.renormalize, d.tie_margin,
@@ -630,7 +608,7 @@ hipError_t launch_route(const moe_dims_t& d, int T, const void* x, const void* w
           (const bf16*)x, logits, T, d.hidden, d.n_experts, d.top_k, d.renormalize, d.tie_margin,
           mode, resident, res_stride, ids, w, exact, flags, mass, (const bf16*)w_sg, g_s, none);
   } else {
-    route_logits_kernel<1><<<lgrid, LOGIT_WAVES * MOE_WAVE, 0, s>>>(
+    route_logits_kernel<<<lgrid, LOGIT_WAVES * MOE_WAVE, 0, s>>>(
         (const float*)x, (const float*)w_router, T, d.hidden, d.n_experts, logits, zero_me);
     if (small)
       route_topk_small_kernel<float><<<1, T * MOE_WAVE, 0, s>>>(
