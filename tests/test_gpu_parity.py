@@ -373,7 +373,7 @@ def _floe_stack(layer, field):
     return np.stack([layer.expert(field, e) for e in range(layer.cfg.n_experts)])
 
 
-def _floe_predict_gpu(layer, T, h_np, ids):
+def _floe_predict_gpu(layer, T, h_np, ids, wdev=None):
     cfg = layer.cfg
     dims = M.Dims(**dims_dict(cfg))
     k, nk = cfg.top_k, cfg.floe_keep
@@ -381,8 +381,8 @@ def _floe_predict_gpu(layer, T, h_np, ids):
     keep = torch.full((T * k * nk,), -3, dtype=torch.int32, device="cuda")
     flags = torch.zeros(T, dtype=torch.int32, device="cuda")
     d_ids = torch.from_numpy(np.ascontiguousarray(ids, np.int32).reshape(-1)).cuda()
-    M.moe_floe_predict(dims, T, tensor(h_np, cfg.dtype, "cuda"), dev_weights(layer), d_ids, keep,
-                       flags, ws)
+    M.moe_floe_predict(dims, T, tensor(h_np, cfg.dtype, "cuda"),
+                       dev_weights(layer) if wdev is None else wdev, d_ids, keep, flags, ws)
     torch.cuda.synchronize()
     return keep.cpu().numpy().reshape(T, k, nk), flags.cpu().numpy().view(np.uint32)
 
@@ -419,6 +419,42 @@ def test_floe_predict_parity(name, T):
             rec.append(O.mask_recall(ok, tk))
     assert (gf & ~np.uint32(O.FLAG_FLOE)).sum() == 0
     say(f"    {name} T={T}: near-ties {n_tie}, oracle recall vs the true mask {np.mean(rec):.3f}")
+
+
+@pytest.mark.parametrize("keep", [104, 105, 520])
+def test_floe_select_exact_channel_ties(keep):
+    """Exact |u| ties over many channels: every even up row is the same row and
+    every odd row's codes equal its zero point (u = 0 up to rounding), so the
+    520 even channels tie exactly and the channel select must keep the lowest
+    `keep` of them (ties to the lower channel), as the oracle's rule does, and
+    raise the mask-edge flag when the edge falls inside the tie.  This takes
+    the select's equal-key ranking."""
+    base = _floe_layer_for("floe_small")
+    layer = W.Layer(dataclasses.replace(base.cfg, floe_keep=keep))
+    cfg = layer.cfg
+    T, k = 5, cfg.top_k
+    q, sc, zp = layer.full("up_q").copy(), layer.full("up_scale").copy(), layer.full("up_zero").copy()
+    q[:, 0::2], sc[:, 0::2], zp[:, 0::2] = q[:, :1], sc[:, :1], zp[:, :1]
+    q[:, 1::2] = 0x55            # every 2-bit code 1
+    zp[:, 1::2] = 0x3C00         # zero point 1.0 (fp16)
+    wdev = dict(dev_weights(layer))
+    wdev["up_q"] = tensor(q, cfg.dtype, "cuda")
+    wdev["up_scale"] = tensor(sc, cfg.dtype, "cuda")
+    wdev["up_zero"] = tensor(zp, cfg.dtype, "cuda")
+    X = O.decode(layer.x(T), cfg.dtype)
+    Xp = O.decode(layer.x_prev(T), cfg.dtype)
+    ids = _oracle_routed(layer, X, k)
+    gk, gf = _floe_predict_gpu(layer, T, layer.x_prev(T), ids, wdev)
+    want = list(range(0, 2 * keep, 2))
+    tie = keep < 520    # at 520 every tied channel is kept: no edge inside the tie
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            ok, ofl, _ = O.floe_channel_mask(Xp[t], q[e], sc[e], zp[e], keep, MARGIN)
+            assert list(ok) == want and ofl == tie
+            assert list(gk[t, j]) == want
+        assert bool(gf[t] & O.FLAG_FLOE) == tie
+    say(f"    exact channel ties, keep {keep}: lowest even channels kept on every pair")
 
 
 @pytest.mark.parametrize("name,T", [("floe_small", 5), ("mixtral", 3)])
