@@ -22,7 +22,7 @@
 // stages had made the L2 -> LDS stream 15% slower (with the arithmetic left
 // out, 131 -> 114 us for the Granite-shaped gate/up launch).  With both the
 // stream and the arithmetic measured apart (114 and 105 us there) the
-// whole launch takes about 133 us: the two overlap only in part.  Each
+// whole launch takes about 132 us: the two overlap only in part.  Each
 // 64-byte weight row holds four 16-byte k chunks stored at chunk ^ ((row / 2)
 // % 4), each 128-byte token row eight stored at chunk ^ (row % 8): a 16-byte
 // LDS read is served eight lanes at a time over 32 banks, and the eight rows
@@ -238,10 +238,10 @@ __device__ __forceinline__ TileMeta tile_get(const TileTable& tt, int j) {
 // Wait until at most N of this wave's vector-memory operations are pending
 // (LDS DMA loads complete in issue order).
 #define GEMM_VMCNT(N) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory")
-// at most two later stages of this thread's DMA loads still pending
 
-// The GTT token fragments (LDS rows sb + 16j) and NW*WT weight fragments (rows
-// sa + m*MW + 16i) of one stage; row offsets are instruction immediates.
+// The GTT token fragments (LDS rows sb + 16j, RS bytes a row) and NW*WT weight
+// fragments (rows sa + m*MW + 16i) of one stage; row offsets are instruction
+// immediates.
 template <int J, int NJ, int RS>
 __device__ __forceinline__ void read_fb(u32x4 (&fb)[NJ], uint32_t sb) {
   if constexpr (J < NJ) {
