@@ -852,22 +852,27 @@ floe_reduce_combine_kernel(const float* __restrict__ part, int H, int k, int n_s
   __shared__ float red[MOE_MAX_TOPK][Q][64];
   const int t = blockIdx.y, c = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int h = blockIdx.x * 64 + c;
-  for (int j = 0; j < k; ++j) {
-    const int p = row_of[(int64_t)t * k + j];
-    float s = 0.f;
-    if (p >= 0) {
-      for (int sl = q; sl < n_slices; sl += Q * B) {
-        float v[B];
+  // two slots at a time, so both pairs' partial loads are in flight together
+  for (int j0 = 0; j0 < k; j0 += 2) {
+    const int j1 = j0 + 1;
+    const int p0 = row_of[(int64_t)t * k + j0];
+    const int p1 = j1 < k ? row_of[(int64_t)t * k + j1] : -1;
+    float s0 = 0.f, s1 = 0.f;
+    for (int sl = q; sl < n_slices; sl += Q * B) {
+      float v0[B], v1[B];
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-          const int ss = sl + Q * b;
-          v[b] = ss < n_slices ? part[((int64_t)ss * P_max + p) * H + h] : 0.f;
-        }
-#pragma unroll
-        for (int b = 0; b < B; ++b) s += v[b];
+      for (int b = 0; b < B; ++b) {
+        const int ss = sl + Q * b;
+        v0[b] = (p0 >= 0 && ss < n_slices) ? part[((int64_t)ss * P_max + p0) * H + h] : 0.f;
+        v1[b] = (p1 >= 0 && ss < n_slices) ? part[((int64_t)ss * P_max + p1) * H + h] : 0.f;
       }
+#pragma unroll
+      for (int b = 0; b < B; ++b) s0 += v0[b];
+#pragma unroll
+      for (int b = 0; b < B; ++b) s1 += v1[b];
     }
-    red[j][q][c] = s;
+    red[j0][q][c] = s0;
+    if (j1 < k) red[j1][q][c] = s1;
   }
   __syncthreads();
   if (q == 0) {
