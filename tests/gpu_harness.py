@@ -74,7 +74,7 @@ def out_to_np(t: torch.Tensor) -> np.ndarray:
 
 
 @dataclasses.dataclass
-class GpuRun:
+class GpuResult:
     out: np.ndarray
     ids: np.ndarray
     w: np.ndarray
@@ -131,7 +131,7 @@ def prefetch_adaptive_gpu(layer: W.Layer, T: int, wdev, tau: float, theta=None, 
 
 
 def run_layer(layer: W.Layer, T: int, mode: str, wdev=None, dims_over=None,
-              resident_masks=None, x_np=None, layout="rows") -> GpuRun:
+              resident_masks=None, x_np=None, layout="rows") -> GpuResult:
     """moe_layer_forward on the first T rows of the layer's x; layout
     "mfma16" packs the expert matrices (of wdev, or the layer's own) first."""
     cfg = layer.cfg
@@ -171,7 +171,7 @@ def run_layer(layer: W.Layer, T: int, mode: str, wdev=None, dims_over=None,
     torch.cuda.synchronize()
     g = {n: t.cpu().numpy() for n, t in dbg.items()}
     keep = g["floe_keep"].reshape(T, k, dd["floe_keep"]) if mode == "floe" else None
-    return GpuRun(out=out_to_np(out), ids=g["topk_ids"].reshape(T, k), w=g["topk_w"].reshape(T, k),
+    return GpuResult(out=out_to_np(out), ids=g["topk_ids"].reshape(T, k), w=g["topk_w"].reshape(T, k),
                   exact=g["exact"].reshape(T, k), flags=g["flags"].view(np.uint32),
                   logits=g["logits"].reshape(T, E), mass=g["mass"], offsets=g["expert_offsets"],
                   perm=g["perm"][: int(g["expert_offsets"][E])], keep=keep, masks=masks)
@@ -195,7 +195,7 @@ def _flag_gap_ok(gap: float) -> bool:
     return abs(gap - MARGIN) < 1e-2 * MARGIN
 
 
-def check_decisions(layer: W.Layer, T: int, mode: str, g: GpuRun, dims_over=None,
+def check_decisions(layer: W.Layer, T: int, mode: str, g: GpuResult, dims_over=None,
                     x_np=None) -> dict:
     """Routing decisions for all T tokens: bit-exact unless the oracle flags a
     near-tie; admissible otherwise.  The GPU's flag bits 1 (route near-tie),
@@ -278,7 +278,7 @@ def check_decisions(layer: W.Layer, T: int, mode: str, g: GpuRun, dims_over=None
     return dict(flagged=n_flag, exact=n_exact, substituted_slots=n_sub, short_sets=n_short)
 
 
-def oracle_forward_forced(layer: W.Layer, T: int, mode: str, g: GpuRun, sample: Sequence[int],
+def oracle_forward_forced(layer: W.Layer, T: int, mode: str, g: GpuResult, sample: Sequence[int],
                           dims_over=None, weights=None, x_np=None):
     """The oracle on tokens `sample`, with the GPU's routing (and FloE mask)
     decisions forced, so a near-tie cannot split the comparison."""
@@ -295,7 +295,7 @@ def oracle_forward_forced(layer: W.Layer, T: int, mode: str, g: GpuRun, sample: 
     return O.layer_forward(x, src, dd, mode, resident=res, force=force, tie_margin=MARGIN)
 
 
-def check_floe_masks(layer: W.Layer, g: GpuRun, ref: dict, sample: Sequence[int]):
+def check_floe_masks(layer: W.Layer, g: GpuResult, ref: dict, sample: Sequence[int]):
     """FloE kept channels: exact where the oracle sees no near-tie at the
     mask edge; admissible within the margin otherwise.  Flag bit 8 of a token
     matches the oracle's (some pair of the token at a near-tie), except where

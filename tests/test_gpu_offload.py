@@ -1,4 +1,4 @@
-"""Exact execution of missed experts on the GPU box [SPICE page, "CPU-GPU
+"""Exact execution of missed experts on the GPU [SPICE page, "CPU-GPU
 collaboration: handling prefetch misses"]: moe_layer_forward_offload with
 every non-resident expert slot on the GPU filled with NaN, so an expert that
 is neither fetched nor run on the host poisons the output.  Each plan (all
