@@ -10,8 +10,10 @@
 // pair's rank among equal buckets is the popcount of its wave's peer mask
 // (eight ballots over the bits of bucket+1) below its lane, plus the counts
 // of the same bucket in the waves before it, so the order is stable and
-// deterministic with no order-dependent atomics.  Up to 1024 pairs the
-// histogram is taken inside the single scatter block (one launch).
+// deterministic with no order-dependent atomics.  Up to a few chunks each
+// scatter block takes the histogram of all pairs itself (one launch).
+#include <algorithm>
+
 #include "permute_block.h"
 
 namespace moe {
@@ -49,13 +51,20 @@ int permute_scratch_bytes(int n_pairs, int E) {
   return nchunks > 1 ? nchunks * 2 * E * 4 : 0;
 }
 
+// Up to this many chunks every scatter block histograms all pairs itself (a
+// few thousand pairs: one launch instead of the count and scatter launches).
+#ifndef PERM_SELF_HIST_CHUNKS
+#define PERM_SELF_HIST_CHUNKS 4
+#endif
+
 hipError_t launch_permute(int n_pairs, int E, const int32_t* ids, const uint8_t* exact,
                           int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* row_of,
                           int32_t* miss_offsets, int32_t* scratch, hipStream_t s) {
   const int nchunks = (n_pairs + PERM_THREADS - 1) / PERM_THREADS;
-  if (nchunks <= 1) {
-    permute_kernel<<<1, PERM_THREADS, 0, s>>>(n_pairs, E, ids, exact, nullptr, offsets, perm, inv,
-                                              row_of, miss_offsets);
+  if (nchunks <= PERM_SELF_HIST_CHUNKS) {
+    permute_kernel<<<std::max(nchunks, 1), PERM_THREADS, 0, s>>>(n_pairs, E, ids, exact, nullptr,
+                                                                offsets, perm, inv, row_of,
+                                                                miss_offsets);
   } else {
     permute_count_kernel<<<nchunks, PERM_THREADS, 0, s>>>(n_pairs, E, ids, exact, scratch);
     permute_kernel<<<nchunks, PERM_THREADS, 0, s>>>(n_pairs, E, ids, exact, scratch, offsets, perm,

@@ -23,8 +23,8 @@ __device__ __forceinline__ int bucket_of(int f, int E, const int32_t* __restrict
 }
 
 // Places chunk `chunk` of `nchunks`; every thread of a 1024-thread block
-// calls it.  counts == nullptr: the block histograms its (single) chunk
-// itself.  A pair's rank among equal buckets in the chunk is the popcount of
+// calls it.  counts == nullptr: the block histograms every pair itself.
+// A pair's rank among equal buckets in the chunk is the popcount of
 // its wave's peer mask (eight ballots over the bits of bucket+1) below its
 // lane, plus that bucket's counts in earlier waves, so the order is stable
 // and deterministic with no order-dependent atomics.
@@ -75,12 +75,22 @@ __device__ __forceinline__ void permute_chunk(int chunk, int nchunks, int n_pair
       before[tid] = sb;
     }
   } else {
+    // no per-chunk histograms: the block counts every pair itself (one
+    // chunk, or a few), all of them for the bucket totals and those of the
+    // chunks before its own for its starts
     if (tid < PERM_BUCKETS) {
       tot[tid] = 0;
       before[tid] = 0;
     }
     __syncthreads();
-    if (b >= 0) atomicAdd(&tot[b], 1);
+    const int lo = chunk * PERM_THREADS;
+    for (int g = tid; g < n_pairs; g += PERM_THREADS) {
+      const int bg = g == f ? b : bucket_of(g, E, ids, exact);
+      if (bg >= 0) {
+        atomicAdd(&tot[bg], 1);
+        if (g < lo) atomicAdd(&before[bg], 1);
+      }
+    }
   }
   __syncthreads();
   if (tid < MOE_WAVE) {

@@ -638,7 +638,8 @@ def test_permute_parity_random():
     rng = np.random.default_rng(7)
     for T, k, E, p_exact in [(1, 1, 1, 1.0), (37, 6, 64, 0.5), (4096, 8, 40, 1.0), (300, 8, 64, 0.0),
                              (1000, 2, 8, 0.7), (5, 8, 64, 1.0), (128, 8, 16, 0.6), (129, 8, 16, 0.6),
-                             (2999, 7, 64, 0.5)]:
+                             (2999, 7, 64, 0.5), (512, 8, 64, 0.5), (4097, 1, 64, 0.5),
+                             (256, 8, 64, 1.0)]:
         ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
         exact = (rng.random((T, k)) < p_exact).astype(np.uint8)
         d_ids = torch.from_numpy(ids.reshape(-1)).cuda()
