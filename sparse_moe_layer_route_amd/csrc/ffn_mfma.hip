@@ -169,9 +169,18 @@ __device__ __forceinline__ void store_bf16x4(bf16* dst, int64_t off, const float
 #ifndef FFN_UNROLL_MID
 #define FFN_UNROLL_MID 1
 #endif
+// Gate/up with two row tiles per wave (long segments): one step per set up
+// to two token tiles, whose registers the wide rows already fill.
+#ifndef FFN_UNROLL_WIDE_UP
+#define FFN_UNROLL_WIDE_UP 1
+#endif
 template <int NA>
 struct Unroll {
   static constexpr int U = NA <= 2 ? FFN_UNROLL_SMALL : (NA == 4 ? FFN_UNROLL_MID : 1);
+};
+template <int NA, int RW>
+struct UpUnroll {
+  static constexpr int U = (RW > 1 && NA <= 2) ? FFN_UNROLL_WIDE_UP : Unroll<NA>::U;
 };
 
 // Wave wk's contiguous share [beg, end) of nsteps k-steps, in nb batches of U.
@@ -208,7 +217,7 @@ __device__ __forceinline__ void up_chunk(const FfnMfmaArgs a, const TileInfo& ti
                                          const bf16* const (&au_row)[RW], bool gated,
                                          bool rows_ok, int row_base, int R,
                                          f32x4_t (*red)[(WK > 1) ? 2 * NTT * RW : 1][MOE_WAVE]) {
-  constexpr int U = Unroll<NA>::U;
+  constexpr int U = UpUnroll<NA, RW>::U;
   const int lane = lane_id(), wv = threadIdx.x >> 6, wk = wv / WM, wm = wv % WM;
   const int r16 = lane & 15, kg = lane >> 4;
   const int H = a.H, ksteps = H >> 5;
